@@ -1,0 +1,218 @@
+"""CPU oracle for the DSA hot path (lightning indexer -> top-k -> sparse GQA attention).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links this
+module; only the tests, the smoke check and the CPU-baseline leg of the benchmark do.
+It shares no code, table or constant with the HIP library.
+
+What is computed, and where it comes from:
+
+* Source A: the digest of the Kwai Keye-VL-2.0-30B-A3B technical report on mqxn.cn
+  (news item 1966), section 一 ("why long video is hard"): a light "scout" module, the
+  Lightning Indexer, scans every position and scores which deserve attention; it uses an
+  MQA-style shared design (one key per position for all indexer heads); for every query
+  token the 2048 most relevant positions of the context are kept; attention then runs only
+  between the query and those positions, turning O(L^2) work into O(L*k).  The same section
+  says the base model is GQA and that DSA was adapted to GQA for the first time.
+* Source A, section 八 (inference engineering): top-k must be deterministic so that
+  training and inference select identical sets.
+* Source B: the aihot summary page "快手开源 Kwai Keye-VL-2.0-30B-A3B ..." (abstract):
+  DSA adapted to a GQA multimodal architecture, lossless 256K context.
+* Source C: the QbitAI re-post on news.chathome.org "將DSA注意力引入多模態 ...": DSA is run
+  in a variable-length (packed) sequence mode.
+
+The pages print no formula.  Readings adopted where they are silent (each one is also
+listed in the design notes):
+  R1  indexer score   I[t,s] = sum_j w[t,j] * max(0, <q_I[t,j,:], k_I[s,:]>), no extra scale
+  R2  w is per (token, head)
+  R3  causal prefix includes the diagonal: s in [0, t]
+  R4  a prefix shorter than k is taken whole; the index list is padded with -1
+  R5  ties go to the lower position; -0 equals +0
+  R6  selected positions are returned in ascending order
+  R8  GQA head h reads KV head h // (Hq // Hkv)
+  R9  softmax scale passed explicitly (1/sqrt(D) by default), lse is natural-log and
+      includes the scale
+  R11 positions are sequence-local; no attention across packed sequences
+  R12 a decode cache of length n holds the new token at position n-1
+
+Everything is float64.  Loops run per query row so that each step reads like its
+definition; speed is not a goal.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "index_scores_row",
+    "index_scores",
+    "select_topk_row",
+    "sparse_gqa_attention_row",
+    "prefill",
+    "decode",
+    "default_softmax_scale",
+]
+
+
+def default_softmax_scale(head_dim: int) -> float:
+    """1/sqrt(D) (reading R9)."""
+    return 1.0 / math.sqrt(head_dim)
+
+
+def index_scores_row(q_idx_row: np.ndarray, w_row: np.ndarray, k_idx_prefix: np.ndarray) -> np.ndarray:
+    """Lightning-indexer scores of one query token against its causal prefix.
+
+    Source A, section 一: one shared key per position (MQA), several indexer heads.
+    Reading R1: I[s] = sum_j w[j] * ReLU(<q_I[j], k_I[s]>).
+
+    q_idx_row    [H_I, d_I]  indexer query heads of the token
+    w_row        [H_I]       per-head weights of the token
+    k_idx_prefix [n, d_I]    indexer keys of positions 0..n-1 (n = t+1)
+    returns      [n] float64
+    """
+    q = np.asarray(q_idx_row, dtype=np.float64)
+    w = np.asarray(w_row, dtype=np.float64)
+    k = np.asarray(k_idx_prefix, dtype=np.float64)
+    logits = q @ k.T                      # [H_I, n]: <q_I[j], k_I[s]>
+    relu = np.maximum(logits, 0.0)        # ReLU per (head, position)
+    return w @ relu                       # weighted sum over heads -> [n]
+
+
+def index_scores(q_idx: np.ndarray, k_idx: np.ndarray, w: np.ndarray, cu_seqlens) -> list:
+    """Scores of every packed query row against its own sequence's causal prefix.
+
+    Returns a list with one float64 vector of length t+1 per packed row (reading R3, R11).
+    """
+    cu = [int(x) for x in cu_seqlens]
+    out = []
+    for b in range(len(cu) - 1):
+        o, n = cu[b], cu[b + 1] - cu[b]
+        for t in range(n):
+            out.append(index_scores_row(q_idx[o + t], w[o + t], k_idx[o:o + t + 1]))
+    return out
+
+
+def select_topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """Per-query top-k (source A, section 一: keep the k most relevant positions).
+
+    Readings R4-R6: a prefix of length <= k is kept whole; otherwise positions are ranked by
+    (-score, position) so equal scores favour the lower position; the kept positions are
+    returned in ascending order and padded with -1 to length k.  -0.0 and +0.0 compare equal
+    under the float comparison used by the sort, so no special case is needed.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    out = np.full(k, -1, dtype=np.int64)
+    if n <= k:
+        out[:n] = np.arange(n)
+        return out
+    # A stable sort on -score keeps equal scores in ascending position order.
+    order = np.argsort(-s, kind="stable")
+    chosen = np.sort(order[:k])
+    out[:] = chosen
+    return out
+
+
+def sparse_gqa_attention_row(q_row: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
+                             idx_row: np.ndarray, softmax_scale: float):
+    """Attention of one token over its selected positions only (source A, section 一),
+    with GQA sharing (source B; reading R8): query head h uses KV head h // G, and every
+    query head of the token uses the same index set.
+
+    q_row   [Hq, D]
+    k_seq   [S, Hkv, D]   keys of the token's sequence (local positions)
+    v_seq   [S, Hkv, D]
+    idx_row [k]           selected local positions, negative entries are padding
+    returns (O [Hq, D] float64, lse [Hq] float64, weight_sums [Hq] float64)
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    hq, d = q.shape
+    hkv = k_seq.shape[1]
+    g_size = hq // hkv
+    sel = np.asarray([int(i) for i in idx_row if int(i) >= 0], dtype=np.int64)
+    o = np.zeros((hq, d), dtype=np.float64)
+    lse = np.full(hq, -np.inf, dtype=np.float64)
+    wsum = np.zeros(hq, dtype=np.float64)
+    if sel.size == 0:
+        return o, lse, wsum
+    for h in range(hq):
+        g = h // g_size
+        keys = np.asarray(k_seq[sel, g, :], dtype=np.float64)    # [n_sel, D]
+        vals = np.asarray(v_seq[sel, g, :], dtype=np.float64)
+        z = softmax_scale * (keys @ q[h])                         # [n_sel]
+        m = z.max()
+        e = np.exp(z - m)
+        denom = e.sum()
+        p = e / denom
+        o[h] = p @ vals
+        lse[h] = m + math.log(denom)
+        wsum[h] = p.sum()
+    return o, lse, wsum
+
+
+def _seq_of_row(cu: list, r: int) -> int:
+    for b in range(len(cu) - 1):
+        if cu[b] <= r < cu[b + 1]:
+            return b
+    raise IndexError(r)
+
+
+def prefill(q, k, v, q_idx, k_idx, w, cu_seqlens, top_k, softmax_scale=None, rows=None):
+    """The whole prefill path for the packed rows listed in `rows` (all rows if None).
+
+    For each row r of sequence b (offset o, local position t = r - o):
+      1. scores over the prefix [0, t] of sequence b     (index_scores_row)
+      2. top-k positions, ascending, -1 padded           (select_topk_row)
+      3. GQA attention over those positions              (sparse_gqa_attention_row)
+
+    Returns dict with 'rows', 'idx' [n_rows, top_k] int64, 'out' [n_rows, Hq, D] float64,
+    'lse' [n_rows, Hq] float64, 'wsum' [n_rows, Hq] float64.
+    """
+    cu = [int(x) for x in cu_seqlens]
+    total = cu[-1]
+    hq, d = q.shape[1], q.shape[2]
+    if softmax_scale is None:
+        softmax_scale = default_softmax_scale(d)
+    rows = list(range(total)) if rows is None else [int(r) for r in rows]
+    idx = np.full((len(rows), top_k), -1, dtype=np.int64)
+    out = np.zeros((len(rows), hq, d), dtype=np.float64)
+    lse = np.zeros((len(rows), hq), dtype=np.float64)
+    wsum = np.zeros((len(rows), hq), dtype=np.float64)
+    for i, r in enumerate(rows):
+        b = _seq_of_row(cu, r)
+        o0, t = cu[b], r - cu[b]
+        sc = index_scores_row(q_idx[r], w[r], k_idx[o0:o0 + t + 1])
+        sel = select_topk_row(sc, top_k)
+        oo, ll, ws = sparse_gqa_attention_row(q[r], k[o0:cu[b + 1]], v[o0:cu[b + 1]], sel, softmax_scale)
+        idx[i], out[i], lse[i], wsum[i] = sel, oo, ll, ws
+    return {"rows": rows, "idx": idx, "out": out, "lse": lse, "wsum": wsum}
+
+
+def decode(q, q_idx, w, k_cache, v_cache, k_idx_cache, seq_lens, top_k, softmax_scale=None, batch=None):
+    """One decode step per sequence (reading R12: the new token sits at position n-1 of a
+    cache of length n and sees positions 0..n-1).
+
+    q [B, Hq, D], q_idx [B, H_I, d_I], w [B, H_I],
+    k_cache/v_cache [B, S_max, Hkv, D], k_idx_cache [B, S_max, d_I], seq_lens [B].
+    Returns dict with 'batch', 'idx' [n, top_k], 'out' [n, Hq, D], 'lse' [n, Hq], 'wsum', 'scores'
+    (list of float64 score vectors, one per sequence).
+    """
+    bsz = q.shape[0]
+    hq, d = q.shape[1], q.shape[2]
+    if softmax_scale is None:
+        softmax_scale = default_softmax_scale(d)
+    batch = list(range(bsz)) if batch is None else [int(b) for b in batch]
+    idx = np.full((len(batch), top_k), -1, dtype=np.int64)
+    out = np.zeros((len(batch), hq, d), dtype=np.float64)
+    lse = np.zeros((len(batch), hq), dtype=np.float64)
+    wsum = np.zeros((len(batch), hq), dtype=np.float64)
+    scores = []
+    for i, b in enumerate(batch):
+        n = int(seq_lens[b])
+        sc = index_scores_row(q_idx[b], w[b], k_idx_cache[b, :n])
+        sel = select_topk_row(sc, top_k)
+        oo, ll, ws = sparse_gqa_attention_row(q[b], k_cache[b, :n], v_cache[b, :n], sel, softmax_scale)
+        idx[i], out[i], lse[i], wsum[i] = sel, oo, ll, ws
+        scores.append(sc)
+    return {"batch": batch, "idx": idx, "out": out, "lse": lse, "wsum": wsum, "scores": scores}

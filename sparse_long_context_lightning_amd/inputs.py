@@ -1,0 +1,226 @@
+"""Seeded synthetic workloads for the DSA path.
+
+This module only draws random numbers and stores them as bf16 bit patterns; it holds none
+of the method's arithmetic.  Both the HIP path (through the tests and the benchmark) and the
+CPU oracle consume the arrays it returns, so the two sides always see identical bf16 values.
+
+Recipe (the same for every workload):
+  * every tensor is split into chunks of 2**22 elements; chunk c of tensor `name` is drawn
+    from numpy's PCG64 seeded with SeedSequence([seed, tensor_id(name), c]), so the values
+    do not depend on thread scheduling;
+  * indexer queries/keys are uniform integers in [-3, 3] (exact in bf16);
+  * indexer weights are 2**-e with e uniform in {0, 1, 2, 3}, stored as float32;
+  * Q, K, V are N(0, 1) float32 rounded once to bf16 (round to nearest even);
+  * "blocks16": positions come in 16-token blocks; the indexer key of position s is
+    clip(o_I[block, :] + round(n_s), -3, 3) with o_I uniform integers in [-2, 2] and n ~ N(0,1),
+    and the attention key is bf16(o[block, g, :] + n) with o, n ~ N(0,1).  This mimics
+    per-frame visual tokens that share content;
+  * "video": from each sequence start, 32 text tokens (i.i.d. as above) alternate with one
+    256-token frame built like a 16-token block but 256 long.
+"""
+
+from __future__ import annotations
+
+import os
+import zlib
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK = 1 << 22
+
+# bf16 bit patterns of the integers -3..3 (sign | exponent | 7-bit mantissa).
+_INT_BF16 = {-3: 0xC040, -2: 0xC000, -1: 0xBF80, 0: 0x0000, 1: 0x3F80, 2: 0x4000, 3: 0x4040}
+_INT_LUT = np.zeros(7, dtype=np.uint16)
+for _v, _b in _INT_BF16.items():
+    _INT_LUT[_v + 3] = _b
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _tensor_id(name: str) -> int:
+    return zlib.crc32(name.encode()) & 0x7FFFFFFF
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest even) and return the 16-bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _fill(name: str, seed: int, n: int, kind: str, out: np.ndarray) -> None:
+    tid = _tensor_id(name)
+    nch = (n + CHUNK - 1) // CHUNK
+
+    def work(c):
+        s = c * CHUNK
+        e = min(n, s + CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, tid, c])))
+        if kind == "int3":
+            out[s:e] = _INT_LUT[rng.integers(0, 7, size=e - s, dtype=np.int8)]
+        elif kind == "int2":
+            out[s:e] = rng.integers(-2, 3, size=e - s, dtype=np.int8)
+        elif kind == "normal_bf16":
+            out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+        elif kind == "normal_f32":
+            out[s:e] = rng.standard_normal(e - s, dtype=np.float32)
+        elif kind == "pow2w":
+            out[s:e] = np.ldexp(np.float32(1.0), -rng.integers(0, 4, size=e - s, dtype=np.int32)).astype(np.float32)
+        else:
+            raise ValueError(kind)
+
+    if nch == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(nch)))
+
+
+def _draw(name, seed, shape, kind):
+    n = int(np.prod(shape))
+    dt = {"int3": np.uint16, "int2": np.int8, "normal_bf16": np.uint16,
+          "normal_f32": np.float32, "pow2w": np.float32}[kind]
+    out = np.empty(n, dtype=dt)
+    _fill(name, seed, n, kind, out)
+    return out.reshape(shape)
+
+
+def _block_ids(total: int, cu: list, structure: str) -> np.ndarray:
+    """Block id per packed position, -1 for positions outside any block."""
+    ids = np.full(total, -1, dtype=np.int64)
+    nxt = 0
+    for b in range(len(cu) - 1):
+        o, n = cu[b], cu[b + 1] - cu[b]
+        t = np.arange(n)
+        if structure == "blocks16":
+            local = t // 16
+        elif structure == "video":
+            per = t % 288
+            local = np.where(per >= 32, t // 288, -1)
+        else:
+            return ids
+        nb = int(local.max()) + 1 if n else 0
+        ids[o:o + n] = np.where(local >= 0, local + nxt, -1)
+        nxt += nb
+    return ids
+
+
+def _structured_keys(name, seed, total, cu, structure, d_idx, hkv, d, k_idx_bits, k_bits):
+    """Overwrite the block positions of k_idx / k with offset + noise (see module docstring)."""
+    ids = _block_ids(total, cu, structure)
+    mask = ids >= 0
+    if not mask.any():
+        return
+    nblk = int(ids.max()) + 1
+    pos = np.nonzero(mask)[0]
+    bid = ids[pos]
+    # Indexer keys: integer offset per (block, dim) plus rounded unit noise, clipped to [-3, 3].
+    off_i = _draw(name + ".k_idx_off", seed, (nblk, d_idx), "int2").astype(np.int16)
+    noise_i = _draw(name + ".k_idx_noise", seed, (total, d_idx), "normal_f32")
+    vals = off_i[bid] + np.rint(noise_i[pos]).astype(np.int16)
+    vals = np.clip(vals, -3, 3)
+    k_idx_bits[pos] = _INT_LUT[vals + 3]
+    # Attention keys: normal offset per (block, head, dim) plus unit normal noise.
+    off = _draw(name + ".k_off", seed, (nblk, hkv, d), "normal_f32")
+    noise = _draw(name + ".k_noise", seed, (total, hkv, d), "normal_f32")
+    k_bits[pos] = f32_to_bf16_bits(off[bid] + noise[pos])
+
+
+@dataclass
+class PrefillInputs:
+    seq_lens: list
+    cu_seqlens: np.ndarray          # int32 [B+1]
+    q: np.ndarray                   # bf16 bits [T, Hq, D]
+    k: np.ndarray                   # bf16 bits [T, Hkv, D]
+    v: np.ndarray                   # bf16 bits [T, Hkv, D]
+    q_idx: np.ndarray               # bf16 bits [T, H_I, d_I]
+    k_idx: np.ndarray               # bf16 bits [T, d_I]
+    w: np.ndarray                   # float32 [T, H_I]
+    top_k: int
+    meta: dict = field(default_factory=dict)
+
+
+@dataclass
+class DecodeInputs:
+    seq_lens: np.ndarray            # int32 [B]
+    s_max: int
+    q: np.ndarray                   # bf16 bits [B, Hq, D]
+    q_idx: np.ndarray               # bf16 bits [B, H_I, d_I]
+    w: np.ndarray                   # float32 [B, H_I]
+    k_cache: np.ndarray             # bf16 bits [B, S_max, Hkv, D]
+    v_cache: np.ndarray             # bf16 bits [B, S_max, Hkv, D]
+    k_idx_cache: np.ndarray         # bf16 bits [B, S_max, d_I]
+    top_k: int
+    meta: dict = field(default_factory=dict)
+
+
+def prefill_inputs(seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="iid", name="prefill"):
+    seq_lens = [int(x) for x in seq_lens]
+    cu = [0]
+    for n in seq_lens:
+        cu.append(cu[-1] + n)
+    total = cu[-1]
+    q_idx = _draw(name + ".q_idx", seed, (total, h_idx, d_idx), "int3")
+    k_idx = _draw(name + ".k_idx", seed, (total, d_idx), "int3")
+    w = _draw(name + ".w", seed, (total, h_idx), "pow2w")
+    q = _draw(name + ".q", seed, (total, hq, d), "normal_bf16")
+    k = _draw(name + ".k", seed, (total, hkv, d), "normal_bf16")
+    v = _draw(name + ".v", seed, (total, hkv, d), "normal_bf16")
+    if structure != "iid":
+        _structured_keys(name, seed, total, cu, structure, d_idx, hkv, d, k_idx, k)
+    return PrefillInputs(seq_lens=seq_lens, cu_seqlens=np.asarray(cu, dtype=np.int32), q=q, k=k, v=v,
+                         q_idx=q_idx, k_idx=k_idx, w=w, top_k=top_k,
+                         meta=dict(h_idx=h_idx, d_idx=d_idx, hq=hq, hkv=hkv, d=d, seed=seed, structure=structure))
+
+
+def decode_inputs(batch, s_max, seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="iid", name="decode"):
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.shape == (batch,) and int(seq_lens.max()) <= s_max
+    q_idx = _draw(name + ".q_idx", seed, (batch, h_idx, d_idx), "int3")
+    w = _draw(name + ".w", seed, (batch, h_idx), "pow2w")
+    q = _draw(name + ".q", seed, (batch, hq, d), "normal_bf16")
+    k_idx_cache = _draw(name + ".k_idx", seed, (batch * s_max, d_idx), "int3")
+    k_cache = _draw(name + ".k", seed, (batch * s_max, hkv, d), "normal_bf16")
+    v_cache = _draw(name + ".v", seed, (batch, s_max, hkv, d), "normal_bf16")
+    if structure != "iid":
+        cu = [b * s_max for b in range(batch + 1)]
+        _structured_keys(name, seed, batch * s_max, cu, structure, d_idx, hkv, d, k_idx_cache, k_cache)
+    return DecodeInputs(seq_lens=seq_lens, s_max=s_max, q=q, q_idx=q_idx, w=w,
+                        k_cache=k_cache.reshape(batch, s_max, hkv, d), v_cache=v_cache,
+                        k_idx_cache=k_idx_cache.reshape(batch, s_max, d_idx), top_k=top_k,
+                        meta=dict(h_idx=h_idx, d_idx=d_idx, hq=hq, hkv=hkv, d=d, seed=seed, structure=structure))
+
+
+# The five synthetic workloads (shapes of the DSA layer at the pages' context lengths).
+WORKLOADS = {
+    "c1_tiny_prefill_4k": dict(kind="prefill", seq_lens=[4096], h_idx=4, d_idx=64, hq=8, hkv=2, d=128,
+                               top_k=256, seed=0, structure="iid"),
+    "c2_prefill_32k": dict(kind="prefill", seq_lens=[32768], h_idx=64, d_idx=128, hq=32, hkv=4, d=128,
+                           top_k=2048, seed=1, structure="iid"),
+    "c3_prefill_128k": dict(kind="prefill", seq_lens=[131072], h_idx=64, d_idx=128, hq=32, hkv=4, d=128,
+                            top_k=2048, seed=2, structure="blocks16"),
+    "c4_decode_b32_128k": dict(kind="decode", batch=32, s_max=131072, h_idx=64, d_idx=128, hq=32, hkv=4,
+                               d=128, top_k=2048, seed=3, structure="iid"),
+    "c5_video_mix_prefill": dict(kind="prefill", seq_lens=[262144, 65536, 8192], h_idx=64, d_idx=128, hq=32,
+                                 hkv=4, d=128, top_k=2048, seed=4, structure="video"),
+    "c5_video_mix_decode": dict(kind="decode", batch=8, s_max=262144, h_idx=64, d_idx=128, hq=32, hkv=4,
+                                d=128, top_k=2048, seed=4, structure="video"),
+}
+
+
+def workload(name: str):
+    spec = dict(WORKLOADS[name])
+    kind = spec.pop("kind")
+    if kind == "prefill":
+        return prefill_inputs(name=name, **spec)
+    batch, s_max = spec.pop("batch"), spec.pop("s_max")
+    return decode_inputs(batch, s_max, [s_max] * batch, name=name, **spec)

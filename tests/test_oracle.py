@@ -1,0 +1,288 @@
+"""Pins of the CPU oracle against things other than itself: hand-worked examples, closed
+forms, library routines (integer matmul, torch.topk, torch SDPA, scipy logsumexp) and brute
+force on tiny inputs.  CPU only."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+from oracle import dsa_oracle as orc
+from sparse_long_context_lightning_amd import inputs as inp
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- indexer scores
+
+def test_scores_hand_worked_example():
+    g = _load("indexer_worked_example.json")
+    q = np.array(g["q_idx"], dtype=np.float64)
+    k = np.array(g["k_idx"], dtype=np.float64)
+    w = np.array(g["w"], dtype=np.float64)
+    got = orc.index_scores(q, k, w, [0, 3])
+    for row, want in zip(got, g["scores"]):
+        assert row.tolist() == want
+
+
+def test_scores_single_head_unit_weight_is_relu_of_integer_matmul():
+    rng = np.random.default_rng(11)
+    t, d = 37, 16
+    q = rng.integers(-3, 4, size=(t, 1, d))
+    k = rng.integers(-3, 4, size=(t, d))
+    w = np.ones((t, 1))
+    full = np.maximum(q[:, 0, :].astype(np.int64) @ k.astype(np.int64).T, 0)  # textbook matmul on int64
+    got = orc.index_scores(q, k, w, [0, t])
+    for r in range(t):
+        assert np.array_equal(got[r], full[r, : r + 1].astype(np.float64))
+
+
+def test_scores_relu_sign_identity():
+    # ReLU(-x) - ReLU(x) = -x, so I(-q) - I(q) = -sum_j w_j <q_j, k_s>: catches a dropped or
+    # mis-signed ReLU and a wrong weight/head pairing.
+    rng = np.random.default_rng(12)
+    t, h, d = 23, 3, 8
+    q = rng.integers(-3, 4, size=(t, h, d)).astype(np.float64)
+    k = rng.integers(-3, 4, size=(t, d)).astype(np.float64)
+    w = rng.choice([0.125, 0.25, 0.5, 1.0, -0.5], size=(t, h))
+    pos = orc.index_scores(q, k, w, [0, t])
+    neg = orc.index_scores(-q, k, w, [0, t])
+    lin = np.einsum("tj,tjd,sd->ts", w, q, k)
+    for r in range(t):
+        assert np.array_equal(neg[r] - pos[r], -lin[r, : r + 1])
+
+
+def test_scores_weight_belongs_to_query_row():
+    rng = np.random.default_rng(13)
+    t, h, d = 17, 4, 8
+    q = rng.integers(-3, 4, size=(t, h, d)).astype(np.float64)
+    k = rng.integers(-3, 4, size=(t, d)).astype(np.float64)
+    w = rng.choice([0.125, 0.25, 0.5, 1.0], size=(t, h))
+    base = orc.index_scores(q, k, w, [0, t])
+    w2 = w.copy()
+    w2[9] *= 2.0
+    moved = orc.index_scores(q, k, w2, [0, t])
+    for r in range(t):
+        assert np.array_equal(moved[r], base[r] * (2.0 if r == 9 else 1.0))
+
+
+def test_scores_are_causal_and_sequence_local():
+    rng = np.random.default_rng(14)
+    lens = [5, 9, 3]
+    tot = sum(lens)
+    q = rng.integers(-3, 4, size=(tot, 2, 4)).astype(np.float64)
+    k = rng.integers(-3, 4, size=(tot, 4)).astype(np.float64)
+    w = np.ones((tot, 2))
+    got = orc.index_scores(q, k, w, [0, 5, 14, 17])
+    assert [len(r) for r in got] == [t + 1 for n in lens for t in range(n)]
+    # brute force with explicit loops for the second sequence
+    for t in range(9):
+        r = 5 + t
+        for s in range(t + 1):
+            want = 0.0
+            for j in range(2):
+                dot = sum(q[r, j, c] * k[5 + s, c] for c in range(4))
+                want += w[r, j] * max(0.0, dot)
+            assert got[r][s] == want
+
+
+def test_scores_exact_for_workload_value_ranges():
+    # Worst case of the large workloads: 64 heads * 128 dims * 9 per product, in 1/8 steps,
+    # stays below 2**24 units, so float32 represents every score exactly.
+    worst = 64 * 128 * 9
+    assert worst * 8 < 2 ** 24
+    pi = inp.prefill_inputs([300], 64, 128, 8, 2, 128, 64, seed=5)
+    q = inp.bf16_bits_to_f32(pi.q_idx).astype(np.float64)
+    k = inp.bf16_bits_to_f32(pi.k_idx).astype(np.float64)
+    rows = orc.index_scores(q, k, pi.w.astype(np.float64), pi.cu_seqlens)
+    for r in rows[::37]:
+        assert np.array_equal(r.astype(np.float32).astype(np.float64), r)
+        assert np.array_equal(r * 8, np.round(r * 8))
+
+
+# ---------------------------------------------------------------- top-k selection
+
+def _brute_topk(scores, k):
+    n = len(scores)
+    if n <= k:
+        return list(range(n)) + [-1] * (k - n)
+    ranked = sorted(range(n), key=lambda s: (-scores[s], s))
+    return sorted(ranked[:k])
+
+
+def test_topk_hand_worked_example():
+    g = _load("indexer_worked_example.json")
+    for kk, want_rows in g["topk"].items():
+        for sc, want in zip(g["scores"], want_rows):
+            assert orc.select_topk_row(np.array(sc), int(kk)).tolist() == want
+    for case in g["tie_rows"]:
+        assert orc.select_topk_row(np.array(case["scores"]), case["k"]).tolist() == case["idx"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_equals_bruteforce_sort_with_ties(seed):
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(60):
+        n = int(rng.integers(1, 70))
+        k = int(rng.integers(1, 40))
+        sc = rng.integers(-2, 4, size=n) / 8.0          # heavy ties
+        assert orc.select_topk_row(sc, k).tolist() == _brute_topk(sc.tolist(), k)
+
+
+def test_topk_special_rows():
+    n, k = 50, 8
+    assert orc.select_topk_row(np.zeros(n), k).tolist() == list(range(k))
+    assert orc.select_topk_row(np.arange(n, 0, -1.0), k).tolist() == list(range(k))
+    assert orc.select_topk_row(np.arange(n, dtype=np.float64), k).tolist() == list(range(n - k, n))
+    assert orc.select_topk_row(np.arange(5.0), k).tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
+    assert orc.select_topk_row(np.arange(8.0), 8).tolist() == list(range(8))
+
+
+def test_topk_matches_torch_topk_without_ties():
+    rng = np.random.default_rng(7)
+    for n, k in [(100, 10), (1000, 256), (4097, 2048)]:
+        sc = rng.permutation(n).astype(np.float64) * 0.5 - 17.0
+        ref = torch.topk(torch.from_numpy(sc), k).indices.sort().values.numpy()
+        assert np.array_equal(orc.select_topk_row(sc, k), ref)
+
+
+# ---------------------------------------------------------------- sparse attention
+
+def test_attention_hand_worked_example():
+    g = _load("attention_worked_example.json")
+    o, lse, ws = orc.sparse_gqa_attention_row(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]),
+                                              np.array(g["idx"]), g["scale"])
+    np.testing.assert_allclose(o, np.array(g["out"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(g["lse"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ws, 1.0, atol=1e-12)
+
+
+def _sdpa_masked(q, k, v, mask, scale):
+    """torch SDPA in float64 on the CPU; q [T,Hq,D], k/v [S,Hkv,D], mask [T,S] bool (True = keep)."""
+    hq, hkv = q.shape[1], k.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0)
+    kt = torch.from_numpy(k).repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+    vt = torch.from_numpy(v).repeat_interleave(hq // hkv, dim=1).permute(1, 0, 2).unsqueeze(0).contiguous()
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask),
+                                                           scale=scale)
+    return out[0].permute(1, 0, 2).numpy()
+
+
+def _rand_attn(seed, t, hq, hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((t, hq, d)), rng.standard_normal((t, hkv, d)), rng.standard_normal((t, hkv, d)))
+
+
+def test_attention_with_k_at_least_length_is_dense_causal_gqa():
+    t, hq, hkv, d, h_i, d_i = 40, 8, 2, 16, 2, 8
+    q, k, v = _rand_attn(21, t, hq, hkv, d)
+    rng = np.random.default_rng(22)
+    qi = rng.integers(-3, 4, size=(t, h_i, d_i)).astype(np.float64)
+    ki = rng.integers(-3, 4, size=(t, d_i)).astype(np.float64)
+    w = np.ones((t, h_i))
+    scale = 1 / math.sqrt(d)
+    res = orc.prefill(q, k, v, qi, ki, w, [0, t], top_k=t, softmax_scale=scale)
+    ref = _sdpa_masked(q, k, v, np.tril(np.ones((t, t), dtype=bool)), scale)
+    np.testing.assert_allclose(res["out"], ref, atol=1e-12)
+
+
+def test_attention_equals_sdpa_with_index_mask():
+    t, hq, hkv, d = 60, 4, 2, 8
+    q, k, v = _rand_attn(31, t, hq, hkv, d)
+    rng = np.random.default_rng(32)
+    scale = 0.3
+    mask = np.zeros((t, t), dtype=bool)
+    for r in range(t):
+        n = int(rng.integers(1, r + 2))
+        sel = np.sort(rng.choice(r + 1, size=n, replace=False))
+        mask[r, sel] = True
+        idx = np.full(t, -1)
+        idx[:n] = sel
+        o, lse, ws = orc.sparse_gqa_attention_row(q[r], k, v, idx, scale)
+        ref = _sdpa_masked(q[r:r + 1], k, v, mask[r:r + 1], scale)[0]
+        np.testing.assert_allclose(o, ref, atol=1e-12)
+        np.testing.assert_allclose(ws, 1.0, atol=1e-12)
+        for h in range(hq):
+            z = scale * (k[sel, h // (hq // hkv)] @ q[r, h])
+            assert abs(lse[h] - logsumexp(z)) < 1e-12
+
+
+def test_attention_unit_values_and_single_position():
+    t, hq, hkv, d = 12, 6, 3, 8
+    q, k, v = _rand_attn(41, t, hq, hkv, d)
+    ones = np.ones_like(v)
+    idx = np.array([0, 3, 7, 11, -1, -1])
+    o, _, _ = orc.sparse_gqa_attention_row(q[11], k, ones, idx, 0.5)
+    np.testing.assert_allclose(o, 1.0, atol=1e-14)
+    o1, lse1, _ = orc.sparse_gqa_attention_row(q[0], k, v, np.array([0, -1]), 0.5)
+    for h in range(hq):
+        assert np.array_equal(o1[h], v[0, h // 2])
+        assert abs(lse1[h] - 0.5 * (k[0, h // 2] @ q[0, h])) < 1e-14
+
+
+def test_attention_index_order_is_irrelevant():
+    t, hq, hkv, d = 30, 4, 1, 8
+    q, k, v = _rand_attn(51, t, hq, hkv, d)
+    idx = np.array([2, 5, 11, 29, 17, -1])
+    a = orc.sparse_gqa_attention_row(q[29], k, v, idx, 0.4)
+    b = orc.sparse_gqa_attention_row(q[29], k, v, idx[[4, 0, 5, 3, 1, 2]], 0.4)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- composition
+
+def test_packed_prefill_equals_separate_sequences():
+    lens = [20, 7, 13]
+    pi = inp.prefill_inputs(lens, 2, 8, 4, 2, 16, 6, seed=9)
+    f = inp.bf16_bits_to_f32
+    arrs = [f(pi.q), f(pi.k), f(pi.v), f(pi.q_idx), f(pi.k_idx), pi.w]
+    packed = orc.prefill(*arrs, pi.cu_seqlens, top_k=6)
+    o = 0
+    for n in lens:
+        part = orc.prefill(*[a[o:o + n] for a in arrs], [0, n], top_k=6)
+        assert np.array_equal(packed["idx"][o:o + n], part["idx"])
+        np.testing.assert_allclose(packed["out"][o:o + n], part["out"], atol=1e-13)
+        o += n
+
+
+def test_decode_equals_last_prefill_row():
+    s, hq, hkv, d, h_i, d_i, kk = 50, 4, 2, 8, 2, 8, 10
+    pi = inp.prefill_inputs([s], h_i, d_i, hq, hkv, d, kk, seed=10)
+    f = inp.bf16_bits_to_f32
+    q, k, v, qi, ki = f(pi.q), f(pi.k), f(pi.v), f(pi.q_idx), f(pi.k_idx)
+    pre = orc.prefill(q, k, v, qi, ki, pi.w, pi.cu_seqlens, top_k=kk, rows=[s - 1])
+    dec = orc.decode(q[s - 1:s], qi[s - 1:s], pi.w[s - 1:s], k[None], v[None], ki[None],
+                     np.array([s]), top_k=kk)
+    assert np.array_equal(pre["idx"][0], dec["idx"][0])
+    np.testing.assert_allclose(pre["out"][0], dec["out"][0], atol=1e-13)
+
+
+# ---------------------------------------------------------------- synthetic inputs
+
+def test_inputs_are_deterministic_and_in_range():
+    a = inp.prefill_inputs([64, 32], 4, 64, 8, 2, 128, 16, seed=3, structure="blocks16")
+    b = inp.prefill_inputs([64, 32], 4, 64, 8, 2, 128, 16, seed=3, structure="blocks16")
+    for x, y in [(a.q, b.q), (a.k_idx, b.k_idx), (a.w, b.w), (a.k, b.k)]:
+        assert np.array_equal(x, y)
+    vals = inp.bf16_bits_to_f32(a.q_idx)
+    assert set(np.unique(vals).tolist()) <= set(range(-3, 4))
+    assert set(np.unique(inp.bf16_bits_to_f32(a.k_idx)).tolist()) <= set(range(-3, 4))
+    assert set(np.unique(a.w).tolist()) <= {1.0, 0.5, 0.25, 0.125}
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(100000) * 10 ** rng.uniform(-3, 3, 100000)).astype(np.float32)
+    ours = inp.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(inp.bf16_bits_to_f32(ours), torch.from_numpy(x).to(torch.bfloat16).float().numpy())
