@@ -1,0 +1,181 @@
+/*
+ * dsa.h - C ABI of the DSA (DeepSeek Sparse Attention, GQA form) hot path for AMD MI355X.
+ *
+ * The path, as the Keye-VL-2.0 report digest (mqxn.cn news 1966, section 一) describes it:
+ * a light "Lightning Indexer" with an MQA-shared key scores every earlier position of each
+ * query token, the 2048 best positions of the context are kept per token, and attention
+ * runs only over those positions.  The same section (and the aihot summary of the report's
+ * abstract) says the method was adapted to a GQA decoder: here every query head of every KV
+ * group of a token uses the token's one index set.  The report runs it over packed
+ * variable-length sequences (QbitAI re-post on news.chathome.org, training-infrastructure
+ * paragraph) and needs a deterministic top-k (digest, section 八).
+ *
+ * The pages print no formula.  This library computes, for packed row r of sequence b
+ * (offset o = cu_seqlens[b], local position t = r - o):
+ *
+ *   score   I[r, s] = sum_j w[r, j] * max(0, <q_idx[r, j, :], k_idx[o + s, :]>),  0 <= s <= t
+ *   select  the k positions with the largest I (ties -> lower s), all of [0, t] if t+1 <= k,
+ *           returned in ascending order and padded with -1
+ *   attend  z_s = scale * <q[r, h, :], k[o + s, h / G, :]>,  O[r, h] = sum_s softmax(z)_s v[o + s, h / G]
+ *           lse[r, h] = log(sum_s exp(z_s))   (natural log, includes the scale)
+ *
+ * Conventions shared by every call:
+ *   - All pointers are device pointers unless the name ends in _host.  Tensors are dense,
+ *     row-major, in the order of their shape.  bf16 tensors are passed as `const void*`
+ *     (16-bit storage, round-to-nearest-even bf16).  `stream` is a hipStream_t (NULL = the
+ *     default stream).
+ *   - The caller owns every buffer, including the workspace and the KV cache.  The library
+ *     allocates nothing, keeps no pointer after a call returns, and never synchronises: work
+ *     is enqueued on `stream` and results are valid once the stream has passed the call.
+ *     Inputs must stay unchanged until then.  Calls on different streams are independent.
+ *   - Arguments are validated on the host before anything is enqueued; on any error nothing
+ *     runs.  Errors: DSA_ERR_INVALID_ARG (null pointer, negative size, inconsistent
+ *     cu_seqlens, misaligned pointer), DSA_ERR_UNSUPPORTED (a shape this build has no kernel
+ *     for), DSA_ERR_WORKSPACE (workspace too small), DSA_ERR_HIP (a launch failed; the HIP
+ *     error text is in dsa_last_error()).  Faults inside kernels are only visible at the next
+ *     synchronisation of the stream.
+ *   - Supported shapes: head_dim = 128; Hq % Hkv == 0 with 1 <= Hq / Hkv <= 16;
+ *     (h_idx, d_idx) in {(4, 64), (16, 128), (32, 128), (64, 128)}; 1 <= top_k <= 2048.
+ *     Every bf16/float pointer must be 16-byte aligned.
+ *   - Positions are sequence-local.  Selected positions that lie outside the causal prefix
+ *     [0, t] (or outside [0, seq_len) in decode) are ignored by the attention calls.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+#define DSA_MAX_TOP_K 2048
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE = 3,
+  DSA_ERR_HIP = 4
+};
+
+/* Version of this ABI (DSA_ABI_VERSION). */
+int dsa_abi_version(void);
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+
+/* Message of the last failing call made by this host thread ("" if none). */
+const char* dsa_last_error(void);
+
+/*
+ * Lightning-indexer scores (digest section 一: light scout, MQA-shared key).
+ *
+ * q_idx   [total_tokens, h_idx, d_idx] bf16    indexer queries of every packed row
+ * k_idx   [total_tokens, d_idx]        bf16    one indexer key per packed position
+ * w       [total_tokens, h_idx]        float   per-row, per-head weights
+ * cu_seqlens_host [batch + 1] int32 (host)     packed offsets, cu[0] = 0, cu[batch] = total_tokens
+ * row_begin, row_count                         packed rows [row_begin, row_begin + row_count) to score
+ * scores  [row_count, ld]              float   output: scores[i * ld + s] = I[row_begin + i, s] for
+ *                                              0 <= s <= t (the row's local position); entries with
+ *                                              s > t are left untouched.  ld >= t + 1 for every row,
+ *                                              ld % 4 == 0.
+ */
+int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w,
+                     const int32_t* cu_seqlens_host, int batch, int total_tokens,
+                     int h_idx, int d_idx, int row_begin, int row_count,
+                     float* scores, int64_t ld, void* stream);
+
+/* Bytes of workspace dsa_topk needs (currently 0; kept so callers can size it once). */
+int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes);
+
+/*
+ * Deterministic per-row top-k (digest section 一: k best positions per query; section 八:
+ * identical sets in training and inference).
+ *
+ * scores  [rows, ld] float     row i holds row_len[i] valid scores in scores[i * ld + 0 .. row_len-1];
+ *                              ld % 4 == 0.  Scores must not be NaN; -0.0 equals +0.0.
+ * row_len [rows] int32         valid length of each row (>= 0, <= ld)
+ * k                            1 <= k <= DSA_MAX_TOP_K
+ * idx_out [rows, k] int32      output: the selected positions in ascending order; if row_len <= k
+ *                              the row is 0 .. row_len-1; padding is -1.  Among equal scores the
+ *                              lower position wins, so the set is unique.
+ * values_out [rows, k] float   optional (NULL): the scores of idx_out, same order; padding -inf.
+ * workspace, workspace_bytes   at least dsa_topk_workspace_size bytes (may be NULL when 0).
+ */
+int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k,
+             int32_t* idx_out, float* values_out, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/*
+ * Sparse GQA attention over selected positions (digest section 一 and the GQA adaptation).
+ *
+ * q   [total_tokens, hq, head_dim]  bf16
+ * k,v [total_tokens, hkv, head_dim] bf16
+ * idx [total_tokens, k_sel] int32   sequence-local positions per row; entries < 0 or > t are ignored
+ * cu_seqlens [batch + 1] int32      device copy of the packed offsets
+ * out [total_tokens, hq, head_dim]  bf16 output.  A row with no valid position gets O = 0.
+ * lse [total_tokens, hq] float      optional (NULL) output; -inf for a row with no valid position.
+ */
+int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
+                        const int32_t* idx, int k_sel,
+                        const int32_t* cu_seqlens, int batch, int total_tokens,
+                        int hq, int hkv, int head_dim, float softmax_scale,
+                        void* out, float* lse, void* stream);
+
+/*
+ * Workspace bytes for dsa_prefill: a score buffer for a chunk of query rows (never the whole
+ * L x L matrix) plus small per-row tables.  A larger workspace lets the call use larger chunks.
+ */
+int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv,
+                               int head_dim, int h_idx, int d_idx, int top_k, size_t* bytes);
+
+/*
+ * Fused prefill: indexer -> top-k -> sparse GQA attention for every packed row.
+ *
+ * q, k, v, q_idx, k_idx, w      as above, over all total_tokens packed rows
+ * cu_seqlens [batch + 1]        device copy of the packed offsets
+ * cu_seqlens_host [batch + 1]   host copy of the same offsets (used to schedule chunks)
+ * max_seqlen                    >= the longest sequence
+ * out [total_tokens, hq, head_dim] bf16, lse [total_tokens, hq] float or NULL
+ * idx_out [total_tokens, top_k] int32   the selected positions (required)
+ * workspace                     >= dsa_prefill_workspace_size(...) for the smallest chunk the call
+ *                               accepts (64 rows x max_seqlen floats); size it with that function.
+ */
+int dsa_prefill(const void* q, const void* k, const void* v,
+                const void* q_idx, const void* k_idx, const float* w,
+                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host,
+                int batch, int total_tokens, int max_seqlen,
+                int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
+                float softmax_scale, void* out, float* lse, int32_t* idx_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for dsa_decode (per-sequence score rows plus split partials). */
+int dsa_decode_workspace_size(int batch, int s_max, int hq, int hkv, int head_dim,
+                              int h_idx, int d_idx, int top_k, size_t* bytes);
+
+/*
+ * Fused decode step over a contiguous KV cache (digest section 八: DSA-specific decode).
+ *
+ * q [batch, hq, head_dim] bf16, q_idx [batch, h_idx, d_idx] bf16, w [batch, h_idx] float:
+ *     the new token of each sequence
+ * k_cache, v_cache [batch, s_max, hkv, head_dim] bf16, k_idx_cache [batch, s_max, d_idx] bf16
+ * seq_lens [batch] int32 (device): valid cache length of each sequence, which already includes
+ *     the new token at position seq_lens[b] - 1; 1 <= seq_lens[b] <= s_max
+ * max_seq_len (host): an upper bound of seq_lens (used to size the launch)
+ * out [batch, hq, head_dim] bf16, lse [batch, hq] float or NULL, idx_out [batch, top_k] int32
+ */
+int dsa_decode(const void* q, const void* q_idx, const float* w,
+               const void* k_cache, const void* v_cache, const void* k_idx_cache,
+               const int32_t* seq_lens, int batch, int s_max, int max_seq_len,
+               int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
+               float softmax_scale, void* out, float* lse, int32_t* idx_out,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

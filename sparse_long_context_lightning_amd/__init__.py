@@ -1,0 +1,33 @@
+"""DSA (lightning indexer -> top-k -> sparse GQA attention) for AMD MI355X.
+
+The compute runs in libdsa.so (hand-written HIP for gfx950) behind the C ABI declared in
+include/dsa.h; this package only binds it.  Build the library with
+`python -m sparse_long_context_lightning_amd.build`.
+"""
+
+from ._lib import (  # noqa: F401
+    DSA_ERR_HIP,
+    DSA_ERR_INVALID_ARG,
+    DSA_ERR_UNSUPPORTED,
+    DSA_ERR_WORKSPACE,
+    DSA_MAX_TOP_K,
+    DSA_OK,
+    EXPORTED,
+    LIB_PATH,
+    DsaError,
+    decode,
+    dsa_abi_version,
+    dsa_decode,
+    dsa_decode_workspace_size,
+    dsa_index_scores,
+    dsa_last_error,
+    dsa_prefill,
+    dsa_prefill_workspace_size,
+    dsa_sparse_gqa_attn,
+    dsa_status_string,
+    dsa_topk,
+    dsa_topk_workspace_size,
+    load,
+    prefill,
+    to_device_bf16,
+)

@@ -1,0 +1,237 @@
+"""ctypes binding of libdsa.so (the C ABI in include/dsa.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.  Tensors are torch
+device tensors; the call is enqueued on torch's current stream.  There is no fallback: if
+the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+DSA_OK = 0
+DSA_ERR_INVALID_ARG = 1
+DSA_ERR_UNSUPPORTED = 2
+DSA_ERR_WORKSPACE = 3
+DSA_ERR_HIP = 4
+DSA_MAX_TOP_K = 2048
+
+EXPORTED = (
+    "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
+    "dsa_topk", "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill", "dsa_decode_workspace_size",
+    "dsa_decode",
+)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+def load():
+    """Load libdsa.so (built in-tree by build.py); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sparse_long_context_lightning_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "dsa_abi_version": ([], _I),
+        "dsa_status_string": ([_I], ctypes.c_char_p),
+        "dsa_last_error": ([], ctypes.c_char_p),
+        "dsa_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
+        "dsa_topk_workspace_size": ([_I, _I64, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_topk": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
+        "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+        "dsa_prefill_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P,
+                         _SZ, _P], _I),
+        "dsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
+                        _P], _I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _status_name(status: int) -> str:
+    return {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+            4: "DSA_ERR_HIP"}.get(status, f"status {status}")
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DsaError(status, load().dsa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _host_i32(x):
+    arr = np.ascontiguousarray(np.asarray(x if not hasattr(x, "cpu") else x.cpu().numpy(), dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------------------- raw entry points
+
+def dsa_abi_version() -> int:
+    return load().dsa_abi_version()
+
+
+def dsa_status_string(status: int) -> str:
+    return load().dsa_status_string(status).decode()
+
+
+def dsa_last_error() -> str:
+    return load().dsa_last_error().decode()
+
+
+def dsa_index_scores(q_idx, k_idx, w, cu_seqlens_host, row_begin, row_count, scores, ld=None, stream=None):
+    """Indexer scores of packed rows [row_begin, row_begin + row_count) into scores[row_count, ld]."""
+    cu, cu_p = _host_i32(cu_seqlens_host)
+    total, h_idx, d_idx = q_idx.shape
+    ld = scores.shape[1] if ld is None else ld
+    _check(load().dsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), cu_p, len(cu) - 1, total, h_idx, d_idx,
+                                   row_begin, row_count, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_topk_workspace_size(rows, ld, k) -> int:
+    n = _SZ(0)
+    _check(load().dsa_topk_workspace_size(rows, ld, k, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_topk(scores, row_len, k, idx_out, values_out=None, workspace=None, ld=None, stream=None):
+    """Per-row top-k of scores[rows, ld] with valid lengths row_len[rows] (int32, device)."""
+    rows = scores.shape[0]
+    ld = scores.shape[1] if ld is None else ld
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_topk(_ptr(scores), ld, rows, _ptr(row_len), k, _ptr(idx_out), _ptr(values_out),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_sparse_gqa_attn(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=None, stream=None):
+    """Sparse GQA attention of every packed row over idx[row, :] (device cu_seqlens)."""
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    _check(load().dsa_sparse_gqa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), idx.shape[1], _ptr(cu_seqlens),
+                                      cu_seqlens.shape[0] - 1, total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
+                                      _stream(stream)))
+
+
+def dsa_prefill_workspace_size(batch, total_tokens, max_seqlen, hq, hkv, head_dim, h_idx, d_idx, top_k) -> int:
+    n = _SZ(0)
+    _check(load().dsa_prefill_workspace_size(batch, total_tokens, max_seqlen, hq, hkv, head_dim, h_idx, d_idx,
+                                             top_k, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_prefill(q, k, v, q_idx, k_idx, w, cu_seqlens, cu_seqlens_host, max_seqlen, top_k, out, lse, idx_out,
+                workspace, softmax_scale=None, stream=None):
+    cu, cu_p = _host_i32(cu_seqlens_host)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    h_idx, d_idx = q_idx.shape[1], q_idx.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(cu_seqlens), cu_p,
+                              len(cu) - 1, total, max_seqlen, hq, hkv, d, h_idx, d_idx, top_k, scale, _ptr(out),
+                              _ptr(lse), _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_decode_workspace_size(batch, s_max, hq, hkv, head_dim, h_idx, d_idx, top_k) -> int:
+    n = _SZ(0)
+    _check(load().dsa_decode_workspace_size(batch, s_max, hq, hkv, head_dim, h_idx, d_idx, top_k, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_decode(q, q_idx, w, k_cache, v_cache, k_idx_cache, seq_lens, max_seq_len, top_k, out, lse, idx_out,
+               workspace, softmax_scale=None, stream=None):
+    batch, hq, d = q.shape
+    s_max, hkv = k_cache.shape[1], k_cache.shape[2]
+    h_idx, d_idx = q_idx.shape[1], q_idx.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().dsa_decode(_ptr(q), _ptr(q_idx), _ptr(w), _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache),
+                             _ptr(seq_lens), batch, s_max, max_seq_len, hq, hkv, d, h_idx, d_idx, top_k, scale,
+                             _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+# ----------------------------------------------------------------------------- allocating helpers
+
+def prefill(q, k, v, q_idx, k_idx, w, cu_seqlens_host, top_k, softmax_scale=None, workspace=None, stream=None):
+    """Allocate outputs and run dsa_prefill.  Returns (out, lse, idx)."""
+    import torch
+    dev = q.device
+    cu = np.asarray(cu_seqlens_host, dtype=np.int32)
+    total, hq, d = q.shape
+    max_seqlen = int(np.max(np.diff(cu))) if len(cu) > 1 else 0
+    cu_dev = torch.from_numpy(cu).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(total, hq, dtype=torch.float32, device=dev)
+    idx = torch.empty(total, top_k, dtype=torch.int32, device=dev)
+    if workspace is None:
+        nbytes = dsa_prefill_workspace_size(len(cu) - 1, total, max_seqlen, hq, k.shape[1], d, q_idx.shape[1],
+                                            q_idx.shape[2], top_k)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    dsa_prefill(q, k, v, q_idx, k_idx, w, cu_dev, cu, max_seqlen, top_k, out, lse, idx, workspace, softmax_scale,
+                stream)
+    return out, lse, idx
+
+
+def decode(q, q_idx, w, k_cache, v_cache, k_idx_cache, seq_lens, top_k, max_seq_len=None, softmax_scale=None,
+           workspace=None, stream=None):
+    """Allocate outputs and run dsa_decode.  Returns (out, lse, idx)."""
+    import torch
+    dev = q.device
+    batch, hq, d = q.shape
+    s_max = k_cache.shape[1]
+    if max_seq_len is None:
+        max_seq_len = s_max
+    out = torch.empty_like(q)
+    lse = torch.empty(batch, hq, dtype=torch.float32, device=dev)
+    idx = torch.empty(batch, top_k, dtype=torch.int32, device=dev)
+    if workspace is None:
+        nbytes = dsa_decode_workspace_size(batch, s_max, hq, k_cache.shape[2], d, q_idx.shape[1], q_idx.shape[2],
+                                           top_k)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    dsa_decode(q, q_idx, w, k_cache, v_cache, k_idx_cache, seq_lens, max_seq_len, top_k, out, lse, idx, workspace,
+               softmax_scale, stream)
+    return out, lse, idx
+
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """Upload bf16 bit patterns (uint16 numpy) as a torch.bfloat16 device tensor."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)

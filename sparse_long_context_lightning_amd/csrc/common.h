@@ -1,0 +1,62 @@
+// Shared device helpers for the gfx950 kernels of the DSA path (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+constexpr int kMaxTopK = 2048;
+
+// 16x16x32 bf16 MFMA (CDNA4).  Lane l supplies A[l % 16][8 * (l / 16) + e] and
+// B[8 * (l / 16) + e][l % 16] for e = 0..7 and receives C[4 * (l / 16) + i][l % 16], i = 0..3.
+// Only the pairing "element e of A in lane l meets element e of B in lane l" matters for
+// the contraction, so callers are free to permute which reduction index a slot carries, as
+// long as both operands use the same permutation.
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed into one dword (lo = a, hi = b).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  ua = (ua + 0x7FFFu + ((ua >> 16) & 1u)) >> 16;
+  ub = (ub + 0x7FFFu + ((ub >> 16) & 1u)) >> 16;
+  return ua | (ub << 16);
+}
+
+// fp32 rounded to the nearest bf16 value (ties to even), returned as fp32.
+__device__ __forceinline__ float round_bf16(float a) {
+  uint32_t u = __float_as_uint(a);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Order-preserving map float -> uint32 (larger float -> larger key).  -0.0 is folded into
+// +0.0 first so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = (u == 0x80000000u) ? 0u : u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Wait for this wave's outstanding LDS operations and keep the compiler from moving memory
+// accesses across the point: used where lanes of one wave exchange data through LDS.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+}  // namespace dsa

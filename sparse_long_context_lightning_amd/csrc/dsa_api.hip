@@ -1,0 +1,440 @@
+// C ABI of the DSA hot path: host-side validation, workspace carving and launch order.
+// The contract of every entry point is documented in include/dsa.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/dsa.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
+
+// Supported indexer shapes (one kernel instantiation each).
+bool indexer_shape_ok(int h_idx, int d_idx) {
+  return (d_idx == 128 && (h_idx == 16 || h_idx == 32 || h_idx == 64)) || (h_idx == 4 && d_idx == 64);
+}
+
+int check_attn_shape(int hq, int hkv, int head_dim) {
+  if (hq <= 0 || hkv <= 0 || head_dim <= 0) return fail(DSA_ERR_INVALID_ARG, "head counts and head_dim must be positive");
+  if (hq % hkv != 0) return fail(DSA_ERR_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (head_dim != 128) return fail(DSA_ERR_UNSUPPORTED, "head_dim %d is not supported (only 128)", head_dim);
+  if (hq / hkv > 16) return fail(DSA_ERR_UNSUPPORTED, "group size hq/hkv = %d exceeds 16", hq / hkv);
+  return DSA_OK;
+}
+
+int check_topk(int k) {
+  if (k < 1 || k > DSA_MAX_TOP_K) return fail(DSA_ERR_UNSUPPORTED, "top_k %d outside [1, %d]", k, DSA_MAX_TOP_K);
+  return DSA_OK;
+}
+
+int check_indexer_shape(int h_idx, int d_idx) {
+  if (h_idx <= 0 || d_idx <= 0) return fail(DSA_ERR_INVALID_ARG, "h_idx and d_idx must be positive");
+  if (!indexer_shape_ok(h_idx, d_idx))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer shape (h_idx=%d, d_idx=%d) is not supported", h_idx, d_idx);
+  return DSA_OK;
+}
+
+// Validates host cu_seqlens and returns the longest sequence in *max_len.
+int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) {
+  if (!cu) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_host is null");
+  if (batch <= 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive");
+  if (cu[0] != 0) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_host[0] must be 0");
+  int ml = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] < cu[b]) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_host must be non-decreasing");
+    ml = std::max(ml, cu[b + 1] - cu[b]);
+  }
+  if (cu[batch] != total_tokens)
+    return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_host[batch] = %d != total_tokens = %d", cu[batch], total_tokens);
+  *max_len = ml;
+  return DSA_OK;
+}
+
+#define DSA_TRY(expr)              \
+  do {                             \
+    const int st_ = (expr);        \
+    if (st_ != DSA_OK) return st_; \
+  } while (0)
+
+#define DSA_NONNULL(p) \
+  if (!(p)) return fail(DSA_ERR_INVALID_ARG, "%s is null", #p)
+
+#define DSA_ALIGNED(p) \
+  if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
+
+constexpr int kKeySplit = 2048;        // keys per prefill-indexer workgroup
+constexpr int kDecodeKeysPerWave = 512;
+constexpr int kMinChunkRows = 64;
+constexpr int kDefaultChunkRows = 2048;
+
+int decode_nsplit(int batch, int hkv, int top_k) {
+  const int nchunk = (top_k + 31) / 32;
+  const int want = (2048 + batch * hkv - 1) / (batch * hkv);
+  return std::max(1, std::min(want, nchunk));
+}
+
+int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu, int batch,
+                      int h_idx, int d_idx, int row_begin, int row_end, int out_row0, float* scores, long long ld,
+                      hipStream_t stream) {
+  for (int b = 0; b < batch; ++b) {
+    const int r0 = std::max(row_begin, cu[b]);
+    const int r1 = std::min(row_end, cu[b + 1]);
+    if (r0 >= r1) continue;
+    dsa::IndexerPrefillArgs a;
+    a.q_idx = static_cast<const uint16_t*>(q_idx);
+    a.k_idx = static_cast<const uint16_t*>(k_idx);
+    a.w = w;
+    a.h_idx = h_idx;
+    a.d_idx = d_idx;
+    a.seq_off = cu[b];
+    a.row_begin = r0;
+    a.row_end = r1;
+    a.out_row0 = out_row0;
+    a.scores = scores;
+    a.ld = ld;
+    a.key_split = kKeySplit;
+    DSA_TRY(hip_status(dsa::launch_indexer_prefill(a, stream), "indexer launch"));
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+    default: return "DSA_ERR_UNKNOWN";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu_seqlens_host, int batch,
+                     int total_tokens, int h_idx, int d_idx, int row_begin, int row_count, float* scores, int64_t ld,
+                     void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q_idx);
+  DSA_NONNULL(k_idx);
+  DSA_NONNULL(w);
+  DSA_NONNULL(scores);
+  DSA_ALIGNED(q_idx);
+  DSA_ALIGNED(k_idx);
+  DSA_ALIGNED(w);
+  DSA_ALIGNED(scores);
+  if (total_tokens < 0 || row_begin < 0 || row_count < 0 || row_begin + (long long)row_count > total_tokens)
+    return fail(DSA_ERR_INVALID_ARG, "row range [%d, %d + %d) outside [0, %d)", row_begin, row_begin, row_count,
+                total_tokens);
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  int max_len = 0;
+  DSA_TRY(check_cu_host(cu_seqlens_host, batch, total_tokens, &max_len));
+  if (ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "ld (%lld) must be a multiple of 4", (long long)ld);
+  for (int b = 0; b < batch; ++b) {
+    const int r1 = std::min(row_begin + row_count, cu_seqlens_host[b + 1]);
+    if (r1 > std::max(row_begin, cu_seqlens_host[b]) && r1 - cu_seqlens_host[b] > ld)
+      return fail(DSA_ERR_INVALID_ARG, "ld (%lld) shorter than a row's prefix (%d)", (long long)ld,
+                  r1 - cu_seqlens_host[b]);
+  }
+  if (row_count == 0) return DSA_OK;
+  return launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, row_begin, row_begin + row_count,
+                           row_begin, scores, ld, static_cast<hipStream_t>(stream));
+}
+
+int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (rows < 0 || ld < 0) return fail(DSA_ERR_INVALID_ARG, "rows and ld must be non-negative");
+  DSA_TRY(check_topk(k));
+  *bytes = 0;
+  return DSA_OK;
+}
+
+int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
+             float* values_out, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_last_error[0] = 0;
+  DSA_NONNULL(scores);
+  DSA_NONNULL(row_len);
+  DSA_NONNULL(idx_out);
+  DSA_ALIGNED(scores);
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "rows must be non-negative");
+  if (ld <= 0 || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "ld (%lld) must be a positive multiple of 4", (long long)ld);
+  DSA_TRY(check_topk(k));
+  if (rows == 0) return DSA_OK;
+  dsa::TopkArgs a;
+  a.scores = scores;
+  a.ld = ld;
+  a.rows = rows;
+  a.row_len = row_len;
+  a.len_base = 0;
+  a.k = k;
+  a.idx_out = idx_out;
+  a.values_out = values_out;
+  return hip_status(dsa::launch_topk(a, static_cast<hipStream_t>(stream)), "top-k launch");
+}
+
+int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32_t* idx, int k_sel,
+                        const int32_t* cu_seqlens, int batch, int total_tokens, int hq, int hkv, int head_dim,
+                        float softmax_scale, void* out, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(idx);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(out);
+  if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
+  if (k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  if (total_tokens == 0) return DSA_OK;
+  dsa::SparseAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.seq_lens = nullptr;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.nsplit = 1;
+  return hip_status(dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
+}
+
+int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv, int head_dim, int h_idx,
+                               int d_idx, int top_k, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (batch <= 0 || total_tokens < 0 || max_seqlen < 0)
+    return fail(DSA_ERR_INVALID_ARG, "batch must be positive, sizes non-negative");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  DSA_TRY(check_topk(top_k));
+  const long long ld = round_up(std::max(max_seqlen, 1), 4);
+  const long long rows = std::max(1, std::min(total_tokens, kDefaultChunkRows));
+  *bytes = (size_t)(rows * ld * 4);
+  return DSA_OK;
+}
+
+int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, const void* k_idx, const float* w,
+                const int32_t* cu_seqlens, const int32_t* cu_seqlens_host, int batch, int total_tokens,
+                int max_seqlen, int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale,
+                void* out, float* lse, int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(q_idx);
+  DSA_NONNULL(k_idx);
+  DSA_NONNULL(w);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(out);
+  DSA_NONNULL(idx_out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(q_idx);
+  DSA_ALIGNED(k_idx);
+  DSA_ALIGNED(w);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(workspace);
+  if (total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens must be non-negative");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  DSA_TRY(check_topk(top_k));
+  int max_len = 0;
+  DSA_TRY(check_cu_host(cu_seqlens_host, batch, total_tokens, &max_len));
+  if (max_seqlen < max_len)
+    return fail(DSA_ERR_INVALID_ARG, "max_seqlen (%d) is below the longest sequence (%d)", max_seqlen, max_len);
+  if (total_tokens == 0) return DSA_OK;
+  const long long ld = round_up(std::max(max_seqlen, 1), 4);
+  const long long min_rows = std::min(total_tokens, kMinChunkRows);
+  if (!workspace || (long long)(workspace_bytes / 4 / ld) < min_rows)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes holds fewer than %lld score rows of %lld", workspace_bytes,
+                min_rows, ld);
+  long long chunk = (long long)(workspace_bytes / 4 / ld);
+  chunk = std::min<long long>(chunk, total_tokens);
+  if (chunk > 64) chunk = chunk / 64 * 64;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* scores = static_cast<float*>(workspace);
+
+  for (int b = 0; b < batch; ++b) {
+    const int o = cu_seqlens_host[b], e = cu_seqlens_host[b + 1];
+    for (int c0 = o; c0 < e; c0 += (int)chunk) {
+      const int c1 = (int)std::min<long long>(e, c0 + chunk);
+      DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s));
+      dsa::TopkArgs t;
+      t.scores = scores;
+      t.ld = ld;
+      t.rows = c1 - c0;
+      t.row_len = nullptr;
+      t.len_base = c0 - o;
+      t.k = top_k;
+      t.idx_out = idx_out + (size_t)c0 * top_k;
+      t.values_out = nullptr;
+      DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+    }
+  }
+  dsa::SparseAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx_out;
+  a.k_sel = top_k;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.seq_lens = nullptr;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.nsplit = 1;
+  return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
+}
+
+int dsa_decode_workspace_size(int batch, int s_max, int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
+                              size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (batch <= 0 || s_max <= 0) return fail(DSA_ERR_INVALID_ARG, "batch and s_max must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  DSA_TRY(check_topk(top_k));
+  const long long ld = round_up(s_max, 4);
+  const long long nsplit = decode_nsplit(batch, hkv, top_k);
+  const long long score_bytes = (long long)batch * ld * 4;
+  const long long part_bytes = (long long)batch * hq * nsplit * (128 + 2) * 4;
+  *bytes = (size_t)(round_up(score_bytes, 256) + part_bytes);
+  return DSA_OK;
+}
+
+int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_cache, const void* v_cache,
+               const void* k_idx_cache, const int32_t* seq_lens, int batch, int s_max, int max_seq_len, int hq,
+               int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale, void* out, float* lse,
+               int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(q_idx);
+  DSA_NONNULL(w);
+  DSA_NONNULL(k_cache);
+  DSA_NONNULL(v_cache);
+  DSA_NONNULL(k_idx_cache);
+  DSA_NONNULL(seq_lens);
+  DSA_NONNULL(out);
+  DSA_NONNULL(idx_out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(q_idx);
+  DSA_ALIGNED(w);
+  DSA_ALIGNED(k_cache);
+  DSA_ALIGNED(v_cache);
+  DSA_ALIGNED(k_idx_cache);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(workspace);
+  if (batch <= 0 || s_max <= 0) return fail(DSA_ERR_INVALID_ARG, "batch and s_max must be positive");
+  if (max_seq_len <= 0 || max_seq_len > s_max)
+    return fail(DSA_ERR_INVALID_ARG, "max_seq_len (%d) must be in [1, s_max = %d]", max_seq_len, s_max);
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  DSA_TRY(check_topk(top_k));
+  size_t need = 0;
+  DSA_TRY(dsa_decode_workspace_size(batch, s_max, hq, hkv, head_dim, h_idx, d_idx, top_k, &need));
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long ld = round_up(s_max, 4);
+  const int nsplit = decode_nsplit(batch, hkv, top_k);
+  float* scores = static_cast<float*>(workspace);
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((long long)batch * ld * 4, 256));
+  float* part_ml = part_o + (size_t)batch * hq * nsplit * 128;
+
+  dsa::IndexerDecodeArgs ia;
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.w = w;
+  ia.k_cache = static_cast<const uint16_t*>(k_idx_cache);
+  ia.seq_lens = seq_lens;
+  ia.batch = batch;
+  ia.s_max = s_max;
+  ia.max_len = max_seq_len;
+  ia.h_idx = h_idx;
+  ia.d_idx = d_idx;
+  ia.scores = scores;
+  ia.ld = ld;
+  ia.keys_per_wave = kDecodeKeysPerWave;
+  DSA_TRY(hip_status(dsa::launch_indexer_decode(ia, s), "decode indexer launch"));
+
+  dsa::TopkArgs t;
+  t.scores = scores;
+  t.ld = ld;
+  t.rows = batch;
+  t.row_len = seq_lens;
+  t.len_base = 0;
+  t.k = top_k;
+  t.idx_out = idx_out;
+  t.values_out = nullptr;
+  DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+
+  dsa::SparseAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.idx = idx_out;
+  a.k_sel = top_k;
+  a.cu_seqlens = nullptr;
+  a.batch = batch;
+  a.seq_lens = seq_lens;
+  a.s_max = s_max;
+  a.rows = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.nsplit = nsplit;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  if (nsplit == 1) return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
+  DSA_TRY(hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch"));
+  return hip_status(dsa::launch_attn_combine(a, s), "combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,302 @@
+// Lightning-indexer score kernels for gfx950 (bf16 MFMA, fused ReLU * weight * head sum).
+//
+// The indexer of the Keye-VL-2.0 report digest (mqxn.cn news 1966, section 一) scores every
+// earlier position of a query token with several light heads that share one key per
+// position (MQA).  The score this library computes is
+//     I[t, s] = sum_j w[t, j] * max(0, <q_idx[t, j, :], k_idx[s, :]>).
+//
+// Both kernels run the contraction on 16x16x32 bf16 MFMA with the (token, head) rows of the
+// query side on the MFMA row axis and 16 keys on the column axis, so each lane ends a tile
+// holding four (head, key) results of one key column: ReLU, the weight multiply and most of
+// the head sum are lane-local, and the remaining sum over the four lane groups is folded
+// into a transpose-reduction that leaves lane l with the score of key l of a 64-key tile
+// (one coalesced 256-byte store per token and tile).
+//
+// The reduction dimension is permuted: MFMA slot (lane group g, k-step s, element e) carries
+// d = (g * NKS + s) * 8 + e, so each lane reads one contiguous 16*NKS-byte run of a key row.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+// Sum the partial scores of four 16-key subtiles over the four lane groups; on return lane l
+// holds the total for subtile l / 16, column l % 16, i.e. key l of the 64-key tile.
+__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3, int lane) {
+  const bool hi = lane >= 32;
+  const float s0 = hi ? p0 : p2, s1 = hi ? p1 : p3;
+  const float k0 = (hi ? p2 : p0) + __shfl_xor(s0, 32);
+  const float k1 = (hi ? p3 : p1) + __shfl_xor(s1, 32);
+  const bool odd = (lane >> 4) & 1;
+  const float s = odd ? k0 : k1;
+  return (odd ? k1 : k0) + __shfl_xor(s, 16);
+}
+
+// ---------------------------------------------------------------------------------------
+// Prefill: a workgroup of 4 waves scores 4 * (64 / H) consecutive query rows of one sequence
+// against one split of keys; key tiles of 64 rows are staged in LDS (double buffered) and
+// shared by the 4 waves.  Each wave keeps its 64 (token, head) query rows in registers.
+template <int H, int DI>
+__global__ __launch_bounds__(256) void indexer_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ w,
+    int seq_off, int row_begin, int row_end, int out_row0, float* __restrict__ scores, long long ld,
+    int key_split, int n_rowblk) {
+  constexpr int TOKW = (H >= 16) ? 64 / H : 16;  // tokens per wave (H = 4: 4 per row tile)
+  constexpr int TOKWG = 4 * TOKW;
+  constexpr int NKS = DI / 32;
+  constexpr int PITCH = DI * 2 + 16;  // bytes per LDS key row (16-byte pad against bank conflicts)
+  constexpr int CPR = DI / 8;         // 16-byte chunks per key row
+  constexpr int NLD = 64 * CPR / 256; // chunks each thread stages per tile
+  constexpr int NSLOT = (H >= 16) ? TOKW : 4;
+  static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
+  static_assert(DI == 64 || DI == 128, "unsupported indexer dim");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][64 * PITCH];
+
+  // XCD-aware order: consecutive work items (same key split, neighbouring rows) land on the
+  // same XCD, whose L2 then serves the shared key tiles.
+  const int per_xcd = gridDim.x >> 3;
+  const int wi = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int split = wi / n_rowblk;
+  const int rb = wi - split * n_rowblk;
+  const int r0 = row_begin + rb * TOKWG;
+  if (r0 >= row_end) return;
+  const int t_last = min(r0 + TOKWG, row_end) - 1 - seq_off;
+  const int kbeg = split * key_split;
+  if (kbeg > t_last) return;
+  const int kend = min(kbeg + key_split, t_last + 1);
+  const int ntiles = (kend - kbeg + 63) >> 6;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, lg = lane >> 4;
+
+  // Query rows of this wave as MFMA A operands: lane supplies row 16*rt + n.
+  u32x4 areg[4][NKS];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int m = 16 * rt + n;
+    const int tok = (H >= 16) ? wave * TOKW + m / H : wave * TOKW + m / 4;
+    const int head = (H >= 16) ? m % H : m % 4;
+    const int r = min(r0 + tok, row_end - 1);
+    const uint16_t* qp = q_idx + ((size_t)r * H + head) * DI + lg * NKS * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) areg[rt][ks] = ldg16(qp + ks * 8);
+  }
+  // Weights of the C rows this lane holds: row 16*rt + 4*lg + i.
+  float wreg[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * rt + 4 * lg + i;
+      const int tok = (H >= 16) ? wave * TOKW + m / H : wave * TOKW + m / 4;
+      const int head = (H >= 16) ? m % H : m % 4;
+      const int r = min(r0 + tok, row_end - 1);
+      wreg[rt][i] = w[(size_t)r * H + head];
+    }
+  // Local position of the wave's last valid token (for skipping fully-masked tiles).
+  const int wave_t_last = min(r0 + wave * TOKW + TOKW, row_end) - 1 - seq_off;
+  const int wave_r0 = r0 + wave * TOKW;
+
+  u32x4 stage[NLD];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+      const int c = threadIdx.x + 256 * p;
+      const int key = c / CPR, part = c % CPR;
+      const int kk = min(kbeg + tile * 64 + key, kend - 1);
+      stage[p] = ldg16(k_idx + (size_t)(seq_off + kk) * DI + part * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < NLD; ++p) {
+      const int c = threadIdx.x + 256 * p;
+      const int key = c / CPR, part = c % CPR;
+      *reinterpret_cast<u32x4*>(&lds[buf][key * PITCH + part * 16]) = stage[p];
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) load_tile(it + 1);
+    const int key0 = kbeg + it * 64;
+    if (wave_r0 < row_end && key0 <= wave_t_last) {
+      const unsigned char* tile = lds[it & 1];
+      float part[4][NSLOT];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const unsigned char* bp = tile + (16 * st + n) * PITCH + lg * NKS * 16;
+        u32x4 breg[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) breg[ks] = *reinterpret_cast<const u32x4*>(bp + ks * 16);
+        f32x4 c[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], breg[ks], c[rt]);
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) part[st][s] = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int slot = (H >= 16) ? (16 * rt) / H : rt;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part[st][slot] = fmaf(fmaxf(c[rt][i], 0.f), wreg[rt][i], part[st][slot]);
+        }
+      }
+      if constexpr (H >= 16) {
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
+          const float v = transpose_reduce4(part[0][s], part[1][s], part[2][s], part[3][s], lane);
+          const int r = wave_r0 + s;
+          const int key = key0 + lane;
+          if (r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NSLOT; ++s) {
+          const int r = wave_r0 + 4 * s + lg;
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int key = key0 + 16 * st + n;
+            if (r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = part[st][s];
+          }
+        }
+      }
+    }
+    if (it + 1 < ntiles) store_tile((it + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Decode: one query token per sequence against its cached keys.  HBM-bound (64 flop per key
+// byte at 64 heads x 128 dims), so key tiles go straight from global memory into MFMA
+// B-operand registers, double buffered, with no LDS.  A workgroup of 4 waves covers
+// 4 * keys_per_wave consecutive keys of one sequence.
+template <int H, int DI>
+__global__ __launch_bounds__(256) void indexer_decode_kernel(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_cache,
+    const int* __restrict__ seq_lens, int s_max, float* __restrict__ scores, long long ld, int keys_per_wave,
+    int nsplit) {
+  constexpr int NKS = DI / 32;
+  constexpr int RT = (H >= 16) ? H / 16 : 1;
+  static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
+  const int b = blockIdx.x / nsplit;
+  const int split = blockIdx.x - b * nsplit;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, lg = lane >> 4;
+  const int len = min(seq_lens[b], s_max);  // defensive: never read past the cache
+  const int kbeg = (split * 4 + wave) * keys_per_wave;
+  if (kbeg >= len) return;
+  const int kend = min(kbeg + keys_per_wave, len);
+  const int ntiles = (kend - kbeg + 63) >> 6;
+
+  u32x4 areg[RT][NKS];
+  float wreg[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int m = 16 * rt + n;
+    const uint16_t* qp = q_idx + ((size_t)b * H + (m < H ? m : 0)) * DI + lg * NKS * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) areg[rt][ks] = (m < H) ? ldg16(qp + ks * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mc = 16 * rt + 4 * lg + i;
+      wreg[rt][i] = (mc < H) ? w[(size_t)b * H + mc] : 0.f;
+    }
+  }
+  const uint16_t* kbase = k_cache + (size_t)b * s_max * DI + lg * NKS * 8;
+
+  u32x4 bufA[4][NKS], bufB[4][NKS];
+  auto load = [&](u32x4 (&dst)[4][NKS], int tile) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kk = min(kbeg + tile * 64 + 16 * st + n, kend - 1);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) dst[st][ks] = ldg16(kbase + (size_t)kk * DI + ks * 8);
+    }
+  };
+  auto compute = [&](const u32x4 (&src)[4][NKS], int tile) {
+    float part[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      f32x4 c[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], src[st][ks], c[rt]);
+      float acc = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(fmaxf(c[rt][i], 0.f), wreg[rt][i], acc);
+      part[st] = acc;
+    }
+    const float v = transpose_reduce4(part[0], part[1], part[2], part[3], lane);
+    const int key = kbeg + tile * 64 + lane;
+    if (key < kend) scores[(size_t)b * ld + key] = v;
+  };
+
+  load(bufA, 0);
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    load(bufB, it + 1);
+    compute(bufA, it);
+    if (it + 2 < ntiles) load(bufA, it + 2);
+    compute(bufB, it + 1);
+  }
+  if (it < ntiles) compute(bufA, it);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------------
+// Host launchers.
+
+template <int H, int DI>
+static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, hipStream_t s) {
+  constexpr int TOKWG = 4 * ((H >= 16) ? 64 / H : 16);
+  const int rows = a.row_end - a.row_begin;
+  const int n_rowblk = (rows + TOKWG - 1) / TOKWG;
+  const int t_max = a.row_end - 1 - a.seq_off;
+  const int n_split = (t_max + a.key_split) / a.key_split;
+  long long n = (long long)n_rowblk * n_split;
+  n = (n + 7) / 8 * 8;
+  hipLaunchKernelGGL((indexer_prefill_kernel<H, DI>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx, a.w,
+                     a.seq_off, a.row_begin, a.row_end, a.out_row0, a.scores, a.ld, a.key_split, n_rowblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s) {
+  if (a.h_idx == 64 && a.d_idx == 128) return launch_prefill_t<64, 128>(a, s);
+  if (a.h_idx == 32 && a.d_idx == 128) return launch_prefill_t<32, 128>(a, s);
+  if (a.h_idx == 16 && a.d_idx == 128) return launch_prefill_t<16, 128>(a, s);
+  if (a.h_idx == 4 && a.d_idx == 64) return launch_prefill_t<4, 64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int H, int DI>
+static hipError_t launch_decode_t(const IndexerDecodeArgs& a, hipStream_t s) {
+  const int kpw = a.keys_per_wave;
+  const int nsplit = (a.max_len + 4 * kpw - 1) / (4 * kpw);
+  hipLaunchKernelGGL((indexer_decode_kernel<H, DI>), dim3((unsigned)(a.batch * nsplit)), dim3(256), 0, s, a.q_idx,
+                     a.w, a.k_cache, a.seq_lens, a.s_max, a.scores, a.ld, kpw, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t s) {
+  if (a.h_idx == 64 && a.d_idx == 128) return launch_decode_t<64, 128>(a, s);
+  if (a.h_idx == 32 && a.d_idx == 128) return launch_decode_t<32, 128>(a, s);
+  if (a.h_idx == 16 && a.d_idx == 128) return launch_decode_t<16, 128>(a, s);
+  if (a.h_idx == 4 && a.d_idx == 64) return launch_decode_t<4, 64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

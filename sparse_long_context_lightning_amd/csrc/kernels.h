@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI (dsa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Scores of packed rows [row_begin, row_end), all in one sequence that starts at packed row
+// seq_off, written to scores[(r - out_row0) * ld + s] for s <= r - seq_off.
+struct IndexerPrefillArgs {
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  const float* w;
+  int h_idx, d_idx;
+  int seq_off, row_begin, row_end, out_row0;
+  float* scores;
+  long long ld;
+  int key_split;  // keys per workgroup, multiple of 64
+};
+
+struct IndexerDecodeArgs {
+  const uint16_t* q_idx;
+  const float* w;
+  const uint16_t* k_cache;
+  const int* seq_lens;
+  int batch, s_max, max_len, h_idx, d_idx;
+  float* scores;
+  long long ld;
+  int keys_per_wave;  // multiple of 64
+};
+
+// Row lengths come from row_len[i] if non-null, else len_base + i + 1 (causal prefill rows).
+struct TopkArgs {
+  const float* scores;
+  long long ld;
+  int rows;
+  const int* row_len;
+  int len_base;
+  int k;
+  int* idx_out;       // [rows, k] at row stride k
+  float* values_out;  // optional
+};
+
+// Row r: prefill mode (seq_lens == nullptr) finds its sequence in cu_seqlens, decode mode uses
+// sequence r with kv rows starting at r * s_max and valid length seq_lens[r].
+struct SparseAttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* idx;
+  int k_sel;
+  const int* cu_seqlens;
+  int batch;
+  const int* seq_lens;
+  int s_max;
+  int rows, hq, hkv;
+  float softmax_scale;
+  uint16_t* out;
+  float* lse;
+  int nsplit;       // > 1: write partials to part_o / part_ml instead of out / lse
+  float* part_o;    // [rows, hq, nsplit, 128]
+  float* part_ml;   // [rows, hq, nsplit, 2] (running max in log2 units, sum)
+};
+
+hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
+hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+hipError_t launch_sparse_attn(const SparseAttnArgs& a, hipStream_t s);
+hipError_t launch_attn_combine(const SparseAttnArgs& a, hipStream_t s);
+
+}  // namespace dsa

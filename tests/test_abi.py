@@ -1,0 +1,127 @@
+"""The C ABI on a host without a GPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_lightning_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+P = ctypes.c_void_p
+FAKE = P(1 << 20)            # aligned, never dereferenced by host validation
+MISALIGNED = P((1 << 20) + 2)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsa.load()
+    names = _declared()
+    assert len(names) == 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dsa.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert dsa.dsa_abi_version() == 1
+    assert dsa.dsa_status_string(0) == "DSA_OK"
+    assert dsa.dsa_status_string(3) == "DSA_ERR_WORKSPACE"
+    assert dsa.dsa_status_string(99) == "DSA_ERR_UNKNOWN"
+
+
+def _cu(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return arr, ctypes.cast(arr, P)
+
+
+def _prefill(lib, **over):
+    cu_arr, cu_p = _cu([0, 100, 300])
+    args = dict(q=FAKE, k=FAKE, v=FAKE, q_idx=FAKE, k_idx=FAKE, w=FAKE, cu=FAKE, cu_host=cu_p, batch=2, total=300,
+                max_seqlen=200, hq=32, hkv=4, d=128, h_idx=64, d_idx=128, top_k=2048, scale=0.1, out=FAKE, lse=None,
+                idx=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return lib.dsa_prefill(*args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(idx=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(cu_host=None), dsa.DSA_ERR_INVALID_ARG),
+    (dict(k=MISALIGNED), dsa.DSA_ERR_INVALID_ARG),
+    (dict(hq=30, hkv=4), dsa.DSA_ERR_INVALID_ARG),
+    (dict(d=64), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(hq=64, hkv=2), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(h_idx=8), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(top_k=0), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(top_k=4096), dsa.DSA_ERR_UNSUPPORTED),
+    (dict(total=299), dsa.DSA_ERR_INVALID_ARG),
+    (dict(max_seqlen=150), dsa.DSA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1000), dsa.DSA_ERR_WORKSPACE),
+    (dict(ws=None), dsa.DSA_ERR_WORKSPACE),
+])
+def test_prefill_rejects_bad_arguments(over, status):
+    lib = dsa.load()
+    assert _prefill(lib, **over) == status
+    assert dsa.dsa_last_error() != ""
+
+
+def test_prefill_rejects_bad_cu_seqlens():
+    lib = dsa.load()
+    for vals in ([1, 100, 300], [0, 200, 100], [0, 100, 301]):
+        arr, p = _cu(vals)
+        assert _prefill(lib, cu_host=p) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_other_entry_points_reject_bad_arguments():
+    lib = dsa.load()
+    cu_arr, cu_p = _cu([0, 64])
+    # index scores: ld not a multiple of 4, row range outside, unsupported shape
+    assert lib.dsa_index_scores(FAKE, FAKE, FAKE, cu_p, 1, 64, 64, 128, 0, 64, FAKE, 66, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_index_scores(FAKE, FAKE, FAKE, cu_p, 1, 64, 64, 128, 10, 60, FAKE, 64, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_index_scores(FAKE, FAKE, FAKE, cu_p, 1, 64, 64, 128, 0, 64, FAKE, 32, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_index_scores(FAKE, FAKE, FAKE, cu_p, 1, 64, 8, 128, 0, 64, FAKE, 64, None) == dsa.DSA_ERR_UNSUPPORTED
+    # top-k
+    assert lib.dsa_topk(FAKE, 64, 4, FAKE, 0, FAKE, None, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk(FAKE, 63, 4, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(None, 64, 4, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk(FAKE, 64, 4, None, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    # sparse attention
+    assert lib.dsa_sparse_gqa_attn(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 64, 8, 2, 128, ctypes.c_float(0.1), FAKE, None,
+                                   None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_gqa_attn(FAKE, FAKE, FAKE, FAKE, 16, FAKE, 1, 64, 8, 3, 128, ctypes.c_float(0.1), FAKE,
+                                   None, None) == dsa.DSA_ERR_INVALID_ARG
+    # decode
+    args = [FAKE] * 7 + [4, 1000, 1000, 32, 4, 128, 64, 128, 2048, ctypes.c_float(0.1), FAKE, None, FAKE, FAKE, 10,
+                         None]
+    assert lib.dsa_decode(*args) == dsa.DSA_ERR_WORKSPACE
+    args2 = list(args)
+    args2[9] = 1001  # max_seq_len > s_max
+    assert lib.dsa_decode(*args2) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_zero_sized_calls_are_no_ops():
+    lib = dsa.load()
+    cu_arr, cu_p = _cu([0, 64])
+    assert lib.dsa_index_scores(FAKE, FAKE, FAKE, cu_p, 1, 64, 64, 128, 0, 0, FAKE, 64, None) == dsa.DSA_OK
+    assert lib.dsa_topk(FAKE, 64, 0, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_OK
+
+
+def test_workspace_sizes():
+    assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == 0
+    # prefill: a 2048-row chunk of 131072 float scores
+    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 32, 4, 128, 64, 128, 2048) == 2048 * 131072 * 4
+    # small problems use the whole row count
+    assert dsa.dsa_prefill_workspace_size(1, 100, 100, 8, 2, 128, 4, 64, 16) == 100 * 100 * 4
+    n = dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 128, 64, 128, 2048)
+    assert n >= 32 * 131072 * 4
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 64, 64, 128, 2048)

@@ -1,0 +1,364 @@
+"""Parity of the HIP path with the CPU oracle at sizes the oracle finishes in seconds
+(several tiles plus ragged tails), through the C ABI.  GPU only."""
+
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as orc
+from sparse_long_context_lightning_amd import inputs as inp
+
+import dsa_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+# ------------------------------------------------------------------------------ indexer
+
+@pytest.mark.parametrize("lens,h_idx,d_idx", [
+    ([4096], 4, 64),            # tiny-prefill shapes, full matrix
+    ([700], 64, 128),           # ragged tail (700 = 10*64 + 60 keys, 175 row blocks)
+    ([130, 517, 66], 64, 128),  # packed varlen
+    ([333], 32, 128),
+    ([301], 16, 128),
+    ([1, 5, 250], 4, 64),
+])
+def test_index_scores_bit_exact(dsa, lens, h_idx, d_idx):
+    torch = _torch()
+    pi = inp.prefill_inputs(lens, h_idx, d_idx, 8, 2, 128, 16, seed=100 + sum(lens))
+    dev = tl.upload_prefill(pi)
+    total = sum(lens)
+    ld = (max(lens) + 3) // 4 * 4
+    scores = torch.full((total, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, 0, total, scores)
+    got = scores.cpu().numpy()
+    want = orc.index_scores(tl.f64(pi.q_idx), tl.f64(pi.k_idx), pi.w.astype(np.float64), pi.cu_seqlens)
+    for r, row in enumerate(want):
+        t = len(row)
+        assert np.array_equal(got[r, :t].astype(np.float64), row), f"row {r}"
+        assert np.all(np.isnan(got[r, t:])), f"row {r} wrote past its prefix"
+
+
+def test_index_scores_row_window(dsa):
+    torch = _torch()
+    lens = [300, 200]
+    pi = inp.prefill_inputs(lens, 64, 128, 8, 2, 128, 16, seed=7)
+    dev = tl.upload_prefill(pi)
+    ld = 300
+    r0, rc = 250, 120  # spans both sequences
+    scores = torch.full((rc, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, r0, rc, scores)
+    got = scores.cpu().numpy()
+    want = orc.index_scores(tl.f64(pi.q_idx), tl.f64(pi.k_idx), pi.w.astype(np.float64), pi.cu_seqlens)
+    for i in range(rc):
+        row = want[r0 + i]
+        assert np.array_equal(got[i, :len(row)].astype(np.float64), row), f"row {r0 + i}"
+
+
+# ------------------------------------------------------------------------------ top-k
+
+def _run_topk(dsa, scores_np, lens, k, values=True):
+    torch = _torch()
+    rows, ld = scores_np.shape
+    s = torch.from_numpy(np.ascontiguousarray(scores_np, dtype=np.float32)).cuda()
+    rl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    val = torch.full((rows, k), float("nan"), dtype=torch.float32, device="cuda") if values else None
+    dsa.dsa_topk(s, rl, k, idx, val)
+    return idx.cpu().numpy(), (val.cpu().numpy() if values else None)
+
+
+def _check_topk(scores_np, lens, k, idx, val):
+    for r in range(scores_np.shape[0]):
+        n = lens[r]
+        want = orc.select_topk_row(scores_np[r, :n].astype(np.float64), k)
+        assert np.array_equal(idx[r], want), f"row {r} (len {n}): first diff at {np.argmax(idx[r] != want)}"
+        if val is not None:
+            m = want >= 0
+            assert np.array_equal(val[r][m], scores_np[r, want[m]].astype(np.float32) + np.float32(0.0))
+            assert np.all(np.isneginf(val[r][~m]))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_topk_random_rows_with_ties(dsa, seed):
+    rng = np.random.default_rng(seed)
+    rows, ld, k = 96, 9000, 256
+    scores = (rng.integers(-40, 400, size=(rows, ld)) / 8.0).astype(np.float32)
+    lens = rng.integers(1, ld + 1, size=rows)
+    lens[:4] = [k - 1, k, k + 1, ld]
+    idx, val = _run_topk(dsa, scores, lens, k)
+    _check_topk(scores, lens, k, idx, val)
+    tl.check_index_structure(idx, lens, k)
+
+
+def test_topk_special_rows(dsa):
+    n, k = 5000, 2048
+    rows = []
+    rows.append(np.zeros(n))                          # all equal -> fallback path, 0..k-1
+    rows.append(np.arange(n, 0, -1.0))                # decreasing -> 0..k-1
+    rows.append(np.arange(n, dtype=np.float64))       # increasing -> n-k..n-1
+    z = np.zeros(n)
+    z[1::2] = -0.0                                    # -0 == +0
+    rows.append(z)
+    r = np.full(n, 3.0)
+    r[::7] = 5.0                                      # many equal maxima then a long tie run
+    rows.append(r)
+    r = np.random.default_rng(3).standard_normal(n) * 1e-30  # tiny magnitudes and both signs
+    rows.append(r)
+    r = np.random.default_rng(4).standard_normal(n) * 1e30
+    rows.append(r)
+    r = np.full(n, -1.0)
+    r[4000] = np.inf
+    r[10] = -np.inf
+    rows.append(r)
+    scores = np.stack(rows).astype(np.float32)
+    lens = [n] * len(rows)
+    idx, val = _run_topk(dsa, scores, lens, k)
+    _check_topk(scores, lens, k, idx, val)
+    assert idx[0].tolist() == list(range(k))
+    assert idx[2].tolist() == list(range(n - k, n))
+
+
+def test_topk_long_rows(dsa):
+    rng = np.random.default_rng(9)
+    ld, k = 131072, 2048
+    scores = (rng.integers(0, 6000, size=(3, ld)) / 8.0).astype(np.float32)
+    lens = [ld, 100000, 70001]
+    idx, val = _run_topk(dsa, scores, lens, k)
+    _check_topk(scores, lens, k, idx, val)
+
+
+def test_topk_short_rows_and_k1(dsa):
+    rng = np.random.default_rng(5)
+    scores = rng.standard_normal((40, 64)).astype(np.float32)
+    lens = list(range(1, 41))
+    for k in (1, 3, 64):
+        idx, val = _run_topk(dsa, scores, lens, k)
+        _check_topk(scores, lens, k, idx, val)
+
+
+# ------------------------------------------------------------------------------ sparse attention
+
+def _attn_inputs(seed, lens, hq, hkv, k_sel, mode="random"):
+    pi = inp.prefill_inputs(lens, 4, 64, hq, hkv, 128, k_sel, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    total = sum(lens)
+    idx = np.full((total, k_sel), -1, dtype=np.int32)
+    cu = pi.cu_seqlens
+    for b in range(len(lens)):
+        for t in range(lens[b]):
+            r = cu[b] + t
+            if mode == "all":
+                sel = np.arange(min(t + 1, k_sel))
+            else:
+                n = int(rng.integers(1, min(t + 1, k_sel) + 1))
+                sel = np.sort(rng.choice(t + 1, size=n, replace=False))
+            idx[r, :len(sel)] = sel
+    return pi, idx
+
+
+def _run_attn(dsa, pi, idx, lse=True):
+    torch = _torch()
+    dev = tl.upload_prefill(pi)
+    idx_t = torch.from_numpy(idx).cuda()
+    out = torch.empty_like(dev["q"])
+    lse_t = torch.empty(dev["q"].shape[0], dev["q"].shape[1], dtype=torch.float32, device="cuda") if lse else None
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx_t, dev["cu"], out, lse_t)
+    torch.cuda.synchronize()
+    return tl.bf16_tensor_to_f64(out), (lse_t.cpu().numpy() if lse else None)
+
+
+def _oracle_attn(pi, idx):
+    q, k, v = tl.f64(pi.q), tl.f64(pi.k), tl.f64(pi.v)
+    cu = pi.cu_seqlens
+    scale = orc.default_softmax_scale(q.shape[2])
+    outs, lses = [], []
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            r = cu[b] + t
+            o, l, ws = orc.sparse_gqa_attention_row(q[r], k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]], idx[r], scale)
+            outs.append(o)
+            lses.append(l)
+    return np.asarray(outs), np.asarray(lses)
+
+
+@pytest.mark.parametrize("lens,hq,hkv,k_sel", [
+    ([300], 32, 4, 96),
+    ([97, 160], 8, 2, 80),
+    ([200], 16, 1, 50),
+    ([150], 4, 4, 33),
+    ([120], 12, 4, 64),
+])
+def test_sparse_attention_matches_oracle(dsa, lens, hq, hkv, k_sel):
+    pi, idx = _attn_inputs(31 + hq, lens, hq, hkv, k_sel)
+    out, lse = _run_attn(dsa, pi, idx)
+    want_o, want_l = _oracle_attn(pi, idx)
+    tl.assert_attn_close(out, want_o, "O")
+    assert np.max(np.abs(lse - want_l)) <= tl.LSE_ABS
+
+
+def test_sparse_attention_with_all_positions_is_dense_causal(dsa):
+    torch = _torch()
+    lens = [200]
+    pi, idx = _attn_inputs(5, lens, 32, 4, 256, mode="all")
+    out, _ = _run_attn(dsa, pi, idx, lse=False)
+    q, k, v = (torch.from_numpy(tl.f64(x)) for x in (pi.q, pi.k, pi.v))
+    qt = q.permute(1, 0, 2)[None]
+    kt = k.repeat_interleave(8, dim=1).permute(1, 0, 2)[None].contiguous()
+    vt = v.repeat_interleave(8, dim=1).permute(1, 0, 2)[None].contiguous()
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)[0].permute(1, 0, 2).numpy()
+    tl.assert_attn_close(out, ref, "dense")
+
+
+def test_sparse_attention_unit_values_single_position_and_lse(dsa):
+    torch = _torch()
+    lens = [130]
+    pi, idx = _attn_inputs(8, lens, 32, 4, 64)
+    pi.v[:] = 0x3F80  # bf16 1.0
+    out, lse = _run_attn(dsa, pi, idx)
+    assert np.max(np.abs(out - 1.0)) == 0.0
+    # row 0 attends only to position 0: O = V[0] exactly (after bf16 rounding of an exact value)
+    pi2, idx2 = _attn_inputs(9, lens, 32, 4, 64)
+    out2, lse2 = _run_attn(dsa, pi2, idx2)
+    v0 = tl.f64(pi2.v)[0]
+    for h in range(32):
+        assert np.array_equal(out2[0, h], v0[h // 8])
+    # softmax weights over the selected set sum to one: sum_s exp(z_s - lse) = 1
+    q, k = tl.f64(pi2.q), tl.f64(pi2.k)
+    for r in (5, 77, 129):
+        sel = idx2[r][idx2[r] >= 0]
+        for h in (0, 13, 31):
+            z = (k[sel, h // 8] @ q[r, h]) / math.sqrt(128)
+            assert abs(np.exp(z - lse2[r, h]).sum() - 1.0) < 1e-3
+
+
+def test_sparse_attention_masks_out_of_range_entries(dsa):
+    lens = [64, 64]
+    pi, idx = _attn_inputs(12, lens, 8, 2, 32)
+    bad = idx.copy()
+    # entries beyond the causal prefix or negative are ignored
+    for r in range(bad.shape[0]):
+        t = r % 64
+        bad[r, -1] = t + 1 + r % 5   # in the future
+        bad[r, -2] = -3
+    clean = np.where((bad >= 0) & (bad <= (np.arange(128) % 64)[:, None]), bad, -1).astype(np.int32)
+    out_bad, lse_bad = _run_attn(dsa, pi, bad.astype(np.int32))
+    want_o, want_l = _oracle_attn(pi, clean)
+    tl.assert_attn_close(out_bad, want_o, "masked")
+
+
+# ------------------------------------------------------------------------------ fused prefill
+
+def test_prefill_tiny_workload_full_oracle(dsa):
+    """The 4K tiny-prefill workload (H_I=4, d_I=64, Hq=8, Hkv=2, k=256): every row."""
+    pi = inp.workload("c1_tiny_prefill_4k")
+    dev = tl.upload_prefill(pi)
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                pi.cu_seqlens, pi.top_k)
+    got_idx = idx.cpu().numpy()
+    want = tl.oracle_prefill_rows(pi, None)
+    tl.assert_idx_equal(got_idx, want["idx"], what="c1 idx")
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(out), want["out"], "c1 O")
+    assert np.max(np.abs(lse.cpu().numpy() - want["lse"])) <= tl.LSE_ABS
+
+
+@pytest.mark.parametrize("lens,chunk_rows", [([700, 64, 1500], None), ([2600], 64), ([1, 2, 2200], 128)])
+def test_prefill_varlen_and_chunking(dsa, lens, chunk_rows):
+    torch = _torch()
+    pi = inp.prefill_inputs(lens, 64, 128, 32, 4, 128, 512, seed=sum(lens), structure="blocks16")
+    dev = tl.upload_prefill(pi)
+    ws = None
+    if chunk_rows is not None:
+        ws = torch.empty(chunk_rows * ((max(lens) + 3) // 4 * 4) * 4, dtype=torch.uint8, device="cuda")
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                pi.cu_seqlens, pi.top_k, workspace=ws)
+    rng = np.random.default_rng(1)
+    total = sum(lens)
+    rows = sorted(set([0, total - 1] + [int(c) for c in pi.cu_seqlens[:-1]] + [int(c) - 1 for c in pi.cu_seqlens[1:]]
+                      + rng.integers(0, total, 40).tolist()))
+    want = tl.oracle_prefill_rows(pi, rows)
+    got_idx = idx.cpu().numpy()
+    tl.assert_idx_equal(got_idx[rows], want["idx"], rows, "idx")
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(out)[rows], want["out"], "O")
+    row_lens = np.concatenate([np.arange(1, n + 1) for n in lens])
+    tl.check_index_structure(got_idx, row_lens, pi.top_k)
+
+
+def test_prefill_equals_composition_and_is_deterministic(dsa):
+    torch = _torch()
+    lens = [900, 333]
+    pi = inp.prefill_inputs(lens, 64, 128, 32, 4, 128, 256, seed=77)
+    dev = tl.upload_prefill(pi)
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                pi.cu_seqlens, pi.top_k)
+    out2, lse2, idx2 = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                   pi.cu_seqlens, pi.top_k)
+    assert torch.equal(idx, idx2) and torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse, lse2)
+    # composition: scores -> top-k -> attention through the separate entry points
+    total = sum(lens)
+    ld = 900
+    scores = torch.empty(total, ld, dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, 0, total, scores)
+    row_len = torch.from_numpy(np.concatenate([np.arange(1, n + 1) for n in lens]).astype(np.int32)).cuda()
+    idx3 = torch.empty(total, pi.top_k, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(scores, row_len, pi.top_k, idx3)
+    out3 = torch.empty_like(out)
+    lse3 = torch.empty_like(lse)
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx3, dev["cu"], out3, lse3)
+    assert torch.equal(idx, idx3)
+    assert torch.equal(out.view(torch.int16), out3.view(torch.int16))
+
+
+def test_prefill_outputs_fully_written(dsa):
+    torch = _torch()
+    lens = [300, 45]
+    pi = inp.prefill_inputs(lens, 4, 64, 8, 2, 128, 64, seed=3)
+    dev = tl.upload_prefill(pi)
+    total = sum(lens)
+    out = torch.full_like(dev["q"], float("nan"))
+    lse = torch.full((total, 8), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((total, 64), -99, dtype=torch.int32, device="cuda")
+    ws = torch.empty(dsa.dsa_prefill_workspace_size(2, total, 300, 8, 2, 128, 4, 64, 64), dtype=torch.uint8,
+                     device="cuda")
+    dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], pi.cu_seqlens,
+                    300, 64, out, lse, idx, ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any()
+    assert (idx != -99).all()
+
+
+# ------------------------------------------------------------------------------ decode
+
+@pytest.mark.parametrize("h_idx,d_idx,hq,hkv,k", [(64, 128, 32, 4, 512), (4, 64, 8, 2, 100), (16, 128, 16, 1, 64)])
+def test_decode_matches_oracle(dsa, h_idx, d_idx, hq, hkv, k):
+    s_max = 3000
+    seq = [3000, 1, 700, k, k + 1, 2999, 1234, 64]
+    di = inp.decode_inputs(len(seq), s_max, seq, h_idx, d_idx, hq, hkv, 128, k, seed=h_idx + k)
+    dev = tl.upload_decode(di)
+    out, lse, idx = dsa.decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
+                               dev["seq_lens"], k, max_seq_len=max(seq))
+    want = tl.oracle_decode_rows_lazy(di, range(len(seq)))
+    tl.assert_idx_equal(idx.cpu().numpy(), np.asarray(want["idx"]), what="decode idx")
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(out), np.asarray(want["out"]), "decode O")
+    assert np.max(np.abs(lse.cpu().numpy() - np.asarray(want["lse"]))) <= tl.LSE_ABS
+
+
+def test_decode_equals_prefill_last_row(dsa):
+    torch = _torch()
+    n, k = 2500, 256
+    pi = inp.prefill_inputs([n], 64, 128, 32, 4, 128, k, seed=55)
+    dev = tl.upload_prefill(pi)
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, k)
+    seq = torch.tensor([n], dtype=torch.int32, device="cuda")
+    dout, dlse, didx = dsa.decode(dev["q"][n - 1:n].contiguous(), dev["q_idx"][n - 1:n].contiguous(),
+                                  dev["w"][n - 1:n].contiguous(), dev["k"][None].contiguous(),
+                                  dev["v"][None].contiguous(), dev["k_idx"][None].contiguous(), seq, k)
+    assert torch.equal(idx[n - 1], didx[0])
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(dout[0]), tl.bf16_tensor_to_f64(out[n - 1]), "decode vs prefill")
