@@ -1,0 +1,348 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+
+A step is one pass of the whole prefill path (indexer -> top-k -> sparse GQA attention) over
+the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexer heads of
+dim 128, 32 query / 4 KV heads of dim 128, keys in 16-token blocks), with every input already
+resident in HBM.  The path is driven through the C ABI's separate entry points in exactly the
+chunk schedule dsa_prefill uses, so HIP events on the launch stream time each kernel inside
+the timed region; the fused dsa_prefill call is timed as well and reported beside it.  The
+decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill.
+
+One JSON line is printed last.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+PREFILL = "c3_prefill_128k"
+DECODE = "c4_decode_b32_128k"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default=PREFILL)
+    ap.add_argument("--decode-workload", default=DECODE)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for counter calibration) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream every library call is enqueued on)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.pending = {}
+        self.total = {}
+        self.count = {}
+
+    def start(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        return (name, ev)
+
+    def stop(self, tok):
+        name, ev0 = tok
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev1.record()
+        self.pending.setdefault(name, []).append((ev0, ev1))
+
+    def collect(self):
+        self.torch.cuda.synchronize()
+        for name, evs in self.pending.items():
+            for a, b in evs:
+                self.total[name] = self.total.get(name, 0.0) + a.elapsed_time(b)
+                self.count[name] = self.count.get(name, 0) + 1
+        self.pending = {}
+
+    def reset(self):
+        self.pending, self.total, self.count = {}, {}, {}
+
+
+def prefill_bench(args, dsa, inp, tl):
+    import torch
+    spec = inp.WORKLOADS[args.workload]
+    assert spec["kind"] == "prefill"
+    t0 = time.time()
+    pi = inp.workload(args.workload)
+    log(f"generated {args.workload} inputs in {time.time() - t0:.1f}s")
+    dev = tl.upload_prefill(pi)
+    lens = [int(x) for x in pi.seq_lens]
+    total = sum(lens)
+    hq, d = pi.q.shape[1], pi.q.shape[2]
+    hkv = pi.k.shape[1]
+    h_idx, d_idx = pi.q_idx.shape[1], pi.q_idx.shape[2]
+    k = pi.top_k
+    max_seqlen = max(lens)
+    ld = (max_seqlen + 3) // 4 * 4
+    cu = pi.cu_seqlens
+    ws_bytes = dsa.dsa_prefill_workspace_size(len(lens), total, max_seqlen, hq, hkv, d, h_idx, d_idx, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    chunk = min(ws_bytes // 4 // ld, total)
+    if chunk > 64:
+        chunk = chunk // 64 * 64
+    scores = ws.view(torch.float32)[: chunk * ld].view(chunk, ld)
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(total, hq, dtype=torch.float32, device="cuda")
+    idx = torch.empty(total, k, dtype=torch.int32, device="cuda")
+    row_len = torch.from_numpy(np.concatenate([np.arange(1, n + 1) for n in lens]).astype(np.int32)).cuda()
+    timer = Timer()
+
+    def step():
+        for b in range(len(lens)):
+            o, e = int(cu[b]), int(cu[b + 1])
+            for c0 in range(o, e, chunk):
+                c1 = min(e, c0 + chunk)
+                tok = timer.start("indexer")
+                dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, c1 - c0, scores, ld=ld)
+                timer.stop(tok)
+                tok = timer.start("topk")
+                dsa.dsa_topk(scores, row_len[c0:c1], k, idx[c0:c1], ld=ld)
+                timer.stop(tok)
+        tok = timer.start("sparse_attn")
+        dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out, lse)
+        timer.stop(tok)
+
+    for _ in range(args.warmup):
+        step()
+    timer.collect()
+    timer.reset()
+    torch.cuda.synchronize()
+    log(f"prefill warmup done; timing {args.steps} steps")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    timer.collect()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    kern = {n: timer.total[n] / args.steps for n in timer.total}            # ms per step
+    launches = {n: timer.count[n] / args.steps for n in timer.count}
+
+    # The fused entry point, same inputs and workspace.
+    for _ in range(max(1, args.warmup)):
+        dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
+                        max_seqlen, k, out, lse, idx, ws)
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for _ in range(args.steps):
+        dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
+                        max_seqlen, k, out, lse, idx, ws)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - tf0) * 1e3 / args.steps
+    log(f"prefill {ms_per_step:.1f} ms/step (fused {fused_ms:.1f}); kernels {kern}")
+
+    # Algorithmic work per step.
+    pairs = sum(n * (n + 1) // 2 for n in lens)
+    idx_flops = pairs * 2 * h_idx * d_idx
+    sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
+    attn_bytes = sel_pairs * (2 * hkv * d * 2 + 4) + total * (2 * hq * d * 2 + 4 * hq)
+    topk_bytes = pairs * 4 * 2 + total * k * 4   # two passes over each row's scores + index write
+    idx_tflops = idx_flops / (kern["indexer"] * 1e-3) / 1e12
+    attn_gbs = attn_bytes / (kern["sparse_attn"] * 1e-3) / 1e9
+    topk_gbs = topk_bytes / (kern["topk"] * 1e-3) / 1e9
+
+    # Parity on a handful of rows (bit-exact indices, outputs within tolerance).
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, k - 1, k, total - 1] + rng.integers(0, total, 4).tolist()))
+    want = tl.oracle_prefill_rows_lazy(pi, rows)
+    got_idx = idx.cpu().numpy()[rows]
+    idx_ok = bool(np.array_equal(got_idx, want["idx"]))
+    err = np.abs(tl.bf16_tensor_to_f64(out[rows]) - want["out"])
+    parity = {"rows_checked": len(rows), "idx_bit_exact": idx_ok, "max_abs": float(err.max()),
+              "mean_abs": float(err.mean())}
+    log(f"parity {parity}")
+
+    res = dict(
+        pi=pi, rows_total=total, ms_per_step=ms_per_step, fused_ms=fused_ms, kern=kern, launches=launches,
+        idx_flops=idx_flops, idx_tflops=idx_tflops, attn_bytes=attn_bytes, attn_gbs=attn_gbs, topk_bytes=topk_bytes,
+        topk_gbs=topk_gbs, parity=parity, pairs=pairs, sel_pairs=sel_pairs,
+    )
+    del dev, ws, scores, out, lse, idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_bench(args, dsa, inp, tl):
+    import torch
+    t0 = time.time()
+    di = inp.workload(args.decode_workload)
+    log(f"generated {args.decode_workload} inputs in {time.time() - t0:.1f}s")
+    dev = tl.upload_decode(di)
+    batch, hq, d = di.q.shape
+    s_max, hkv = di.k_cache.shape[1], di.k_cache.shape[2]
+    h_idx, d_idx = di.q_idx.shape[1], di.q_idx.shape[2]
+    k = di.top_k
+    ws = torch.empty(dsa.dsa_decode_workspace_size(batch, s_max, hq, hkv, d, h_idx, d_idx, k), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(batch, hq, dtype=torch.float32, device="cuda")
+    idx = torch.empty(batch, k, dtype=torch.int32, device="cuda")
+    max_len = int(di.seq_lens.max())
+
+    def step():
+        dsa.dsa_decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
+                       dev["seq_lens"], max_len, k, out, lse, idx, ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    n_iter = max(20, args.steps * 4)
+    evs = []
+    for _ in range(n_iter):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    us_median = times[len(times) // 2]
+    us_min = times[0]
+    lens = di.seq_lens.astype(np.int64)
+    bytes_step = int((lens * d_idx * 2).sum() + (lens * 4 * 2).sum()
+                     + (np.minimum(lens, k) * (2 * hkv * d * 2 + 4)).sum() + batch * hq * d * 2 * 2)
+    brow = [0, batch - 1]
+    want = tl.oracle_decode_rows_lazy(di, brow)
+    got_idx = idx.cpu().numpy()[brow]
+    err = np.abs(tl.bf16_tensor_to_f64(out[brow]) - np.asarray(want["out"]))
+    parity = {"rows_checked": len(brow), "idx_bit_exact": bool(np.array_equal(got_idx, np.asarray(want["idx"]))),
+              "max_abs": float(err.max()), "mean_abs": float(err.mean())}
+    log(f"decode median {us_median:.1f} us (min {us_min:.1f}); parity {parity}")
+    del dev, ws
+    torch.cuda.empty_cache()
+    return dict(us_median=us_median, us_min=us_min, bytes_step=bytes_step,
+                gbs=bytes_step / (us_median * 1e-6) / 1e9, parity=parity, batch=batch, s_max=s_max)
+
+
+def cpu_baseline(args, pi, tl):
+    """The oracle as it stands, on a bounded sample of rows of the same workload."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    total = sum(int(x) for x in pi.seq_lens)
+    rng = np.random.default_rng(123)
+    rows = rng.integers(0, total, 4096).tolist()
+    done = 0
+    t0 = time.perf_counter()
+    while done < len(rows) and time.perf_counter() - t0 < args.cpu_seconds:
+        tl.oracle_prefill_rows_lazy(pi, rows[done:done + 4])
+        done += 4
+    el = time.perf_counter() - t0
+    work_sample = sum(r + 1 for r in rows[:done])           # indexer work grows with the prefix length
+    work_all = total * (total + 1) / 2
+    rows_per_s = done / el
+    tokens_per_s = total / (el * work_all / work_sample)     # whole-job rate, extrapolated by work
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} uniformly drawn rows of the 128K prefill in {el:.1f}s ({rows_per_s:.2f} rows/s); "
+                      f"whole-job rate extrapolated by causal work (sum of t+1)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    import sparse_long_context_lightning_amd as dsa
+    from sparse_long_context_lightning_amd import inputs as inp
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import dsa_testlib as tl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dsa.load()
+    pre = prefill_bench(args, dsa, inp, tl)
+    dec = None if args.no_decode else decode_bench(args, dsa, inp, tl)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"], tl)
+
+    total = pre["rows_total"]
+    value = total / (pre["ms_per_step"] * 1e-3)
+    kern = pre["kern"]
+    line = {
+        "metric": "DSA prefill tokens/s at 128K (k=2048) + decode µs/step; % HBM/MFMA peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_128k_blocks16: batch 1, L=131072 causal, k=2048, indexer 64x128 bf16, "
+                               "GQA 32q/4kv heads x 128",
+                   "global_batch": 1, "seq_len": total, "top_k": 2048},
+        "fused_prefill_ms_per_step": pre["fused_ms"],
+        "kernel_ms_per_step": kern,
+        "kernel_launches_per_step": pre["launches"],
+        "roofline": {"bound": "mfma", "kernel": "indexer_prefill", "achieved": pre["idx_tflops"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "roofline_sparse_attn": {"bound": "hbm", "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": pre["attn_gbs"] / PEAK_HBM_GBS, "traffic": None},
+        "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": pre["topk_gbs"] / PEAK_HBM_GBS},
+        "parity_prefill": pre["parity"],
+        "cpu_baseline": cpu,
+    }
+    if dec is not None:
+        line["decode_us_per_step"] = dec["us_median"]
+        line["decode_us_min"] = dec["us_min"]
+        line["decode_config"] = {"workload": "decode_b32_128k: batch 32, 131072-token caches, k=2048"}
+        line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": dec["gbs"] / PEAK_HBM_GBS}
+        line["parity_decode"] = dec["parity"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
