@@ -29,6 +29,8 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results stay in VGPRs so the fused epilogues read them without accvgpr moves.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -39,6 +39,11 @@ __device__ __forceinline__ float round_bf16(float a) {
   return __uint_as_float(u);
 }
 
+// max(x, 0) as one integer max on the bit pattern: negative floats (and -0) are negative
+// int32 values, non-negative floats pass through unchanged.  Avoids the NaN-quieting
+// canonicalisation an IEEE-mode fmaxf carries.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
 // Order-preserving map float -> uint32 (larger float -> larger key).  -0.0 is folded into

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         for (int rt = 0; rt < 4; ++rt) {
           const int slot = (H >= 16) ? (16 * rt) / H : rt;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part[st][slot] = fmaf(fmaxf(c[rt][i], 0.f), wreg[rt][i], part[st][slot]);
+          for (int i = 0; i < 4; ++i) part[st][slot] = fmaf(relu(c[rt][i]), wreg[rt][i], part[st][slot]);
         }
       }
       if constexpr (H >= 16) {
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(fmaxf(c[rt][i], 0.f), wreg[rt][i], acc);
+        for (int i = 0; i < 4; ++i) acc = fmaf(relu(c[rt][i]), wreg[rt][i], acc);
       part[st] = acc;
     }
     const float v = transpose_reduce4(part[0], part[1], part[2], part[3], lane);

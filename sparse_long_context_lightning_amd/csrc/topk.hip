@@ -6,19 +6,17 @@
 // equal scores the lower position; the positions are returned in ascending order.
 //
 // Scores are mapped to order-preserving 32-bit keys (-0 folded into +0).  Per row:
-//   1. a strided sample of 4096 scores gives the key range [lo, hi] the row occupies, which
-//      defines 4094 equal-width buckets plus one below and one above the range, so the LDS
-//      histogram spreads over many bins (few atomic collisions) even when scores cluster;
-//   2. one pass builds the bucket histogram and finds the bucket b* holding the k-th key;
-//   3. one ordered pass (block-wide scans keep position order) collects every position of a
-//      bucket above b* (all selected) and every candidate of b* into LDS;
-//   4. an 8-bit radix select over the candidates finds the exact k-th key tau and how many
-//      positions equal to tau are taken; candidates are kept in position order, so the lowest
-//      such positions win;
-//   5. the two ascending lists are merged into the output.
-// Rows whose candidate bucket overflows LDS (long runs of equal scores) fall back to an exact
-// radix select over global memory followed by an ordered emit pass.  The result does not
-// depend on the path taken or on thread timing.
+//   1. a jittered stratified sample of up to 8192 keys (the whole row when it is that short)
+//      goes to LDS, and an 8-bit radix select over it picks a threshold tau_lo that the true
+//      k-th key clears with a wide margin (the whole-row case gives the exact k-th key);
+//   2. ONE ordered pass over the row (loads run one round ahead of the scans) (block-wide scans keep position order) copies every
+//      position with key >= tau_lo, with its key, into LDS;
+//   3. an 8-bit radix select over those candidates finds the exact k-th key tau and how many
+//      positions equal to tau are taken; a last ordered pass over the candidates writes the
+//      selected positions, which come out ascending, lowest positions winning ties.
+// If the sample misjudged the row (fewer than k candidates, or more than LDS holds, e.g. long
+// runs of equal scores), the row falls back to an exact radix select over global memory and an
+// ordered emit pass.  The result does not depend on the path taken or on thread timing.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,21 +25,15 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;
-constexpr int kCap = 8192;
-constexpr int kSample = 4096;
+constexpr int kCap = 8192;  // candidate capacity (and sample size)
+constexpr int kPer = 8;     // consecutive positions per thread in the ordered pass
 
 struct TopkSmem {
-  uint32_t hist[kBins];
-  uint32_t cand_key[kCap];
+  uint32_t cand_key[kCap];  // holds the sample first, then the candidates' keys
   int cand_pos[kCap];
-  uint32_t sel_key[kMaxTopK];
-  int sel_pos[kMaxTopK];
-  uint32_t sel2_key[kMaxTopK];
-  int sel2_pos[kMaxTopK];
+  uint32_t hist[256];
   uint32_t wsum[kWaves];
-  uint32_t red[2][kWaves];
-  uint32_t bstar, n_above, digit, digit_above;
+  uint32_t digit, digit_above;
 };
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -83,37 +75,88 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
   }
 }
 
-// Given a histogram of nbins bins (high bins = large keys) and a rank `need` (1-based, counted
-// from the top), find the bin holding that rank and the count strictly above it.  Bins are
-// scanned from the top in per-thread runs.  Contains barriers.
-__device__ void find_rank_bin(const uint32_t* hist, int nbins, uint32_t need, TopkSmem& sm, uint32_t* out_bin,
-                              uint32_t* out_above) {
-  const int per = (nbins + kThreads - 1) / kThreads;  // bins per thread
-  const int tid = threadIdx.x;
-  // Thread tid owns bins [nbins - per*(tid+1), nbins - per*tid), scanned high to low.
-  const int hi = nbins - per * tid;
-  uint32_t local = 0;
-  for (int j = 0; j < per; ++j) {
-    const int b = hi - 1 - j;
-    if (b >= 0) local += hist[b];
-  }
+// In the 256-bin histogram (high bins = large keys) find the bin holding rank `need` counted
+// from the top (1-based) and the count strictly above it.  Contains barriers.
+__device__ void find_rank_bin(TopkSmem& sm, uint32_t need) {
+  const int b = 255 - (int)threadIdx.x;  // thread t owns bin 255 - t (threads >= 256 own none)
+  const uint32_t c = (b >= 0) ? sm.hist[b] : 0u;
   uint32_t tot;
-  uint32_t run = block_excl_scan(local, sm.wsum, tot);
-  for (int j = 0; j < per; ++j) {
-    const int b = hi - 1 - j;
-    if (b < 0) break;
-    const uint32_t c = hist[b];
-    if (run < need && run + c >= need) {
-      *out_bin = (uint32_t)b;
-      *out_above = run;
-    }
-    run += c;
+  const uint32_t run = block_excl_scan(c, sm.wsum, tot);
+  if (b >= 0 && run < need && run + c >= need) {
+    sm.digit = (uint32_t)b;
+    sm.digit_above = run;
   }
   __syncthreads();
 }
 
-__device__ __forceinline__ uint32_t bucket_of(uint32_t key, uint32_t lo, uint32_t hi, uint32_t shift) {
-  return key < lo ? 0u : (key > hi ? (uint32_t)(kBins - 1) : 1u + ((key - lo) >> shift));
+// The need-th largest of the keys produced by key_at(i), i < count, and how many keys equal
+// to it complete `need` together with all larger keys.  Contains barriers.
+template <typename KeyAt>
+__device__ void radix_select(TopkSmem& sm, KeyAt key_at, uint32_t count, uint32_t need, uint32_t* tau,
+                             uint32_t* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sm.hist[tid] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < count; i += kThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift) & 255u);
+    }
+    __syncthreads();
+    find_rank_bin(sm, need);
+    prefix |= sm.digit << shift;
+    mask |= 255u << shift;
+    need -= sm.digit_above;
+    __syncthreads();
+  }
+  *tau = prefix;
+  *n_eq = need;
+}
+
+// Ordered selection over count items (key_at, pos_at), position order = item order: emit
+// key > tau, and key == tau while fewer than n_eq such items were emitted.  Contains barriers.
+template <typename KeyAt, typename PosAt>
+__device__ void emit_ordered(TopkSmem& sm, KeyAt key_at, PosAt pos_at, uint32_t count, uint32_t tau, uint32_t n_eq,
+                             int* out, float* vout) {
+  uint32_t written = 0, eq_seen = 0;
+  for (uint32_t base = 0; base < count; base += 4 * kThreads) {
+    const uint32_t i0 = base + 4 * threadIdx.x;
+    uint32_t key[4];
+    uint32_t ce = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      key[c] = (i0 + c < count) ? key_at(i0 + c) : 0u;
+      ce += (i0 + c < count && key[c] == tau) ? 1u : 0u;
+    }
+    uint32_t tot_e;
+    uint32_t rank = eq_seen + block_excl_scan(ce, sm.wsum, tot_e);
+    bool take[4];
+    uint32_t cs = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      take[c] = false;
+      if (i0 + c >= count) continue;
+      if (key[c] > tau) {
+        take[c] = true;
+      } else if (key[c] == tau) {
+        take[c] = rank < n_eq;
+        ++rank;
+      }
+      cs += take[c] ? 1u : 0u;
+    }
+    uint32_t tot_s;
+    uint32_t os = written + block_excl_scan(cs, sm.wsum, tot_s);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (take[c]) {
+        out[os] = pos_at(i0 + c);
+        if (vout) vout[os] = key_float(key[c]);
+        ++os;
+      }
+    written += tot_s;
+    eq_seen += tot_e;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores, long long ld, int rows,
@@ -136,256 +179,90 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     return;
   }
 
-  // 1. Key range from a strided sample.
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  {
-    const int ns = n < kSample ? n : kSample;
-    for (int i = tid; i < ns; i += kThreads) {
-      const long long p = (long long)i * n / ns;
-      const uint32_t key = float_key(src[p]);
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
+  // 1. Threshold from a sample (jittered strata; the whole row if it fits).
+  const int m = n < kCap ? n : kCap;
+  const int stride = n / m;  // >= 1
+  for (int i = tid; i < m; i += kThreads) {
+    int p = i;
+    if (m < n) {
+      const uint32_t h = (uint32_t)i * 2654435761u;
+      p = min((int)((long long)i * n / m) + (int)((h >> 8) % (uint32_t)stride), n - 1);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-    }
-    if (lane_id() == 0) {
-      sm.red[0][wave_id()] = kmin;
-      sm.red[1][wave_id()] = kmax;
-    }
-    for (int i = tid; i < kBins; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
-    kmin = 0xFFFFFFFFu;
-    kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      kmin = min(kmin, sm.red[0][i]);
-      kmax = max(kmax, sm.red[1][i]);
-    }
+    sm.cand_key[i] = float_key(src[p]);
   }
-  const uint32_t lo = kmin, hi = kmax;
-  uint32_t shift = 0;
-  while (((hi - lo) >> shift) > (uint32_t)(kBins - 3)) ++shift;
+  __syncthreads();
+  uint32_t r;
+  if (m == n) {
+    r = (uint32_t)k;
+  } else {
+    const float e = (float)m * (float)k / (float)n;
+    r = (uint32_t)fminf((float)m, 1.5f * e + 4.f * sqrtf(e) + 16.f);
+  }
+  uint32_t tau_lo, unused;
+  radix_select(sm, [&](uint32_t i) { return sm.cand_key[i]; }, (uint32_t)m, r, &tau_lo, &unused);
 
-  // 2. Bucket histogram (coalesced float4 reads; order does not matter here).
+  // 2. One ordered pass: every position with key >= tau_lo, in position order.  Thread t owns
+  //    kPer consecutive positions per round; the next round's loads are issued before this
+  //    round's scan.
   const int n4 = (n + 3) >> 2;
   const float4* src4 = reinterpret_cast<const float4*>(src);
-  for (int base = 0; base < n4; base += 4 * kThreads) {
-    float4 v[4];
+  auto load_round = [&](int base, float4 (&v)[kPer / 4]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * kThreads + tid;
-      if (i < n4) v[u] = src4[i];
+    for (int u = 0; u < kPer / 4; ++u) {
+      const int i4 = ((base + kPer * tid) >> 2) + u;
+      v[u] = (i4 < n4) ? src4[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  uint32_t n_cand = 0;
+  float4 cur[kPer / 4], nxt[kPer / 4];
+  load_round(0, cur);
+  for (int base = 0; base < n; base += kPer * kThreads) {
+    if (base + kPer * kThreads < n) load_round(base + kPer * kThreads, nxt);
+    const int p0 = base + kPer * tid;
+    uint32_t key[kPer];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < kPer / 4; ++u) {
+      key[4 * u + 0] = float_key(cur[u].x);
+      key[4 * u + 1] = float_key(cur[u].y);
+      key[4 * u + 2] = float_key(cur[u].z);
+      key[4 * u + 3] = float_key(cur[u].w);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = base + u * kThreads + tid;
-      if (i < n4) {
-        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (4 * i + c < n) hist_add(sm.hist, bucket_of(float_key(e[c]), lo, hi, shift));
-      }
-    }
-  }
-  __syncthreads();
-  find_rank_bin(sm.hist, kBins, (uint32_t)k, sm, &sm.bstar, &sm.n_above);
-  const uint32_t bstar = sm.bstar;
-
-  // 3. Ordered collection: thread tid owns 16 consecutive positions per round.
-  uint32_t n_sel = 0, n_cand = 0;
-  for (int base = 0; base < n; base += 16 * kThreads) {
-    const int p0 = base + 16 * tid;
-    float e[16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i4 = (p0 >> 2) + u;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i4 < n4) v = src4[i4];
-      e[4 * u + 0] = v.x;
-      e[4 * u + 1] = v.y;
-      e[4 * u + 2] = v.z;
-      e[4 * u + 3] = v.w;
-    }
-    uint32_t key[16];
-    uint32_t ca = 0, cc = 0;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      key[c] = float_key(e[c]);
-      const uint32_t b = bucket_of(key[c], lo, hi, shift);
-      const bool valid = p0 + c < n;
-      ca += (valid && b > bstar) ? 1u : 0u;
-      cc += (valid && b == bstar) ? 1u : 0u;
-    }
+    for (int c = 0; c < kPer; ++c) cnt += (p0 + c < n && key[c] >= tau_lo) ? 1u : 0u;
     uint32_t tot;
-    const uint32_t off = block_excl_scan(ca | (cc << 16), sm.wsum, tot);
-    uint32_t oa = n_sel + (off & 0xFFFFu), oc = n_cand + (off >> 16);
+    uint32_t o = n_cand + block_excl_scan(cnt, sm.wsum, tot);
+    if (cnt) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      if (p0 + c >= n) break;
-      const uint32_t b = bucket_of(key[c], lo, hi, shift);
-      if (b > bstar) {
-        sm.sel_key[oa] = key[c];
-        sm.sel_pos[oa] = p0 + c;
-        ++oa;
-      } else if (b == bstar) {
-        if (oc < (uint32_t)kCap) {
-          sm.cand_key[oc] = key[c];
-          sm.cand_pos[oc] = p0 + c;
+      for (int c = 0; c < kPer; ++c) {
+        if (p0 + c < n && key[c] >= tau_lo) {
+          if (o < (uint32_t)kCap) {
+            sm.cand_key[o] = key[c];
+            sm.cand_pos[o] = p0 + c;
+          }
+          ++o;
         }
-        ++oc;
       }
     }
-    n_sel += tot & 0xFFFFu;
-    n_cand += tot >> 16;
+    n_cand += tot;
+#pragma unroll
+    for (int u = 0; u < kPer / 4; ++u) cur[u] = nxt[u];
   }
   __syncthreads();
 
-  if (n_cand <= (uint32_t)kCap) {
-    // 4. Exact k-th key among the candidates: four 8-bit radix rounds in LDS.
-    uint32_t need = (uint32_t)k - n_sel;  // >= 1
-    uint32_t prefix = 0, mask = 0;
-    for (int shift8 = 24; shift8 >= 0; shift8 -= 8) {
-      for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < n_cand; i += kThreads) {
-        const uint32_t key = sm.cand_key[i];
-        if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift8) & 255u);
-      }
-      __syncthreads();
-      find_rank_bin(sm.hist, 256, need, sm, &sm.digit, &sm.digit_above);
-      prefix |= sm.digit << shift8;
-      mask |= 255u << shift8;
-      need -= sm.digit_above;
-    }
-    const uint32_t tau = prefix;
-    const uint32_t n_eq = need;  // positions equal to tau that are taken (lowest first)
-
-    // Candidates in position order: select key > tau, or key == tau within the first n_eq.
-    uint32_t n_sel2 = 0, eq_seen = 0;
-    for (uint32_t base = 0; base < n_cand; base += 4 * kThreads) {
-      const uint32_t i0 = base + 4 * tid;
-      uint32_t key[4];
-      int pos[4];
-      uint32_t ce = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool valid = i0 + c < n_cand;
-        key[c] = valid ? sm.cand_key[i0 + c] : 0u;
-        pos[c] = valid ? sm.cand_pos[i0 + c] : -1;
-        ce += (valid && key[c] == tau) ? 1u : 0u;
-      }
-      uint32_t tot_e;
-      const uint32_t off_e = block_excl_scan(ce, sm.wsum, tot_e);
-      uint32_t rank = eq_seen + off_e;
-      uint32_t cs = 0;
-      bool take[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        take[c] = false;
-        if (pos[c] < 0) continue;
-        if (key[c] > tau) take[c] = true;
-        else if (key[c] == tau) {
-          take[c] = rank < n_eq;
-          ++rank;
-        }
-        cs += take[c] ? 1u : 0u;
-      }
-      uint32_t tot_s;
-      uint32_t os = n_sel2 + block_excl_scan(cs, sm.wsum, tot_s);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (take[c]) {
-          sm.sel2_key[os] = key[c];
-          sm.sel2_pos[os] = pos[c];
-          ++os;
-        }
-      n_sel2 += tot_s;
-      eq_seen += tot_e;
-    }
-    __syncthreads();
-
-    // 5. Merge the two ascending position lists (positions are distinct).
-    for (uint32_t i = tid; i < n_sel; i += kThreads) {
-      const int p = sm.sel_pos[i];
-      uint32_t a = 0, b = n_sel2;
-      while (a < b) {
-        const uint32_t m = (a + b) >> 1;
-        if (sm.sel2_pos[m] < p) a = m + 1; else b = m;
-      }
-      out[i + a] = p;
-      if (vout) vout[i + a] = key_float(sm.sel_key[i]);
-    }
-    for (uint32_t j = tid; j < n_sel2; j += kThreads) {
-      const int p = sm.sel2_pos[j];
-      uint32_t a = 0, b = n_sel;
-      while (a < b) {
-        const uint32_t m = (a + b) >> 1;
-        if (sm.sel_pos[m] < p) a = m + 1; else b = m;
-      }
-      out[j + a] = p;
-      if (vout) vout[j + a] = key_float(sm.sel2_key[j]);
-    }
+  uint32_t tau, n_eq;
+  if (n_cand >= (uint32_t)k && n_cand <= (uint32_t)kCap) {
+    // 3. Exact k-th key among the candidates, then the ordered selection.
+    radix_select(sm, [&](uint32_t i) { return sm.cand_key[i]; }, n_cand, (uint32_t)k, &tau, &n_eq);
+    emit_ordered(sm, [&](uint32_t i) { return sm.cand_key[i]; }, [&](uint32_t i) { return sm.cand_pos[i]; }, n_cand,
+                 tau, n_eq, out, vout);
     return;
   }
 
   // Fallback: exact radix select over global memory, then an ordered emit pass.
-  uint32_t need = (uint32_t)k;
-  uint32_t prefix = 0, mask = 0;
-  for (int shift8 = 24; shift8 >= 0; shift8 -= 8) {
-    for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t key = float_key(src[i]);
-      if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift8) & 255u);
-    }
-    __syncthreads();
-    find_rank_bin(sm.hist, 256, need, sm, &sm.digit, &sm.digit_above);
-    prefix |= sm.digit << shift8;
-    mask |= 255u << shift8;
-    need -= sm.digit_above;
-  }
-  const uint32_t tau = prefix;
-  const uint32_t n_eq = need;
-  uint32_t written = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += 4 * kThreads) {
-    const int p0 = base + 4 * tid;
-    uint32_t key[4];
-    uint32_t ce = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      key[c] = (p0 + c < n) ? float_key(src[p0 + c]) : 0u;
-      ce += (p0 + c < n && key[c] == tau) ? 1u : 0u;
-    }
-    uint32_t tot_e;
-    uint32_t rank = eq_seen + block_excl_scan(ce, sm.wsum, tot_e);
-    bool take[4];
-    uint32_t cs = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      take[c] = false;
-      if (p0 + c >= n) continue;
-      if (key[c] > tau) take[c] = true;
-      else if (key[c] == tau) {
-        take[c] = rank < n_eq;
-        ++rank;
-      }
-      cs += take[c] ? 1u : 0u;
-    }
-    uint32_t tot_s;
-    uint32_t os = written + block_excl_scan(cs, sm.wsum, tot_s);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (take[c]) {
-        out[os] = p0 + c;
-        if (vout) vout[os] = key_float(key[c]);
-        ++os;
-      }
-    written += tot_s;
-    eq_seen += tot_e;
-  }
+  radix_select(sm, [&](uint32_t i) { return float_key(src[i]); }, (uint32_t)n, (uint32_t)k, &tau, &n_eq);
+  emit_ordered(sm, [&](uint32_t i) { return float_key(src[i]); }, [&](uint32_t i) { return (int)i; }, (uint32_t)n,
+               tau, n_eq, out, vout);
 }
 
 }  // namespace

@@ -125,6 +125,19 @@ def test_topk_special_rows(dsa):
     assert idx[2].tolist() == list(range(n - k, n))
 
 
+def test_topk_rows_that_overflow_the_candidate_buffer(dsa):
+    # long runs of equal scores: more than 8192 positions tie at the threshold, so the row
+    # takes the exact global-memory path; the result must still be the unique lowest-position set
+    rng = np.random.default_rng(21)
+    ld, k = 50000, 2048
+    rows = [np.zeros(ld), (rng.random(ld) < 0.5).astype(np.float64), np.repeat(np.arange(10.0), ld // 10),
+            rng.integers(0, 3, ld).astype(np.float64)]
+    scores = np.stack(rows).astype(np.float32)
+    lens = [ld, ld, ld, 20000]
+    idx, val = _run_topk(dsa, scores, lens, k)
+    _check_topk(scores, lens, k, idx, val)
+
+
 def test_topk_long_rows(dsa):
     rng = np.random.default_rng(9)
     ld, k = 131072, 2048
