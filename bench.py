@@ -34,6 +34,22 @@ PREFILL = "c3_prefill_128k"
 DECODE = "c4_decode_b32_128k"
 
 
+def counter_traffic(kernel_key):
+    """HBM bytes per launch (read + write, calibrated) from the committed counter runs, or None
+    when the kernel source changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        data = json.load(open(path))
+        ent = data["kernels"][kernel_key]
+        cur = hashlib.sha256(open(os.path.join(ROOT, ent["source"]), "rb").read()).hexdigest()[:16]
+        if cur != ent["sha256_16"]:
+            return None
+        return (ent["read_gb_per_launch"] + ent["write_gb_per_launch"]) * 1e9
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -326,9 +342,14 @@ def main():
         "kernel_launches_per_step": pre["launches"],
         "roofline": {"bound": "mfma", "kernel": "indexer_prefill", "achieved": pre["idx_tflops"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": counter_traffic("indexer_prefill_kernel@prefill_128k"),
+                     "traffic_unit": "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)",
+                     "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
+                     "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]},
         "roofline_sparse_attn": {"bound": "hbm", "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": pre["attn_gbs"] / PEAK_HBM_GBS, "traffic": None},
+                                 "frac": pre["attn_gbs"] / PEAK_HBM_GBS,
+                                 "traffic": counter_traffic("sparse_attn_kernel@prefill_128k"),
+                                 "algorithmic_bytes_per_launch": pre["attn_bytes"]},
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pre["topk_gbs"] / PEAK_HBM_GBS},
         "parity_prefill": pre["parity"],
