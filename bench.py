@@ -134,10 +134,11 @@ def prefill_bench(args, dsa, inp, tl):
     cu = pi.cu_seqlens
     ws_bytes = dsa.dsa_prefill_workspace_size(len(lens), total, max_seqlen, hq, hkv, d, h_idx, d_idx, k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    chunk = min(ws_bytes // 4 // ld, total)
-    if chunk > 64:
-        chunk = chunk // 64 * 64
+    chunk = min(total, 2048)   # the default chunk dsa_prefill_workspace_size provides for
     scores = ws.view(torch.float32)[: chunk * ld].view(chunk, ld)
+    # Same carving as dsa_prefill: the chunk's scores, then the top-k scratch (256-byte aligned).
+    topk_off = (chunk * ld * 4 + 255) // 256 * 256
+    topk_ws = ws[topk_off:]
     out = torch.empty_like(dev["q"])
     lse = torch.empty(total, hq, dtype=torch.float32, device="cuda")
     idx = torch.empty(total, k, dtype=torch.int32, device="cuda")
@@ -153,7 +154,7 @@ def prefill_bench(args, dsa, inp, tl):
                 dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, c1 - c0, scores, ld=ld)
                 timer.stop(tok)
                 tok = timer.start("topk")
-                dsa.dsa_topk(scores, row_len[c0:c1], k, idx[c0:c1], ld=ld)
+                dsa.dsa_topk(scores, row_len[c0:c1], k, idx[c0:c1], workspace=topk_ws, ld=ld)
                 timer.stop(tok)
         tok = timer.start("sparse_attn")
         dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out, lse)
@@ -193,7 +194,7 @@ def prefill_bench(args, dsa, inp, tl):
     idx_flops = pairs * 2 * h_idx * d_idx
     sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
     attn_bytes = sel_pairs * (2 * hkv * d * 2 + 4) + total * (2 * hq * d * 2 + 4 * hq)
-    topk_bytes = pairs * 4 * 2 + total * k * 4   # two passes over each row's scores + index write
+    topk_bytes = pairs * 4 + total * k * 4   # one pass over each row's scores + index write
     idx_tflops = idx_flops / (kern["indexer"] * 1e-3) / 1e12
     attn_gbs = attn_bytes / (kern["sparse_attn"] * 1e-3) / 1e9
     topk_gbs = topk_bytes / (kern["topk"] * 1e-3) / 1e9

@@ -88,7 +88,8 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w,
                      int h_idx, int d_idx, int row_begin, int row_count,
                      float* scores, int64_t ld, void* stream);
 
-/* Bytes of workspace dsa_topk needs (currently 0; kept so callers can size it once). */
+/* Bytes of scratch the fast dsa_topk path uses for `rows` rows of stride ld (0 when ld > 262144,
+ * where only the scratch-free path exists). */
 int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes);
 
 /*
@@ -103,7 +104,11 @@ int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes);
  *                              the row is 0 .. row_len-1; padding is -1.  Among equal scores the
  *                              lower position wins, so the set is unique.
  * values_out [rows, k] float   optional (NULL): the scores of idx_out, same order; padding -inf.
- * workspace, workspace_bytes   at least dsa_topk_workspace_size bytes (may be NULL when 0).
+ * workspace, workspace_bytes   NULL, or at least dsa_topk_workspace_size bytes: with it, rows of
+ *                              ld <= 262144 use the wave-parallel kernels (a sampled threshold, one
+ *                              streaming pass, an exact select over the candidates); without it a
+ *                              scratch-free row-per-workgroup kernel runs.  Both give the same result.
+ *                              A non-NULL workspace below the needed size is DSA_ERR_WORKSPACE.
  */
 int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k,
              int32_t* idx_out, float* values_out, void* workspace, size_t workspace_bytes,
@@ -127,7 +132,8 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
 
 /*
  * Workspace bytes for dsa_prefill: a score buffer for a chunk of query rows (never the whole
- * L x L matrix) plus small per-row tables.  A larger workspace lets the call use larger chunks.
+ * L x L matrix) plus the top-k scratch of those rows; the default chunk is 2048 rows.  A larger
+ * workspace lets the call use larger chunks, a smaller one (down to 64 rows) smaller ones.
  */
 int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv,
                                int head_dim, int h_idx, int d_idx, int top_k, size_t* bytes);
@@ -141,8 +147,9 @@ int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int 
  * max_seqlen                    >= the longest sequence
  * out [total_tokens, hq, head_dim] bf16, lse [total_tokens, hq] float or NULL
  * idx_out [total_tokens, top_k] int32   the selected positions (required)
- * workspace                     >= dsa_prefill_workspace_size(...) for the smallest chunk the call
- *                               accepts (64 rows x max_seqlen floats); size it with that function.
+ * workspace                     the call uses the largest chunk of rows whose scores and top-k
+ *                               scratch fit; it must hold at least a 64-row chunk (or all rows if
+ *                               fewer).  dsa_prefill_workspace_size gives the 2048-row default.
  */
 int dsa_prefill(const void* q, const void* k, const void* v,
                 const void* q_idx, const void* k_idx, const float* w,

@@ -88,6 +88,15 @@ constexpr int kDecodeKeysPerWave = 512;
 constexpr int kMinChunkRows = 64;
 constexpr int kDefaultChunkRows = 2048;
 
+size_t topk_scratch(int rows, long long ld) {
+  return ld <= dsa::kTopkWaveMaxLd ? round_up((long long)dsa::topk_wave_workspace_bytes(rows), 256) : 0;
+}
+
+// Workspace of one prefill chunk: its fp32 score rows, then the top-k scratch.
+size_t prefill_chunk_bytes(int rows, long long ld) {
+  return (size_t)round_up((long long)rows * ld * 4, 256) + topk_scratch(rows, ld);
+}
+
 int decode_nsplit(int batch, int hkv, int top_k) {
   const int nchunk = (top_k + 31) / 32;
   const int want = (2048 + batch * hkv - 1) / (batch * hkv);
@@ -173,14 +182,12 @@ int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes) {
   DSA_NONNULL(bytes);
   if (rows < 0 || ld < 0) return fail(DSA_ERR_INVALID_ARG, "rows and ld must be non-negative");
   DSA_TRY(check_topk(k));
-  *bytes = 0;
+  *bytes = topk_scratch(rows, ld);
   return DSA_OK;
 }
 
 int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
              float* values_out, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   g_last_error[0] = 0;
   DSA_NONNULL(scores);
   DSA_NONNULL(row_len);
@@ -189,7 +196,11 @@ int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, 
   if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "rows must be non-negative");
   if (ld <= 0 || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "ld (%lld) must be a positive multiple of 4", (long long)ld);
   DSA_TRY(check_topk(k));
+  DSA_ALIGNED(workspace);
   if (rows == 0) return DSA_OK;
+  const size_t need = topk_scratch(rows, ld);
+  if (workspace && workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
   dsa::TopkArgs a;
   a.scores = scores;
   a.ld = ld;
@@ -199,6 +210,7 @@ int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, 
   a.k = k;
   a.idx_out = idx_out;
   a.values_out = values_out;
+  a.workspace = need ? workspace : nullptr;
   return hip_status(dsa::launch_topk(a, static_cast<hipStream_t>(stream)), "top-k launch");
 }
 
@@ -249,8 +261,8 @@ int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int 
   DSA_TRY(check_indexer_shape(h_idx, d_idx));
   DSA_TRY(check_topk(top_k));
   const long long ld = round_up(std::max(max_seqlen, 1), 4);
-  const long long rows = std::max(1, std::min(total_tokens, kDefaultChunkRows));
-  *bytes = (size_t)(rows * ld * 4);
+  const int rows = std::max(1, std::min(total_tokens, kDefaultChunkRows));
+  *bytes = prefill_chunk_bytes(rows, ld);
   return DSA_OK;
 }
 
@@ -286,15 +298,19 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
     return fail(DSA_ERR_INVALID_ARG, "max_seqlen (%d) is below the longest sequence (%d)", max_seqlen, max_len);
   if (total_tokens == 0) return DSA_OK;
   const long long ld = round_up(std::max(max_seqlen, 1), 4);
-  const long long min_rows = std::min(total_tokens, kMinChunkRows);
-  if (!workspace || (long long)(workspace_bytes / 4 / ld) < min_rows)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes holds fewer than %lld score rows of %lld", workspace_bytes,
-                min_rows, ld);
-  long long chunk = (long long)(workspace_bytes / 4 / ld);
-  chunk = std::min<long long>(chunk, total_tokens);
+  const int min_rows = std::min(total_tokens, kMinChunkRows);
+  if (!workspace || workspace_bytes < prefill_chunk_bytes(min_rows, ld))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes of the smallest chunk (%d rows)",
+                workspace_bytes, prefill_chunk_bytes(min_rows, ld), min_rows);
+  // Largest chunk (a multiple of 64 rows when above 64) whose scores and top-k scratch fit.
+  long long chunk = std::min<long long>(total_tokens, (long long)(workspace_bytes / (ld * 4)));
+  while (chunk > min_rows && prefill_chunk_bytes((int)chunk, ld) > workspace_bytes) --chunk;
   if (chunk > 64) chunk = chunk / 64 * 64;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = static_cast<float*>(workspace);
+  void* topk_ws = topk_scratch((int)chunk, ld)
+                      ? static_cast<void*>(static_cast<char*>(workspace) + round_up(chunk * ld * 4, 256))
+                      : nullptr;
 
   for (int b = 0; b < batch; ++b) {
     const int o = cu_seqlens_host[b], e = cu_seqlens_host[b + 1];
@@ -310,6 +326,7 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
       t.k = top_k;
       t.idx_out = idx_out + (size_t)c0 * top_k;
       t.values_out = nullptr;
+      t.workspace = topk_ws;
       DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
     }
   }
@@ -344,7 +361,7 @@ int dsa_decode_workspace_size(int batch, int s_max, int hq, int hkv, int head_di
   const long long nsplit = decode_nsplit(batch, hkv, top_k);
   const long long score_bytes = (long long)batch * ld * 4;
   const long long part_bytes = (long long)batch * hq * nsplit * (128 + 2) * 4;
-  *bytes = (size_t)(round_up(score_bytes, 256) + part_bytes);
+  *bytes = (size_t)(round_up(score_bytes, 256) + topk_scratch(batch, ld) + part_bytes);
   return DSA_OK;
 }
 
@@ -384,7 +401,9 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   const long long ld = round_up(s_max, 4);
   const int nsplit = decode_nsplit(batch, hkv, top_k);
   float* scores = static_cast<float*>(workspace);
-  float* part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up((long long)batch * ld * 4, 256));
+  char* after_scores = static_cast<char*>(workspace) + round_up((long long)batch * ld * 4, 256);
+  void* topk_ws = topk_scratch(batch, ld) ? static_cast<void*>(after_scores) : nullptr;
+  float* part_o = reinterpret_cast<float*>(after_scores + topk_scratch(batch, ld));
   float* part_ml = part_o + (size_t)batch * hq * nsplit * 128;
 
   dsa::IndexerDecodeArgs ia;
@@ -411,6 +430,7 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   t.k = top_k;
   t.idx_out = idx_out;
   t.values_out = nullptr;
+  t.workspace = topk_ws;
   DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
 
   dsa::SparseAttnArgs a = {};

@@ -40,7 +40,14 @@ struct TopkArgs {
   int k;
   int* idx_out;       // [rows, k] at row stride k
   float* values_out;  // optional
+  void* workspace;    // >= topk_wave_workspace_bytes(rows) selects the wave-parallel kernels; may be null
 };
+
+// Scratch of the wave-parallel top-k (per-row threshold, counter and candidate list).
+size_t topk_wave_workspace_bytes(int rows);
+// Longest row (ld) the wave-parallel top-k handles; longer rows use the row-block kernel.
+constexpr long long kTopkWaveMaxLd = 262144;
+hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s);
 
 // Row r: prefill mode (seq_lens == nullptr) finds its sequence in cu_seqlens, decode mode uses
 // sequence r with kv rows starting at r * s_max and valid length seq_lens[r].

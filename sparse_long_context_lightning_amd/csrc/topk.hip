@@ -1,4 +1,6 @@
-// Deterministic per-row top-k for gfx950 (one 1024-thread workgroup per row).
+// Deterministic per-row top-k for gfx950, row-block form (one 1024-thread workgroup per row).
+// Used for rows longer than the wave-parallel kernels of topk_wave.hip handle, or when the
+// caller passes no scratch.
 //
 // The digest of the Keye-VL-2.0 report (mqxn.cn news 1966) keeps the 2048 best positions per
 // query token (section 一) and requires the selection to be deterministic so training and
@@ -269,6 +271,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
+  if (a.workspace && a.ld <= kTopkWaveMaxLd) return launch_topk_wave(a, s);
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.rows), dim3(kThreads), 0, s, a.scores, a.ld, a.rows, a.row_len,
                      a.len_base, a.k, a.idx_out, a.values_out);
   return hipGetLastError();

@@ -1,0 +1,428 @@
+// Deterministic per-row top-k for gfx950, wave-parallel form (rows up to 262144 scores).
+//
+// Same contract as the row-block kernel in topk.hip (the Keye-VL-2.0 report digest, mqxn.cn
+// news 1966: 2048 best positions per query in section 一, deterministic selection in section
+// 八): the unique set "larger score first, lower position among equals", returned ascending.
+//
+// Three launches, none of which needs a workgroup barrier while streaming the row:
+//   1. threshold: one wave per row takes a jittered stratified sample of up to 4096 scores
+//      (64 per lane, in registers) and runs an 8-bit radix select on it with a wave-private LDS
+//      histogram; the result tau_lo is a key that the row's true k-th key clears with a wide
+//      statistical margin (for rows of at most 4096 scores the sample is the row and tau_lo is
+//      exactly the k-th key).  It also clears the row's candidate counter;
+//   2. collect: one wave per (row, segment) streams its segment once (next loads in flight
+//      while the current ones are filtered) and appends every (key, position) with
+//      key >= tau_lo to a wave-private LDS stage, flushed to the row's global candidate list
+//      with one atomic reservation per flush.  Candidate order does not matter;
+//   3. select: one 256-thread workgroup per row loads the candidates into LDS, finds the exact
+//      k-th key tau and the number n_eq of positions equal to tau to take by an 8-bit radix
+//      select, marks positions equal to tau in an LDS bitmap to find the n_eq-th lowest one,
+//      then marks every selected position and writes the bitmap's set bits in ascending order.
+// A row whose candidates number fewer than k or more than the list holds is redone exactly
+// from global memory inside the select kernel.  No result depends on the path or on timing.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kCapW = 6144;       // candidate list length per row
+constexpr int kSampleW = 4096;    // sample size (64 per lane)
+constexpr int kStage = 512;       // per-wave LDS stage of the collect kernel
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / 64;
+
+__device__ __forceinline__ int lane_of() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int row_length(const int* row_len, int len_base, int row, long long ld) {
+  return max(0, (int)min((long long)(row_len ? row_len[row] : len_base + row + 1), ld));
+}
+
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int lane) {
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+// Rank threshold for a sample of m of the row's n keys: the sample's r-th largest key is
+// exceeded by the true k-th key with overwhelming probability while the number of row keys
+// at or above it stays near k * 1.25 + O(sqrt) (well inside the candidate list).
+__device__ __forceinline__ uint32_t sample_rank(int m, int n, int k) {
+  if (m == n) return (uint32_t)k;
+  const float e = (float)m * (float)k / (float)n;
+  return (uint32_t)fminf((float)m, 1.25f * e + 3.f * sqrtf(e) + 8.f);
+}
+
+// The need-th largest (1-based) of the sample keys held 64 per lane (slot j of lane l is
+// sample l + 64 j, valid when < m).  hist is a wave-private 256-entry LDS array.
+__device__ uint32_t wave_radix_select(const uint32_t (&key)[64], int m, uint32_t need, uint32_t* hist, int lane) {
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hist[lane + 64 * q] = 0;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      if (lane + 64 * j < m && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
+    wave_lds_sync();
+    // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
+    uint32_t c[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[255 - 4 * lane - q];
+      s += c[q];
+    }
+    uint32_t run = wave_excl_scan(s, lane);
+    int found = -1;
+    uint32_t above = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (run < need && run + c[q] >= need) {
+        found = 255 - 4 * lane - q;
+        above = run;
+      }
+      run += c[q];
+    }
+    const unsigned long long b = __ballot(found >= 0);
+    const int src_lane = __builtin_ctzll(b);
+    const int digit = __shfl(found, src_lane);
+    prefix |= (uint32_t)digit << shift;
+    mask |= 255u << shift;
+    need -= __shfl(above, src_lane);
+    wave_lds_sync();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __restrict__ scores, long long ld, int rows,
+                                                             const int* __restrict__ row_len, int len_base, int k,
+                                                             uint32_t* __restrict__ tau_lo, uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t hist_all[4][256];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int n = row_length(row_len, len_base, row, ld);
+  if (lane == 0) cnt[row] = 0;
+  if (n <= k) return;
+  const float* src = scores + (size_t)row * ld;
+  const int m = min(n, kSampleW);
+  const int stride = n / m;
+  uint32_t key[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const int i = lane + 64 * j;
+    int p = i;
+    if (m < n) {
+      const uint32_t h = (uint32_t)i * 2654435761u;
+      p = min((int)((long long)i * n / m) + (int)((h >> 8) % (uint32_t)stride), n - 1);
+    }
+    key[j] = (i < m) ? float_key(src[p]) : 0u;
+  }
+  const uint32_t t = wave_radix_select(key, m, sample_rank(m, n, k), hist_all[wave], lane);
+  if (lane == 0) tau_lo[row] = t;
+}
+
+__global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restrict__ scores, long long ld, int rows,
+                                                           const int* __restrict__ row_len, int len_base, int k,
+                                                           int seg_len, int nseg, const uint32_t* __restrict__ tau_lo,
+                                                           uint32_t* __restrict__ cnt, uint2* __restrict__ cand) {
+  __shared__ uint2 stage_all[4][kStage];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + wave;
+  const int row = (int)(item / nseg);
+  const int seg = (int)(item - (long long)row * nseg);
+  if (row >= rows) return;
+  const int n = row_length(row_len, len_base, row, ld);
+  if (n <= k) return;
+  const int p0 = seg * seg_len;
+  if (p0 >= n) return;
+  const int p1 = min(n, p0 + seg_len);
+  const uint32_t tau = tau_lo[row];
+  const float* src = scores + (size_t)row * ld;
+  uint2* stage = stage_all[wave];
+  uint2* cand_row = cand + (size_t)row * kCapW;
+  uint32_t ns = 0;
+
+  auto flush = [&]() {
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&cnt[row], ns);
+    base = __shfl(base, 0);
+    wave_lds_sync();
+    for (uint32_t i = lane; i < ns; i += 64)
+      if (base + i < (uint32_t)kCapW) cand_row[base + i] = stage[i];
+    ns = 0;
+    wave_lds_sync();
+  };
+  auto load = [&](int base, float4 (&v)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int pos = base + 256 * u + 4 * lane;
+      v[u] = (pos < p1) ? *reinterpret_cast<const float4*>(src + pos) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+
+  float4 cur[4], nxt[4];
+  load(p0, cur);
+  for (int base = p0; base < p1; base += 1024) {
+    if (base + 1024 < p1) load(base + 1024, nxt);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float e[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int pos = base + 256 * u + 4 * lane + c;
+        const uint32_t key = float_key(e[c]);
+        const bool flag = pos < p1 && key >= tau;
+        const unsigned long long b = __ballot(flag);
+        if (flag) stage[ns + lanes_below(b)] = make_uint2(key, (uint32_t)pos);
+        ns += (uint32_t)__popcll(b);
+      }
+      if (ns >= (uint32_t)(kStage - 256)) flush();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+  }
+  if (ns) flush();
+}
+
+// ------------------------------------------------------------------------- select kernel
+
+struct SelSmem {
+  uint32_t hist[256];
+  uint32_t wsum[kSelWaves];
+  uint32_t digit, digit_above, pstar;
+};
+
+__device__ uint32_t block_excl_scan256(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = lane_of(), wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    const uint32_t s = wsum[i];
+    pre += (i < wave) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
+// 8-bit radix select with a 256-thread block; key_at(i) for i < count.  Contains barriers.
+template <typename KeyAt>
+__device__ void block_radix_select(SelSmem& sm, KeyAt key_at, uint32_t count, uint32_t need, uint32_t* tau,
+                                   uint32_t* n_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    sm.hist[tid] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < count; i += kSelThreads) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int b = 255 - tid;
+    const uint32_t c = sm.hist[b];
+    uint32_t tot;
+    const uint32_t run = block_excl_scan256(c, sm.wsum, tot);
+    if (run < need && run + c >= need) {
+      sm.digit = (uint32_t)b;
+      sm.digit_above = run;
+    }
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    mask |= 255u << shift;
+    need -= sm.digit_above;
+    __syncthreads();
+  }
+  *tau = prefix;
+  *n_eq = need;
+}
+
+template <int NW>
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ scores, long long ld,
+                                                                  int rows, const int* __restrict__ row_len,
+                                                                  int len_base, int k, const uint32_t* __restrict__ cnt,
+                                                                  const uint2* __restrict__ cand,
+                                                                  int* __restrict__ idx_out,
+                                                                  float* __restrict__ values_out) {
+  constexpr int WPT = NW / kSelThreads;  // bitmap words per thread (a contiguous run)
+  __shared__ uint32_t ckey[kCapW];
+  __shared__ int cpos[kCapW];
+  __shared__ uint32_t bits[NW];
+  __shared__ SelSmem sm;
+  const int tid = threadIdx.x;
+  const int row = rows - 1 - (int)blockIdx.x;
+  const int n = row_length(row_len, len_base, row, ld);
+  int* out = idx_out + (size_t)row * k;
+  float* vout = values_out ? values_out + (size_t)row * k : nullptr;
+  const float* src = scores + (size_t)row * ld;
+
+  if (n <= k) {
+    for (int i = tid; i < k; i += kSelThreads) {
+      out[i] = i < n ? i : -1;
+      if (vout) vout[i] = i < n ? key_float(float_key(src[i])) : -INFINITY;
+    }
+    return;
+  }
+  const uint32_t count = cnt[row];
+  uint32_t tau, n_eq;
+  if (count >= (uint32_t)k && count <= (uint32_t)kCapW) {
+    const uint2* cr = cand + (size_t)row * kCapW;
+    for (uint32_t i = tid; i < count; i += kSelThreads) {
+      const uint2 c = cr[i];
+      ckey[i] = c.x;
+      cpos[i] = (int)c.y;
+    }
+    __syncthreads();
+    block_radix_select(sm, [&](uint32_t i) { return ckey[i]; }, count, (uint32_t)k, &tau, &n_eq);
+
+    const int nwords = (n + 31) >> 5;
+    const int w0 = tid * WPT;
+    // Positions equal to tau: find the n_eq-th lowest.
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) bits[w0 + j] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < count; i += kSelThreads)
+      if (ckey[i] == tau) atomicOr(&bits[cpos[i] >> 5], 1u << (cpos[i] & 31));
+    __syncthreads();
+    {
+      uint32_t local = 0;
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) local += (w0 + j < nwords) ? (uint32_t)__popc(bits[w0 + j]) : 0u;
+      uint32_t tot;
+      uint32_t run = block_excl_scan256(local, sm.wsum, tot);
+      if (run < n_eq && run + local >= n_eq) {
+        for (int j = 0; j < WPT; ++j) {
+          uint32_t wbits = bits[w0 + j];
+          const uint32_t c = (uint32_t)__popc(wbits);
+          if (run + c >= n_eq) {
+            for (uint32_t skip = n_eq - run - 1; skip > 0; --skip) wbits &= wbits - 1;
+            sm.pstar = (uint32_t)((w0 + j) * 32 + __builtin_ctz(wbits));
+            break;
+          }
+          run += c;
+        }
+      }
+      __syncthreads();
+    }
+    const int pstar = (int)sm.pstar;
+    // Every selected position.
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) bits[w0 + j] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < count; i += kSelThreads) {
+      const uint32_t key = ckey[i];
+      const int p = cpos[i];
+      if (key > tau || (key == tau && p <= pstar)) atomicOr(&bits[p >> 5], 1u << (p & 31));
+    }
+    __syncthreads();
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) local += (w0 + j < nwords) ? (uint32_t)__popc(bits[w0 + j]) : 0u;
+    uint32_t tot;
+    uint32_t rank = block_excl_scan256(local, sm.wsum, tot);
+    for (int j = 0; j < WPT; ++j) {
+      uint32_t wbits = (w0 + j < nwords) ? bits[w0 + j] : 0u;
+      while (wbits) {
+        const int p = (w0 + j) * 32 + __builtin_ctz(wbits);
+        wbits &= wbits - 1;
+        out[rank] = p;
+        if (vout) vout[rank] = key_float(float_key(src[p]));
+        ++rank;
+      }
+    }
+    return;
+  }
+
+  // Fallback: exact radix select over the row itself, then an ordered emit pass.
+  block_radix_select(sm, [&](uint32_t i) { return float_key(src[i]); }, (uint32_t)n, (uint32_t)k, &tau, &n_eq);
+  uint32_t written = 0, eq_seen = 0;
+  for (int base = 0; base < n; base += 4 * kSelThreads) {
+    const int q0 = base + 4 * tid;
+    uint32_t key[4];
+    uint32_t ce = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      key[c] = (q0 + c < n) ? float_key(src[q0 + c]) : 0u;
+      ce += (q0 + c < n && key[c] == tau) ? 1u : 0u;
+    }
+    uint32_t tot_e;
+    uint32_t r = eq_seen + block_excl_scan256(ce, sm.wsum, tot_e);
+    bool take[4];
+    uint32_t cs = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      take[c] = false;
+      if (q0 + c >= n) continue;
+      if (key[c] > tau) {
+        take[c] = true;
+      } else if (key[c] == tau) {
+        take[c] = r < n_eq;
+        ++r;
+      }
+      cs += take[c] ? 1u : 0u;
+    }
+    uint32_t tot_s;
+    uint32_t os = written + block_excl_scan256(cs, sm.wsum, tot_s);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (take[c]) {
+        out[os] = q0 + c;
+        if (vout) vout[os] = key_float(key[c]);
+        ++os;
+      }
+    written += tot_s;
+    eq_seen += tot_e;
+  }
+}
+
+}  // namespace
+
+size_t topk_wave_workspace_bytes(int rows) {
+  const size_t head = ((size_t)rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+  return head + (size_t)rows * kCapW * sizeof(uint2);
+}
+
+hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
+  uint32_t* tau_lo = static_cast<uint32_t*>(a.workspace);
+  uint32_t* cnt = tau_lo + a.rows;
+  const size_t head = ((size_t)a.rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+  uint2* cand = reinterpret_cast<uint2*>(static_cast<char*>(a.workspace) + head);
+  hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a.scores, a.ld,
+                     a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
+  // Segment length: enough waves to keep every CU streaming, in multiples of 1024 positions.
+  const long long want_waves = 4096;
+  long long nseg = (want_waves + a.rows - 1) / a.rows;
+  long long seg_len = (a.ld + nseg - 1) / nseg;
+  seg_len = (seg_len + 1023) / 1024 * 1024;
+  nseg = (a.ld + seg_len - 1) / seg_len;
+  const long long items = (long long)a.rows * nseg;
+  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a.scores, a.ld, a.rows,
+                     a.row_len, a.len_base, a.k, (int)seg_len, (int)nseg, tau_lo, cnt, cand);
+  if (a.ld <= 131072)
+    hipLaunchKernelGGL((topk_select_kernel<4096>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores, a.ld,
+                       a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<8192>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores, a.ld,
+                       a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -115,13 +115,30 @@ def test_zero_sized_calls_are_no_ops():
     assert lib.dsa_topk(FAKE, 64, 0, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_OK
 
 
+def _topk_scratch(rows):
+    head = (rows * 8 + 255) // 256 * 256
+    return (head + rows * 6144 * 8 + 255) // 256 * 256
+
+
 def test_workspace_sizes():
-    assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == 0
-    # prefill: a 2048-row chunk of 131072 float scores
-    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 32, 4, 128, 64, 128, 2048) == 2048 * 131072 * 4
+    # top-k: per-row threshold + counter, then a 6144-entry (key, position) list per row;
+    # rows longer than 262144 have only the scratch-free path
+    assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == _topk_scratch(100)
+    assert dsa.dsa_topk_workspace_size(100, 262148, 2048) == 0
+    # prefill: a 2048-row chunk of 131072 float scores plus its top-k scratch
+    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 32, 4, 128, 64, 128, 2048) == \
+        2048 * 131072 * 4 + _topk_scratch(2048)
     # small problems use the whole row count
-    assert dsa.dsa_prefill_workspace_size(1, 100, 100, 8, 2, 128, 4, 64, 16) == 100 * 100 * 4
+    assert dsa.dsa_prefill_workspace_size(1, 100, 100, 8, 2, 128, 4, 64, 16) == \
+        (100 * 100 * 4 + 255) // 256 * 256 + _topk_scratch(100)
     n = dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 128, 64, 128, 2048)
-    assert n >= 32 * 131072 * 4
+    assert n >= 32 * 131072 * 4 + _topk_scratch(32)
     with pytest.raises(dsa.DsaError):
         dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 64, 64, 128, 2048)
+
+
+def test_topk_rejects_short_workspace():
+    lib = dsa.load()
+    need = dsa.dsa_topk_workspace_size(4, 64, 8)
+    assert lib.dsa_topk(FAKE, 64, 4, FAKE, 8, FAKE, None, FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_topk(FAKE, 64, 4, FAKE, 8, FAKE, None, MISALIGNED, need, None) == dsa.DSA_ERR_INVALID_ARG

@@ -64,14 +64,25 @@ def test_index_scores_row_window(dsa):
 # ------------------------------------------------------------------------------ top-k
 
 def _run_topk(dsa, scores_np, lens, k, values=True):
+    """Runs both top-k paths (wave-parallel with scratch, row-block without) and checks they agree."""
     torch = _torch()
     rows, ld = scores_np.shape
     s = torch.from_numpy(np.ascontiguousarray(scores_np, dtype=np.float32)).cuda()
     rl = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
-    idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
-    val = torch.full((rows, k), float("nan"), dtype=torch.float32, device="cuda") if values else None
-    dsa.dsa_topk(s, rl, k, idx, val)
-    return idx.cpu().numpy(), (val.cpu().numpy() if values else None)
+    res = []
+    for with_ws in (True, False):
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+        val = torch.full((rows, k), float("nan"), dtype=torch.float32, device="cuda") if values else None
+        ws = None
+        if with_ws:
+            nbytes = dsa.dsa_topk_workspace_size(rows, ld, k)
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        dsa.dsa_topk(s, rl, k, idx, val, workspace=ws)
+        res.append((idx.cpu().numpy(), val.cpu().numpy() if values else None))
+    assert np.array_equal(res[0][0], res[1][0]), "the two top-k paths disagree"
+    if values:
+        assert np.array_equal(res[0][1], res[1][1])
+    return res[0]
 
 
 def _check_topk(scores_np, lens, k, idx, val):
