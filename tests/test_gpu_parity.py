@@ -299,7 +299,9 @@ def test_prefill_varlen_and_chunking(dsa, lens, chunk_rows):
     dev = tl.upload_prefill(pi)
     ws = None
     if chunk_rows is not None:
-        ws = torch.empty(chunk_rows * ((max(lens) + 3) // 4 * 4) * 4, dtype=torch.uint8, device="cuda")
+        ld = (max(lens) + 3) // 4 * 4
+        nbytes = (chunk_rows * ld * 4 + 255) // 256 * 256 + dsa.dsa_topk_workspace_size(chunk_rows, ld, 512)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
                                 pi.cu_seqlens, pi.top_k, workspace=ws)
     rng = np.random.default_rng(1)
