@@ -5,19 +5,21 @@
 // 八): the unique set "larger score first, lower position among equals", returned ascending.
 //
 // Three launches, none of which needs a workgroup barrier while streaming the row:
-//   1. threshold: one wave per row takes a jittered stratified sample of up to 4096 scores
-//      (64 per lane, in registers) and runs an 8-bit radix select on it with a wave-private LDS
-//      histogram; the result tau_lo is a key that the row's true k-th key clears with a wide
-//      statistical margin (for rows of at most 4096 scores the sample is the row and tau_lo is
-//      exactly the k-th key).  It also clears the row's candidate counter;
+//   1. threshold: one wave per row reads 1024 jittered strata of 4 consecutive scores (the
+//      whole row when it has at most 4096), and one 1024-bin histogram over the key bits below
+//      the sample's common prefix gives tau_lo, the lower edge of the bin that holds the
+//      sample's r-th largest key.  r is chosen so the row's true k-th key clears tau_lo with a
+//      wide statistical margin while about 1.25 k positions reach it.  It also clears the
+//      row's candidate counter;
 //   2. collect: one wave per (row, segment) streams its segment once (next loads in flight
 //      while the current ones are filtered) and appends every (key, position) with
 //      key >= tau_lo to a wave-private LDS stage, flushed to the row's global candidate list
 //      with one atomic reservation per flush.  Candidate order does not matter;
 //   3. select: one 256-thread workgroup per row loads the candidates into LDS, finds the exact
-//      k-th key tau and the number n_eq of positions equal to tau to take by an 8-bit radix
-//      select, marks positions equal to tau in an LDS bitmap to find the n_eq-th lowest one,
-//      then marks every selected position and writes the bitmap's set bits in ascending order.
+//      k-th key tau and the number n_eq of positions equal to tau to take (radix rounds of 11
+//      bits over the bits below the candidates' common prefix), marks positions equal to tau
+//      in an LDS bitmap to find the n_eq-th lowest one, then marks every selected position and
+//      writes the bitmap's set bits in ascending order.
 // A row whose candidates number fewer than k or more than the list holds is redone exactly
 // from global memory inside the select kernel.  No result depends on the path or on timing.
 #include "common.h"
@@ -27,7 +29,10 @@ namespace dsa {
 namespace {
 
 constexpr int kCapW = 6144;       // candidate list length per row
-constexpr int kSampleW = 4096;    // sample size (64 per lane)
+constexpr int kStrata = 1024;     // sample strata per row (4 consecutive scores each, 16 per lane)
+constexpr int kTBins = 1024;      // threshold histogram bins
+constexpr int kSBits = 11;        // select radix digit width
+constexpr int kSBins = 1 << kSBits;
 constexpr int kStage = 512;       // per-wave LDS stage of the collect kernel
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
@@ -61,51 +66,21 @@ __device__ __forceinline__ uint32_t sample_rank(int m, int n, int k) {
   return (uint32_t)fminf((float)m, 1.25f * e + 3.f * sqrtf(e) + 8.f);
 }
 
-// The need-th largest (1-based) of the sample keys held 64 per lane (slot j of lane l is
-// sample l + 64 j, valid when < m).  hist is a wave-private 256-entry LDS array.
-__device__ uint32_t wave_radix_select(const uint32_t (&key)[64], int m, uint32_t need, uint32_t* hist, int lane) {
-  uint32_t prefix = 0, mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) hist[lane + 64 * q] = 0;
-    wave_lds_sync();
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
-      if (lane + 64 * j < m && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & 255u], 1u);
-    wave_lds_sync();
-    // Lane l owns bins 255-4l .. 252-4l, scanned from the top.
-    uint32_t c[4], s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = hist[255 - 4 * lane - q];
-      s += c[q];
-    }
-    uint32_t run = wave_excl_scan(s, lane);
-    int found = -1;
-    uint32_t above = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (run < need && run + c[q] >= need) {
-        found = 255 - 4 * lane - q;
-        above = run;
-      }
-      run += c[q];
-    }
-    const unsigned long long b = __ballot(found >= 0);
-    const int src_lane = __builtin_ctzll(b);
-    const int digit = __shfl(found, src_lane);
-    prefix |= (uint32_t)digit << shift;
-    mask |= 255u << shift;
-    need -= __shfl(above, src_lane);
-    wave_lds_sync();
-  }
-  return prefix;
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
 }
 
 __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __restrict__ scores, long long ld, int rows,
                                                              const int* __restrict__ row_len, int len_base, int k,
                                                              uint32_t* __restrict__ tau_lo, uint32_t* __restrict__ cnt) {
-  __shared__ uint32_t hist_all[4][256];
+  __shared__ uint32_t hist_all[4][kTBins];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
@@ -113,21 +88,70 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   if (lane == 0) cnt[row] = 0;
   if (n <= k) return;
   const float* src = scores + (size_t)row * ld;
-  const int m = min(n, kSampleW);
-  const int stride = n / m;
+  uint32_t* hist = hist_all[wave];
+  const bool whole = n <= 4 * kStrata;
+  // Stratum s = lane + 64 j: 4 consecutive scores at a jittered, 4-aligned offset inside it.
   uint32_t key[64];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  int m = 0;
 #pragma unroll
-  for (int j = 0; j < 64; ++j) {
-    const int i = lane + 64 * j;
-    int p = i;
-    if (m < n) {
-      const uint32_t h = (uint32_t)i * 2654435761u;
-      p = min((int)((long long)i * n / m) + (int)((h >> 8) % (uint32_t)stride), n - 1);
+  for (int j = 0; j < 16; ++j) {
+    const int st = lane + 64 * j;
+    int p;
+    if (whole) {
+      p = 4 * st;
+    } else {
+      const long long lo = (long long)st * n / kStrata, hi = (long long)(st + 1) * n / kStrata;
+      const int slots = (int)max(1LL, (hi - lo) / 4);
+      const uint32_t h = (uint32_t)st * 2654435761u;
+      p = (int)min((lo & ~3LL) + 4LL * ((h >> 8) % (uint32_t)slots), (long long)((n - 4) & ~3));
     }
-    key[j] = (i < m) ? float_key(src[p]) : 0u;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < n) v = *reinterpret_cast<const float4*>(src + p);
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool ok = p + c < n;
+      key[4 * j + c] = ok ? float_key(e[c]) : 0u;
+      if (ok) {
+        kmin = min(kmin, key[4 * j + c]);
+        kmax = max(kmax, key[4 * j + c]);
+      }
+    }
   }
-  const uint32_t t = wave_radix_select(key, m, sample_rank(m, n, k), hist_all[wave], lane);
-  if (lane == 0) tau_lo[row] = t;
+  m = whole ? n : 4 * kStrata;
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  // One histogram round over the bits below the sample's common prefix.
+  const int nb = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // bits below the common prefix (>= 1)
+  const int shift = max(0, nb - 10);
+  const uint32_t base = kmin >> shift;
+#pragma unroll
+  for (int q = 0; q < kTBins / 64; ++q) hist[lane + 64 * q] = 0;
+  wave_lds_sync();
+#pragma unroll
+  for (int j = 0; j < 64; ++j)
+    if (key[j] >= kmin && (whole ? (4 * (lane + 64 * (j >> 2)) + (j & 3) < n) : true))
+      atomicAdd(&hist[(key[j] >> shift) - base], 1u);
+  wave_lds_sync();
+  // Lane l owns bins 1023-16l .. 1008-16l, scanned from the top.
+  const uint32_t need = sample_rank(m, n, k);
+  uint32_t c[16], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    c[q] = hist[kTBins - 1 - 16 * lane - q];
+    sum += c[q];
+  }
+  uint32_t run = wave_excl_scan(sum, lane);
+  int found = -1;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (run < need && run + c[q] >= need) found = kTBins - 1 - 16 * lane - q;
+    run += c[q];
+  }
+  const unsigned long long bal = __ballot(found >= 0);
+  const int bin = __shfl(found, __builtin_ctzll(bal));
+  if (lane == 0) tau_lo[row] = (base + (uint32_t)bin) << shift;
 }
 
 __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restrict__ scores, long long ld, int rows,
@@ -196,8 +220,9 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restri
 // ------------------------------------------------------------------------- select kernel
 
 struct SelSmem {
-  uint32_t hist[256];
+  uint32_t hist[kSBins];
   uint32_t wsum[kSelWaves];
+  uint32_t red[2][kSelWaves];
   uint32_t digit, digit_above, pstar;
 };
 
@@ -223,32 +248,82 @@ __device__ uint32_t block_excl_scan256(uint32_t v, uint32_t* wsum, uint32_t& tot
   return pre + x - v;
 }
 
-// 8-bit radix select with a 256-thread block; key_at(i) for i < count.  Contains barriers.
+// LDS histogram increment; a wave whose active lanes all hit one bin issues a single add.
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
+  const uint32_t first = __builtin_amdgcn_readfirstlane(bin);
+  const unsigned long long active = __ballot(1);
+  const unsigned long long same = __ballot(bin == first);
+  if (same == active) {
+    if (lane_of() == __builtin_ctzll(active)) atomicAdd(&h[first], (uint32_t)__popcll(active));
+  } else {
+    atomicAdd(&h[bin], 1u);
+  }
+}
+
+// Exact radix select with a 256-thread block over key_at(i), i < count: the need-th largest key
+// and how many keys equal to it complete `need`.  Digits of 11 bits are taken below the common
+// prefix of the keys' minimum and maximum, so the first round already spreads.  Barriers inside.
 template <typename KeyAt>
 __device__ void block_radix_select(SelSmem& sm, KeyAt key_at, uint32_t count, uint32_t need, uint32_t* tau,
                                    uint32_t* n_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    sm.hist[tid] = 0;
+  const int tid = threadIdx.x, lane = lane_of(), wave = tid >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (uint32_t i = tid; i < count; i += kSelThreads) {
+    const uint32_t key = key_at(i);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    sm.red[0][wave] = kmin;
+    sm.red[1][wave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kSelWaves; ++i) {
+    kmin = min(kmin, sm.red[0][i]);
+    kmax = max(kmax, sm.red[1][i]);
+  }
+  uint32_t prefix = kmin, mask = 0;
+  int low = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // bits still undecided: [0, low)
+  if (kmin == kmax) low = 0;
+  mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+  prefix &= mask;
+  while (low > 0) {
+    const int width = min(low, kSBits);
+    const int shift = low - width;
+    const uint32_t nbin = 1u << width;
+    for (uint32_t i = tid; i < nbin; i += kSelThreads) sm.hist[i] = 0;
     __syncthreads();
     for (uint32_t i = tid; i < count; i += kSelThreads) {
       const uint32_t key = key_at(i);
-      if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 255u], 1u);
+      if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift) & (nbin - 1u));
     }
     __syncthreads();
-    const int b = 255 - tid;
-    const uint32_t c = sm.hist[b];
+    // Thread t owns bins [nbin - per*(t+1), nbin - per*t), scanned from the top.
+    const int per = (int)((nbin + kSelThreads - 1) / kSelThreads);
+    const int hi = (int)nbin - per * tid;
+    uint32_t local = 0;
+    for (int j = 0; j < per; ++j)
+      if (hi - 1 - j >= 0) local += sm.hist[hi - 1 - j];
     uint32_t tot;
-    const uint32_t run = block_excl_scan256(c, sm.wsum, tot);
-    if (run < need && run + c >= need) {
-      sm.digit = (uint32_t)b;
-      sm.digit_above = run;
+    uint32_t run = block_excl_scan256(local, sm.wsum, tot);
+    for (int j = 0; j < per; ++j) {
+      const int bidx = hi - 1 - j;
+      if (bidx < 0) break;
+      const uint32_t c = sm.hist[bidx];
+      if (run < need && run + c >= need) {
+        sm.digit = (uint32_t)bidx;
+        sm.digit_above = run;
+      }
+      run += c;
     }
     __syncthreads();
     prefix |= sm.digit << shift;
-    mask |= 255u << shift;
+    mask |= (nbin - 1u) << shift;
     need -= sm.digit_above;
+    low = shift;
     __syncthreads();
   }
   *tau = prefix;
@@ -408,7 +483,7 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a.scores, a.ld,
                      a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
   // Segment length: enough waves to keep every CU streaming, in multiples of 1024 positions.
-  const long long want_waves = 4096;
+  const long long want_waves = 16384;
   long long nseg = (want_waves + a.rows - 1) / a.rows;
   long long seg_len = (a.ld + nseg - 1) / nseg;
   seg_len = (seg_len + 1023) / 1024 * 1024;
