@@ -6,9 +6,9 @@
 //
 // Three launches, none of which needs a workgroup barrier while streaming the row:
 //   1. threshold: one wave per row reads 1024 jittered strata of 4 consecutive scores (the
-//      whole row when it has at most 4096), and one 1024-bin histogram over the key bits below
-//      the sample's common prefix gives tau_lo, the lower edge of the bin that holds the
-//      sample's r-th largest key.  r is chosen so the row's true k-th key clears tau_lo with a
+//      whole row when it has at most 4096), and two 1024-bin histogram rounds over the key bits
+//      below the sample's common prefix give tau_lo, the lower edge of the sub-bin that holds
+//      the sample's r-th largest key.  r is chosen so the row's true k-th key clears tau_lo with a
 //      wide statistical margin while about 1.25 k positions reach it.  It also clears the
 //      row's candidate counter;
 //   2. collect: one wave per (row, segment) streams its segment once (next loads in flight
@@ -122,36 +122,56 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   m = whole ? n : 4 * kStrata;
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
-  // One histogram round over the bits below the sample's common prefix.
-  const int nb = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // bits below the common prefix (>= 1)
-  const int shift = max(0, nb - 10);
-  const uint32_t base = kmin >> shift;
+  // Two histogram rounds of 10 bits over the bits below the sample's common prefix: the
+  // first finds the bin holding the sample's need-th largest key, the second narrows to a
+  // sub-bin of it, and tau_lo is that sub-bin's lower edge.
+  uint32_t need = sample_rank(m, n, k);
+  uint32_t prefix = kmin, mask;
+  int low = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // undecided low bits
+  if (kmin == kmax) low = 0;
+  mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+  prefix &= mask;
+  for (int round = 0; round < 2 && low > 0; ++round) {
+    const int width = min(low, 10);
+    const int shift = low - width;
+    const uint32_t nbin = 1u << width;
 #pragma unroll
-  for (int q = 0; q < kTBins / 64; ++q) hist[lane + 64 * q] = 0;
-  wave_lds_sync();
+    for (int q = 0; q < kTBins / 64; ++q) hist[lane + 64 * q] = 0;
+    wave_lds_sync();
 #pragma unroll
-  for (int j = 0; j < 64; ++j)
-    if (key[j] >= kmin && (whole ? (4 * (lane + 64 * (j >> 2)) + (j & 3) < n) : true))
-      atomicAdd(&hist[(key[j] >> shift) - base], 1u);
-  wave_lds_sync();
-  // Lane l owns bins 1023-16l .. 1008-16l, scanned from the top.
-  const uint32_t need = sample_rank(m, n, k);
-  uint32_t c[16], sum = 0;
+    for (int j = 0; j < 64; ++j) {
+      const bool valid = !whole || 4 * (lane + 64 * (j >> 2)) + (j & 3) < n;
+      if (valid && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (nbin - 1u)], 1u);
+    }
+    wave_lds_sync();
+    // Lane l owns bins nbin-1-16l .. nbin-16-16l, scanned from the top (absent bins count 0).
+    uint32_t c[16], sum = 0;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    c[q] = hist[kTBins - 1 - 16 * lane - q];
-    sum += c[q];
+    for (int q = 0; q < 16; ++q) {
+      const int bidx = (int)nbin - 1 - 16 * lane - q;
+      c[q] = bidx >= 0 ? hist[bidx] : 0u;
+      sum += c[q];
+    }
+    uint32_t run = wave_excl_scan(sum, lane);
+    int found = -1;
+    uint32_t above = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (run < need && run + c[q] >= need) {
+        found = (int)nbin - 1 - 16 * lane - q;
+        above = run;
+      }
+      run += c[q];
+    }
+    const unsigned long long bal = __ballot(found >= 0);
+    const int src_lane = __builtin_ctzll(bal);
+    prefix |= (uint32_t)__shfl(found, src_lane) << shift;
+    mask |= (nbin - 1u) << shift;
+    need -= __shfl(above, src_lane);
+    low = shift;
+    wave_lds_sync();
   }
-  uint32_t run = wave_excl_scan(sum, lane);
-  int found = -1;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    if (run < need && run + c[q] >= need) found = kTBins - 1 - 16 * lane - q;
-    run += c[q];
-  }
-  const unsigned long long bal = __ballot(found >= 0);
-  const int bin = __shfl(found, __builtin_ctzll(bal));
-  if (lane == 0) tau_lo[row] = (base + (uint32_t)bin) << shift;
+  if (lane == 0) tau_lo[row] = prefix;
 }
 
 __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restrict__ scores, long long ld, int rows,
