@@ -15,29 +15,25 @@
 //      while the current ones are filtered) and appends every (key, position) with
 //      key >= tau_lo to a wave-private LDS stage, flushed to the row's global candidate list
 //      with one atomic reservation per flush.  Candidate order does not matter;
-//   3. select: one 256-thread workgroup per row loads the candidates into LDS, finds the exact
-//      k-th key tau and the number n_eq of positions equal to tau to take (radix rounds of 11
-//      bits over the bits below the candidates' common prefix), marks positions equal to tau
-//      in an LDS bitmap to find the n_eq-th lowest one, then marks every selected position and
-//      writes the bitmap's set bits in ascending order.
-// A row whose candidates number fewer than k or more than the list holds is redone exactly
-// from global memory inside the select kernel.  No result depends on the path or on timing.
+//   3. select: one 256-thread workgroup per row loads its candidates into registers (24 per
+//      thread, all loads in flight at once), finds the exact k-th key tau and the number n_eq
+//      of positions equal to tau to take (10-bit radix rounds over the bits below the
+//      candidates' common prefix, LDS histogram), sets every selected position in an LDS
+//      bitmap (only when more than n_eq positions tie at tau is the n_eq-th lowest of them
+//      located first, from a bitmap of the tied positions), and writes the set bits in
+//      ascending order.  About 20 KB of LDS per row lets several rows run per CU.
+// A row whose candidates number fewer than k or more than the list holds is redone exactly by
+// the same workgroup from the row itself.  No result depends on the path taken or on timing.
 #include "common.h"
 #include "kernels.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kCapW = 6144;       // candidate list length per row
-constexpr int kStrata = 1024;     // sample strata per row (4 consecutive scores each, 16 per lane)
-constexpr int kTBins = 1024;      // threshold histogram bins
-constexpr int kSBits = 11;        // select radix digit width
-constexpr int kSBins = 1 << kSBits;
-constexpr int kStage = 512;       // per-wave LDS stage of the collect kernel
-constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / 64;
-
-__device__ __forceinline__ int lane_of() { return threadIdx.x & 63; }
+constexpr int kCapW = 6144;    // candidate list length per row
+constexpr int kStrata = 1024;  // sample strata per row (4 consecutive scores each, 16 per lane)
+constexpr int kBins = 1024;    // radix histogram bins (10-bit digits)
+constexpr int kStage = 512;    // per-wave LDS stage of the collect kernel
 
 __device__ __forceinline__ int row_length(const int* row_len, int len_base, int row, long long ld) {
   return max(0, (int)min((long long)(row_len ? row_len[row] : len_base + row + 1), ld));
@@ -57,15 +53,6 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int lane) {
   return x - v;
 }
 
-// Rank threshold for a sample of m of the row's n keys: the sample's r-th largest key is
-// exceeded by the true k-th key with overwhelming probability while the number of row keys
-// at or above it stays near k * 1.25 + O(sqrt) (well inside the candidate list).
-__device__ __forceinline__ uint32_t sample_rank(int m, int n, int k) {
-  if (m == n) return (uint32_t)k;
-  const float e = (float)m * (float)k / (float)n;
-  return (uint32_t)fminf((float)m, 1.25f * e + 3.f * sqrtf(e) + 8.f);
-}
-
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
@@ -76,11 +63,66 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
   return v;
 }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += (uint32_t)__shfl_xor((int)v, o);
+  return v;
+}
+
+// Rank threshold for a sample of m of the row's n keys: the sample's r-th largest key is
+// exceeded by the true k-th key with overwhelming probability while the number of row keys
+// at or above it stays near 1.25 k plus a few standard deviations (inside the candidate list).
+__device__ __forceinline__ uint32_t sample_rank(int m, int n, int k) {
+  if (m == n) return (uint32_t)k;
+  const float e = (float)m * (float)k / (float)n;
+  return (uint32_t)fminf((float)m, 1.25f * e + 3.f * sqrtf(e) + 8.f);
+}
+
+// One 10-bit radix round over a key stream: histogram of the digit at `shift` of the keys
+// matching (prefix, mask), then the bin holding rank `need` from the top.  Returns the digit;
+// *above = keys in higher bins, *in_bin = keys in that bin.  hist holds kBins entries.
+template <typename Each>
+__device__ uint32_t wave_radix_round(Each each, uint32_t prefix, uint32_t mask, int shift, int width, uint32_t need,
+                                     uint32_t* hist, int lane, uint32_t* above, uint32_t* in_bin) {
+  const uint32_t nbin = 1u << width;
+#pragma unroll
+  for (int q = 0; q < kBins / 64; ++q) hist[lane + 64 * q] = 0;
+  wave_lds_sync();
+  each([&](uint32_t key, uint32_t) {
+    if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & (nbin - 1u)], 1u);
+  });
+  wave_lds_sync();
+  // Lane l owns bins kBins-1-16l .. kBins-16-16l (bins >= nbin are empty), scanned from the top.
+  uint32_t c[16], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    c[q] = hist[kBins - 1 - 16 * lane - q];
+    sum += c[q];
+  }
+  uint32_t run = wave_excl_scan(sum, lane);
+  int found = -1;
+  uint32_t ab = 0, cb = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (run < need && run + c[q] >= need) {
+      found = kBins - 1 - 16 * lane - q;
+      ab = run;
+      cb = c[q];
+    }
+    run += c[q];
+  }
+  const int src = __builtin_ctzll(__ballot(found >= 0));
+  *above = (uint32_t)__shfl((int)ab, src);
+  *in_bin = (uint32_t)__shfl((int)cb, src);
+  const uint32_t digit = (uint32_t)__shfl(found, src);
+  wave_lds_sync();
+  return digit;
+}
 
 __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __restrict__ scores, long long ld, int rows,
                                                              const int* __restrict__ row_len, int len_base, int k,
                                                              uint32_t* __restrict__ tau_lo, uint32_t* __restrict__ cnt) {
-  __shared__ uint32_t hist_all[4][kTBins];
+  __shared__ uint32_t hist_all[4][kBins];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + wave;
   if (row >= rows) return;
@@ -88,88 +130,54 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   if (lane == 0) cnt[row] = 0;
   if (n <= k) return;
   const float* src = scores + (size_t)row * ld;
-  uint32_t* hist = hist_all[wave];
   const bool whole = n <= 4 * kStrata;
-  // Stratum s = lane + 64 j: 4 consecutive scores at a jittered, 4-aligned offset inside it.
+  const uint32_t sf = whole ? 1u : (uint32_t)(n >> 2) / kStrata;  // float4 slots per stratum
+  // Stratum s = lane + 64 j: the float4 slot s*sf + jitter (the whole row when it is short).
   uint32_t key[64];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  int m = 0;
+  unsigned long long valid = 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    const int st = lane + 64 * j;
-    int p;
-    if (whole) {
-      p = 4 * st;
-    } else {
-      const long long lo = (long long)st * n / kStrata, hi = (long long)(st + 1) * n / kStrata;
-      const int slots = (int)max(1LL, (hi - lo) / 4);
-      const uint32_t h = (uint32_t)st * 2654435761u;
-      p = (int)min((lo & ~3LL) + 4LL * ((h >> 8) % (uint32_t)slots), (long long)((n - 4) & ~3));
-    }
+    const uint32_t st = (uint32_t)(lane + 64 * j);
+    const uint32_t f4 = whole ? st : st * sf + ((st * 2654435761u) >> 8) % sf;
+    const int p = (int)(4 * f4);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p < n) v = *reinterpret_cast<const float4*>(src + p);
-    const float e[4] = {v.x, v.y, v.z, v.w};
+    key[4 * j + 0] = float_key(v.x);
+    key[4 * j + 1] = float_key(v.y);
+    key[4 * j + 2] = float_key(v.z);
+    key[4 * j + 3] = float_key(v.w);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool ok = p + c < n;
-      key[4 * j + c] = ok ? float_key(e[c]) : 0u;
-      if (ok) {
-        kmin = min(kmin, key[4 * j + c]);
-        kmax = max(kmax, key[4 * j + c]);
-      }
-    }
+    for (int c = 0; c < 4; ++c) valid |= (unsigned long long)(p + c < n) << (4 * j + c);
   }
-  m = whole ? n : 4 * kStrata;
+  const int m = whole ? n : 4 * kStrata;
+  // Two 10-bit rounds below the sample's common prefix; tau_lo is the lower edge of the sub-bin
+  // that holds the sample's r-th largest key.
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < 64; ++j)
+      if ((valid >> j) & 1ull) f(key[j], 0u);
+  };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  each([&](uint32_t kk, uint32_t) {
+    kmin = min(kmin, kk);
+    kmax = max(kmax, kk);
+  });
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
-  // Two histogram rounds of 10 bits over the bits below the sample's common prefix: the
-  // first finds the bin holding the sample's need-th largest key, the second narrows to a
-  // sub-bin of it, and tau_lo is that sub-bin's lower edge.
   uint32_t need = sample_rank(m, n, k);
-  uint32_t prefix = kmin, mask;
-  int low = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // undecided low bits
-  if (kmin == kmax) low = 0;
-  mask = low >= 32 ? 0u : ~((1u << low) - 1u);
-  prefix &= mask;
+  int low = (kmin == kmax) ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+  uint32_t prefix = kmin & mask;
   for (int round = 0; round < 2 && low > 0; ++round) {
     const int width = min(low, 10);
     const int shift = low - width;
-    const uint32_t nbin = 1u << width;
-#pragma unroll
-    for (int q = 0; q < kTBins / 64; ++q) hist[lane + 64 * q] = 0;
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const bool valid = !whole || 4 * (lane + 64 * (j >> 2)) + (j & 3) < n;
-      if (valid && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & (nbin - 1u)], 1u);
-    }
-    wave_lds_sync();
-    // Lane l owns bins nbin-1-16l .. nbin-16-16l, scanned from the top (absent bins count 0).
-    uint32_t c[16], sum = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int bidx = (int)nbin - 1 - 16 * lane - q;
-      c[q] = bidx >= 0 ? hist[bidx] : 0u;
-      sum += c[q];
-    }
-    uint32_t run = wave_excl_scan(sum, lane);
-    int found = -1;
-    uint32_t above = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      if (run < need && run + c[q] >= need) {
-        found = (int)nbin - 1 - 16 * lane - q;
-        above = run;
-      }
-      run += c[q];
-    }
-    const unsigned long long bal = __ballot(found >= 0);
-    const int src_lane = __builtin_ctzll(bal);
-    prefix |= (uint32_t)__shfl(found, src_lane) << shift;
-    mask |= (nbin - 1u) << shift;
-    need -= __shfl(above, src_lane);
+    uint32_t above, in_bin;
+    const uint32_t digit =
+        wave_radix_round(each, prefix, mask, shift, width, need, hist_all[wave], lane, &above, &in_bin);
+    prefix |= digit << shift;
+    mask |= ((1u << width) - 1u) << shift;
+    need -= above;
     low = shift;
-    wave_lds_sync();
   }
   if (lane == 0) tau_lo[row] = prefix;
 }
@@ -178,6 +186,7 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restri
                                                            const int* __restrict__ row_len, int len_base, int k,
                                                            int seg_len, int nseg, const uint32_t* __restrict__ tau_lo,
                                                            uint32_t* __restrict__ cnt, uint2* __restrict__ cand) {
+  constexpr int U = 8;  // float4 per lane per round (2048 positions per wave round)
   __shared__ uint2 stage_all[4][kStage];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long long item = (long long)blockIdx.x * 4 + wave;
@@ -205,20 +214,20 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restri
     ns = 0;
     wave_lds_sync();
   };
-  auto load = [&](int base, float4 (&v)[4]) {
+  auto load = [&](int base, float4 (&v)[U]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int pos = base + 256 * u + 4 * lane;
       v[u] = (pos < p1) ? *reinterpret_cast<const float4*>(src + pos) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   };
 
-  float4 cur[4], nxt[4];
+  float4 cur[U], nxt[U];
   load(p0, cur);
-  for (int base = p0; base < p1; base += 1024) {
-    if (base + 1024 < p1) load(base + 1024, nxt);
+  for (int base = p0; base < p1; base += 256 * U) {
+    if (base + 256 * U < p1) load(base + 256 * U, nxt);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const float e[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -232,22 +241,28 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restri
       if (ns >= (uint32_t)(kStage - 256)) flush();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
   if (ns) flush();
 }
 
-// ------------------------------------------------------------------------- select kernel
+// ---------------------------------------------------------------------------------------
+// Select: one 256-thread workgroup per row, the candidates held in registers (24 per thread).
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kPer = kCapW / kSelThreads;  // candidates per thread
 
 struct SelSmem {
-  uint32_t hist[kSBins];
+  uint32_t hist[kBins];
   uint32_t wsum[kSelWaves];
   uint32_t red[2][kSelWaves];
-  uint32_t digit, digit_above, pstar;
+  uint32_t digit, above, in_bin;
+  int pstar;
 };
 
-__device__ uint32_t block_excl_scan256(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = lane_of(), wave = threadIdx.x >> 6;
+__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -274,80 +289,160 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
   const unsigned long long active = __ballot(1);
   const unsigned long long same = __ballot(bin == first);
   if (same == active) {
-    if (lane_of() == __builtin_ctzll(active)) atomicAdd(&h[first], (uint32_t)__popcll(active));
+    if ((threadIdx.x & 63) == (unsigned)__builtin_ctzll(active)) atomicAdd(&h[first], (uint32_t)__popcll(active));
   } else {
     atomicAdd(&h[bin], 1u);
   }
 }
 
-// Exact radix select with a 256-thread block over key_at(i), i < count: the need-th largest key
-// and how many keys equal to it complete `need`.  Digits of 11 bits are taken below the common
-// prefix of the keys' minimum and maximum, so the first round already spreads.  Barriers inside.
-template <typename KeyAt>
-__device__ void block_radix_select(SelSmem& sm, KeyAt key_at, uint32_t count, uint32_t need, uint32_t* tau,
-                                   uint32_t* n_eq) {
-  const int tid = threadIdx.x, lane = lane_of(), wave = tid >> 6;
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (uint32_t i = tid; i < count; i += kSelThreads) {
-    const uint32_t key = key_at(i);
+// Exact need-th largest key over a block-wide stream (each(f) calls f(key, pos) for this
+// thread's elements), with n_eq and eq_total as in wave_select.  Barriers inside.
+template <typename Each>
+__device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* tau, uint32_t* n_eq,
+                             uint32_t* eq_total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0;
+  each([&](uint32_t key, uint32_t) {
     kmin = min(kmin, key);
     kmax = max(kmax, key);
-  }
+    ++cnt;
+  });
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
   if (lane == 0) {
     sm.red[0][wave] = kmin;
     sm.red[1][wave] = kmax;
   }
-  __syncthreads();
+  uint32_t tot_cnt;
+  block_excl_scan(cnt, sm.wsum, tot_cnt);  // also orders the red[] writes before the reads below
 #pragma unroll
   for (int i = 0; i < kSelWaves; ++i) {
     kmin = min(kmin, sm.red[0][i]);
     kmax = max(kmax, sm.red[1][i]);
   }
-  uint32_t prefix = kmin, mask = 0;
-  int low = 32 - __builtin_clz((kmin ^ kmax) | 1u);  // bits still undecided: [0, low)
-  if (kmin == kmax) low = 0;
-  mask = low >= 32 ? 0u : ~((1u << low) - 1u);
-  prefix &= mask;
+  int low = (kmin == kmax) ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+  uint32_t prefix = kmin & mask;
+  uint32_t in_bin = tot_cnt;
   while (low > 0) {
-    const int width = min(low, kSBits);
+    const int width = min(low, 10);
     const int shift = low - width;
     const uint32_t nbin = 1u << width;
-    for (uint32_t i = tid; i < nbin; i += kSelThreads) sm.hist[i] = 0;
+#pragma unroll
+    for (int q = 0; q < kBins / kSelThreads; ++q) sm.hist[tid + kSelThreads * q] = 0;
     __syncthreads();
-    for (uint32_t i = tid; i < count; i += kSelThreads) {
-      const uint32_t key = key_at(i);
+    each([&](uint32_t key, uint32_t) {
       if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift) & (nbin - 1u));
-    }
+    });
     __syncthreads();
-    // Thread t owns bins [nbin - per*(t+1), nbin - per*t), scanned from the top.
-    const int per = (int)((nbin + kSelThreads - 1) / kSelThreads);
-    const int hi = (int)nbin - per * tid;
-    uint32_t local = 0;
-    for (int j = 0; j < per; ++j)
-      if (hi - 1 - j >= 0) local += sm.hist[hi - 1 - j];
+    // Thread t owns bins kBins-1-4t .. kBins-4-4t, scanned from the top.
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = sm.hist[kBins - 1 - 4 * tid - q];
+      sum += c[q];
+    }
     uint32_t tot;
-    uint32_t run = block_excl_scan256(local, sm.wsum, tot);
-    for (int j = 0; j < per; ++j) {
-      const int bidx = hi - 1 - j;
-      if (bidx < 0) break;
-      const uint32_t c = sm.hist[bidx];
-      if (run < need && run + c >= need) {
-        sm.digit = (uint32_t)bidx;
-        sm.digit_above = run;
+    uint32_t run = block_excl_scan(sum, sm.wsum, tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (run < need && run + c[q] >= need) {
+        sm.digit = (uint32_t)(kBins - 1 - 4 * tid - q);
+        sm.above = run;
+        sm.in_bin = c[q];
       }
-      run += c;
+      run += c[q];
     }
     __syncthreads();
     prefix |= sm.digit << shift;
     mask |= (nbin - 1u) << shift;
-    need -= sm.digit_above;
+    need -= sm.above;
+    in_bin = sm.in_bin;
     low = shift;
     __syncthreads();
   }
   *tau = prefix;
   *n_eq = need;
+  *eq_total = in_bin;
+}
+
+// Ascending emission of the set bits of bits[0 .. NW): out[rank] = position.  Barriers inside.
+template <int NW>
+__device__ void block_emit_bits(SelSmem& sm, const uint32_t* bits, const float* src, int* out, float* vout) {
+  constexpr int W = NW / kSelThreads;
+  const int w0 = threadIdx.x * W;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) local += (uint32_t)__popc(bits[w0 + j]);
+  uint32_t tot;
+  uint32_t rank = block_excl_scan(local, sm.wsum, tot);
+  for (int j = 0; j < W; ++j) {
+    uint32_t w = bits[w0 + j];
+    while (w) {
+      const int p = (w0 + j) * 32 + __builtin_ctz(w);
+      w &= w - 1;
+      out[rank] = p;
+      if (vout) vout[rank] = key_float(float_key(src[p]));
+      ++rank;
+    }
+  }
+}
+
+// Position of the need-th lowest set bit of bits[0 .. NW).  Barriers inside.
+template <int NW>
+__device__ int block_nth_bit(SelSmem& sm, const uint32_t* bits, uint32_t need) {
+  constexpr int W = NW / kSelThreads;
+  const int w0 = threadIdx.x * W;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < W; ++j) local += (uint32_t)__popc(bits[w0 + j]);
+  uint32_t tot;
+  uint32_t run = block_excl_scan(local, sm.wsum, tot);
+  if (run < need && run + local >= need) {
+    for (int j = 0; j < W; ++j) {
+      uint32_t w = bits[w0 + j];
+      const uint32_t c = (uint32_t)__popc(w);
+      if (run + c >= need) {
+        for (uint32_t skip = need - run - 1; skip > 0; --skip) w &= w - 1;
+        sm.pstar = (w0 + j) * 32 + __builtin_ctz(w);
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  return sm.pstar;
+}
+
+template <int NW>
+__device__ void block_zero(uint32_t* bits) {
+  uint4* b4 = reinterpret_cast<uint4*>(bits);
+  for (int j = threadIdx.x; j < NW / 4; j += kSelThreads) b4[j] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+}
+
+// The k positions from a stream that holds every selectable position: exact tau and n_eq,
+// the n_eq-th lowest tied position when ties exceed n_eq, bitmap, ascending emission.
+template <int NW, typename Each>
+__device__ void block_select_emit(SelSmem& sm, uint32_t* bits, Each each, int k, const float* src, int* out,
+                                  float* vout) {
+  uint32_t tau, n_eq, eq_total;
+  block_select(sm, each, (uint32_t)k, &tau, &n_eq, &eq_total);
+  int pstar = 0x7FFFFFFF;
+  if (eq_total > n_eq) {
+    block_zero<NW>(bits);
+    each([&](uint32_t key, uint32_t pos) {
+      if (key == tau) atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+    });
+    __syncthreads();
+    pstar = block_nth_bit<NW>(sm, bits, n_eq);
+  }
+  block_zero<NW>(bits);
+  each([&](uint32_t key, uint32_t pos) {
+    if (key > tau || (key == tau && (int)pos <= pstar)) atomicOr(&bits[pos >> 5], 1u << (pos & 31));
+  });
+  __syncthreads();
+  block_emit_bits<NW>(sm, bits, src, out, vout);
 }
 
 template <int NW>
@@ -357,13 +452,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
                                                                   const uint2* __restrict__ cand,
                                                                   int* __restrict__ idx_out,
                                                                   float* __restrict__ values_out) {
-  constexpr int WPT = NW / kSelThreads;  // bitmap words per thread (a contiguous run)
-  __shared__ uint32_t ckey[kCapW];
-  __shared__ int cpos[kCapW];
-  __shared__ uint32_t bits[NW];
+  __shared__ __attribute__((aligned(16))) uint32_t bits[NW];
   __shared__ SelSmem sm;
   const int tid = threadIdx.x;
-  const int row = rows - 1 - (int)blockIdx.x;
+  const int row = rows - 1 - (int)blockIdx.x;  // longest rows first
   const int n = row_length(row_len, len_base, row, ld);
   int* out = idx_out + (size_t)row * k;
   float* vout = values_out ? values_out + (size_t)row * k : nullptr;
@@ -377,114 +469,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     return;
   }
   const uint32_t count = cnt[row];
-  uint32_t tau, n_eq;
   if (count >= (uint32_t)k && count <= (uint32_t)kCapW) {
     const uint2* cr = cand + (size_t)row * kCapW;
-    for (uint32_t i = tid; i < count; i += kSelThreads) {
-      const uint2 c = cr[i];
-      ckey[i] = c.x;
-      cpos[i] = (int)c.y;
+    uint32_t ck[kPer], cp[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = tid + kSelThreads * j;
+      const uint2 c = (i < count) ? cr[i] : make_uint2(0u, 0u);
+      ck[j] = c.x;
+      cp[j] = c.y;
     }
-    __syncthreads();
-    block_radix_select(sm, [&](uint32_t i) { return ckey[i]; }, count, (uint32_t)k, &tau, &n_eq);
-
-    const int nwords = (n + 31) >> 5;
-    const int w0 = tid * WPT;
-    // Positions equal to tau: find the n_eq-th lowest.
+    auto each = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) bits[w0 + j] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < count; i += kSelThreads)
-      if (ckey[i] == tau) atomicOr(&bits[cpos[i] >> 5], 1u << (cpos[i] & 31));
-    __syncthreads();
-    {
-      uint32_t local = 0;
-#pragma unroll
-      for (int j = 0; j < WPT; ++j) local += (w0 + j < nwords) ? (uint32_t)__popc(bits[w0 + j]) : 0u;
-      uint32_t tot;
-      uint32_t run = block_excl_scan256(local, sm.wsum, tot);
-      if (run < n_eq && run + local >= n_eq) {
-        for (int j = 0; j < WPT; ++j) {
-          uint32_t wbits = bits[w0 + j];
-          const uint32_t c = (uint32_t)__popc(wbits);
-          if (run + c >= n_eq) {
-            for (uint32_t skip = n_eq - run - 1; skip > 0; --skip) wbits &= wbits - 1;
-            sm.pstar = (uint32_t)((w0 + j) * 32 + __builtin_ctz(wbits));
-            break;
-          }
-          run += c;
-        }
-      }
-      __syncthreads();
-    }
-    const int pstar = (int)sm.pstar;
-    // Every selected position.
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) bits[w0 + j] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < count; i += kSelThreads) {
-      const uint32_t key = ckey[i];
-      const int p = cpos[i];
-      if (key > tau || (key == tau && p <= pstar)) atomicOr(&bits[p >> 5], 1u << (p & 31));
-    }
-    __syncthreads();
-    uint32_t local = 0;
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) local += (w0 + j < nwords) ? (uint32_t)__popc(bits[w0 + j]) : 0u;
-    uint32_t tot;
-    uint32_t rank = block_excl_scan256(local, sm.wsum, tot);
-    for (int j = 0; j < WPT; ++j) {
-      uint32_t wbits = (w0 + j < nwords) ? bits[w0 + j] : 0u;
-      while (wbits) {
-        const int p = (w0 + j) * 32 + __builtin_ctz(wbits);
-        wbits &= wbits - 1;
-        out[rank] = p;
-        if (vout) vout[rank] = key_float(float_key(src[p]));
-        ++rank;
-      }
-    }
-    return;
-  }
-
-  // Fallback: exact radix select over the row itself, then an ordered emit pass.
-  block_radix_select(sm, [&](uint32_t i) { return float_key(src[i]); }, (uint32_t)n, (uint32_t)k, &tau, &n_eq);
-  uint32_t written = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += 4 * kSelThreads) {
-    const int q0 = base + 4 * tid;
-    uint32_t key[4];
-    uint32_t ce = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      key[c] = (q0 + c < n) ? float_key(src[q0 + c]) : 0u;
-      ce += (q0 + c < n && key[c] == tau) ? 1u : 0u;
-    }
-    uint32_t tot_e;
-    uint32_t r = eq_seen + block_excl_scan256(ce, sm.wsum, tot_e);
-    bool take[4];
-    uint32_t cs = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      take[c] = false;
-      if (q0 + c >= n) continue;
-      if (key[c] > tau) {
-        take[c] = true;
-      } else if (key[c] == tau) {
-        take[c] = r < n_eq;
-        ++r;
-      }
-      cs += take[c] ? 1u : 0u;
-    }
-    uint32_t tot_s;
-    uint32_t os = written + block_excl_scan256(cs, sm.wsum, tot_s);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (take[c]) {
-        out[os] = q0 + c;
-        if (vout) vout[os] = key_float(key[c]);
-        ++os;
-      }
-    written += tot_s;
-    eq_seen += tot_e;
+      for (int j = 0; j < kPer; ++j)
+        if (tid + kSelThreads * j < (int)count) f(ck[j], cp[j]);
+    };
+    block_select_emit<NW>(sm, bits, each, k, src, out, vout);
+  } else {
+    auto each = [&](auto f) {
+      for (int i = tid; i < n; i += kSelThreads) f(float_key(src[i]), (uint32_t)i);
+    };
+    block_select_emit<NW>(sm, bits, each, k, src, out, vout);
   }
 }
 
@@ -500,13 +505,14 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
   uint32_t* cnt = tau_lo + a.rows;
   const size_t head = ((size_t)a.rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   uint2* cand = reinterpret_cast<uint2*>(static_cast<char*>(a.workspace) + head);
-  hipLaunchKernelGGL(topk_threshold_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a.scores, a.ld,
-                     a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
-  // Segment length: enough waves to keep every CU streaming, in multiples of 1024 positions.
+  const unsigned groups = (unsigned)((a.rows + 3) / 4);
+  hipLaunchKernelGGL(topk_threshold_kernel, dim3(groups), dim3(256), 0, s, a.scores, a.ld, a.rows, a.row_len,
+                     a.len_base, a.k, tau_lo, cnt);
+  // Segment length: enough waves to keep every CU streaming, in multiples of 2048 positions.
   const long long want_waves = 16384;
   long long nseg = (want_waves + a.rows - 1) / a.rows;
   long long seg_len = (a.ld + nseg - 1) / nseg;
-  seg_len = (seg_len + 1023) / 1024 * 1024;
+  seg_len = (seg_len + 2047) / 2048 * 2048;
   nseg = (a.ld + seg_len - 1) / seg_len;
   const long long items = (long long)a.rows * nseg;
   hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a.scores, a.ld, a.rows,
