@@ -5,8 +5,8 @@
 // 八): the unique set "larger score first, lower position among equals", returned ascending.
 //
 // Three launches, none of which needs a workgroup barrier while streaming the row:
-//   1. threshold: one wave per row reads 1024 jittered strata of 4 consecutive scores (the
-//      whole row when it has at most 4096), and two 1024-bin histogram rounds over the key bits
+//   1. threshold: one wave per row reads 512 jittered strata of 4 consecutive scores (the
+//      whole row when it has at most 2048), and two 1024-bin histogram rounds over the key bits
 //      below the sample's common prefix give tau_lo, the lower edge of the sub-bin that holds
 //      the sample's r-th largest key.  r is chosen so the row's true k-th key clears tau_lo with a
 //      wide statistical margin while about 1.25 k positions reach it.  It also clears the
@@ -15,7 +15,7 @@
 //      while the current ones are filtered) and appends every (key, position) with
 //      key >= tau_lo to a wave-private LDS stage, flushed to the row's global candidate list
 //      with one atomic reservation per flush.  Candidate order does not matter;
-//   3. select: one 256-thread workgroup per row loads its candidates into registers (24 per
+//   3. select: one 256-thread workgroup per row loads its candidates into registers (32 per
 //      thread, all loads in flight at once), finds the exact k-th key tau and the number n_eq
 //      of positions equal to tau to take (10-bit radix rounds over the bits below the
 //      candidates' common prefix, LDS histogram), sets every selected position in an LDS
@@ -30,8 +30,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kCapW = 6144;    // candidate list length per row
-constexpr int kStrata = 1024;  // sample strata per row (4 consecutive scores each, 16 per lane)
+constexpr int kCapW = 8192;    // candidate list length per row
+constexpr int kStrata = 512;   // sample strata per row: 4 consecutive scores each (8 per lane)
 constexpr int kBins = 1024;    // radix histogram bins (10-bit digits)
 constexpr int kStage = 512;    // per-wave LDS stage of the collect kernel
 
@@ -132,14 +132,16 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   const float* src = scores + (size_t)row * ld;
   const bool whole = n <= 4 * kStrata;
   const uint32_t sf = whole ? 1u : (uint32_t)(n >> 2) / kStrata;  // float4 slots per stratum
-  // Stratum s = lane + 64 j: the float4 slot s*sf + jitter (the whole row when it is short).
-  uint32_t key[64];
+  // Stratum s = lane + 64 j: 4 consecutive scores at a jittered float4 slot inside it, or the
+  // whole row when it is short.  Single positions per stratum keep the sample close to
+  // independent even where neighbouring positions are correlated.
+  uint32_t key[32];
   unsigned long long valid = 0;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const uint32_t st = (uint32_t)(lane + 64 * j);
-    const uint32_t f4 = whole ? st : st * sf + ((st * 2654435761u) >> 8) % sf;
-    const int p = (int)(4 * f4);
+    const uint32_t slot = whole ? st : st * sf + ((st * 2654435761u) >> 8) % sf;
+    const int p = (int)(4 * slot);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p < n) v = *reinterpret_cast<const float4*>(src + p);
     key[4 * j + 0] = float_key(v.x);
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   // that holds the sample's r-th largest key.
   auto each = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < 64; ++j)
+    for (int j = 0; j < 32; ++j)
       if ((valid >> j) & 1ull) f(key[j], 0u);
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;

@@ -117,11 +117,11 @@ def test_zero_sized_calls_are_no_ops():
 
 def _topk_scratch(rows):
     head = (rows * 8 + 255) // 256 * 256
-    return (head + rows * 6144 * 8 + 255) // 256 * 256
+    return (head + rows * 8192 * 8 + 255) // 256 * 256
 
 
 def test_workspace_sizes():
-    # top-k: per-row threshold + counter, then a 6144-entry (key, position) list per row;
+    # top-k: per-row threshold + counter, then an 8192-entry (key, position) list per row;
     # rows longer than 262144 have only the scratch-free path
     assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == _topk_scratch(100)
     assert dsa.dsa_topk_workspace_size(100, 262148, 2048) == 0
