@@ -22,14 +22,22 @@ namespace {
 
 // Sum the partial scores of four 16-key subtiles over the four lane groups; on return lane l
 // holds the total for subtile l / 16, column l % 16, i.e. key l of the 64-key tile.
-__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3, int lane) {
-  const bool hi = lane >= 32;
-  const float s0 = hi ? p0 : p2, s1 = hi ? p1 : p3;
-  const float k0 = (hi ? p2 : p0) + __shfl_xor(s0, 32);
-  const float k1 = (hi ? p3 : p1) + __shfl_xor(s1, 32);
-  const bool odd = (lane >> 4) & 1;
-  const float s = odd ? k0 : k1;
-  return (odd ? k1 : k0) + __shfl_xor(s, 16);
+// permlane32_swap(a, b) yields (a.lo32 | b.lo32, a.hi32 | b.hi32) and permlane16_swap does the
+// same per 16-lane quarter inside each half, so the sum of the two results pairs every lane
+// with its partner group in one exchange: three exchanges and three adds in all.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(a), __float_as_int(b), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(a), __float_as_int(b), false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+__device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3) {
+  // lanes < 32 now hold subtiles 0 / 1 over groups {g, g^2}; lanes >= 32 subtiles 2 / 3
+  const float k0 = swap_sum32(p0, p2);
+  const float k1 = swap_sum32(p1, p3);
+  return swap_sum16(k0, k1);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -97,22 +105,31 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int wave_t_last = min(r0 + wave * TOKW + TOKW, row_end) - 1 - seq_off;
   const int wave_r0 = r0 + wave * TOKW;
 
+  // Tile staging: thread t moves chunks t + 256 p (key c / CPR, 16-byte part c % CPR).  Full
+  // tiles use a fixed per-thread offset from a tile base that advances uniformly; only the
+  // last, partial tile clamps its keys to the range.
   u32x4 stage[NLD];
+  const uint16_t* ktile = k_idx + (size_t)(seq_off + kbeg) * DI;
   auto load_tile = [&](int tile) {
+    const uint16_t* base = ktile + (size_t)tile * 64 * DI;
+    const int keys_left = kend - kbeg - tile * 64;
+    if (keys_left >= 64) {
 #pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const int c = threadIdx.x + 256 * p;
-      const int key = c / CPR, part = c % CPR;
-      const int kk = min(kbeg + tile * 64 + key, kend - 1);
-      stage[p] = ldg16(k_idx + (size_t)(seq_off + kk) * DI + part * 8);
+      for (int p = 0; p < NLD; ++p) stage[p] = ldg16(base + (threadIdx.x + 256 * p) * 8);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NLD; ++p) {
+        const int c = threadIdx.x + 256 * p;
+        const int key = min(c / CPR, keys_left - 1);
+        stage[p] = ldg16(base + key * DI + (c % CPR) * 8);
+      }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < NLD; ++p) {
       const int c = threadIdx.x + 256 * p;
-      const int key = c / CPR, part = c % CPR;
-      *reinterpret_cast<u32x4*>(&lds[buf][key * PITCH + part * 16]) = stage[p];
+      *reinterpret_cast<u32x4*>(&lds[buf][(c / CPR) * PITCH + (c % CPR) * 16]) = stage[p];
     }
   };
 
@@ -151,7 +168,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
       if constexpr (H >= 16) {
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
-          const float v = transpose_reduce4(part[0][s], part[1][s], part[2][s], part[3][s], lane);
+          const float v = transpose_reduce4(part[0][s], part[1][s], part[2][s], part[3][s]);
           const int r = wave_r0 + s;
           const int key = key0 + lane;
           if (r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
@@ -239,7 +256,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
         for (int i = 0; i < 4; ++i) acc = fmaf(relu(c[rt][i]), wreg[rt][i], acc);
       part[st] = acc;
     }
-    const float v = transpose_reduce4(part[0], part[1], part[2], part[3], lane);
+    const float v = transpose_reduce4(part[0], part[1], part[2], part[3]);
     const int key = kbeg + tile * 64 + lane;
     if (key < kend) scores[(size_t)b * ld + key] = v;
   };
