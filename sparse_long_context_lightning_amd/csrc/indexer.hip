@@ -41,21 +41,23 @@ __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2,
 }
 
 // ---------------------------------------------------------------------------------------
-// Prefill: a workgroup of 4 waves scores 4 * (64 / H) consecutive query rows of one sequence
-// against one split of keys; key tiles of 64 rows are staged in LDS (double buffered) and
-// shared by the 4 waves.  Each wave keeps its 64 (token, head) query rows in registers.
-template <int H, int DI>
+// Prefill: a workgroup of 4 waves scores 4 * (16 RT / H) consecutive query rows of one
+// sequence against one split of keys; key tiles of 64 rows are staged in LDS (double buffered)
+// and shared by the 4 waves.  Each wave keeps its 16 RT (token, head) query rows in registers
+// (RT = 4: one token of 64 heads), so every key operand read from LDS feeds RT MFMAs.
+template <int H, int DI, int RT>
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ w,
     int seq_off, int row_begin, int row_end, int out_row0, float* __restrict__ scores, long long ld,
     int key_split, int n_rowblk) {
-  constexpr int TOKW = (H >= 16) ? 64 / H : 16;  // tokens per wave (H = 4: 4 per row tile)
+  // RT row tiles of 16 (token, head) rows per wave.
+  constexpr int TOKW = (H >= 16) ? 16 * RT / H : 4 * RT;  // tokens per wave (H = 4: 4 per row tile)
   constexpr int TOKWG = 4 * TOKW;
   constexpr int NKS = DI / 32;
   constexpr int PITCH = DI * 2 + 16;  // bytes per LDS key row (16-byte pad against bank conflicts)
   constexpr int CPR = DI / 8;         // 16-byte chunks per key row
   constexpr int NLD = 64 * CPR / 256; // chunks each thread stages per tile
-  constexpr int NSLOT = (H >= 16) ? TOKW : 4;
+  constexpr int NSLOT = (H >= 16) ? TOKW : RT;
   static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
   static_assert(DI == 64 || DI == 128, "unsupported indexer dim");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][64 * PITCH];
@@ -78,9 +80,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int n = lane & 15, lg = lane >> 4;
 
   // Query rows of this wave as MFMA A operands: lane supplies row 16*rt + n.
-  u32x4 areg[4][NKS];
+  u32x4 areg[RT][NKS];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const int m = 16 * rt + n;
     const int tok = (H >= 16) ? wave * TOKW + m / H : wave * TOKW + m / 4;
     const int head = (H >= 16) ? m % H : m % 4;
@@ -90,9 +92,9 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     for (int ks = 0; ks < NKS; ++ks) areg[rt][ks] = ldg16(qp + ks * 8);
   }
   // Weights of the C rows this lane holds: row 16*rt + 4*lg + i.
-  float wreg[4][4];
+  float wreg[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = 16 * rt + 4 * lg + i;
@@ -149,17 +151,17 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         u32x4 breg[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) breg[ks] = *reinterpret_cast<const u32x4*>(bp + ks * 16);
-        f32x4 c[4];
+        f32x4 c[RT];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], breg[ks], c[rt]);
+          for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], breg[ks], c[rt]);
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) part[st][s] = 0.f;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < RT; ++rt) {
           const int slot = (H >= 16) ? (16 * rt) / H : rt;
 #pragma unroll
           for (int i = 0; i < 4; ++i) part[st][slot] = fmaf(relu(c[rt][i]), wreg[rt][i], part[st][slot]);
@@ -277,25 +279,25 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
 // ---------------------------------------------------------------------------------------
 // Host launchers.
 
-template <int H, int DI>
+template <int H, int DI, int RT>
 static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, hipStream_t s) {
-  constexpr int TOKWG = 4 * ((H >= 16) ? 64 / H : 16);
+  constexpr int TOKWG = 4 * ((H >= 16) ? 16 * RT / H : 4 * RT);
   const int rows = a.row_end - a.row_begin;
   const int n_rowblk = (rows + TOKWG - 1) / TOKWG;
   const int t_max = a.row_end - 1 - a.seq_off;
   const int n_split = (t_max + a.key_split) / a.key_split;
   long long n = (long long)n_rowblk * n_split;
   n = (n + 7) / 8 * 8;
-  hipLaunchKernelGGL((indexer_prefill_kernel<H, DI>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx, a.w,
+  hipLaunchKernelGGL((indexer_prefill_kernel<H, DI, RT>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx, a.w,
                      a.seq_off, a.row_begin, a.row_end, a.out_row0, a.scores, a.ld, a.key_split, n_rowblk);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s) {
-  if (a.h_idx == 64 && a.d_idx == 128) return launch_prefill_t<64, 128>(a, s);
-  if (a.h_idx == 32 && a.d_idx == 128) return launch_prefill_t<32, 128>(a, s);
-  if (a.h_idx == 16 && a.d_idx == 128) return launch_prefill_t<16, 128>(a, s);
-  if (a.h_idx == 4 && a.d_idx == 64) return launch_prefill_t<4, 64>(a, s);
+  if (a.h_idx == 64 && a.d_idx == 128) return launch_prefill_t<64, 128, 4>(a, s);
+  if (a.h_idx == 32 && a.d_idx == 128) return launch_prefill_t<32, 128, 4>(a, s);
+  if (a.h_idx == 16 && a.d_idx == 128) return launch_prefill_t<16, 128, 4>(a, s);
+  if (a.h_idx == 4 && a.d_idx == 64) return launch_prefill_t<4, 64, 4>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -40,8 +40,11 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, floa
   const long long item = (long long)wg * 4 + wave;
   const long long n_items = (long long)a.rows * a.nsplit * a.hkv;
   if (item >= n_items) return;
-  const int g = (int)(item % a.hkv);
-  const long long tmp = item / a.hkv;
+  // KV group slowest: all rows of group g run before group g+1, so the gathered K/V rows of
+  // one group (a quarter of the cache at 4 KV heads) stay resident in the last-level cache.
+  const long long per_group = (long long)a.rows * a.nsplit;
+  const int g = (int)(item / per_group);
+  const long long tmp = item - (long long)g * per_group;
   const int sp = (int)(tmp % a.nsplit);
   const int row = (int)(tmp / a.nsplit);
   unsigned char* vlds = vlds_all[wave];
