@@ -64,4 +64,10 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_wave_base + 16 l
+// (lds_wave_base must be the same for the whole wave).  Completion is tracked by vmcnt.
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
+}
+
 }  // namespace dsa

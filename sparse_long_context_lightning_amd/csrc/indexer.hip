@@ -54,12 +54,15 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   constexpr int TOKW = (H >= 16) ? 16 * RT / H : 4 * RT;  // tokens per wave (H = 4: 4 per row tile)
   constexpr int TOKWG = 4 * TOKW;
   constexpr int NKS = DI / 32;
-  constexpr int PITCH = DI * 2 + 16;  // bytes per LDS key row (16-byte pad against bank conflicts)
+  constexpr int PITCH = DI * 2;       // bytes per LDS key row
   constexpr int CPR = DI / 8;         // 16-byte chunks per key row
   constexpr int NLD = 64 * CPR / 256; // chunks each thread stages per tile
   constexpr int NSLOT = (H >= 16) ? TOKW : RT;
   static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
   static_assert(DI == 64 || DI == 128, "unsupported indexer dim");
+  // Key tiles: 64 rows, chunk c of row r stored at slot c ^ (r % CPR) (XOR swizzle keeps the
+  // MFMA operand reads free of bank conflicts without padding, so whole waves can fill the
+  // tile with direct global-to-LDS loads).
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][64 * PITCH];
 
   // XCD-aware order: consecutive work items (same key split, neighbouring rows) land on the
@@ -107,50 +110,50 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int wave_t_last = min(r0 + wave * TOKW + TOKW, row_end) - 1 - seq_off;
   const int wave_r0 = r0 + wave * TOKW;
 
-  // Tile staging: thread t moves chunks t + 256 p (key c / CPR, 16-byte part c % CPR).  Full
-  // tiles use a fixed per-thread offset from a tile base that advances uniformly; only the
-  // last, partial tile clamps its keys to the range.
-  u32x4 stage[NLD];
+  // Tile staging: instruction p of wave w fills LDS bytes [p*4096 + w*1024, +1024) of the
+  // tile, lane l the 16 bytes at + 16 l, i.e. row r = (p*4096 + w*1024 + 16 l) / PITCH, slot
+  // l % CPR, which holds the row's chunk (l % CPR) ^ (r % CPR).  Full tiles use fixed
+  // per-thread offsets from a tile base that advances uniformly; only the last, partial tile
+  // clamps its rows to the key range.
   const uint16_t* ktile = k_idx + (size_t)(seq_off + kbeg) * DI;
-  auto load_tile = [&](int tile) {
+  int st_row[NLD], st_off[NLD];
+#pragma unroll
+  for (int p = 0; p < NLD; ++p) {
+    const int pos = p * 4096 + wave * 1024 + lane * 16;
+    const int r = pos / PITCH;
+    const int chunk = (lane % CPR) ^ (r % CPR);
+    st_row[p] = r;
+    st_off[p] = r * DI + chunk * 8;  // elements
+  }
+  auto load_tile = [&](int tile, int buf) {
     const uint16_t* base = ktile + (size_t)tile * 64 * DI;
     const int keys_left = kend - kbeg - tile * 64;
-    if (keys_left >= 64) {
-#pragma unroll
-      for (int p = 0; p < NLD; ++p) stage[p] = ldg16(base + (threadIdx.x + 256 * p) * 8);
-    } else {
-#pragma unroll
-      for (int p = 0; p < NLD; ++p) {
-        const int c = threadIdx.x + 256 * p;
-        const int key = min(c / CPR, keys_left - 1);
-        stage[p] = ldg16(base + key * DI + (c % CPR) * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < NLD; ++p) {
-      const int c = threadIdx.x + 256 * p;
-      *reinterpret_cast<u32x4*>(&lds[buf][(c / CPR) * PITCH + (c % CPR) * 16]) = stage[p];
+      const uint16_t* g = base + st_off[p];
+      if (keys_left < 64) g = base + min(st_row[p], keys_left - 1) * DI + (st_off[p] - st_row[p] * DI);
+      lds_dma16(g, &lds[buf][p * 4096 + wave * 1024]);
     }
   };
+  auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_tile();
   __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) load_tile(it + 1);
+    if (it + 1 < ntiles) load_tile(it + 1, (it + 1) & 1);
     const int key0 = kbeg + it * 64;
     if (wave_r0 < row_end && key0 <= wave_t_last) {
       const unsigned char* tile = lds[it & 1];
       float part[4][NSLOT];
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const unsigned char* bp = tile + (16 * st + n) * PITCH + lg * NKS * 16;
+        const unsigned char* bp = tile + (16 * st + n) * PITCH;
         u32x4 breg[NKS];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) breg[ks] = *reinterpret_cast<const u32x4*>(bp + ks * 16);
+        for (int ks = 0; ks < NKS; ++ks)
+          breg[ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * NKS + ks) ^ (n % CPR)) * 16));
         f32x4 c[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         }
       }
     }
-    if (it + 1 < ntiles) store_tile((it + 1) & 1);
+    if (it + 1 < ntiles) wait_tile();
     __syncthreads();
   }
 }
