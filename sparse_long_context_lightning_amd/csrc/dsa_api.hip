@@ -84,7 +84,7 @@ int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) 
   if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
 
 constexpr int kKeySplit = 2048;        // keys per prefill-indexer workgroup
-constexpr int kDecodeKeysPerWave = 512;
+constexpr int kDecodeKeysPerWave = 1024;
 constexpr int kMinChunkRows = 64;
 constexpr int kDefaultChunkRows = 2048;
 

@@ -197,8 +197,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
 
 // ---------------------------------------------------------------------------------------
 // Decode: one query token per sequence against its cached keys.  HBM-bound (64 flop per key
-// byte at 64 heads x 128 dims), so key tiles go straight from global memory into MFMA
-// B-operand registers, double buffered, with no LDS.  A workgroup of 4 waves covers
+// byte at 64 heads x 128 dims).  The workgroup's 4 waves serve one sequence, so its query rows
+// sit once in LDS (chunk c of row r at slot c ^ (r % CPR), conflict-free operand reads) and
+// the registers go to a 3-deep ring of key tiles read straight from global memory into MFMA
+// B operands: two tiles are in flight while the third is scored.  A workgroup covers
 // 4 * keys_per_wave consecutive keys of one sequence.
 template <int H, int DI>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(
@@ -207,53 +209,67 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     int nsplit) {
   constexpr int NKS = DI / 32;
   constexpr int RT = (H >= 16) ? H / 16 : 1;
+  constexpr int CPR = DI / 8;  // 16-byte chunks per query row
   static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
+  __shared__ __attribute__((aligned(16))) unsigned char qlds[16 * RT * DI * 2];
   const int b = blockIdx.x / nsplit;
   const int split = blockIdx.x - b * nsplit;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
+
+  for (int c = threadIdx.x; c < 16 * RT * CPR; c += 256) {
+    const int r = c / CPR, ch = c % CPR;
+    const u32x4 v = (r < H) ? ldg16(q_idx + ((size_t)b * H + r) * DI + ch * 8) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(qlds + r * DI * 2 + ((ch ^ (r % CPR)) * 16)) = v;
+  }
+  __syncthreads();
+
   const int len = min(seq_lens[b], s_max);  // defensive: never read past the cache
   const int kbeg = (split * 4 + wave) * keys_per_wave;
   if (kbeg >= len) return;
   const int kend = min(kbeg + keys_per_wave, len);
   const int ntiles = (kend - kbeg + 63) >> 6;
 
-  u32x4 areg[RT][NKS];
   float wreg[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int m = 16 * rt + n;
-    const uint16_t* qp = q_idx + ((size_t)b * H + (m < H ? m : 0)) * DI + lg * NKS * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) areg[rt][ks] = (m < H) ? ldg16(qp + ks * 8) : u32x4{0, 0, 0, 0};
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int mc = 16 * rt + 4 * lg + i;
       wreg[rt][i] = (mc < H) ? w[(size_t)b * H + mc] : 0.f;
     }
-  }
-  const uint16_t* kbase = k_cache + (size_t)b * s_max * DI + lg * NKS * 8;
+  // The reduction index is permuted the same way on both operands: k-step ks of lane group lg
+  // takes 16-byte chunk 4 ks + lg, so the four lanes of one key read 64 contiguous bytes per
+  // load.  The A fragment (row 16 rt + n, chunk 4 ks + lg) lives at slot chunk ^ (n % CPR).
+  const unsigned char* qrow = qlds + n * DI * 2;
+  const uint16_t* kbase = k_cache + (size_t)b * s_max * DI + lg * 8;
 
-  u32x4 bufA[4][NKS], bufB[4][NKS];
+  u32x4 buf0[4][NKS], buf1[4][NKS], buf2[4][NKS];
   auto load = [&](u32x4 (&dst)[4][NKS], int tile) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kk = min(kbeg + tile * 64 + 16 * st + n, kend - 1);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) dst[st][ks] = ldg16(kbase + (size_t)kk * DI + ks * 8);
+      for (int ks = 0; ks < NKS; ++ks) dst[st][ks] = ldg16(kbase + (size_t)kk * DI + ks * 32);
     }
   };
   auto compute = [&](const u32x4 (&src)[4][NKS], int tile) {
     float part[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      // Re-read the query fragments from LDS per subtile rather than holding them in registers.
+      asm volatile("" ::: "memory");
       f32x4 c[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], src[st][ks], c[rt]);
+        for (int rt = 0; rt < RT; ++rt) {
+          const u32x4 aq = *reinterpret_cast<const u32x4*>(qrow + rt * 16 * DI * 2 +
+                                                            (((ks * 4 + lg) ^ (n % CPR)) * 16));
+          c[rt] = mfma16x16x32(aq, src[st][ks], c[rt]);
+        }
       float acc = 0.f;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -266,15 +282,19 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(
     if (key < kend) scores[(size_t)b * ld + key] = v;
   };
 
-  load(bufA, 0);
-  int it = 0;
-  for (; it + 1 < ntiles; it += 2) {
-    load(bufB, it + 1);
-    compute(bufA, it);
-    if (it + 2 < ntiles) load(bufA, it + 2);
-    compute(bufB, it + 1);
+  load(buf0, 0);
+  if (ntiles > 1) load(buf1, 1);
+  for (int it = 0;; it += 3) {
+    if (it + 2 < ntiles) load(buf2, it + 2);
+    compute(buf0, it);
+    if (it + 1 >= ntiles) break;
+    if (it + 3 < ntiles) load(buf0, it + 3);
+    compute(buf1, it + 1);
+    if (it + 2 >= ntiles) break;
+    if (it + 4 < ntiles) load(buf1, it + 4);
+    compute(buf2, it + 2);
+    if (it + 3 >= ntiles) break;
   }
-  if (it < ntiles) compute(bufA, it);
 }
 
 }  // namespace

@@ -128,3 +128,39 @@ def check_index_structure(idx, row_lens, k):
     d = np.diff(idx, axis=1)
     both = valid[:, 1:]
     assert np.all(d[both] > 0), "indices must be strictly ascending"
+
+
+def check_index_structure_device(idx, row_lens, k):
+    """check_index_structure on the device, for index sets too large to copy to the host."""
+    import torch
+    row_lens = row_lens.to(idx.device).to(torch.int64)
+    cnt = torch.clamp(row_lens, max=k)
+    pos = torch.arange(k, device=idx.device)[None, :]
+    valid = pos < cnt[:, None]
+    assert bool((idx[~valid] == -1).all()), "padding must be -1"
+    v = idx.to(torch.int64)
+    assert bool(((v >= 0) & (v < row_lens[:, None]) | ~valid).all()), "index out of range"
+    d = v[:, 1:] - v[:, :-1]
+    assert bool(((d > 0) | ~valid[:, 1:]).all()), "indices must be strictly ascending"
+
+
+def sample_rows(cu_seqlens, k, n_random, seed, period=None):
+    """Deterministic row sample of a packed prefill: row 0, the first and last row of each
+    sequence, rows k-2 .. k+1 of each sequence, the text/frame boundaries of the first and last
+    periods when `period` is given (32 text tokens then a frame), and n_random rows drawn from
+    PCG64(seed + 100)."""
+    cu = [int(x) for x in cu_seqlens]
+    rows = {0}
+    for b in range(len(cu) - 1):
+        o, n = cu[b], cu[b + 1] - cu[b]
+        if n == 0:
+            continue
+        rows |= {o, o + n - 1}
+        rows |= {o + t for t in (k - 2, k - 1, k, k + 1) if 0 <= t < n}
+        if period:
+            last = (n - 1) // period
+            for j in (0, 1, last // 2, last):
+                rows |= {o + j * period + t for t in (31, 32, period - 1) if j * period + t < n}
+    rng = np.random.default_rng(seed + 100)
+    rows |= set(int(x) for x in rng.integers(0, cu[-1], n_random))
+    return sorted(rows)
