@@ -13,8 +13,9 @@
 //      row's candidate counter;
 //   2. collect: one wave per (row, segment) streams its segment once (next loads in flight
 //      while the current ones are filtered) and appends every (key, position) with
-//      key >= tau_lo to a wave-private LDS stage, flushed to the row's global candidate list
-//      with one atomic reservation per flush.  Candidate order does not matter;
+//      key >= tau_lo to a wave-private LDS stage; the waves of a workgroup (consecutive
+//      segments of one row) then reserve room in the row's global candidate list with a single
+//      atomic.  Candidate order does not matter;
 //   3. select: one 256-thread workgroup per row loads its candidates into registers (32 per
 //      thread, all loads in flight at once), finds the exact k-th key tau and the number n_eq
 //      of positions equal to tau to take (10-bit radix rounds over the bits below the
@@ -184,21 +185,29 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   if (lane == 0) tau_lo[row] = prefix;
 }
 
-__global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restrict__ scores, long long ld, int rows,
-                                                           const int* __restrict__ row_len, int len_base, int k,
-                                                           int seg_len, int nseg, const uint32_t* __restrict__ tau_lo,
-                                                           uint32_t* __restrict__ cnt, uint2* __restrict__ cand) {
+// Collect: a workgroup of NW waves streams NW consecutive segments of one row.  Each wave
+// stages its candidates in LDS; the workgroup then reserves room for all of them with one
+// atomic on the row's counter (same-address atomics from many workgroups serialise, so their
+// number per row is kept small), and each wave copies its stage to its share.  A wave whose
+// stage fills up part way flushes it on its own.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void topk_collect_kernel(const float* __restrict__ scores, long long ld,
+                                                               int rows, const int* __restrict__ row_len,
+                                                               int len_base, int k, int seg_len, int nseg,
+                                                               const uint32_t* __restrict__ tau_lo,
+                                                               uint32_t* __restrict__ cnt, uint2* __restrict__ cand) {
   constexpr int U = 8;  // float4 per lane per round (2048 positions per wave round)
-  __shared__ uint2 stage_all[4][kStage];
+  __shared__ uint2 stage_all[NW][kStage];
+  __shared__ uint32_t wave_cnt[NW];
+  __shared__ uint32_t wg_base;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + wave;
-  const int row = (int)(item / nseg);
-  const int seg = (int)(item - (long long)row * nseg);
-  if (row >= rows) return;
+  const int wg_per_row = nseg / NW;
+  const int row = blockIdx.x / wg_per_row;
+  const int seg = (blockIdx.x - row * wg_per_row) * NW + wave;
+  if (row >= rows) return;  // uniform over the workgroup
   const int n = row_length(row_len, len_base, row, ld);
-  if (n <= k) return;
+  if (n <= k) return;       // uniform over the workgroup
   const int p0 = seg * seg_len;
-  if (p0 >= n) return;
   const int p1 = min(n, p0 + seg_len);
   const uint32_t tau = tau_lo[row];
   const float* src = scores + (size_t)row * ld;
@@ -224,28 +233,42 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(const float* __restri
     }
   };
 
-  float4 cur[U], nxt[U];
-  load(p0, cur);
-  for (int base = p0; base < p1; base += 256 * U) {
-    if (base + 256 * U < p1) load(base + 256 * U, nxt);
+  if (p0 < p1) {
+    float4 cur[U], nxt[U];
+    load(p0, cur);
+    for (int base = p0; base < p1; base += 256 * U) {
+      if (base + 256 * U < p1) load(base + 256 * U, nxt);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float e[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
+      for (int u = 0; u < U; ++u) {
+        const float e[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int pos = base + 256 * u + 4 * lane + c;
-        const uint32_t key = float_key(e[c]);
-        const bool flag = pos < p1 && key >= tau;
-        const unsigned long long b = __ballot(flag);
-        if (flag) stage[ns + lanes_below(b)] = make_uint2(key, (uint32_t)pos);
-        ns += (uint32_t)__popcll(b);
+        for (int c = 0; c < 4; ++c) {
+          const int pos = base + 256 * u + 4 * lane + c;
+          const uint32_t key = float_key(e[c]);
+          const bool flag = pos < p1 && key >= tau;
+          const unsigned long long b = __ballot(flag);
+          if (flag) stage[ns + lanes_below(b)] = make_uint2(key, (uint32_t)pos);
+          ns += (uint32_t)__popcll(b);
+        }
+        if (ns >= (uint32_t)(kStage - 256)) flush();
       }
-      if (ns >= (uint32_t)(kStage - 256)) flush();
-    }
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
   }
-  if (ns) flush();
+  // One reservation for what the workgroup's stages still hold.
+  if (lane == 0) wave_cnt[wave] = ns;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t total = 0;
+    for (int w = 0; w < NW; ++w) total += wave_cnt[w];
+    wg_base = total ? atomicAdd(&cnt[row], total) : 0u;
+  }
+  __syncthreads();
+  uint32_t off = wg_base;
+  for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+  for (uint32_t i = lane; i < ns; i += 64)
+    if (off + i < (uint32_t)kCapW) cand_row[off + i] = stage[i];
 }
 
 // ---------------------------------------------------------------------------------------
@@ -299,9 +322,11 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
 
 // Exact need-th largest key over a block-wide stream (each(f) calls f(key, pos) for this
 // thread's elements), with n_eq and eq_total as in wave_select.  Barriers inside.
+// With max_rounds limiting the 10-bit rounds, *tau is the lower edge of the sub-bin that holds
+// the need-th largest key (bits below the resolved digits zero).
 template <typename Each>
 __device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* tau, uint32_t* n_eq,
-                             uint32_t* eq_total) {
+                             uint32_t* eq_total, int max_rounds = 4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0;
   each([&](uint32_t key, uint32_t) {
@@ -326,7 +351,7 @@ __device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* ta
   uint32_t mask = low >= 32 ? 0u : ~((1u << low) - 1u);
   uint32_t prefix = kmin & mask;
   uint32_t in_bin = tot_cnt;
-  while (low > 0) {
+  for (int round = 0; round < max_rounds && low > 0; ++round) {
     const int width = min(low, 10);
     const int shift = low - width;
     const uint32_t nbin = 1u << width;
@@ -495,6 +520,57 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   }
 }
 
+// Threshold, block form for few long rows: one workgroup per row samples 1024 * SPT scores
+// (jittered single float4 slots, or the whole row when it is short) and, like the wave form,
+// takes the lower edge of the sub-bin (two 10-bit rounds) that holds the sample_rank-th largest
+// sampled key.  Four times the wave form's sample keeps the candidate
+// count of rows up to 262144 scores close to its mean.
+template <int SPT>
+__global__ __launch_bounds__(kSelThreads) void topk_threshold_block_kernel(const float* __restrict__ scores,
+                                                                           long long ld, int rows,
+                                                                           const int* __restrict__ row_len,
+                                                                           int len_base, int k,
+                                                                           uint32_t* __restrict__ tau_lo,
+                                                                           uint32_t* __restrict__ cnt) {
+  static_assert(4 * SPT <= 32, "valid mask is 32 bits");
+  constexpr int kStrataB = kSelThreads * SPT;
+  __shared__ SelSmem sm;
+  const int tid = threadIdx.x;
+  const int row = blockIdx.x;
+  if (row >= rows) return;
+  const int n = row_length(row_len, len_base, row, ld);
+  if (tid == 0) cnt[row] = 0;
+  if (n <= k) return;
+  const float* src = scores + (size_t)row * ld;
+  const bool whole = n <= 4 * kStrataB;
+  const uint32_t sf = whole ? 1u : (uint32_t)(n >> 2) / kStrataB;  // float4 slots per stratum
+  uint32_t key[4 * SPT];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const uint32_t st = (uint32_t)(tid + kSelThreads * j);
+    const uint32_t slot = whole ? st : st * sf + ((st * 2654435761u) >> 8) % sf;
+    const int p = (int)(4 * slot);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < n) v = *reinterpret_cast<const float4*>(src + p);
+    key[4 * j + 0] = float_key(v.x);
+    key[4 * j + 1] = float_key(v.y);
+    key[4 * j + 2] = float_key(v.z);
+    key[4 * j + 3] = float_key(v.w);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) valid |= (uint32_t)(p + c < n) << (4 * j + c);
+  }
+  const int m = whole ? n : 4 * kStrataB;
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < 4 * SPT; ++j)
+      if ((valid >> j) & 1u) f(key[j], 0u);
+  };
+  uint32_t tau, n_eq, eq_total;
+  block_select(sm, each, sample_rank(m, n, k), &tau, &n_eq, &eq_total, 2);
+  if (tid == 0) tau_lo[row] = tau;
+}
+
 }  // namespace
 
 size_t topk_wave_workspace_bytes(int rows) {
@@ -507,18 +583,31 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
   uint32_t* cnt = tau_lo + a.rows;
   const size_t head = ((size_t)a.rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   uint2* cand = reinterpret_cast<uint2*>(static_cast<char*>(a.workspace) + head);
-  const unsigned groups = (unsigned)((a.rows + 3) / 4);
-  hipLaunchKernelGGL(topk_threshold_kernel, dim3(groups), dim3(256), 0, s, a.scores, a.ld, a.rows, a.row_len,
-                     a.len_base, a.k, tau_lo, cnt);
+  if (a.rows <= 512) {
+    // few rows: a workgroup per row and a four times larger sample
+    hipLaunchKernelGGL(topk_threshold_block_kernel<8>, dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores,
+                       a.ld, a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
+  } else {
+    const unsigned groups = (unsigned)((a.rows + 3) / 4);
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(groups), dim3(256), 0, s, a.scores, a.ld, a.rows, a.row_len,
+                       a.len_base, a.k, tau_lo, cnt);
+  }
   // Segment length: enough waves to keep every CU streaming, in multiples of 2048 positions.
   const long long want_waves = 16384;
   long long nseg = (want_waves + a.rows - 1) / a.rows;
   long long seg_len = (a.ld + nseg - 1) / nseg;
   seg_len = (seg_len + 2047) / 2048 * 2048;
   nseg = (a.ld + seg_len - 1) / seg_len;
-  const long long items = (long long)a.rows * nseg;
-  hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, a.scores, a.ld, a.rows,
-                     a.row_len, a.len_base, a.k, (int)seg_len, (int)nseg, tau_lo, cnt, cand);
+  // Workgroups of 16 waves when rows are few and long (fewer atomics per row), else 4.
+  if (nseg >= 16) {
+    nseg = (nseg + 15) / 16 * 16;
+    hipLaunchKernelGGL(topk_collect_kernel<16>, dim3((unsigned)(a.rows * (nseg / 16))), dim3(1024), 0, s, a.scores,
+                       a.ld, a.rows, a.row_len, a.len_base, a.k, (int)seg_len, (int)nseg, tau_lo, cnt, cand);
+  } else {
+    nseg = (nseg + 3) / 4 * 4;
+    hipLaunchKernelGGL(topk_collect_kernel<4>, dim3((unsigned)(a.rows * (nseg / 4))), dim3(256), 0, s, a.scores,
+                       a.ld, a.rows, a.row_len, a.len_base, a.k, (int)seg_len, (int)nseg, tau_lo, cnt, cand);
+  }
   if (a.ld <= 131072)
     hipLaunchKernelGGL((topk_select_kernel<4096>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores, a.ld,
                        a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
