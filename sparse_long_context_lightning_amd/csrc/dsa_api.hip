@@ -99,7 +99,7 @@ size_t prefill_chunk_bytes(int rows, long long ld) {
 
 int decode_nsplit(int batch, int hkv, int top_k) {
   const int nchunk = (top_k + 31) / 32;
-  const int want = (2048 + batch * hkv - 1) / (batch * hkv);
+  const int want = (1024 + batch * hkv - 1) / (batch * hkv);
   return std::max(1, std::min(want, nchunk));
 }
 

@@ -157,10 +157,14 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
         f32x4 c[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Raised wave priority while this wave issues its MFMAs: the arbiter then prefers the
+        // waves that keep the matrix pipe fed over those in their epilogue.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], breg[ks], c[rt]);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) part[st][s] = 0.f;
 #pragma unroll
