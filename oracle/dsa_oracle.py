@@ -28,6 +28,7 @@ listed in the design notes):
   R4  a prefix shorter than k is taken whole; the index list is padded with -1
   R5  ties go to the lower position; -0 equals +0
   R6  selected positions are returned in ascending order
+  R21 the torch.topk-shaped variant orders the same set by descending score, then position
   R8  GQA head h reads KV head h // (Hq // Hkv)
   R9  softmax scale passed explicitly (1/sqrt(D) by default), lse is natural-log and
       includes the scale
@@ -112,6 +113,28 @@ def select_topk_row(scores: np.ndarray, k: int) -> np.ndarray:
     chosen = np.sort(order[:k])
     out[:] = chosen
     return out
+
+
+def select_topk_sorted_row(scores: np.ndarray, k: int):
+    """Deterministic top-k in the shape of torch.topk(sorted=True) (source A, section 八: a
+    deterministic top-k takes the place of torch.topk so that training and inference keep
+    identical sets).
+
+    Reading R21: the kept set is the one select_topk_row keeps; it is returned ordered by
+    descending score and, among equal scores, ascending position, with the scores alongside;
+    a row shorter than k is padded at the end with position -1 and score -inf.
+    returns (idx [k] int64, values [k] float64)
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    m = min(n, k)
+    idx = np.full(k, -1, dtype=np.int64)
+    val = np.full(k, -np.inf, dtype=np.float64)
+    # The same stable ranking as select_topk_row, kept in rank order instead of position order.
+    order = np.argsort(-s, kind="stable")[:m]
+    idx[:m] = order
+    val[:m] = s[order]
+    return idx, val
 
 
 def sparse_gqa_attention_row(q_row: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,

@@ -155,6 +155,47 @@ def test_topk_matches_torch_topk_without_ties():
         assert np.array_equal(orc.select_topk_row(sc, k), ref)
 
 
+def _brute_topk_sorted(scores, k):
+    """Pure-Python ranking by (-score, position), kept in rank order, padded with -1 / -inf."""
+    n = len(scores)
+    ranked = sorted(range(n), key=lambda s: (-scores[s], s))[:k]
+    return ranked + [-1] * (k - len(ranked)), [scores[s] for s in ranked] + [-math.inf] * (k - len(ranked))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_sorted_equals_bruteforce_ranking_with_ties(seed):
+    rng = np.random.default_rng(300 + seed)
+    for _ in range(60):
+        n = int(rng.integers(1, 70))
+        k = int(rng.integers(1, 40))
+        sc = rng.integers(-2, 4, size=n) / 8.0          # heavy ties
+        idx, val = orc.select_topk_sorted_row(sc, k)
+        want_idx, want_val = _brute_topk_sorted(sc.tolist(), k)
+        assert idx.tolist() == want_idx
+        assert val.tolist() == want_val
+
+
+def test_topk_sorted_matches_torch_topk_sorted_without_ties():
+    rng = np.random.default_rng(8)
+    for n, k in [(100, 10), (1000, 256), (4097, 2048)]:
+        sc = rng.permutation(n).astype(np.float64) * 0.25 - 3.0
+        ref = torch.topk(torch.from_numpy(sc), k, sorted=True)
+        idx, val = orc.select_topk_sorted_row(sc, k)
+        assert np.array_equal(idx, ref.indices.numpy())
+        assert np.array_equal(val, ref.values.numpy())
+
+
+def test_topk_sorted_keeps_the_same_set_as_the_ascending_form():
+    rng = np.random.default_rng(9)
+    for n, k in [(3, 8), (64, 64), (500, 37), (3000, 2048)]:
+        sc = rng.integers(-5, 6, size=n) / 4.0
+        idx, val = orc.select_topk_sorted_row(sc, k)
+        asc = orc.select_topk_row(sc, k)
+        assert np.array_equal(np.sort(idx[idx >= 0]), asc[asc >= 0])
+        assert np.all(np.diff(val[idx >= 0]) <= 0)
+        assert np.all(idx[min(n, k):] == -1) and np.all(np.isneginf(val[min(n, k):]))
+
+
 # ---------------------------------------------------------------- sparse attention
 
 def test_attention_hand_worked_example():
