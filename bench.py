@@ -267,10 +267,43 @@ def decode_bench(args, dsa, inp, tl):
     parity = {"rows_checked": len(brow), "idx_bit_exact": bool(np.array_equal(got_idx, np.asarray(want["idx"]))),
               "max_abs": float(err.max()), "mean_abs": float(err.mean())}
     log(f"decode median {us_median:.1f} us (min {us_min:.1f}); parity {parity}")
-    del dev, ws
+
+    # The torch.topk-shaped top-k on the decode step's own scores (the first region of the decode
+    # workspace, left there by the last step), beside the ascending form.
+    ld = (s_max + 3) // 4 * 4
+    scores = ws.view(torch.float32)[: batch * ld].view(batch, ld)
+    row_len = dev["seq_lens"]
+    tk_ws = torch.empty(dsa.dsa_topk_workspace_size(batch, ld, k), dtype=torch.uint8, device="cuda")
+    idx_s = torch.empty(batch, k, dtype=torch.int32, device="cuda")
+    val_s = torch.empty(batch, k, dtype=torch.float32, device="cuda")
+    timing = {}
+    for name, fn in (("ascending", dsa.dsa_topk), ("sorted", dsa.dsa_topk_sorted)):
+        for _ in range(3):
+            fn(scores, row_len, k, idx_s, val_s, workspace=tk_ws)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            fn(scores, row_len, k, idx_s, val_s, workspace=tk_ws)
+        b.record()
+        torch.cuda.synchronize()
+        timing[name] = a.elapsed_time(b) * 1e3 / 20
+    got_i = idx_s.cpu().numpy()[brow]
+    got_v = val_s.cpu().numpy()[brow].astype(np.float64)
+    ok = True
+    for j, sc in enumerate(want["scores"]):
+        wi, wv = tl.orc.select_topk_sorted_row(sc, k)
+        ok = ok and bool(np.array_equal(got_i[j], wi) and np.array_equal(got_v[j], wv))
+    topk_sorted = {"rows": batch, "row_len": int(lens.max()), "k": k, "us_sorted": timing["sorted"],
+                   "us_ascending": timing["ascending"], "rows_checked": len(brow), "bit_exact": ok}
+    log(f"torch.topk-shaped top-k {timing['sorted']:.1f} us (ascending form {timing['ascending']:.1f} us); "
+        f"bit-exact {ok}")
+    del dev, ws, tk_ws
     torch.cuda.empty_cache()
     return dict(us_median=us_median, us_min=us_min, bytes_step=bytes_step,
-                gbs=bytes_step / (us_median * 1e-6) / 1e9, parity=parity, batch=batch, s_max=s_max)
+                gbs=bytes_step / (us_median * 1e-6) / 1e9, parity=parity, batch=batch, s_max=s_max,
+                topk_sorted=topk_sorted)
 
 
 def cpu_baseline(args, pi, tl):
@@ -363,6 +396,7 @@ def main():
         line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": dec["gbs"] / PEAK_HBM_GBS}
         line["parity_decode"] = dec["parity"]
+        line["topk_sorted_decode_scores"] = dec["topk_sorted"]
     print(json.dumps(line), flush=True)
 
 

@@ -115,6 +115,19 @@ int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, 
              void* stream);
 
 /*
+ * Deterministic top-k in the shape of torch.topk(sorted=True) (digest section 八: a
+ * deterministic top-k in place of torch.topk, so training and inference keep identical sets).
+ *
+ * Same arguments, workspace and set as dsa_topk; only the order differs.  idx_out[i, :] holds
+ * the kept positions by descending score, equal scores by ascending position; values_out
+ * (optional) the scores in that order, -0.0 returned as +0.0.  A row with row_len < k keeps all
+ * its positions and is padded at the end with -1 (values -inf).
+ */
+int dsa_topk_sorted(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k,
+                    int32_t* idx_out, float* values_out, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
  * Sparse GQA attention over selected positions (digest section 一 and the GQA adaptation).
  *
  * q   [total_tokens, hq, head_dim]  bf16

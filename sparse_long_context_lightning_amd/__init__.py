@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     dsa_sparse_gqa_attn,
     dsa_status_string,
     dsa_topk,
+    dsa_topk_sorted,
     dsa_topk_workspace_size,
     load,
     prefill,

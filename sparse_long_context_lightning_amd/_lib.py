@@ -25,8 +25,8 @@ DSA_MAX_TOP_K = 2048
 
 EXPORTED = (
     "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
-    "dsa_topk", "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill", "dsa_decode_workspace_size",
-    "dsa_decode",
+    "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill",
+    "dsa_decode_workspace_size", "dsa_decode",
 )
 
 
@@ -60,6 +60,7 @@ def load():
         "dsa_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
         "dsa_topk_workspace_size": ([_I, _I64, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_topk": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
+        "dsa_topk_sorted": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_prefill_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P,
@@ -138,6 +139,15 @@ def dsa_topk(scores, row_len, k, idx_out, values_out=None, workspace=None, ld=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().dsa_topk(_ptr(scores), ld, rows, _ptr(row_len), k, _ptr(idx_out), _ptr(values_out),
                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dsa_topk_sorted(scores, row_len, k, idx_out, values_out=None, workspace=None, ld=None, stream=None):
+    """dsa_topk in torch.topk(sorted=True) order: descending score, equal scores by position."""
+    rows = scores.shape[0]
+    ld = scores.shape[1] if ld is None else ld
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().dsa_topk_sorted(_ptr(scores), ld, rows, _ptr(row_len), k, _ptr(idx_out), _ptr(values_out),
+                                  _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def dsa_sparse_gqa_attn(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=None, stream=None):

@@ -186,8 +186,10 @@ int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes) {
   return DSA_OK;
 }
 
-int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
-             float* values_out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int topk_entry(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
+               float* values_out, void* workspace, size_t workspace_bytes, void* stream, bool ranked) {
   g_last_error[0] = 0;
   DSA_NONNULL(scores);
   DSA_NONNULL(row_len);
@@ -209,9 +211,25 @@ int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, 
   a.len_base = 0;
   a.k = k;
   a.idx_out = idx_out;
-  a.values_out = values_out;
+  a.values_out = ranked ? nullptr : values_out;
   a.workspace = need ? workspace : nullptr;
-  return hip_status(dsa::launch_topk(a, static_cast<hipStream_t>(stream)), "top-k launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DSA_TRY(hip_status(dsa::launch_topk(a, s), "top-k launch"));
+  if (!ranked) return DSA_OK;
+  a.values_out = values_out;
+  return hip_status(dsa::launch_topk_rank(a, s), "top-k rank-order launch");
+}
+
+}  // namespace
+
+int dsa_topk(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
+             float* values_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_entry(scores, ld, rows, row_len, k, idx_out, values_out, workspace, workspace_bytes, stream, false);
+}
+
+int dsa_topk_sorted(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
+                    float* values_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return topk_entry(scores, ld, rows, row_len, k, idx_out, values_out, workspace, workspace_bytes, stream, true);
 }
 
 int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32_t* idx, int k_sel,

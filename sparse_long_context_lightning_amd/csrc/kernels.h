@@ -73,6 +73,9 @@ struct SparseAttnArgs {
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
 hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// Reorder each row's selected positions (idx_out, as launch_topk leaves them) by descending score,
+// equal scores by ascending position; values_out (optional) gets the scores in that order.
+hipError_t launch_topk_rank(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn(const SparseAttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const SparseAttnArgs& a, hipStream_t s);
 

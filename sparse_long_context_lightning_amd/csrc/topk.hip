@@ -267,6 +267,54 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                tau, n_eq, out, vout);
 }
 
+// Rank order for the torch.topk-shaped form: one 256-thread workgroup per row reorders the
+// row's selected positions (as the selection kernels leave them, ascending) by descending
+// score, equal scores by ascending position.  Each entry becomes the 64-bit word
+// (~key << 32) | position, so one ascending bitonic sort over the next power of two >= k gives
+// that order; padding (-1) sorts last as all-ones.
+constexpr int kRankMax = 2048;
+
+__global__ __launch_bounds__(256) void topk_rank_kernel(const float* __restrict__ scores, long long ld, int k,
+                                                       int* __restrict__ idx_out, float* __restrict__ values_out) {
+  __shared__ unsigned long long w[kRankMax];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  int np2 = 1;
+  while (np2 < k) np2 <<= 1;
+  int* out = idx_out + (size_t)row * k;
+  const float* src = scores + (size_t)row * ld;
+  for (int i = tid; i < np2; i += 256) {
+    unsigned long long c = ~0ull;
+    if (i < k) {
+      const int p = out[i];
+      if (p >= 0) c = ((unsigned long long)(~float_key(src[p])) << 32) | (uint32_t)p;
+    }
+    w[i] = c;
+  }
+  __syncthreads();
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (np2 >> 1); i += 256) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const unsigned long long a = w[lo], b = w[hi];
+        const bool up = (lo & size) == 0;
+        if ((a > b) == up) {
+          w[lo] = b;
+          w[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += 256) {
+    const unsigned long long c = w[i];
+    const bool pad = c == ~0ull;
+    out[i] = pad ? -1 : (int)(uint32_t)c;
+    if (values_out) values_out[(size_t)row * k + i] = pad ? -INFINITY : key_float(~(uint32_t)(c >> 32));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
@@ -274,6 +322,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s) {
   if (a.workspace && a.ld <= kTopkWaveMaxLd) return launch_topk_wave(a, s);
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.rows), dim3(kThreads), 0, s, a.scores, a.ld, a.rows, a.row_len,
                      a.len_base, a.k, a.idx_out, a.values_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rank(const TopkArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.k > kRankMax) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_rank_kernel, dim3((unsigned)a.rows), dim3(256), 0, s, a.scores, a.ld, a.k, a.idx_out,
+                     a.values_out);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -94,6 +94,9 @@ def test_other_entry_points_reject_bad_arguments():
     assert lib.dsa_topk(FAKE, 63, 4, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk(None, 64, 4, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     assert lib.dsa_topk(FAKE, 64, 4, None, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_sorted(FAKE, 64, 4, FAKE, 4096, FAKE, None, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_topk_sorted(FAKE, 62, 4, FAKE, 8, FAKE, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_topk_sorted(FAKE, 64, 4, FAKE, 8, None, None, None, 0, None) == dsa.DSA_ERR_INVALID_ARG
     # sparse attention
     assert lib.dsa_sparse_gqa_attn(FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1, 64, 8, 2, 128, ctypes.c_float(0.1), FAKE, None,
                                    None) == dsa.DSA_ERR_INVALID_ARG
