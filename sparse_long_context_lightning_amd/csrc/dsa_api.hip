@@ -84,7 +84,6 @@ int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) 
   if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
 
 constexpr int kKeySplit = 2048;        // keys per prefill-indexer workgroup
-constexpr int kDecodeKeysPerWave = 1024;
 constexpr int kMinChunkRows = 64;
 constexpr int kDefaultChunkRows = 2048;
 
@@ -436,7 +435,6 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   ia.d_idx = d_idx;
   ia.scores = scores;
   ia.ld = ld;
-  ia.keys_per_wave = kDecodeKeysPerWave;
   DSA_TRY(hip_status(dsa::launch_indexer_decode(ia, s), "decode indexer launch"));
 
   dsa::TopkArgs t;

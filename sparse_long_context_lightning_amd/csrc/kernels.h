@@ -27,7 +27,6 @@ struct IndexerDecodeArgs {
   int batch, s_max, max_len, h_idx, d_idx;
   float* scores;
   long long ld;
-  int keys_per_wave;  // multiple of 64
 };
 
 // Row lengths come from row_len[i] if non-null, else len_base + i + 1 (causal prefill rows).
