@@ -29,6 +29,7 @@ listed in the design notes):
   R5  ties go to the lower position; -0 equals +0
   R6  selected positions are returned in ascending order
   R21 the torch.topk-shaped variant orders the same set by descending score, then position
+  R22 the backward recomputes the softmax over the selected keys; every index entry is one key
   R8  GQA head h reads KV head h // (Hq // Hkv)
   R9  softmax scale passed explicitly (1/sqrt(D) by default), lse is natural-log and
       includes the scale
@@ -172,6 +173,67 @@ def sparse_gqa_attention_row(q_row: np.ndarray, k_seq: np.ndarray, v_seq: np.nda
         lse[h] = m + math.log(denom)
         wsum[h] = p.sum()
     return o, lse, wsum
+
+
+def sparse_gqa_attention_row_grad(q_row: np.ndarray, k_seq: np.ndarray, v_seq: np.ndarray,
+                                  idx_row: np.ndarray, softmax_scale: float, dout_row: np.ndarray):
+    """Gradients of the selected-position attention of one token (the sparse adaptation stage
+    of source A, section 一, trains the whole model through this attention; reading R22).
+
+    Same arguments as sparse_gqa_attention_row plus dout_row [Hq, D], the gradient of the loss
+    with respect to O.  Per query head, with p the softmax weights over the selected keys:
+        dp_s = <dO, v_s>,   dz_s = p_s (dp_s - sum_u p_u dp_u)      (softmax backward)
+        dq   = scale * sum_s dz_s k_s
+        dk_s += scale * dz_s q,   dv_s += p_s dO                   (summed over the group's heads)
+    Each index entry is one key, so a repeated entry contributes once per occurrence.
+    returns (dq [Hq, D], dk_seq [S, Hkv, D], dv_seq [S, Hkv, D]) float64: this row's contributions
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    do = np.asarray(dout_row, dtype=np.float64)
+    hq, d = q.shape
+    n_pos, hkv = k_seq.shape[0], k_seq.shape[1]
+    g_size = hq // hkv
+    sel = np.asarray([int(i) for i in idx_row if 0 <= int(i) < n_pos], dtype=np.int64)
+    dq = np.zeros((hq, d), dtype=np.float64)
+    dk = np.zeros((n_pos, hkv, d), dtype=np.float64)
+    dv = np.zeros((n_pos, hkv, d), dtype=np.float64)
+    if sel.size == 0:
+        return dq, dk, dv
+    for h in range(hq):
+        g = h // g_size
+        keys = np.asarray(k_seq[sel, g, :], dtype=np.float64)    # [n_sel, D]
+        vals = np.asarray(v_seq[sel, g, :], dtype=np.float64)
+        z = softmax_scale * (keys @ q[h])
+        e = np.exp(z - z.max())
+        p = e / e.sum()
+        dp = vals @ do[h]
+        dz = p * (dp - p @ dp)
+        dq[h] = softmax_scale * (dz @ keys)
+        np.add.at(dk[:, g, :], sel, softmax_scale * np.outer(dz, q[h]))
+        np.add.at(dv[:, g, :], sel, np.outer(p, do[h]))
+    return dq, dk, dv
+
+
+def sparse_attention_grad(q, k, v, idx, cu_seqlens, dout, softmax_scale=None):
+    """Backward of the sparse GQA attention over packed sequences (reading R22): dq for every
+    row, dk and dv summed over every row and head that selected each position.  Entries of
+    idx outside a row's causal prefix are ignored, as in the forward."""
+    q = np.asarray(q, dtype=np.float64)
+    total, hq, d = q.shape
+    scale = default_softmax_scale(d) if softmax_scale is None else softmax_scale
+    cu = [int(x) for x in cu_seqlens]
+    dq = np.zeros_like(q)
+    dk = np.zeros(np.shape(k), dtype=np.float64)
+    dv = np.zeros(np.shape(v), dtype=np.float64)
+    for b in range(len(cu) - 1):
+        o = cu[b]
+        for t in range(cu[b + 1] - o):
+            r = o + t
+            gq, gk, gv = sparse_gqa_attention_row_grad(q[r], k[o:o + t + 1], v[o:o + t + 1], idx[r], scale, dout[r])
+            dq[r] = gq
+            dk[o:o + t + 1] += gk
+            dv[o:o + t + 1] += gv
+    return dq, dk, dv
 
 
 def _seq_of_row(cu: list, r: int) -> int:

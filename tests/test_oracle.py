@@ -281,6 +281,86 @@ def test_attention_index_order_is_irrelevant():
 
 # ---------------------------------------------------------------- composition
 
+# ---------------------------------------------------------------- sparse attention backward
+
+def _sparse_loss(q, k, v, idx, cu, dout, scale):
+    """sum(dout * O) through the oracle forward: its gradient is what the backward returns."""
+    total = 0.0
+    for b in range(len(cu) - 1):
+        o = cu[b]
+        for t in range(cu[b + 1] - o):
+            r = o + t
+            sel = np.asarray([i for i in idx[r] if 0 <= i <= t])
+            out, _, _ = orc.sparse_gqa_attention_row(q[r], k[o:o + t + 1], v[o:o + t + 1], sel, scale)
+            total += float((out * dout[r]).sum())
+    return total
+
+
+def test_attention_grad_matches_central_differences():
+    rng = np.random.default_rng(31)
+    lens, hq, hkv, d, k_sel = [5, 4], 4, 2, 6, 3
+    cu = [0, 5, 9]
+    total = sum(lens)
+    q, k, v = _rand_attn(32, total, hq, hkv, d)
+    dout = rng.standard_normal((total, hq, d))
+    idx = np.full((total, k_sel), -1, dtype=np.int64)
+    for b in range(2):
+        for t in range(lens[b]):
+            n = int(rng.integers(1, min(t + 1, k_sel) + 1))
+            idx[cu[b] + t, :n] = rng.choice(t + 1, size=n, replace=False)
+    idx[6, 1] = 7 if idx[6, 1] < 0 else idx[6, 1]     # an out-of-prefix entry (t = 1) is ignored
+    scale = 0.37
+    dq, dk, dv = orc.sparse_attention_grad(q, k, v, idx, cu, dout, scale)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(*x.shape):
+            old = x[pos]
+            x[pos] = old + eps
+            lp = _sparse_loss(q, k, v, idx, cu, dout, scale)
+            x[pos] = old - eps
+            lm = _sparse_loss(q, k, v, idx, cu, dout, scale)
+            x[pos] = old
+            num[pos] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+def test_attention_grad_with_all_positions_is_dense_causal_gqa_autograd():
+    t, hq, hkv, d = 24, 8, 2, 16
+    q, k, v = _rand_attn(33, t, hq, hkv, d)
+    dout = np.random.default_rng(34).standard_normal((t, hq, d))
+    idx = np.full((t, t), -1, dtype=np.int64)
+    for r in range(t):
+        idx[r, :r + 1] = np.arange(r + 1)
+    scale = 1 / math.sqrt(d)
+    dq, dk, dv = orc.sparse_attention_grad(q, k, v, idx, [0, t], dout, scale)
+    qt = torch.from_numpy(q).permute(1, 0, 2).unsqueeze(0).requires_grad_(True)
+    kt = torch.from_numpy(k).permute(1, 0, 2).unsqueeze(0).requires_grad_(True)
+    vt = torch.from_numpy(v).permute(1, 0, 2).unsqueeze(0).requires_grad_(True)
+    g = hq // hkv
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(g, dim=1), vt.repeat_interleave(g, dim=1), is_causal=True, scale=scale)
+    out.backward(torch.from_numpy(dout).permute(1, 0, 2).unsqueeze(0))
+    np.testing.assert_allclose(dq, qt.grad[0].permute(1, 0, 2).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad[0].permute(1, 0, 2).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_attention_grad_single_position_closed_form():
+    # one selected key: p = 1, so dq = 0, dk = 0 and dv = sum of the group's dO rows
+    t, hq, hkv, d = 3, 4, 2, 5
+    q, k, v = _rand_attn(35, t, hq, hkv, d)
+    dout = np.random.default_rng(36).standard_normal((t, hq, d))
+    idx = np.array([[0], [0], [2]])
+    dq, dk, dv = orc.sparse_attention_grad(q, k, v, idx, [0, t], dout, 0.5)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    want = np.zeros_like(v)
+    for r, s in ((0, 0), (1, 0), (2, 2)):
+        for h in range(hq):
+            want[s, h // 2] += dout[r, h]
+    np.testing.assert_allclose(dv, want, atol=1e-14)
+
+
 def test_packed_prefill_equals_separate_sequences():
     lens = [20, 7, 13]
     pi = inp.prefill_inputs(lens, 2, 8, 4, 2, 16, 6, seed=9)
