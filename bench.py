@@ -1,6 +1,6 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-bwd] [--no-cpu-baseline]
 
 A step is one pass of the whole prefill path (indexer -> top-k -> sparse GQA attention) over
 the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexer heads of
@@ -8,7 +8,9 @@ dim 128, 32 query / 4 KV heads of dim 128, keys in 16-token blocks), with every 
 resident in HBM.  The path is driven through the C ABI's separate entry points in exactly the
 chunk schedule dsa_prefill uses, so HIP events on the launch stream time each kernel inside
 the timed region; the fused dsa_prefill call is timed as well and reported beside it.  The
-decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill.
+decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
+the torch.topk-shaped top-k on the decode scores and the backward of the sparse attention on
+the 32K prefill (context lines beside the headline value).
 
 One JSON line is printed last.
 """
@@ -62,6 +64,8 @@ def parse():
     ap.add_argument("--workload", default=PREFILL)
     ap.add_argument("--decode-workload", default=DECODE)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--bwd-workload", default="c2_prefill_32k")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -306,6 +310,54 @@ def decode_bench(args, dsa, inp, tl):
                 topk_sorted=topk_sorted)
 
 
+def attn_bwd_bench(args, dsa, inp, tl):
+    """Backward of the sparse attention on the 32K prefill (training side), after one fused
+    prefill that provides O, lse and the index sets; dO is synthetic."""
+    import torch
+    pi = inp.workload(args.bwd_workload)
+    dev = tl.upload_prefill(pi)
+    k = pi.top_k
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                pi.cu_seqlens, k)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dout = torch.randn(out.shape, generator=g, device="cuda").to(torch.bfloat16)
+    dq = torch.empty(out.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(dev["k"].shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+
+    def run():
+        dsa.dsa_sparse_gqa_attn_bwd(dev["q"], dev["k"], dev["v"], out, lse, dout, idx, dev["cu"], dq, dk, dv)
+
+    run()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(3):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 3
+    a.record()
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out, lse)
+    b.record()
+    torch.cuda.synchronize()
+    fwd_ms = a.elapsed_time(b)
+    lens = [int(x) for x in pi.seq_lens]
+    hkv, d = pi.k.shape[1], pi.k.shape[2]
+    sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
+    # per selected (row, KV group): K and V rows gathered (2 x 256 B) and 2 x 128 fp32 atomics
+    algo_bytes = sel_pairs * hkv * (2 * d * 2 + 2 * d * 4)
+    total = sum(lens)
+    log(f"attention backward {ms:.1f} ms (forward {fwd_ms:.1f} ms) on {args.bwd_workload}")
+    del dev, dq, dk, dv, dout, out, lse, idx
+    torch.cuda.empty_cache()
+    return {"workload": args.bwd_workload, "ms": ms, "forward_ms": fwd_ms, "tokens_per_s": total / (ms * 1e-3),
+            "algorithmic_gb_per_s": algo_bytes / (ms * 1e-3) / 1e9,
+            "note": "dq, dk, dv from dO; dk/dv scattered with fp32 atomics (bound by L2 atomic throughput)"}
+
+
 def cpu_baseline(args, pi, tl):
     """The oracle as it stands, on a bounded sample of rows of the same workload."""
     try:
@@ -350,6 +402,7 @@ def main():
     dsa.load()
     pre = prefill_bench(args, dsa, inp, tl)
     dec = None if args.no_decode else decode_bench(args, dsa, inp, tl)
+    bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp, tl)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"], tl)
 
     total = pre["rows_total"]
@@ -397,6 +450,8 @@ def main():
                                    "frac": dec["gbs"] / PEAK_HBM_GBS}
         line["parity_decode"] = dec["parity"]
         line["topk_sorted_decode_scores"] = dec["topk_sorted"]
+    if bwd is not None:
+        line["sparse_attn_backward"] = bwd
     print(json.dumps(line), flush=True)
 
 

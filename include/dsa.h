@@ -144,6 +144,29 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
                         void* out, float* lse, void* stream);
 
 /*
+ * Backward of dsa_sparse_gqa_attn (digest section 一: the sparse adaptation stage trains the
+ * whole model in the sparse mode, so gradients pass through this attention).
+ *
+ * q, k, v, idx, k_sel, cu_seqlens, batch, total_tokens, hq, hkv, head_dim, softmax_scale
+ *                                   as for the forward call
+ * out  [total_tokens, hq, head_dim] bf16   the forward's output O
+ * lse  [total_tokens, hq] float            the forward's log-sum-exp (required)
+ * dout [total_tokens, hq, head_dim] bf16   gradient of the loss with respect to O
+ * dq   [total_tokens, hq, head_dim] float  output, written
+ * dk, dv [total_tokens, hkv, head_dim] float  outputs: zeroed by the call, then every
+ *                                   (row, head, selected position) adds its contribution with
+ *                                   float atomics, so the summation order (and the last bits)
+ *                                   can vary from run to run.
+ * The softmax weights are recomputed from lse; they and dZ are rounded to bf16 as MFMA
+ * operands (fp32 accumulation).
+ */
+int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const float* lse, const void* dout, const int32_t* idx, int k_sel,
+                            const int32_t* cu_seqlens, int batch, int total_tokens,
+                            int hq, int hkv, int head_dim, float softmax_scale,
+                            float* dq, float* dk, float* dv, void* stream);
+
+/*
  * Workspace bytes for dsa_prefill: a score buffer for a chunk of query rows (never the whole
  * L x L matrix) plus the top-k scratch of those rows; the default chunk is 2048 rows.  A larger
  * workspace lets the call use larger chunks, a smaller one (down to 64 rows) smaller ones.

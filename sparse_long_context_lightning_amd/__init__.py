@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     dsa_prefill,
     dsa_prefill_workspace_size,
     dsa_sparse_gqa_attn,
+    dsa_sparse_gqa_attn_bwd,
     dsa_status_string,
     dsa_topk,
     dsa_topk_sorted,

@@ -25,8 +25,8 @@ DSA_MAX_TOP_K = 2048
 
 EXPORTED = (
     "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
-    "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_prefill_workspace_size", "dsa_prefill",
-    "dsa_decode_workspace_size", "dsa_decode",
+    "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
+    "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode",
 )
 
 
@@ -62,6 +62,8 @@ def load():
         "dsa_topk": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_topk_sorted": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+        "dsa_sparse_gqa_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
+                                    _I),
         "dsa_prefill_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P,
                          _SZ, _P], _I),
@@ -158,6 +160,16 @@ def dsa_sparse_gqa_attn(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=N
     _check(load().dsa_sparse_gqa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), idx.shape[1], _ptr(cu_seqlens),
                                       cu_seqlens.shape[0] - 1, total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
                                       _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_bwd(q, k, v, out, lse, dout, idx, cu_seqlens, dq, dk, dv, softmax_scale=None, stream=None):
+    """Backward of dsa_sparse_gqa_attn: dq written, dk / dv zeroed and accumulated (float32)."""
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    _check(load().dsa_sparse_gqa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(idx),
+                                          idx.shape[1], _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, total, hq, hkv, d,
+                                          scale, _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def dsa_prefill_workspace_size(batch, total_tokens, max_seqlen, hq, hkv, head_dim, h_idx, d_idx, top_k) -> int:

@@ -268,6 +268,55 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
   return hip_status(dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
 }
 
+int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                            const void* dout, const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch,
+                            int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, float* dq,
+                            float* dk, float* dv, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(out);
+  DSA_NONNULL(lse);
+  DSA_NONNULL(dout);
+  DSA_NONNULL(idx);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(dq);
+  DSA_NONNULL(dk);
+  DSA_NONNULL(dv);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(dout);
+  DSA_ALIGNED(dq);
+  DSA_ALIGNED(dk);
+  DSA_ALIGNED(dv);
+  if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
+  if (k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  if (total_tokens == 0) return DSA_OK;
+  dsa::SparseAttnBwdArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  return hip_status(dsa::launch_sparse_attn_bwd(a, static_cast<hipStream_t>(stream)), "sparse attention backward launch");
+}
+
 int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv, int head_dim, int h_idx,
                                int d_idx, int top_k, size_t* bytes) {
   g_last_error[0] = 0;

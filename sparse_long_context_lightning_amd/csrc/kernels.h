@@ -69,6 +69,25 @@ struct SparseAttnArgs {
   float* part_ml;   // [rows, hq, nsplit, 2] (running max in log2 units, sum)
 };
 
+// Backward of the sparse attention (prefill layout): dq written, dk / dv zeroed then accumulated.
+struct SparseAttnBwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;   // forward output O
+  const uint16_t* dout;  // dL/dO
+  const float* lse;      // forward log-sum-exp (natural log)
+  const int* idx;
+  int k_sel;
+  const int* cu_seqlens;
+  int batch;
+  int rows, hq, hkv;
+  float softmax_scale;
+  float* dq;  // [rows, hq, 128]
+  float* dk;  // [rows, hkv, 128]
+  float* dv;  // [rows, hkv, 128]
+};
+
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
 hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
@@ -77,5 +96,6 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_rank(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn(const SparseAttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const SparseAttnArgs& a, hipStream_t s);
+hipError_t launch_sparse_attn_bwd(const SparseAttnBwdArgs& a, hipStream_t s);
 
 }  // namespace dsa
