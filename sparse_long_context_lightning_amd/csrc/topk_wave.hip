@@ -592,12 +592,15 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(topk_threshold_kernel, dim3(groups), dim3(256), 0, s, a.scores, a.ld, a.rows, a.row_len,
                        a.len_base, a.k, tau_lo, cnt);
   }
-  // Segment length: enough waves to keep every CU streaming, in multiples of 2048 positions.
+  // Segment length: enough waves to keep every CU streaming, in multiples of 2048 positions,
+  // over the longest row actually present (causal rows end at len_base + rows, often far below
+  // the stride), so a short row is split over several waves instead of one wave's serial rounds.
   const long long want_waves = 16384;
+  const long long eff_len = a.row_len ? a.ld : std::min<long long>(a.ld, (long long)a.len_base + a.rows);
   long long nseg = (want_waves + a.rows - 1) / a.rows;
-  long long seg_len = (a.ld + nseg - 1) / nseg;
+  long long seg_len = (eff_len + nseg - 1) / nseg;
   seg_len = (seg_len + 2047) / 2048 * 2048;
-  nseg = (a.ld + seg_len - 1) / seg_len;
+  nseg = (eff_len + seg_len - 1) / seg_len;
   // Workgroups of 16 waves when rows are few and long (fewer atomics per row), else 4.
   if (nseg >= 16) {
     nseg = (nseg + 15) / 16 * 16;
