@@ -83,7 +83,7 @@ int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) 
 #define DSA_ALIGNED(p) \
   if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
 
-constexpr int kKeySplit = 2048;        // keys per prefill-indexer workgroup
+constexpr int kKeySplit = 4096;        // keys per prefill-indexer workgroup
 constexpr int kMinChunkRows = 64;
 constexpr int kDefaultChunkRows = 2048;
 
