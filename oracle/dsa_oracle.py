@@ -30,6 +30,8 @@ listed in the design notes):
   R6  selected positions are returned in ascending order
   R21 the torch.topk-shaped variant orders the same set by descending score, then position
   R22 the backward recomputes the softmax over the selected keys; every index entry is one key
+  R23 warm-up target = head-mean of the dense causal attention distribution; KL(target || indexer),
+      summed over rows; the target is fixed (the attention is not trained in that stage)
   R8  GQA head h reads KV head h // (Hq // Hkv)
   R9  softmax scale passed explicitly (1/sqrt(D) by default), lse is natural-log and
       includes the scale
@@ -234,6 +236,89 @@ def sparse_attention_grad(q, k, v, idx, cu_seqlens, dout, softmax_scale=None):
             dk[o:o + t + 1] += gk
             dv[o:o + t + 1] += gv
     return dq, dk, dv
+
+
+def attention_head_mean_row(q_row: np.ndarray, k_prefix: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Target of the indexer's dense warm-up (source A, section 一: with the full attention left
+    unchanged, the indexer is trained to follow the full attention distribution, the gap measured
+    by KL divergence; reading R23): the causal softmax of every query head over the whole prefix,
+    averaged over the query heads (GQA head h reads KV head h // G).
+
+    q_row [Hq, D], k_prefix [n, Hkv, D] -> [n] float64, summing to 1
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    hq = q.shape[0]
+    g_size = hq // k_prefix.shape[1]
+    acc = np.zeros(k_prefix.shape[0], dtype=np.float64)
+    for h in range(hq):
+        z = softmax_scale * (np.asarray(k_prefix[:, h // g_size, :], dtype=np.float64) @ q[h])
+        e = np.exp(z - z.max())
+        acc += e / e.sum()
+    return acc / hq
+
+
+def indexer_kl_row(scores_row: np.ndarray, target_row: np.ndarray):
+    """KL(target || softmax(scores)) over one causal prefix, and its gradient with respect to
+    the scores (reading R23; the target is fixed):
+        r = softmax(I),  loss = sum_s p_s (log p_s - log r_s)  (terms with p_s = 0 are 0),
+        dloss/dI_s = r_s - p_s
+    returns (loss float, grad [n] float64)
+    """
+    i_row = np.asarray(scores_row, dtype=np.float64)
+    p = np.asarray(target_row, dtype=np.float64)
+    m = i_row.max()
+    lse = m + math.log(np.exp(i_row - m).sum())
+    log_r = i_row - lse
+    pos = p > 0
+    loss = float((p[pos] * (np.log(p[pos]) - log_r[pos])).sum())
+    return loss, np.exp(log_r) - p
+
+
+def index_scores_row_grad(q_idx_row: np.ndarray, w_row: np.ndarray, k_idx_prefix: np.ndarray,
+                          dscores: np.ndarray):
+    """Backward of index_scores_row (reading R1) for one query row: with c[j, s] = <q_j, k_s>,
+        dw_j = sum_s dI_s max(0, c[j, s])
+        dq_j = w_j sum_s dI_s [c[j, s] > 0] k_s
+        dk_s = dI_s sum_j w_j [c[j, s] > 0] q_j
+    (the ReLU's derivative is taken as 0 at 0).
+    returns (dq [H_I, d_I], dw [H_I], dk [n, d_I]) float64
+    """
+    q = np.asarray(q_idx_row, dtype=np.float64)
+    w = np.asarray(w_row, dtype=np.float64)
+    k = np.asarray(k_idx_prefix, dtype=np.float64)
+    d_i = np.asarray(dscores, dtype=np.float64)
+    c = q @ k.T                                   # [H_I, n]
+    dw = np.maximum(c, 0.0) @ d_i
+    gmat = (w[:, None] * d_i[None, :]) * (c > 0)  # d loss / d c
+    return gmat @ k, dw, gmat.T @ q
+
+
+def indexer_warmup_loss_grads(q, k, q_idx, k_idx, w, cu_seqlens, softmax_scale=None):
+    """Dense warm-up loss of the indexer (reading R23) over packed sequences: the sum over rows
+    of KL(head-mean causal attention distribution || softmax of the row's indexer scores), and
+    its gradients with respect to q_idx, k_idx and w (the attention inputs are not trained).
+    returns (row_loss [T], dq_idx [T, H_I, d_I], dk_idx [T, d_I], dw [T, H_I]) float64
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total, hq, d = q.shape
+    scale = default_softmax_scale(d) if softmax_scale is None else softmax_scale
+    cu = [int(x) for x in cu_seqlens]
+    row_loss = np.zeros(total, dtype=np.float64)
+    dq_idx = np.zeros(np.shape(q_idx), dtype=np.float64)
+    dk_idx = np.zeros(np.shape(k_idx), dtype=np.float64)
+    dw = np.zeros(np.shape(w), dtype=np.float64)
+    for b in range(len(cu) - 1):
+        o = cu[b]
+        for t in range(cu[b + 1] - o):
+            r = o + t
+            target = attention_head_mean_row(q[r], k[o:o + t + 1], scale)
+            scores = index_scores_row(q_idx[r], w[r], k_idx[o:o + t + 1])
+            row_loss[r], d_i = indexer_kl_row(scores, target)
+            gq, gw, gk = index_scores_row_grad(q_idx[r], w[r], k_idx[o:o + t + 1], d_i)
+            dq_idx[r] = gq
+            dw[r] = gw
+            dk_idx[o:o + t + 1] += gk
+    return row_loss, dq_idx, dk_idx, dw
 
 
 def _seq_of_row(cu: list, r: int) -> int:

@@ -361,6 +361,106 @@ def test_attention_grad_single_position_closed_form():
     np.testing.assert_allclose(dv, want, atol=1e-14)
 
 
+# ---------------------------------------------------------------- indexer warm-up (KL) loss
+
+def _torch_warmup(q, k, qi, ki, w, lens, scale):
+    """The warm-up loss written with torch ops (masked dense matrices, autograd for the gradients)."""
+    out_loss, grads = [], []
+    qi_t = torch.from_numpy(qi).requires_grad_(True)
+    ki_t = torch.from_numpy(ki).requires_grad_(True)
+    w_t = torch.from_numpy(w).requires_grad_(True)
+    total = 0
+    o = 0
+    loss_sum = torch.zeros((), dtype=torch.float64)
+    for n in lens:
+        qs, ks = torch.from_numpy(q[o:o + n]), torch.from_numpy(k[o:o + n])
+        g = qs.shape[1] // ks.shape[1]
+        causal = torch.tril(torch.ones(n, n, dtype=torch.bool))
+        logits = scale * torch.einsum("thd,shd->hts", qs, ks.repeat_interleave(g, dim=1))
+        logits = logits.masked_fill(~causal, float("-inf"))
+        target = torch.softmax(logits, dim=-1).mean(dim=0)                       # [t, s]
+        c = torch.einsum("tjd,sd->tjs", qi_t[o:o + n], ki_t[o:o + n])
+        scores = (w_t[o:o + n, :, None] * torch.relu(c)).sum(dim=1)              # [t, s]
+        log_r = torch.log_softmax(scores.masked_fill(~causal, float("-inf")), dim=-1)
+        safe = torch.where(target > 0, target, torch.ones_like(target))
+        kl = torch.where(target > 0, target * (torch.log(safe) - log_r), torch.zeros_like(target)).sum(dim=-1)
+        out_loss.append(kl.detach().numpy())
+        loss_sum = loss_sum + kl.sum()
+        o += n
+    loss_sum.backward()
+    return np.concatenate(out_loss), qi_t.grad.numpy(), ki_t.grad.numpy(), w_t.grad.numpy()
+
+
+def test_warmup_loss_and_grads_match_torch_autograd():
+    rng = np.random.default_rng(41)
+    lens, hq, hkv, d, h_i, d_i = [9, 5], 4, 2, 8, 3, 6
+    total = sum(lens)
+    q, k, _ = _rand_attn(42, total, hq, hkv, d)
+    qi = rng.standard_normal((total, h_i, d_i))
+    ki = rng.standard_normal((total, d_i))
+    w = rng.standard_normal((total, h_i))                 # signed weights: both branches of ReLU matter
+    scale = 0.3
+    got = orc.indexer_warmup_loss_grads(q, k, qi, ki, w, [0, 9, 14], scale)
+    want = _torch_warmup(q, k, qi, ki, w, lens, scale)
+    for name, a, b in zip(("loss", "dq_idx", "dk_idx", "dw"), got, want):
+        np.testing.assert_allclose(a, b, atol=1e-12, err_msg=name)
+
+
+def test_warmup_grads_match_central_differences():
+    rng = np.random.default_rng(43)
+    lens, hq, hkv, d, h_i, d_i = [6], 2, 1, 4, 2, 3
+    q, k, _ = _rand_attn(44, 6, hq, hkv, d)
+    qi = rng.standard_normal((6, h_i, d_i))
+    ki = rng.standard_normal((6, d_i))
+    w = rng.standard_normal((6, h_i))
+    _, dq, dk, dw = orc.indexer_warmup_loss_grads(q, k, qi, ki, w, [0, 6], 0.5)
+
+    def total_loss():
+        return orc.indexer_warmup_loss_grads(q, k, qi, ki, w, [0, 6], 0.5)[0].sum()
+
+    eps = 1e-6
+    for name, x, g in (("q_idx", qi, dq), ("k_idx", ki, dk), ("w", w, dw)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(*x.shape):
+            old = x[pos]
+            x[pos] = old + eps
+            lp = total_loss()
+            x[pos] = old - eps
+            lm = total_loss()
+            x[pos] = old
+            num[pos] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+def test_kl_is_zero_when_the_indexer_matches_the_target_and_positive_otherwise():
+    rng = np.random.default_rng(45)
+    p = rng.random(50)
+    p /= p.sum()
+    loss, grad = orc.indexer_kl_row(np.log(p) + 3.0, p)
+    assert abs(loss) < 1e-12 and np.max(np.abs(grad)) < 1e-12
+    loss2, grad2 = orc.indexer_kl_row(rng.standard_normal(50), p)
+    assert loss2 > 0 and abs(grad2.sum()) < 1e-12
+    # a target with zeros: those terms add nothing to the loss
+    p0 = p.copy()
+    p0[:10] = 0
+    p0 /= p0.sum()
+    sc = rng.standard_normal(50)
+    r = np.exp(sc - sc.max())
+    r /= r.sum()
+    want = float(np.sum(p0[10:] * (np.log(p0[10:]) - np.log(r[10:]))))
+    assert abs(orc.indexer_kl_row(sc, p0)[0] - want) < 1e-12
+
+
+def test_head_mean_target_is_a_distribution_and_single_head_softmax():
+    q, k, _ = _rand_attn(46, 7, 4, 2, 8)
+    for t in range(7):
+        p = orc.attention_head_mean_row(q[t], k[:t + 1], 0.4)
+        assert p.shape == (t + 1,) and abs(p.sum() - 1) < 1e-12 and np.all(p > 0)
+    q1, k1, _ = _rand_attn(47, 5, 1, 1, 8)
+    z = 0.4 * (k1[:, 0] @ q1[4, 0])
+    np.testing.assert_allclose(orc.attention_head_mean_row(q1[4], k1, 0.4), np.exp(z) / np.exp(z).sum(), atol=1e-15)
+
+
 def test_packed_prefill_equals_separate_sequences():
     lens = [20, 7, 13]
     pi = inp.prefill_inputs(lens, 2, 8, 4, 2, 16, 6, seed=9)
