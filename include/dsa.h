@@ -88,6 +88,35 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w,
                      int h_idx, int d_idx, int row_begin, int row_count,
                      float* scores, int64_t ld, void* stream);
 
+/*
+ * Target of the indexer's dense warm-up (digest section 一: with the full attention unchanged,
+ * the indexer is trained to follow the full attention distribution, measured by KL divergence).
+ *
+ * For packed rows [row_begin, row_begin + row_count) with local position t:
+ *   probs[i * ld + s] = (1 / hq) sum_h softmax_s(scale <q[r, h], k[o + s, h / G]>)  for s <= t
+ *   lse[i * hq + h]   = log sum_s exp(scale <q[r, h], k[o + s, h / G]>)  (the dense causal lse)
+ * (i = r - row_begin).  Entries with s > t are left untouched.  q, k, cu_seqlens_host as for
+ * dsa_prefill / dsa_index_scores.  Needs hq / hkv >= 4 and hkv in {1, 2, 4, 8}.  Costs two dense
+ * passes of Q K^T over the causal prefix (statistics, then probabilities).
+ */
+int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_host, int batch,
+                       int total_tokens, int hq, int hkv, int head_dim, float softmax_scale,
+                       int row_begin, int row_count, float* probs, int64_t ld, float* lse,
+                       void* stream);
+
+/*
+ * KL divergence from a target to the indexer's distribution, per row, with its gradient
+ * (digest section 一, dense warm-up).
+ *
+ * scores, target [rows, ld] float: row i holds row_len[i] entries (indexer scores I and a
+ *   target distribution p over the same positions).
+ * row_loss [rows] float: sum_s p_s (log p_s - log r_s), r = softmax(I) over the row (terms with
+ *   p_s = 0 are 0).
+ * grad [rows, ld] float: d row_loss / d I_s = r_s - p_s; may alias scores.
+ */
+int dsa_indexer_kl(const float* scores, const float* target, int64_t ld, int rows,
+                   const int32_t* row_len, float* row_loss, float* grad, void* stream);
+
 /* Bytes of scratch the fast dsa_topk path uses for `rows` rows of stride ld (0 when ld > 262144,
  * where only the scratch-free path exists). */
 int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes);

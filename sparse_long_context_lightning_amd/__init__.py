@@ -19,7 +19,9 @@ from ._lib import (  # noqa: F401
     dsa_abi_version,
     dsa_decode,
     dsa_decode_workspace_size,
+    dsa_attn_head_mean,
     dsa_index_scores,
+    dsa_indexer_kl,
     dsa_last_error,
     dsa_prefill,
     dsa_prefill_workspace_size,

@@ -26,7 +26,7 @@ DSA_MAX_TOP_K = 2048
 EXPORTED = (
     "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
     "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
-    "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode",
+    "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean", "dsa_indexer_kl",
 )
 
 
@@ -61,6 +61,8 @@ def load():
         "dsa_topk_workspace_size": ([_I, _I64, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_topk": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_topk_sorted": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
+        "dsa_attn_head_mean": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _I64, _P, _P], _I),
+        "dsa_indexer_kl": ([_P, _P, _I64, _I, _P, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
                                     _I),
@@ -126,6 +128,27 @@ def dsa_index_scores(q_idx, k_idx, w, cu_seqlens_host, row_begin, row_count, sco
     ld = scores.shape[1] if ld is None else ld
     _check(load().dsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), cu_p, len(cu) - 1, total, h_idx, d_idx,
                                    row_begin, row_count, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_attn_head_mean(q, k, cu_seqlens_host, row_begin, row_count, probs, lse, softmax_scale=None, ld=None,
+                       stream=None):
+    """Head-mean causal attention distribution (warm-up target) of packed rows into probs[row_count, ld],
+    and the dense per-head log-sum-exp into lse[row_count, hq]."""
+    cu, cu_p = _host_i32(cu_seqlens_host)
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    ld = probs.shape[1] if ld is None else ld
+    _check(load().dsa_attn_head_mean(_ptr(q), _ptr(k), cu_p, len(cu) - 1, total, hq, hkv, d, scale, row_begin,
+                                     row_count, _ptr(probs), ld, _ptr(lse), _stream(stream)))
+
+
+def dsa_indexer_kl(scores, target, row_len, row_loss, grad, ld=None, stream=None):
+    """Per-row KL(target || softmax(scores)) and its gradient r - p (grad may be scores itself)."""
+    rows = scores.shape[0]
+    ld = scores.shape[1] if ld is None else ld
+    _check(load().dsa_indexer_kl(_ptr(scores), _ptr(target), ld, rows, _ptr(row_len), _ptr(row_loss), _ptr(grad),
+                                 _stream(stream)))
 
 
 def dsa_topk_workspace_size(rows, ld, k) -> int:

@@ -176,6 +176,69 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
                            row_begin, scores, ld, static_cast<hipStream_t>(stream));
 }
 
+int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_host, int batch, int total_tokens,
+                       int hq, int hkv, int head_dim, float softmax_scale, int row_begin, int row_count, float* probs,
+                       int64_t ld, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(probs);
+  DSA_NONNULL(lse);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  if (total_tokens < 0 || row_begin < 0 || row_count < 0 || row_begin + (long long)row_count > total_tokens)
+    return fail(DSA_ERR_INVALID_ARG, "row range [%d, %d + %d) outside [0, %d)", row_begin, row_begin, row_count,
+                total_tokens);
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  if (hq / hkv < 4 || (hkv != 1 && hkv != 2 && hkv != 4 && hkv != 8))
+    return fail(DSA_ERR_UNSUPPORTED, "the head-mean target needs hq / hkv >= 4 and hkv in {1, 2, 4, 8}");
+  int max_len = 0;
+  DSA_TRY(check_cu_host(cu_seqlens_host, batch, total_tokens, &max_len));
+  if (ld <= 0) return fail(DSA_ERR_INVALID_ARG, "ld must be positive");
+  for (int b = 0; b < batch; ++b) {
+    const int r1 = std::min(row_begin + row_count, cu_seqlens_host[b + 1]);
+    if (r1 > std::max(row_begin, cu_seqlens_host[b]) && r1 - cu_seqlens_host[b] > ld)
+      return fail(DSA_ERR_INVALID_ARG, "ld (%lld) shorter than a row's prefix (%d)", (long long)ld,
+                  r1 - cu_seqlens_host[b]);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b = 0; b < batch; ++b) {
+    const int r0 = std::max(row_begin, cu_seqlens_host[b]);
+    const int r1 = std::min(row_begin + row_count, cu_seqlens_host[b + 1]);
+    if (r0 >= r1) continue;
+    dsa::HeadMeanArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.hq = hq;
+    a.hkv = hkv;
+    a.seq_off = cu_seqlens_host[b];
+    a.row_begin = r0;
+    a.row_end = r1;
+    a.out_row0 = row_begin;
+    a.softmax_scale = softmax_scale;
+    a.lse = lse;
+    a.probs = probs;
+    a.ld = ld;
+    DSA_TRY(hip_status(dsa::launch_attn_head_mean(a, s), "head-mean target launch"));
+  }
+  return DSA_OK;
+}
+
+int dsa_indexer_kl(const float* scores, const float* target, int64_t ld, int rows, const int32_t* row_len,
+                   float* row_loss, float* grad, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(scores);
+  DSA_NONNULL(target);
+  DSA_NONNULL(row_len);
+  DSA_NONNULL(row_loss);
+  DSA_NONNULL(grad);
+  if (rows < 0 || ld <= 0) return fail(DSA_ERR_INVALID_ARG, "rows must be non-negative and ld positive");
+  if (rows == 0) return DSA_OK;
+  return hip_status(dsa::launch_indexer_kl(scores, target, ld, rows, row_len, 0, row_loss, grad,
+                                           static_cast<hipStream_t>(stream)),
+                    "indexer KL launch");
+}
+
 int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes) {
   g_last_error[0] = 0;
   DSA_NONNULL(bytes);

@@ -88,7 +88,26 @@ struct SparseAttnBwdArgs {
   float* dv;  // [rows, hkv, 128]
 };
 
+// Head-mean causal attention distribution of packed rows [row_begin, row_end) of one sequence
+// starting at packed row seq_off: probs[(r - out_row0) * ld + s] for s <= r - seq_off, and the
+// per-head log-sum-exp lse[(r - out_row0) * hq + h].  Requires hq / hkv >= 4.
+struct HeadMeanArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  int hq, hkv;
+  int seq_off, row_begin, row_end, out_row0;
+  float softmax_scale;
+  float* lse;
+  float* probs;
+  long long ld;
+};
+
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
+hipError_t launch_attn_head_mean(const HeadMeanArgs& a, hipStream_t s);
+// Row loss KL(target || softmax(scores)) and grad = softmax(scores) - target (grad may alias
+// scores); row lengths from row_len or len_base + row + 1.
+hipError_t launch_indexer_kl(const float* scores, const float* target, long long ld, int rows, const int* row_len,
+                             int len_base, float* row_loss, float* grad, hipStream_t s);
 hipError_t launch_indexer_decode(const IndexerDecodeArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 // Reorder each row's selected positions (idx_out, as launch_topk leaves them) by descending score,

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
