@@ -9,8 +9,8 @@ resident in HBM.  The path is driven through the C ABI's separate entry points i
 chunk schedule dsa_prefill uses, so HIP events on the launch stream time each kernel inside
 the timed region; the fused dsa_prefill call is timed as well and reported beside it.  The
 decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
-the torch.topk-shaped top-k on the decode scores and the backward of the sparse attention on
-the 32K prefill (context lines beside the headline value).
+the torch.topk-shaped top-k on the decode scores, the backward of the sparse attention and the
+indexer's warm-up objective on the 32K prefill (context lines beside the headline value).
 
 One JSON line is printed last.
 """
@@ -358,6 +358,72 @@ def attn_bwd_bench(args, dsa, inp, tl):
             "note": "dq, dk, dv from dO; dk/dv scattered with fp32 atomics (bound by L2 atomic throughput)"}
 
 
+def warmup_bench(args, dsa, inp, tl):
+    """The indexer's dense warm-up objective on the 32K prefill: per chunk of 2048 rows the indexer
+    scores, the head-mean causal attention target and the per-row KL with its gradient (the
+    gradient's backward through the indexer is not part of the library)."""
+    import torch
+    pi = inp.workload(args.bwd_workload)
+    dev = tl.upload_prefill(pi)
+    lens = [int(x) for x in pi.seq_lens]
+    total = sum(lens)
+    hq, d = pi.q.shape[1], pi.q.shape[2]
+    ld = (max(lens) + 3) // 4 * 4
+    chunk = min(total, 2048)
+    scores = torch.empty(chunk, ld, dtype=torch.float32, device="cuda")
+    probs = torch.empty(chunk, ld, dtype=torch.float32, device="cuda")
+    lse = torch.empty(chunk, hq, dtype=torch.float32, device="cuda")
+    loss = torch.empty(total, dtype=torch.float32, device="cuda")
+    row_len = torch.from_numpy(np.concatenate([np.arange(1, n + 1) for n in lens]).astype(np.int32)).cuda()
+    cu = pi.cu_seqlens
+    t_target = [0.0]
+
+    def step():
+        for c0 in range(0, total, chunk):
+            n = min(chunk, total - c0)
+            dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, n, scores, ld=ld)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            dsa.dsa_attn_head_mean(dev["q"], dev["k"], cu, c0, n, probs, lse, ld=ld)
+            b.record()
+            t_target.append((a, b))
+            dsa.dsa_indexer_kl(scores, probs, row_len[c0:c0 + n], loss[c0:c0 + n], scores, ld=ld)
+
+    step()
+    torch.cuda.synchronize()
+    t_target.clear()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    target_ms = sum(a.elapsed_time(b) for a, b in t_target)
+    pairs = sum(n * (n + 1) // 2 for n in lens)
+    target_flops = 2 * pairs * 2 * hq * d          # two passes of the causal Q K^T, all heads
+    # parity on two rows
+    rows = [total // 3, total - 1]
+    cu_l = [int(x) for x in cu]
+    ok = True
+    for r in rows:
+        o = max(c for c in cu_l[:-1] if c <= r)
+        t = r - o
+        want_loss, _ = tl.orc.indexer_kl_row(
+            tl.orc.index_scores_row(tl.f64(pi.q_idx[r]), pi.w[r].astype(np.float64), tl.f64(pi.k_idx[o:o + t + 1])),
+            tl.orc.attention_head_mean_row(tl.f64(pi.q[r]), tl.f64(pi.k[o:o + t + 1]), tl.orc.default_softmax_scale(d)))
+        got = float(loss[r].item())
+        ok = ok and abs(got - want_loss) <= 1e-3 * max(1.0, abs(want_loss))
+    log(f"indexer warm-up objective {ms:.1f} ms per pass (target {target_ms:.1f} ms, "
+        f"{target_flops / (target_ms * 1e-3) / 1e12:.0f} TFLOP/s); row-loss parity {ok}")
+    del dev, scores, probs, lse, loss
+    torch.cuda.empty_cache()
+    return {"workload": args.bwd_workload, "ms": ms, "tokens_per_s": total / (ms * 1e-3), "target_ms": target_ms,
+            "target_tflops": target_flops / (target_ms * 1e-3) / 1e12, "rows_checked": len(rows), "loss_parity": ok,
+            "note": "indexer scores + head-mean dense attention target + per-row KL and d loss / d scores"}
+
+
 def cpu_baseline(args, pi, tl):
     """The oracle as it stands, on a bounded sample of rows of the same workload."""
     try:
@@ -403,6 +469,7 @@ def main():
     pre = prefill_bench(args, dsa, inp, tl)
     dec = None if args.no_decode else decode_bench(args, dsa, inp, tl)
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp, tl)
+    wup = None if args.no_bwd else warmup_bench(args, dsa, inp, tl)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"], tl)
 
     total = pre["rows_total"]
@@ -452,6 +519,8 @@ def main():
         line["topk_sorted_decode_scores"] = dec["topk_sorted"]
     if bwd is not None:
         line["sparse_attn_backward"] = bwd
+    if wup is not None:
+        line["indexer_warmup_objective"] = wup
     print(json.dumps(line), flush=True)
 
 
