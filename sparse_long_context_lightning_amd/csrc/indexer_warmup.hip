@@ -18,26 +18,36 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
-// Head-mean target, two passes over the causal keys of a block of 16 / G consecutive query
-// tokens (one wave): the 16 (token, head) rows of one KV group sit on the MFMA row axis and 16
-// keys of that group on the column axis (16x16x32 bf16, key rows gathered straight into B
-// registers, two tiles in flight).  PASS 1 keeps a lane-local online (max, sum) per row over
-// the keys the lane sees and merges the 16 lanes of each row at the end: lse per (token, head).
-// PASS 2 recomputes the logits, turns them into probabilities with that lse, sums the token's
-// heads over all groups and writes p_t[s] / Hq.  Needs G = Hq / Hkv >= 4, so each lane's four
-// C rows belong to one token.
+// Head-mean target, two passes over the causal keys of a workgroup of 4 waves, each wave a
+// block of 16 / G consecutive query tokens: the block's 16 (token, head) rows of one KV group
+// sit on the MFMA row axis and 16 keys of that group on the column axis (16x16x32 bf16).  Key
+// tiles of TK positions hold every group's 256-byte row of each position (one contiguous KiB
+// per position at 4 KV heads); they are DMA'd global->LDS, double buffered and shared by the 4
+// waves, with 16-byte piece c of position p stored at slot c ^ (p mod 16) (conflict-free B
+// reads).  PASS 1 keeps a lane-local online (max, sum) per row over the keys the lane sees and
+// merges the 16 lanes of each row at the end: lse per (token, head).  PASS 2 recomputes the
+// logits, turns them into probabilities with that lse, sums the token's heads over all groups
+// and writes p_t[s] / Hq.  Needs G = Hq / Hkv >= 4, so each lane's four C rows are one token's.
 template <int PASS, int HKV>
 __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, float scale_log2, int n_blocks) {
+  constexpr int ROWB = HKV * 256;            // bytes per key position (all KV groups)
+  constexpr int TK = HKV <= 4 ? 32 : 16;     // positions per tile
+  constexpr int TILE = TK * ROWB;
+  constexpr int NLD = TILE / 4096;           // 16-byte DMA pieces per thread per tile
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[2][TILE];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
-  const int blk = blockIdx.x * 4 + wave;
-  if (blk >= n_blocks) return;
   const int hq = a.hq, G = hq / HKV, TB = 16 / G;
+  const int blk = blockIdx.x * 4 + wave;
+  const int wg_r0 = a.row_begin + blockIdx.x * 4 * TB;
+  const int wg_last = min(wg_r0 + 4 * TB, a.row_end) - 1;
+  const int ntiles = (wg_last - a.seq_off) / TK + 1;
+  const bool active = blk < n_blocks;
   const int r0 = a.row_begin + blk * TB;
-  const int r_last = min(r0 + TB, a.row_end) - 1;
+  const int r_last = active ? min(r0 + TB, a.row_end) - 1 : r0;
   const int t_max = r_last - a.seq_off;
   // Row m of a group's tile: token m / G of the block, head g G + m % G.
-  const int a_tok = min(r0 + n / G, r_last);
+  const int a_tok = min(min(r0 + n / G, r_last), a.row_end - 1);
   u32x4 qa[HKV][4];
 #pragma unroll
   for (int g = 0; g < HKV; ++g) {
@@ -45,12 +55,10 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qa[g][ks] = ldg16(qp + ks * 8);
   }
-  // This lane's C rows 4 lg + i all belong to token c_tok (G >= 4).
-  const int c_tok_local = (4 * lg) / G;
-  const int c_row = r0 + c_tok_local;
-  const bool c_ok = c_row <= r_last;
-  const int c_t = c_row - a.seq_off;  // causal limit of this lane's rows
-  const uint16_t* kseq = a.k + (size_t)a.seq_off * HKV * 128 + lg * 32;
+  // This lane's C rows 4 lg + i all belong to token c_row (G >= 4).
+  const int c_row = r0 + (4 * lg) / G;
+  const bool c_ok = active && c_row <= r_last;
+  const int c_t = c_row - a.seq_off;
 
   float m_st[HKV][4], l_st[HKV][4], lse2[HKV][4];
 #pragma unroll
@@ -66,56 +74,77 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
       }
     }
 
-  const int ntiles = t_max / 16 + 1;
-  auto load = [&](int tile, u32x4 (&kb)[HKV][4]) {
-    const int key = min(tile * 16 + n, t_max);
+  // DMA mapping: instruction p of wave w fills LDS bytes [p*4096 + w*1024, +1024); lane l's 16
+  // bytes land at row (position pos, group g), slot l % 16, which holds piece (l % 16) ^ (pos % 16).
+  const uint16_t* kseq = a.k + (size_t)a.seq_off * HKV * 128;
+  int st_pos[NLD], st_off[NLD];
 #pragma unroll
-    for (int g = 0; g < HKV; ++g)
+  for (int p = 0; p < NLD; ++p) {
+    const int byte = p * 4096 + wave * 1024 + lane * 16;
+    const int pos = byte / ROWB;
+    const int g = (byte % ROWB) / 256;
+    const int piece = (lane & 15) ^ (pos & 15);
+    st_pos[p] = pos;
+    st_off[p] = g * 128 + piece * 8;  // elements within the position's HKV * 128
+  }
+  const int kv_len = wg_last - a.seq_off + 1;  // positions the workgroup can use
+  auto load_tile = [&](int tile, int buf) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[g][ks] = ldg16(kseq + ((size_t)key * HKV + g) * 128 + ks * 8);
+    for (int p = 0; p < NLD; ++p) {
+      const int pos = min(tile * TK + st_pos[p], kv_len - 1);
+      lds_dma16(kseq + (size_t)pos * HKV * 128 + st_off[p], &tiles[buf][p * 4096 + wave * 1024]);
+    }
   };
-  auto compute = [&](int tile, const u32x4 (&kb)[HKV][4]) {
-    const int key = tile * 16 + n;
-    const bool kv = c_ok && key <= c_t;
-    float tok_sum = 0.f;
+
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) load_tile(it + 1, (it + 1) & 1);
+    if (active && it * TK <= t_max) {
+      const unsigned char* tile = tiles[it & 1];
 #pragma unroll
-    for (int g = 0; g < HKV; ++g) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < TK / 16; ++st) {
+        const int pos_t = 16 * st + n;      // position within the tile
+        const int key = it * TK + pos_t;
+        const bool kv = c_ok && key <= c_t;
+        float tok_sum = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) c = mfma16x16x32(qa[g][ks], kb[g][ks], c);
+        for (int g = 0; g < HKV; ++g) {
+          const unsigned char* rowp = tile + (pos_t * HKV + g) * 256;
+          f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float z = c[i] * scale_log2;
-        if (PASS == 1) {
-          if (kv) {
-            const float mn = fmaxf(m_st[g][i], z);
-            l_st[g][i] = l_st[g][i] * exp2f(m_st[g][i] - mn) + exp2f(z - mn);
-            m_st[g][i] = mn;
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 kb = *reinterpret_cast<const u32x4*>(rowp + (((lg * 4 + ks) ^ (pos_t & 15)) * 16));
+            c = mfma16x16x32(qa[g][ks], kb, c);
           }
-        } else {
-          tok_sum += kv ? exp2f(z - lse2[g][i]) : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float z = c[i] * scale_log2;
+            if (PASS == 1) {
+              if (kv) {
+                const float mn = fmaxf(m_st[g][i], z);
+                l_st[g][i] = l_st[g][i] * exp2f(m_st[g][i] - mn) + exp2f(z - mn);
+                m_st[g][i] = mn;
+              }
+            } else {
+              tok_sum += kv ? exp2f(z - lse2[g][i]) : 0.f;
+            }
+          }
+        }
+        if (PASS == 2) {
+          // Sum the token's lane groups (G / 4 of them) and store from its first one.
+          if (G >= 8) tok_sum += __shfl_xor(tok_sum, 16);
+          if (G >= 16) tok_sum += __shfl_xor(tok_sum, 32);
+          if (kv && (4 * lg) % G == 0) a.probs[(size_t)(c_row - a.out_row0) * a.ld + key] = tok_sum / (float)hq;
         }
       }
     }
-    if (PASS == 2) {
-      // Sum the token's lane groups (G / 4 of them) and store from its first one.
-      if (G >= 8) tok_sum += __shfl_xor(tok_sum, 16);
-      if (G >= 16) tok_sum += __shfl_xor(tok_sum, 32);
-      if (kv && (4 * lg) % G == 0) a.probs[(size_t)(c_row - a.out_row0) * a.ld + key] = tok_sum / (float)hq;
-    }
-  };
-
-  u32x4 kA[HKV][4], kB[HKV][4];
-  load(0, kA);
-  for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) load(it + 1, kB);
-    compute(it, kA);
-    if (it + 1 >= ntiles) break;
-    if (it + 2 < ntiles) load(it + 2, kA);
-    compute(it + 1, kB);
+    if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
-  if (PASS == 1) {
+  if (PASS == 1 && active) {
     // Merge the 16 lanes of each row (same lg): log-sum-exp of (m, l) pairs.
 #pragma unroll
     for (int g = 0; g < HKV; ++g)
