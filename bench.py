@@ -359,9 +359,9 @@ def attn_bwd_bench(args, dsa, inp, tl):
 
 
 def warmup_bench(args, dsa, inp, tl):
-    """The indexer's dense warm-up objective on the 32K prefill: per chunk of 2048 rows the indexer
-    scores, the head-mean causal attention target and the per-row KL with its gradient (the
-    gradient's backward through the indexer is not part of the library)."""
+    """The indexer's dense warm-up step on the 32K prefill: per chunk of 2048 rows the indexer
+    scores, the head-mean causal attention target, the per-row KL with its gradient, and that
+    gradient's backward through the indexer (dq_idx, dw, dk_idx)."""
     import torch
     pi = inp.workload(args.bwd_workload)
     dev = tl.upload_prefill(pi)
@@ -376,23 +376,37 @@ def warmup_bench(args, dsa, inp, tl):
     loss = torch.empty(total, dtype=torch.float32, device="cuda")
     row_len = torch.from_numpy(np.concatenate([np.arange(1, n + 1) for n in lens]).astype(np.int32)).cuda()
     cu = pi.cu_seqlens
-    t_target = [0.0]
+    h_idx, d_idx = pi.q_idx.shape[1], pi.q_idx.shape[2]
+    dq = torch.empty(total, h_idx, d_idx, dtype=torch.float32, device="cuda")
+    dw = torch.empty(total, h_idx, dtype=torch.float32, device="cuda")
+    dk = torch.empty(total, d_idx, dtype=torch.float32, device="cuda")
+    ws = torch.empty(dsa.dsa_index_scores_bwd_workspace_size(total, h_idx, d_idx, chunk), dtype=torch.uint8,
+                     device="cuda")
+    t_target = []
+    t_bwd = []
+
+    def timed(fn, into):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        into.append((a, b))
 
     def step():
+        dk.zero_()
         for c0 in range(0, total, chunk):
             n = min(chunk, total - c0)
             dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, n, scores, ld=ld)
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            dsa.dsa_attn_head_mean(dev["q"], dev["k"], cu, c0, n, probs, lse, ld=ld)
-            b.record()
-            t_target.append((a, b))
+            timed(lambda: dsa.dsa_attn_head_mean(dev["q"], dev["k"], cu, c0, n, probs, lse, ld=ld), t_target)
             dsa.dsa_indexer_kl(scores, probs, row_len[c0:c0 + n], loss[c0:c0 + n], scores, ld=ld)
+            timed(lambda: dsa.dsa_index_scores_bwd(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, n, scores, dq, dw, dk,
+                                                   workspace=ws, ld=ld), t_bwd)
 
     step()
     torch.cuda.synchronize()
     t_target.clear()
+    t_bwd.clear()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -401,8 +415,25 @@ def warmup_bench(args, dsa, inp, tl):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     target_ms = sum(a.elapsed_time(b) for a, b in t_target)
+    bwd_ms = sum(a.elapsed_time(b) for a, b in t_bwd)
     pairs = sum(n * (n + 1) // 2 for n in lens)
     target_flops = 2 * pairs * 2 * hq * d          # two passes of the causal Q K^T, all heads
+    bwd_flops = 3 * pairs * 2 * h_idx * d_idx      # recompute c, then u (-> dq, dw) and dk
+    # backward parity on two rows of the last chunk (whose gradient is still in `scores`)
+    c_last = (total - 1) // chunk * chunk
+    bwd_ok = True
+    for r in (total - 1, c_last + 7):
+        o = max(c for c in [int(x) for x in cu][:-1] if c <= r)
+        t = r - o
+        g_row = scores[r - c_last, :t + 1].double().cpu().numpy()
+        want_q, want_w, _ = tl.orc.index_scores_row_grad(tl.f64(pi.q_idx[r]), pi.w[r].astype(np.float64),
+                                                         tl.f64(pi.k_idx[o:o + t + 1]), g_row)
+        got_q = dq[r].double().cpu().numpy()
+        got_w = dw[r].double().cpu().numpy()
+        scale_q = max(np.abs(want_q).max(), 1e-30)
+        scale_w = max(np.abs(want_w).max(), 1e-30)
+        bwd_ok = bwd_ok and bool(np.abs(got_q - want_q).max() <= 1e-2 * scale_q) and \
+            bool(np.abs(got_w - want_w).max() <= 1e-2 * scale_w)
     # parity on two rows
     rows = [total // 3, total - 1]
     cu_l = [int(x) for x in cu]
@@ -415,13 +446,18 @@ def warmup_bench(args, dsa, inp, tl):
             tl.orc.attention_head_mean_row(tl.f64(pi.q[r]), tl.f64(pi.k[o:o + t + 1]), tl.orc.default_softmax_scale(d)))
         got = float(loss[r].item())
         ok = ok and abs(got - want_loss) <= 1e-3 * max(1.0, abs(want_loss))
-    log(f"indexer warm-up objective {ms:.1f} ms per pass (target {target_ms:.1f} ms, "
-        f"{target_flops / (target_ms * 1e-3) / 1e12:.0f} TFLOP/s); row-loss parity {ok}")
-    del dev, scores, probs, lse, loss
+    log(f"indexer warm-up step {ms:.1f} ms per pass (target {target_ms:.1f} ms, "
+        f"{target_flops / (target_ms * 1e-3) / 1e12:.0f} TFLOP/s; indexer backward {bwd_ms:.1f} ms, "
+        f"{bwd_flops / (bwd_ms * 1e-3) / 1e12:.0f} TFLOP/s); row-loss parity {ok}, backward rows {bwd_ok}")
+    del dev, scores, probs, lse, loss, dq, dw, dk, ws
     torch.cuda.empty_cache()
     return {"workload": args.bwd_workload, "ms": ms, "tokens_per_s": total / (ms * 1e-3), "target_ms": target_ms,
             "target_tflops": target_flops / (target_ms * 1e-3) / 1e12, "rows_checked": len(rows), "loss_parity": ok,
-            "note": "indexer scores + head-mean dense attention target + per-row KL and d loss / d scores"}
+            "indexer_bwd_ms": bwd_ms, "indexer_bwd_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+            "indexer_bwd_rows_parity": bwd_ok,
+            "note": "indexer scores + head-mean dense attention target + per-row KL and d loss / d scores + "
+                    "the indexer backward (dq_idx, dw, dk_idx); backward TFLOP/s counts 3 x 2 H_I d_I flop per "
+                    "causal pair"}
 
 
 def cpu_baseline(args, pi, tl):

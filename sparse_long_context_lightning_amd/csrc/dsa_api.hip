@@ -55,6 +55,15 @@ int check_indexer_shape(int h_idx, int d_idx) {
   return DSA_OK;
 }
 
+// The indexer backward is built for the 64-head, 128-dim indexer only.
+int check_indexer_bwd_shape(int h_idx, int d_idx) {
+  if (h_idx <= 0 || d_idx <= 0) return fail(DSA_ERR_INVALID_ARG, "h_idx and d_idx must be positive");
+  if (h_idx != 64 || d_idx != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer backward supports h_idx = 64, d_idx = 128 only (got %d, %d)", h_idx,
+                d_idx);
+  return DSA_OK;
+}
+
 // Validates host cu_seqlens and returns the longest sequence in *max_len.
 int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) {
   if (!cu) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_host is null");
@@ -174,6 +183,76 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
   if (row_count == 0) return DSA_OK;
   return launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, row_begin, row_begin + row_count,
                            row_begin, scores, ld, static_cast<hipStream_t>(stream));
+}
+
+int dsa_index_scores_bwd_workspace_size(int total_tokens, int h_idx, int d_idx, int row_count, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (total_tokens < 0 || row_count < 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens and row_count must be >= 0");
+  DSA_TRY(check_indexer_bwd_shape(h_idx, d_idx));
+  *bytes = dsa::indexer_bwd_workspace_bytes(row_count, total_tokens);
+  return DSA_OK;
+}
+
+int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu_seqlens_host,
+                         int batch, int total_tokens, int h_idx, int d_idx, int row_begin, int row_count,
+                         const float* dscores, int64_t ld, float* dq_idx, float* dw, float* dk_idx, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q_idx);
+  DSA_NONNULL(k_idx);
+  DSA_NONNULL(w);
+  DSA_NONNULL(dscores);
+  DSA_NONNULL(dq_idx);
+  DSA_NONNULL(dw);
+  DSA_NONNULL(dk_idx);
+  DSA_ALIGNED(q_idx);
+  DSA_ALIGNED(k_idx);
+  DSA_ALIGNED(w);
+  DSA_ALIGNED(dscores);
+  DSA_ALIGNED(dq_idx);
+  DSA_ALIGNED(dk_idx);
+  if (total_tokens < 0 || row_begin < 0 || row_count < 0 || row_begin + (long long)row_count > total_tokens)
+    return fail(DSA_ERR_INVALID_ARG, "row range [%d, %d + %d) outside [0, %d)", row_begin, row_begin, row_count,
+                total_tokens);
+  DSA_TRY(check_indexer_bwd_shape(h_idx, d_idx));
+  int max_len = 0;
+  DSA_TRY(check_cu_host(cu_seqlens_host, batch, total_tokens, &max_len));
+  if (ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "ld (%lld) must be a multiple of 4", (long long)ld);
+  for (int b = 0; b < batch; ++b) {
+    const int r1 = std::min(row_begin + row_count, cu_seqlens_host[b + 1]);
+    if (r1 > std::max(row_begin, cu_seqlens_host[b]) && r1 - cu_seqlens_host[b] > ld)
+      return fail(DSA_ERR_INVALID_ARG, "ld (%lld) shorter than a row's prefix (%d)", (long long)ld,
+                  r1 - cu_seqlens_host[b]);
+  }
+  if (row_count == 0) return DSA_OK;
+  const size_t need = dsa::indexer_bwd_workspace_bytes(row_count, max_len);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  DSA_ALIGNED(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int b = 0; b < batch; ++b) {
+    const int r0 = std::max(row_begin, cu_seqlens_host[b]);
+    const int r1 = std::min(row_begin + row_count, cu_seqlens_host[b + 1]);
+    if (r0 >= r1) continue;
+    dsa::IndexerBwdArgs a;
+    a.q_idx = static_cast<const uint16_t*>(q_idx);
+    a.k_idx = static_cast<const uint16_t*>(k_idx);
+    a.w = w;
+    a.g = dscores;
+    a.ld = ld;
+    a.seq_off = cu_seqlens_host[b];
+    a.row_begin = r0;
+    a.row_end = r1;
+    a.grad_row0 = row_begin;
+    a.ws_rows = row_count;
+    a.workspace = static_cast<uint16_t*>(workspace);
+    a.dq = dq_idx;
+    a.dw = dw;
+    a.dk = dk_idx;
+    DSA_TRY(hip_status(dsa::launch_indexer_bwd(a, s), "indexer backward launch"));
+  }
+  return DSA_OK;
 }
 
 int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_host, int batch, int total_tokens,

@@ -1,0 +1,460 @@
+// Backward of the lightning-indexer scores for gfx950 (bf16 MFMA, fp32 accumulation).
+//
+// The indexer of the Keye-VL-2.0 report digest (mqxn.cn news 1966, section 一) is trained in the
+// dense warm-up stage to follow the full attention distribution, so its scores
+//     I[t, s] = sum_j w[t, j] * relu(c[t, j, s]),   c[t, j, s] = <q_idx[t, j], k_idx[s]>,
+// need a backward.  With g[t, s] the incoming gradient of I and m = [c > 0]:
+//     u[t, j]  = sum_s g[t, s] m[t, j, s] k_idx[s]
+//     dq[t, j] = w[t, j] u[t, j]
+//     dw[t, j] = sum_s g[t, s] relu(c[t, j, s]) = <q_idx[t, j], u[t, j]>      (m c = relu(c))
+//     dk[s]    = sum_t sum_j g[t, s] m[t, j, s] (w[t, j] q_idx[t, j])
+// Two kernels share the work.  The query-major one streams key tiles through LDS and keeps u of
+// its (token, head) rows in registers (dq, dw); the key-major one streams query tokens through
+// LDS and keeps dk of its keys in registers.  Each recomputes c on MFMA with the forward's
+// operands and fp32 accumulation, so m is the forward's ReLU decision; the second contraction
+// takes g m (and w q_idx) rounded to bf16.  Its contracted operand has to be laid out with the
+// reduction index (s, or the heads) contiguous, which is the transpose of how k_idx and q_idx
+// are stored, so a small kernel first writes transposed 64-row tiles of both into the workspace.
+//
+// MFMA C layout: lane (a, n) with a = lane / 16, n = lane % 16 holds C[4a + i][n], i = 0..3.
+// Both second contractions take their B operand straight from the first one's C registers:
+// C rows 4a + i of two 16-row tiles (h = 0, 1) become the 8 reduction slots e = 4h + i of lane
+// group a, and the transposed tiles store row 32p + 16h + 4a + i at column 32p + 8a + 4h + i so
+// that the matching A operand is one contiguous 16-byte read.
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kBH = 64;    // indexer heads
+constexpr int kBD = 128;   // indexer dim
+constexpr int kTileElems = 64 * kBD;  // one transposed tile: 128 rows of 64 bf16
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to one dword of bf16 (round to nearest even, lo = a).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Column of source row r (0..63) in a transposed tile.
+__device__ __forceinline__ int tcol(int r) {
+  return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+// ---------------------------------------------------------------------------------------
+// Transposed tiles: tile i takes source rows [64 i, 64 i + 64) of a row-major [rows][128] bf16
+// array (rows >= nrows read as zero), multiplies row r by scale[r] if scale is given (rounded
+// back to bf16), and writes dst[i][d][tcol(r)].
+__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __restrict__ src,
+                                                            const float* __restrict__ scale, int nrows,
+                                                            uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[kBD * 64];
+  const int tile = blockIdx.x;
+  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;  // row, quarter of its 128 values
+  const long long row = (long long)tile * 64 + r;
+  const int col = tcol(r);
+  if (row < nrows) {
+    const uint16_t* sp = src + row * kBD + part * 32;
+    const float sc = scale ? scale[row] : 1.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 v = ldg16(sp + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t h = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+        if (scale) {
+          const float f = bf16_to_f32(h) * sc;
+          h = uint16_t(cvt_bf16x2(f, 0.f) & 0xFFFFu);
+        }
+        t[(part * 32 + c * 8 + e) * 64 + col] = h;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) t[(part * 32 + e) * 64 + col] = 0;
+  }
+  __syncthreads();
+  uint16_t* dp = dst + (size_t)tile * kTileElems;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int off = (threadIdx.x + 256 * m) * 8;
+    *reinterpret_cast<u32x4*>(dp + off) = *reinterpret_cast<const u32x4*>(t + off);
+  }
+}
+
+// LDS tiles of both kernels (bytes):
+//   row tile [64 rows][256 B]: 16-byte piece c of row r at slot c ^ (r & 15)
+//   T tile   [128 rows][128 B]: piece c of row d at slot c ^ ((d >> 1) & 7)
+// (the 16 lanes of one LDS phase of an operand read then hit 16 distinct bank groups).
+constexpr int kRowTileBytes = 64 * 256;
+constexpr int kTTileBytes = 128 * 128;
+
+// Global source of DMA lane l of row-tile job P (P = 0..15): the piece that belongs at LDS
+// byte 1024 P + 16 l.  base points at row 0; rows past last_row are clamped to it.
+__device__ __forceinline__ const uint16_t* row_tile_src(const uint16_t* base, int P, int lane, int last_row) {
+  const int row = 4 * P + (lane >> 4);
+  const int piece = (lane & 15) ^ (row & 15);
+  return base + (size_t)min(row, last_row) * kBD + piece * 8;
+}
+__device__ __forceinline__ const uint16_t* t_tile_src(const uint16_t* tile, int P, int lane) {
+  const int d = 8 * P + (lane >> 3);
+  const int piece = (lane & 7) ^ ((d >> 1) & 7);
+  return tile + d * 64 + piece * 8;
+}
+
+// ---------------------------------------------------------------------------------------
+// dq and dw: a workgroup of 2 NTOK waves takes NTOK consecutive query rows of one sequence and
+// one split of their keys; wave w handles heads 32 (w & 1) .. + 31 of token w / 2.  Per 64-key
+// tile (k rows, their transposed tile and the tokens' g values DMA'd to LDS, double buffered):
+//   X^T = K Q^T           (A: key rows from LDS, B: the wave's q rows in registers)
+//   u^T += K^T (g m)^T    (A: transposed key tile, B: bf16 of g m from the X^T registers)
+template <int NTOK>
+__global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ kT,
+    const float* __restrict__ w, const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end,
+    int grad_row0, float* __restrict__ dq, float* __restrict__ dw, int key_split, int n_rowblk, int n_items,
+    int accumulate) {
+  constexpr int NWV = 2 * NTOK;
+  constexpr int GBYTES = ((NTOK * 256 + 1023) / 1024) * 1024;
+  constexpr int NJOB = 32 + GBYTES / 1024;
+  __shared__ __attribute__((aligned(16))) unsigned char kt_lds[2][kRowTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ktt_lds[2][kTTileBytes];
+  __shared__ __attribute__((aligned(16))) float g_lds[2][GBYTES / 4];
+
+  const int per_xcd = gridDim.x >> 3;
+  const int wi = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (wi >= n_items) return;
+  const int split = wi / n_rowblk;
+  const int rb = wi - split * n_rowblk;
+  const int r0 = row_begin + rb * NTOK;
+  const int t_last = min(r0 + NTOK, row_end) - 1 - seq_off;
+  const int kbeg = split * key_split;
+  if (kbeg > t_last) return;
+  const int kend = min(kbeg + key_split, t_last + 1);
+  const int ntiles = (kend - kbeg + 63) >> 6;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, lg = lane >> 4;
+  const int tok = wave >> 1, hh = wave & 1;
+  const int r = r0 + tok;
+  const bool row_ok = r < row_end;
+  const int rr = min(r, row_end - 1);
+  const int t = rr - seq_off;
+
+  // B operands of X^T: head 32 hh + 16 ht + n, reduction piece lg * 4 + ks (as the forward).
+  u32x4 qreg[2][4];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const uint16_t* qp = q_idx + ((size_t)rr * kBH + 32 * hh + 16 * ht + n) * kBD + lg * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qreg[ht][ks] = ldg16(qp + ks * 8);
+  }
+  f32x4 u[8][2];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) u[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kseq = k_idx + (size_t)seq_off * kBD;
+  auto stage = [&](int it, int buf) {
+    const int key0 = kbeg + it * 64;
+    const int last = kend - 1 - key0;
+    for (int P = wave; P < NJOB; P += NWV) {
+      if (P < 16) {
+        lds_dma16(row_tile_src(kseq + (size_t)key0 * kBD, P, lane, last), &kt_lds[buf][P * 1024]);
+      } else if (P < 32) {
+        lds_dma16(t_tile_src(kT + (size_t)(key0 >> 6) * kTileElems, P - 16, lane), &ktt_lds[buf][(P - 16) * 1024]);
+      } else {
+        const int m = (P - 32) * 64 + lane;  // 16-byte piece: token m / 16, keys 4 (m % 16) ..
+        const int gr = min(r0 + min(m >> 4, NTOK - 1), row_end - 1);
+        int a = key0 + 4 * (m & 15);
+        if (a > gr - seq_off) a = 0;  // past the row's prefix: any valid address (masked below)
+        lds_dma16(g + (size_t)(gr - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 32) * 1024);
+      }
+    }
+  };
+
+  stage(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
+    const int key0 = kbeg + it * 64;
+    if (row_ok && key0 <= t) {
+      const unsigned char* ktile = kt_lds[buf];
+      const unsigned char* kttile = ktt_lds[buf];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4 yv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kt = 2 * p + h;
+          f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          const unsigned char* bp = ktile + (16 * kt + n) * 256;
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) x[ht] = mfma16x16x32(a, qreg[ht][ks], x[ht]);
+          }
+          __builtin_amdgcn_s_setprio(0);
+          // g of keys key0 + 16 kt + 4 lg + i for this wave's token, zero past its prefix.
+          const int kl = 16 * kt + 4 * lg;
+          const f32x4 gv = *reinterpret_cast<const f32x4*>(&g_lds[buf][tok * 64 + kl]);
+          float gm[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gm[i] = (key0 + kl + i <= t) ? gv[i] : 0.f;
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            yv[ht][2 * h] = cvt_bf16x2(x[ht][0] > 0.f ? gm[0] : 0.f, x[ht][1] > 0.f ? gm[1] : 0.f);
+            yv[ht][2 * h + 1] = cvt_bf16x2(x[ht][2] > 0.f ? gm[2] : 0.f, x[ht][3] > 0.f ? gm[3] : 0.f);
+          }
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int d = 16 * dt + n;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) u[dt][ht] = mfma16x16x32(a, yv[ht], u[dt][ht]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  // Lane (lg, n) holds u^T[16 dt + 4 lg + i][head 32 hh + 16 ht + n].
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head = 32 * hh + 16 * ht + n;
+    const size_t hrow = (size_t)r * kBH + head;
+    const float wv = w[hrow];
+    const uint16_t* qp = q_idx + hrow * kBD + 4 * lg;
+    float* dqp = dq + hrow * kBD + 4 * lg;
+    float dot = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint2 qv = *reinterpret_cast<const uint2*>(qp + 16 * dt);
+      dot = fmaf(__uint_as_float(qv.x << 16), u[dt][ht][0], dot);
+      dot = fmaf(__uint_as_float(qv.x & 0xFFFF0000u), u[dt][ht][1], dot);
+      dot = fmaf(__uint_as_float(qv.y << 16), u[dt][ht][2], dot);
+      dot = fmaf(__uint_as_float(qv.y & 0xFFFF0000u), u[dt][ht][3], dot);
+      const f32x4 v = u[dt][ht] * wv;
+      if (accumulate) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dqp + 16 * dt + i, v[i]);
+      } else {
+        *reinterpret_cast<f32x4*>(dqp + 16 * dt) = v;
+      }
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    if (lg == 0) {
+      if (accumulate) unsafeAtomicAdd(dw + hrow, dot);
+      else dw[hrow] = dot;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dk: a workgroup of NW waves takes 32 NW consecutive keys of one sequence and one group of
+// query tokens; wave w holds keys 32 w .. + 31 of the block.  Per token (its 64 q rows, its
+// transposed w-scaled tile and its g values over the block DMA'd to LDS, double buffered):
+//   X = Q K^T             (A: q rows from LDS, B: the wave's key rows in registers)
+//   dk^T += (w Q)^T (g m) (A: transposed w q tile, B: bf16 of g m from the X registers)
+// and the block's dk is added to the output with fp32 atomics at the end.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ qwT, const uint16_t* __restrict__ k_idx,
+    const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end, int grad_row0,
+    float* __restrict__ dk, int tok_group, int n_keyblk, int n_items) {
+  constexpr int KB = 32 * NW;
+  constexpr int GBYTES = ((KB * 4 + 1023) / 1024) * 1024;
+  constexpr int NJOB = 32 + GBYTES / 1024;
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][kRowTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char qt_lds[2][kTTileBytes];
+  __shared__ __attribute__((aligned(16))) float g_lds[2][GBYTES / 4];
+
+  const int per_xcd = gridDim.x >> 3;
+  const int wi = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (wi >= n_items) return;
+  const int tg = wi / n_keyblk;
+  const int kb = wi - tg * n_keyblk;
+  const int kb0 = kb * KB;                                     // local key of the block start
+  const int tb = row_begin - seq_off + tg * tok_group;         // local token range of the group
+  const int te = min(tb + tok_group, row_end - seq_off);
+  const int ts = max(tb, kb0);                                  // earlier tokens see none of the block
+  if (ts >= te) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, lg = lane >> 4;
+  const int kw0 = kb0 + 32 * wave;
+
+  // B operands of X: key kw0 + 16 kt + n, reduction piece lg * 4 + ks.
+  u32x4 kreg[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(kw0 + 16 * kt + n, te - 1);
+    const uint16_t* kp = k_idx + ((size_t)seq_off + key) * kBD + lg * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kreg[kt][ks] = ldg16(kp + ks * 8);
+  }
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto stage = [&](int tl, int buf) {
+    const int r = seq_off + tl;
+    for (int P = wave; P < NJOB; P += NW) {
+      if (P < 16) {
+        lds_dma16(row_tile_src(q_idx + (size_t)r * kBH * kBD, P, lane, kBH - 1), &q_lds[buf][P * 1024]);
+      } else if (P < 32) {
+        lds_dma16(t_tile_src(qwT + (size_t)(r - grad_row0) * kTileElems, P - 16, lane), &qt_lds[buf][(P - 16) * 1024]);
+      } else {
+        int a = kb0 + 4 * ((P - 32) * 64 + lane);
+        if (a > tl) a = kb0;  // past the row's prefix: any valid address (masked below)
+        lds_dma16(g + (size_t)(r - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 32) * 1024);
+      }
+    }
+  };
+
+  stage(ts, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int tl = ts; tl < te; ++tl) {
+    const int buf = (tl - ts) & 1;
+    if (tl + 1 < te) stage(tl + 1, buf ^ 1);
+    if (kw0 <= tl) {
+      const unsigned char* qtile = q_lds[buf];
+      const unsigned char* qttile = qt_lds[buf];
+      float gk[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int key = kw0 + 16 * kt + n;
+        gk[kt] = (key <= tl) ? g_lds[buf][key - kb0] : 0.f;
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4 yv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ht = 2 * p + h;
+          f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          const unsigned char* bp = qtile + (16 * ht + n) * 256;
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) x[kt] = mfma16x16x32(a, kreg[kt][ks], x[kt]);
+          }
+          __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            yv[kt][2 * h] = cvt_bf16x2(x[kt][0] > 0.f ? gk[kt] : 0.f, x[kt][1] > 0.f ? gk[kt] : 0.f);
+            yv[kt][2 * h + 1] = cvt_bf16x2(x[kt][2] > 0.f ? gk[kt] : 0.f, x[kt][3] > 0.f ? gk[kt] : 0.f);
+          }
+        }
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const int d = 16 * dt + n;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(qttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma16x16x32(a, yv[kt], acc[dt][kt]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    if (tl + 1 < te) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // Lane (lg, n) holds dk^T[16 dt + 4 lg + i][key kw0 + 16 kt + n]; keys past the group's last
+  // token received nothing (and may lie past the sequence).
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = kw0 + 16 * kt + n;
+    if (key >= te) continue;
+    float* dkp = dk + ((size_t)seq_off + key) * kBD + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) unsafeAtomicAdd(dkp + 16 * dt + i, acc[dt][kt][i]);
+  }
+}
+
+__global__ void bwd_zero_kernel(float* __restrict__ p, long long n) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+constexpr int kBwdTok = 4;     // query tokens per dq workgroup (8 waves)
+constexpr int kBwdKeyW = 12;   // waves per dk workgroup (384 keys)
+constexpr int kBwdTokGroup = 256;
+
+}  // namespace
+
+size_t indexer_bwd_workspace_bytes(int rows, int max_keys) {
+  const size_t q_part = ((size_t)rows * kTileElems * 2 + 255) / 256 * 256;
+  const size_t k_part = (size_t)((max_keys + 63) / 64) * kTileElems * 2;
+  return q_part + k_part;
+}
+
+hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s) {
+  const int rows = a.row_end - a.row_begin;
+  if (rows <= 0) return hipSuccess;
+  const int t_last = a.row_end - 1 - a.seq_off;
+  const int nkeys = t_last + 1;
+  uint16_t* qwT = a.workspace + (size_t)(a.row_begin - a.grad_row0) * kTileElems;
+  uint16_t* kT = a.workspace + ((size_t)a.ws_rows * kTileElems * 2 + 255) / 256 * 256 / 2;
+  // Transposed tiles: the sequence's keys [0, nkeys), the rows' w-scaled queries.
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((nkeys + 63) / 64), dim3(256), 0, s,
+                     a.k_idx + (size_t)a.seq_off * kBD, (const float*)nullptr, nkeys, kT);
+  hipLaunchKernelGGL(bwd_transpose_kernel, dim3(rows), dim3(256), 0, s, a.q_idx + (size_t)a.row_begin * kBH * kBD,
+                     a.w + (size_t)a.row_begin * kBH, rows * kBH, qwT);
+
+  // dq, dw: row blocks x key splits; split the keys only while the row blocks alone leave
+  // the chip under-filled.
+  const int n_rowblk = (rows + kBwdTok - 1) / kBwdTok;
+  const int ktiles = (nkeys + 63) / 64;
+  int nsplit = n_rowblk >= 256 ? 1 : std::min(ktiles, (512 + n_rowblk - 1) / n_rowblk);
+  const int key_split = ((ktiles + nsplit - 1) / nsplit) * 64;
+  nsplit = (nkeys + key_split - 1) / key_split;
+  const int accumulate = nsplit > 1;
+  if (accumulate) {
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(std::min(1024, (rows * kBH * kBD + 255) / 256)), dim3(256), 0, s,
+                       a.dq + (size_t)a.row_begin * kBH * kBD, (long long)rows * kBH * kBD);
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(std::min(1024, (rows * kBH + 255) / 256)), dim3(256), 0, s,
+                       a.dw + (size_t)a.row_begin * kBH, (long long)rows * kBH);
+  }
+  const int q_items = n_rowblk * nsplit;
+  hipLaunchKernelGGL(indexer_bwd_q_kernel<kBwdTok>, dim3((q_items + 7) / 8 * 8), dim3(128 * kBwdTok), 0, s,
+                     a.q_idx, a.k_idx, (const uint16_t*)kT, a.w, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
+                     a.grad_row0, a.dq, a.dw, key_split, n_rowblk, q_items, accumulate);
+
+  // dk: key blocks x token groups.
+  const int n_keyblk = (nkeys + 32 * kBwdKeyW - 1) / (32 * kBwdKeyW);
+  const int n_tg = (rows + kBwdTokGroup - 1) / kBwdTokGroup;
+  const int k_items = n_keyblk * n_tg;
+  hipLaunchKernelGGL(indexer_bwd_k_kernel<kBwdKeyW>, dim3((k_items + 7) / 8 * 8), dim3(64 * kBwdKeyW), 0, s,
+                     a.q_idx, (const uint16_t*)a.workspace, a.k_idx, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
+                     a.grad_row0, a.dk, kBwdTokGroup, n_keyblk, k_items);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

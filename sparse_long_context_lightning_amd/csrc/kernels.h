@@ -88,6 +88,24 @@ struct SparseAttnBwdArgs {
   float* dv;  // [rows, hkv, 128]
 };
 
+// Backward of the indexer scores for packed rows [row_begin, row_end) of one sequence starting at
+// packed row seq_off (64 heads x 128 only).  g[(r - grad_row0) * ld + s] is the gradient of
+// I[r, s]; dq / dw of the rows are written, dk of the sequence's keys accumulated.  workspace
+// holds ws_rows transposed query tiles (row grad_row0 first), then the key tiles of one sequence.
+struct IndexerBwdArgs {
+  const uint16_t* q_idx;
+  const uint16_t* k_idx;
+  const float* w;
+  const float* g;
+  long long ld;
+  int seq_off, row_begin, row_end, grad_row0, ws_rows;
+  uint16_t* workspace;
+  float* dq;
+  float* dw;
+  float* dk;
+};
+size_t indexer_bwd_workspace_bytes(int rows, int max_keys);
+
 // Head-mean causal attention distribution of packed rows [row_begin, row_end) of one sequence
 // starting at packed row seq_off: probs[(r - out_row0) * ld + s] for s <= r - seq_off, and the
 // per-head log-sum-exp lse[(r - out_row0) * hq + h].  Requires hq / hkv >= 4.
@@ -116,5 +134,6 @@ hipError_t launch_topk_rank(const TopkArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn(const SparseAttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const SparseAttnArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn_bwd(const SparseAttnBwdArgs& a, hipStream_t s);
+hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s);
 
 }  // namespace dsa
