@@ -107,13 +107,37 @@ __device__ __forceinline__ const uint16_t* t_tile_src(const uint16_t* tile, int 
   return tile + d * 64 + piece * 8;
 }
 
+// Wait until at most n of this wave's vector-memory operations are outstanding (n is
+// wave-uniform; the largest listed immediate <= n is used, which only ever waits longer).
+template <int N>
+__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void vm_wait_at_most(int n) {
+  if (n >= 15) vm_wait<15>();
+  else if (n >= 12) vm_wait<12>();
+  else if (n >= 10) vm_wait<10>();
+  else if (n >= 9) vm_wait<9>();
+  else if (n >= 8) vm_wait<8>();
+  else if (n >= 6) vm_wait<6>();
+  else if (n >= 5) vm_wait<5>();
+  else if (n >= 4) vm_wait<4>();
+  else if (n >= 3) vm_wait<3>();
+  else if (n >= 2) vm_wait<2>();
+  else if (n >= 1) vm_wait<1>();
+  else vm_wait<0>();
+}
+// Barrier of a staging ring: this wave's LDS operations done, every wave past the point.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 // ---------------------------------------------------------------------------------------
 // dq and dw: a workgroup of 2 NTOK waves takes NTOK consecutive query rows of one sequence and
 // one split of their keys; wave w handles heads 32 (w & 1) .. + 31 of token w / 2.  Per 64-key
 // tile (k rows, their transposed tile and the tokens' g values DMA'd to LDS, double buffered):
 //   X^T = K Q^T           (A: key rows from LDS, B: the wave's q rows in registers)
 //   u^T += K^T (g m)^T    (A: transposed key tile, B: bf16 of g m from the X^T registers)
-template <int NTOK>
+template <int NTOK, int NST>
 __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ kT,
     const float* __restrict__ w, const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end,
@@ -122,9 +146,9 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
   constexpr int NWV = 2 * NTOK;
   constexpr int GBYTES = ((NTOK * 256 + 1023) / 1024) * 1024;
   constexpr int NJOB = 32 + GBYTES / 1024;
-  __shared__ __attribute__((aligned(16))) unsigned char kt_lds[2][kRowTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char ktt_lds[2][kTTileBytes];
-  __shared__ __attribute__((aligned(16))) float g_lds[2][GBYTES / 4];
+  __shared__ __attribute__((aligned(16))) unsigned char kt_lds[NST][kRowTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ktt_lds[NST][kTTileBytes];
+  __shared__ __attribute__((aligned(16))) float g_lds[NST][GBYTES / 4];
 
   const int per_xcd = gridDim.x >> 3;
   const int wi = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -161,7 +185,10 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     for (int ht = 0; ht < 2; ++ht) u[dt][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* kseq = k_idx + (size_t)seq_off * kBD;
-  auto stage = [&](int it, int buf) {
+  // DMA jobs of 1 KiB each per stage: P = wave, wave + NWV, ... < NJOB.
+  const int jobs = (NJOB - wave + NWV - 1) / NWV;
+  auto stage = [&](int it) {
+    const int buf = it % NST;
     const int key0 = kbeg + it * 64;
     const int last = kend - 1 - key0;
     for (int P = wave; P < NJOB; P += NWV) {
@@ -179,58 +206,71 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     }
   };
 
-  stage(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Ring of NST stages: tiles it + 1 .. it + NST - 1 are in flight while tile it is used.
+  for (int i = 0; i < NST - 1 && i < ntiles; ++i) stage(i);
+  vm_wait_at_most(jobs * (min(NST - 1, ntiles) - 1));
+  ring_barrier();
 
   for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < ntiles) stage(it + 1, buf ^ 1);
+    const int buf = it % NST;
+    if (it + NST - 1 < ntiles) stage(it + NST - 1);
     const int key0 = kbeg + it * 64;
     if (row_ok && key0 <= t) {
       const unsigned char* ktile = kt_lds[buf];
       const unsigned char* kttile = ktt_lds[buf];
+      const bool diag = key0 + 63 > t;   // the token's last tile: keys past t get g = 0
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        u32x4 yv[2];
+        // All LDS operands of the 32-key pair first, so their latency hides under the MFMAs.
+        u32x4 ax[2][4], au[8];
+        f32x4 gv[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int kt = 2 * p + h;
-          f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-          const unsigned char* bp = ktile + (16 * kt + n) * 256;
-          __builtin_amdgcn_s_setprio(1);
+          const unsigned char* bp = ktile + (16 * (2 * p + h) + n) * 256;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
-#pragma unroll
-            for (int ht = 0; ht < 2; ++ht) x[ht] = mfma16x16x32(a, qreg[ht][ks], x[ht]);
-          }
-          __builtin_amdgcn_s_setprio(0);
-          // g of keys key0 + 16 kt + 4 lg + i for this wave's token, zero past its prefix.
-          const int kl = 16 * kt + 4 * lg;
-          const f32x4 gv = *reinterpret_cast<const f32x4*>(&g_lds[buf][tok * 64 + kl]);
-          float gm[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) gm[i] = (key0 + kl + i <= t) ? gv[i] : 0.f;
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht) {
-            yv[ht][2 * h] = cvt_bf16x2(x[ht][0] > 0.f ? gm[0] : 0.f, x[ht][1] > 0.f ? gm[1] : 0.f);
-            yv[ht][2 * h + 1] = cvt_bf16x2(x[ht][2] > 0.f ? gm[2] : 0.f, x[ht][3] > 0.f ? gm[3] : 0.f);
-          }
+          for (int ks = 0; ks < 4; ++ks) ax[h][ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
+          gv[h] = *reinterpret_cast<const f32x4*>(&g_lds[buf][tok * 64 + 16 * (2 * p + h) + 4 * lg]);
         }
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const int d = 16 * dt + n;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
-#pragma unroll
-          for (int ht = 0; ht < 2; ++ht) u[dt][ht] = mfma16x16x32(a, yv[ht], u[dt][ht]);
+          au[dt] = *reinterpret_cast<const u32x4*>(kttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
         }
-        __builtin_amdgcn_s_setprio(0);
+        f32x4 x[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) x[h][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht) x[h][ht] = mfma16x16x32(ax[h][ks], qreg[ht][ks], x[h][ht]);
+        if (diag) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (key0 + 16 * (2 * p + h) + 4 * lg + i > t) gv[h][i] = 0.f;
+        }
+        u32x4 yv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) {
+            yv[ht][2 * h] = cvt_bf16x2(x[h][ht][0] > 0.f ? gv[h][0] : 0.f, x[h][ht][1] > 0.f ? gv[h][1] : 0.f);
+            yv[ht][2 * h + 1] = cvt_bf16x2(x[h][ht][2] > 0.f ? gv[h][2] : 0.f, x[h][ht][3] > 0.f ? gv[h][3] : 0.f);
+          }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) u[dt][ht] = mfma16x16x32(au[dt], yv[ht], u[dt][ht]);
       }
     }
-    if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Tile it + 1 must have landed; later stages may stay in flight.
+    if (it + 1 < ntiles) vm_wait_at_most(jobs * (min(it + NST - 1, ntiles - 1) - (it + 1)));
+    ring_barrier();
   }
 
   if (!row_ok) return;
@@ -274,7 +314,7 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
 //   X = Q K^T             (A: q rows from LDS, B: the wave's key rows in registers)
 //   dk^T += (w Q)^T (g m) (A: transposed w q tile, B: bf16 of g m from the X registers)
 // and the block's dk is added to the output with fp32 atomics at the end.
-template <int NW>
+template <int NW, int NST>
 __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ qwT, const uint16_t* __restrict__ k_idx,
     const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end, int grad_row0,
@@ -282,9 +322,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
   constexpr int KB = 32 * NW;
   constexpr int GBYTES = ((KB * 4 + 1023) / 1024) * 1024;
   constexpr int NJOB = 32 + GBYTES / 1024;
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][kRowTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char qt_lds[2][kTTileBytes];
-  __shared__ __attribute__((aligned(16))) float g_lds[2][GBYTES / 4];
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[NST][kRowTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char qt_lds[NST][kTTileBytes];
+  __shared__ __attribute__((aligned(16))) float g_lds[NST][GBYTES / 4];
 
   const int per_xcd = gridDim.x >> 3;
   const int wi = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -316,7 +356,9 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto stage = [&](int tl, int buf) {
+  const int jobs = (NJOB - wave + NW - 1) / NW;
+  auto stage = [&](int tl) {
+    const int buf = (tl - ts) % NST;
     const int r = seq_off + tl;
     for (int P = wave; P < NJOB; P += NW) {
       if (P < 16) {
@@ -331,13 +373,15 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
     }
   };
 
-  stage(ts, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  // Ring of NST stages: tokens tl + 1 .. tl + NST - 1 are in flight while token tl is used.
+  const int ntok = te - ts;
+  for (int i = 0; i < NST - 1 && i < ntok; ++i) stage(ts + i);
+  vm_wait_at_most(jobs * (min(NST - 1, ntok) - 1));
+  ring_barrier();
 
   for (int tl = ts; tl < te; ++tl) {
-    const int buf = (tl - ts) & 1;
-    if (tl + 1 < te) stage(tl + 1, buf ^ 1);
+    const int buf = (tl - ts) % NST;
+    if (tl + NST - 1 < te) stage(tl + NST - 1);
     if (kw0 <= tl) {
       const unsigned char* qtile = q_lds[buf];
       const unsigned char* qttile = qt_lds[buf];
@@ -355,21 +399,18 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
           const int ht = 2 * p + h;
           f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
           const unsigned char* bp = qtile + (16 * ht + n) * 256;
-          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) x[kt] = mfma16x16x32(a, kreg[kt][ks], x[kt]);
           }
-          __builtin_amdgcn_s_setprio(0);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
             yv[kt][2 * h] = cvt_bf16x2(x[kt][0] > 0.f ? gk[kt] : 0.f, x[kt][1] > 0.f ? gk[kt] : 0.f);
             yv[kt][2 * h + 1] = cvt_bf16x2(x[kt][2] > 0.f ? gk[kt] : 0.f, x[kt][3] > 0.f ? gk[kt] : 0.f);
           }
         }
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const int d = 16 * dt + n;
@@ -377,11 +418,10 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma16x16x32(a, yv[kt], acc[dt][kt]);
         }
-        __builtin_amdgcn_s_setprio(0);
       }
     }
-    if (tl + 1 < te) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    if (tl + 1 < te) vm_wait_at_most(jobs * (min(tl + NST - 1, te - 1) - (tl + 1)));
+    ring_barrier();
   }
 
   // Lane (lg, n) holds dk^T[16 dt + 4 lg + i][key kw0 + 16 kt + n]; keys past the group's last
@@ -405,7 +445,8 @@ __global__ void bwd_zero_kernel(float* __restrict__ p, long long n) {
 
 constexpr int kBwdTok = 4;     // query tokens per dq workgroup (8 waves)
 constexpr int kBwdKeyW = 12;   // waves per dk workgroup (384 keys)
-constexpr int kBwdTokGroup = 256;
+constexpr int kBwdTokGroup = 128;
+constexpr int kBwdStages = 2;  // staging ring depth of both kernels
 
 }  // namespace
 
@@ -443,7 +484,7 @@ hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s) {
                        a.dw + (size_t)a.row_begin * kBH, (long long)rows * kBH);
   }
   const int q_items = n_rowblk * nsplit;
-  hipLaunchKernelGGL(indexer_bwd_q_kernel<kBwdTok>, dim3((q_items + 7) / 8 * 8), dim3(128 * kBwdTok), 0, s,
+  hipLaunchKernelGGL((indexer_bwd_q_kernel<kBwdTok, kBwdStages>), dim3((q_items + 7) / 8 * 8), dim3(128 * kBwdTok), 0, s,
                      a.q_idx, a.k_idx, (const uint16_t*)kT, a.w, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
                      a.grad_row0, a.dq, a.dw, key_split, n_rowblk, q_items, accumulate);
 
@@ -451,7 +492,7 @@ hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s) {
   const int n_keyblk = (nkeys + 32 * kBwdKeyW - 1) / (32 * kBwdKeyW);
   const int n_tg = (rows + kBwdTokGroup - 1) / kBwdTokGroup;
   const int k_items = n_keyblk * n_tg;
-  hipLaunchKernelGGL(indexer_bwd_k_kernel<kBwdKeyW>, dim3((k_items + 7) / 8 * 8), dim3(64 * kBwdKeyW), 0, s,
+  hipLaunchKernelGGL((indexer_bwd_k_kernel<kBwdKeyW, kBwdStages>), dim3((k_items + 7) / 8 * 8), dim3(64 * kBwdKeyW), 0, s,
                      a.q_idx, (const uint16_t*)a.workspace, a.k_idx, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
                      a.grad_row0, a.dk, kBwdTokGroup, n_keyblk, k_items);
   return hipGetLastError();
