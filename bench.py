@@ -10,7 +10,8 @@ driven through the C ABI's separate entry points with HIP events on the launch s
 every kernel, which gives the per-kernel times (and the rooflines) beside it.  The
 decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
 the torch.topk-shaped top-k on the decode scores, the backward of the sparse attention and the
-indexer's warm-up objective on the 32K prefill (context lines beside the headline value).
+indexer's warm-up step (target, KL and the indexer backward) on the 32K prefill (context lines
+beside the headline value).
 
 One JSON line is printed last.
 """
