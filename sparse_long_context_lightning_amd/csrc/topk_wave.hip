@@ -274,18 +274,21 @@ __global__ __launch_bounds__(NW * 64) void topk_collect_kernel(const float* __re
 // ---------------------------------------------------------------------------------------
 // Select: one 256-thread workgroup per row, the candidates held in registers (24 per thread).
 
+// Workgroup sizes of the block-wide select: 256 threads when rows are many (a row per
+// workgroup, several workgroups per CU), 1024 when they are few (decode: a CU per row).
 constexpr int kSelThreads = 256;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kPer = kCapW / kSelThreads;  // candidates per thread
+constexpr int kSelThreadsFew = 1024;
 
+template <int NT>
 struct SelSmem {
   uint32_t hist[kBins];
-  uint32_t wsum[kSelWaves];
-  uint32_t red[2][kSelWaves];
+  uint32_t wsum[NT / 64];
+  uint32_t red[2][NT / 64];
   uint32_t digit, above, in_bin;
   int pstar;
 };
 
+template <int NT>
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -298,7 +301,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total)
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const uint32_t s = wsum[i];
     pre += (i < wave) ? s : 0u;
     tot += s;
@@ -324,9 +327,10 @@ __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t bin) {
 // thread's elements), with n_eq and eq_total as in wave_select.  Barriers inside.
 // With max_rounds limiting the 10-bit rounds, *tau is the lower edge of the sub-bin that holds
 // the need-th largest key (bits below the resolved digits zero).
-template <typename Each>
-__device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* tau, uint32_t* n_eq,
+template <int NT, typename Each>
+__device__ void block_select(SelSmem<NT>& sm, Each each, uint32_t need, uint32_t* tau, uint32_t* n_eq,
                              uint32_t* eq_total, int max_rounds = 4) {
+  constexpr int BPT = kBins / NT;  // histogram bins per thread in the scan
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, cnt = 0;
   each([&](uint32_t key, uint32_t) {
@@ -341,9 +345,9 @@ __device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* ta
     sm.red[1][wave] = kmax;
   }
   uint32_t tot_cnt;
-  block_excl_scan(cnt, sm.wsum, tot_cnt);  // also orders the red[] writes before the reads below
+  block_excl_scan<NT>(cnt, sm.wsum, tot_cnt);  // also orders the red[] writes before the reads below
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     kmin = min(kmin, sm.red[0][i]);
     kmax = max(kmax, sm.red[1][i]);
   }
@@ -356,25 +360,25 @@ __device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* ta
     const int shift = low - width;
     const uint32_t nbin = 1u << width;
 #pragma unroll
-    for (int q = 0; q < kBins / kSelThreads; ++q) sm.hist[tid + kSelThreads * q] = 0;
+    for (int q = 0; q < BPT; ++q) sm.hist[tid + NT * q] = 0;
     __syncthreads();
     each([&](uint32_t key, uint32_t) {
       if ((key & mask) == prefix) hist_add(sm.hist, (key >> shift) & (nbin - 1u));
     });
     __syncthreads();
-    // Thread t owns bins kBins-1-4t .. kBins-4-4t, scanned from the top.
-    uint32_t c[4], sum = 0;
+    // Thread t owns bins kBins-1-BPT*t .. kBins-BPT-BPT*t, scanned from the top.
+    uint32_t c[BPT], sum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      c[q] = sm.hist[kBins - 1 - 4 * tid - q];
+    for (int q = 0; q < BPT; ++q) {
+      c[q] = sm.hist[kBins - 1 - BPT * tid - q];
       sum += c[q];
     }
     uint32_t tot;
-    uint32_t run = block_excl_scan(sum, sm.wsum, tot);
+    uint32_t run = block_excl_scan<NT>(sum, sm.wsum, tot);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < BPT; ++q) {
       if (run < need && run + c[q] >= need) {
-        sm.digit = (uint32_t)(kBins - 1 - 4 * tid - q);
+        sm.digit = (uint32_t)(kBins - 1 - BPT * tid - q);
         sm.above = run;
         sm.in_bin = c[q];
       }
@@ -394,15 +398,15 @@ __device__ void block_select(SelSmem& sm, Each each, uint32_t need, uint32_t* ta
 }
 
 // Ascending emission of the set bits of bits[0 .. NW): out[rank] = position.  Barriers inside.
-template <int NW>
-__device__ void block_emit_bits(SelSmem& sm, const uint32_t* bits, const float* src, int* out, float* vout) {
-  constexpr int W = NW / kSelThreads;
+template <int NT, int NW>
+__device__ void block_emit_bits(SelSmem<NT>& sm, const uint32_t* bits, const float* src, int* out, float* vout) {
+  constexpr int W = NW / NT;
   const int w0 = threadIdx.x * W;
   uint32_t local = 0;
 #pragma unroll
   for (int j = 0; j < W; ++j) local += (uint32_t)__popc(bits[w0 + j]);
   uint32_t tot;
-  uint32_t rank = block_excl_scan(local, sm.wsum, tot);
+  uint32_t rank = block_excl_scan<NT>(local, sm.wsum, tot);
   for (int j = 0; j < W; ++j) {
     uint32_t w = bits[w0 + j];
     while (w) {
@@ -416,15 +420,15 @@ __device__ void block_emit_bits(SelSmem& sm, const uint32_t* bits, const float* 
 }
 
 // Position of the need-th lowest set bit of bits[0 .. NW).  Barriers inside.
-template <int NW>
-__device__ int block_nth_bit(SelSmem& sm, const uint32_t* bits, uint32_t need) {
-  constexpr int W = NW / kSelThreads;
+template <int NT, int NW>
+__device__ int block_nth_bit(SelSmem<NT>& sm, const uint32_t* bits, uint32_t need) {
+  constexpr int W = NW / NT;
   const int w0 = threadIdx.x * W;
   uint32_t local = 0;
 #pragma unroll
   for (int j = 0; j < W; ++j) local += (uint32_t)__popc(bits[w0 + j]);
   uint32_t tot;
-  uint32_t run = block_excl_scan(local, sm.wsum, tot);
+  uint32_t run = block_excl_scan<NT>(local, sm.wsum, tot);
   if (run < need && run + local >= need) {
     for (int j = 0; j < W; ++j) {
       uint32_t w = bits[w0 + j];
@@ -441,46 +445,47 @@ __device__ int block_nth_bit(SelSmem& sm, const uint32_t* bits, uint32_t need) {
   return sm.pstar;
 }
 
-template <int NW>
+template <int NT, int NW>
 __device__ void block_zero(uint32_t* bits) {
   uint4* b4 = reinterpret_cast<uint4*>(bits);
-  for (int j = threadIdx.x; j < NW / 4; j += kSelThreads) b4[j] = make_uint4(0u, 0u, 0u, 0u);
+  for (int j = threadIdx.x; j < NW / 4; j += NT) b4[j] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
 }
 
 // The k positions from a stream that holds every selectable position: exact tau and n_eq,
 // the n_eq-th lowest tied position when ties exceed n_eq, bitmap, ascending emission.
-template <int NW, typename Each>
-__device__ void block_select_emit(SelSmem& sm, uint32_t* bits, Each each, int k, const float* src, int* out,
+template <int NT, int NW, typename Each>
+__device__ void block_select_emit(SelSmem<NT>& sm, uint32_t* bits, Each each, int k, const float* src, int* out,
                                   float* vout) {
   uint32_t tau, n_eq, eq_total;
-  block_select(sm, each, (uint32_t)k, &tau, &n_eq, &eq_total);
+  block_select<NT>(sm, each, (uint32_t)k, &tau, &n_eq, &eq_total);
   int pstar = 0x7FFFFFFF;
   if (eq_total > n_eq) {
-    block_zero<NW>(bits);
+    block_zero<NT, NW>(bits);
     each([&](uint32_t key, uint32_t pos) {
       if (key == tau) atomicOr(&bits[pos >> 5], 1u << (pos & 31));
     });
     __syncthreads();
-    pstar = block_nth_bit<NW>(sm, bits, n_eq);
+    pstar = block_nth_bit<NT, NW>(sm, bits, n_eq);
   }
-  block_zero<NW>(bits);
+  block_zero<NT, NW>(bits);
   each([&](uint32_t key, uint32_t pos) {
     if (key > tau || (key == tau && (int)pos <= pstar)) atomicOr(&bits[pos >> 5], 1u << (pos & 31));
   });
   __syncthreads();
-  block_emit_bits<NW>(sm, bits, src, out, vout);
+  block_emit_bits<NT, NW>(sm, bits, src, out, vout);
 }
 
-template <int NW>
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ scores, long long ld,
+template <int NW, int NT>
+__global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict__ scores, long long ld,
                                                                   int rows, const int* __restrict__ row_len,
                                                                   int len_base, int k, const uint32_t* __restrict__ cnt,
                                                                   const uint2* __restrict__ cand,
                                                                   int* __restrict__ idx_out,
                                                                   float* __restrict__ values_out) {
+  constexpr int kPer = kCapW / NT;  // candidates per thread
   __shared__ __attribute__((aligned(16))) uint32_t bits[NW];
-  __shared__ SelSmem sm;
+  __shared__ SelSmem<NT> sm;
   const int tid = threadIdx.x;
   const int row = rows - 1 - (int)blockIdx.x;  // longest rows first
   const int n = row_length(row_len, len_base, row, ld);
@@ -489,7 +494,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   const float* src = scores + (size_t)row * ld;
 
   if (n <= k) {
-    for (int i = tid; i < k; i += kSelThreads) {
+    for (int i = tid; i < k; i += NT) {
       out[i] = i < n ? i : -1;
       if (vout) vout[i] = i < n ? key_float(float_key(src[i])) : -INFINITY;
     }
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     uint32_t ck[kPer], cp[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const uint32_t i = tid + kSelThreads * j;
+      const uint32_t i = tid + NT * j;
       const uint2 c = (i < count) ? cr[i] : make_uint2(0u, 0u);
       ck[j] = c.x;
       cp[j] = c.y;
@@ -509,14 +514,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     auto each = [&](auto f) {
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (tid + kSelThreads * j < (int)count) f(ck[j], cp[j]);
+        if (tid + NT * j < (int)count) f(ck[j], cp[j]);
     };
-    block_select_emit<NW>(sm, bits, each, k, src, out, vout);
+    block_select_emit<NT, NW>(sm, bits, each, k, src, out, vout);
   } else {
     auto each = [&](auto f) {
-      for (int i = tid; i < n; i += kSelThreads) f(float_key(src[i]), (uint32_t)i);
+      for (int i = tid; i < n; i += NT) f(float_key(src[i]), (uint32_t)i);
     };
-    block_select_emit<NW>(sm, bits, each, k, src, out, vout);
+    block_select_emit<NT, NW>(sm, bits, each, k, src, out, vout);
   }
 }
 
@@ -525,16 +530,16 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
 // takes the lower edge of the sub-bin (two 10-bit rounds) that holds the sample_rank-th largest
 // sampled key.  Four times the wave form's sample keeps the candidate
 // count of rows up to 262144 scores close to its mean.
-template <int SPT>
-__global__ __launch_bounds__(kSelThreads) void topk_threshold_block_kernel(const float* __restrict__ scores,
+template <int SPT, int NT>
+__global__ __launch_bounds__(NT) void topk_threshold_block_kernel(const float* __restrict__ scores,
                                                                            long long ld, int rows,
                                                                            const int* __restrict__ row_len,
                                                                            int len_base, int k,
                                                                            uint32_t* __restrict__ tau_lo,
                                                                            uint32_t* __restrict__ cnt) {
   static_assert(4 * SPT <= 32, "valid mask is 32 bits");
-  constexpr int kStrataB = kSelThreads * SPT;
-  __shared__ SelSmem sm;
+  constexpr int kStrataB = NT * SPT;
+  __shared__ SelSmem<NT> sm;
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   if (row >= rows) return;
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_block_kernel(const
   uint32_t valid = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
-    const uint32_t st = (uint32_t)(tid + kSelThreads * j);
+    const uint32_t st = (uint32_t)(tid + NT * j);
     const uint32_t slot = whole ? st : st * sf + ((st * 2654435761u) >> 8) % sf;
     const int p = (int)(4 * slot);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -567,7 +572,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_threshold_block_kernel(const
       if ((valid >> j) & 1u) f(key[j], 0u);
   };
   uint32_t tau, n_eq, eq_total;
-  block_select(sm, each, sample_rank(m, n, k), &tau, &n_eq, &eq_total, 2);
+  block_select<NT>(sm, each, sample_rank(m, n, k), &tau, &n_eq, &eq_total, 2);
   if (tid == 0) tau_lo[row] = tau;
 }
 
@@ -583,10 +588,11 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
   uint32_t* cnt = tau_lo + a.rows;
   const size_t head = ((size_t)a.rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   uint2* cand = reinterpret_cast<uint2*>(static_cast<char*>(a.workspace) + head);
-  if (a.rows <= 512) {
-    // few rows: a workgroup per row and a four times larger sample
-    hipLaunchKernelGGL(topk_threshold_block_kernel<8>, dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores,
-                       a.ld, a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
+  const bool few = a.rows <= 512;
+  if (few) {
+    // few rows: a 1024-thread workgroup per row and a four times larger sample
+    hipLaunchKernelGGL((topk_threshold_block_kernel<2, kSelThreadsFew>), dim3((unsigned)a.rows), dim3(kSelThreadsFew),
+                       0, s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, tau_lo, cnt);
   } else {
     const unsigned groups = (unsigned)((a.rows + 3) / 4);
     hipLaunchKernelGGL(topk_threshold_kernel, dim3(groups), dim3(256), 0, s, a.scores, a.ld, a.rows, a.row_len,
@@ -611,12 +617,21 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(topk_collect_kernel<4>, dim3((unsigned)(a.rows * (nseg / 4))), dim3(256), 0, s, a.scores,
                        a.ld, a.rows, a.row_len, a.len_base, a.k, (int)seg_len, (int)nseg, tau_lo, cnt, cand);
   }
-  if (a.ld <= 131072)
-    hipLaunchKernelGGL((topk_select_kernel<4096>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores, a.ld,
-                       a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
-  else
-    hipLaunchKernelGGL((topk_select_kernel<8192>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s, a.scores, a.ld,
-                       a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+  if (few) {
+    if (a.ld <= 131072)
+      hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreadsFew>), dim3((unsigned)a.rows), dim3(kSelThreadsFew), 0,
+                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+    else
+      hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreadsFew>), dim3((unsigned)a.rows), dim3(kSelThreadsFew), 0,
+                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+  } else {
+    if (a.ld <= 131072)
+      hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
+                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+    else
+      hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
+                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+  }
   return hipGetLastError();
 }
 
