@@ -381,8 +381,6 @@ def warmup_bench(args, dsa, inp, tl):
     dq = torch.empty(total, h_idx, d_idx, dtype=torch.float32, device="cuda")
     dw = torch.empty(total, h_idx, dtype=torch.float32, device="cuda")
     dk = torch.empty(total, d_idx, dtype=torch.float32, device="cuda")
-    ws = torch.empty(dsa.dsa_index_scores_bwd_workspace_size(total, h_idx, d_idx, chunk), dtype=torch.uint8,
-                     device="cuda")
     t_target = []
     t_bwd = []
 
@@ -402,7 +400,7 @@ def warmup_bench(args, dsa, inp, tl):
             timed(lambda: dsa.dsa_attn_head_mean(dev["q"], dev["k"], cu, c0, n, probs, lse, ld=ld), t_target)
             dsa.dsa_indexer_kl(scores, probs, row_len[c0:c0 + n], loss[c0:c0 + n], scores, ld=ld)
             timed(lambda: dsa.dsa_index_scores_bwd(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, n, scores, dq, dw, dk,
-                                                   workspace=ws, ld=ld), t_bwd)
+                                                   ld=ld), t_bwd)
 
     step()
     torch.cuda.synchronize()
@@ -450,7 +448,7 @@ def warmup_bench(args, dsa, inp, tl):
     log(f"indexer warm-up step {ms:.1f} ms per pass (target {target_ms:.1f} ms, "
         f"{target_flops / (target_ms * 1e-3) / 1e12:.0f} TFLOP/s; indexer backward {bwd_ms:.1f} ms, "
         f"{bwd_flops / (bwd_ms * 1e-3) / 1e12:.0f} TFLOP/s); row-loss parity {ok}, backward rows {bwd_ok}")
-    del dev, scores, probs, lse, loss, dq, dw, dk, ws
+    del dev, scores, probs, lse, loss, dq, dw, dk
     torch.cuda.empty_cache()
     return {"workload": args.bwd_workload, "ms": ms, "tokens_per_s": total / (ms * 1e-3), "target_ms": target_ms,
             "target_tflops": target_flops / (target_ms * 1e-3) / 1e12, "rows_checked": len(rows), "loss_parity": ok,

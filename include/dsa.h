@@ -102,20 +102,16 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w,
  * dq_idx [total_tokens, h_idx, d_idx], dw [total_tokens, h_idx], dk_idx [total_tokens, d_idx]
  *   float.  dk_idx is added to, so a pass over several row chunks zeroes it once first.
  * Arithmetic: c is recomputed on bf16 MFMA with fp32 accumulation ([c > 0] is the forward's
- *   ReLU decision); g [c > 0] and w q_idx are rounded to bf16 for the second contraction, fp32
- *   accumulation.  dk_idx (and dq_idx / dw when a row's keys are split over workgroups) is
- *   summed with fp32 atomics, so its last bits can differ between runs.
- * workspace (device, 16-byte aligned) of at least dsa_index_scores_bwd_workspace_size bytes:
- *   transposed copies of the rows' w-scaled queries and of one sequence's keys.
- * Supports h_idx = 64, d_idx = 128 (DSA_ERR_UNSUPPORTED otherwise).
+ *   ReLU decision); g [c > 0] (for dk_idx g w [c > 0]) is rounded to bf16 for the second
+ *   contraction, fp32 accumulation.  dk_idx (and dq_idx / dw when a row's keys are split over
+ *   workgroups) is summed with fp32 atomics, so its last bits can differ between runs.
+ * Needs no workspace.  Supports h_idx = 64, d_idx = 128 (DSA_ERR_UNSUPPORTED otherwise).
  */
-int dsa_index_scores_bwd_workspace_size(int total_tokens, int h_idx, int d_idx, int row_count, size_t* bytes);
 int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w,
                          const int32_t* cu_seqlens_host, int batch, int total_tokens,
                          int h_idx, int d_idx, int row_begin, int row_count,
                          const float* dscores, int64_t ld,
-                         float* dq_idx, float* dw, float* dk_idx,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         float* dq_idx, float* dw, float* dk_idx, void* stream);
 
 /*
  * Target of the indexer's dense warm-up (digest section 一: with the full attention unchanged,

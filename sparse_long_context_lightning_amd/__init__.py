@@ -22,7 +22,6 @@ from ._lib import (  # noqa: F401
     dsa_attn_head_mean,
     dsa_index_scores,
     dsa_index_scores_bwd,
-    dsa_index_scores_bwd_workspace_size,
     dsa_indexer_kl,
     dsa_last_error,
     dsa_prefill,

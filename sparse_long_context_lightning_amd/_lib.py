@@ -27,7 +27,7 @@ EXPORTED = (
     "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
     "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
     "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean", "dsa_indexer_kl",
-    "dsa_index_scores_bwd_workspace_size", "dsa_index_scores_bwd",
+    "dsa_index_scores_bwd",
 )
 
 
@@ -64,8 +64,7 @@ def load():
         "dsa_topk_sorted": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_attn_head_mean": ([_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _I64, _P, _P], _I),
         "dsa_indexer_kl": ([_P, _P, _I64, _I, _P, _P, _P, _P], _I),
-        "dsa_index_scores_bwd_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
-        "dsa_index_scores_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P, _P, _P, _P, _SZ, _P], _I),
+        "dsa_index_scores_bwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
                                     _I),
@@ -154,26 +153,16 @@ def dsa_indexer_kl(scores, target, row_len, row_loss, grad, ld=None, stream=None
                                  _stream(stream)))
 
 
-def dsa_index_scores_bwd_workspace_size(total_tokens, h_idx, d_idx, row_count) -> int:
-    n = _SZ(0)
-    _check(load().dsa_index_scores_bwd_workspace_size(total_tokens, h_idx, d_idx, row_count, ctypes.byref(n)))
-    return n.value
-
-
 def dsa_index_scores_bwd(q_idx, k_idx, w, cu_seqlens_host, row_begin, row_count, dscores, dq_idx, dw, dk_idx,
-                         workspace=None, ld=None, stream=None):
+                         ld=None, stream=None):
     """Backward of dsa_index_scores for packed rows [row_begin, row_begin + row_count): dq_idx and dw of
     those rows are written, dk_idx is added to.  dscores[row_count, ld] is the gradient of their scores."""
-    import torch
     cu, cu_p = _host_i32(cu_seqlens_host)
     total, h_idx, d_idx = q_idx.shape
     ld = dscores.shape[1] if ld is None else ld
-    if workspace is None:
-        need = dsa_index_scores_bwd_workspace_size(total, h_idx, d_idx, row_count)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_idx.device)
     _check(load().dsa_index_scores_bwd(_ptr(q_idx), _ptr(k_idx), _ptr(w), cu_p, len(cu) - 1, total, h_idx, d_idx,
                                        row_begin, row_count, _ptr(dscores), ld, _ptr(dq_idx), _ptr(dw),
-                                       _ptr(dk_idx), _ptr(workspace), workspace.numel(), _stream(stream)))
+                                       _ptr(dk_idx), _stream(stream)))
 
 
 def dsa_topk_workspace_size(rows, ld, k) -> int:

@@ -185,19 +185,9 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
                            row_begin, scores, ld, static_cast<hipStream_t>(stream));
 }
 
-int dsa_index_scores_bwd_workspace_size(int total_tokens, int h_idx, int d_idx, int row_count, size_t* bytes) {
-  g_last_error[0] = 0;
-  DSA_NONNULL(bytes);
-  if (total_tokens < 0 || row_count < 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens and row_count must be >= 0");
-  DSA_TRY(check_indexer_bwd_shape(h_idx, d_idx));
-  *bytes = dsa::indexer_bwd_workspace_bytes(row_count, total_tokens);
-  return DSA_OK;
-}
-
 int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu_seqlens_host,
                          int batch, int total_tokens, int h_idx, int d_idx, int row_begin, int row_count,
-                         const float* dscores, int64_t ld, float* dq_idx, float* dw, float* dk_idx, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         const float* dscores, int64_t ld, float* dq_idx, float* dw, float* dk_idx, void* stream) {
   g_last_error[0] = 0;
   DSA_NONNULL(q_idx);
   DSA_NONNULL(k_idx);
@@ -226,10 +216,6 @@ int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, c
                   r1 - cu_seqlens_host[b]);
   }
   if (row_count == 0) return DSA_OK;
-  const size_t need = dsa::indexer_bwd_workspace_bytes(row_count, max_len);
-  if (!workspace || workspace_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
-  DSA_ALIGNED(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   for (int b = 0; b < batch; ++b) {
     const int r0 = std::max(row_begin, cu_seqlens_host[b]);
@@ -245,8 +231,6 @@ int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, c
     a.row_begin = r0;
     a.row_end = r1;
     a.grad_row0 = row_begin;
-    a.ws_rows = row_count;
-    a.workspace = static_cast<uint16_t*>(workspace);
     a.dq = dq_idx;
     a.dw = dw;
     a.dk = dk_idx;

@@ -12,15 +12,14 @@
 // its (token, head) rows in registers (dq, dw); the key-major one streams query tokens through
 // LDS and keeps dk of its keys in registers.  Each recomputes c on MFMA with the forward's
 // operands and fp32 accumulation, so m is the forward's ReLU decision; the second contraction
-// takes g m (and w q_idx) rounded to bf16.  Its contracted operand has to be laid out with the
-// reduction index (s, or the heads) contiguous, which is the transpose of how k_idx and q_idx
-// are stored, so a small kernel first writes transposed 64-row tiles of both into the workspace.
+// takes g m (g w m for dk) rounded to bf16.  That contraction runs over the keys (or the heads),
+// so its A operand is the staged tile read transposed, with ds_read_b64_tr_b16.
 //
 // MFMA C layout: lane (a, n) with a = lane / 16, n = lane % 16 holds C[4a + i][n], i = 0..3.
 // Both second contractions take their B operand straight from the first one's C registers:
 // C rows 4a + i of two 16-row tiles (h = 0, 1) become the 8 reduction slots e = 4h + i of lane
-// group a, and the transposed tiles store row 32p + 16h + 4a + i at column 32p + 8a + 4h + i so
-// that the matching A operand is one contiguous 16-byte read.
+// group a, and the transposed reads gather the same 8 tile rows 32p + 16h + 4a + i for lane
+// group a, so both operands agree on which key (head) each slot carries.
 #include <algorithm>
 
 #include "common.h"
@@ -31,7 +30,6 @@ namespace {
 
 constexpr int kBH = 64;    // indexer heads
 constexpr int kBD = 128;   // indexer dim
-constexpr int kTileElems = 64 * kBD;  // one transposed tile: 128 rows of 64 bf16
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -41,70 +39,31 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Column of source row r (0..63) in a transposed tile.
-__device__ __forceinline__ int tcol(int r) {
-  return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
-}
-
-// ---------------------------------------------------------------------------------------
-// Transposed tiles: tile i takes source rows [64 i, 64 i + 64) of a row-major [rows][128] bf16
-// array (rows >= nrows read as zero), multiplies row r by scale[r] if scale is given (rounded
-// back to bf16), and writes dst[i][d][tcol(r)].
-__global__ __launch_bounds__(256) void bwd_transpose_kernel(const uint16_t* __restrict__ src,
-                                                            const float* __restrict__ scale, int nrows,
-                                                            uint16_t* __restrict__ dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[kBD * 64];
-  const int tile = blockIdx.x;
-  const int r = threadIdx.x >> 2, part = threadIdx.x & 3;  // row, quarter of its 128 values
-  const long long row = (long long)tile * 64 + r;
-  const int col = tcol(r);
-  if (row < nrows) {
-    const uint16_t* sp = src + row * kBD + part * 32;
-    const float sc = scale ? scale[row] : 1.f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 v = ldg16(sp + c * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t h = uint16_t(v[e >> 1] >> (16 * (e & 1)));
-        if (scale) {
-          const float f = bf16_to_f32(h) * sc;
-          h = uint16_t(cvt_bf16x2(f, 0.f) & 0xFFFFu);
-        }
-        t[(part * 32 + c * 8 + e) * 64 + col] = h;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 32; ++e) t[(part * 32 + e) * 64 + col] = 0;
-  }
-  __syncthreads();
-  uint16_t* dp = dst + (size_t)tile * kTileElems;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int off = (threadIdx.x + 256 * m) * 8;
-    *reinterpret_cast<u32x4*>(dp + off) = *reinterpret_cast<const u32x4*>(t + off);
-  }
-}
-
-// LDS tiles of both kernels (bytes):
-//   row tile [64 rows][256 B]: 16-byte piece c of row r at slot c ^ (r & 15)
-//   T tile   [128 rows][128 B]: piece c of row d at slot c ^ ((d >> 1) & 7)
-// (the 16 lanes of one LDS phase of an operand read then hit 16 distinct bank groups).
 constexpr int kRowTileBytes = 64 * 256;
-constexpr int kTTileBytes = 128 * 128;
 
-// Global source of DMA lane l of row-tile job P (P = 0..15): the piece that belongs at LDS
-// byte 1024 P + 16 l.  base points at row 0; rows past last_row are clamped to it.
-__device__ __forceinline__ const uint16_t* row_tile_src(const uint16_t* base, int P, int lane, int last_row) {
+// Row tiles of both passes (64 keys, or one token's 64 heads), read both ways: [64 rows][256 B]
+// with piece c of row r at slot c ^ swz(r), where for r mod 16 = 4a + b,
+// swz = (b << 1) | (a >> 1) | ((a & 1) << 3).  It is a permutation of 0..15, so the 16 rows of
+// one row-wise operand read hit 16 distinct slots, and the transposed reads below (rows
+// 4a + 0..3, two neighbouring pieces, two lane groups a) hit distinct slots as well.
+__device__ __forceinline__ int swz(int r) {
+  const int a = (r >> 2) & 3, b = r & 3;
+  return (b << 1) | (a >> 1) | ((a & 1) << 3);
+}
+__device__ __forceinline__ const uint16_t* swz_tile_src(const uint16_t* base, int P, int lane, int last_row) {
   const int row = 4 * P + (lane >> 4);
-  const int piece = (lane & 15) ^ (row & 15);
+  const int piece = (lane & 15) ^ swz(row);
   return base + (size_t)min(row, last_row) * kBD + piece * 8;
 }
-__device__ __forceinline__ const uint16_t* t_tile_src(const uint16_t* tile, int P, int lane) {
-  const int d = 8 * P + (lane >> 3);
-  const int piece = (lane & 7) ^ ((d >> 1) & 7);
-  return tile + d * 64 + piece * 8;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// words that lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 address (in that order).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 // Wait until at most n of this wave's vector-memory operations are outstanding (n is
@@ -134,20 +93,19 @@ __device__ __forceinline__ void ring_barrier() {
 // ---------------------------------------------------------------------------------------
 // dq and dw: a workgroup of 2 NTOK waves takes NTOK consecutive query rows of one sequence and
 // one split of their keys; wave w handles heads 32 (w & 1) .. + 31 of token w / 2.  Per 64-key
-// tile (k rows, their transposed tile and the tokens' g values DMA'd to LDS, double buffered):
+// tile (the k rows and the tokens' g values DMA'd to LDS, in a ring of NST stages):
 //   X^T = K Q^T           (A: key rows from LDS, B: the wave's q rows in registers)
-//   u^T += K^T (g m)^T    (A: transposed key tile, B: bf16 of g m from the X^T registers)
+//   u^T += K^T (g m)^T    (A: the same key rows read transposed, B: bf16 of g m from the X^T
+//                          registers)
 template <int NTOK, int NST>
 __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ kT,
-    const float* __restrict__ w, const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end,
-    int grad_row0, float* __restrict__ dq, float* __restrict__ dw, int key_split, int n_rowblk, int n_items,
-    int accumulate) {
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ w,
+    const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end, int grad_row0,
+    float* __restrict__ dq, float* __restrict__ dw, int key_split, int n_rowblk, int n_items, int accumulate) {
   constexpr int NWV = 2 * NTOK;
   constexpr int GBYTES = ((NTOK * 256 + 1023) / 1024) * 1024;
-  constexpr int NJOB = 32 + GBYTES / 1024;
+  constexpr int NJOB = 16 + GBYTES / 1024;
   __shared__ __attribute__((aligned(16))) unsigned char kt_lds[NST][kRowTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char ktt_lds[NST][kTTileBytes];
   __shared__ __attribute__((aligned(16))) float g_lds[NST][GBYTES / 4];
 
   const int per_xcd = gridDim.x >> 3;
@@ -193,15 +151,13 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     const int last = kend - 1 - key0;
     for (int P = wave; P < NJOB; P += NWV) {
       if (P < 16) {
-        lds_dma16(row_tile_src(kseq + (size_t)key0 * kBD, P, lane, last), &kt_lds[buf][P * 1024]);
-      } else if (P < 32) {
-        lds_dma16(t_tile_src(kT + (size_t)(key0 >> 6) * kTileElems, P - 16, lane), &ktt_lds[buf][(P - 16) * 1024]);
+        lds_dma16(swz_tile_src(kseq + (size_t)key0 * kBD, P, lane, last), &kt_lds[buf][P * 1024]);
       } else {
-        const int m = (P - 32) * 64 + lane;  // 16-byte piece: token m / 16, keys 4 (m % 16) ..
+        const int m = (P - 16) * 64 + lane;  // 16-byte piece: token m / 16, keys 4 (m % 16) ..
         const int gr = min(r0 + min(m >> 4, NTOK - 1), row_end - 1);
         int a = key0 + 4 * (m & 15);
         if (a > gr - seq_off) a = 0;  // past the row's prefix: any valid address (masked below)
-        lds_dma16(g + (size_t)(gr - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 32) * 1024);
+        lds_dma16(g + (size_t)(gr - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
       }
     }
   };
@@ -217,8 +173,12 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     const int key0 = kbeg + it * 64;
     if (row_ok && key0 <= t) {
       const unsigned char* ktile = kt_lds[buf];
-      const unsigned char* kttile = ktt_lds[buf];
       const bool diag = key0 + 63 > t;   // the token's last tile: keys past t get g = 0
+      // Transposed reads: lane j of lane group lg addresses key 32 p + 16 h + 4 lg + j / 4, dims
+      // 16 dt + 4 (j % 4) .. + 3, so lane n receives dim 16 dt + n of those four keys.
+      const int trow = 4 * lg + (n >> 2);
+      const int tm = n & 3;
+      const int tsw = swz(trow);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         // All LDS operands of the 32-key pair first, so their latency hides under the MFMAs.
@@ -228,13 +188,17 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
         for (int h = 0; h < 2; ++h) {
           const unsigned char* bp = ktile + (16 * (2 * p + h) + n) * 256;
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) ax[h][ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
+          for (int ks = 0; ks < 4; ++ks)
+            ax[h][ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ swz(n)) << 4));
           gv[h] = *reinterpret_cast<const f32x4*>(&g_lds[buf][tok * 64 + 16 * (2 * p + h) + 4 * lg]);
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const int d = 16 * dt + n;
-          au[dt] = *reinterpret_cast<const u32x4*>(kttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
+          const int piece = 2 * dt + (tm >> 1);
+          const unsigned char* b0 = ktile + (32 * p + trow) * 256 + ((piece ^ tsw) << 4) + 8 * (tm & 1);
+          const uint2 lo = lds_read_tr16(b0);
+          const uint2 hi = lds_read_tr16(b0 + 16 * 256);
+          au[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
         }
         f32x4 x[2][2];
 #pragma unroll
@@ -308,22 +272,22 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// dk: a workgroup of NW waves takes 32 NW consecutive keys of one sequence and one group of
-// query tokens; wave w holds keys 32 w .. + 31 of the block.  Per token (its 64 q rows, its
-// transposed w-scaled tile and its g values over the block DMA'd to LDS, double buffered):
+// dk: a workgroup of NW waves takes 16 KT NW consecutive keys of one sequence and one group of
+// query tokens; wave w holds keys 16 KT w .. + 16 KT - 1 of the block.  Per token (its 64 q rows, its g
+// values over the block and its 64 weights DMA'd to LDS, double buffered):
 //   X = Q K^T             (A: q rows from LDS, B: the wave's key rows in registers)
-//   dk^T += (w Q)^T (g m) (A: transposed w q tile, B: bf16 of g m from the X registers)
+//   dk^T += Q^T (g w m)   (A: the same q rows read transposed, B: bf16 of g w m from the X
+//                          registers)
 // and the block's dk is added to the output with fp32 atomics at the end.
-template <int NW, int NST>
+template <int NW, int KT, int NST>
 __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
-    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ qwT, const uint16_t* __restrict__ k_idx,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const float* __restrict__ g, long long ld, int seq_off, int row_begin, int row_end, int grad_row0,
     float* __restrict__ dk, int tok_group, int n_keyblk, int n_items) {
-  constexpr int KB = 32 * NW;
-  constexpr int GBYTES = ((KB * 4 + 1023) / 1024) * 1024;
-  constexpr int NJOB = 32 + GBYTES / 1024;
+  constexpr int KB = 16 * KT * NW;  // keys of the block (16 KT per wave)
+  constexpr int GBYTES = ((KB * 4 + 256 + 1023) / 1024) * 1024;  // g of the block, then the 64 weights
+  constexpr int NJOB = 16 + GBYTES / 1024;
   __shared__ __attribute__((aligned(16))) unsigned char q_lds[NST][kRowTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char qt_lds[NST][kTTileBytes];
   __shared__ __attribute__((aligned(16))) float g_lds[NST][GBYTES / 4];
 
   const int per_xcd = gridDim.x >> 3;
@@ -339,22 +303,22 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
-  const int kw0 = kb0 + 32 * wave;
+  const int kw0 = kb0 + 16 * KT * wave;
 
   // B operands of X: key kw0 + 16 kt + n, reduction piece lg * 4 + ks.
-  u32x4 kreg[2][4];
+  u32x4 kreg[KT][4];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = min(kw0 + 16 * kt + n, te - 1);
     const uint16_t* kp = k_idx + ((size_t)seq_off + key) * kBD + lg * 32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) kreg[kt][ks] = ldg16(kp + ks * 8);
   }
-  f32x4 acc[8][2];
+  f32x4 acc[8][KT];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int jobs = (NJOB - wave + NW - 1) / NW;
   auto stage = [&](int tl) {
@@ -362,13 +326,18 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
     const int r = seq_off + tl;
     for (int P = wave; P < NJOB; P += NW) {
       if (P < 16) {
-        lds_dma16(row_tile_src(q_idx + (size_t)r * kBH * kBD, P, lane, kBH - 1), &q_lds[buf][P * 1024]);
-      } else if (P < 32) {
-        lds_dma16(t_tile_src(qwT + (size_t)(r - grad_row0) * kTileElems, P - 16, lane), &qt_lds[buf][(P - 16) * 1024]);
+        lds_dma16(swz_tile_src(q_idx + (size_t)r * kBH * kBD, P, lane, kBH - 1), &q_lds[buf][P * 1024]);
       } else {
-        int a = kb0 + 4 * ((P - 32) * 64 + lane);
-        if (a > tl) a = kb0;  // past the row's prefix: any valid address (masked below)
-        lds_dma16(g + (size_t)(r - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 32) * 1024);
+        const int m = (P - 16) * 64 + lane;  // 16-byte piece of the g / w region
+        const float* src;
+        if (m < KB / 4) {
+          int a = kb0 + 4 * m;
+          if (a > tl) a = kb0;  // past the row's prefix: any valid address (masked below)
+          src = g + (size_t)(r - grad_row0) * ld + a;
+        } else {
+          src = w + (size_t)r * kBH + 4 * min(m - KB / 4, kBH / 4 - 1);
+        }
+        lds_dma16(src, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
       }
     }
   };
@@ -384,39 +353,52 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
     if (tl + NST - 1 < te) stage(tl + NST - 1);
     if (kw0 <= tl) {
       const unsigned char* qtile = q_lds[buf];
-      const unsigned char* qttile = qt_lds[buf];
-      float gk[2];
+      const float* wl = g_lds[buf] + KB;  // the token's 64 weights
+      float gk[KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         const int key = kw0 + 16 * kt + n;
         gk[kt] = (key <= tl) ? g_lds[buf][key - kb0] : 0.f;
       }
+      // Transposed reads: lane j of lane group lg addresses head 32 p + 16 h + 4 lg + j / 4,
+      // dims 16 dt + 4 (j % 4) .. + 3, so lane n receives dim 16 dt + n of those four heads.
+      const int trow = 4 * lg + (n >> 2);
+      const int tm = n & 3;
+      const int tsw = swz(trow);
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        u32x4 yv[2];
+        u32x4 yv[KT];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int ht = 2 * p + h;
-          f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+          f32x4 x[KT];
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) x[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
           const unsigned char* bp = qtile + (16 * ht + n) * 256;
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ n) << 4));
+            const u32x4 a = *reinterpret_cast<const u32x4*>(bp + (((lg * 4 + ks) ^ swz(n)) << 4));
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) x[kt] = mfma16x16x32(a, kreg[kt][ks], x[kt]);
+            for (int kt = 0; kt < KT; ++kt) x[kt] = mfma16x16x32(a, kreg[kt][ks], x[kt]);
           }
+          // weights of heads 16 ht + 4 lg + i (the C rows this lane holds)
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(wl + 16 * ht + 4 * lg);
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            yv[kt][2 * h] = cvt_bf16x2(x[kt][0] > 0.f ? gk[kt] : 0.f, x[kt][1] > 0.f ? gk[kt] : 0.f);
-            yv[kt][2 * h + 1] = cvt_bf16x2(x[kt][2] > 0.f ? gk[kt] : 0.f, x[kt][3] > 0.f ? gk[kt] : 0.f);
+          for (int kt = 0; kt < KT; ++kt) {
+            const f32x4 gw = wv * gk[kt];
+            yv[kt][2 * h] = cvt_bf16x2(x[kt][0] > 0.f ? gw[0] : 0.f, x[kt][1] > 0.f ? gw[1] : 0.f);
+            yv[kt][2 * h + 1] = cvt_bf16x2(x[kt][2] > 0.f ? gw[2] : 0.f, x[kt][3] > 0.f ? gw[3] : 0.f);
           }
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const int d = 16 * dt + n;
-          const u32x4 a = *reinterpret_cast<const u32x4*>(qttile + d * 128 + (((4 * p + lg) ^ ((d >> 1) & 7)) << 4));
+          const int piece = 2 * dt + (tm >> 1);
+          const unsigned char* b0 = qtile + (32 * p + trow) * 256 + ((piece ^ tsw) << 4) + 8 * (tm & 1);
+          const uint2 lo = lds_read_tr16(b0);
+          const uint2 hi = lds_read_tr16(b0 + 16 * 256);
+          const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) acc[dt][kt] = mfma16x16x32(a, yv[kt], acc[dt][kt]);
+          for (int kt = 0; kt < KT; ++kt) acc[dt][kt] = mfma16x16x32(a, yv[kt], acc[dt][kt]);
         }
       }
     }
@@ -427,7 +409,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
   // Lane (lg, n) holds dk^T[16 dt + 4 lg + i][key kw0 + 16 kt + n]; keys past the group's last
   // token received nothing (and may lie past the sequence).
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = kw0 + 16 * kt + n;
     if (key >= te) continue;
     float* dkp = dk + ((size_t)seq_off + key) * kBD + 4 * lg;
@@ -444,31 +426,19 @@ __global__ void bwd_zero_kernel(float* __restrict__ p, long long n) {
 }
 
 constexpr int kBwdTok = 4;     // query tokens per dq workgroup (8 waves)
-constexpr int kBwdKeyW = 12;   // waves per dk workgroup (384 keys)
+constexpr int kBwdKeyW = 12;   // waves per dk workgroup
+constexpr int kBwdKeyT = 2;    // 16-key tiles per dk wave (384 keys per workgroup)
 constexpr int kBwdTokGroup = 128;
-constexpr int kBwdStages = 2;  // staging ring depth of both kernels
+constexpr int kBwdStages = 2;  // staging ring depth of the dk pass
+constexpr int kBwdStagesQ = 2; // and of the dq pass
 
 }  // namespace
-
-size_t indexer_bwd_workspace_bytes(int rows, int max_keys) {
-  const size_t q_part = ((size_t)rows * kTileElems * 2 + 255) / 256 * 256;
-  const size_t k_part = (size_t)((max_keys + 63) / 64) * kTileElems * 2;
-  return q_part + k_part;
-}
 
 hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
   if (rows <= 0) return hipSuccess;
   const int t_last = a.row_end - 1 - a.seq_off;
   const int nkeys = t_last + 1;
-  uint16_t* qwT = a.workspace + (size_t)(a.row_begin - a.grad_row0) * kTileElems;
-  uint16_t* kT = a.workspace + ((size_t)a.ws_rows * kTileElems * 2 + 255) / 256 * 256 / 2;
-  // Transposed tiles: the sequence's keys [0, nkeys), the rows' w-scaled queries.
-  hipLaunchKernelGGL(bwd_transpose_kernel, dim3((nkeys + 63) / 64), dim3(256), 0, s,
-                     a.k_idx + (size_t)a.seq_off * kBD, (const float*)nullptr, nkeys, kT);
-  hipLaunchKernelGGL(bwd_transpose_kernel, dim3(rows), dim3(256), 0, s, a.q_idx + (size_t)a.row_begin * kBH * kBD,
-                     a.w + (size_t)a.row_begin * kBH, rows * kBH, qwT);
-
   // dq, dw: row blocks x key splits; split the keys only while the row blocks alone leave
   // the chip under-filled.
   const int n_rowblk = (rows + kBwdTok - 1) / kBwdTok;
@@ -484,16 +454,16 @@ hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s) {
                        a.dw + (size_t)a.row_begin * kBH, (long long)rows * kBH);
   }
   const int q_items = n_rowblk * nsplit;
-  hipLaunchKernelGGL((indexer_bwd_q_kernel<kBwdTok, kBwdStages>), dim3((q_items + 7) / 8 * 8), dim3(128 * kBwdTok), 0, s,
-                     a.q_idx, a.k_idx, (const uint16_t*)kT, a.w, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
-                     a.grad_row0, a.dq, a.dw, key_split, n_rowblk, q_items, accumulate);
+  hipLaunchKernelGGL((indexer_bwd_q_kernel<kBwdTok, kBwdStagesQ>), dim3((q_items + 7) / 8 * 8), dim3(128 * kBwdTok), 0, s,
+                     a.q_idx, a.k_idx, a.w, a.g, a.ld, a.seq_off, a.row_begin, a.row_end, a.grad_row0, a.dq, a.dw,
+                     key_split, n_rowblk, q_items, accumulate);
 
   // dk: key blocks x token groups.
-  const int n_keyblk = (nkeys + 32 * kBwdKeyW - 1) / (32 * kBwdKeyW);
+  const int n_keyblk = (nkeys + 16 * kBwdKeyT * kBwdKeyW - 1) / (16 * kBwdKeyT * kBwdKeyW);
   const int n_tg = (rows + kBwdTokGroup - 1) / kBwdTokGroup;
   const int k_items = n_keyblk * n_tg;
-  hipLaunchKernelGGL((indexer_bwd_k_kernel<kBwdKeyW, kBwdStages>), dim3((k_items + 7) / 8 * 8), dim3(64 * kBwdKeyW), 0, s,
-                     a.q_idx, (const uint16_t*)a.workspace, a.k_idx, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
+  hipLaunchKernelGGL((indexer_bwd_k_kernel<kBwdKeyW, kBwdKeyT, kBwdStages>), dim3((k_items + 7) / 8 * 8), dim3(64 * kBwdKeyW), 0, s,
+                     a.q_idx, a.w, a.k_idx, a.g, a.ld, a.seq_off, a.row_begin, a.row_end,
                      a.grad_row0, a.dk, kBwdTokGroup, n_keyblk, k_items);
   return hipGetLastError();
 }

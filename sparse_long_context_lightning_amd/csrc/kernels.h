@@ -90,21 +90,18 @@ struct SparseAttnBwdArgs {
 
 // Backward of the indexer scores for packed rows [row_begin, row_end) of one sequence starting at
 // packed row seq_off (64 heads x 128 only).  g[(r - grad_row0) * ld + s] is the gradient of
-// I[r, s]; dq / dw of the rows are written, dk of the sequence's keys accumulated.  workspace
-// holds ws_rows transposed query tiles (row grad_row0 first), then the key tiles of one sequence.
+// I[r, s]; dq / dw of the rows are written, dk of the sequence's keys accumulated.
 struct IndexerBwdArgs {
   const uint16_t* q_idx;
   const uint16_t* k_idx;
   const float* w;
   const float* g;
   long long ld;
-  int seq_off, row_begin, row_end, grad_row0, ws_rows;
-  uint16_t* workspace;
+  int seq_off, row_begin, row_end, grad_row0;
   float* dq;
   float* dw;
   float* dk;
 };
-size_t indexer_bwd_workspace_bytes(int rows, int max_keys);
 
 // Head-mean causal attention distribution of packed rows [row_begin, row_end) of one sequence
 // starting at packed row seq_off: probs[(r - out_row0) * ld + s] for s <= r - seq_off, and the

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -150,25 +150,18 @@ def test_topk_rejects_short_workspace():
 def test_index_scores_bwd_validation():
     lib = dsa.load()
     cu_arr, cu_p = _cu([0, 100, 300])
-    need = dsa.dsa_index_scores_bwd_workspace_size(300, 64, 128, 50)
-    # 50 transposed query tiles (16 KiB each), then key tiles for up to 300 keys (5 tiles)
-    assert need == 50 * 16384 + 5 * 16384
 
     def call(**over):
         a = dict(q=FAKE, k=FAKE, w=FAKE, cu=cu_p, batch=2, total=300, h=64, d=128, r0=80, rows=50, g=FAKE, ld=200,
-                 dq=FAKE, dw=FAKE, dk=FAKE, ws=FAKE, ws_bytes=need, stream=None)
+                 dq=FAKE, dw=FAKE, dk=FAKE, stream=None)
         a.update(over)
         return lib.dsa_index_scores_bwd(*a.values())
 
-    # the call itself needs key tiles for its longest sequence only (200 keys: 4 tiles)
-    assert call(ws_bytes=50 * 16384 + 4 * 16384 - 1) == dsa.DSA_ERR_WORKSPACE
-    assert call(ws=None) == dsa.DSA_ERR_WORKSPACE
     assert call(h=4, d=64) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(h=32, d=128) == dsa.DSA_ERR_UNSUPPORTED
     assert call(ld=198) == dsa.DSA_ERR_INVALID_ARG      # not a multiple of 4
     assert call(ld=28) == dsa.DSA_ERR_INVALID_ARG       # shorter than row 129's prefix (30)
     assert call(rows=300) == dsa.DSA_ERR_INVALID_ARG    # past total_tokens
     assert call(dq=MISALIGNED) == dsa.DSA_ERR_INVALID_ARG
     assert call(dk=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(rows=0) == dsa.DSA_OK
-    with pytest.raises(dsa.DsaError):
-        dsa.dsa_index_scores_bwd_workspace_size(300, 32, 128, 50)

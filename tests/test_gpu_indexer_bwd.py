@@ -2,8 +2,8 @@
 index_scores_row_grad.  GPU only.
 
 Tolerance, from the arithmetic: the ReLU mask [c > 0] is exact on both sides (the integer
-indexer inputs make c exact in fp32), w q_idx is exact in bf16 (power-of-two w), and the one
-rounding is g [c > 0] to bf16 (relative 2^-9 per term) ahead of fp32 accumulation.  So each
+indexer inputs make c exact in fp32), and the one rounding is g [c > 0] (for dk_idx
+g w [c > 0], w a power of two) to bf16 (relative 2^-9 per term) ahead of fp32 accumulation.  So each
 output differs from the float64 oracle by at most 2^-9 times the sum of the absolute values of
 its terms, plus fp32 accumulation error; the tests allow 2^-8 times that sum, computed here
 from the same inputs with every factor replaced by its absolute value."""
