@@ -18,6 +18,14 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
+// Start value of a running max: below every logit the kernel meets (|scale * <q, k>| of bf16
+// inputs is far smaller), yet finite, so differences against it never form inf - inf.
+constexpr float kNoLogit = -1.0e30f;
+
+// 2^x on the hardware exp2 (results below 2^-126 flush to zero, which no softmax sum here
+// notices: every sum holds a term equal to 1).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Head-mean target, two passes over the causal keys of a workgroup of 4 waves, each wave a
 // block of 16 / G consecutive query tokens: the block's 16 (token, head) rows of one KV group
 // sit on the MFMA row axis and 16 keys of that group on the column axis (16x16x32 bf16).  Key
@@ -25,22 +33,25 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // per position at 4 KV heads); they are DMA'd global->LDS, double buffered and shared by the 4
 // waves, with 16-byte piece c of position p stored at slot c ^ (p mod 16) (conflict-free B
 // reads).  PASS 1 keeps a lane-local online (max, sum) per row over the keys the lane sees and
-// merges the 16 lanes of each row at the end: lse per (token, head).  PASS 2 recomputes the
+// merges the 16 lanes of each row at the end: lse per (token, head).  Its update takes one exp2
+// per logit: with d = z - m, e = 2^-|d| is both the new term (d <= 0) and the rescale of the old
+// sum (d > 0, then the new term is 1).  PASS 2 recomputes the
 // logits, turns them into probabilities with that lse, sums the token's heads over all groups
 // and writes p_t[s] / Hq.  Needs G = Hq / Hkv >= 4, so each lane's four C rows are one token's.
-template <int PASS, int HKV>
-__global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, float scale_log2, int n_blocks) {
+template <int PASS, int HKV, int NWV>
+__global__ __launch_bounds__(64 * NWV) void attn_head_mean_kernel(HeadMeanArgs a, float scale_log2, int n_blocks) {
   constexpr int ROWB = HKV * 256;            // bytes per key position (all KV groups)
   constexpr int TK = HKV <= 4 ? 32 : 16;     // positions per tile
   constexpr int TILE = TK * ROWB;
-  constexpr int NLD = TILE / 4096;           // 16-byte DMA pieces per thread per tile
+  constexpr int NJOB = TILE / 1024;          // 1 KiB DMA instructions per tile
+  constexpr int NLD = (NJOB + NWV - 1) / NWV;  // of them per wave (the last may be idle)
   __shared__ __attribute__((aligned(16))) unsigned char tiles[2][TILE];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
   const int hq = a.hq, G = hq / HKV, TB = 16 / G;
-  const int blk = blockIdx.x * 4 + wave;
-  const int wg_r0 = a.row_begin + blockIdx.x * 4 * TB;
-  const int wg_last = min(wg_r0 + 4 * TB, a.row_end) - 1;
+  const int blk = blockIdx.x * NWV + wave;
+  const int wg_r0 = a.row_begin + blockIdx.x * NWV * TB;
+  const int wg_last = min(wg_r0 + NWV * TB, a.row_end) - 1;
   const int ntiles = (wg_last - a.seq_off) / TK + 1;
   const bool active = blk < n_blocks;
   const int r0 = a.row_begin + blk * TB;
@@ -65,7 +76,7 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
   for (int g = 0; g < HKV; ++g)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      m_st[g][i] = -INFINITY;
+      m_st[g][i] = kNoLogit;
       l_st[g][i] = 0.f;
       lse2[g][i] = 0.f;
       if (PASS == 2 && c_ok) {
@@ -74,13 +85,14 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
       }
     }
 
-  // DMA mapping: instruction p of wave w fills LDS bytes [p*4096 + w*1024, +1024); lane l's 16
-  // bytes land at row (position pos, group g), slot l % 16, which holds piece (l % 16) ^ (pos % 16).
+  // DMA mapping: instruction p of wave w (job P = p * NWV + w) fills LDS bytes [P*1024, +1024);
+  // lane l's 16 bytes land at row (position pos, group g), slot l % 16, which holds piece
+  // (l % 16) ^ (pos % 16).
   const uint16_t* kseq = a.k + (size_t)a.seq_off * HKV * 128;
   int st_pos[NLD], st_off[NLD];
 #pragma unroll
   for (int p = 0; p < NLD; ++p) {
-    const int byte = p * 4096 + wave * 1024 + lane * 16;
+    const int byte = min(p * NWV + wave, NJOB - 1) * 1024 + lane * 16;
     const int pos = byte / ROWB;
     const int g = (byte % ROWB) / 256;
     const int piece = (lane & 15) ^ (pos & 15);
@@ -91,8 +103,9 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
   auto load_tile = [&](int tile, int buf) {
 #pragma unroll
     for (int p = 0; p < NLD; ++p) {
+      if (NJOB % NWV != 0 && p * NWV + wave >= NJOB) break;
       const int pos = min(tile * TK + st_pos[p], kv_len - 1);
-      lds_dma16(kseq + (size_t)pos * HKV * 128 + st_off[p], &tiles[buf][p * 4096 + wave * 1024]);
+      lds_dma16(kseq + (size_t)pos * HKV * 128 + st_off[p], &tiles[buf][(p * NWV + wave) * 1024]);
     }
   };
 
@@ -122,13 +135,14 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
           for (int i = 0; i < 4; ++i) {
             const float z = c[i] * scale_log2;
             if (PASS == 1) {
-              if (kv) {
-                const float mn = fmaxf(m_st[g][i], z);
-                l_st[g][i] = l_st[g][i] * exp2f(m_st[g][i] - mn) + exp2f(z - mn);
-                m_st[g][i] = mn;
-              }
+              // masked keys enter as a logit far below any real one: e = 0, no update of m
+              const float d = (kv ? z : 2.f * kNoLogit) - m_st[g][i];
+              const float e = fast_exp2(-fabsf(d));
+              const bool up = d > 0.f;
+              l_st[g][i] = up ? fmaf(l_st[g][i], e, 1.f) : l_st[g][i] + e;
+              m_st[g][i] = up ? z : m_st[g][i];
             } else {
-              tok_sum += kv ? exp2f(z - lse2[g][i]) : 0.f;
+              tok_sum += kv ? fast_exp2(z - lse2[g][i]) : 0.f;
             }
           }
         }
@@ -155,7 +169,7 @@ __global__ __launch_bounds__(256) void attn_head_mean_kernel(HeadMeanArgs a, flo
         for (int o = 1; o < 16; o <<= 1) {
           const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
           const float mn = fmaxf(m, mo);
-          l = (mn == -INFINITY) ? 0.f : l * exp2f(m - mn) + lo * exp2f(mo - mn);
+          l = l * fast_exp2(m - mn) + lo * fast_exp2(mo - mn);
           m = mn;
         }
         if (n == 0 && c_ok) {
@@ -214,16 +228,21 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(const float* scores, co
   if (threadIdx.x == 0) row_loss[row] = loss;
 }
 
+// Waves (token blocks) per head-mean workgroup, all sharing its staged key tiles.
+constexpr int kHeadMeanWaves = 4;
+
 template <int HKV>
 hipError_t launch_head_mean_t(const HeadMeanArgs& a, hipStream_t s) {
   const int G = a.hq / HKV;
   const int TB = 16 / G;
   const int rows = a.row_end - a.row_begin;
   const int n_blocks = (rows + TB - 1) / TB;
-  const unsigned grid = (unsigned)((n_blocks + 3) / 4);
+  const unsigned grid = (unsigned)((n_blocks + kHeadMeanWaves - 1) / kHeadMeanWaves);
   const float scale_log2 = a.softmax_scale * kLog2e;
-  hipLaunchKernelGGL((attn_head_mean_kernel<1, HKV>), dim3(grid), dim3(256), 0, s, a, scale_log2, n_blocks);
-  hipLaunchKernelGGL((attn_head_mean_kernel<2, HKV>), dim3(grid), dim3(256), 0, s, a, scale_log2, n_blocks);
+  hipLaunchKernelGGL((attn_head_mean_kernel<1, HKV, kHeadMeanWaves>), dim3(grid), dim3(64 * kHeadMeanWaves), 0, s, a,
+                     scale_log2, n_blocks);
+  hipLaunchKernelGGL((attn_head_mean_kernel<2, HKV, kHeadMeanWaves>), dim3(grid), dim3(64 * kHeadMeanWaves), 0, s, a,
+                     scale_log2, n_blocks);
   return hipGetLastError();
 }
 
