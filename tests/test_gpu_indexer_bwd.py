@@ -127,3 +127,52 @@ def test_indexer_bwd_leaves_other_rows_untouched(dsa):
     _check("dq", dq, wq, bq, rows=np.r_[120:220])
     _check("dw", dw, ww, bw, rows=np.r_[120:220])
     _check("dk", dk, wk, bk)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_indexer_bwd_full_32k_chunked(dsa):
+    """The 32K prefill in the benchmark's launch configuration (16 calls of 2048 rows, dk_I
+    accumulated over them): dq_I and dw on sampled rows recomputed by the oracle one by one, and
+    dk_I of the last 16 keys, which only the last 16 rows reach, recomputed from those rows."""
+    import torch
+    pi = inp.workload("c2_prefill_32k")
+    total = int(pi.cu_seqlens[-1])
+    dev = tl.upload_prefill(pi)
+    rng = np.random.default_rng(31)
+    chunk = 2048
+    # Seeded gradient rows N(0, 1)/(t+1) on each prefix, generated per chunk on the host.
+    dq = torch.full((total, H, DI), float("nan"), dtype=torch.float32, device="cuda")
+    dw = torch.full((total, H), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((total, DI), dtype=torch.float32, device="cuda")
+    g_rows = {}
+    check = [0, 1, 2047, 2048, 9000, 20001, total - 17, total - 1] + list(range(total - 16, total))
+    buf = np.zeros((chunk, total), dtype=np.float32)
+    for c0 in range(0, total, chunk):
+        n = min(chunk, total - c0)
+        buf[:] = 0.0
+        for i in range(n):
+            t = c0 + i
+            buf[i, :t + 1] = (rng.standard_normal(t + 1) / (t + 1)).astype(np.float32)
+            if t in check:
+                g_rows[t] = buf[i, :t + 1].astype(np.float64).copy()
+        g_t = torch.from_numpy(buf[:n]).cuda()
+        dsa.dsa_index_scores_bwd(dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, c0, n, g_t, dq, dw, dk)
+    torch.cuda.synchronize()
+    q, k, w = tl.f64(pi.q_idx), tl.f64(pi.k_idx), pi.w.astype(np.float64)
+    got_q, got_w, got_k = dq.cpu().numpy(), dw.cpu().numpy(), dk.cpu().numpy()
+    want_k = np.zeros((16, DI))
+    bound_k = np.zeros((16, DI))
+    for t in sorted(set(check)):
+        kp = k[:t + 1]
+        gq, gw, gk = orc.index_scores_row_grad(q[t], w[t], kp, g_rows[t])
+        m = (q[t] @ kp.T) > 0
+        ag = np.abs(g_rows[t])[None, :] * m
+        ua = ag @ np.abs(kp)
+        _check(f"dq row {t}", got_q[t][None], gq[None], (np.abs(w[t])[:, None] * ua)[None])
+        _check(f"dw row {t}", got_w[t][None], gw[None], np.sum(np.abs(q[t]) * ua, axis=1)[None])
+        if t >= total - 16:
+            s0 = total - 16          # row t reaches keys s0 .. t
+            want_k[:t + 1 - s0] += gk[s0:]
+            bound_k[:t + 1 - s0] += (ag.T @ (np.abs(w[t])[:, None] * np.abs(q[t])))[s0:]
+    _check("dk last 16 keys", got_k[total - 16:], want_k, bound_k)

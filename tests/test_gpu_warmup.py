@@ -88,3 +88,27 @@ def test_indexer_kl_matches_oracle(dsa):
         assert abs(got_l[i] - want_l) <= 1e-4 * max(1.0, abs(want_l)), (i, got_l[i], want_l)
         np.testing.assert_allclose(got_g[i, :n], want_g, atol=2e-6)
         np.testing.assert_array_equal(got_inplace[i, :n], got_g[i, :n])
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_head_mean_target_full_32k(dsa):
+    """The 32K prefill's target in the benchmark's launch configuration (2048-row windows):
+    sampled rows of the first and the last window recomputed by the oracle one by one."""
+    import torch
+    pi = inp.workload("c2_prefill_32k")
+    total = int(pi.cu_seqlens[-1])
+    hq = pi.q.shape[1]
+    dev = tl.upload_prefill(pi)
+    q, k = tl.f64(pi.q), tl.f64(pi.k)
+    scale = orc.default_softmax_scale(128)
+    chunk = 2048
+    probs = torch.empty(chunk, total, dtype=torch.float32, device="cuda")
+    lse = torch.empty(chunk, hq, dtype=torch.float32, device="cuda")
+    for c0, rows in ((0, [0, 1, 777, 2047]), (total - chunk, [total - chunk, total - 1000, total - 1])):
+        dsa.dsa_attn_head_mean(dev["q"], dev["k"], pi.cu_seqlens, c0, chunk, probs, lse, ld=total)
+        torch.cuda.synchronize()
+        got = probs.cpu().numpy().astype(np.float64)
+        for r in rows:
+            want = orc.attention_head_mean_row(q[r], k[:r + 1], scale)
+            np.testing.assert_allclose(got[r - c0, :r + 1], want, atol=2e-6, rtol=2e-4, err_msg=f"row {r}")
