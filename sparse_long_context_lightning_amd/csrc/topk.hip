@@ -270,48 +270,82 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 // Rank order for the torch.topk-shaped form: one 256-thread workgroup per row reorders the
 // row's selected positions (as the selection kernels leave them, ascending) by descending
 // score, equal scores by ascending position.  Each entry becomes the 64-bit word
-// (~key << 32) | position, so one ascending bitonic sort over the next power of two >= k gives
-// that order; padding (-1) sorts last as all-ones.
+// (~key << 32) | position, so one ascending bitonic sort of 2048 words gives that order;
+// padding (-1, and the slots past k) sorts last as all-ones.  Thread t holds words 8t .. 8t+7
+// in registers: compare-exchange distances below 8 stay inside a thread, 8 .. 256 are lane
+// exchanges inside the wave, and only 512 and 1024 go through LDS (3 of the 66 stages).
 constexpr int kRankMax = 2048;
+constexpr int kRankPer = kRankMax / 256;
+
+__device__ __forceinline__ void rank_cas(unsigned long long& a, unsigned long long& b, bool up) {
+  const bool sw = (a > b) == up;
+  const unsigned long long lo = sw ? b : a, hi = sw ? a : b;
+  a = lo;
+  b = hi;
+}
 
 __global__ __launch_bounds__(256) void topk_rank_kernel(const float* __restrict__ scores, long long ld, int k,
                                                        int* __restrict__ idx_out, float* __restrict__ values_out) {
   __shared__ unsigned long long w[kRankMax];
   const int row = blockIdx.x;
-  const int tid = threadIdx.x;
-  int np2 = 1;
-  while (np2 < k) np2 <<= 1;
+  const int tid = threadIdx.x, lane = tid & 63;
   int* out = idx_out + (size_t)row * k;
   const float* src = scores + (size_t)row * ld;
-  for (int i = tid; i < np2; i += 256) {
+  unsigned long long e[kRankPer];
+#pragma unroll
+  for (int j = 0; j < kRankPer; ++j) {
+    const int i = kRankPer * tid + j;
     unsigned long long c = ~0ull;
     if (i < k) {
       const int p = out[i];
       if (p >= 0) c = ((unsigned long long)(~float_key(src[p])) << 32) | (uint32_t)p;
     }
-    w[i] = c;
+    e[j] = c;
   }
-  __syncthreads();
-  for (int size = 2; size <= np2; size <<= 1) {
+#pragma unroll
+  for (int size = 2; size <= kRankMax; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < (np2 >> 1); i += 256) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const unsigned long long a = w[lo], b = w[hi];
-        const bool up = (lo & size) == 0;
-        if ((a > b) == up) {
-          w[lo] = b;
-          w[hi] = a;
+      if (stride >= 64 * kRankPer) {
+        // partner in another wave: through LDS
+#pragma unroll
+        for (int j = 0; j < kRankPer; ++j) w[kRankPer * tid + j] = e[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kRankPer; ++j) {
+          const int i = kRankPer * tid + j;
+          const unsigned long long o = w[i ^ stride];
+          const bool keep_min = ((i & stride) == 0) == ((i & size) == 0);
+          e[j] = keep_min ? (o < e[j] ? o : e[j]) : (o > e[j] ? o : e[j]);
         }
+        __syncthreads();
+      } else if (stride >= kRankPer) {
+        // partner in another lane of this wave (same slot j)
+        const int ls = stride / kRankPer;
+        const bool lower = (lane & ls) == 0;
+#pragma unroll
+        for (int j = 0; j < kRankPer; ++j) {
+          const int i = kRankPer * tid + j;
+          const unsigned long long o = __shfl_xor(e[j], ls);
+          const bool keep_min = lower == ((i & size) == 0);
+          e[j] = keep_min ? (o < e[j] ? o : e[j]) : (o > e[j] ? o : e[j]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kRankPer; ++j)
+          if ((j & stride) == 0) rank_cas(e[j], e[j | stride], ((kRankPer * tid + j) & size) == 0);
       }
-      __syncthreads();
     }
   }
-  for (int i = tid; i < k; i += 256) {
-    const unsigned long long c = w[i];
-    const bool pad = c == ~0ull;
-    out[i] = pad ? -1 : (int)(uint32_t)c;
-    if (values_out) values_out[(size_t)row * k + i] = pad ? -INFINITY : key_float(~(uint32_t)(c >> 32));
+#pragma unroll
+  for (int j = 0; j < kRankPer; ++j) {
+    const int i = kRankPer * tid + j;
+    if (i < k) {
+      const unsigned long long c = e[j];
+      const bool pad = c == ~0ull;
+      out[i] = pad ? -1 : (int)(uint32_t)c;
+      if (values_out) values_out[(size_t)row * k + i] = pad ? -INFINITY : key_float(~(uint32_t)(c >> 32));
+    }
   }
 }
 
