@@ -487,8 +487,8 @@ def cpu_baseline(args, pi, tl):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (this build has no "
-              f"multi-GPU path)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the library has no "
+              f"multi-GPU path; the sharding it would take is described in the design notes)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()

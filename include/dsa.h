@@ -30,7 +30,7 @@
  *     Inputs must stay unchanged until then.  Calls on different streams are independent.
  *   - Arguments are validated on the host before anything is enqueued; on any error nothing
  *     runs.  Errors: DSA_ERR_INVALID_ARG (null pointer, negative size, inconsistent
- *     cu_seqlens, misaligned pointer), DSA_ERR_UNSUPPORTED (a shape this build has no kernel
+ *     cu_seqlens, misaligned pointer), DSA_ERR_UNSUPPORTED (a shape the library has no kernel
  *     for), DSA_ERR_WORKSPACE (workspace too small), DSA_ERR_HIP (a launch failed; the HIP
  *     error text is in dsa_last_error()).  Faults inside kernels are only visible at the next
  *     synchronisation of the stream.
