@@ -40,11 +40,20 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, floa
   const long long item = (long long)wg * 4 + wave;
   const long long n_items = (long long)a.rows * a.nsplit * a.hkv;
   if (item >= n_items) return;
-  // KV group slowest: all rows of group g run before group g+1, so the gathered K/V rows of
-  // one group (a quarter of the cache at 4 KV heads) stay resident in the last-level cache.
+  // Prefill: KV group slowest, so all rows of group g run before group g+1 and the gathered K/V
+  // rows of one group (a quarter of the cache at 4 KV heads) stay resident in the last-level
+  // cache.  Decode (each cache read by one query): KV group fastest, so the waves of a workgroup
+  // gather the groups of the same positions, one contiguous KiB per position between them.
   const long long per_group = (long long)a.rows * a.nsplit;
-  const int g = (int)(item / per_group);
-  const long long tmp = item - (long long)g * per_group;
+  int g;
+  long long tmp;
+  if (a.seq_lens) {
+    g = (int)(item % a.hkv);
+    tmp = item / a.hkv;
+  } else {
+    g = (int)(item / per_group);
+    tmp = item - (long long)g * per_group;
+  }
   const int sp = (int)(tmp % a.nsplit);
   const int row = (int)(tmp / a.nsplit);
   unsigned char* vlds = vlds_all[wave];
