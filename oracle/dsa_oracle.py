@@ -37,6 +37,8 @@ listed in the design notes):
       includes the scale
   R11 positions are sequence-local; no attention across packed sequences
   R12 a decode cache of length n holds the new token at position n-1
+  R25 adjacent-query dedup: blocks of 16 consecutive packed rows; the union is over packed KV
+      rows, each row keeps its own distinct valid positions through a 16-bit mask
 
 Everything is float64.  Loops run per query row so that each step reads like its
 definition; speed is not a goal.
@@ -56,6 +58,8 @@ __all__ = [
     "prefill",
     "decode",
     "default_softmax_scale",
+    "adjacent_query_union",
+    "sparse_gqa_attention_union",
 ]
 
 
@@ -326,6 +330,67 @@ def _seq_of_row(cu: list, r: int) -> int:
         if cu[b] <= r < cu[b + 1]:
             return b
     raise IndexError(r)
+
+
+def adjacent_query_union(idx, cu_seqlens, block_rows=16, blocks=None):
+    """Merged index sets of neighbouring query rows (source A, section 八: adjacent queries
+    choose largely the same positions, so their top-k sets are de-duplicated and every KV row
+    of the merged set is fetched once; a mask keeps each query to its own positions).
+
+    Reading R25: block b holds the packed rows block_rows*b .. block_rows*b + block_rows - 1
+    (the last block may be shorter, and a block may span two sequences).  Entry p of row r,
+    whose sequence starts at packed row o and whose local position is t = r - o, counts when
+    0 <= p <= t and stands for the packed KV row o + p.  The block's union is the set of those
+    KV rows in ascending order; bit j of a KV row's mask is set when row block_rows*b + j
+    selected it.  A position listed twice by one row appears once.
+
+    idx [total_rows, k] (any integers), cu_seqlens [B+1].
+    Returns one (kv_rows int64 [U], masks int64 [U]) pair per block in `blocks` (all if None).
+    """
+    cu = [int(x) for x in cu_seqlens]
+    total = cu[-1]
+    n_blocks = (total + block_rows - 1) // block_rows
+    blocks = range(n_blocks) if blocks is None else [int(b) for b in blocks]
+    result = []
+    for b in blocks:
+        mask_of = {}
+        for j in range(block_rows):
+            r = b * block_rows + j
+            if r >= total:
+                break
+            s = _seq_of_row(cu, r)
+            t = r - cu[s]
+            for p in idx[r]:
+                p = int(p)
+                if 0 <= p <= t:
+                    kv = cu[s] + p
+                    mask_of[kv] = mask_of.get(kv, 0) | (1 << j)
+        kv_rows = sorted(mask_of)
+        result.append((np.asarray(kv_rows, dtype=np.int64),
+                       np.asarray([mask_of[x] for x in kv_rows], dtype=np.int64)))
+    return result
+
+
+def sparse_gqa_attention_union(q, k, v, kv_rows, masks, first_row, n_rows, softmax_scale):
+    """Attention of the rows first_row .. first_row + n_rows - 1 of one block computed from the
+    block's merged set (reading R25): row first_row + j attends over the packed KV rows whose
+    mask has bit j, with the softmax and GQA sharing of sparse_gqa_attention_row.
+
+    q [T, Hq, D], k / v [T, Hkv, D] over all packed rows; kv_rows, masks from
+    adjacent_query_union.  Returns (O [n_rows, Hq, D], lse [n_rows, Hq]) in float64.
+    """
+    hq, d = q.shape[1], q.shape[2]
+    out = np.zeros((n_rows, hq, d), dtype=np.float64)
+    lse = np.zeros((n_rows, hq), dtype=np.float64)
+    kv_rows = np.asarray(kv_rows, dtype=np.int64)
+    masks = np.asarray(masks, dtype=np.int64)
+    for j in range(n_rows):
+        mine = kv_rows[((masks >> j) & 1) == 1]
+        # The selected rows are addressed directly in the packed K / V (local position = the
+        # packed row itself when the "sequence" starts at row 0).
+        o, l, _ = sparse_gqa_attention_row(q[first_row + j], k, v, mine, softmax_scale)
+        out[j], lse[j] = o, l
+    return out, lse
 
 
 def prefill(q, k, v, q_idx, k_idx, w, cu_seqlens, top_k, softmax_scale=None, rows=None):

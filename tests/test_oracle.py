@@ -279,6 +279,93 @@ def test_attention_index_order_is_irrelevant():
     np.testing.assert_allclose(a[0], b[0], atol=1e-13)
 
 
+# ---------------------------------------------------------------- adjacent-query dedup
+
+def test_union_hand_worked_example():
+    g = _load("dedup_worked_example.json")
+    got = orc.adjacent_query_union(np.array(g["idx"]), g["cu_seqlens"], block_rows=g["block_rows"])
+    assert len(got) == len(g["blocks"])
+    for (kv, m), want in zip(got, g["blocks"]):
+        assert kv.tolist() == want["kv_rows"]
+        assert m.tolist() == want["masks"]
+
+
+def _random_index_lists(rng, cu, k, p_bad=0.1):
+    """Index lists with repeats, negative entries and entries past the causal prefix."""
+    total = cu[-1]
+    idx = np.empty((total, k), dtype=np.int64)
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            row = rng.integers(0, t + 1, size=k)
+            bad = rng.random(k) < p_bad
+            row[bad] = rng.choice([-1, -7, t + 1, t + 40], size=int(bad.sum()))
+            idx[cu[b] + t] = row
+    return idx
+
+
+@pytest.mark.parametrize("block_rows", [16, 5])
+def test_union_masks_rebuild_every_rows_distinct_valid_set(block_rows):
+    rng = np.random.default_rng(61)
+    cu = [0, 37, 38, 90]
+    idx = _random_index_lists(rng, cu, 12)
+    blocks = orc.adjacent_query_union(idx, cu, block_rows=block_rows)
+    assert len(blocks) == (cu[-1] + block_rows - 1) // block_rows
+    for b, (kv, m) in enumerate(blocks):
+        assert np.all(np.diff(kv) > 0) and np.all(m > 0) and np.all(m < (1 << block_rows))
+        for j in range(block_rows):
+            r = b * block_rows + j
+            mine = set(kv[((m >> j) & 1) == 1].tolist())
+            if r >= cu[-1]:
+                assert not mine
+                continue
+            s = max(i for i in range(len(cu) - 1) if cu[i] <= r)
+            t = r - cu[s]
+            assert mine == {cu[s] + int(p) for p in idx[r] if 0 <= p <= t}, (b, j)
+        want = np.unique(np.concatenate([kv[((m >> j) & 1) == 1] for j in range(block_rows)] + [kv[:0]]))
+        assert np.array_equal(kv, want)
+
+
+def test_union_size_matches_independent_inclusion_probability():
+    # Rows that draw k distinct positions uniformly from their prefixes [0, t_j] include a given
+    # position s with probability k / (t_j + 1), independently of each other, so the expected
+    # union size of a block is sum_s (1 - prod_j (1 - [s <= t_j] k / (t_j + 1))).
+    rng = np.random.default_rng(62)
+    t0, n_blocks, k = 600, 40, 64
+    total = t0 + 16 * n_blocks
+    idx = np.full((total, k), -1, dtype=np.int64)
+    for t in range(t0, total):
+        idx[t] = rng.choice(t + 1, size=k, replace=False)
+    blocks = orc.adjacent_query_union(idx, [0, total], blocks=range(t0 // 16 + 1, total // 16))
+    got = np.mean([len(kv) for kv, _ in blocks])
+    want = []
+    for b in range(t0 // 16 + 1, total // 16):
+        ts = np.arange(16 * b, 16 * b + 16)
+        s = np.arange(ts[-1] + 1)[:, None]
+        miss = np.where(s <= ts[None, :], 1.0 - k / (ts[None, :] + 1.0), 1.0)
+        want.append(float(np.sum(1.0 - np.prod(miss, axis=1))))
+    want = float(np.mean(want))
+    assert abs(got - want) < 0.01 * want, (got, want)
+
+
+def test_union_attention_equals_per_row_attention_over_distinct_positions():
+    hq, hkv, d = 4, 2, 8
+    cu = [0, 21, 40]
+    rng = np.random.default_rng(63)
+    q, k, v = _rand_attn(64, cu[-1], hq, hkv, d)
+    idx = _random_index_lists(rng, cu, 6)
+    for b, (kv, m) in enumerate(orc.adjacent_query_union(idx, cu, block_rows=8)):
+        n = min(8, cu[-1] - 8 * b)
+        o, lse = orc.sparse_gqa_attention_union(q, k, v, kv, m, 8 * b, n, 0.3)
+        for j in range(n):
+            r = 8 * b + j
+            s = 0 if r < cu[1] else 1
+            t = r - cu[s]
+            sel = np.unique([p for p in idx[r] if 0 <= p <= t]).astype(np.int64)
+            o_ref, l_ref, _ = orc.sparse_gqa_attention_row(q[r], k[cu[s]:cu[s + 1]], v[cu[s]:cu[s + 1]], sel, 0.3)
+            np.testing.assert_allclose(o[j], o_ref, atol=1e-13)
+            np.testing.assert_allclose(lse[j], l_ref, atol=1e-13)
+
+
 # ---------------------------------------------------------------- composition
 
 # ---------------------------------------------------------------- sparse attention backward
