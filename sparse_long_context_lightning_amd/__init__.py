@@ -26,8 +26,11 @@ from ._lib import (  # noqa: F401
     dsa_last_error,
     dsa_prefill,
     dsa_prefill_workspace_size,
+    dsa_query_union,
+    dsa_query_union_size,
     dsa_sparse_gqa_attn,
     dsa_sparse_gqa_attn_bwd,
+    dsa_sparse_gqa_attn_union,
     dsa_status_string,
     dsa_topk,
     dsa_topk_sorted,

@@ -70,4 +70,26 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
 }
 
+// The same copies issued from inline assembly, which the compiler does not track.  Its
+// wait-count pass cannot tell which LDS bytes a tracked copy writes, so before an LDS read that
+// might overlap (any transposed read, for one) it waits for every copy in flight, including the
+// ring stages issued ahead of the read.  With these forms the caller alone orders the copies and
+// its LDS reads, with s_waitcnt vmcnt and a barrier.  M0 carries the LDS base (wave-uniform).
+// M0 is listed as clobbered (the compiler reserves it and warns; it sets M0 itself right before
+// each instruction of its own that reads it).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_offset(const void* lds_ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_ptr;
+}
+__device__ __forceinline__ void lds_dma16_untracked(const void* g, void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_untracked(const void* g, void* lds_wave_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace dsa

@@ -394,6 +394,89 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
   return hip_status(dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
 }
 
+int dsa_query_union_size(int total_tokens, int k_sel, int* n_blocks, int* cap) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(n_blocks);
+  DSA_NONNULL(cap);
+  if (total_tokens < 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens >= 0 and k_sel > 0 required");
+  if (k_sel > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "k_sel %d too large", k_sel);
+  *n_blocks = (total_tokens + dsa::kQueryBlock - 1) / dsa::kQueryBlock;
+  *cap = (int)round_up((long long)dsa::kQueryBlock * k_sel, dsa::kUnionChunk);
+  return DSA_OK;
+}
+
+int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens, int cap,
+                    int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(idx);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(counts);
+  DSA_NONNULL(kv_rows);
+  DSA_NONNULL(masks);
+  DSA_ALIGNED(kv_rows);
+  if (reinterpret_cast<uintptr_t>(masks) & 3u) return fail(DSA_ERR_INVALID_ARG, "masks must be 4-byte aligned");
+  if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
+  int n_blocks = 0, need = 0;
+  DSA_TRY(dsa_query_union_size(total_tokens, k_sel, &n_blocks, &need));
+  if (cap < need || cap % dsa::kUnionChunk != 0)
+    return fail(DSA_ERR_INVALID_ARG, "cap %d must be a multiple of %d and >= %d", cap, dsa::kUnionChunk, need);
+  if (total_tokens == 0) return DSA_OK;
+  dsa::QueryUnionArgs a = {};
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.rows = total_tokens;
+  a.block_begin = 0;
+  a.block_end = n_blocks;
+  a.cap = cap;
+  a.counts = counts;
+  a.kv_rows = kv_rows;
+  a.masks = masks;
+  return hip_status(dsa::launch_query_union(a, static_cast<hipStream_t>(stream)), "query union launch");
+}
+
+int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const int32_t* counts,
+                              const int32_t* kv_rows, const uint16_t* masks, int cap, int total_tokens, int hq,
+                              int hkv, int head_dim, float softmax_scale, void* out, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(counts);
+  DSA_NONNULL(kv_rows);
+  DSA_NONNULL(masks);
+  DSA_NONNULL(out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(kv_rows);
+  if (reinterpret_cast<uintptr_t>(masks) & 3u) return fail(DSA_ERR_INVALID_ARG, "masks must be 4-byte aligned");
+  if (total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (cap <= 0 || cap % dsa::kUnionChunk != 0)
+    return fail(DSA_ERR_INVALID_ARG, "cap %d must be a positive multiple of %d", cap, dsa::kUnionChunk);
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  if (!dsa::union_attn_supported(hq, hkv))
+    return fail(DSA_ERR_UNSUPPORTED, "merged-set attention supports hq / hkv in {4, 8, 16} (got %d)", hq / hkv);
+  if (total_tokens == 0) return DSA_OK;
+  dsa::UnionAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.counts = counts;
+  a.kv_rows = kv_rows;
+  a.masks = masks;
+  a.cap = cap;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  return hip_status(dsa::launch_sparse_attn_union(a, static_cast<hipStream_t>(stream)), "merged-set attention launch");
+}
+
 int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                             const void* dout, const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch,
                             int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, float* dq,

@@ -117,6 +117,43 @@ struct HeadMeanArgs {
   long long ld;
 };
 
+// Adjacent-query dedup.  Block b = packed rows kQueryBlock * b .. + kQueryBlock - 1 (the last
+// one may be shorter).  Its merged list has counts[b] entries at kv_rows / masks + b * cap:
+// packed KV rows in ascending order and 16-bit masks (bit j: row kQueryBlock * b + j selected
+// the KV row), padded with mask-0 entries to a multiple of kUnionChunk.  cap must be a multiple
+// of kUnionChunk and at least kQueryBlock * k_sel rounded up to one.
+constexpr int kQueryBlock = 16;
+constexpr int kUnionChunk = 32;
+struct QueryUnionArgs {
+  const int* idx;
+  int k_sel;
+  const int* cu_seqlens;
+  int batch;
+  int rows;                     // packed rows in all (for the last, shorter block)
+  int block_begin, block_end;   // blocks built by this launch
+  int cap;
+  int* counts;
+  int* kv_rows;
+  uint16_t* masks;
+};
+struct UnionAttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* counts;
+  const int* kv_rows;
+  const uint16_t* masks;
+  int cap;
+  int rows, hq, hkv;
+  float softmax_scale;
+  uint16_t* out;
+  float* lse;
+};
+hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s);
+// The union attention handles G = hq / hkv in {4, 8, 16}.
+bool union_attn_supported(int hq, int hkv);
+hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s);
+
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
 hipError_t launch_attn_head_mean(const HeadMeanArgs& a, hipStream_t s);
 // Row loss KL(target || softmax(scores)) and grad = softmax(scores) - target (grad may alias

@@ -1,0 +1,428 @@
+// Sparse GQA attention over the merged index sets of adjacent query rows, for gfx950.
+//
+// Neighbouring query tokens select largely the same positions (Keye-VL-2.0 report digest,
+// mqxn.cn news 1966, section 八: the top-k sets of adjacent queries are de-duplicated and the
+// attention kernel masks inside its matrix tiles), so the sets of 16 consecutive packed rows
+// are merged, every KV row of the merged set is fetched once for all 16 rows, and a 16-bit
+// mask per merged position keeps each row to its own positions.
+//
+// query_union_kernel: one workgroup per block of 16 rows.  Entry p of row r (sequence offset
+// o, local position t) counts when 0 <= p <= t and names packed KV row o + p; bit j (row j of
+// the block) is OR-ed into a 16-bit-per-position bitmap in LDS, one window of 32768 KV rows
+// at a time, and each window is compacted in ascending order with ballots.  The list is
+// padded to a multiple of 32 entries with (the block's smallest possible KV row, mask 0).
+//
+// sparse_attn_union_kernel: one workgroup of 4 waves per (block, KV group).  Per chunk of 32
+// merged positions the workgroup DMAs the 32 key rows and 32 value rows of the group into LDS
+// (a 3-stage ring; a chunk's positions and masks are DMA'd two chunks earlier, so the gather
+// addresses are read from LDS), and each wave uses them for its 4 rows x G heads:
+//   * S^T = K Q^T on 16x16x32 bf16 MFMA, keys on rows, (row, head) pairs on columns; with
+//     G = 8 one 16-column tile is two rows' eight heads;
+//   * the lane that holds S^T[key][column] tests the column's row bit in the key's mask and
+//     sets the logit to -inf where the row did not select the key;
+//   * online softmax in base 2 per column, as in the per-row kernel;
+//   * O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16) in the key order
+//     the P^T registers carry.
+#include "common.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kUnionThreads = 256;
+constexpr int kUnionWindow = 32768;  // KV rows per LDS bitmap pass (two 16-bit masks per dword)
+
+__device__ __forceinline__ int seq_of_row(const int* cu, int batch, int r) {
+  int lo = 0, hi = batch;  // largest s with cu[s] <= r
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+}
+
+__global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t bm[kUnionWindow / 2];
+  __shared__ int row_base[kQueryBlock], row_t[kQueryBlock];
+  __shared__ int wave_cnt[kUnionThreads / 64];
+  const int b = a.block_begin + blockIdx.x;
+  const int r0 = b * kQueryBlock;
+  const int nr = min(kQueryBlock, a.rows - r0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < kQueryBlock) {
+    int base = 0, t = -1;
+    if (tid < nr) {
+      base = a.cu_seqlens[seq_of_row(a.cu_seqlens, a.batch, r0 + tid)];
+      t = r0 + tid - base;
+    }
+    row_base[tid] = base;
+    row_t[tid] = t;
+  }
+  __syncthreads();
+  const int b0 = row_base[0];          // no entry of the block names a KV row below this one
+  const int span = r0 + nr - b0;       // KV rows b0 .. r0 + nr - 1
+  int* out_rows = a.kv_rows + (size_t)b * a.cap;
+  uint16_t* out_masks = a.masks + (size_t)b * a.cap;
+  const uint16_t* bm16 = reinterpret_cast<const uint16_t*>(bm);
+  constexpr int kSeg = kUnionWindow / (kUnionThreads / 64);  // positions per wave in a window
+  int total = 0;
+  for (int w0 = 0; w0 < span; w0 += kUnionWindow) {
+    const int lo = b0 + w0;
+    const int limit = min(kUnionWindow, span - w0);
+    for (int i = tid; i < (limit + 7) / 8; i += kUnionThreads) reinterpret_cast<uint4*>(bm)[i] = uint4{0, 0, 0, 0};
+    __syncthreads();
+    for (int j = 0; j < nr; ++j) {
+      const int* ir = a.idx + (size_t)(r0 + j) * a.k_sel;
+      const int off = row_base[j] - lo, t = row_t[j];
+      const uint32_t bit = 1u << j;
+#pragma unroll 4
+      for (int i = tid; i < a.k_sel; i += kUnionThreads) {
+        const int p = ir[i];
+        const int x = off + p;
+        if (p >= 0 && p <= t && x >= 0 && x < limit) atomicOr(&bm[x >> 1], bit << ((x & 1) << 4));
+      }
+    }
+    __syncthreads();
+    const int s_begin = wave * kSeg, s_end = min(s_begin + kSeg, limit);
+    int c = 0;
+    for (int s = s_begin; s < s_end; s += 64) {
+      const int x = s + lane;
+      c += __popcll(__ballot(x < s_end && bm16[x] != 0));
+    }
+    if (lane == 0) wave_cnt[wave] = c;
+    __syncthreads();
+    int pos = total;
+    for (int w = 0; w < wave; ++w) pos += wave_cnt[w];
+    for (int w = 0; w < kUnionThreads / 64; ++w) total += wave_cnt[w];
+    for (int s = s_begin; s < s_end; s += 64) {
+      const int x = s + lane;
+      const uint32_t m = x < s_end ? bm16[x] : 0u;
+      const uint64_t bal = __ballot(m != 0u);
+      if (m != 0u) {
+        const int e = pos + lanes_below(bal);
+        out_rows[e] = lo + x;
+        out_masks[e] = (uint16_t)m;
+      }
+      pos += __popcll(bal);
+    }
+    __syncthreads();  // the next window clears the bitmap and rewrites wave_cnt
+  }
+  const int padded = (total + kUnionChunk - 1) / kUnionChunk * kUnionChunk;
+  for (int e = total + tid; e < padded; e += kUnionThreads) {
+    out_rows[e] = b0;
+    out_masks[e] = 0;
+  }
+  if (tid == 0) a.counts[b] = total;
+}
+
+// ---------------------------------------------------------------------------------------
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLazyMax = 8.f;  // log2 units the softmax offset may lag the largest logit
+constexpr int kRowBytes = 128 * 2;                    // one key or value row of a group
+constexpr int kStageBytes = 2 * kUnionChunk * kRowBytes;  // 32 key rows, then 32 value rows
+constexpr int kStages = 4;                            // chunks in the K/V ring
+constexpr int kMetaBytes = 256;                       // positions (128 B) + masks (64 B) of a chunk
+
+// Chunk rows in LDS: [32 rows][256 B], 16-byte piece c of row r at slot c ^ swz(r).  For
+// r mod 16 = 4a + b, swz = (b << 1) | (a >> 1) | ((a & 1) << 3), a permutation of 0..15: the 16
+// rows one row-wise MFMA operand read touches hit 16 distinct slots, and the transposed reads
+// (rows 4a + 0..3, two neighbouring pieces, two lane groups) do as well.
+__device__ __forceinline__ int swz(int r) {
+  const int a = (r >> 2) & 3, b = r & 3;
+  return (b << 1) | (a >> 1) | ((a & 1) << 3);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// words that lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 address (in that order).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// s_waitcnt vmcnt(N) through the builtin, so the compiler's own wait-count bookkeeping sees it
+// (after vmcnt(0) it knows its earlier loads have landed and adds no wait of its own for them).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // lgkmcnt and expcnt fields at their maximum: no wait
+  asm volatile("" ::: "memory");
+}
+// Wait until at most n of this wave's vector-memory operations are outstanding (the largest
+// listed immediate <= n is used, which only ever waits longer).
+__device__ __forceinline__ void vm_wait_at_most(int n) {
+  if (n >= 15) vm_wait<15>();
+  else if (n >= 12) vm_wait<12>();
+  else if (n >= 10) vm_wait<10>();
+  else if (n >= 8) vm_wait<8>();
+  else if (n >= 6) vm_wait<6>();
+  else if (n >= 5) vm_wait<5>();
+  else if (n >= 4) vm_wait<4>();
+  else if (n >= 3) vm_wait<3>();
+  else if (n >= 2) vm_wait<2>();
+  else if (n >= 1) vm_wait<1>();
+  else vm_wait<0>();
+}
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int G, int NST>
+__global__ __launch_bounds__(256) void sparse_attn_union_kernel(UnionAttnArgs a, float scale_log2, int n_blocks) {
+  constexpr int CT = G / 4;  // 16-column tiles per wave: 4 rows x G heads
+  // A chunk's metadata is DMA'd NST - 1 chunks ahead of its K/V stage, which is issued NST - 1
+  // chunks ahead of its use: 2 NST - 1 chunks of metadata are live at once.
+  constexpr int MS = (2 * NST - 1 <= 8) ? 8 : 16;
+  __shared__ __attribute__((aligned(16))) unsigned char kv_lds[NST][kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char meta_lds[MS][kMetaBytes];
+  // Workgroups are dispatched to the 8 XCDs round-robin; XCD x takes runs of 16 consecutive
+  // items (runs x, x + 8, ...), so neighbouring blocks, whose merged sets overlap, share an L2
+  // while every XCD gets an even share of long and short blocks.  KV group slowest (its
+  // gathered rows stay in the last-level cache); within a group the latest blocks, whose
+  // merged sets are the largest, start first.
+  const int xp = blockIdx.x >> 3;
+  const int wi = ((xp >> 4) * 8 + (blockIdx.x & 7)) * 16 + (xp & 15);
+  if (wi >= n_blocks * a.hkv) return;
+  const int g = wi / n_blocks;
+  const int blk = n_blocks - 1 - (wi - g * n_blocks);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, lg = lane >> 4;
+  const int r0 = blk * kQueryBlock;
+  const int hq = a.hq;
+  const int n_u = min(a.counts[blk], a.cap);
+  const int nchunk = (n_u + kUnionChunk - 1) / kUnionChunk;
+  const int* urows = a.kv_rows + (size_t)blk * a.cap;
+  const uint16_t* umask = a.masks + (size_t)blk * a.cap;
+  const size_t row_stride = (size_t)a.hkv * 128;
+  const uint16_t* kg = a.k + (size_t)g * 128;
+  const uint16_t* vg = a.v + (size_t)g * 128;
+
+  // B operands of S^T: column n of tile T = CT wave + c is block row (16 T + n) / G, head
+  // (16 T + n) % G of group g; rows past the end give zero columns.
+  u32x4 qreg[CT][4];
+  int rbit[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int col = 16 * (CT * wave + c) + n;
+    rbit[c] = col / G;
+    const int row = r0 + rbit[c];
+    const uint16_t* qp = a.q + ((size_t)min(row, a.rows - 1) * hq + g * G + col % G) * 128 + lg * 32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qreg[c][ks] = row < a.rows ? ldg16(qp + ks * 8) : u32x4{0, 0, 0, 0};
+  }
+  const uint32_t wave_rows = 0xFu << (4 * wave);
+
+  f32x4 oacc[8][CT];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) oacc[dt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Running offsets (base-2 logits) and row sums.  The sums are an MFMA accumulator: the A
+  // operand "ones" has bf16 1.0 in row 0 and zeros elsewhere, so C row 0 (element 0 of the
+  // lanes of group 0) collects the column sums of P^T.
+  float m_run[CT];
+  f32x4 lacc[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    m_run[c] = -INFINITY;
+    lacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint32_t one2 = n == 0 ? 0x3F803F80u : 0u;
+  const u32x4 ones = {one2, one2, one2, one2};
+
+  // Positions (dwords 0..31) and masks (dwords 32..47) of chunk ch into meta slot ch % 8.
+  auto meta_dma = [&](int ch) {
+    const void* src = lane < 32 ? (const void*)(urows + ch * kUnionChunk + lane)
+                                : (const void*)(umask + ch * kUnionChunk + 2 * (min(lane, 47) - 32));
+    lds_dma4_untracked(src, meta_lds[ch % MS]);
+  };
+  // Every wave gathers key and value rows 4 wave + lane / 16 and 16 + 4 wave + lane / 16.
+  auto stage = [&](int ch) {
+    const int* pos = reinterpret_cast<const int*>(meta_lds[ch % MS]);
+    const int rr = 4 * wave + (lane >> 4);
+    // Clamped into [0, rows): a foreign list can not make the gather leave K / V.
+    const int p0 = min(max(pos[rr], 0), a.rows - 1), p1 = min(max(pos[16 + rr], 0), a.rows - 1);
+    const int piece = (lane & 15) ^ swz(rr);
+    unsigned char* buf = kv_lds[ch % NST];
+    lds_dma16_untracked(kg + (size_t)p0 * row_stride + piece * 8, buf + (4 * wave) * kRowBytes);
+    lds_dma16_untracked(kg + (size_t)p1 * row_stride + piece * 8, buf + (16 + 4 * wave) * kRowBytes);
+    lds_dma16_untracked(vg + (size_t)p0 * row_stride + piece * 8, buf + (32 + 4 * wave) * kRowBytes);
+    lds_dma16_untracked(vg + (size_t)p1 * row_stride + piece * 8, buf + (48 + 4 * wave) * kRowBytes);
+    if (wave == 0 && ch + NST - 1 < nchunk) meta_dma(ch + NST - 1);
+  };
+  auto stage_ops = [&](int ch) { return 4 + ((wave == 0 && ch + NST - 1 < nchunk) ? 1 : 0); };
+
+  const int trow = 4 * lg + (n >> 2), tm = n & 3, tsw = swz(trow);
+  auto compute = [&](int ch) {
+    const unsigned char* kt = kv_lds[ch % NST];
+    const unsigned char* vt = kt + kUnionChunk * kRowBytes;
+    const unsigned char* meta = meta_lds[ch % MS];
+    // Masks of keys 4 lg + i (lo) and 16 + 4 lg + i (hi), i = 0..3.
+    const uint2 mlo = *reinterpret_cast<const uint2*>(meta + 128 + 8 * lg);
+    const uint2 mhi = *reinterpret_cast<const uint2*>(meta + 128 + 32 + 8 * lg);
+    const uint32_t any = mlo.x | mlo.y | mhi.x | mhi.y;
+    if (__ballot(((any | (any >> 16)) & wave_rows) != 0u) == 0ull) return;  // none of the wave's rows
+    u32x4 ak[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        ak[j][ks] = *reinterpret_cast<const u32x4*>(kt + (16 * j + n) * kRowBytes + (((4 * lg + ks) ^ swz(n)) << 4));
+    // V^T operands: lane j of lane group lg addresses key 4 lg + j / 4 (and 16 + that), dims
+    // 16 dt + 4 (j % 4) .. + 3, so lane n receives dim 16 dt + n of keys 4 lg + 0..3 (16 + ..).
+    u32x4 av[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int piece = 2 * dt + (tm >> 1);
+      const unsigned char* p = vt + trow * kRowBytes + ((piece ^ tsw) << 4) + 8 * (tm & 1);
+      const uint2 lo = lds_read_tr16(p);
+      const uint2 hi = lds_read_tr16(p + 16 * kRowBytes);
+      av[dt] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    }
+    f32x4 s[2][CT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) s[j][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) s[j][c] = mfma16x16x32(ak[j][ks], qreg[c][ks], s[j][c]);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      // Slot e of the lane carries key 16 (e / 4) + 4 lg + e % 4; its mask is 16-bit field
+      // e % 2 of dword mdw[e / 2], and the column's row is bit rbit[c] of a field.
+      const uint32_t mdw[4] = {mlo.x, mlo.y, mhi.x, mhi.y};
+      float mx = s[0][c][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e >> 2][c][e & 3]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // The offset m_run may lag the column's largest selected logit by up to kLazyMax (the
+      // weights then stay below 2^kLazyMax); it is raised, with a rescale, only when the
+      // chunk's largest logit (selected or not, an upper bound) passes that margin.
+      if (__ballot(mx * scale_log2 > m_run[c] + kLazyMax) != 0ull) {
+        float zm = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool sel = (mdw[e >> 1] >> (((e & 1) << 4) + rbit[c])) & 1u;
+          zm = fmaxf(zm, sel ? s[e >> 2][c][e & 3] : -INFINITY);
+        }
+        zm = fmaxf(zm, __shfl_xor(zm, 16));
+        zm = fmaxf(zm, __shfl_xor(zm, 32));
+        const float m_new = fmaxf(m_run[c], zm * scale_log2);
+        const float alpha = m_new > m_run[c] ? __builtin_amdgcn_exp2f(m_run[c] - m_new) : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[dt][c] *= alpha;
+        lacc[c] *= alpha;
+        m_run[c] = m_new;
+      }
+      const float moff = (m_run[c] == -INFINITY) ? 0.f : m_run[c];
+      const int sh = 15 - rbit[c];
+      u32x4 pb;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        // The weights enter the P.V product as bf16.  The row bit of each half is moved to the
+        // half's top bit and sign-extended over the half (v_perm selectors 8 and 9), so the
+        // AND keeps the weights of selected keys and zeroes the rest (an overflowed inf too).
+        const uint32_t w2 = cvt_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[e2 >> 1][c][2 * (e2 & 1)], scale_log2, -moff)),
+                                       __builtin_amdgcn_exp2f(fmaf(s[e2 >> 1][c][2 * (e2 & 1) + 1], scale_log2, -moff)));
+        pb[e2] = w2 & __builtin_amdgcn_perm(0u, mdw[e2] << sh, 0x09090808u);
+      }
+      // O^T += V^T P^T, and the row sums of the same bf16 weights on the ones operand.
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt][c] = mfma16x16x32(av[dt], pb, oacc[dt][c]);
+      lacc[c] = mfma16x16x32(ones, pb, lacc[c]);
+    }
+  };
+
+  // Operations of the stages after `ch` that are already issued when stage ch must be complete.
+  auto ops_after = [&](int ch, int last_issued) {
+    int n_ops = 0;
+    for (int c = ch + 1; c <= last_issued; ++c) n_ops += stage_ops(c);
+    return n_ops;
+  };
+  if (nchunk > 0) {
+    if (wave == 0)
+      for (int c = 0; c < NST - 1 && c < nchunk; ++c) meta_dma(c);
+    vm_wait<0>();
+    ring_barrier();
+    for (int c = 0; c < NST - 1 && c < nchunk; ++c) stage(c);
+    vm_wait_at_most(ops_after(0, min(NST - 2, nchunk - 1)));
+    ring_barrier();
+    for (int ch = 0; ch < nchunk; ++ch) {
+      if (ch + NST - 1 < nchunk) stage(ch + NST - 1);
+      compute(ch);
+      // Chunk ch + 1 (with the metadata its stage brought in) must have landed; the later
+      // stages may stay in flight.
+      if (ch + 1 < nchunk) vm_wait_at_most(ops_after(ch + 1, min(ch + NST - 1, nchunk - 1)));
+      ring_barrier();
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const float l_tot = __shfl(lacc[c][0], n);  // lane (group 0, column n) holds the sum
+    const int row = r0 + rbit[c];
+    if (row >= a.rows) continue;
+    const int h = g * G + (16 * (CT * wave + c) + n) % G;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* op = a.out + ((size_t)row * hq + h) * 128 + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 st;
+      st.x = pack_bf16x2(oacc[dt][c][0] * inv, oacc[dt][c][1] * inv);
+      st.y = pack_bf16x2(oacc[dt][c][2] * inv, oacc[dt][c][3] * inv);
+      *reinterpret_cast<uint2*>(op + 16 * dt) = st;
+    }
+    const float moff = (m_run[c] == -INFINITY) ? 0.f : m_run[c];
+    if (a.lse && lg == 0) a.lse[(size_t)row * hq + h] = l_tot > 0.f ? (moff + log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s) {
+  const int nb = a.block_end - a.block_begin;
+  if (nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(query_union_kernel, dim3(nb), dim3(kUnionThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+bool union_attn_supported(int hq, int hkv) {
+  const int g = hkv > 0 ? hq / hkv : 0;
+  return hkv > 0 && hq % hkv == 0 && (g == 4 || g == 8 || g == 16);
+}
+
+hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const int n_blocks = (a.rows + kQueryBlock - 1) / kQueryBlock;
+  const long long items = (long long)n_blocks * a.hkv;
+  const long long grid = (items + 127) / 128 * 128;  // whole runs of 16 on each of the 8 XCDs
+  const float scale_log2 = a.softmax_scale * 1.4426950408889634f;
+  switch (a.hq / a.hkv) {
+    case 4: hipLaunchKernelGGL((sparse_attn_union_kernel<4, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
+    case 8: hipLaunchKernelGGL((sparse_attn_union_kernel<8, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
+    case 16: hipLaunchKernelGGL((sparse_attn_union_kernel<16, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

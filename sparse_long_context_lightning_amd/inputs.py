@@ -16,7 +16,11 @@ Recipe (the same for every workload):
     and the attention key is bf16(o[block, g, :] + n) with o, n ~ N(0,1).  This mimics
     per-frame visual tokens that share content;
   * "video": from each sequence start, 32 text tokens (i.i.d. as above) alternate with one
-    256-token frame built like a 16-token block but 256 long.
+    256-token frame built like a 16-token block but 256 long;
+  * "blocks16q": "blocks16" keys, and the indexer queries of each 16-token block share content
+    too: q_I[t, j, :] = clip(o_Q[block, j, :] + round(q_noise * n), -3, 3) with o_Q uniform
+    integers in [-2, 2] and n ~ N(0,1), so neighbouring query tokens score positions alike and
+    select overlapping sets (q_noise sets how much they differ).
 """
 
 from __future__ import annotations
@@ -101,7 +105,7 @@ def _block_ids(total: int, cu: list, structure: str) -> np.ndarray:
     for b in range(len(cu) - 1):
         o, n = cu[b], cu[b + 1] - cu[b]
         t = np.arange(n)
-        if structure == "blocks16":
+        if structure in ("blocks16", "blocks16q"):
             local = t // 16
         elif structure == "video":
             per = t % 288
@@ -112,6 +116,17 @@ def _block_ids(total: int, cu: list, structure: str) -> np.ndarray:
         ids[o:o + n] = np.where(local >= 0, local + nxt, -1)
         nxt += nb
     return ids
+
+
+def _structured_queries(name, seed, total, cu, h_idx, d_idx, q_idx_bits, q_noise):
+    """Overwrite the indexer queries of 16-token blocks with a shared offset plus scaled, rounded
+    noise (see module docstring)."""
+    ids = _block_ids(total, cu, "blocks16")
+    nblk = int(ids.max()) + 1
+    off = _draw(name + ".q_idx_off", seed, (nblk, h_idx, d_idx), "int2").astype(np.int16)
+    noise = _draw(name + ".q_idx_noise", seed, (total, h_idx, d_idx), "normal_f32")
+    vals = off[ids] + np.rint(np.float32(q_noise) * noise).astype(np.int16)
+    q_idx_bits[:] = _INT_LUT[np.clip(vals, -3, 3) + 3]
 
 
 def _structured_keys(name, seed, total, cu, structure, d_idx, hkv, d, k_idx_bits, k_bits):
@@ -163,7 +178,7 @@ class DecodeInputs:
     meta: dict = field(default_factory=dict)
 
 
-def prefill_inputs(seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="iid", name="prefill"):
+def prefill_inputs(seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="iid", name="prefill", q_noise=0.5):
     seq_lens = [int(x) for x in seq_lens]
     cu = [0]
     for n in seq_lens:
@@ -177,9 +192,12 @@ def prefill_inputs(seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="i
     v = _draw(name + ".v", seed, (total, hkv, d), "normal_bf16")
     if structure != "iid":
         _structured_keys(name, seed, total, cu, structure, d_idx, hkv, d, k_idx, k)
+    if structure == "blocks16q":
+        _structured_queries(name, seed, total, cu, h_idx, d_idx, q_idx, q_noise)
     return PrefillInputs(seq_lens=seq_lens, cu_seqlens=np.asarray(cu, dtype=np.int32), q=q, k=k, v=v,
                          q_idx=q_idx, k_idx=k_idx, w=w, top_k=top_k,
-                         meta=dict(h_idx=h_idx, d_idx=d_idx, hq=hq, hkv=hkv, d=d, seed=seed, structure=structure))
+                         meta=dict(h_idx=h_idx, d_idx=d_idx, hq=hq, hkv=hkv, d=d, seed=seed, structure=structure,
+                                   q_noise=q_noise))
 
 
 def decode_inputs(batch, s_max, seq_lens, h_idx, d_idx, hq, hkv, d, top_k, seed, structure="iid", name="decode"):

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -109,6 +109,37 @@ def test_other_entry_points_reject_bad_arguments():
     args2 = list(args)
     args2[9] = 1001  # max_seq_len > s_max
     assert lib.dsa_decode(*args2) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_query_union_validation():
+    lib = dsa.load()
+    assert dsa.dsa_query_union_size(300, 2048) == (19, 32768)
+    assert dsa.dsa_query_union_size(16, 3) == (1, 64)
+    ok_cap = 32768
+    # null pointers, misaligned outputs, a capacity below 16 * k_sel or not a multiple of 32
+    assert lib.dsa_query_union(None, 2048, FAKE, 1, 300, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap, FAKE, MISALIGNED, FAKE, None) == \
+        dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap, FAKE, FAKE, MISALIGNED, None) == \
+        dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap - 32, FAKE, FAKE, FAKE, None) == \
+        dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap + 16, FAKE, FAKE, FAKE, None) == \
+        dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 0, FAKE, 1, 300, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 0, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_OK
+    sc = ctypes.c_float(0.1)
+    # merged-set attention: group sizes 4, 8, 16 only; cap a multiple of 32
+    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 300, 8, 4, 128, sc, FAKE, None,
+                                         None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 300, 32, 4, 64, sc, FAKE, None,
+                                         None) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 48, 300, 32, 4, 128, sc, FAKE, None,
+                                         None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, None, FAKE, FAKE, ok_cap, 300, 32, 4, 128, sc, FAKE, None,
+                                         None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 0, 32, 4, 128, sc, FAKE, None,
+                                         None) == dsa.DSA_OK
 
 
 def test_zero_sized_calls_are_no_ops():

@@ -1,0 +1,211 @@
+"""GPU parity of adjacent-query dedup: the merged index sets of 16-row blocks (bit for bit
+against the oracle's adjacent_query_union) and the attention computed from them (against the
+oracle's per-row attention and against the per-row GPU kernel)."""
+
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as orc
+from sparse_long_context_lightning_amd import inputs as inp
+
+from dsa_testlib import LSE_ABS, assert_attn_close, bf16_tensor_to_f64, f64, oracle_prefill_rows_lazy
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
+
+
+def _index_lists(cu, k, seed, repeats=False, p_bad=0.1, empty_rows=()):
+    """Per-row index lists: k positions of the row's prefix (distinct unless `repeats`), with a
+    fraction replaced by -1 or by positions past the prefix; rows in empty_rows get only -1."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((cu[-1], k), -1, dtype=np.int32)
+    for b in range(len(cu) - 1):
+        for t in range(cu[b + 1] - cu[b]):
+            r = cu[b] + t
+            if r in empty_rows:
+                continue
+            if repeats:
+                row = rng.integers(0, t + 1, size=k)
+            elif t + 1 >= k:
+                row = rng.choice(t + 1, size=k, replace=False)
+            else:
+                row = np.concatenate([rng.permutation(t + 1), np.full(k - t - 1, -1)])
+            bad = rng.random(k) < p_bad
+            row[bad] = rng.choice([-1, -5, t + 1, t + 1000], size=int(bad.sum()))
+            idx[r] = row
+    return idx
+
+
+def _gpu_union(dsa, idx_np, cu):
+    import torch
+    total, k = idx_np.shape
+    nb, cap = dsa.dsa_query_union_size(total, k)
+    idx = torch.from_numpy(idx_np).cuda()
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    counts = torch.full((nb,), -7, dtype=torch.int32, device="cuda")
+    rows = torch.full((nb, cap), -7, dtype=torch.int32, device="cuda")
+    masks = torch.full((nb, cap), 0x5A5A, dtype=torch.int16, device="cuda")
+    dsa.dsa_query_union(idx, cu_d, counts, rows, masks)
+    torch.cuda.synchronize()
+    return counts, rows, masks
+
+
+def _check_union_blocks(counts, rows, masks, want, blocks, cu):
+    counts = counts.cpu().numpy()
+    rows = rows.cpu().numpy()
+    masks = masks.cpu().numpy().view(np.uint16).astype(np.int64)
+    for b, (kv, m) in zip(blocks, want):
+        n = int(counts[b])
+        assert n == len(kv), f"block {b}: {n} merged rows, oracle {len(kv)}"
+        assert np.array_equal(rows[b, :n], kv), f"block {b}: KV rows differ"
+        assert np.array_equal(masks[b, :n], m), f"block {b}: masks differ"
+        # padding to a multiple of 32: the block's first sequence offset, mask 0
+        first = max(i for i in range(len(cu) - 1) if cu[i] <= 16 * b)
+        pad = (n + 31) // 32 * 32
+        assert np.all(rows[b, n:pad] == cu[first]) and np.all(masks[b, n:pad] == 0), f"block {b}: padding"
+
+
+@pytest.mark.parametrize("repeats", [False, True])
+def test_union_lists_match_oracle_packed(dsa, repeats):
+    cu = [0, 300, 301, 431]
+    idx = _index_lists(cu, 64, seed=71 + repeats, repeats=repeats, empty_rows={5, 300})
+    print(f"[union] packed {cu}, k=64, repeats={repeats}", flush=True)
+    counts, rows, masks = _gpu_union(dsa, idx, cu)
+    want = orc.adjacent_query_union(idx, cu)
+    _check_union_blocks(counts, rows, masks, want, range(len(want)), cu)
+
+
+def test_union_lists_match_oracle_over_several_windows(dsa):
+    # 70001 rows: the last blocks span more than two 32768-row bitmap windows, and the last
+    # block holds one row.
+    cu = [0, 70001]
+    rng = np.random.default_rng(73)
+    k = 32
+    t = np.arange(cu[-1])[:, None]
+    idx = (rng.random((cu[-1], k)) * (t + 1)).astype(np.int32)
+    idx[rng.random(idx.shape) < 0.05] = -1
+    print("[union] one sequence of 70001 rows, k=32", flush=True)
+    counts, rows, masks = _gpu_union(dsa, idx, cu)
+    nb = (cu[-1] + 15) // 16
+    blocks = [0, 1, 2047, 2048, 2049, 4095, nb - 2, nb - 1]
+    want = orc.adjacent_query_union(idx, cu, blocks=blocks)
+    _check_union_blocks(counts, rows, masks, want, blocks, cu)
+
+
+def _attn_inputs(cu, hq, hkv, seed):
+    pi = inp.prefill_inputs([cu[i + 1] - cu[i] for i in range(len(cu) - 1)], 4, 64, hq, hkv, 128, 16, seed=seed)
+    return pi
+
+
+def _run_union_attn(dsa, pi, idx_np, cu):
+    import torch
+    from dsa_testlib import upload_prefill
+    dev = upload_prefill(pi)
+    total, hq = pi.q.shape[0], pi.q.shape[1]
+    counts, rows, masks = _gpu_union(dsa, idx_np, cu)
+    out = torch.empty((total, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((total, hq), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out, lse)
+    ref_out = torch.empty_like(out)
+    ref_lse = torch.empty_like(lse)
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], torch.from_numpy(idx_np).cuda(), dev["cu"], ref_out,
+                            ref_lse)
+    torch.cuda.synchronize()
+    return (bf16_tensor_to_f64(out), lse.cpu().numpy().astype(np.float64), bf16_tensor_to_f64(ref_out),
+            ref_lse.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 4), (16, 4), (32, 2)])
+def test_union_attention_matches_oracle_and_per_row_kernel(dsa, hq, hkv):
+    cu = [0, 300, 301, 431]
+    pi = _attn_inputs(cu, hq, hkv, seed=81)
+    idx = _index_lists(cu, 64, seed=82, empty_rows={7, 300})
+    print(f"[union-attn] packed {cu}, hq={hq}, hkv={hkv}, k=64", flush=True)
+    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu)
+    q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
+    scale = orc.default_softmax_scale(128)
+    want_o = np.zeros_like(out)
+    want_l = np.zeros_like(lse)
+    for r in range(cu[-1]):
+        s = max(i for i in range(len(cu) - 1) if cu[i] <= r)
+        t = r - cu[s]
+        sel = np.asarray([p for p in idx[r] if 0 <= p <= t], dtype=np.int64)
+        o, l, _ = orc.sparse_gqa_attention_row(q[r], k[cu[s]:cu[s + 1]], v[cu[s]:cu[s + 1]], sel, scale)
+        want_o[r], want_l[r] = o, l
+    assert_attn_close(out, want_o, "merged-set attention vs oracle")
+    fin = np.isfinite(want_l)
+    assert np.all(np.isneginf(lse[~fin])) and np.all(out[~fin] == 0.0), "rows without positions"
+    assert np.abs(lse[fin] - want_l[fin]).max() <= LSE_ABS
+    assert_attn_close(out, ref_out, "merged-set vs per-row kernel")
+    assert np.abs(lse[fin] - ref_lse[fin]).max() <= LSE_ABS
+
+
+def test_union_attention_counts_a_repeated_position_once(dsa):
+    cu = [0, 200]
+    pi = _attn_inputs(cu, 32, 4, seed=83)
+    idx = _index_lists(cu, 48, seed=84, repeats=True)
+    print("[union-attn] repeated positions", flush=True)
+    out, lse, _, _ = _run_union_attn(dsa, pi, idx, cu)
+    q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
+    scale = orc.default_softmax_scale(128)
+    for b, (kv, m) in enumerate(orc.adjacent_query_union(idx, cu)):
+        n = min(16, cu[-1] - 16 * b)
+        o, l = orc.sparse_gqa_attention_union(q, k, v, kv, m, 16 * b, n, scale)
+        assert_attn_close(out[16 * b:16 * b + n], o, f"block {b}")
+        assert np.abs(lse[16 * b:16 * b + n] - l).max() <= LSE_ABS
+
+
+def test_union_attention_long_merged_sets(dsa):
+    # 16 rows x 512 positions of a 4096-row prefix: merged sets of up to 8192 rows (256 chunks).
+    cu = [0, 4096]
+    pi = _attn_inputs(cu, 32, 4, seed=85)
+    idx = _index_lists(cu, 512, seed=86, p_bad=0.02)
+    print("[union-attn] one sequence of 4096 rows, k=512", flush=True)
+    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu)
+    assert_attn_close(out, ref_out, "merged-set vs per-row kernel")
+    q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
+    scale = orc.default_softmax_scale(128)
+    rows = [0, 1, 15, 16, 511, 512, 2047, 4080, 4094, 4095]
+    want = []
+    for r in rows:
+        sel = np.asarray([p for p in idx[r] if 0 <= p <= r], dtype=np.int64)
+        want.append(orc.sparse_gqa_attention_row(q[r], k, v, sel, scale)[0])
+    assert_attn_close(out[rows], np.asarray(want), "merged-set attention vs oracle")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_union_full_c3_prefill_128k(dsa):
+    """At the benchmark's 128K workload: the prefill's own top-k sets, merged and attended, equal the
+    per-row kernel's output on every row, and on two sampled blocks the oracle's own top-k sets,
+    merged sets and attention."""
+    import torch
+    from dsa_testlib import upload_prefill
+    pi = inp.workload("c3_prefill_128k")
+    total = pi.q.shape[0]
+    dev = upload_prefill(pi)
+    cu = [int(x) for x in pi.cu_seqlens]
+    print("[union] c3 prefill 128K", flush=True)
+    out_ref, _, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens,
+                                  pi.top_k)
+    nb, cap = dsa.dsa_query_union_size(total, pi.top_k)
+    counts = torch.empty((nb,), dtype=torch.int32, device="cuda")
+    rows = torch.empty((nb, cap), dtype=torch.int32, device="cuda")
+    masks = torch.empty((nb, cap), dtype=torch.int16, device="cuda")
+    dsa.dsa_query_union(idx, dev["cu"], counts, rows, masks)
+    out = torch.empty_like(out_ref)
+    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out)
+    torch.cuda.synchronize()
+    err = (out.float() - out_ref.float()).abs()
+    assert float(err.max()) <= 2e-2 and float(err.mean()) <= 2e-3, (float(err.max()), float(err.mean()))
+    for b in (4100, nb - 1):
+        block_rows = list(range(16 * b, min(16 * b + 16, total)))
+        want = oracle_prefill_rows_lazy(pi, block_rows)
+        assert np.array_equal(idx[block_rows].cpu().numpy(), want["idx"]), f"block {b}: top-k sets"
+        idx_full = np.full((total, pi.top_k), -1, dtype=np.int64)
+        idx_full[block_rows] = want["idx"]
+        (kv, m), = orc.adjacent_query_union(idx_full, cu, blocks=[b])
+        n = int(counts[b])
+        assert n == len(kv)
+        assert np.array_equal(rows[b, :n].cpu().numpy(), kv)
+        assert np.array_equal(masks[b, :n].cpu().numpy().view(np.uint16).astype(np.int64), m)
+        assert_attn_close(bf16_tensor_to_f64(out[block_rows]), want["out"], f"block {b} vs oracle")
