@@ -241,6 +241,26 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
                               void* stream);
 
 /*
+ * Sparse GQA attention with adjacent-query dedup: what dsa_sparse_gqa_attn computes (up to
+ * rounding), with the same arguments plus a workspace.  The call builds the merged sets of every
+ * 16-row block (dsa_query_union) in the workspace and attends a block from its merged set
+ * (dsa_sparse_gqa_attn_union) when that set has at most 0.68 x (rows x k_sel) entries, a cost
+ * crossover measured on MI355X; other blocks, and blocks in which a row lists a position twice,
+ * are attended per row.  For hq / hkv outside {4, 8, 16} the workspace size is 0 and the call is
+ * dsa_sparse_gqa_attn.
+ *
+ * workspace  device buffer of at least dsa_sparse_gqa_attn_dedup_workspace_size bytes, 16-byte
+ *            aligned (DSA_ERR_WORKSPACE if smaller); its contents on return are unspecified.
+ */
+int dsa_sparse_gqa_attn_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv, size_t* bytes);
+int dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v,
+                              const int32_t* idx, int k_sel,
+                              const int32_t* cu_seqlens, int batch, int total_tokens,
+                              int hq, int hkv, int head_dim, float softmax_scale,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Backward of dsa_sparse_gqa_attn (digest section 一: the sparse adaptation stage trains the
  * whole model in the sparse mode, so gradients pass through this attention).
  *
@@ -264,9 +284,11 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
                             float* dq, float* dk, float* dv, void* stream);
 
 /*
- * Workspace bytes for dsa_prefill: a score buffer for a chunk of query rows (never the whole
- * L x L matrix) plus the top-k scratch of those rows; the default chunk is 2048 rows.  A larger
- * workspace lets the call use larger chunks, a smaller one (down to 64 rows) smaller ones.
+ * Workspace bytes for dsa_prefill: the larger of (a) a score buffer for a chunk of 2048 query
+ * rows (never the whole L x L matrix) plus the top-k scratch of those rows and (b), when
+ * hq / hkv is 4, 8 or 16, the merged index sets of dsa_sparse_gqa_attn_dedup, which reuse the
+ * same memory after the last chunk.  A smaller workspace gives smaller chunks (down to 64 rows)
+ * and, below (b), the attention without dedup.
  */
 int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv,
                                int head_dim, int h_idx, int d_idx, int top_k, size_t* bytes);
@@ -280,9 +302,13 @@ int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int 
  * max_seqlen                    >= the longest sequence
  * out [total_tokens, hq, head_dim] bf16, lse [total_tokens, hq] float or NULL
  * idx_out [total_tokens, top_k] int32   the selected positions (required)
- * workspace                     the call uses the largest chunk of rows whose scores and top-k
- *                               scratch fit; it must hold at least a 64-row chunk (or all rows if
- *                               fewer).  dsa_prefill_workspace_size gives the 2048-row default.
+ * workspace                     the call uses the largest chunk of at most 2048 rows whose scores
+ *                               and top-k scratch fit; it must hold at least a 64-row chunk (or all
+ *                               rows if fewer).  When it also holds the merged index sets
+ *                               (dsa_sparse_gqa_attn_dedup_workspace_size), the attention step is
+ *                               dsa_sparse_gqa_attn_dedup, else dsa_sparse_gqa_attn; the two give
+ *                               the same result up to rounding.  dsa_prefill_workspace_size gives
+ *                               the size for both.
  */
 int dsa_prefill(const void* q, const void* k, const void* v,
                 const void* q_idx, const void* k_idx, const float* w,

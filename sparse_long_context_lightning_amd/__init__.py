@@ -30,6 +30,8 @@ from ._lib import (  # noqa: F401
     dsa_query_union_size,
     dsa_sparse_gqa_attn,
     dsa_sparse_gqa_attn_bwd,
+    dsa_sparse_gqa_attn_dedup,
+    dsa_sparse_gqa_attn_dedup_workspace_size,
     dsa_sparse_gqa_attn_union,
     dsa_status_string,
     dsa_topk,

@@ -28,6 +28,7 @@ EXPORTED = (
     "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
     "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean", "dsa_indexer_kl",
     "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union", "dsa_sparse_gqa_attn_union",
+    "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
 )
 
 
@@ -71,6 +72,8 @@ def load():
         "dsa_query_union_size": ([_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
         "dsa_query_union": ([_P, _I, _P, _I, _I, _I, _P, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_union": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+        "dsa_sparse_gqa_attn_dedup_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_sparse_gqa_attn_dedup": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P], _I),
         "dsa_prefill_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_prefill": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P,
                          _SZ, _P], _I),
@@ -224,6 +227,29 @@ def dsa_sparse_gqa_attn_union(q, k, v, counts, kv_rows, masks, out, lse=None, so
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     _check(load().dsa_sparse_gqa_attn_union(_ptr(q), _ptr(k), _ptr(v), _ptr(counts), _ptr(kv_rows), _ptr(masks),
                                             kv_rows.shape[1], total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
+                                            _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_dedup_workspace_size(total_tokens, k_sel, hq, hkv):
+    n = _SZ(0)
+    _check(load().dsa_sparse_gqa_attn_dedup_workspace_size(total_tokens, k_sel, hq, hkv, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_sparse_gqa_attn_dedup(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=None, workspace=None,
+                              stream=None):
+    """dsa_sparse_gqa_attn with adjacent-query dedup (merged sets of 16-row blocks where they pay);
+    allocates the workspace when none is given."""
+    import torch
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if workspace is None:
+        nbytes = dsa_sparse_gqa_attn_dedup_workspace_size(total, idx.shape[1], hq, hkv)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(load().dsa_sparse_gqa_attn_dedup(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), idx.shape[1], _ptr(cu_seqlens),
+                                            cu_seqlens.shape[0] - 1, total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
+                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                             _stream(stream)))
 
 

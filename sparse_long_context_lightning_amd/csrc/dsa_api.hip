@@ -105,6 +105,81 @@ size_t prefill_chunk_bytes(int rows, long long ld) {
   return (size_t)round_up((long long)rows * ld * 4, 256) + topk_scratch(rows, ld);
 }
 
+// Per 16-row block, the merged-set attention is used when the block's merged set has at most
+// kUnionRatio x (rows x k_sel) entries.  Measured on MI355X at 128K / k = 2048 / GQA 32:4: the
+// merged-set kernel costs about 0.31 ns per merged entry and the per-row kernel about 0.21 ns per
+// (row, index slot), all KV groups included.
+constexpr float kUnionRatio = 0.68f;
+
+// Workspace of the dedup attention: per-block counts and path flags, merged KV rows and masks.
+struct UnionLayout {
+  int n_blocks = 0, cap = 0;
+  size_t counts = 0, flags = 0, rows = 0, masks = 0, bytes = 0;
+};
+UnionLayout union_layout(int total_tokens, int k_sel) {
+  UnionLayout u;
+  u.n_blocks = (total_tokens + dsa::kQueryBlock - 1) / dsa::kQueryBlock;
+  u.cap = (int)round_up((long long)dsa::kQueryBlock * k_sel, dsa::kUnionChunk);
+  long long off = 0;
+  u.counts = (size_t)off;
+  off += round_up((long long)u.n_blocks * 4, 256);
+  u.flags = (size_t)off;
+  off += round_up((long long)u.n_blocks * 4, 256);
+  u.rows = (size_t)off;
+  off += round_up((long long)u.n_blocks * u.cap * 4, 256);
+  u.masks = (size_t)off;
+  off += round_up((long long)u.n_blocks * u.cap * 2, 256);
+  u.bytes = (size_t)off;
+  return u;
+}
+
+// Sparse attention of the prefill rows described by `a` with adjacent-query dedup: merged sets
+// of every 16-row block, the merged-set kernel on the blocks flagged for it, the per-row kernel
+// on the others.  `ws` holds union_layout(a.rows, a.k_sel).bytes bytes.
+hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
+  const UnionLayout u = union_layout(a.rows, a.k_sel);
+  char* base = static_cast<char*>(ws);
+  int* counts = reinterpret_cast<int*>(base + u.counts);
+  int* flags = reinterpret_cast<int*>(base + u.flags);
+  int* kv_rows = reinterpret_cast<int*>(base + u.rows);
+  uint16_t* masks = reinterpret_cast<uint16_t*>(base + u.masks);
+  dsa::QueryUnionArgs q = {};
+  q.idx = a.idx;
+  q.k_sel = a.k_sel;
+  q.cu_seqlens = a.cu_seqlens;
+  q.batch = a.batch;
+  q.rows = a.rows;
+  q.block_begin = 0;
+  q.block_end = u.n_blocks;
+  q.cap = u.cap;
+  q.counts = counts;
+  q.kv_rows = kv_rows;
+  q.masks = masks;
+  q.use_union = flags;
+  q.ratio = kUnionRatio;
+  hipError_t e = dsa::launch_query_union(q, s);
+  if (e != hipSuccess) return e;
+  dsa::UnionAttnArgs m = {};
+  m.q = a.q;
+  m.k = a.k;
+  m.v = a.v;
+  m.counts = counts;
+  m.kv_rows = kv_rows;
+  m.masks = masks;
+  m.cap = u.cap;
+  m.rows = a.rows;
+  m.hq = a.hq;
+  m.hkv = a.hkv;
+  m.softmax_scale = a.softmax_scale;
+  m.out = a.out;
+  m.lse = a.lse;
+  m.use_union = flags;
+  e = dsa::launch_sparse_attn_union(m, s);
+  if (e != hipSuccess) return e;
+  a.skip_block = flags;
+  return dsa::launch_sparse_attn(a, s);
+}
+
 int decode_nsplit(int batch, int hkv, int top_k) {
   const int nchunk = (top_k + 31) / 32;
   const int want = (1024 + batch * hkv - 1) / (batch * hkv);
@@ -477,6 +552,60 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
   return hip_status(dsa::launch_sparse_attn_union(a, static_cast<hipStream_t>(stream)), "merged-set attention launch");
 }
 
+int dsa_sparse_gqa_attn_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (total_tokens < 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens >= 0 and k_sel > 0 required");
+  if (k_sel > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "k_sel %d too large", k_sel);
+  *bytes = dsa::union_attn_supported(hq, hkv) ? union_layout(total_tokens, k_sel).bytes : 0;
+  return DSA_OK;
+}
+
+int dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v, const int32_t* idx, int k_sel,
+                              const int32_t* cu_seqlens, int batch, int total_tokens, int hq, int hkv, int head_dim,
+                              float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(idx);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(out);
+  if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
+  if (k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  size_t need = 0;
+  DSA_TRY(dsa_sparse_gqa_attn_dedup_workspace_size(total_tokens, k_sel, hq, hkv, &need));
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
+  if (need > 0) DSA_ALIGNED(workspace);
+  if (total_tokens == 0) return DSA_OK;
+  dsa::SparseAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.seq_lens = nullptr;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.nsplit = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
+  return hip_status(launch_attn_dedup(a, workspace, s), "dedup attention launch");
+}
+
 int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
                             const void* dout, const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch,
                             int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, float* dq,
@@ -537,7 +666,9 @@ int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int 
   DSA_TRY(check_topk(top_k));
   const long long ld = round_up(std::max(max_seqlen, 1), 4);
   const int rows = std::max(1, std::min(total_tokens, kDefaultChunkRows));
-  *bytes = prefill_chunk_bytes(rows, ld);
+  // The dedup attention's merged sets use the same memory once the chunk loop is over.
+  const size_t dedup = dsa::union_attn_supported(hq, hkv) ? union_layout(total_tokens, top_k).bytes : 0;
+  *bytes = std::max(prefill_chunk_bytes(rows, ld), dedup);
   return DSA_OK;
 }
 
@@ -577,8 +708,9 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
   if (!workspace || workspace_bytes < prefill_chunk_bytes(min_rows, ld))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes of the smallest chunk (%d rows)",
                 workspace_bytes, prefill_chunk_bytes(min_rows, ld), min_rows);
-  // Largest chunk (a multiple of 64 rows when above 64) whose scores and top-k scratch fit.
-  long long chunk = std::min<long long>(total_tokens, (long long)(workspace_bytes / (ld * 4)));
+  // Largest chunk of at most kDefaultChunkRows rows (a multiple of 64 when above 64) whose scores
+  // and top-k scratch fit (larger chunks measured slower).
+  long long chunk = std::min<long long>(std::min(total_tokens, kDefaultChunkRows), (long long)(workspace_bytes / (ld * 4)));
   while (chunk > min_rows && prefill_chunk_bytes((int)chunk, ld) > workspace_bytes) --chunk;
   if (chunk > 64) chunk = chunk / 64 * 64;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -621,6 +753,10 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.nsplit = 1;
+  // With room for the merged sets (they reuse the chunk memory, no longer needed), the attention
+  // runs with adjacent-query dedup; otherwise per row.
+  if (dsa::union_attn_supported(hq, hkv) && workspace_bytes >= union_layout(total_tokens, top_k).bytes)
+    return hip_status(launch_attn_dedup(a, workspace, s), "dedup attention launch");
   return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
 }
 

@@ -68,8 +68,15 @@ __device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
 
 // Wait until at most n of this wave's vector-memory operations are outstanding (n is
 // wave-uniform; the largest listed immediate <= n is used, which only ever waits longer).
+// s_waitcnt vmcnt(N) through the builtin, so the compiler's wait-count bookkeeping sees it.  The
+// tile copies are issued untracked (lds_dma16_untracked): a tracked copy makes the compiler wait
+// for every copy in flight, the ring's next stage included, before each transposed LDS read.
 template <int N>
-__device__ __forceinline__ void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // lgkmcnt and expcnt fields at their maximum: no wait
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void vm_wait_at_most(int n) {
   if (n >= 15) vm_wait<15>();
   else if (n >= 12) vm_wait<12>();
@@ -151,13 +158,13 @@ __global__ __launch_bounds__(128 * NTOK) void indexer_bwd_q_kernel(
     const int last = kend - 1 - key0;
     for (int P = wave; P < NJOB; P += NWV) {
       if (P < 16) {
-        lds_dma16(swz_tile_src(kseq + (size_t)key0 * kBD, P, lane, last), &kt_lds[buf][P * 1024]);
+        lds_dma16_untracked(swz_tile_src(kseq + (size_t)key0 * kBD, P, lane, last), &kt_lds[buf][P * 1024]);
       } else {
         const int m = (P - 16) * 64 + lane;  // 16-byte piece: token m / 16, keys 4 (m % 16) ..
         const int gr = min(r0 + min(m >> 4, NTOK - 1), row_end - 1);
         int a = key0 + 4 * (m & 15);
         if (a > gr - seq_off) a = 0;  // past the row's prefix: any valid address (masked below)
-        lds_dma16(g + (size_t)(gr - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
+        lds_dma16_untracked(g + (size_t)(gr - grad_row0) * ld + a, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
       }
     }
   };
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
     const int r = seq_off + tl;
     for (int P = wave; P < NJOB; P += NW) {
       if (P < 16) {
-        lds_dma16(swz_tile_src(q_idx + (size_t)r * kBH * kBD, P, lane, kBH - 1), &q_lds[buf][P * 1024]);
+        lds_dma16_untracked(swz_tile_src(q_idx + (size_t)r * kBH * kBD, P, lane, kBH - 1), &q_lds[buf][P * 1024]);
       } else {
         const int m = (P - 16) * 64 + lane;  // 16-byte piece of the g / w region
         const float* src;
@@ -337,7 +344,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_bwd_k_kernel(
         } else {
           src = w + (size_t)r * kBH + 4 * min(m - KB / 4, kBH / 4 - 1);
         }
-        lds_dma16(src, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
+        lds_dma16_untracked(src, reinterpret_cast<unsigned char*>(g_lds[buf]) + (P - 16) * 1024);
       }
     }
   };

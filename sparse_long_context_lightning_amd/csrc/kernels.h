@@ -67,6 +67,7 @@ struct SparseAttnArgs {
   int nsplit;       // > 1: write partials to part_o / part_ml instead of out / lse
   float* part_o;    // [rows, hq, nsplit, 128]
   float* part_ml;   // [rows, hq, nsplit, 2] (running max in log2 units, sum)
+  const int* skip_block;  // prefill, optional: rows of 16-row blocks b with skip_block[b] != 0 are left alone
 };
 
 // Backward of the sparse attention (prefill layout): dq written, dk / dv zeroed then accumulated.
@@ -135,6 +136,11 @@ struct QueryUnionArgs {
   int* counts;
   int* kv_rows;
   uint16_t* masks;
+  // Optional: use_union[b] = 1 when the merged set is at most ratio x (rows x k_sel) entries,
+  // i.e. when the merged-set attention is expected to beat the per-row one for the block, and
+  // no row of the block lists a position twice.
+  int* use_union;
+  float ratio;
 };
 struct UnionAttnArgs {
   const uint16_t* q;
@@ -148,6 +154,7 @@ struct UnionAttnArgs {
   float softmax_scale;
   uint16_t* out;
   float* lse;
+  const int* use_union;  // optional: blocks with use_union[b] == 0 are left alone
 };
 hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s);
 // The union attention handles G = hq / hkv in {4, 8, 16}.

@@ -32,8 +32,17 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, float scale_log2, int n_wg) {
   __shared__ __attribute__((aligned(16))) unsigned char vlds_all[4][32 * kVPitch];
-  const int per_xcd = gridDim.x >> 3;
-  const int wg = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // Workgroups reach the 8 XCDs round-robin; XCD x takes the x-th eighth of the items.  When
+  // blocks of rows are skipped (attended from their merged sets instead), XCD x takes runs of 16
+  // consecutive workgroups (64 rows), runs x, x + 8, ..., so every XCD keeps an even share of
+  // the remaining rows while neighbouring rows, whose selections overlap, still share an L2.
+  int wg;
+  if (!a.skip_block) {
+    wg = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  } else {
+    const int xp = blockIdx.x >> 3;
+    wg = ((xp >> 4) * 8 + (blockIdx.x & 7)) * 16 + (xp & 15);
+  }
   if (wg >= n_wg) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
@@ -56,6 +65,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, floa
   }
   const int sp = (int)(tmp % a.nsplit);
   const int row = (int)(tmp / a.nsplit);
+  if (a.skip_block && a.skip_block[row / kQueryBlock]) return;  // attended from its block's merged set
   unsigned char* vlds = vlds_all[wave];
 
   // Row -> key/value rows and the last valid position.
@@ -262,7 +272,7 @@ hipError_t launch_sparse_attn(const SparseAttnArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   const long long items = (long long)a.rows * a.nsplit * a.hkv;
   const long long n_wg = (items + 3) / 4;
-  const long long grid = (n_wg + 7) / 8 * 8;
+  const long long grid = a.skip_block ? (n_wg + 127) / 128 * 128 : (n_wg + 7) / 8 * 8;
   const float scale_log2 = a.softmax_scale * 1.4426950408889634f;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, (int)n_wg);
   return hipGetLastError();

@@ -49,6 +49,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
   __shared__ __attribute__((aligned(16))) uint32_t bm[kUnionWindow / 2];
   __shared__ int row_base[kQueryBlock], row_t[kQueryBlock];
   __shared__ int wave_cnt[kUnionThreads / 64];
+  __shared__ int repeated;  // some row lists one position twice
   const int b = a.block_begin + blockIdx.x;
   const int r0 = b * kQueryBlock;
   const int nr = min(kQueryBlock, a.rows - r0);
@@ -62,6 +63,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
     row_base[tid] = base;
     row_t[tid] = t;
   }
+  if (tid == 0) repeated = 0;
   __syncthreads();
   const int b0 = row_base[0];          // no entry of the block names a KV row below this one
   const int span = r0 + nr - b0;       // KV rows b0 .. r0 + nr - 1
@@ -83,7 +85,10 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
       for (int i = tid; i < a.k_sel; i += kUnionThreads) {
         const int p = ir[i];
         const int x = off + p;
-        if (p >= 0 && p <= t && x >= 0 && x < limit) atomicOr(&bm[x >> 1], bit << ((x & 1) << 4));
+        if (p >= 0 && p <= t && x >= 0 && x < limit) {
+          const uint32_t b2 = bit << ((x & 1) << 4);
+          if (atomicOr(&bm[x >> 1], b2) & b2) repeated = 1;
+        }
       }
     }
     __syncthreads();
@@ -116,7 +121,12 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
     out_rows[e] = b0;
     out_masks[e] = 0;
   }
-  if (tid == 0) a.counts[b] = total;
+  if (tid == 0) {
+    a.counts[b] = total;
+    // A block whose rows repeat a position stays with the per-row attention, which counts each
+    // listed entry.
+    if (a.use_union) a.use_union[b] = (!repeated && (float)total <= a.ratio * (float)nr * (float)a.k_sel) ? 1 : 0;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(256) void sparse_attn_union_kernel(UnionAttnArgs a,
   const int blk = n_blocks - 1 - (wi - g * n_blocks);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
+  if (a.use_union && a.use_union[blk] == 0) return;
   const int r0 = blk * kQueryBlock;
   const int hq = a.hq;
   const int n_u = min(a.counts[blk], a.cap);

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -142,6 +142,25 @@ def test_query_union_validation():
                                          None) == dsa.DSA_OK
 
 
+def test_dedup_attention_validation():
+    lib = dsa.load()
+    sc = ctypes.c_float(0.1)
+    need = dsa.dsa_sparse_gqa_attn_dedup_workspace_size(300, 64, 32, 4)
+    base = [FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 300, 32, 4, 128, sc, FAKE, None]
+    assert lib.dsa_sparse_gqa_attn_dedup(*base, None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_gqa_attn_dedup(*base, FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_gqa_attn_dedup(*base, MISALIGNED, need, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(base)
+    bad[3] = None
+    assert lib.dsa_sparse_gqa_attn_dedup(*bad, FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(base)
+    bad[8], bad[9] = 30, 4
+    assert lib.dsa_sparse_gqa_attn_dedup(*bad, FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+    zero = list(base)
+    zero[7] = 0
+    assert lib.dsa_sparse_gqa_attn_dedup(*zero, FAKE, need, None) == dsa.DSA_OK
+
+
 def test_zero_sized_calls_are_no_ops():
     lib = dsa.load()
     cu_arr, cu_p = _cu([0, 64])
@@ -159,12 +178,24 @@ def test_workspace_sizes():
     # rows longer than 262144 have only the scratch-free path
     assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == _topk_scratch(100)
     assert dsa.dsa_topk_workspace_size(100, 262148, 2048) == 0
-    # prefill: a 2048-row chunk of 131072 float scores plus its top-k scratch
-    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 32, 4, 128, 64, 128, 2048) == \
-        2048 * 131072 * 4 + _topk_scratch(2048)
+    # prefill: the larger of a 2048-row chunk of 131072 float scores plus its top-k scratch and the
+    # merged index sets of the dedup attention (per 16-row block: count, flag, 16 k int32 KV rows,
+    # 16 k uint16 masks, each array 256-byte aligned)
+    def _union(total, k):
+        nb, cap = (total + 15) // 16, (16 * k + 31) // 32 * 32
+        r = lambda x: (x + 255) // 256 * 256
+        return 2 * r(nb * 4) + r(nb * cap * 4) + r(nb * cap * 2)
+    chunk = 2048 * 131072 * 4 + _topk_scratch(2048)
+    assert _union(131072, 2048) > chunk
+    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 32, 4, 128, 64, 128, 2048) == _union(131072, 2048)
+    assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(131072, 2048, 32, 4) == _union(131072, 2048)
+    # group size 3 has no merged-set kernel: no dedup workspace, the chunk alone
+    assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(131072, 2048, 12, 4) == 0
+    assert dsa.dsa_prefill_workspace_size(1, 131072, 131072, 12, 4, 128, 64, 128, 2048) == chunk
     # small problems use the whole row count
-    assert dsa.dsa_prefill_workspace_size(1, 100, 100, 8, 2, 128, 4, 64, 16) == \
-        (100 * 100 * 4 + 255) // 256 * 256 + _topk_scratch(100)
+    small = (100 * 100 * 4 + 255) // 256 * 256 + _topk_scratch(100)
+    assert small > _union(100, 16)
+    assert dsa.dsa_prefill_workspace_size(1, 100, 100, 8, 2, 128, 4, 64, 16) == small
     n = dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 128, 64, 128, 2048)
     assert n >= 32 * 131072 * 4 + _topk_scratch(32)
     with pytest.raises(dsa.DsaError):

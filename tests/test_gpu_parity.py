@@ -337,9 +337,15 @@ def test_prefill_equals_composition_and_is_deterministic(dsa):
     dsa.dsa_topk(scores, row_len, pi.top_k, idx3)
     out3 = torch.empty_like(out)
     lse3 = torch.empty_like(lse)
-    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx3, dev["cu"], out3, lse3)
+    # With its default workspace the prefill's attention step is the dedup call (bit for bit) ...
+    dsa.dsa_sparse_gqa_attn_dedup(dev["q"], dev["k"], dev["v"], idx3, dev["cu"], out3, lse3)
     assert torch.equal(idx, idx3)
     assert torch.equal(out.view(torch.int16), out3.view(torch.int16))
+    assert torch.equal(lse, lse3)
+    # ... which agrees with the per-row call within the attention tolerance.
+    out4 = torch.empty_like(out)
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx3, dev["cu"], out4, None)
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(out), tl.bf16_tensor_to_f64(out4), "prefill vs per-row attention")
 
 
 def test_prefill_outputs_fully_written(dsa):

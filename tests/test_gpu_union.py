@@ -172,6 +172,60 @@ def test_union_attention_long_merged_sets(dsa):
     assert_attn_close(out[rows], np.asarray(want), "merged-set attention vs oracle")
 
 
+@pytest.mark.parametrize("k,dup_rows", [(16, ()), (64, ()), (16, (100, 1700))])
+def test_dedup_attention_equals_per_row_attention_and_oracle(dsa, k, dup_rows):
+    """dsa_sparse_gqa_attn_dedup picks, per 16-row block, the merged-set or the per-row kernel; its
+    result must be dsa_sparse_gqa_attn's (a block where a row repeats a position goes per row, so
+    the repeat counts twice, as the oracle counts it)."""
+    import torch
+    cu = [0, 1500, 1501, 1900]
+    pi = _attn_inputs(cu, 32, 4, seed=91)
+    idx = _index_lists(cu, k, seed=92 + k, empty_rows={3, 1500})
+    for r in dup_rows:
+        idx[r, 1] = idx[r, 0] = max(0, r - cu[0 if r < cu[1] else 2] - 1)
+    print(f"[dedup-attn] packed {cu}, k={k}, repeated rows {dup_rows}", flush=True)
+    from dsa_testlib import upload_prefill
+    dev = upload_prefill(pi)
+    total = cu[-1]
+    idx_d = torch.from_numpy(idx).cuda()
+    out = torch.empty((total, 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((total, 32), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_gqa_attn_dedup(dev["q"], dev["k"], dev["v"], idx_d, dev["cu"], out, lse)
+    ref = torch.empty_like(out)
+    ref_lse = torch.empty_like(lse)
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx_d, dev["cu"], ref, ref_lse)
+    torch.cuda.synchronize()
+    # Both paths must have been taken.
+    counts, _, _ = _gpu_union(dsa, idx, cu)
+    counts = counts.cpu().numpy()
+    nr = np.minimum(16, total - 16 * np.arange(len(counts)))
+    merged = (counts <= 0.68 * nr * k)
+    for r in dup_rows:
+        merged[r // 16] = False
+    assert merged.any() and (~merged).any(), merged.sum()
+    got, got_l = bf16_tensor_to_f64(out), lse.cpu().numpy().astype(np.float64)
+    assert_attn_close(got, bf16_tensor_to_f64(ref), "dedup vs per-row kernel")
+    q, kk, v = f64(pi.q), f64(pi.k), f64(pi.v)
+    scale = orc.default_softmax_scale(128)
+    want_o = np.zeros_like(got)
+    want_l = np.full(got_l.shape, -np.inf)
+    for r in range(total):
+        s = max(i for i in range(len(cu) - 1) if cu[i] <= r)
+        t = r - cu[s]
+        sel = np.asarray([p for p in idx[r] if 0 <= p <= t], dtype=np.int64)
+        want_o[r], want_l[r], _ = orc.sparse_gqa_attention_row(q[r], kk[cu[s]:cu[s + 1]], v[cu[s]:cu[s + 1]], sel, scale)
+    assert_attn_close(got, want_o, "dedup vs oracle")
+    fin = np.isfinite(want_l)
+    assert np.all(np.isneginf(got_l[~fin]))
+    # Every weight enters the row sum rounded to bf16 (unit roundoff 2^-8), so the sum is within a
+    # factor 1 +- 2^-8 of the exact one and |d lse| <= -ln(1 - 2^-8); with only 16 positions per
+    # row the roundings do not average out as they do at k = 2048.
+    lse_bound = -np.log1p(-2.0 ** -8) + 1e-5
+    assert np.abs(got_l[fin] - want_l[fin]).max() <= (LSE_ABS if k >= 64 else lse_bound)
+    for r in dup_rows:   # the repeated position carries twice the weight
+        np.testing.assert_allclose(got[r], want_o[r], atol=2e-2)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_union_full_c3_prefill_128k(dsa):
