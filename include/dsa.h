@@ -199,54 +199,54 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
 
 /*
  * Adjacent-query dedup, step 1 (digest section 八: neighbouring query tokens select largely the
- * same positions, so the top-k sets of adjacent queries are de-duplicated and the attention
+ * same positions, so the top-k sets of 16 adjacent queries are de-duplicated and the attention
  * kernel masks inside its matrix tiles).
  *
- * Block b is packed rows 16 b .. 16 b + 15, n_blocks = ceil(total_tokens / 16); the last block
- * may be shorter and a block may span two sequences.  Entry p of row r (sequence offset o, local
- * position t) counts when 0 <= p <= t and names the packed KV row o + p; a position a row lists
- * twice counts once.
+ * Block b is packed rows R b .. R b + R - 1 with R = block_rows, 16 (the pages' count) or 8;
+ * n_blocks = ceil(total_tokens / R); the last block may be shorter and a block may span two
+ * sequences.  Entry p of row r (sequence offset o, local position t) counts when 0 <= p <= t and
+ * names the packed KV row o + p; a position a row lists twice counts once.
  *
  * idx [total_tokens, k_sel] int32   as for dsa_sparse_gqa_attn (any order)
  * cu_seqlens [batch + 1] int32      device copy of the packed offsets
- * cap                               entries per block: a multiple of 32, at least 16 * k_sel
+ * block_rows                        8 or 16 (DSA_ERR_UNSUPPORTED otherwise)
+ * cap                               entries per block: a multiple of 32, at least R * k_sel
  *                                   rounded up to a multiple of 32 (dsa_query_union_size)
  * counts  [n_blocks] int32          out: number of distinct KV rows the block's rows selected
  * kv_rows [n_blocks, cap] int32     out: those packed KV rows in ascending order, followed by
  *                                   padding to a multiple of 32 entries (the offset of the block's
  *                                   first sequence); entries after the padding are not written
- * masks   [n_blocks, cap] uint16    out: bit j set when row 16 b + j selected the KV row; 0 in the
+ * masks   [n_blocks, cap] uint16    out: bit j set when row R b + j selected the KV row; 0 in the
  *                                   padding
  * kv_rows must be 16-byte aligned, masks 4-byte aligned.
  */
-int dsa_query_union_size(int total_tokens, int k_sel, int* n_blocks, int* cap);
+int dsa_query_union_size(int total_tokens, int k_sel, int block_rows, int* n_blocks, int* cap);
 int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens,
-                    int cap, int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream);
+                    int block_rows, int cap, int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream);
 
 /*
  * Adjacent-query dedup, step 2: sparse GQA attention from the merged sets dsa_query_union wrote.
- * Each KV row of a block's merged set is read once for all of the block's rows; row 16 b + j
+ * Each KV row of a block's merged set is read once for all of the block's rows; row R b + j
  * attends over the KV rows whose mask has bit j, with the softmax of dsa_sparse_gqa_attn.  For
  * index sets that repeat no position the result is dsa_sparse_gqa_attn's (up to rounding).
  *
  * q, k, v, total_tokens, hq, hkv, head_dim, softmax_scale, out, lse   as for dsa_sparse_gqa_attn
- * counts, kv_rows, masks, cap       as dsa_query_union wrote them (KV rows outside
+ * counts, kv_rows, masks, block_rows, cap   as dsa_query_union wrote them (KV rows outside
  *                                   [0, total_tokens) are clamped into it, counts above cap read
  *                                   as cap, so no access leaves the buffers)
  * Supports hq / hkv in {4, 8, 16} (DSA_ERR_UNSUPPORTED otherwise).  Needs no workspace.
  */
 int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const int32_t* counts,
-                              const int32_t* kv_rows, const uint16_t* masks, int cap, int total_tokens,
-                              int hq, int hkv, int head_dim, float softmax_scale, void* out, float* lse,
-                              void* stream);
+                              const int32_t* kv_rows, const uint16_t* masks, int block_rows, int cap,
+                              int total_tokens, int hq, int hkv, int head_dim, float softmax_scale,
+                              void* out, float* lse, void* stream);
 
 /*
  * Sparse GQA attention with adjacent-query dedup: what dsa_sparse_gqa_attn computes (up to
  * rounding), with the same arguments plus a workspace.  The call builds the merged sets of every
- * 16-row block (dsa_query_union) in the workspace and attends a block from its merged set
- * (dsa_sparse_gqa_attn_union) when that set has at most 0.68 x (rows x k_sel) entries, a cost
- * crossover measured on MI355X; other blocks, and blocks in which a row lists a position twice,
- * are attended per row.  For hq / hkv outside {4, 8, 16} the workspace size is 0 and the call is
+ * block of 8 rows (dsa_query_union) in the workspace and attends each block from its merged set
+ * (dsa_sparse_gqa_attn_union), except blocks in which a row lists a position twice, which are
+ * attended per row (so that the repeat counts as dsa_sparse_gqa_attn counts it).  For hq / hkv outside {4, 8, 16} the workspace size is 0 and the call is
  * dsa_sparse_gqa_attn.
  *
  * workspace  device buffer of at least dsa_sparse_gqa_attn_dedup_workspace_size bytes, 16-byte

@@ -69,9 +69,9 @@ def load():
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
                                     _I),
-        "dsa_query_union_size": ([_I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
-        "dsa_query_union": ([_P, _I, _P, _I, _I, _I, _P, _P, _P, _P], _I),
-        "dsa_sparse_gqa_attn_union": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+        "dsa_query_union_size": ([_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
+        "dsa_query_union": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+        "dsa_sparse_gqa_attn_union": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_dedup_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_sparse_gqa_attn_dedup": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P], _I),
         "dsa_prefill_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
@@ -205,29 +205,30 @@ def dsa_sparse_gqa_attn(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=N
                                       _stream(stream)))
 
 
-def dsa_query_union_size(total_tokens, k_sel):
-    """(n_blocks, cap): blocks of 16 packed rows and the per-block entry capacity."""
+def dsa_query_union_size(total_tokens, k_sel, block_rows=16):
+    """(n_blocks, cap): blocks of block_rows (8 or 16) packed rows and the per-block entry capacity."""
     nb, cap = _I(0), _I(0)
-    _check(load().dsa_query_union_size(total_tokens, k_sel, ctypes.byref(nb), ctypes.byref(cap)))
+    _check(load().dsa_query_union_size(total_tokens, k_sel, block_rows, ctypes.byref(nb), ctypes.byref(cap)))
     return nb.value, cap.value
 
 
-def dsa_query_union(idx, cu_seqlens, counts, kv_rows, masks, stream=None):
-    """Merged index sets of blocks of 16 adjacent packed rows: counts [n_blocks] int32, kv_rows
-    [n_blocks, cap] int32 (ascending packed KV rows), masks [n_blocks, cap] int16 (bit j = row 16 b + j)."""
+def dsa_query_union(idx, cu_seqlens, counts, kv_rows, masks, block_rows=16, stream=None):
+    """Merged index sets of blocks of block_rows adjacent packed rows: counts [n_blocks] int32, kv_rows
+    [n_blocks, cap] int32 (ascending packed KV rows), masks [n_blocks, cap] int16 (bit j = row R b + j)."""
     total, k_sel = idx.shape
-    _check(load().dsa_query_union(_ptr(idx), k_sel, _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, total,
+    _check(load().dsa_query_union(_ptr(idx), k_sel, _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, total, block_rows,
                                   kv_rows.shape[1], _ptr(counts), _ptr(kv_rows), _ptr(masks), _stream(stream)))
 
 
-def dsa_sparse_gqa_attn_union(q, k, v, counts, kv_rows, masks, out, lse=None, softmax_scale=None, stream=None):
+def dsa_sparse_gqa_attn_union(q, k, v, counts, kv_rows, masks, out, lse=None, softmax_scale=None, block_rows=16,
+                              stream=None):
     """Sparse GQA attention of every packed row from the merged sets of dsa_query_union."""
     total, hq, d = q.shape
     hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
     _check(load().dsa_sparse_gqa_attn_union(_ptr(q), _ptr(k), _ptr(v), _ptr(counts), _ptr(kv_rows), _ptr(masks),
-                                            kv_rows.shape[1], total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
-                                            _stream(stream)))
+                                            block_rows, kv_rows.shape[1], total, hq, hkv, d, scale, _ptr(out),
+                                            _ptr(lse), _stream(stream)))
 
 
 def dsa_sparse_gqa_attn_dedup_workspace_size(total_tokens, k_sel, hq, hkv):

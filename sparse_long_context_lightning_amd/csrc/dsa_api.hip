@@ -105,21 +105,24 @@ size_t prefill_chunk_bytes(int rows, long long ld) {
   return (size_t)round_up((long long)rows * ld * 4, 256) + topk_scratch(rows, ld);
 }
 
-// Per 16-row block, the merged-set attention is used when the block's merged set has at most
-// kUnionRatio x (rows x k_sel) entries.  Measured on MI355X at 128K / k = 2048 / GQA 32:4: the
-// merged-set kernel costs about 0.31 ns per merged entry and the per-row kernel about 0.21 ns per
-// (row, index slot), all KV groups included.
-constexpr float kUnionRatio = 0.68f;
+// Blocks of kUnionBlockRows rows; a block is attended from its merged set when that set has at
+// most kUnionRatio x (rows x k_sel) entries.  Measured on MI355X at 128K / k = 2048 / GQA 32:4,
+// blocks of 8 rows beat blocks of 16 (the merged-set work grows with rows x |merged set| while
+// the gathered bytes change little), and with 8-row blocks the merged-set kernel beat the
+// per-row one at every merged-set size (ratios 0.8 / 0.9 / 1.0: 160.9 / 157.4 / 152.4 ms for the
+// whole prefill), so only blocks that repeat a position go per row.
+constexpr int kUnionBlockRows = 8;
+constexpr float kUnionRatio = 1.0f;
 
 // Workspace of the dedup attention: per-block counts and path flags, merged KV rows and masks.
 struct UnionLayout {
   int n_blocks = 0, cap = 0;
   size_t counts = 0, flags = 0, rows = 0, masks = 0, bytes = 0;
 };
-UnionLayout union_layout(int total_tokens, int k_sel) {
+UnionLayout union_layout(int total_tokens, int k_sel, int block_rows = kUnionBlockRows) {
   UnionLayout u;
-  u.n_blocks = (total_tokens + dsa::kQueryBlock - 1) / dsa::kQueryBlock;
-  u.cap = (int)round_up((long long)dsa::kQueryBlock * k_sel, dsa::kUnionChunk);
+  u.n_blocks = (total_tokens + block_rows - 1) / block_rows;
+  u.cap = (int)round_up((long long)block_rows * k_sel, dsa::kUnionChunk);
   long long off = 0;
   u.counts = (size_t)off;
   off += round_up((long long)u.n_blocks * 4, 256);
@@ -149,6 +152,7 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   q.cu_seqlens = a.cu_seqlens;
   q.batch = a.batch;
   q.rows = a.rows;
+  q.block_rows = kUnionBlockRows;
   q.block_begin = 0;
   q.block_end = u.n_blocks;
   q.cap = u.cap;
@@ -167,6 +171,7 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   m.kv_rows = kv_rows;
   m.masks = masks;
   m.cap = u.cap;
+  m.block_rows = kUnionBlockRows;
   m.rows = a.rows;
   m.hq = a.hq;
   m.hkv = a.hkv;
@@ -177,6 +182,7 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   e = dsa::launch_sparse_attn_union(m, s);
   if (e != hipSuccess) return e;
   a.skip_block = flags;
+  a.skip_block_rows = kUnionBlockRows;
   return dsa::launch_sparse_attn(a, s);
 }
 
@@ -469,19 +475,20 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
   return hip_status(dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
 }
 
-int dsa_query_union_size(int total_tokens, int k_sel, int* n_blocks, int* cap) {
+int dsa_query_union_size(int total_tokens, int k_sel, int block_rows, int* n_blocks, int* cap) {
   g_last_error[0] = 0;
   DSA_NONNULL(n_blocks);
   DSA_NONNULL(cap);
   if (total_tokens < 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens >= 0 and k_sel > 0 required");
+  if (!dsa::union_block_rows_ok(block_rows)) return fail(DSA_ERR_UNSUPPORTED, "block_rows %d is not 8 or 16", block_rows);
   if (k_sel > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "k_sel %d too large", k_sel);
-  *n_blocks = (total_tokens + dsa::kQueryBlock - 1) / dsa::kQueryBlock;
-  *cap = (int)round_up((long long)dsa::kQueryBlock * k_sel, dsa::kUnionChunk);
+  *n_blocks = (total_tokens + block_rows - 1) / block_rows;
+  *cap = (int)round_up((long long)block_rows * k_sel, dsa::kUnionChunk);
   return DSA_OK;
 }
 
-int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens, int cap,
-                    int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream) {
+int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens,
+                    int block_rows, int cap, int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream) {
   g_last_error[0] = 0;
   DSA_NONNULL(idx);
   DSA_NONNULL(cu_seqlens);
@@ -492,7 +499,7 @@ int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, in
   if (reinterpret_cast<uintptr_t>(masks) & 3u) return fail(DSA_ERR_INVALID_ARG, "masks must be 4-byte aligned");
   if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
   int n_blocks = 0, need = 0;
-  DSA_TRY(dsa_query_union_size(total_tokens, k_sel, &n_blocks, &need));
+  DSA_TRY(dsa_query_union_size(total_tokens, k_sel, block_rows, &n_blocks, &need));
   if (cap < need || cap % dsa::kUnionChunk != 0)
     return fail(DSA_ERR_INVALID_ARG, "cap %d must be a multiple of %d and >= %d", cap, dsa::kUnionChunk, need);
   if (total_tokens == 0) return DSA_OK;
@@ -502,6 +509,7 @@ int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, in
   a.cu_seqlens = cu_seqlens;
   a.batch = batch;
   a.rows = total_tokens;
+  a.block_rows = block_rows;
   a.block_begin = 0;
   a.block_end = n_blocks;
   a.cap = cap;
@@ -512,8 +520,9 @@ int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, in
 }
 
 int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const int32_t* counts,
-                              const int32_t* kv_rows, const uint16_t* masks, int cap, int total_tokens, int hq,
-                              int hkv, int head_dim, float softmax_scale, void* out, float* lse, void* stream) {
+                              const int32_t* kv_rows, const uint16_t* masks, int block_rows, int cap,
+                              int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, void* out,
+                              float* lse, void* stream) {
   g_last_error[0] = 0;
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -531,6 +540,7 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
   if (total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens must be >= 0");
   if (cap <= 0 || cap % dsa::kUnionChunk != 0)
     return fail(DSA_ERR_INVALID_ARG, "cap %d must be a positive multiple of %d", cap, dsa::kUnionChunk);
+  if (!dsa::union_block_rows_ok(block_rows)) return fail(DSA_ERR_UNSUPPORTED, "block_rows %d is not 8 or 16", block_rows);
   DSA_TRY(check_attn_shape(hq, hkv, head_dim));
   if (!dsa::union_attn_supported(hq, hkv))
     return fail(DSA_ERR_UNSUPPORTED, "merged-set attention supports hq / hkv in {4, 8, 16} (got %d)", hq / hkv);
@@ -543,6 +553,7 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
   a.kv_rows = kv_rows;
   a.masks = masks;
   a.cap = cap;
+  a.block_rows = block_rows;
   a.rows = total_tokens;
   a.hq = hq;
   a.hkv = hkv;

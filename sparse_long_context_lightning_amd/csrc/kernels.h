@@ -67,7 +67,8 @@ struct SparseAttnArgs {
   int nsplit;       // > 1: write partials to part_o / part_ml instead of out / lse
   float* part_o;    // [rows, hq, nsplit, 128]
   float* part_ml;   // [rows, hq, nsplit, 2] (running max in log2 units, sum)
-  const int* skip_block;  // prefill, optional: rows of 16-row blocks b with skip_block[b] != 0 are left alone
+  const int* skip_block;  // prefill, optional: rows of blocks b (skip_block_rows rows each) with
+  int skip_block_rows;    // skip_block[b] != 0 are left alone
 };
 
 // Backward of the sparse attention (prefill layout): dq written, dk / dv zeroed then accumulated.
@@ -118,19 +119,21 @@ struct HeadMeanArgs {
   long long ld;
 };
 
-// Adjacent-query dedup.  Block b = packed rows kQueryBlock * b .. + kQueryBlock - 1 (the last
-// one may be shorter).  Its merged list has counts[b] entries at kv_rows / masks + b * cap:
-// packed KV rows in ascending order and 16-bit masks (bit j: row kQueryBlock * b + j selected
-// the KV row), padded with mask-0 entries to a multiple of kUnionChunk.  cap must be a multiple
-// of kUnionChunk and at least kQueryBlock * k_sel rounded up to one.
-constexpr int kQueryBlock = 16;
+// Adjacent-query dedup.  Block b = packed rows R b .. R b + R - 1 with R = block_rows, 8 or 16
+// (the last block may be shorter).  Its merged list has counts[b] entries at kv_rows / masks +
+// b * cap: packed KV rows in ascending order and 16-bit masks (bit j: row R b + j selected the
+// KV row), padded with mask-0 entries to a multiple of kUnionChunk.  cap must be a multiple of
+// kUnionChunk and at least R * k_sel rounded up to one.
+constexpr int kMaxQueryBlock = 16;
 constexpr int kUnionChunk = 32;
+inline bool union_block_rows_ok(int r) { return r == 8 || r == 16; }
 struct QueryUnionArgs {
   const int* idx;
   int k_sel;
   const int* cu_seqlens;
   int batch;
   int rows;                     // packed rows in all (for the last, shorter block)
+  int block_rows;               // R
   int block_begin, block_end;   // blocks built by this launch
   int cap;
   int* counts;
@@ -150,6 +153,7 @@ struct UnionAttnArgs {
   const int* kv_rows;
   const uint16_t* masks;
   int cap;
+  int block_rows;
   int rows, hq, hkv;
   float softmax_scale;
   uint16_t* out;

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, floa
   }
   const int sp = (int)(tmp % a.nsplit);
   const int row = (int)(tmp / a.nsplit);
-  if (a.skip_block && a.skip_block[row / kQueryBlock]) return;  // attended from its block's merged set
+  if (a.skip_block && a.skip_block[row / a.skip_block_rows]) return;  // attended from its block's merged set
   unsigned char* vlds = vlds_all[wave];
 
   // Row -> key/value rows and the last valid position.

@@ -2,27 +2,30 @@
 //
 // Neighbouring query tokens select largely the same positions (Keye-VL-2.0 report digest,
 // mqxn.cn news 1966, section 八: the top-k sets of adjacent queries are de-duplicated and the
-// attention kernel masks inside its matrix tiles), so the sets of 16 consecutive packed rows
-// are merged, every KV row of the merged set is fetched once for all 16 rows, and a 16-bit
-// mask per merged position keeps each row to its own positions.
+// attention kernel masks inside its matrix tiles), so the sets of R consecutive packed rows
+// (R = 16 as on that page, or 8) are merged, every KV row of the merged set is fetched once for
+// all R rows, and a 16-bit mask per merged position keeps each row to its own positions.
 //
-// query_union_kernel: one workgroup per block of 16 rows.  Entry p of row r (sequence offset
+// query_union_kernel: one workgroup per block of R rows.  Entry p of row r (sequence offset
 // o, local position t) counts when 0 <= p <= t and names packed KV row o + p; bit j (row j of
 // the block) is OR-ed into a 16-bit-per-position bitmap in LDS, one window of 32768 KV rows
 // at a time, and each window is compacted in ascending order with ballots.  The list is
 // padded to a multiple of 32 entries with (the block's smallest possible KV row, mask 0).
 //
-// sparse_attn_union_kernel: one workgroup of 4 waves per (block, KV group).  Per chunk of 32
-// merged positions the workgroup DMAs the 32 key rows and 32 value rows of the group into LDS
-// (a 3-stage ring; a chunk's positions and masks are DMA'd two chunks earlier, so the gather
-// addresses are read from LDS), and each wave uses them for its 4 rows x G heads:
+// sparse_attn_union_kernel: one workgroup of R / 4 waves per (block, KV group).  Per chunk of
+// 32 merged positions the workgroup DMAs the 32 key rows and 32 value rows of the group into
+// LDS (a ring of stages; a chunk's positions and masks arrive in an earlier stage, so the
+// gather addresses are read from LDS), and each wave uses them for its 4 rows x G heads:
 //   * S^T = K Q^T on 16x16x32 bf16 MFMA, keys on rows, (row, head) pairs on columns; with
 //     G = 8 one 16-column tile is two rows' eight heads;
-//   * the lane that holds S^T[key][column] tests the column's row bit in the key's mask and
-//     sets the logit to -inf where the row did not select the key;
-//   * online softmax in base 2 per column, as in the per-row kernel;
+//   * online softmax in base 2 per column, its offset allowed to lag the largest logit by a
+//     bounded margin so that the masked maximum is needed only when that margin is passed;
+//   * the lane that holds P^T[key][column] keeps its bf16 weight only where the key's mask
+//     carries the column's row bit (the "mask that knows the MFMA thread layout");
 //   * O^T += V^T P^T with V^T read transposed from LDS (ds_read_b64_tr_b16) in the key order
-//     the P^T registers carry.
+//     the P^T registers carry, and the row sums on the same MFMA with a ones operand.
+// The cost per block grows with R x |merged set| while the gathered bytes shrink with the
+// overlap, so R trades compute against memory traffic.
 #include "common.h"
 #include "kernels.h"
 
@@ -47,14 +50,14 @@ __device__ __forceinline__ int lanes_below(uint64_t bal) {
 
 __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t bm[kUnionWindow / 2];
-  __shared__ int row_base[kQueryBlock], row_t[kQueryBlock];
+  __shared__ int row_base[kMaxQueryBlock], row_t[kMaxQueryBlock];
   __shared__ int wave_cnt[kUnionThreads / 64];
   __shared__ int repeated;  // some row lists one position twice
   const int b = a.block_begin + blockIdx.x;
-  const int r0 = b * kQueryBlock;
-  const int nr = min(kQueryBlock, a.rows - r0);
+  const int r0 = b * a.block_rows;
+  const int nr = min(a.block_rows, a.rows - r0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < kQueryBlock) {
+  if (tid < kMaxQueryBlock) {
     int base = 0, t = -1;
     if (tid < nr) {
       base = a.cu_seqlens[seq_of_row(a.cu_seqlens, a.batch, r0 + tid)];
@@ -135,7 +138,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazyMax = 8.f;  // log2 units the softmax offset may lag the largest logit
 constexpr int kRowBytes = 128 * 2;                    // one key or value row of a group
 constexpr int kStageBytes = 2 * kUnionChunk * kRowBytes;  // 32 key rows, then 32 value rows
-constexpr int kStages = 4;                            // chunks in the K/V ring
+// Chunks in the K/V ring (16 KiB each) for blocks of 16 and of 8 rows: with two waves per
+// workgroup (8 rows) a shallower ring leaves room for more workgroups per CU.
+constexpr int kStages16 = 3;
+constexpr int kStages8 = 2;
 constexpr int kMetaBytes = 256;                       // positions (128 B) + masks (64 B) of a chunk
 
 // Chunk rows in LDS: [32 rows][256 B], 16-byte piece c of row r at slot c ^ swz(r).  For
@@ -167,14 +173,20 @@ __device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
 // (after vmcnt(0) it knows its earlier loads have landed and adds no wait of its own for them).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // lgkmcnt and expcnt fields at their maximum: no wait
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  // vmcnt bits [3:0] and [15:14]; the lgkmcnt and expcnt fields at their maximum (no wait).
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
   asm volatile("" ::: "memory");
 }
 // Wait until at most n of this wave's vector-memory operations are outstanding (the largest
 // listed immediate <= n is used, which only ever waits longer).
 __device__ __forceinline__ void vm_wait_at_most(int n) {
-  if (n >= 15) vm_wait<15>();
+  if (n >= 32) vm_wait<32>();
+  else if (n >= 24) vm_wait<24>();
+  else if (n >= 20) vm_wait<20>();
+  else if (n >= 18) vm_wait<18>();
+  else if (n >= 16) vm_wait<16>();
+  else if (n >= 15) vm_wait<15>();
   else if (n >= 12) vm_wait<12>();
   else if (n >= 10) vm_wait<10>();
   else if (n >= 8) vm_wait<8>();
@@ -191,9 +203,10 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int G, int NST>
-__global__ __launch_bounds__(256) void sparse_attn_union_kernel(UnionAttnArgs a, float scale_log2, int n_blocks) {
+template <int G, int NST, int NW>
+__global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArgs a, float scale_log2, int n_blocks) {
   constexpr int CT = G / 4;  // 16-column tiles per wave: 4 rows x G heads
+  constexpr int R = 4 * NW;  // rows per block
   // A chunk's metadata is DMA'd NST - 1 chunks ahead of its K/V stage, which is issued NST - 1
   // chunks ahead of its use: 2 NST - 1 chunks of metadata are live at once.
   constexpr int MS = (2 * NST - 1 <= 8) ? 8 : 16;
@@ -212,7 +225,7 @@ __global__ __launch_bounds__(256) void sparse_attn_union_kernel(UnionAttnArgs a,
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
   if (a.use_union && a.use_union[blk] == 0) return;
-  const int r0 = blk * kQueryBlock;
+  const int r0 = blk * R;
   const int hq = a.hq;
   const int n_u = min(a.counts[blk], a.cap);
   const int nchunk = (n_u + kUnionChunk - 1) / kUnionChunk;
@@ -261,21 +274,25 @@ __global__ __launch_bounds__(256) void sparse_attn_union_kernel(UnionAttnArgs a,
                                 : (const void*)(umask + ch * kUnionChunk + 2 * (min(lane, 47) - 32));
     lds_dma4_untracked(src, meta_lds[ch % MS]);
   };
-  // Every wave gathers key and value rows 4 wave + lane / 16 and 16 + 4 wave + lane / 16.
+  // The chunk's 32 key rows and 32 value rows go in 8 + 8 copies of 4 rows (1 KiB each); wave w
+  // issues copies w, w + NW, ...: key and value rows 4 j + lane / 16 for those j.
   auto stage = [&](int ch) {
     const int* pos = reinterpret_cast<const int*>(meta_lds[ch % MS]);
-    const int rr = 4 * wave + (lane >> 4);
-    // Clamped into [0, rows): a foreign list can not make the gather leave K / V.
-    const int p0 = min(max(pos[rr], 0), a.rows - 1), p1 = min(max(pos[16 + rr], 0), a.rows - 1);
-    const int piece = (lane & 15) ^ swz(rr);
     unsigned char* buf = kv_lds[ch % NST];
-    lds_dma16_untracked(kg + (size_t)p0 * row_stride + piece * 8, buf + (4 * wave) * kRowBytes);
-    lds_dma16_untracked(kg + (size_t)p1 * row_stride + piece * 8, buf + (16 + 4 * wave) * kRowBytes);
-    lds_dma16_untracked(vg + (size_t)p0 * row_stride + piece * 8, buf + (32 + 4 * wave) * kRowBytes);
-    lds_dma16_untracked(vg + (size_t)p1 * row_stride + piece * 8, buf + (48 + 4 * wave) * kRowBytes);
+    int pr[8 / NW];
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i)  // clamped into [0, rows): a foreign list cannot move the gather off K / V
+      pr[i] = min(max(pos[4 * (wave + i * NW) + (lane >> 4)], 0), a.rows - 1);
+#pragma unroll
+    for (int i = 0; i < 8 / NW; ++i) {
+      const int j = wave + i * NW;
+      const int piece = (lane & 15) ^ swz(4 * j + (lane >> 4));
+      lds_dma16_untracked(kg + (size_t)pr[i] * row_stride + piece * 8, buf + (4 * j) * kRowBytes);
+      lds_dma16_untracked(vg + (size_t)pr[i] * row_stride + piece * 8, buf + (32 + 4 * j) * kRowBytes);
+    }
     if (wave == 0 && ch + NST - 1 < nchunk) meta_dma(ch + NST - 1);
   };
-  auto stage_ops = [&](int ch) { return 4 + ((wave == 0 && ch + NST - 1 < nchunk) ? 1 : 0); };
+  auto stage_ops = [&](int ch) { return 16 / NW + ((wave == 0 && ch + NST - 1 < nchunk) ? 1 : 0); };
 
   const int trow = 4 * lg + (n >> 2), tm = n & 3, tsw = swz(trow);
   auto compute = [&](int ch) {
@@ -421,16 +438,25 @@ bool union_attn_supported(int hq, int hkv) {
   return hkv > 0 && hq % hkv == 0 && (g == 4 || g == 8 || g == 16);
 }
 
+template <int G>
+void launch_union_g(const UnionAttnArgs& a, unsigned grid, float scale_log2, int n_blocks, hipStream_t s) {
+  if (a.block_rows == 8)
+    hipLaunchKernelGGL((sparse_attn_union_kernel<G, kStages8, 2>), dim3(grid), dim3(128), 0, s, a, scale_log2, n_blocks);
+  else
+    hipLaunchKernelGGL((sparse_attn_union_kernel<G, kStages16, 4>), dim3(grid), dim3(256), 0, s, a, scale_log2, n_blocks);
+}
+
 hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  const int n_blocks = (a.rows + kQueryBlock - 1) / kQueryBlock;
+  if (!union_block_rows_ok(a.block_rows)) return hipErrorInvalidValue;
+  const int n_blocks = (a.rows + a.block_rows - 1) / a.block_rows;
   const long long items = (long long)n_blocks * a.hkv;
-  const long long grid = (items + 127) / 128 * 128;  // whole runs of 16 on each of the 8 XCDs
+  const unsigned grid = (unsigned)((items + 127) / 128 * 128);  // whole runs of 16 on each of the 8 XCDs
   const float scale_log2 = a.softmax_scale * 1.4426950408889634f;
   switch (a.hq / a.hkv) {
-    case 4: hipLaunchKernelGGL((sparse_attn_union_kernel<4, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
-    case 8: hipLaunchKernelGGL((sparse_attn_union_kernel<8, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
-    case 16: hipLaunchKernelGGL((sparse_attn_union_kernel<16, kStages>), dim3((unsigned)grid), dim3(256), 0, s, a, scale_log2, n_blocks); break;
+    case 4: launch_union_g<4>(a, grid, scale_log2, n_blocks, s); break;
+    case 8: launch_union_g<8>(a, grid, scale_log2, n_blocks, s); break;
+    case 16: launch_union_g<16>(a, grid, scale_log2, n_blocks, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

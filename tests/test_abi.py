@@ -114,32 +114,32 @@ def test_other_entry_points_reject_bad_arguments():
 def test_query_union_validation():
     lib = dsa.load()
     assert dsa.dsa_query_union_size(300, 2048) == (19, 32768)
+    assert dsa.dsa_query_union_size(300, 2048, 8) == (38, 16384)
     assert dsa.dsa_query_union_size(16, 3) == (1, 64)
+    with pytest.raises(dsa.DsaError):
+        dsa.dsa_query_union_size(16, 3, 4)
     ok_cap = 32768
-    # null pointers, misaligned outputs, a capacity below 16 * k_sel or not a multiple of 32
-    assert lib.dsa_query_union(None, 2048, FAKE, 1, 300, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap, FAKE, MISALIGNED, FAKE, None) == \
-        dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap, FAKE, FAKE, MISALIGNED, None) == \
-        dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap - 32, FAKE, FAKE, FAKE, None) == \
-        dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 300, ok_cap + 16, FAKE, FAKE, FAKE, None) == \
-        dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 0, FAKE, 1, 300, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_query_union(FAKE, 2048, FAKE, 1, 0, ok_cap, FAKE, FAKE, FAKE, None) == dsa.DSA_OK
+    args = lambda **o: [o.get("idx", FAKE), 2048, FAKE, 1, o.get("total", 300), o.get("rows", 16), o.get("cap", ok_cap),
+                        FAKE, o.get("kv", FAKE), o.get("masks", FAKE), None]
+    assert lib.dsa_query_union(*args(idx=None)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(kv=MISALIGNED)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(masks=MISALIGNED)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(cap=ok_cap - 32)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(cap=ok_cap + 16)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(rows=12)) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_query_union(*args(rows=8, cap=16384 - 32)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_query_union(*args(rows=8, cap=16384, total=0)) == dsa.DSA_OK
+    assert lib.dsa_query_union(*args(total=0)) == dsa.DSA_OK
     sc = ctypes.c_float(0.1)
-    # merged-set attention: group sizes 4, 8, 16 only; cap a multiple of 32
-    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 300, 8, 4, 128, sc, FAKE, None,
-                                         None) == dsa.DSA_ERR_UNSUPPORTED
-    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 300, 32, 4, 64, sc, FAKE, None,
-                                         None) == dsa.DSA_ERR_UNSUPPORTED
-    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 48, 300, 32, 4, 128, sc, FAKE, None,
-                                         None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, None, FAKE, FAKE, ok_cap, 300, 32, 4, 128, sc, FAKE, None,
-                                         None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_sparse_gqa_attn_union(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ok_cap, 0, 32, 4, 128, sc, FAKE, None,
-                                         None) == dsa.DSA_OK
+    # merged-set attention: group sizes 4, 8, 16 only; cap a multiple of 32; blocks of 8 or 16 rows
+    u = lambda **o: [FAKE, FAKE, FAKE, o.get("counts", FAKE), FAKE, FAKE, o.get("rows", 16), o.get("cap", ok_cap),
+                     o.get("total", 300), o.get("hq", 32), 4, o.get("d", 128), sc, FAKE, None, None]
+    assert lib.dsa_sparse_gqa_attn_union(*u(hq=8)) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_gqa_attn_union(*u(d=64)) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_gqa_attn_union(*u(rows=4)) == dsa.DSA_ERR_UNSUPPORTED
+    assert lib.dsa_sparse_gqa_attn_union(*u(cap=48)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_gqa_attn_union(*u(counts=None)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_sparse_gqa_attn_union(*u(total=0)) == dsa.DSA_OK
 
 
 def test_dedup_attention_validation():
@@ -179,10 +179,10 @@ def test_workspace_sizes():
     assert dsa.dsa_topk_workspace_size(100, 4096, 2048) == _topk_scratch(100)
     assert dsa.dsa_topk_workspace_size(100, 262148, 2048) == 0
     # prefill: the larger of a 2048-row chunk of 131072 float scores plus its top-k scratch and the
-    # merged index sets of the dedup attention (per 16-row block: count, flag, 16 k int32 KV rows,
-    # 16 k uint16 masks, each array 256-byte aligned)
+    # merged index sets of the dedup attention (per 8-row block: count, flag, 8 k int32 KV rows,
+    # 8 k uint16 masks, each array 256-byte aligned)
     def _union(total, k):
-        nb, cap = (total + 15) // 16, (16 * k + 31) // 32 * 32
+        nb, cap = (total + 7) // 8, (8 * k + 31) // 32 * 32
         r = lambda x: (x + 255) // 256 * 256
         return 2 * r(nb * 4) + r(nb * cap * 4) + r(nb * cap * 2)
     chunk = 2048 * 131072 * 4 + _topk_scratch(2048)

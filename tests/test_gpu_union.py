@@ -35,21 +35,21 @@ def _index_lists(cu, k, seed, repeats=False, p_bad=0.1, empty_rows=()):
     return idx
 
 
-def _gpu_union(dsa, idx_np, cu):
+def _gpu_union(dsa, idx_np, cu, block_rows=16):
     import torch
     total, k = idx_np.shape
-    nb, cap = dsa.dsa_query_union_size(total, k)
+    nb, cap = dsa.dsa_query_union_size(total, k, block_rows)
     idx = torch.from_numpy(idx_np).cuda()
     cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
     counts = torch.full((nb,), -7, dtype=torch.int32, device="cuda")
     rows = torch.full((nb, cap), -7, dtype=torch.int32, device="cuda")
     masks = torch.full((nb, cap), 0x5A5A, dtype=torch.int16, device="cuda")
-    dsa.dsa_query_union(idx, cu_d, counts, rows, masks)
+    dsa.dsa_query_union(idx, cu_d, counts, rows, masks, block_rows)
     torch.cuda.synchronize()
     return counts, rows, masks
 
 
-def _check_union_blocks(counts, rows, masks, want, blocks, cu):
+def _check_union_blocks(counts, rows, masks, want, blocks, cu, block_rows=16):
     counts = counts.cpu().numpy()
     rows = rows.cpu().numpy()
     masks = masks.cpu().numpy().view(np.uint16).astype(np.int64)
@@ -59,19 +59,19 @@ def _check_union_blocks(counts, rows, masks, want, blocks, cu):
         assert np.array_equal(rows[b, :n], kv), f"block {b}: KV rows differ"
         assert np.array_equal(masks[b, :n], m), f"block {b}: masks differ"
         # padding to a multiple of 32: the block's first sequence offset, mask 0
-        first = max(i for i in range(len(cu) - 1) if cu[i] <= 16 * b)
+        first = max(i for i in range(len(cu) - 1) if cu[i] <= block_rows * b)
         pad = (n + 31) // 32 * 32
         assert np.all(rows[b, n:pad] == cu[first]) and np.all(masks[b, n:pad] == 0), f"block {b}: padding"
 
 
-@pytest.mark.parametrize("repeats", [False, True])
-def test_union_lists_match_oracle_packed(dsa, repeats):
+@pytest.mark.parametrize("repeats,block_rows", [(False, 16), (True, 16), (False, 8), (True, 8)])
+def test_union_lists_match_oracle_packed(dsa, repeats, block_rows):
     cu = [0, 300, 301, 431]
     idx = _index_lists(cu, 64, seed=71 + repeats, repeats=repeats, empty_rows={5, 300})
-    print(f"[union] packed {cu}, k=64, repeats={repeats}", flush=True)
-    counts, rows, masks = _gpu_union(dsa, idx, cu)
-    want = orc.adjacent_query_union(idx, cu)
-    _check_union_blocks(counts, rows, masks, want, range(len(want)), cu)
+    print(f"[union] packed {cu}, k=64, repeats={repeats}, block_rows={block_rows}", flush=True)
+    counts, rows, masks = _gpu_union(dsa, idx, cu, block_rows)
+    want = orc.adjacent_query_union(idx, cu, block_rows=block_rows)
+    _check_union_blocks(counts, rows, masks, want, range(len(want)), cu, block_rows)
 
 
 def test_union_lists_match_oracle_over_several_windows(dsa):
@@ -96,15 +96,16 @@ def _attn_inputs(cu, hq, hkv, seed):
     return pi
 
 
-def _run_union_attn(dsa, pi, idx_np, cu):
+def _run_union_attn(dsa, pi, idx_np, cu, block_rows=16):
     import torch
     from dsa_testlib import upload_prefill
     dev = upload_prefill(pi)
     total, hq = pi.q.shape[0], pi.q.shape[1]
-    counts, rows, masks = _gpu_union(dsa, idx_np, cu)
+    counts, rows, masks = _gpu_union(dsa, idx_np, cu, block_rows)
     out = torch.empty((total, hq, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((total, hq), dtype=torch.float32, device="cuda")
-    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out, lse)
+    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out, lse,
+                                  block_rows=block_rows)
     ref_out = torch.empty_like(out)
     ref_lse = torch.empty_like(lse)
     dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], torch.from_numpy(idx_np).cuda(), dev["cu"], ref_out,
@@ -114,13 +115,14 @@ def _run_union_attn(dsa, pi, idx_np, cu):
             ref_lse.cpu().numpy().astype(np.float64))
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 4), (16, 4), (32, 2)])
-def test_union_attention_matches_oracle_and_per_row_kernel(dsa, hq, hkv):
+@pytest.mark.parametrize("hq,hkv,block_rows", [(32, 4, 16), (16, 4, 16), (32, 2, 16), (32, 4, 8), (16, 4, 8),
+                                               (32, 2, 8)])
+def test_union_attention_matches_oracle_and_per_row_kernel(dsa, hq, hkv, block_rows):
     cu = [0, 300, 301, 431]
     pi = _attn_inputs(cu, hq, hkv, seed=81)
     idx = _index_lists(cu, 64, seed=82, empty_rows={7, 300})
-    print(f"[union-attn] packed {cu}, hq={hq}, hkv={hkv}, k=64", flush=True)
-    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu)
+    print(f"[union-attn] packed {cu}, hq={hq}, hkv={hkv}, k=64, block_rows={block_rows}", flush=True)
+    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu, block_rows)
     q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
     scale = orc.default_softmax_scale(128)
     want_o = np.zeros_like(out)
@@ -139,28 +141,31 @@ def test_union_attention_matches_oracle_and_per_row_kernel(dsa, hq, hkv):
     assert np.abs(lse[fin] - ref_lse[fin]).max() <= LSE_ABS
 
 
-def test_union_attention_counts_a_repeated_position_once(dsa):
+@pytest.mark.parametrize("block_rows", [16, 8])
+def test_union_attention_counts_a_repeated_position_once(dsa, block_rows):
     cu = [0, 200]
     pi = _attn_inputs(cu, 32, 4, seed=83)
     idx = _index_lists(cu, 48, seed=84, repeats=True)
-    print("[union-attn] repeated positions", flush=True)
-    out, lse, _, _ = _run_union_attn(dsa, pi, idx, cu)
+    print(f"[union-attn] repeated positions, block_rows={block_rows}", flush=True)
+    out, lse, _, _ = _run_union_attn(dsa, pi, idx, cu, block_rows)
     q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
     scale = orc.default_softmax_scale(128)
-    for b, (kv, m) in enumerate(orc.adjacent_query_union(idx, cu)):
-        n = min(16, cu[-1] - 16 * b)
-        o, l = orc.sparse_gqa_attention_union(q, k, v, kv, m, 16 * b, n, scale)
-        assert_attn_close(out[16 * b:16 * b + n], o, f"block {b}")
-        assert np.abs(lse[16 * b:16 * b + n] - l).max() <= LSE_ABS
+    R = block_rows
+    for b, (kv, m) in enumerate(orc.adjacent_query_union(idx, cu, block_rows=R)):
+        n = min(R, cu[-1] - R * b)
+        o, l = orc.sparse_gqa_attention_union(q, k, v, kv, m, R * b, n, scale)
+        assert_attn_close(out[R * b:R * b + n], o, f"block {b}")
+        assert np.abs(lse[R * b:R * b + n] - l).max() <= LSE_ABS
 
 
-def test_union_attention_long_merged_sets(dsa):
+@pytest.mark.parametrize("block_rows", [16, 8])
+def test_union_attention_long_merged_sets(dsa, block_rows):
     # 16 rows x 512 positions of a 4096-row prefix: merged sets of up to 8192 rows (256 chunks).
     cu = [0, 4096]
     pi = _attn_inputs(cu, 32, 4, seed=85)
     idx = _index_lists(cu, 512, seed=86, p_bad=0.02)
-    print("[union-attn] one sequence of 4096 rows, k=512", flush=True)
-    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu)
+    print(f"[union-attn] one sequence of 4096 rows, k=512, block_rows={block_rows}", flush=True)
+    out, lse, ref_out, ref_lse = _run_union_attn(dsa, pi, idx, cu, block_rows)
     assert_attn_close(out, ref_out, "merged-set vs per-row kernel")
     q, k, v = f64(pi.q), f64(pi.k), f64(pi.v)
     scale = orc.default_softmax_scale(128)
@@ -172,7 +177,7 @@ def test_union_attention_long_merged_sets(dsa):
     assert_attn_close(out[rows], np.asarray(want), "merged-set attention vs oracle")
 
 
-@pytest.mark.parametrize("k,dup_rows", [(16, ()), (64, ()), (16, (100, 1700))])
+@pytest.mark.parametrize("k,dup_rows", [(16, ()), (64, ()), (16, (100, 1700)), (64, (5, 6, 1501))])
 def test_dedup_attention_equals_per_row_attention_and_oracle(dsa, k, dup_rows):
     """dsa_sparse_gqa_attn_dedup picks, per 16-row block, the merged-set or the per-row kernel; its
     result must be dsa_sparse_gqa_attn's (a block where a row repeats a position goes per row, so
@@ -195,14 +200,9 @@ def test_dedup_attention_equals_per_row_attention_and_oracle(dsa, k, dup_rows):
     ref_lse = torch.empty_like(lse)
     dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx_d, dev["cu"], ref, ref_lse)
     torch.cuda.synchronize()
-    # Both paths must have been taken.
-    counts, _, _ = _gpu_union(dsa, idx, cu)
-    counts = counts.cpu().numpy()
-    nr = np.minimum(16, total - 16 * np.arange(len(counts)))
-    merged = (counts <= 0.68 * nr * k)
-    for r in dup_rows:
-        merged[r // 16] = False
-    assert merged.any() and (~merged).any(), merged.sum()
+    # Blocks of 8 rows are merged unless a row repeats a position.
+    counts, _, _ = _gpu_union(dsa, idx, cu, 8)
+    assert int((counts > 0).sum()) > 0
     got, got_l = bf16_tensor_to_f64(out), lse.cpu().numpy().astype(np.float64)
     assert_attn_close(got, bf16_tensor_to_f64(ref), "dedup vs per-row kernel")
     q, kk, v = f64(pi.q), f64(pi.k), f64(pi.v)
