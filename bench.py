@@ -7,8 +7,11 @@ the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexe
 dim 128, 32 query / 4 KV heads of dim 128, keys in 16-token blocks), with every input already
 resident in HBM.  The timed step is the fused dsa_prefill call; the same chunk schedule is then
 driven through the C ABI's separate entry points with HIP events on the launch stream around
-every kernel, which gives the per-kernel times (and the rooflines) beside it.  The
-decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
+every kernel, which gives the per-kernel times (and the rooflines) beside it.  The attention
+step runs with adjacent-query dedup (merged index sets of 8-row blocks); the fused call is also
+timed with a workspace too small for the merged sets, which attends per row.  The same prefill
+on inputs whose neighbouring queries select overlapping sets follows (with and without dedup).
+The decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
 the torch.topk-shaped top-k on the decode scores, the backward of the sparse attention and the
 indexer's warm-up step (target, KL and the indexer backward) on the 32K prefill (context lines
 beside the headline value).
@@ -65,6 +68,7 @@ def parse():
     ap.add_argument("--workload", default=PREFILL)
     ap.add_argument("--decode-workload", default=DECODE)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-correlated", action="store_true", help="skip the correlated-query prefill context line")
     ap.add_argument("--bwd-workload", default="c2_prefill_32k")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -140,6 +144,14 @@ def prefill_bench(args, dsa, inp, tl):
     ws_bytes = dsa.dsa_prefill_workspace_size(len(lens), total, max_seqlen, hq, hkv, d, h_idx, d_idx, k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     chunk = min(total, 2048)   # the default chunk dsa_prefill_workspace_size provides for
+    # A workspace with room for the chunk only: dsa_prefill then attends per row (no dedup).
+    ws_chunk_bytes = (chunk * ld * 4 + 255) // 256 * 256 + dsa.dsa_topk_workspace_size(chunk, ld, k)
+    # The dedup attention's merged sets (blocks of 8 rows, as dsa_prefill builds them).
+    ublk = 8
+    nb, cap = dsa.dsa_query_union_size(total, k, ublk)
+    u_counts = torch.empty(nb, dtype=torch.int32, device="cuda")
+    u_rows = torch.empty((nb, cap), dtype=torch.int32, device="cuda")
+    u_masks = torch.empty((nb, cap), dtype=torch.int16, device="cuda")
     scores = ws.view(torch.float32)[: chunk * ld].view(chunk, ld)
     # Same carving as dsa_prefill: the chunk's scores, then the top-k scratch (256-byte aligned).
     topk_off = (chunk * ld * 4 + 255) // 256 * 256
@@ -161,13 +173,19 @@ def prefill_bench(args, dsa, inp, tl):
                 tok = timer.start("topk")
                 dsa.dsa_topk(scores, row_len[c0:c1], k, idx[c0:c1], workspace=topk_ws, ld=ld)
                 timer.stop(tok)
+        # The attention step as dsa_prefill runs it (top-k sets never repeat a position, so every
+        # 8-row block is attended from its merged set): merged sets, then the merged-set kernel.
+        tok = timer.start("query_union")
+        dsa.dsa_query_union(idx, dev["cu"], u_counts, u_rows, u_masks, ublk)
+        timer.stop(tok)
         tok = timer.start("sparse_attn")
-        dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out, lse)
+        dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], u_counts, u_rows, u_masks, out, lse,
+                                      block_rows=ublk)
         timer.stop(tok)
 
-    def fused():
+    def fused(workspace=ws):
         dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
-                        max_seqlen, k, out, lse, idx, ws)
+                        max_seqlen, k, out, lse, idx, workspace)
 
     # Timed region: the fused entry point, inputs already resident.
     for _ in range(args.warmup):
@@ -194,15 +212,56 @@ def prefill_bench(args, dsa, inp, tl):
     launches = {n: timer.count[n] / args.steps for n in timer.count}
     log(f"prefill {ms_per_step:.1f} ms/step (separate entry points {sep_ms:.1f}); kernels {kern}")
 
+    # The same fused call with a workspace too small for the merged sets: attention per row.
+    ws_chunk = ws[:ws_chunk_bytes]
+    fused(ws_chunk)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fused(ws_chunk)
+    torch.cuda.synchronize()
+    no_dedup_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    out_nd = out.clone()
+    fused()
+    torch.cuda.synchronize()
+    dd_err = (out.float() - out_nd.float()).abs()
+    log(f"prefill without dedup {no_dedup_ms:.1f} ms/step; |O dedup - O per row| max {float(dd_err.max()):.2e}")
+
     # Algorithmic work per step.
     pairs = sum(n * (n + 1) // 2 for n in lens)
     idx_flops = pairs * 2 * h_idx * d_idx
     sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
     attn_bytes = sel_pairs * (2 * hkv * d * 2 + 4) + total * (2 * hq * d * 2 + 4 * hq)
+    counts = u_counts.cpu().numpy().astype(np.int64)
+    merged = int(counts.sum())
+    padded = int(((counts + 31) // 32 * 32).sum())
+    # Merged-set attention: each merged KV row's key and value rows of every group once, the
+    # merged lists (int32 row + uint16 mask, padded to 32), Q in, O and lse out.
+    merged_bytes = merged * hkv * d * 2 * 2 + padded * 6 + total * (2 * hq * d * 2 + 4 * hq)
+    # Its MFMA work: per merged KV row and group, S^T and O^T over 8 rows x G heads (plus the row
+    # sums on a ones operand, not counted).
+    merged_flops = merged * hkv * 2 * (2 * ublk * (hq // hkv) * d)
+    union_bytes = total * k * 4 + padded * 6
     topk_bytes = pairs * 4 + total * k * 4   # one pass over each row's scores + index write
     idx_tflops = idx_flops / (kern["indexer"] * 1e-3) / 1e12
-    attn_gbs = attn_bytes / (kern["sparse_attn"] * 1e-3) / 1e9
+    attn_gbs = merged_bytes / (kern["sparse_attn"] * 1e-3) / 1e9
+    attn_tflops = merged_flops / (kern["sparse_attn"] * 1e-3) / 1e12
+    union_gbs = union_bytes / (kern["query_union"] * 1e-3) / 1e9
     topk_gbs = topk_bytes / (kern["topk"] * 1e-3) / 1e9
+    stats16 = {}
+    nb16, cap16 = dsa.dsa_query_union_size(total, k, 16)
+    c16 = torch.empty(nb16, dtype=torch.int32, device="cuda")
+    r16 = torch.empty((nb16, cap16), dtype=torch.int32, device="cuda")
+    m16 = torch.empty((nb16, cap16), dtype=torch.int16, device="cuda")
+    dsa.dsa_query_union(idx, dev["cu"], c16, r16, m16, 16)
+    c16 = c16.cpu().numpy()
+    for t in (8192, 32768, 65536, total - 16):
+        stats16[str(t)] = int(c16[min(t // 16, nb16 - 1)])
+    dedup = {"block_rows": ublk, "merged_rows_per_block_mean": float(counts.mean()),
+             "index_slots_per_block": ublk * k, "merged_fraction": merged / float(total * k),
+             "prefill_ms_without_dedup": no_dedup_ms, "max_abs_out_vs_per_row": float(dd_err.max()),
+             "union16_at_t": stats16, "union16_mean": float(c16.mean())}
+    del r16, m16
 
     # Parity on a handful of rows (bit-exact indices, outputs within tolerance).
     rng = np.random.default_rng(0)
@@ -218,11 +277,77 @@ def prefill_bench(args, dsa, inp, tl):
     res = dict(
         pi=pi, rows_total=total, ms_per_step=ms_per_step, sep_ms=sep_ms, kern=kern, launches=launches,
         idx_flops=idx_flops, idx_tflops=idx_tflops, attn_bytes=attn_bytes, attn_gbs=attn_gbs, topk_bytes=topk_bytes,
-        topk_gbs=topk_gbs, parity=parity, pairs=pairs, sel_pairs=sel_pairs,
+        topk_gbs=topk_gbs, parity=parity, pairs=pairs, sel_pairs=sel_pairs, merged_bytes=merged_bytes,
+        merged_flops=merged_flops, attn_tflops=attn_tflops, union_gbs=union_gbs, union_bytes=union_bytes, dedup=dedup,
     )
-    del dev, ws, scores, out, lse, idx
+    del dev, ws, scores, out, lse, idx, u_rows, u_masks
     torch.cuda.empty_cache()
     return res
+
+
+def correlated_bench(args, dsa, inp, tl):
+    """The fused prefill on the 128K workload whose neighbouring queries select overlapping sets,
+    with and without dedup (the workspace decides), plus the merged-set sizes of 16-row blocks
+    (the pages report about 8000 of 32768 at 128K on real inputs: context, not a target)."""
+    import torch
+    name = "c3q_prefill_128k_qblocks16"
+    t0 = time.time()
+    pi = inp.workload(name)
+    log(f"generated {name} inputs in {time.time() - t0:.1f}s")
+    dev = tl.upload_prefill(pi)
+    lens = [int(x) for x in pi.seq_lens]
+    total, k = sum(lens), pi.top_k
+    hq, d, hkv = pi.q.shape[1], pi.q.shape[2], pi.k.shape[1]
+    h_idx, d_idx = pi.q_idx.shape[1], pi.q_idx.shape[2]
+    max_seqlen = max(lens)
+    ld = (max_seqlen + 3) // 4 * 4
+    ws = torch.empty(dsa.dsa_prefill_workspace_size(1, total, max_seqlen, hq, hkv, d, h_idx, d_idx, k),
+                     dtype=torch.uint8, device="cuda")
+    chunk = min(total, 2048)
+    ws_chunk = ws[:(chunk * ld * 4 + 255) // 256 * 256 + dsa.dsa_topk_workspace_size(chunk, ld, k)]
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(total, hq, dtype=torch.float32, device="cuda")
+    idx = torch.empty(total, k, dtype=torch.int32, device="cuda")
+    cu = pi.cu_seqlens
+    res = {}
+    for label, w in (("with_dedup", ws), ("without_dedup", ws_chunk)):
+        dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
+                        max_seqlen, k, out, lse, idx, w)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
+                            max_seqlen, k, out, lse, idx, w)
+        torch.cuda.synchronize()
+        res[label] = (time.perf_counter() - t0) * 1e3 / args.steps
+        if label == "with_dedup":
+            out_dd = out.clone()
+    err = (out_dd.float() - out.float()).abs()
+    nb16, cap16 = dsa.dsa_query_union_size(total, k, 16)
+    c16 = torch.empty(nb16, dtype=torch.int32, device="cuda")
+    r16 = torch.empty((nb16, cap16), dtype=torch.int32, device="cuda")
+    m16 = torch.empty((nb16, cap16), dtype=torch.int16, device="cuda")
+    dsa.dsa_query_union(idx, dev["cu"], c16, r16, m16, 16)
+    c16 = c16.cpu().numpy()
+    rows = [total - 1, total // 2]
+    want = tl.oracle_prefill_rows_lazy(pi, rows)
+    sel = torch.tensor(rows, dtype=torch.int64, device="cuda")
+    o_err = np.abs(tl.bf16_tensor_to_f64(out_dd[sel]) - want["out"])
+    out_j = {"workload": f"{name}: the 128K prefill with the indexer queries of each 16-token block sharing "
+                         f"content (q_noise {pi.meta['q_noise']})",
+             "prefill_ms_with_dedup": res["with_dedup"], "prefill_ms_without_dedup": res["without_dedup"],
+             "tokens_per_s_with_dedup": total / (res["with_dedup"] * 1e-3),
+             "union16_mean": float(c16.mean()),
+             "union16_at_t": {str(t): int(c16[min(t // 16, nb16 - 1)]) for t in (8192, 32768, 65536, total - 16)},
+             "pages_union16_at_128k_real_inputs": 8000,
+             "max_abs_out_dedup_vs_per_row": float(err.max()),
+             "parity_rows": {"rows_checked": len(rows),
+                             "idx_bit_exact": bool(np.array_equal(idx[sel].cpu().numpy(), want["idx"])),
+                             "max_abs": float(o_err.max())}}
+    log(f"correlated-query prefill: {out_j}")
+    del dev, ws, out, lse, idx, r16, m16
+    torch.cuda.empty_cache()
+    return out_j
 
 
 def decode_bench(args, dsa, inp, tl):
@@ -502,6 +627,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dsa.load()
     pre = prefill_bench(args, dsa, inp, tl)
+    corr = None if args.no_correlated else correlated_bench(args, dsa, inp, tl)
     dec = None if args.no_decode else decode_bench(args, dsa, inp, tl)
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp, tl)
     wup = None if args.no_bwd else warmup_bench(args, dsa, inp, tl)
@@ -535,10 +661,18 @@ def main():
                      "traffic_unit": "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)",
                      "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
                      "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]},
-        "roofline_sparse_attn": {"bound": "hbm", "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "roofline_sparse_attn": {"bound": "hbm", "kernel": "sparse_attn_union (8-row blocks)",
+                                 "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": pre["attn_gbs"] / PEAK_HBM_GBS,
-                                 "traffic": counter_traffic("sparse_attn_kernel@prefill_128k"),
-                                 "algorithmic_bytes_per_launch": pre["attn_bytes"]},
+                                 "traffic": counter_traffic("sparse_attn_union_kernel@prefill_128k"),
+                                 "algorithmic_bytes_per_launch": pre["merged_bytes"],
+                                 "mfma_tflops": pre["attn_tflops"], "mfma_frac": pre["attn_tflops"] / PEAK_BF16_TFLOPS,
+                                 "bytes_without_dedup": pre["attn_bytes"]},
+        "roofline_query_union": {"bound": "hbm", "achieved": pre["union_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": pre["union_gbs"] / PEAK_HBM_GBS,
+                                 "algorithmic_bytes_per_launch": pre["union_bytes"]},
+        "dedup": pre["dedup"],
+        "prefill_correlated_queries": corr,
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pre["topk_gbs"] / PEAK_HBM_GBS},
         "parity_prefill": pre["parity"],

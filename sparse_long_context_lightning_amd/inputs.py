@@ -226,6 +226,10 @@ WORKLOADS = {
                            top_k=2048, seed=1, structure="iid"),
     "c3_prefill_128k": dict(kind="prefill", seq_lens=[131072], h_idx=64, d_idx=128, hq=32, hkv=4, d=128,
                             top_k=2048, seed=2, structure="blocks16"),
+    # The 128K prefill with correlated neighbouring queries: adjacent tokens' top-k sets overlap,
+    # as the pages report for real inputs (a stand-in; the pages' own statistic is context only).
+    "c3q_prefill_128k_qblocks16": dict(kind="prefill", seq_lens=[131072], h_idx=64, d_idx=128, hq=32, hkv=4,
+                                       d=128, top_k=2048, seed=2, structure="blocks16q", q_noise=0.25),
     "c4_decode_b32_128k": dict(kind="decode", batch=32, s_max=131072, h_idx=64, d_idx=128, hq=32, hkv=4,
                                d=128, top_k=2048, seed=3, structure="iid"),
     "c5_video_mix_prefill": dict(kind="prefill", seq_lens=[262144, 65536, 8192], h_idx=64, d_idx=128, hq=32,
