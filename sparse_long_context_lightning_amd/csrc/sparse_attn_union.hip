@@ -8,9 +8,10 @@
 //
 // query_union_kernel: one workgroup per block of R rows.  Entry p of row r (sequence offset
 // o, local position t) counts when 0 <= p <= t and names packed KV row o + p; bit j (row j of
-// the block) is OR-ed into a 16-bit-per-position bitmap in LDS, one window of 32768 KV rows
-// at a time, and each window is compacted in ascending order with ballots.  The list is
-// padded to a multiple of 32 entries with (the block's smallest possible KV row, mask 0).
+// the block) is OR-ed into an R-bit-per-position bitmap in LDS (128 KiB: one window of 131072
+// KV rows at R = 8, 65536 at R = 16), and each window is compacted in ascending order with
+// ballots.  The list is padded to a multiple of 32 entries with (the block's smallest possible
+// KV row, mask 0).
 //
 // sparse_attn_union_kernel: one workgroup of R / 4 waves per (block, KV group).  Per chunk of
 // 32 merged positions the workgroup DMAs the 32 key rows and 32 value rows of the group into
@@ -32,8 +33,8 @@
 namespace dsa {
 namespace {
 
-constexpr int kUnionThreads = 256;
-constexpr int kUnionWindow = 32768;  // KV rows per LDS bitmap pass (two 16-bit masks per dword)
+constexpr int kUnionThreads = 512;
+constexpr int kBitmapWords = 32768;  // 128 KiB of LDS: 4 positions per dword at 8 rows, 2 at 16
 
 __device__ __forceinline__ int seq_of_row(const int* cu, int batch, int r) {
   int lo = 0, hi = batch;  // largest s with cu[s] <= r
@@ -48,10 +49,17 @@ __device__ __forceinline__ int lanes_below(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
 }
 
+// BPP bits per position (8 for blocks of up to 8 rows, 16 for up to 16): a window covers
+// kBitmapWords * 32 / BPP KV rows.
+template <int BPP>
 __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionArgs a) {
-  __shared__ __attribute__((aligned(16))) uint32_t bm[kUnionWindow / 2];
+  constexpr int PPW = 32 / BPP;                  // positions per dword
+  constexpr int kWindow = kBitmapWords * PPW;
+  constexpr uint32_t kField = BPP == 8 ? 0xFFu : 0xFFFFu;
+  constexpr int kWaves = kUnionThreads / 64;
+  __shared__ __attribute__((aligned(16))) uint32_t bm[kBitmapWords];
   __shared__ int row_base[kMaxQueryBlock], row_t[kMaxQueryBlock];
-  __shared__ int wave_cnt[kUnionThreads / 64];
+  __shared__ int wave_cnt[kWaves];
   __shared__ int repeated;  // some row lists one position twice
   const int b = a.block_begin + blockIdx.x;
   const int r0 = b * a.block_rows;
@@ -72,50 +80,65 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
   const int span = r0 + nr - b0;       // KV rows b0 .. r0 + nr - 1
   int* out_rows = a.kv_rows + (size_t)b * a.cap;
   uint16_t* out_masks = a.masks + (size_t)b * a.cap;
-  const uint16_t* bm16 = reinterpret_cast<const uint16_t*>(bm);
-  constexpr int kSeg = kUnionWindow / (kUnionThreads / 64);  // positions per wave in a window
   int total = 0;
-  for (int w0 = 0; w0 < span; w0 += kUnionWindow) {
+  for (int w0 = 0; w0 < span; w0 += kWindow) {
     const int lo = b0 + w0;
-    const int limit = min(kUnionWindow, span - w0);
-    for (int i = tid; i < (limit + 7) / 8; i += kUnionThreads) reinterpret_cast<uint4*>(bm)[i] = uint4{0, 0, 0, 0};
+    const int limit = min(kWindow, span - w0);   // positions in this window
+    const int words = (limit + PPW - 1) / PPW;
+    for (int i = tid; i < (words + 3) / 4; i += kUnionThreads) reinterpret_cast<uint4*>(bm)[i] = uint4{0, 0, 0, 0};
     __syncthreads();
     for (int j = 0; j < nr; ++j) {
       const int* ir = a.idx + (size_t)(r0 + j) * a.k_sel;
       const int off = row_base[j] - lo, t = row_t[j];
-      const uint32_t bit = 1u << j;
-#pragma unroll 4
+#pragma unroll 8
       for (int i = tid; i < a.k_sel; i += kUnionThreads) {
         const int p = ir[i];
         const int x = off + p;
         if (p >= 0 && p <= t && x >= 0 && x < limit) {
-          const uint32_t b2 = bit << ((x & 1) << 4);
-          if (atomicOr(&bm[x >> 1], b2) & b2) repeated = 1;
+          const uint32_t bit = 1u << (BPP * (x % PPW) + j);
+          if (atomicOr(&bm[x / PPW], bit) & bit) repeated = 1;
         }
       }
     }
     __syncthreads();
-    const int s_begin = wave * kSeg, s_end = min(s_begin + kSeg, limit);
-    int c = 0;
+    // Compaction, one dword (PPW positions) per lane and step; wave w takes a contiguous share.
+    // A lane's entry count c (at most PPW) is split into bits, one ballot each, for the prefix.
+    const int per_wave = (words + kWaves - 1) / kWaves;
+    const int s_begin = wave * per_wave, s_end = min(s_begin + per_wave, words);
+    auto nz_count = [&](uint32_t wd) {
+      int c = 0;
+#pragma unroll
+      for (int f = 0; f < PPW; ++f) c += ((wd >> (BPP * f)) & kField) != 0u;
+      return c;
+    };
+    int cnt = 0;
     for (int s = s_begin; s < s_end; s += 64) {
       const int x = s + lane;
-      c += __popcll(__ballot(x < s_end && bm16[x] != 0));
+      cnt += x < s_end ? nz_count(bm[x]) : 0;
     }
-    if (lane == 0) wave_cnt[wave] = c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) wave_cnt[wave] = cnt;
     __syncthreads();
     int pos = total;
     for (int w = 0; w < wave; ++w) pos += wave_cnt[w];
-    for (int w = 0; w < kUnionThreads / 64; ++w) total += wave_cnt[w];
+    for (int w = 0; w < kWaves; ++w) total += wave_cnt[w];
     for (int s = s_begin; s < s_end; s += 64) {
       const int x = s + lane;
-      const uint32_t m = x < s_end ? bm16[x] : 0u;
-      const uint64_t bal = __ballot(m != 0u);
-      if (m != 0u) {
-        const int e = pos + lanes_below(bal);
-        out_rows[e] = lo + x;
-        out_masks[e] = (uint16_t)m;
+      const uint32_t wd = x < s_end ? bm[x] : 0u;
+      const int c = nz_count(wd);
+      const uint64_t b1 = __ballot(c & 1), b2 = __ballot(c & 2), b4 = __ballot(c & 4);
+      int e = pos + lanes_below(b1) + 2 * lanes_below(b2) + 4 * lanes_below(b4);
+#pragma unroll
+      for (int f = 0; f < PPW; ++f) {
+        const uint32_t m = (wd >> (BPP * f)) & kField;
+        if (m != 0u) {
+          out_rows[e] = lo + x * PPW + f;
+          out_masks[e] = (uint16_t)m;
+          ++e;
+        }
       }
-      pos += __popcll(bal);
+      pos += __popcll(b1) + 2 * __popcll(b2) + 4 * __popcll(b4);
     }
     __syncthreads();  // the next window clears the bitmap and rewrites wave_cnt
   }
@@ -429,7 +452,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArg
 hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s) {
   const int nb = a.block_end - a.block_begin;
   if (nb <= 0) return hipSuccess;
-  hipLaunchKernelGGL(query_union_kernel, dim3(nb), dim3(kUnionThreads), 0, s, a);
+  if (!union_block_rows_ok(a.block_rows)) return hipErrorInvalidValue;
+  if (a.block_rows <= 8)
+    hipLaunchKernelGGL(query_union_kernel<8>, dim3(nb), dim3(kUnionThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(query_union_kernel<16>, dim3(nb), dim3(kUnionThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -74,21 +74,23 @@ def test_union_lists_match_oracle_packed(dsa, repeats, block_rows):
     _check_union_blocks(counts, rows, masks, want, range(len(want)), cu, block_rows)
 
 
-def test_union_lists_match_oracle_over_several_windows(dsa):
-    # 70001 rows: the last blocks span more than two 32768-row bitmap windows, and the last
-    # block holds one row.
-    cu = [0, 70001]
+@pytest.mark.parametrize("n,block_rows", [(140001, 16), (140001, 8)])
+def test_union_lists_match_oracle_over_several_windows(dsa, n, block_rows):
+    # 140001 rows: the last blocks span more than one bitmap window (65536 KV rows at 16 rows per
+    # block, 131072 at 8), and the last block holds one row.
+    cu = [0, n]
     rng = np.random.default_rng(73)
     k = 32
     t = np.arange(cu[-1])[:, None]
     idx = (rng.random((cu[-1], k)) * (t + 1)).astype(np.int32)
     idx[rng.random(idx.shape) < 0.05] = -1
-    print("[union] one sequence of 70001 rows, k=32", flush=True)
-    counts, rows, masks = _gpu_union(dsa, idx, cu)
-    nb = (cu[-1] + 15) // 16
-    blocks = [0, 1, 2047, 2048, 2049, 4095, nb - 2, nb - 1]
-    want = orc.adjacent_query_union(idx, cu, blocks=blocks)
-    _check_union_blocks(counts, rows, masks, want, blocks, cu)
+    idx[-3:, :4] = np.arange(4)[None, :]            # positions at the start of the sequence
+    print(f"[union] one sequence of {n} rows, k=32, block_rows={block_rows}", flush=True)
+    counts, rows, masks = _gpu_union(dsa, idx, cu, block_rows)
+    nb = (cu[-1] + block_rows - 1) // block_rows
+    blocks = sorted(b for b in {0, 1, 4095, 4096, 4097, 8191, 8192, 16383, nb - 2, nb - 1} if b < nb)
+    want = orc.adjacent_query_union(idx, cu, block_rows=block_rows, blocks=blocks)
+    _check_union_blocks(counts, rows, masks, want, blocks, cu, block_rows)
 
 
 def _attn_inputs(cu, hq, hkv, seed):
