@@ -164,6 +164,7 @@ constexpr int kStageBytes = 2 * kUnionChunk * kRowBytes;  // 32 key rows, then 3
 // Chunks in the K/V ring (16 KiB each) for blocks of 16 and of 8 rows: with two waves per
 // workgroup (8 rows) a shallower ring leaves room for more workgroups per CU.
 constexpr int kStages16 = 3;
+constexpr int kUnionRun = 16;  // consecutive blocks per XCD run
 constexpr int kStages8 = 2;
 constexpr int kMetaBytes = 256;                       // positions (128 B) + masks (64 B) of a chunk
 
@@ -235,13 +236,15 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArg
   constexpr int MS = (2 * NST - 1 <= 8) ? 8 : 16;
   __shared__ __attribute__((aligned(16))) unsigned char kv_lds[NST][kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char meta_lds[MS][kMetaBytes];
-  // Workgroups are dispatched to the 8 XCDs round-robin; XCD x takes runs of 16 consecutive
-  // items (runs x, x + 8, ...), so neighbouring blocks, whose merged sets overlap, share an L2
-  // while every XCD gets an even share of long and short blocks.  KV group slowest (its
-  // gathered rows stay in the last-level cache); within a group the latest blocks, whose
-  // merged sets are the largest, start first.
+  // Workgroups are dispatched to the 8 XCDs round-robin; XCD x takes runs of RUN consecutive
+  // items (runs x, x + 8, ...).  The blocks of a run start together and scan their merged sets
+  // in ascending order at about the same pace, so a KV row several of them selected is fetched
+  // from HBM once and then hit in the XCD's L2; every XCD still gets an even share of long and
+  // short blocks.  KV group slowest (its gathered rows stay in the last-level cache); within a
+  // group the latest blocks, whose merged sets are the largest, start first.
+  constexpr int RUN = kUnionRun;
   const int xp = blockIdx.x >> 3;
-  const int wi = ((xp >> 4) * 8 + (blockIdx.x & 7)) * 16 + (xp & 15);
+  const int wi = ((xp / RUN) * 8 + (blockIdx.x & 7)) * RUN + (xp % RUN);
   if (wi >= n_blocks * a.hkv) return;
   const int g = wi / n_blocks;
   const int blk = n_blocks - 1 - (wi - g * n_blocks);
@@ -478,7 +481,7 @@ hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s) {
   if (!union_block_rows_ok(a.block_rows)) return hipErrorInvalidValue;
   const int n_blocks = (a.rows + a.block_rows - 1) / a.block_rows;
   const long long items = (long long)n_blocks * a.hkv;
-  const unsigned grid = (unsigned)((items + 127) / 128 * 128);  // whole runs of 16 on each of the 8 XCDs
+  const unsigned grid = (unsigned)((items + 8 * kUnionRun - 1) / (8 * kUnionRun) * (8 * kUnionRun));  // whole runs
   const float scale_log2 = a.softmax_scale * 1.4426950408889634f;
   switch (a.hq / a.hkv) {
     case 4: launch_union_g<4>(a, grid, scale_log2, n_blocks, s); break;
