@@ -70,6 +70,68 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Two fp32 values to one dword of bf16 (round to nearest even, lo = a): v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// 256-byte rows staged in LDS with 16-byte piece c of row r at slot c ^ swz(r), where for
+// r mod 16 = 4a + b, swz = (b << 1) | (a >> 1) | ((a & 1) << 3).  It is a permutation of 0..15,
+// so the 16 rows one row-wise MFMA operand read touches hit 16 distinct slots, and the
+// transposed reads (rows 4a + 0..3, two neighbouring pieces, two lane groups a) do as well.
+__device__ __forceinline__ int swz(int r) {
+  const int a = (r >> 2) & 3, b = r & 3;
+  return (b << 1) | (a >> 1) | ((a & 1) << 3);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
+// words that lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 address (in that order).
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
+// s_waitcnt vmcnt(N) through the builtin, so the compiler's own wait-count bookkeeping sees it
+// (after vmcnt(0) it knows its earlier loads have landed and adds no wait of its own for them).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  // vmcnt bits [3:0] and [15:14]; the lgkmcnt and expcnt fields at their maximum (no wait).
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+// Wait until at most n of this wave's vector-memory operations are outstanding (the largest
+// listed immediate <= n is used, which only ever waits longer).
+__device__ __forceinline__ void vm_wait_at_most(int n) {
+  if (n >= 32) vm_wait<32>();
+  else if (n >= 24) vm_wait<24>();
+  else if (n >= 20) vm_wait<20>();
+  else if (n >= 18) vm_wait<18>();
+  else if (n >= 16) vm_wait<16>();
+  else if (n >= 15) vm_wait<15>();
+  else if (n >= 12) vm_wait<12>();
+  else if (n >= 10) vm_wait<10>();
+  else if (n >= 9) vm_wait<9>();
+  else if (n >= 8) vm_wait<8>();
+  else if (n >= 6) vm_wait<6>();
+  else if (n >= 5) vm_wait<5>();
+  else if (n >= 4) vm_wait<4>();
+  else if (n >= 3) vm_wait<3>();
+  else if (n >= 2) vm_wait<2>();
+  else if (n >= 1) vm_wait<1>();
+  else vm_wait<0>();
+}
+// Barrier of a staging ring: this wave's LDS operations done, every wave past the point.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
 // The same copies issued from inline assembly, which the compiler does not track.  Its
 // wait-count pass cannot tell which LDS bytes a tracked copy writes, so before an LDS read that
 // might overlap (any transposed read, for one) it waits for every copy in flight, including the

@@ -31,70 +31,14 @@ namespace {
 constexpr int kBH = 64;    // indexer heads
 constexpr int kBD = 128;   // indexer dim
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 values to one dword of bf16 (round to nearest even, lo = a).
-__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
 constexpr int kRowTileBytes = 64 * 256;
 
-// Row tiles of both passes (64 keys, or one token's 64 heads), read both ways: [64 rows][256 B]
-// with piece c of row r at slot c ^ swz(r), where for r mod 16 = 4a + b,
-// swz = (b << 1) | (a >> 1) | ((a & 1) << 3).  It is a permutation of 0..15, so the 16 rows of
-// one row-wise operand read hit 16 distinct slots, and the transposed reads below (rows
-// 4a + 0..3, two neighbouring pieces, two lane groups a) hit distinct slots as well.
-__device__ __forceinline__ int swz(int r) {
-  const int a = (r >> 2) & 3, b = r & 3;
-  return (b << 1) | (a >> 1) | ((a & 1) << 3);
-}
+// Row tiles of both passes (64 keys, or one token's 64 heads) are staged with the swz layout and
+// read both ways (row-wise and transposed).
 __device__ __forceinline__ const uint16_t* swz_tile_src(const uint16_t* base, int P, int lane, int last_row) {
   const int row = 4 * P + (lane >> 4);
   const int piece = (lane & 15) ^ swz(row);
   return base + (size_t)min(row, last_row) * kBD + piece * 8;
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
-// words that lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 address (in that order).
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  return __builtin_bit_cast(uint2, v);
-}
-
-// Wait until at most n of this wave's vector-memory operations are outstanding (n is
-// wave-uniform; the largest listed immediate <= n is used, which only ever waits longer).
-// s_waitcnt vmcnt(N) through the builtin, so the compiler's wait-count bookkeeping sees it.  The
-// tile copies are issued untracked (lds_dma16_untracked): a tracked copy makes the compiler wait
-// for every copy in flight, the ring's next stage included, before each transposed LDS read.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);  // lgkmcnt and expcnt fields at their maximum: no wait
-  asm volatile("" ::: "memory");
-}
-__device__ __forceinline__ void vm_wait_at_most(int n) {
-  if (n >= 15) vm_wait<15>();
-  else if (n >= 12) vm_wait<12>();
-  else if (n >= 10) vm_wait<10>();
-  else if (n >= 9) vm_wait<9>();
-  else if (n >= 8) vm_wait<8>();
-  else if (n >= 6) vm_wait<6>();
-  else if (n >= 5) vm_wait<5>();
-  else if (n >= 4) vm_wait<4>();
-  else if (n >= 3) vm_wait<3>();
-  else if (n >= 2) vm_wait<2>();
-  else if (n >= 1) vm_wait<1>();
-  else vm_wait<0>();
-}
-// Barrier of a staging ring: this wave's LDS operations done, every wave past the point.
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
 }
 
 // ---------------------------------------------------------------------------------------

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLazyMax = 8.f;  // log2 units the softmax offset may lag the largest logit
-constexpr int kRowBytes = 128 * 2;                    // one key or value row of a group
+constexpr int kRowBytes = 128 * 2;                    // one key or value row of a group (swz layout)
 constexpr int kStageBytes = 2 * kUnionChunk * kRowBytes;  // 32 key rows, then 32 value rows
 // Chunks in the K/V ring (16 KiB each) for blocks of 16 and of 8 rows: with two waves per
 // workgroup (8 rows) a shallower ring leaves room for more workgroups per CU.
@@ -167,65 +167,6 @@ constexpr int kStages16 = 3;
 constexpr int kUnionRun = 16;  // consecutive blocks per XCD run
 constexpr int kStages8 = 2;
 constexpr int kMetaBytes = 256;                       // positions (128 B) + masks (64 B) of a chunk
-
-// Chunk rows in LDS: [32 rows][256 B], 16-byte piece c of row r at slot c ^ swz(r).  For
-// r mod 16 = 4a + b, swz = (b << 1) | (a >> 1) | ((a & 1) << 3), a permutation of 0..15: the 16
-// rows one row-wise MFMA operand read touches hit 16 distinct slots, and the transposed reads
-// (rows 4a + 0..3, two neighbouring pieces, two lane groups) do as well.
-__device__ __forceinline__ int swz(int r) {
-  const int a = (r >> 2) & 3, b = r & 3;
-  return (b << 1) | (a >> 1) | ((a & 1) << 3);
-}
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4 of the 8-byte
-// words that lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 address (in that order).
-__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
-  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-  return __builtin_bit_cast(uint2, v);
-}
-
-__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-// s_waitcnt vmcnt(N) through the builtin, so the compiler's own wait-count bookkeeping sees it
-// (after vmcnt(0) it knows its earlier loads have landed and adds no wait of its own for them).
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  // vmcnt bits [3:0] and [15:14]; the lgkmcnt and expcnt fields at their maximum (no wait).
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-  asm volatile("" ::: "memory");
-}
-// Wait until at most n of this wave's vector-memory operations are outstanding (the largest
-// listed immediate <= n is used, which only ever waits longer).
-__device__ __forceinline__ void vm_wait_at_most(int n) {
-  if (n >= 32) vm_wait<32>();
-  else if (n >= 24) vm_wait<24>();
-  else if (n >= 20) vm_wait<20>();
-  else if (n >= 18) vm_wait<18>();
-  else if (n >= 16) vm_wait<16>();
-  else if (n >= 15) vm_wait<15>();
-  else if (n >= 12) vm_wait<12>();
-  else if (n >= 10) vm_wait<10>();
-  else if (n >= 8) vm_wait<8>();
-  else if (n >= 6) vm_wait<6>();
-  else if (n >= 5) vm_wait<5>();
-  else if (n >= 4) vm_wait<4>();
-  else if (n >= 3) vm_wait<3>();
-  else if (n >= 2) vm_wait<2>();
-  else if (n >= 1) vm_wait<1>();
-  else vm_wait<0>();
-}
-__device__ __forceinline__ void ring_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-}
 
 template <int G, int NST, int NW>
 __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArgs a, float scale_log2, int n_blocks) {
