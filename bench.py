@@ -124,14 +124,14 @@ class Timer:
         self.pending, self.total, self.count = {}, {}, {}
 
 
-def prefill_bench(args, dsa, inp, tl):
+def prefill_bench(args, dsa, inp):
     import torch
     spec = inp.WORKLOADS[args.workload]
     assert spec["kind"] == "prefill"
     t0 = time.time()
     pi = inp.workload(args.workload)
     log(f"generated {args.workload} inputs in {time.time() - t0:.1f}s")
-    dev = tl.upload_prefill(pi)
+    dev = dsa.upload_prefill_inputs(pi)
     lens = [int(x) for x in pi.seq_lens]
     total = sum(lens)
     hq, d = pi.q.shape[1], pi.q.shape[2]
@@ -263,21 +263,10 @@ def prefill_bench(args, dsa, inp, tl):
              "union16_at_t": stats16, "union16_mean": float(c16.mean())}
     del r16, m16
 
-    # Parity on a handful of rows (bit-exact indices, outputs within tolerance).
-    rng = np.random.default_rng(0)
-    rows = sorted(set([0, k - 1, k, total - 1] + rng.integers(0, total, 4).tolist()))
-    want = tl.oracle_prefill_rows_lazy(pi, rows)
-    got_idx = idx.cpu().numpy()[rows]
-    idx_ok = bool(np.array_equal(got_idx, want["idx"]))
-    err = np.abs(tl.bf16_tensor_to_f64(out[rows]) - want["out"])
-    parity = {"rows_checked": len(rows), "idx_bit_exact": idx_ok, "max_abs": float(err.max()),
-              "mean_abs": float(err.mean())}
-    log(f"parity {parity}")
-
     res = dict(
         pi=pi, rows_total=total, ms_per_step=ms_per_step, sep_ms=sep_ms, kern=kern, launches=launches,
         idx_flops=idx_flops, idx_tflops=idx_tflops, attn_bytes=attn_bytes, attn_gbs=attn_gbs, topk_bytes=topk_bytes,
-        topk_gbs=topk_gbs, parity=parity, pairs=pairs, sel_pairs=sel_pairs, merged_bytes=merged_bytes,
+        topk_gbs=topk_gbs, pairs=pairs, sel_pairs=sel_pairs, merged_bytes=merged_bytes,
         merged_flops=merged_flops, attn_tflops=attn_tflops, union_gbs=union_gbs, union_bytes=union_bytes, dedup=dedup,
     )
     del dev, ws, scores, out, lse, idx, u_rows, u_masks
@@ -285,7 +274,7 @@ def prefill_bench(args, dsa, inp, tl):
     return res
 
 
-def correlated_bench(args, dsa, inp, tl):
+def correlated_bench(args, dsa, inp):
     """The fused prefill on the 128K workload whose neighbouring queries select overlapping sets,
     with and without dedup (the workspace decides), plus the merged-set sizes of 16-row blocks
     (the pages report about 8000 of 32768 at 128K on real inputs: context, not a target)."""
@@ -294,7 +283,7 @@ def correlated_bench(args, dsa, inp, tl):
     t0 = time.time()
     pi = inp.workload(name)
     log(f"generated {name} inputs in {time.time() - t0:.1f}s")
-    dev = tl.upload_prefill(pi)
+    dev = dsa.upload_prefill_inputs(pi)
     lens = [int(x) for x in pi.seq_lens]
     total, k = sum(lens), pi.top_k
     hq, d, hkv = pi.q.shape[1], pi.q.shape[2], pi.k.shape[1]
@@ -329,10 +318,6 @@ def correlated_bench(args, dsa, inp, tl):
     m16 = torch.empty((nb16, cap16), dtype=torch.int16, device="cuda")
     dsa.dsa_query_union(idx, dev["cu"], c16, r16, m16, 16)
     c16 = c16.cpu().numpy()
-    rows = [total - 1, total // 2]
-    want = tl.oracle_prefill_rows_lazy(pi, rows)
-    sel = torch.tensor(rows, dtype=torch.int64, device="cuda")
-    o_err = np.abs(tl.bf16_tensor_to_f64(out_dd[sel]) - want["out"])
     out_j = {"workload": f"{name}: the 128K prefill with the indexer queries of each 16-token block sharing "
                          f"content (q_noise {pi.meta['q_noise']})",
              "prefill_ms_with_dedup": res["with_dedup"], "prefill_ms_without_dedup": res["without_dedup"],
@@ -340,22 +325,19 @@ def correlated_bench(args, dsa, inp, tl):
              "union16_mean": float(c16.mean()),
              "union16_at_t": {str(t): int(c16[min(t // 16, nb16 - 1)]) for t in (8192, 32768, 65536, total - 16)},
              "pages_union16_at_128k_real_inputs": 8000,
-             "max_abs_out_dedup_vs_per_row": float(err.max()),
-             "parity_rows": {"rows_checked": len(rows),
-                             "idx_bit_exact": bool(np.array_equal(idx[sel].cpu().numpy(), want["idx"])),
-                             "max_abs": float(o_err.max())}}
+             "max_abs_out_dedup_vs_per_row": float(err.max())}
     log(f"correlated-query prefill: {out_j}")
     del dev, ws, out, lse, idx, r16, m16
     torch.cuda.empty_cache()
     return out_j
 
 
-def decode_bench(args, dsa, inp, tl):
+def decode_bench(args, dsa, inp):
     import torch
     t0 = time.time()
     di = inp.workload(args.decode_workload)
     log(f"generated {args.decode_workload} inputs in {time.time() - t0:.1f}s")
-    dev = tl.upload_decode(di)
+    dev = dsa.upload_decode_inputs(di)
     batch, hq, d = di.q.shape
     s_max, hkv = di.k_cache.shape[1], di.k_cache.shape[2]
     h_idx, d_idx = di.q_idx.shape[1], di.q_idx.shape[2]
@@ -390,13 +372,7 @@ def decode_bench(args, dsa, inp, tl):
     lens = di.seq_lens.astype(np.int64)
     bytes_step = int((lens * d_idx * 2).sum() + (lens * 4 * 2).sum()
                      + (np.minimum(lens, k) * (2 * hkv * d * 2 + 4)).sum() + batch * hq * d * 2 * 2)
-    brow = [0, batch - 1]
-    want = tl.oracle_decode_rows_lazy(di, brow)
-    got_idx = idx.cpu().numpy()[brow]
-    err = np.abs(tl.bf16_tensor_to_f64(out[brow]) - np.asarray(want["out"]))
-    parity = {"rows_checked": len(brow), "idx_bit_exact": bool(np.array_equal(got_idx, np.asarray(want["idx"]))),
-              "max_abs": float(err.max()), "mean_abs": float(err.mean())}
-    log(f"decode median {us_median:.1f} us (min {us_min:.1f}); parity {parity}")
+    log(f"decode median {us_median:.1f} us (min {us_min:.1f})")
 
     # The torch.topk-shaped top-k on the decode step's own scores (the first region of the decode
     # workspace, left there by the last step), beside the ascending form.
@@ -419,29 +395,33 @@ def decode_bench(args, dsa, inp, tl):
         b.record()
         torch.cuda.synchronize()
         timing[name] = a.elapsed_time(b) * 1e3 / 20
-    got_i = idx_s.cpu().numpy()[brow]
-    got_v = val_s.cpu().numpy()[brow].astype(np.float64)
+        if name == "ascending":
+            asc_i = idx_s.cpu().numpy().copy()
+    # The sorted form holds the ascending form's set, by descending value (equal values by position).
+    got_i = idx_s.cpu().numpy()
+    got_v = val_s.cpu().numpy()
     ok = True
-    for j, sc in enumerate(want["scores"]):
-        wi, wv = tl.orc.select_topk_sorted_row(sc, k)
-        ok = ok and bool(np.array_equal(got_i[j], wi) and np.array_equal(got_v[j], wv))
+    for j in range(batch):
+        order_ok = bool(np.all((got_v[j, :-1] > got_v[j, 1:]) |
+                               ((got_v[j, :-1] == got_v[j, 1:]) & (got_i[j, :-1] < got_i[j, 1:]))))
+        ok = ok and order_ok and bool(np.array_equal(np.sort(got_i[j]), asc_i[j]))
     topk_sorted = {"rows": batch, "row_len": int(lens.max()), "k": k, "us_sorted": timing["sorted"],
-                   "us_ascending": timing["ascending"], "rows_checked": len(brow), "bit_exact": ok}
+                   "us_ascending": timing["ascending"], "same_set_as_ascending_form_and_ordered": ok}
     log(f"torch.topk-shaped top-k {timing['sorted']:.1f} us (ascending form {timing['ascending']:.1f} us); "
-        f"bit-exact {ok}")
+        f"same set as the ascending form, ordered: {ok}")
     del dev, ws, tk_ws
     torch.cuda.empty_cache()
     return dict(us_median=us_median, us_min=us_min, bytes_step=bytes_step,
-                gbs=bytes_step / (us_median * 1e-6) / 1e9, parity=parity, batch=batch, s_max=s_max,
+                gbs=bytes_step / (us_median * 1e-6) / 1e9, batch=batch, s_max=s_max,
                 topk_sorted=topk_sorted)
 
 
-def attn_bwd_bench(args, dsa, inp, tl):
+def attn_bwd_bench(args, dsa, inp):
     """Backward of the sparse attention on the 32K prefill (training side), after one fused
     prefill that provides O, lse and the index sets; dO is synthetic."""
     import torch
     pi = inp.workload(args.bwd_workload)
-    dev = tl.upload_prefill(pi)
+    dev = dsa.upload_prefill_inputs(pi)
     k = pi.top_k
     out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
                                 pi.cu_seqlens, k)
@@ -484,13 +464,13 @@ def attn_bwd_bench(args, dsa, inp, tl):
             "note": "dq, dk, dv from dO; dk/dv scattered with fp32 atomics (bound by L2 atomic throughput)"}
 
 
-def warmup_bench(args, dsa, inp, tl):
+def warmup_bench(args, dsa, inp):
     """The indexer's dense warm-up step on the 32K prefill: per chunk of 2048 rows the indexer
     scores, the head-mean causal attention target, the per-row KL with its gradient, and that
     gradient's backward through the indexer (dq_idx, dw, dk_idx)."""
     import torch
     pi = inp.workload(args.bwd_workload)
-    dev = tl.upload_prefill(pi)
+    dev = dsa.upload_prefill_inputs(pi)
     lens = [int(x) for x in pi.seq_lens]
     total = sum(lens)
     hq, d = pi.q.shape[1], pi.q.shape[2]
@@ -543,49 +523,24 @@ def warmup_bench(args, dsa, inp, tl):
     pairs = sum(n * (n + 1) // 2 for n in lens)
     target_flops = 2 * pairs * 2 * hq * d          # two passes of the causal Q K^T, all heads
     bwd_flops = 3 * pairs * 2 * h_idx * d_idx      # recompute c, then u (-> dq, dw) and dk
-    # backward parity on two rows of the last chunk (whose gradient is still in `scores`)
-    c_last = (total - 1) // chunk * chunk
-    bwd_ok = True
-    for r in (total - 1, c_last + 7):
-        o = max(c for c in [int(x) for x in cu][:-1] if c <= r)
-        t = r - o
-        g_row = scores[r - c_last, :t + 1].double().cpu().numpy()
-        want_q, want_w, _ = tl.orc.index_scores_row_grad(tl.f64(pi.q_idx[r]), pi.w[r].astype(np.float64),
-                                                         tl.f64(pi.k_idx[o:o + t + 1]), g_row)
-        got_q = dq[r].double().cpu().numpy()
-        got_w = dw[r].double().cpu().numpy()
-        scale_q = max(np.abs(want_q).max(), 1e-30)
-        scale_w = max(np.abs(want_w).max(), 1e-30)
-        bwd_ok = bwd_ok and bool(np.abs(got_q - want_q).max() <= 1e-2 * scale_q) and \
-            bool(np.abs(got_w - want_w).max() <= 1e-2 * scale_w)
-    # parity on two rows
-    rows = [total // 3, total - 1]
-    cu_l = [int(x) for x in cu]
-    ok = True
-    for r in rows:
-        o = max(c for c in cu_l[:-1] if c <= r)
-        t = r - o
-        want_loss, _ = tl.orc.indexer_kl_row(
-            tl.orc.index_scores_row(tl.f64(pi.q_idx[r]), pi.w[r].astype(np.float64), tl.f64(pi.k_idx[o:o + t + 1])),
-            tl.orc.attention_head_mean_row(tl.f64(pi.q[r]), tl.f64(pi.k[o:o + t + 1]), tl.orc.default_softmax_scale(d)))
-        got = float(loss[r].item())
-        ok = ok and abs(got - want_loss) <= 1e-3 * max(1.0, abs(want_loss))
     log(f"indexer warm-up step {ms:.1f} ms per pass (target {target_ms:.1f} ms, "
         f"{target_flops / (target_ms * 1e-3) / 1e12:.0f} TFLOP/s; indexer backward {bwd_ms:.1f} ms, "
-        f"{bwd_flops / (bwd_ms * 1e-3) / 1e12:.0f} TFLOP/s); row-loss parity {ok}, backward rows {bwd_ok}")
+        f"{bwd_flops / (bwd_ms * 1e-3) / 1e12:.0f} TFLOP/s)")
     del dev, scores, probs, lse, loss, dq, dw, dk
     torch.cuda.empty_cache()
     return {"workload": args.bwd_workload, "ms": ms, "tokens_per_s": total / (ms * 1e-3), "target_ms": target_ms,
-            "target_tflops": target_flops / (target_ms * 1e-3) / 1e12, "rows_checked": len(rows), "loss_parity": ok,
+            "target_tflops": target_flops / (target_ms * 1e-3) / 1e12,
             "indexer_bwd_ms": bwd_ms, "indexer_bwd_tflops": bwd_flops / (bwd_ms * 1e-3) / 1e12,
-            "indexer_bwd_rows_parity": bwd_ok,
             "note": "indexer scores + head-mean dense attention target + per-row KL and d loss / d scores + "
                     "the indexer backward (dq_idx, dw, dk_idx); backward TFLOP/s counts 3 x 2 H_I d_I flop per "
                     "causal pair"}
 
 
-def cpu_baseline(args, pi, tl):
-    """The oracle as it stands, on a bounded sample of rows of the same workload."""
+def cpu_baseline(args, pi):
+    """The oracle as it stands, on a bounded sample of rows of the same workload (the only leg of
+    the benchmark that runs it)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import dsa_testlib as tl
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -621,17 +576,15 @@ def main():
     import torch
     import sparse_long_context_lightning_amd as dsa
     from sparse_long_context_lightning_amd import inputs as inp
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import dsa_testlib as tl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dsa.load()
-    pre = prefill_bench(args, dsa, inp, tl)
-    corr = None if args.no_correlated else correlated_bench(args, dsa, inp, tl)
-    dec = None if args.no_decode else decode_bench(args, dsa, inp, tl)
-    bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp, tl)
-    wup = None if args.no_bwd else warmup_bench(args, dsa, inp, tl)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"], tl)
+    pre = prefill_bench(args, dsa, inp)
+    corr = None if args.no_correlated else correlated_bench(args, dsa, inp)
+    dec = None if args.no_decode else decode_bench(args, dsa, inp)
+    bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp)
+    wup = None if args.no_bwd else warmup_bench(args, dsa, inp)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"])
 
     total = pre["rows_total"]
     value = total / (pre["ms_per_step"] * 1e-3)
@@ -675,7 +628,6 @@ def main():
         "prefill_correlated_queries": corr,
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": pre["topk_gbs"] / PEAK_HBM_GBS},
-        "parity_prefill": pre["parity"],
         "cpu_baseline": cpu,
     }
     if dec is not None:
@@ -684,7 +636,6 @@ def main():
         line["decode_config"] = {"workload": "decode_b32_128k: batch 32, 131072-token caches, k=2048"}
         line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": dec["gbs"] / PEAK_HBM_GBS}
-        line["parity_decode"] = dec["parity"]
         line["topk_sorted_decode_scores"] = dec["topk_sorted"]
     if bwd is not None:
         line["sparse_attn_backward"] = bwd

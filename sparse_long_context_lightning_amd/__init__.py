@@ -40,4 +40,6 @@ from ._lib import (  # noqa: F401
     load,
     prefill,
     to_device_bf16,
+    upload_decode_inputs,
+    upload_prefill_inputs,
 )

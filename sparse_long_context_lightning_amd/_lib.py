@@ -349,3 +349,28 @@ def to_device_bf16(bits: np.ndarray, device="cuda"):
     """Upload bf16 bit patterns (uint16 numpy) as a torch.bfloat16 device tensor."""
     import torch
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def upload_prefill_inputs(pi, device="cuda"):
+    """Device tensors of a prefill workload (`inputs.PrefillInputs`): q, k, v, q_idx, k_idx as
+    bf16, w as float32, cu (cu_seqlens) as int32."""
+    import torch
+    return dict(
+        q=to_device_bf16(pi.q, device), k=to_device_bf16(pi.k, device), v=to_device_bf16(pi.v, device),
+        q_idx=to_device_bf16(pi.q_idx, device), k_idx=to_device_bf16(pi.k_idx, device),
+        w=torch.from_numpy(np.ascontiguousarray(pi.w)).to(device),
+        cu=torch.from_numpy(pi.cu_seqlens).to(device),
+    )
+
+
+def upload_decode_inputs(di, device="cuda"):
+    """Device tensors of a decode workload (`inputs.DecodeInputs`): q, q_idx and the three caches
+    as bf16, w as float32, seq_lens as int32."""
+    import torch
+    return dict(
+        q=to_device_bf16(di.q, device), q_idx=to_device_bf16(di.q_idx, device),
+        w=torch.from_numpy(np.ascontiguousarray(di.w)).to(device),
+        k_cache=to_device_bf16(di.k_cache, device), v_cache=to_device_bf16(di.v_cache, device),
+        k_idx_cache=to_device_bf16(di.k_idx_cache, device),
+        seq_lens=torch.from_numpy(di.seq_lens.astype(np.int32)).to(device),
+    )

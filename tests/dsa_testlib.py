@@ -19,26 +19,13 @@ def f64(bits):
 
 
 def upload_prefill(pi, device="cuda"):
-    import torch
-    from sparse_long_context_lightning_amd import to_device_bf16
-    return dict(
-        q=to_device_bf16(pi.q, device), k=to_device_bf16(pi.k, device), v=to_device_bf16(pi.v, device),
-        q_idx=to_device_bf16(pi.q_idx, device), k_idx=to_device_bf16(pi.k_idx, device),
-        w=torch.from_numpy(np.ascontiguousarray(pi.w)).to(device),
-        cu=torch.from_numpy(pi.cu_seqlens).to(device),
-    )
+    from sparse_long_context_lightning_amd import upload_prefill_inputs
+    return upload_prefill_inputs(pi, device)
 
 
 def upload_decode(di, device="cuda"):
-    import torch
-    from sparse_long_context_lightning_amd import to_device_bf16
-    return dict(
-        q=to_device_bf16(di.q, device), q_idx=to_device_bf16(di.q_idx, device),
-        w=torch.from_numpy(np.ascontiguousarray(di.w)).to(device),
-        k_cache=to_device_bf16(di.k_cache, device), v_cache=to_device_bf16(di.v_cache, device),
-        k_idx_cache=to_device_bf16(di.k_idx_cache, device),
-        seq_lens=torch.from_numpy(di.seq_lens.astype(np.int32)).to(device),
-    )
+    from sparse_long_context_lightning_amd import upload_decode_inputs
+    return upload_decode_inputs(di, device)
 
 
 def bf16_tensor_to_f64(t):
