@@ -1,6 +1,6 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-bwd] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-bwd] [--no-dense] [--no-cpu-baseline]
 
 A step is one pass of the whole prefill path (indexer -> top-k -> sparse GQA attention) over
 the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexer heads of
@@ -11,10 +11,11 @@ every kernel, which gives the per-kernel times (and the rooflines) beside it.  T
 step runs with adjacent-query dedup (merged index sets of 8-row blocks); the fused call is also
 timed with a workspace too small for the merged sets, which attends per row.  The same prefill
 on inputs whose neighbouring queries select overlapping sets follows (with and without dedup).
-The decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, then
-the torch.topk-shaped top-k on the decode scores, the backward of the sparse attention and the
-indexer's warm-up step (target, KL and the indexer backward) on the 32K prefill (context lines
-beside the headline value).
+The decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, eagerly
+and captured in a HIP graph, then the torch.topk-shaped top-k on the decode scores, the backward
+of the sparse attention and the indexer's warm-up step (target, KL and the indexer backward) on
+the 32K prefill, and dense causal GQA attention on the prefill and decode shapes through torch's
+fused SDPA (context lines beside the headline value).
 
 One JSON line is printed last.
 """
@@ -72,6 +73,7 @@ def parse():
     ap.add_argument("--bwd-workload", default="c2_prefill_32k")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention context line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration) and exit")
@@ -374,6 +376,36 @@ def decode_bench(args, dsa, inp):
                      + (np.minimum(lens, k) * (2 * hkv * d * 2 + 4)).sum() + batch * hq * d * 2 * 2)
     log(f"decode median {us_median:.1f} us (min {us_min:.1f})")
 
+    # The same step captured once in a HIP graph and replayed: no host launch work per step.
+    eager = (out.clone(), lse.clone(), idx.clone())
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    gevs = []
+    for _ in range(n_iter):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        gevs.append((a, b))
+    torch.cuda.synchronize()
+    gtimes = sorted(a.elapsed_time(b) * 1e3 for a, b in gevs)
+    graph_same = bool(torch.equal(out, eager[0]) and torch.equal(lse, eager[1]) and torch.equal(idx, eager[2]))
+    graph_us = {"median": gtimes[len(gtimes) // 2], "min": gtimes[0], "same_outputs_as_eager": graph_same}
+    log(f"decode in a HIP graph: median {graph_us['median']:.1f} us (min {graph_us['min']:.1f}); "
+        f"outputs equal to the eager call: {graph_same}")
+    del graph
+
     # The torch.topk-shaped top-k on the decode step's own scores (the first region of the decode
     # workspace, left there by the last step), beside the ascending form.
     ld = (s_max + 3) // 4 * 4
@@ -411,7 +443,7 @@ def decode_bench(args, dsa, inp):
         f"same set as the ascending form, ordered: {ok}")
     del dev, ws, tk_ws
     torch.cuda.empty_cache()
-    return dict(us_median=us_median, us_min=us_min, bytes_step=bytes_step,
+    return dict(us_median=us_median, us_min=us_min, graph_us=graph_us, bytes_step=bytes_step,
                 gbs=bytes_step / (us_median * 1e-6) / 1e9, batch=batch, s_max=s_max,
                 topk_sorted=topk_sorted)
 
@@ -536,6 +568,99 @@ def warmup_bench(args, dsa, inp):
                     "causal pair"}
 
 
+def _sdpa_first_backend(torch, fn):
+    """Run fn under the first fused SDPA backend that accepts it (flash, then memory-efficient;
+    never the math backend, which would materialise the score matrix).  Returns (name, result)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION), ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        try:
+            with sdpa_kernel([backend]):
+                res = fn()
+            torch.cuda.synchronize()
+            return name, res
+        except RuntimeError as e:
+            log(f"torch SDPA backend {name} refused: {str(e).splitlines()[0][:160]}")
+    return None, None
+
+
+def dense_bench(args, dsa, inp, dsa_prefill_ms, dsa_decode_us):
+    """Dense causal GQA attention on the same shapes through torch's fused SDPA (context for the
+    sparse path's ratio to full attention; not a path of this library)."""
+    import math
+    import torch
+    import torch.nn.functional as F
+
+    def timed_ms(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    res = {"what": "torch.nn.functional.scaled_dot_product_attention on the benchmark shapes (K/V heads "
+                   "repeated per query head in prefill; the query heads of a group as query rows in decode)"}
+    pi = inp.workload(args.workload)
+    q = dsa.to_device_bf16(pi.q)
+    total, hq, d = q.shape
+    hkv = pi.k.shape[1]
+    grp = hq // hkv
+    scale = 1.0 / math.sqrt(d)
+    qh = q.permute(1, 0, 2).unsqueeze(0).contiguous()
+    kh = dsa.to_device_bf16(pi.k).permute(1, 0, 2).repeat_interleave(grp, dim=0).unsqueeze(0).contiguous()
+    vh = dsa.to_device_bf16(pi.v).permute(1, 0, 2).repeat_interleave(grp, dim=0).unsqueeze(0).contiguous()
+    fn = lambda: F.scaled_dot_product_attention(qh, kh, vh, is_causal=True, scale=scale)  # noqa: E731
+    backend, o = _sdpa_first_backend(torch, fn)
+    if backend is not None:
+        # Cross-check on the rows whose top-k keeps every position (t < k): there the sparse
+        # attention is the dense one.
+        k_sel = pi.top_k
+        n = min(k_sel, total)
+        pos = torch.arange(k_sel, dtype=torch.int32, device="cuda")
+        idx = torch.where(pos[None, :] <= pos[:n, None], pos[None, :], torch.full_like(pos[None, :], -1))
+        cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        o_sp = torch.empty((n, hq, d), dtype=torch.bfloat16, device="cuda")
+        dsa.dsa_sparse_gqa_attn(q[:n].contiguous(), dsa.to_device_bf16(pi.k[:n]), dsa.to_device_bf16(pi.v[:n]),
+                                idx.contiguous(), cu, o_sp, softmax_scale=scale)
+        o_dense = o[0].permute(1, 0, 2)[:n].float()
+        ms = timed_ms(fn, 3)
+        causal_flops = 4.0 * hq * d * total * (total + 1) / 2
+        floor_ms = causal_flops / (PEAK_BF16_TFLOPS * 1e12) * 1e3
+        res["prefill"] = {"backend": backend, "ms": ms, "tflops": causal_flops / (ms * 1e-3) / 1e12,
+                          "dsa_prefill_over_dense": dsa_prefill_ms / ms,
+                          "dense_floor_ms_at_bf16_peak": floor_ms,
+                          "dsa_prefill_over_dense_floor": dsa_prefill_ms / floor_ms,
+                          "max_abs_vs_sparse_attn_all_positions_rows_below_k": float((o_dense - o_sp.float()).abs().max())}
+        log(f"dense prefill ({backend}): {ms:.1f} ms; DSA prefill / dense = {dsa_prefill_ms / ms:.3f}")
+    del q, qh, kh, vh, o
+    torch.cuda.empty_cache()
+
+    if dsa_decode_us is not None:
+        di = inp.workload(args.decode_workload)
+        batch, s_max = di.k_cache.shape[0], di.k_cache.shape[1]
+        qd = dsa.to_device_bf16(di.q).view(batch, hkv, grp, d)
+        kd = dsa.to_device_bf16(di.k_cache).permute(0, 2, 1, 3).contiguous()
+        vd = dsa.to_device_bf16(di.v_cache).permute(0, 2, 1, 3).contiguous()
+        fn = lambda: F.scaled_dot_product_attention(qd, kd, vd, scale=scale)  # noqa: E731
+        backend, _ = _sdpa_first_backend(torch, fn)
+        if backend is not None:
+            us = timed_ms(fn, 20) * 1e3
+            nbytes = 2 * kd.numel() * 2
+            floor_us = nbytes / (PEAK_HBM_GBS * 1e9) * 1e6
+            res["decode"] = {"backend": backend, "us": us, "gbs": nbytes / (us * 1e-6) / 1e9,
+                             "dsa_decode_over_dense": dsa_decode_us / us,
+                             "dense_floor_us_at_hbm_peak": floor_us,
+                             "dsa_decode_over_dense_floor": dsa_decode_us / floor_us}
+            log(f"dense decode ({backend}): {us:.1f} us; DSA decode / dense = {dsa_decode_us / us:.3f}")
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(args, pi):
     """The oracle as it stands, on a bounded sample of rows of the same workload (the only leg of
     the benchmark that runs it)."""
@@ -584,6 +709,8 @@ def main():
     dec = None if args.no_decode else decode_bench(args, dsa, inp)
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp)
     wup = None if args.no_bwd else warmup_bench(args, dsa, inp)
+    dense = None if args.no_dense else dense_bench(args, dsa, inp, pre["ms_per_step"],
+                                                   None if dec is None else dec["us_median"])
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"])
 
     total = pre["rows_total"]
@@ -633,6 +760,7 @@ def main():
     if dec is not None:
         line["decode_us_per_step"] = dec["us_median"]
         line["decode_us_min"] = dec["us_min"]
+        line["decode_us_per_step_hip_graph"] = dec["graph_us"]
         line["decode_config"] = {"workload": "decode_b32_128k: batch 32, 131072-token caches, k=2048"}
         line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                    "frac": dec["gbs"] / PEAK_HBM_GBS}
@@ -641,6 +769,8 @@ def main():
         line["sparse_attn_backward"] = bwd
     if wup is not None:
         line["indexer_warmup_objective"] = wup
+    if dense is not None:
+        line["dense_attention_context"] = dense
     print(json.dumps(line), flush=True)
 
 
