@@ -568,6 +568,44 @@ def warmup_bench(args, dsa, inp):
                     "causal pair"}
 
 
+def measured_peaks(dsa):
+    """What the box reaches on the two priced resources (the library's probe kernels): an
+    MFMA-only loop of 16x16x32 and of 32x32x16 bf16 instructions, and a streaming read of 4 GiB.
+    Best of several timed launches each."""
+    import torch
+
+    def best_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        out = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b))
+        return min(out)
+
+    grid, iters = 2048, 20000
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+    res = {}
+    for shape in (16, 32):
+        flops = dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink)
+        ms = best_ms(lambda: dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink), 5)
+        res[f"mfma_bf16_{shape}x{shape}x{512 // shape}_tflops"] = flops / (ms * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    best = {g: buf.numel() / (best_ms(lambda: dsa.dsa_probe_stream_read(buf, g, sink), 6) * 1e-3) / 1e9
+            for g in (2048, 8192, 16384, 32768, 65536)}
+    res["stream_read_gbs"] = max(best.values())
+    res["stream_read_gbs_by_grid"] = best
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"measured peaks: {res}")
+    return res
+
+
 def _sdpa_first_backend(torch, fn):
     """Run fn under the first fused SDPA backend that accepts it (flash, then memory-efficient;
     never the math backend, which would materialise the score matrix).  Returns (name, result)."""
@@ -705,6 +743,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dsa.load()
     pre = prefill_bench(args, dsa, inp)
+    peaks = measured_peaks(dsa)
     corr = None if args.no_correlated else correlated_bench(args, dsa, inp)
     dec = None if args.no_decode else decode_bench(args, dsa, inp)
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp)
@@ -740,10 +779,14 @@ def main():
                      "traffic": counter_traffic("indexer_prefill_kernel@prefill_128k"),
                      "traffic_unit": "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)",
                      "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
+                     "measured_peak": peaks["mfma_bf16_16x16x32_tflops"],
+                     "frac_of_measured_peak": pre["idx_tflops"] / peaks["mfma_bf16_16x16x32_tflops"],
                      "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]},
         "roofline_sparse_attn": {"bound": "hbm", "kernel": "sparse_attn_union (8-row blocks)",
                                  "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": pre["attn_gbs"] / PEAK_HBM_GBS,
+                                 "measured_peak": peaks["stream_read_gbs"],
+                                 "frac_of_measured_peak": pre["attn_gbs"] / peaks["stream_read_gbs"],
                                  "traffic": counter_traffic("sparse_attn_union_kernel@prefill_128k"),
                                  "algorithmic_bytes_per_launch": pre["merged_bytes"],
                                  "mfma_tflops": pre["attn_tflops"], "mfma_frac": pre["attn_tflops"] / PEAK_BF16_TFLOPS,
@@ -751,6 +794,7 @@ def main():
         "roofline_query_union": {"bound": "hbm", "achieved": pre["union_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": pre["union_gbs"] / PEAK_HBM_GBS,
                                  "algorithmic_bytes_per_launch": pre["union_bytes"]},
+        "measured_peaks": peaks,
         "dedup": pre["dedup"],
         "prefill_correlated_queries": corr,
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -763,7 +807,8 @@ def main():
         line["decode_us_per_step_hip_graph"] = dec["graph_us"]
         line["decode_config"] = {"workload": "decode_b32_128k: batch 32, 131072-token caches, k=2048"}
         line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": dec["gbs"] / PEAK_HBM_GBS}
+                                   "frac": dec["gbs"] / PEAK_HBM_GBS,
+                                   "frac_of_measured_peak": dec["gbs"] / peaks["stream_read_gbs"]}
         line["topk_sorted_decode_scores"] = dec["topk_sorted"]
     if bwd is not None:
         line["sparse_attn_backward"] = bwd

@@ -340,6 +340,26 @@ int dsa_decode(const void* q, const void* q_idx, const float* w,
                float softmax_scale, void* out, float* lse, int32_t* idx_out,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement probes.  They compute nothing of the method: they measure what the device
+ * reaches on the two resources the path's kernels are priced against, so that a kernel's
+ * fraction of a spec peak can be read beside its fraction of an achievable one.
+ *
+ * dsa_probe_mfma_bf16: `grid` workgroups of four waves, each running `iters` iterations of
+ *     eight independent 16x16x32 (shape 16, the prefill indexer's instruction) or four
+ *     32x32x16 (shape 32) bf16 MFMA chains with operands in registers.  sink [grid] float
+ *     (device) is written only in a case the probe never produces.  *flops (host, may be NULL)
+ *     receives the floating-point operations one call executes.  Errors: DSA_ERR_INVALID_ARG
+ *     (shape not 16 or 32, grid outside [1, 2^20], iters < 1, null sink), DSA_ERR_HIP.
+ * dsa_probe_stream_read: reads `bytes` of src (device, 16-byte aligned, a positive multiple of
+ *     16 bytes) once with 16-byte loads from `grid` workgroups of 256 threads, grid-stride;
+ *     sink [grid] uint32 (device) is written only in a case the probe never produces.  Errors:
+ *     DSA_ERR_INVALID_ARG, DSA_ERR_HIP.
+ * Both only enqueue work on `stream`; time them with events on that stream.
+ */
+int dsa_probe_mfma_bf16(int shape, int grid, int iters, float* sink, long long* flops, void* stream);
+int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,8 @@ from ._lib import (  # noqa: F401
     dsa_last_error,
     dsa_prefill,
     dsa_prefill_workspace_size,
+    dsa_probe_mfma_bf16,
+    dsa_probe_stream_read,
     dsa_query_union,
     dsa_query_union_size,
     dsa_sparse_gqa_attn,

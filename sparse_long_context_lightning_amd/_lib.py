@@ -28,7 +28,8 @@ EXPORTED = (
     "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
     "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean", "dsa_indexer_kl",
     "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union", "dsa_sparse_gqa_attn_union",
-    "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
+    "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup", "dsa_probe_mfma_bf16",
+    "dsa_probe_stream_read",
 )
 
 
@@ -80,6 +81,8 @@ def load():
         "dsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                         _P], _I),
+        "dsa_probe_mfma_bf16": ([_I, _I, _I, _P, ctypes.POINTER(ctypes.c_longlong), _P], _I),
+        "dsa_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -374,3 +377,16 @@ def upload_decode_inputs(di, device="cuda"):
         k_idx_cache=to_device_bf16(di.k_idx_cache, device),
         seq_lens=torch.from_numpy(di.seq_lens.astype(np.int32)).to(device),
     )
+
+
+def dsa_probe_mfma_bf16(shape, grid, iters, sink, stream=None) -> int:
+    """Enqueue the MFMA-only probe; returns the flops it executes."""
+    flops = ctypes.c_longlong(0)
+    _check(load().dsa_probe_mfma_bf16(shape, grid, iters, _ptr(sink), ctypes.byref(flops), _stream(stream)))
+    return flops.value
+
+
+def dsa_probe_stream_read(src, grid, sink, stream=None):
+    """Enqueue the streaming-read probe over the whole of `src`."""
+    _check(load().dsa_probe_stream_read(_ptr(src), src.numel() * src.element_size(), grid, _ptr(sink),
+                                        _stream(stream)))

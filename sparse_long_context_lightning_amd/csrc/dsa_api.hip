@@ -878,4 +878,21 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   return hip_status(dsa::launch_attn_combine(a, s), "combine launch");
 }
 
+int dsa_probe_mfma_bf16(int shape, int grid, int iters, float* sink, long long* flops, void* stream) {
+  if (shape != 16 && shape != 32) return fail(DSA_ERR_INVALID_ARG, "probe shape must be 16 or 32, got %d", shape);
+  if (grid < 1 || grid > (1 << 20) || iters < 1) return fail(DSA_ERR_INVALID_ARG, "probe grid / iters out of range");
+  if (!sink) return fail(DSA_ERR_INVALID_ARG, "probe sink is null");
+  if (flops) *flops = dsa::peak_mfma_flops(shape, grid, iters);
+  return hip_status(dsa::launch_peak_mfma(shape, grid, iters, sink, static_cast<hipStream_t>(stream)), "probe launch");
+}
+
+int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream) {
+  if (!src || !sink) return fail(DSA_ERR_INVALID_ARG, "probe pointers must not be null");
+  if (!aligned16(src) || bytes % 16 != 0 || bytes == 0)
+    return fail(DSA_ERR_INVALID_ARG, "probe source must be 16-byte aligned with a positive multiple of 16 bytes");
+  if (grid < 1 || grid > (1 << 20)) return fail(DSA_ERR_INVALID_ARG, "probe grid out of range");
+  return hip_status(dsa::launch_peak_stream_read(src, (long long)bytes, grid, sink, static_cast<hipStream_t>(stream)),
+                    "probe launch");
+}
+
 }  // extern "C"

@@ -181,4 +181,10 @@ hipError_t launch_attn_combine(const SparseAttnArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn_bwd(const SparseAttnBwdArgs& a, hipStream_t s);
 hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s);
 
+// Achievable-peak probes (no part of the method): an MFMA-only loop of 16x16x32 (shape 16) or
+// 32x32x16 (shape 32) bf16 instructions, and a streaming read of `bytes` (a multiple of 16).
+hipError_t launch_peak_mfma(int shape, int grid, int iters, float* sink, hipStream_t s);
+long long peak_mfma_flops(int shape, int grid, int iters);
+hipError_t launch_peak_stream_read(const void* src, long long bytes, int grid, unsigned* sink, hipStream_t s);
+
 }  // namespace dsa

@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 21
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -109,6 +109,20 @@ def test_other_entry_points_reject_bad_arguments():
     args2 = list(args)
     args2[9] = 1001  # max_seq_len > s_max
     assert lib.dsa_decode(*args2) == dsa.DSA_ERR_INVALID_ARG
+
+
+def test_probe_validation():
+    lib = dsa.load()
+    flops = ctypes.c_longlong(0)
+    assert lib.dsa_probe_mfma_bf16(8, 64, 10, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_mfma_bf16(16, 0, 10, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_mfma_bf16(16, 64, 0, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_mfma_bf16(32, 64, 10, None, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_stream_read(MISALIGNED, 1 << 20, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_stream_read(FAKE, (1 << 20) + 8, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_stream_read(FAKE, 0, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 0, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 64, None, None) == dsa.DSA_ERR_INVALID_ARG
 
 
 def test_query_union_validation():
