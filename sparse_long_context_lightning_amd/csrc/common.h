@@ -148,6 +148,12 @@ __device__ __forceinline__ void lds_dma16_untracked(const void* g, void* lds_wav
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
+// Scalar-base form: the wave-uniform 64-bit base in SGPRs, a 32-bit per-lane byte offset, and
+// the LDS destination (wave-uniform) already in an SGPR, so no vector address arithmetic runs.
+__device__ __forceinline__ void lds_dma16_saddr(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_dma4_untracked(const void* g, void* lds_wave_base) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_offset(lds_wave_base));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(base) : "memory", "m0");

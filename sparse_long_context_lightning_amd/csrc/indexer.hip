@@ -113,26 +113,36 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   // Tile staging: instruction p of wave w fills LDS bytes [p*4096 + w*1024, +1024) of the
   // tile, lane l the 16 bytes at + 16 l, i.e. row r = (p*4096 + w*1024 + 16 l) / PITCH, slot
   // l % CPR, which holds the row's chunk (l % CPR) ^ (r % CPR).  Full tiles use fixed
-  // per-thread offsets from a tile base that advances uniformly; only the last, partial tile
-  // clamps its rows to the key range.
-  const uint16_t* ktile = k_idx + (size_t)(seq_off + kbeg) * DI;
-  int st_row[NLD], st_off[NLD];
+  // per-thread byte offsets from a tile base that advances uniformly (kept in scalar registers,
+  // as are the LDS destinations, so a copy costs no vector instruction); only the last, partial
+  // tile clamps its rows to the key range.
+  const char* ktile = reinterpret_cast<const char*>(k_idx + (size_t)(seq_off + kbeg) * DI);
+  int st_row[NLD];
+  uint32_t st_off[NLD];      // byte offset of the lane's 16 bytes within a tile
+  uint32_t lds_dst[2][NLD];  // wave-uniform LDS destinations
 #pragma unroll
   for (int p = 0; p < NLD; ++p) {
     const int pos = p * 4096 + wave * 1024 + lane * 16;
     const int r = pos / PITCH;
     const int chunk = (lane % CPR) ^ (r % CPR);
     st_row[p] = r;
-    st_off[p] = r * DI + chunk * 8;  // elements
+    st_off[p] = (uint32_t)(r * DI + chunk * 8) * 2u;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      lds_dst[b][p] = __builtin_amdgcn_readfirstlane(lds_offset(&lds[b][p * 4096 + wave * 1024]));
   }
   auto load_tile = [&](int tile, int buf) {
-    const uint16_t* base = ktile + (size_t)tile * 64 * DI;
+    const char* base = ktile + (size_t)tile * 64 * DI * 2;
     const int keys_left = kend - kbeg - tile * 64;
+    if (keys_left >= 64) {
 #pragma unroll
-    for (int p = 0; p < NLD; ++p) {
-      const uint16_t* g = base + st_off[p];
-      if (keys_left < 64) g = base + min(st_row[p], keys_left - 1) * DI + (st_off[p] - st_row[p] * DI);
-      lds_dma16(g, &lds[buf][p * 4096 + wave * 1024]);
+      for (int p = 0; p < NLD; ++p) lds_dma16_saddr(base, st_off[p], buf ? lds_dst[1][p] : lds_dst[0][p]);
+    } else {
+#pragma unroll
+      for (int p = 0; p < NLD; ++p) {
+        const uint32_t off = st_off[p] - (uint32_t)(st_row[p] - min(st_row[p], keys_left - 1)) * (uint32_t)(DI * 2);
+        lds_dma16_saddr(base, off, buf ? lds_dst[1][p] : lds_dst[0][p]);
+      }
     }
   };
   auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
