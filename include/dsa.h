@@ -234,7 +234,8 @@ int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, in
  * counts, kv_rows, masks, block_rows, cap   as dsa_query_union wrote them (KV rows outside
  *                                   [0, total_tokens) are clamped into it, counts above cap read
  *                                   as cap, so no access leaves the buffers)
- * Supports hq / hkv in {4, 8, 16} (DSA_ERR_UNSUPPORTED otherwise).  Needs no workspace.
+ * Supports hq / hkv in {4, 8, 16} and total_tokens * hkv < 2^24 (K and V rows are addressed
+ * with 32-bit byte offsets; DSA_ERR_UNSUPPORTED otherwise).  Needs no workspace.
  */
 int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const int32_t* counts,
                               const int32_t* kv_rows, const uint16_t* masks, int block_rows, int cap,
@@ -246,8 +247,9 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
  * rounding), with the same arguments plus a workspace.  The call builds the merged sets of every
  * block of 8 rows (dsa_query_union) in the workspace and attends each block from its merged set
  * (dsa_sparse_gqa_attn_union), except blocks in which a row lists a position twice, which are
- * attended per row (so that the repeat counts as dsa_sparse_gqa_attn counts it).  For hq / hkv outside {4, 8, 16} the workspace size is 0 and the call is
- * dsa_sparse_gqa_attn.
+ * attended per row (so that the repeat counts as dsa_sparse_gqa_attn counts it).  Where
+ * dsa_sparse_gqa_attn_union does not apply (hq / hkv outside {4, 8, 16}, or total_tokens * hkv
+ * >= 2^24) the workspace size is 0 and the call is dsa_sparse_gqa_attn.
  *
  * workspace  device buffer of at least dsa_sparse_gqa_attn_dedup_workspace_size bytes, 16-byte
  *            aligned (DSA_ERR_WORKSPACE if smaller); its contents on return are unspecified.

@@ -542,8 +542,9 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
     return fail(DSA_ERR_INVALID_ARG, "cap %d must be a positive multiple of %d", cap, dsa::kUnionChunk);
   if (!dsa::union_block_rows_ok(block_rows)) return fail(DSA_ERR_UNSUPPORTED, "block_rows %d is not 8 or 16", block_rows);
   DSA_TRY(check_attn_shape(hq, hkv, head_dim));
-  if (!dsa::union_attn_supported(hq, hkv))
-    return fail(DSA_ERR_UNSUPPORTED, "merged-set attention supports hq / hkv in {4, 8, 16} (got %d)", hq / hkv);
+  if (!dsa::union_attn_supported(hq, hkv, total_tokens))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "merged-set attention supports hq / hkv in {4, 8, 16} (got %d) and total_tokens * hkv < 2^24", hq / hkv);
   if (total_tokens == 0) return DSA_OK;
   dsa::UnionAttnArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
@@ -568,7 +569,7 @@ int dsa_sparse_gqa_attn_dedup_workspace_size(int total_tokens, int k_sel, int hq
   DSA_NONNULL(bytes);
   if (total_tokens < 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens >= 0 and k_sel > 0 required");
   if (k_sel > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "k_sel %d too large", k_sel);
-  *bytes = dsa::union_attn_supported(hq, hkv) ? union_layout(total_tokens, k_sel).bytes : 0;
+  *bytes = dsa::union_attn_supported(hq, hkv, total_tokens) ? union_layout(total_tokens, k_sel).bytes : 0;
   return DSA_OK;
 }
 
@@ -678,7 +679,7 @@ int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int 
   const long long ld = round_up(std::max(max_seqlen, 1), 4);
   const int rows = std::max(1, std::min(total_tokens, kDefaultChunkRows));
   // The dedup attention's merged sets use the same memory once the chunk loop is over.
-  const size_t dedup = dsa::union_attn_supported(hq, hkv) ? union_layout(total_tokens, top_k).bytes : 0;
+  const size_t dedup = dsa::union_attn_supported(hq, hkv, total_tokens) ? union_layout(total_tokens, top_k).bytes : 0;
   *bytes = std::max(prefill_chunk_bytes(rows, ld), dedup);
   return DSA_OK;
 }
@@ -766,7 +767,7 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
   a.nsplit = 1;
   // With room for the merged sets (they reuse the chunk memory, no longer needed), the attention
   // runs with adjacent-query dedup; otherwise per row.
-  if (dsa::union_attn_supported(hq, hkv) && workspace_bytes >= union_layout(total_tokens, top_k).bytes)
+  if (dsa::union_attn_supported(hq, hkv, total_tokens) && workspace_bytes >= union_layout(total_tokens, top_k).bytes)
     return hip_status(launch_attn_dedup(a, workspace, s), "dedup attention launch");
   return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
 }

@@ -162,7 +162,7 @@ struct UnionAttnArgs {
 };
 hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s);
 // The union attention handles G = hq / hkv in {4, 8, 16}.
-bool union_attn_supported(int hq, int hkv);
+bool union_attn_supported(int hq, int hkv, long long rows);
 hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s);
 
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);

@@ -254,8 +254,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArg
     for (int i = 0; i < 8 / NW; ++i) {
       const int j = wave + i * NW;
       const int piece = (lane & 15) ^ swz(4 * j + (lane >> 4));
-      lds_dma16_untracked(kg + (size_t)pr[i] * row_stride + piece * 8, buf + (4 * j) * kRowBytes);
-      lds_dma16_untracked(vg + (size_t)pr[i] * row_stride + piece * 8, buf + (32 + 4 * j) * kRowBytes);
+      const uint32_t off = (uint32_t)pr[i] * (uint32_t)(row_stride * 2) + (uint32_t)piece * 16u;
+      lds_dma16_saddr(kg, off, __builtin_amdgcn_readfirstlane(lds_offset(buf + (4 * j) * kRowBytes)));
+      lds_dma16_saddr(vg, off, __builtin_amdgcn_readfirstlane(lds_offset(buf + (32 + 4 * j) * kRowBytes)));
     }
     if (wave == 0 && ch + NST - 1 < nchunk) meta_dma(ch + NST - 1);
   };
@@ -404,9 +405,10 @@ hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-bool union_attn_supported(int hq, int hkv) {
+bool union_attn_supported(int hq, int hkv, long long rows) {
   const int g = hkv > 0 ? hq / hkv : 0;
-  return hkv > 0 && hq % hkv == 0 && (g == 4 || g == 8 || g == 16);
+  // K / V rows are addressed with 32-bit byte offsets from the group's base.
+  return hkv > 0 && hq % hkv == 0 && (g == 4 || g == 8 || g == 16) && rows * hkv * 256 < (1ll << 32);
 }
 
 template <int G>

@@ -173,6 +173,10 @@ def test_dedup_attention_validation():
     zero = list(base)
     zero[7] = 0
     assert lib.dsa_sparse_gqa_attn_dedup(*zero, FAKE, need, None) == dsa.DSA_OK
+    # the merged-set kernel addresses K / V with 32-bit byte offsets: total_tokens * hkv < 2^24
+    assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size((1 << 22) - 1, 64, 32, 4) > 0
+    assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(1 << 22, 64, 32, 4) == 0
+    assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(1 << 22, 64, 16, 2) > 0
 
 
 def test_zero_sized_calls_are_no_ops():
