@@ -242,7 +242,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArg
     lds_dma4_untracked(src, meta_lds[ch % MS]);
   };
   // The chunk's 32 key rows and 32 value rows go in 8 + 8 copies of 4 rows (1 KiB each); wave w
-  // issues copies w, w + NW, ...: key and value rows 4 j + lane / 16 for those j.
+  // issues copies w, w + NW, ...: key and value rows 4 j + lane / 16 for those j.  Each copy
+  // takes the group's K or V base in scalar registers and a 32-bit byte offset per lane (the
+  // host admits this kernel only for total_tokens * hkv < 2^24).
   auto stage = [&](int ch) {
     const int* pos = reinterpret_cast<const int*>(meta_lds[ch % MS]);
     unsigned char* buf = kv_lds[ch % NST];
