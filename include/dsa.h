@@ -39,6 +39,8 @@
  *     Every bf16/float pointer must be 16-byte aligned.
  *   - Positions are sequence-local.  Selected positions that lie outside the causal prefix
  *     [0, t] (or outside [0, seq_len) in decode) are ignored by the attention calls.
+ *   - With DSA_LOG=1 in the environment every entry point logs its call (name and sizes) and
+ *     every rejected call its reason, one line each on stderr.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -87,6 +89,26 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w,
                      const int32_t* cu_seqlens_host, int batch, int total_tokens,
                      int h_idx, int d_idx, int row_begin, int row_count,
                      float* scores, int64_t ld, void* stream);
+
+/*
+ * Lightning-indexer scores of one new token per sequence against its cached keys (the decode
+ * form of dsa_index_scores; digest section 一 for the indexer, section 八 for DSA-specific decode).
+ *
+ * q_idx   [batch, h_idx, d_idx] bf16       indexer query of each sequence's new token
+ * w       [batch, h_idx]        float      its per-head weights
+ * k_idx_cache [batch, s_max, d_idx] bf16   cached indexer keys; sequence b uses rows 0 .. seq_lens[b]-1
+ * seq_lens [batch] int32 (device)          cache length of each sequence, including the new token;
+ *                                          1 <= seq_lens[b] <= max_seq_len
+ * max_seq_len (host)                       upper bound of seq_lens, 1 <= max_seq_len <= s_max (sizes the launch)
+ * scores  [batch, ld]           float      output: scores[b * ld + s] = I[b, s] for 0 <= s < seq_lens[b];
+ *                                          entries at s >= seq_lens[b] are left untouched.  ld >= s_max,
+ *                                          ld % 4 == 0.
+ * Same arithmetic as dsa_index_scores, so for the same bf16 values the scores are equal bit for bit.
+ * dsa_decode runs exactly this step first, on the first batch * ld floats of its workspace.
+ */
+int dsa_decode_index_scores(const void* q_idx, const float* w, const void* k_idx_cache, const int32_t* seq_lens,
+                            int batch, int s_max, int max_seq_len, int h_idx, int d_idx, float* scores, int64_t ld,
+                            void* stream);
 
 /*
  * Backward of dsa_index_scores (digest section 一: the dense warm-up trains the indexer, which
@@ -341,26 +363,6 @@ int dsa_decode(const void* q, const void* q_idx, const float* w,
                int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
                float softmax_scale, void* out, float* lse, int32_t* idx_out,
                void* workspace, size_t workspace_bytes, void* stream);
-
-/*
- * Measurement probes.  They compute nothing of the method: they measure what the device
- * reaches on the two resources the path's kernels are priced against, so that a kernel's
- * fraction of a spec peak can be read beside its fraction of an achievable one.
- *
- * dsa_probe_mfma_bf16: `grid` workgroups of four waves, each running `iters` iterations of
- *     eight independent 16x16x32 (shape 16, the prefill indexer's instruction) or four
- *     32x32x16 (shape 32) bf16 MFMA chains with operands in registers.  sink [grid] float
- *     (device) is written only in a case the probe never produces.  *flops (host, may be NULL)
- *     receives the floating-point operations one call executes.  Errors: DSA_ERR_INVALID_ARG
- *     (shape not 16 or 32, grid outside [1, 2^20], iters < 1, null sink), DSA_ERR_HIP.
- * dsa_probe_stream_read: reads `bytes` of src (device, 16-byte aligned, a positive multiple of
- *     16 bytes) once with 16-byte loads from `grid` workgroups of 256 threads, grid-stride;
- *     sink [grid] uint32 (device) is written only in a case the probe never produces.  Errors:
- *     DSA_ERR_INVALID_ARG, DSA_ERR_HIP.
- * Both only enqueue work on `stream`; time them with events on that stream.
- */
-int dsa_probe_mfma_bf16(int shape, int grid, int iters, float* sink, long long* flops, void* stream);
-int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

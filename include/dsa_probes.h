@@ -1,0 +1,64 @@
+/*
+ * dsa_probes.h - measurement probes for MI355X, built as their own library (libdsa_probes.so).
+ *
+ * They compute nothing of the method.  They measure what the device reaches on the resources
+ * the DSA path's kernels are priced against (bf16 MFMA issue, streaming HBM reads, and random
+ * 256-byte row gathers in the sparse attention's access pattern), so that a kernel's fraction of
+ * a spec peak can be read beside its fraction of an achievable one.  The benchmark is their only
+ * user; the product library (dsa.h) does not depend on them.
+ *
+ * Conventions: device pointers; `stream` is a hipStream_t (NULL = default stream); each call
+ * only enqueues work, so time it with events on that stream.  Sinks are written only in a case
+ * the probes never produce (they keep the loads live).  Errors: DSA_PROBE_ERR_INVALID_ARG (checked
+ * on the host, nothing enqueued) and DSA_PROBE_ERR_HIP (launch failed); the message of the last
+ * failing call of this host thread is in dsa_probe_last_error().
+ */
+#ifndef DSA_PROBES_H
+#define DSA_PROBES_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_PROBE_OK 0
+#define DSA_PROBE_ERR_INVALID_ARG 1
+#define DSA_PROBE_ERR_HIP 4
+
+const char* dsa_probe_last_error(void);
+
+/*
+ * `grid` workgroups of four waves, each running `iters` iterations of eight independent
+ * 16x16x32 (shape 16, the prefill indexer's instruction) or four 32x32x16 (shape 32) bf16 MFMA
+ * chains with operands in registers.  sink [grid] float.  *flops (host, may be NULL) receives
+ * the floating-point operations one call executes.  Grid in [1, 2^20], iters >= 1.
+ */
+int dsa_probe_mfma_bf16(int shape, int grid, int iters, float* sink, long long* flops, void* stream);
+
+/*
+ * Reads `bytes` of src (16-byte aligned, a positive multiple of 16) once with 16-byte loads from
+ * `grid` workgroups of 256 threads, grid-stride.  sink [grid] uint32.
+ */
+int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream);
+
+/*
+ * The memory traffic of the sparse GQA attention with no arithmetic: one wave per (row, KV
+ * group g, split) reads, for every index entry p >= 0 of its row (idx [rows, k_sel] int32, the
+ * row's entries split into nsplit ranges of 32-entry chunks), the key row and the value row
+ * k[P, g, :], v[P, g, :] with P = row * row_stride + p (256 bytes each; P >= n_pos reads row 0),
+ * with the same 16-byte loads and `depth` (1, 2 or 4) chunks of 32 entries in flight.  Work
+ * order: KV group slowest (group_fastest = 0, the prefill kernels') or fastest (the decode
+ * kernel's).  k, v [n_pos, hkv, 128] bf16, 16-byte aligned.  sink [sink_len] uint32 with
+ * sink_len >= the number of workgroups, ceil(rows * hkv * nsplit / 4) rounded up to 8.
+ */
+int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const int32_t* idx, int k_sel, int rows,
+                     int nsplit, int64_t row_stride, int group_fastest, int depth, uint32_t* sink, int64_t sink_len,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_PROBES_H */

@@ -1,7 +1,8 @@
 """DSA (lightning indexer -> top-k -> sparse GQA attention) for AMD MI355X.
 
 The compute runs in libdsa.so (hand-written HIP for gfx950) behind the C ABI declared in
-include/dsa.h; this package only binds it.  Build the library with
+include/dsa.h; this package only binds it.  The benchmark's measurement probes are a separate
+library, libdsa_probes.so (include/dsa_probes.h).  Build the library with
 `python -m sparse_long_context_lightning_amd.build`.
 """
 
@@ -14,10 +15,13 @@ from ._lib import (  # noqa: F401
     DSA_OK,
     EXPORTED,
     LIB_PATH,
+    PROBES_EXPORTED,
+    PROBES_LIB_PATH,
     DsaError,
     decode,
     dsa_abi_version,
     dsa_decode,
+    dsa_decode_index_scores,
     dsa_decode_workspace_size,
     dsa_attn_head_mean,
     dsa_index_scores,
@@ -26,6 +30,7 @@ from ._lib import (  # noqa: F401
     dsa_last_error,
     dsa_prefill,
     dsa_prefill_workspace_size,
+    dsa_probe_gather,
     dsa_probe_mfma_bf16,
     dsa_probe_stream_read,
     dsa_query_union,
@@ -40,6 +45,7 @@ from ._lib import (  # noqa: F401
     dsa_topk_sorted,
     dsa_topk_workspace_size,
     load,
+    load_probes,
     prefill,
     to_device_bf16,
     upload_decode_inputs,

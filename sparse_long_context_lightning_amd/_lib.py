@@ -15,6 +15,7 @@ import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
+PROBES_LIB_PATH = os.path.join(_PKG, "libdsa_probes.so")
 
 DSA_OK = 0
 DSA_ERR_INVALID_ARG = 1
@@ -24,13 +25,14 @@ DSA_ERR_HIP = 4
 DSA_MAX_TOP_K = 2048
 
 EXPORTED = (
-    "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_topk_workspace_size",
-    "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd", "dsa_prefill_workspace_size",
-    "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean", "dsa_indexer_kl",
-    "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union", "dsa_sparse_gqa_attn_union",
-    "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup", "dsa_probe_mfma_bf16",
-    "dsa_probe_stream_read",
+    "dsa_abi_version", "dsa_status_string", "dsa_last_error", "dsa_index_scores", "dsa_decode_index_scores",
+    "dsa_topk_workspace_size", "dsa_topk", "dsa_topk_sorted", "dsa_sparse_gqa_attn", "dsa_sparse_gqa_attn_bwd",
+    "dsa_prefill_workspace_size", "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean",
+    "dsa_indexer_kl", "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union",
+    "dsa_sparse_gqa_attn_union", "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
 )
+# The measurement probes (include/dsa_probes.h), a separate library used by the benchmark.
+PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather")
 
 
 class DsaError(RuntimeError):
@@ -61,6 +63,7 @@ def load():
         "dsa_status_string": ([_I], ctypes.c_char_p),
         "dsa_last_error": ([], ctypes.c_char_p),
         "dsa_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
+        "dsa_decode_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
         "dsa_topk_workspace_size": ([_I, _I64, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_topk": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
         "dsa_topk_sorted": ([_P, _I64, _I, _P, _I, _P, _P, _P, _SZ, _P], _I),
@@ -81,8 +84,6 @@ def load():
         "dsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                         _P], _I),
-        "dsa_probe_mfma_bf16": ([_I, _I, _I, _P, ctypes.POINTER(ctypes.c_longlong), _P], _I),
-        "dsa_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -90,6 +91,36 @@ def load():
         fn.restype = res
     _lib = lib
     return lib
+
+
+_probes = None
+
+
+def load_probes():
+    """Load libdsa_probes.so (the measurement probes, built beside libdsa.so); raises if absent."""
+    global _probes
+    if _probes is not None:
+        return _probes
+    if not os.path.exists(PROBES_LIB_PATH):
+        raise RuntimeError(f"{PROBES_LIB_PATH} is missing: build it with `python -m sparse_long_context_lightning_amd.build`")
+    lib = ctypes.CDLL(PROBES_LIB_PATH)
+    sig = {
+        "dsa_probe_last_error": ([], ctypes.c_char_p),
+        "dsa_probe_mfma_bf16": ([_I, _I, _I, _P, ctypes.POINTER(ctypes.c_longlong), _P], _I),
+        "dsa_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
+        "dsa_probe_gather": ([_P, _P, _I64, _I, _P, _I, _I, _I, _I64, _I, _I, _P, _I64, _P], _I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _probes = lib
+    return lib
+
+
+def _check_probe(status: int):
+    if status != 0:
+        raise DsaError(status, load_probes().dsa_probe_last_error().decode())
 
 
 def _status_name(status: int) -> str:
@@ -139,6 +170,16 @@ def dsa_index_scores(q_idx, k_idx, w, cu_seqlens_host, row_begin, row_count, sco
     ld = scores.shape[1] if ld is None else ld
     _check(load().dsa_index_scores(_ptr(q_idx), _ptr(k_idx), _ptr(w), cu_p, len(cu) - 1, total, h_idx, d_idx,
                                    row_begin, row_count, _ptr(scores), ld, _stream(stream)))
+
+
+def dsa_decode_index_scores(q_idx, w, k_idx_cache, seq_lens, max_seq_len, scores, ld=None, stream=None):
+    """Indexer scores of each sequence's new token against its cached keys into scores[batch, ld]
+    (entries at positions >= seq_lens[b] untouched)."""
+    batch, h_idx, d_idx = q_idx.shape
+    s_max = k_idx_cache.shape[1]
+    ld = scores.shape[1] if ld is None else ld
+    _check(load().dsa_decode_index_scores(_ptr(q_idx), _ptr(w), _ptr(k_idx_cache), _ptr(seq_lens), batch, s_max,
+                                          max_seq_len, h_idx, d_idx, _ptr(scores), ld, _stream(stream)))
 
 
 def dsa_attn_head_mean(q, k, cu_seqlens_host, row_begin, row_count, probs, lse, softmax_scale=None, ld=None,
@@ -382,11 +423,22 @@ def upload_decode_inputs(di, device="cuda"):
 def dsa_probe_mfma_bf16(shape, grid, iters, sink, stream=None) -> int:
     """Enqueue the MFMA-only probe; returns the flops it executes."""
     flops = ctypes.c_longlong(0)
-    _check(load().dsa_probe_mfma_bf16(shape, grid, iters, _ptr(sink), ctypes.byref(flops), _stream(stream)))
+    _check_probe(load_probes().dsa_probe_mfma_bf16(shape, grid, iters, _ptr(sink), ctypes.byref(flops),
+                                                   _stream(stream)))
     return flops.value
 
 
 def dsa_probe_stream_read(src, grid, sink, stream=None):
     """Enqueue the streaming-read probe over the whole of `src`."""
-    _check(load().dsa_probe_stream_read(_ptr(src), src.numel() * src.element_size(), grid, _ptr(sink),
-                                        _stream(stream)))
+    _check_probe(load_probes().dsa_probe_stream_read(_ptr(src), src.numel() * src.element_size(), grid, _ptr(sink),
+                                                     _stream(stream)))
+
+
+def dsa_probe_gather(k, v, idx, sink, nsplit=1, row_stride=0, group_fastest=False, depth=2, stream=None):
+    """Enqueue the gather probe: the key and value rows the sparse attention reads for index sets
+    idx[rows, k_sel] over k, v [n_pos, hkv, 128] (position row * row_stride + p)."""
+    n_pos, hkv = k.shape[0], k.shape[1]
+    rows, k_sel = idx.shape
+    _check_probe(load_probes().dsa_probe_gather(_ptr(k), _ptr(v), n_pos, hkv, _ptr(idx), k_sel, rows, nsplit,
+                                                row_stride, int(bool(group_fastest)), depth, _ptr(sink), sink.numel(),
+                                                _stream(stream)))

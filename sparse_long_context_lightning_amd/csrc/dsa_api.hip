@@ -2,6 +2,7 @@
 // The contract of every entry point is documented in include/dsa.h.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -13,12 +14,29 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 
+// DSA_LOG=1 in the environment: every entry point logs its call (name and sizes) and every
+// rejected call its reason, one line each on stderr.  Read once.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = getenv("DSA_LOG");
+    return v && v[0] && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+
+int vfail(int status, const char* fmt, va_list ap) {
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  if (log_enabled()) fprintf(stderr, "[dsa] -> status %d: %s\n", status, g_last_error);
+  return status;
+}
+
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  const int st = vfail(status, fmt, ap);
   va_end(ap);
-  return status;
+  return st;
 }
 
 int hip_status(hipError_t e, const char* what) {
@@ -219,6 +237,26 @@ int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, cons
 
 }  // namespace
 
+namespace dsa {
+int api_fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int st = vfail(status, fmt, ap);
+  va_end(ap);
+  return st;
+}
+void api_clear_error() { g_last_error[0] = 0; }
+void api_log(const char* name, const char* fmt, ...) {
+  if (!log_enabled()) return;
+  char buf[400];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[dsa] %s(%s)\n", name, buf);
+}
+}  // namespace dsa
+
 extern "C" {
 
 int dsa_abi_version(void) { return DSA_ABI_VERSION; }
@@ -240,6 +278,7 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
                      int total_tokens, int h_idx, int d_idx, int row_begin, int row_count, float* scores, int64_t ld,
                      void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_index_scores", "batch=%d total=%d h_idx=%d d_idx=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, h_idx, d_idx, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q_idx);
   DSA_NONNULL(k_idx);
   DSA_NONNULL(w);
@@ -266,10 +305,47 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
                            row_begin, scores, ld, static_cast<hipStream_t>(stream));
 }
 
+int dsa_decode_index_scores(const void* q_idx, const float* w, const void* k_idx_cache, const int32_t* seq_lens,
+                            int batch, int s_max, int max_seq_len, int h_idx, int d_idx, float* scores, int64_t ld,
+                            void* stream) {
+  g_last_error[0] = 0;
+  dsa::api_log("dsa_decode_index_scores", "batch=%d s_max=%d max_seq_len=%d h_idx=%d d_idx=%d ld=%lld", batch, s_max,
+           max_seq_len, h_idx, d_idx, (long long)ld);
+  DSA_NONNULL(q_idx);
+  DSA_NONNULL(w);
+  DSA_NONNULL(k_idx_cache);
+  DSA_NONNULL(seq_lens);
+  DSA_NONNULL(scores);
+  DSA_ALIGNED(q_idx);
+  DSA_ALIGNED(w);
+  DSA_ALIGNED(k_idx_cache);
+  DSA_ALIGNED(scores);
+  if (batch <= 0 || s_max <= 0) return fail(DSA_ERR_INVALID_ARG, "batch and s_max must be positive");
+  if (max_seq_len <= 0 || max_seq_len > s_max)
+    return fail(DSA_ERR_INVALID_ARG, "max_seq_len (%d) must be in [1, s_max = %d]", max_seq_len, s_max);
+  DSA_TRY(check_indexer_shape(h_idx, d_idx));
+  if (ld < s_max || ld % 4 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "ld (%lld) must be a multiple of 4 and >= s_max (%d)", (long long)ld, s_max);
+  dsa::IndexerDecodeArgs ia;
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.w = w;
+  ia.k_cache = static_cast<const uint16_t*>(k_idx_cache);
+  ia.seq_lens = seq_lens;
+  ia.batch = batch;
+  ia.s_max = s_max;
+  ia.max_len = max_seq_len;
+  ia.h_idx = h_idx;
+  ia.d_idx = d_idx;
+  ia.scores = scores;
+  ia.ld = ld;
+  return hip_status(dsa::launch_indexer_decode(ia, static_cast<hipStream_t>(stream)), "decode indexer launch");
+}
+
 int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu_seqlens_host,
                          int batch, int total_tokens, int h_idx, int d_idx, int row_begin, int row_count,
                          const float* dscores, int64_t ld, float* dq_idx, float* dw, float* dk_idx, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_index_scores_bwd", "batch=%d total=%d h_idx=%d d_idx=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, h_idx, d_idx, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q_idx);
   DSA_NONNULL(k_idx);
   DSA_NONNULL(w);
@@ -324,6 +400,7 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
                        int hq, int hkv, int head_dim, float softmax_scale, int row_begin, int row_count, float* probs,
                        int64_t ld, float* lse, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_attn_head_mean", "batch=%d total=%d hq=%d hkv=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, hq, hkv, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(probs);
@@ -371,6 +448,7 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
 int dsa_indexer_kl(const float* scores, const float* target, int64_t ld, int rows, const int32_t* row_len,
                    float* row_loss, float* grad, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_indexer_kl", "rows=%d ld=%lld", rows, (long long)ld);
   DSA_NONNULL(scores);
   DSA_NONNULL(target);
   DSA_NONNULL(row_len);
@@ -397,6 +475,7 @@ namespace {
 int topk_entry(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
                float* values_out, void* workspace, size_t workspace_bytes, void* stream, bool ranked) {
   g_last_error[0] = 0;
+  dsa::api_log(ranked ? "dsa_topk_sorted" : "dsa_topk", "rows=%d ld=%lld k=%d ws=%zu", rows, (long long)ld, k, workspace_bytes);
   DSA_NONNULL(scores);
   DSA_NONNULL(row_len);
   DSA_NONNULL(idx_out);
@@ -442,6 +521,7 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
                         const int32_t* cu_seqlens, int batch, int total_tokens, int hq, int hkv, int head_dim,
                         float softmax_scale, void* out, float* lse, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn", "batch=%d total=%d hq=%d hkv=%d d=%d k_sel=%d", batch, total_tokens, hq, hkv, head_dim, k_sel);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(v);
@@ -490,6 +570,7 @@ int dsa_query_union_size(int total_tokens, int k_sel, int block_rows, int* n_blo
 int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens,
                     int block_rows, int cap, int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_query_union", "batch=%d total=%d k_sel=%d block_rows=%d cap=%d", batch, total_tokens, k_sel, block_rows, cap);
   DSA_NONNULL(idx);
   DSA_NONNULL(cu_seqlens);
   DSA_NONNULL(counts);
@@ -524,6 +605,7 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
                               int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, void* out,
                               float* lse, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn_union", "total=%d hq=%d hkv=%d block_rows=%d cap=%d", total_tokens, hq, hkv, block_rows, cap);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(v);
@@ -578,6 +660,7 @@ int dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v, const
                               float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn_dedup", "batch=%d total=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, total_tokens, hq, hkv, k_sel, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(v);
@@ -623,6 +706,7 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
                             int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, float* dq,
                             float* dk, float* dv, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn_bwd", "batch=%d total=%d hq=%d hkv=%d k_sel=%d", batch, total_tokens, hq, hkv, k_sel);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(v);
@@ -689,6 +773,7 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
                 int max_seqlen, int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale,
                 void* out, float* lse, int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_prefill", "batch=%d total=%d max_seqlen=%d hq=%d hkv=%d h_idx=%d d_idx=%d top_k=%d ws=%zu", batch, total_tokens, max_seqlen, hq, hkv, h_idx, d_idx, top_k, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
   DSA_NONNULL(v);
@@ -793,6 +878,7 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
                int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale, void* out, float* lse,
                int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  dsa::api_log("dsa_decode", "batch=%d s_max=%d max_seq_len=%d hq=%d hkv=%d h_idx=%d d_idx=%d top_k=%d ws=%zu", batch, s_max, max_seq_len, hq, hkv, h_idx, d_idx, top_k, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(q_idx);
   DSA_NONNULL(w);
@@ -877,23 +963,6 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   if (nsplit == 1) return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
   DSA_TRY(hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch"));
   return hip_status(dsa::launch_attn_combine(a, s), "combine launch");
-}
-
-int dsa_probe_mfma_bf16(int shape, int grid, int iters, float* sink, long long* flops, void* stream) {
-  if (shape != 16 && shape != 32) return fail(DSA_ERR_INVALID_ARG, "probe shape must be 16 or 32, got %d", shape);
-  if (grid < 1 || grid > (1 << 20) || iters < 1) return fail(DSA_ERR_INVALID_ARG, "probe grid / iters out of range");
-  if (!sink) return fail(DSA_ERR_INVALID_ARG, "probe sink is null");
-  if (flops) *flops = dsa::peak_mfma_flops(shape, grid, iters);
-  return hip_status(dsa::launch_peak_mfma(shape, grid, iters, sink, static_cast<hipStream_t>(stream)), "probe launch");
-}
-
-int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream) {
-  if (!src || !sink) return fail(DSA_ERR_INVALID_ARG, "probe pointers must not be null");
-  if (!aligned16(src) || bytes % 16 != 0 || bytes == 0)
-    return fail(DSA_ERR_INVALID_ARG, "probe source must be 16-byte aligned with a positive multiple of 16 bytes");
-  if (grid < 1 || grid > (1 << 20)) return fail(DSA_ERR_INVALID_ARG, "probe grid out of range");
-  return hip_status(dsa::launch_peak_stream_read(src, (long long)bytes, grid, sink, static_cast<hipStream_t>(stream)),
-                    "probe launch");
 }
 
 }  // extern "C"

@@ -38,16 +38,23 @@ def oracle_prefill_rows(pi, rows):
                        pi.cu_seqlens, pi.top_k, rows=rows)
 
 
-def oracle_prefill_rows_lazy(pi, rows):
-    """Oracle on sampled rows of a large workload without widening whole tensors up front."""
+def oracle_prefill_rows_lazy(pi, rows, keep_scores=False):
+    """Oracle on sampled rows of a large workload without widening whole tensors up front.  With
+    keep_scores, also each row's indexer scores (exact in fp32 for the integer indexer inputs, so
+    kept as float32 to halve the memory; the cast is checked to be exact)."""
     cu = [int(x) for x in pi.cu_seqlens]
     hq, d = pi.q.shape[1], pi.q.shape[2]
     scale = orc.default_softmax_scale(d)
     out = {"idx": [], "out": [], "lse": [], "wsum": []}
+    scores = []
     for r in rows:
         b = max(i for i in range(len(cu) - 1) if cu[i] <= r)
         o, t = cu[b], r - cu[b]
         sc = orc.index_scores_row(f64(pi.q_idx[r]), pi.w[r].astype(np.float64), f64(pi.k_idx[o:o + t + 1]))
+        if keep_scores:
+            sc32 = sc.astype(np.float32)
+            assert np.array_equal(sc32.astype(np.float64), sc), "scores not exact in fp32"
+            scores.append(sc32)
         sel = orc.select_topk_row(sc, pi.top_k)
         valid = sel[sel >= 0]
         # only the selected key/value rows are widened
@@ -60,7 +67,10 @@ def oracle_prefill_rows_lazy(pi, rows):
         out["out"].append(oo)
         out["lse"].append(ll)
         out["wsum"].append(ws)
-    return {k: np.asarray(v) for k, v in out.items()}
+    res = {k: np.asarray(v) for k, v in out.items()}
+    if keep_scores:
+        res["scores"] = scores
+    return res
 
 
 def oracle_decode_rows_lazy(di, batch_rows):

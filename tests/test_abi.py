@@ -11,24 +11,36 @@ import sparse_long_context_lightning_amd as dsa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa.h")
+PROBES_HEADER = os.path.join(ROOT, "include", "dsa_probes.h")
 
 P = ctypes.c_void_p
 FAKE = P(1 << 20)            # aligned, never dereferenced by host validation
 MISALIGNED = P((1 << 20) + 2)
 
 
-def _declared():
-    text = open(HEADER).read()
+def _declared(header=HEADER):
+    text = open(header).read()
     return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dsa_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
+    # the measurement probes live in their own library, not in the product ABI
+    assert not any(n.startswith("dsa_probe") for n in names)
+    assert not hasattr(lib, "dsa_probe_mfma_bf16")
+
+
+def test_probe_library_exports_every_declared_symbol():
+    lib = dsa.load_probes()
+    names = _declared(PROBES_HEADER)
+    assert set(names) == set(dsa.PROBES_EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings():
@@ -109,20 +121,44 @@ def test_other_entry_points_reject_bad_arguments():
     args2 = list(args)
     args2[9] = 1001  # max_seq_len > s_max
     assert lib.dsa_decode(*args2) == dsa.DSA_ERR_INVALID_ARG
+    # decode indexer scores: ld below s_max or not a multiple of 4, bad max_seq_len, unsupported shape
+    d = lambda **o: [FAKE, FAKE, FAKE, FAKE, o.get("batch", 4), 1000, o.get("mx", 1000), o.get("h", 64), 128, FAKE,
+                     o.get("ld", 1000), None]
+    assert lib.dsa_decode_index_scores(*d(ld=996)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode_index_scores(*d(ld=1002)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode_index_scores(*d(mx=1001)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode_index_scores(*d(mx=0)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode_index_scores(*d(batch=0)) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_decode_index_scores(*d(h=8)) == dsa.DSA_ERR_UNSUPPORTED
 
 
 def test_probe_validation():
-    lib = dsa.load()
+    lib = dsa.load_probes()
+    bad = 1  # DSA_PROBE_ERR_INVALID_ARG
     flops = ctypes.c_longlong(0)
-    assert lib.dsa_probe_mfma_bf16(8, 64, 10, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_mfma_bf16(16, 0, 10, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_mfma_bf16(16, 64, 0, FAKE, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_mfma_bf16(32, 64, 10, None, ctypes.byref(flops), None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_stream_read(MISALIGNED, 1 << 20, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_stream_read(FAKE, (1 << 20) + 8, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_stream_read(FAKE, 0, 64, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 0, FAKE, None) == dsa.DSA_ERR_INVALID_ARG
-    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 64, None, None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_probe_mfma_bf16(8, 64, 10, FAKE, ctypes.byref(flops), None) == bad
+    assert lib.dsa_probe_mfma_bf16(16, 0, 10, FAKE, ctypes.byref(flops), None) == bad
+    assert lib.dsa_probe_mfma_bf16(16, 64, 0, FAKE, ctypes.byref(flops), None) == bad
+    assert lib.dsa_probe_mfma_bf16(32, 64, 10, None, ctypes.byref(flops), None) == bad
+    assert lib.dsa_probe_last_error() != b""
+    assert lib.dsa_probe_stream_read(MISALIGNED, 1 << 20, 64, FAKE, None) == bad
+    assert lib.dsa_probe_stream_read(FAKE, (1 << 20) + 8, 64, FAKE, None) == bad
+    assert lib.dsa_probe_stream_read(FAKE, 0, 64, FAKE, None) == bad
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 0, FAKE, None) == bad
+    assert lib.dsa_probe_stream_read(FAKE, 1 << 20, 64, None, None) == bad
+
+    def gather(**o):
+        a = dict(k=FAKE, v=FAKE, n_pos=1024, hkv=4, idx=FAKE, k_sel=64, rows=100, nsplit=1, row_stride=0,
+                 group_fastest=0, depth=2, sink=FAKE, sink_len=1 << 20, stream=None)
+        a.update(o)
+        return lib.dsa_probe_gather(*a.values())
+
+    assert gather(k=MISALIGNED) == bad
+    assert gather(idx=None) == bad
+    assert gather(depth=3) == bad
+    assert gather(rows=0) == bad
+    assert gather(row_stride=-1) == bad
+    assert gather(sink_len=99) == bad     # 100 rows x 4 groups / 4 waves = 100 workgroups, padded to 104
 
 
 def test_query_union_validation():
@@ -245,3 +281,50 @@ def test_index_scores_bwd_validation():
     assert call(dq=MISALIGNED) == dsa.DSA_ERR_INVALID_ARG
     assert call(dk=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(rows=0) == dsa.DSA_OK
+
+
+def test_valid_call_without_a_gpu_reports_a_hip_error():
+    """On a host without a usable GPU a call that passes validation fails at its first launch with
+    DSA_ERR_HIP and the HIP message, instead of crashing (the pointers are never dereferenced: the
+    launch is refused before any kernel runs).  Runs in a child process so that no HIP state of this
+    process is touched."""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import sparse_long_context_lightning_amd as dsa
+lib = dsa.load()
+cu = (ctypes.c_int32 * 2)(0, 64)
+st = lib.dsa_index_scores(ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 20),
+                          ctypes.cast(cu, ctypes.c_void_p), 1, 64, 64, 128, 0, 64, ctypes.c_void_p(1 << 20), 64, None)
+print(st, dsa.dsa_last_error())
+""" % ROOT
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stderr
+    status, _, msg = res.stdout.strip().partition(" ")
+    assert int(status) == dsa.DSA_ERR_HIP, res.stdout
+    assert msg.startswith("indexer launch:"), msg
+
+
+def test_dsa_log_reports_calls_and_rejections():
+    """DSA_LOG=1: one stderr line per entry-point call (name and sizes) and one per rejection."""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, sys
+sys.path.insert(0, %r)
+import sparse_long_context_lightning_amd as dsa
+lib = dsa.load()
+lib.dsa_topk(ctypes.c_void_p(1 << 20), 64, 4, ctypes.c_void_p(1 << 20), 0, ctypes.c_void_p(1 << 20), None, None, 0, None)
+""" % ROOT
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         env=dict(os.environ, DSA_LOG="1"), timeout=120)
+    assert res.returncode == 0, res.stderr
+    lines = [l for l in res.stderr.splitlines() if l.startswith("[dsa]")]
+    assert lines[0] == "[dsa] dsa_topk(rows=4 ld=64 k=0 ws=0)", lines
+    assert lines[1].startswith("[dsa] -> status 2: top_k 0 outside"), lines
+    quiet = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                           env={k: v for k, v in os.environ.items() if k != "DSA_LOG"}, timeout=120)
+    assert "[dsa]" not in quiet.stderr

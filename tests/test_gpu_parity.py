@@ -61,6 +61,52 @@ def test_index_scores_row_window(dsa):
         assert np.array_equal(got[i, :len(row)].astype(np.float64), row), f"row {r0 + i}"
 
 
+@pytest.mark.parametrize("h_idx,d_idx", [(64, 128), (4, 64), (32, 128), (16, 128)])
+def test_index_scores_bit_exact_across_key_splits(dsa, h_idx, d_idx):
+    """Rows whose prefixes span several 4096-key workgroup splits, with a partial last split: windows
+    around the split boundaries and the last rows of a 9500-token sequence packed after a 700-token
+    one (window starts not aligned to the 4-token workgroups)."""
+    torch = _torch()
+    lens = [700, 9500]
+    pi = inp.prefill_inputs(lens, h_idx, d_idx, 8, 2, 128, 16, seed=901 + h_idx)
+    dev = tl.upload_prefill(pi)
+    ld = 9500
+    o = lens[0]
+    windows = [(o + 4089, 13), (o + 8187, 10), (o + 9381, 119), (0, 5), (o - 3, 6)]
+    f_q, f_k, w64 = tl.f64(pi.q_idx), tl.f64(pi.k_idx), pi.w.astype(np.float64)
+    cu = [int(x) for x in pi.cu_seqlens]
+    for r0, rc in windows:
+        scores = torch.full((rc, ld), float("nan"), dtype=torch.float32, device="cuda")
+        dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens, r0, rc, scores)
+        got = scores.cpu().numpy()
+        for i in range(rc):
+            r = r0 + i
+            b = 0 if r < cu[1] else 1
+            t = r - cu[b]
+            want = orc.index_scores_row(f_q[r], w64[r], f_k[cu[b]:cu[b] + t + 1])
+            assert np.array_equal(got[i, :t + 1].astype(np.float64), want), f"row {r} (t = {t})"
+            assert np.all(np.isnan(got[i, t + 1:])), f"row {r} wrote past its prefix"
+
+
+@pytest.mark.parametrize("h_idx,d_idx", [(64, 128), (4, 64), (32, 128), (16, 128)])
+def test_decode_index_scores_bit_exact(dsa, h_idx, d_idx):
+    """The decode indexer (one token per sequence against its cache) against the oracle, on ragged
+    cache lengths including 1, a partial 64-key tile and a partial 128-key workgroup."""
+    torch = _torch()
+    seq = [3000, 1, 129, 2048, 1500, 65]
+    s_max = 3000
+    di = inp.decode_inputs(len(seq), s_max, seq, h_idx, d_idx, 8, 2, 128, 16, seed=77 + h_idx)
+    dev = tl.upload_decode(di)
+    ld = 3004
+    scores = torch.full((len(seq), ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_decode_index_scores(dev["q_idx"], dev["w"], dev["k_idx_cache"], dev["seq_lens"], max(seq), scores)
+    got = scores.cpu().numpy()
+    for b, n in enumerate(seq):
+        want = orc.index_scores_row(tl.f64(di.q_idx[b]), di.w[b].astype(np.float64), tl.f64(di.k_idx_cache[b, :n]))
+        assert np.array_equal(got[b, :n].astype(np.float64), want), f"sequence {b} (len {n})"
+        assert np.all(np.isnan(got[b, n:])), f"sequence {b} wrote past its cache length"
+
+
 # ------------------------------------------------------------------------------ top-k
 
 def _run_topk(dsa, scores_np, lens, k, values=True):
@@ -394,3 +440,75 @@ def test_decode_equals_prefill_last_row(dsa):
                                   dev["v"][None].contiguous(), dev["k_idx"][None].contiguous(), seq, k)
     assert torch.equal(idx[n - 1], didx[0])
     tl.assert_attn_close(tl.bf16_tensor_to_f64(dout[0]), tl.bf16_tensor_to_f64(out[n - 1]), "decode vs prefill")
+
+
+# ------------------------------------------------------------------------------ guard bands
+
+GUARD = 4096  # bytes of canary on each side of every buffer
+
+
+def _guarded(shape, dtype, fill):
+    """A tensor of `shape` in the middle of a larger canary-filled buffer: (whole buffer, view)."""
+    torch = _torch()
+    es = torch.empty((), dtype=dtype).element_size()
+    n = int(np.prod(shape))
+    g = GUARD // es
+    whole = torch.full((n + 2 * g,), fill, dtype=dtype, device="cuda")
+    return whole, whole[g:g + n].view(*shape)
+
+
+def _assert_guards_intact(whole, fill, what):
+    torch = _torch()
+    g = GUARD // whole.element_size()
+    for band in (whole[:g], whole[-g:]):
+        if whole.dtype.is_floating_point:
+            assert bool(torch.isnan(band.float()).all() if np.isnan(fill) else (band == fill).all()), what
+        else:
+            assert bool((band == fill).all()), what
+
+
+def test_outputs_and_workspaces_leave_guard_bands_untouched(dsa):
+    """Every output of the fused prefill and decode, and their workspaces of exactly the reported
+    size, sit between canary bands; no call writes outside its buffers, and every output element
+    is written."""
+    torch = _torch()
+    nan = float("nan")
+    lens = [700, 64, 1500]
+    k = 512
+    pi = inp.prefill_inputs(lens, 64, 128, 32, 4, 128, k, seed=4242, structure="blocks16")
+    dev = tl.upload_prefill(pi)
+    total, hq = sum(lens), 32
+    out_w, out = _guarded((total, hq, 128), torch.bfloat16, nan)
+    lse_w, lse = _guarded((total, hq), torch.float32, nan)
+    idx_w, idx = _guarded((total, k), torch.int32, -99)
+    nbytes = dsa.dsa_prefill_workspace_size(3, total, 1500, hq, 4, 128, 64, 128, k)
+    ws_w, ws = _guarded((nbytes,), torch.uint8, 0xA5)
+    dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], pi.cu_seqlens,
+                    1500, k, out, lse, idx, ws)
+    torch.cuda.synchronize()
+    for whole, fill, what in ((out_w, nan, "prefill O"), (lse_w, nan, "prefill lse"), (idx_w, -99, "prefill idx"),
+                              (ws_w, 0xA5, "prefill workspace")):
+        _assert_guards_intact(whole, fill, what)
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any() and bool((idx != -99).all())
+    rows = [0, 699, 700, 763, 764, 1500, total - 1]
+    want = tl.oracle_prefill_rows(pi, rows)
+    tl.assert_idx_equal(idx.cpu().numpy()[rows], want["idx"], rows, "guarded prefill idx")
+
+    seq = [3000, 1, 129, 2048]
+    di = inp.decode_inputs(len(seq), 3000, seq, 64, 128, 32, 4, 128, k, seed=4243)
+    dd = tl.upload_decode(di)
+    b = len(seq)
+    out_w, out = _guarded((b, hq, 128), torch.bfloat16, nan)
+    lse_w, lse = _guarded((b, hq), torch.float32, nan)
+    idx_w, idx = _guarded((b, k), torch.int32, -99)
+    nbytes = dsa.dsa_decode_workspace_size(b, 3000, hq, 4, 128, 64, 128, k)
+    ws_w, ws = _guarded((nbytes,), torch.uint8, 0xA5)
+    dsa.dsa_decode(dd["q"], dd["q_idx"], dd["w"], dd["k_cache"], dd["v_cache"], dd["k_idx_cache"], dd["seq_lens"],
+                   3000, k, out, lse, idx, ws)
+    torch.cuda.synchronize()
+    for whole, fill, what in ((out_w, nan, "decode O"), (lse_w, nan, "decode lse"), (idx_w, -99, "decode idx"),
+                              (ws_w, 0xA5, "decode workspace")):
+        _assert_guards_intact(whole, fill, what)
+    assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any() and bool((idx != -99).all())
+    want = tl.oracle_decode_rows_lazy(di, range(b))
+    tl.assert_idx_equal(idx.cpu().numpy(), np.asarray(want["idx"]), what="guarded decode idx")

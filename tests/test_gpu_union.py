@@ -231,9 +231,11 @@ def test_dedup_attention_equals_per_row_attention_and_oracle(dsa, k, dup_rows):
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_union_full_c3_prefill_128k(dsa):
-    """At the benchmark's 128K workload: the prefill's own top-k sets, merged and attended, equal the
-    per-row kernel's output on every row, and on two sampled blocks the oracle's own top-k sets,
-    merged sets and attention."""
+    """At the benchmark's 128K workload, on the prefill's own top-k sets: the per-row kernel
+    (dsa_sparse_gqa_attn), the merged-set kernel on 16-row blocks and the prefill's own output
+    (merged sets of 8-row blocks) agree on every row within the attention tolerance, and on two
+    sampled 16-row blocks the oracle's top-k sets, merged sets and attention equal what the kernels
+    used and produced."""
     import torch
     from dsa_testlib import upload_prefill
     pi = inp.workload("c3_prefill_128k")
@@ -241,18 +243,21 @@ def test_union_full_c3_prefill_128k(dsa):
     dev = upload_prefill(pi)
     cu = [int(x) for x in pi.cu_seqlens]
     print("[union] c3 prefill 128K", flush=True)
-    out_ref, _, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens,
-                                  pi.top_k)
+    out_pf, _, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], pi.cu_seqlens,
+                                 pi.top_k)
+    out_row = torch.empty_like(out_pf)
+    dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out_row)
     nb, cap = dsa.dsa_query_union_size(total, pi.top_k)
     counts = torch.empty((nb,), dtype=torch.int32, device="cuda")
     rows = torch.empty((nb, cap), dtype=torch.int32, device="cuda")
     masks = torch.empty((nb, cap), dtype=torch.int16, device="cuda")
     dsa.dsa_query_union(idx, dev["cu"], counts, rows, masks)
-    out = torch.empty_like(out_ref)
-    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out)
+    out16 = torch.empty_like(out_pf)
+    dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], counts, rows, masks, out16)
     torch.cuda.synchronize()
-    err = (out.float() - out_ref.float()).abs()
-    assert float(err.max()) <= 2e-2 and float(err.mean()) <= 2e-3, (float(err.max()), float(err.mean()))
+    for label, other in (("16-row merged sets", out16), ("prefill (8-row merged sets)", out_pf)):
+        err = (other.float() - out_row.float()).abs()
+        assert float(err.max()) <= 2e-2 and float(err.mean()) <= 2e-3, (label, float(err.max()), float(err.mean()))
     for b in (4100, nb - 1):
         block_rows = list(range(16 * b, min(16 * b + 16, total)))
         want = oracle_prefill_rows_lazy(pi, block_rows)
@@ -264,4 +269,5 @@ def test_union_full_c3_prefill_128k(dsa):
         assert n == len(kv)
         assert np.array_equal(rows[b, :n].cpu().numpy(), kv)
         assert np.array_equal(masks[b, :n].cpu().numpy().view(np.uint16).astype(np.int64), m)
-        assert_attn_close(bf16_tensor_to_f64(out[block_rows]), want["out"], f"block {b} vs oracle")
+        assert_attn_close(bf16_tensor_to_f64(out16[block_rows]), want["out"], f"block {b}: merged sets vs oracle")
+        assert_attn_close(bf16_tensor_to_f64(out_row[block_rows]), want["out"], f"block {b}: per row vs oracle")
