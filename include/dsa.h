@@ -364,6 +364,30 @@ int dsa_decode(const void* q, const void* q_idx, const float* w,
                float softmax_scale, void* out, float* lse, int32_t* idx_out,
                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Scratch bytes dsa_decode_noalloc holds per device (32 MiB). */
+#define DSA_DECODE_NOALLOC_MAX_BYTES (32u << 20)
+
+/*
+ * dsa_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * dsa_decode, without the workspace: the step's scratch is a static device array of
+ * DSA_DECODE_NOALLOC_MAX_BYTES inside the library, one per device, held until the process ends.
+ * The call allocates and frees nothing.
+ *   - Uses the scratch of the current device (hipGetDevice); `stream` must belong to that device.
+ *     The first call on a device looks the array's address up (no allocation).
+ *   - Every call on a device shares that device's array and leaves its contents behind: calls
+ *     that can overlap on one device (different streams, or different host threads) race and
+ *     must be serialised by the caller.
+ *   - A step whose dsa_decode_workspace_size exceeds DSA_DECODE_NOALLOC_MAX_BYTES is rejected with
+ *     DSA_ERR_WORKSPACE before anything is enqueued (batch 32 x 131072 and batch 8 x 262144 caches
+ *     at k = 2048 fit).
+ */
+int dsa_decode_noalloc(const void* q, const void* q_idx, const float* w,
+                       const void* k_cache, const void* v_cache, const void* k_idx_cache,
+                       const int32_t* seq_lens, int batch, int s_max, int max_seq_len,
+                       int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
+                       float softmax_scale, void* out, float* lse, int32_t* idx_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

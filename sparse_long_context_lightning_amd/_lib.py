@@ -30,6 +30,7 @@ EXPORTED = (
     "dsa_prefill_workspace_size", "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean",
     "dsa_indexer_kl", "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union",
     "dsa_sparse_gqa_attn_union", "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
+    "dsa_decode_noalloc",
 )
 # The measurement probes (include/dsa_probes.h), a separate library used by the benchmark.
 PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather")
@@ -84,6 +85,8 @@ def load():
         "dsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                         _P], _I),
+        "dsa_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
+                               _I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

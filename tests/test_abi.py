@@ -26,7 +26,7 @@ def _declared(header=HEADER):
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -328,3 +328,17 @@ lib.dsa_topk(ctypes.c_void_p(1 << 20), 64, 4, ctypes.c_void_p(1 << 20), 0, ctype
     quiet = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                            env={k: v for k, v in os.environ.items() if k != "DSA_LOG"}, timeout=120)
     assert "[dsa]" not in quiet.stderr
+
+
+def test_noalloc_decode_validation_without_a_gpu():
+    """dsa_decode_noalloc checks its arguments on the host like dsa_decode, and refuses a step whose
+    scratch need exceeds the library's static scratch before touching any device."""
+    lib = dsa.load()
+    f = ctypes.c_float(0.1)
+    big = [FAKE] * 7 + [64, 262144, 262144, 32, 4, 128, 64, 128, 2048, f, FAKE, None, FAKE, None]
+    assert lib.dsa_decode_noalloc(*big) == dsa.DSA_ERR_WORKSPACE
+    assert "static scratch" in dsa.dsa_last_error()
+    bad_shape = [FAKE] * 7 + [4, 1000, 1000, 32, 4, 64, 64, 128, 2048, f, FAKE, None, FAKE, None]
+    assert lib.dsa_decode_noalloc(*bad_shape) == dsa.DSA_ERR_UNSUPPORTED
+    assert dsa.dsa_decode_workspace_size(32, 131072, 32, 4, 128, 64, 128, 2048) <= (32 << 20)
+    assert dsa.dsa_decode_workspace_size(8, 262144, 32, 4, 128, 64, 128, 2048) <= (32 << 20)
