@@ -1,6 +1,7 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-bwd] [--no-dense] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-extra] [--no-bwd] [--no-dense]
+                    [--no-correlated] [--no-cpu-baseline]
 
 A step is one pass of the whole prefill path (indexer -> top-k -> sparse GQA attention) over
 the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexer heads of
@@ -9,13 +10,24 @@ resident in HBM.  The timed step is the fused dsa_prefill call; the same chunk s
 driven through the C ABI's separate entry points with HIP events on the launch stream around
 every kernel, which gives the per-kernel times (and the rooflines) beside it.  The attention
 step runs with adjacent-query dedup (merged index sets of 8-row blocks); the fused call is also
-timed with a workspace too small for the merged sets, which attends per row.  The same prefill
-on inputs whose neighbouring queries select overlapping sets follows (with and without dedup).
-The decode step (batch 32 over 131072-token caches, k = 2048) is timed after the prefill, eagerly
-and captured in a HIP graph, then the torch.topk-shaped top-k on the decode scores, the backward
-of the sparse attention and the indexer's warm-up step (target, KL and the indexer backward) on
-the 32K prefill, and dense causal GQA attention on the prefill and decode shapes through torch's
-fused SDPA (context lines beside the headline value).
+timed with a workspace too small for the merged sets, which attends per row.
+
+Each sparse-attention kernel is read three ways: its HBM traffic from the committed rocprofv3
+counter runs (FETCH_SIZE + WRITE_SIZE, calibrated) over its time against the 8 TB/s peak, its
+algorithmic gather bytes over its time (an "effective" rate that L2 and last-level-cache reuse
+can push past the peak), and against a gather probe (libdsa_probes.so) that reads exactly the
+same key and value rows in the same work order with no arithmetic, the achievable ceiling of
+that access pattern on the box.
+
+Also timed: the decode step (batch 32 over 131072-token caches, k = 2048), eagerly, per kernel
+through the separate entry points, and captured in a HIP graph; the 256K long-video mix (packed
+262144 + 65536 + 8192-token prefill, then batch-8 decode over 262144-token caches) and the 32K
+prefill as extra fields; the correlated-query 128K prefill with and without dedup; the
+torch.topk-shaped top-k on the decode scores; the backward of the sparse attention and the
+indexer's warm-up step on the 32K prefill; dense causal GQA attention on the prefill and decode
+shapes through torch's fused SDPA (context); and the CPU oracle on sampled rows of the same
+128K workload (its rate, and its agreement with the timed run's outputs on those rows and on
+every decode row).
 
 One JSON line is printed last.
 """
@@ -25,6 +37,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -39,11 +52,14 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
 PREFILL = "c3_prefill_128k"
 DECODE = "c4_decode_b32_128k"
+EXTRA_PREFILL = ("c5_video_mix_prefill", "c2_prefill_32k")
+EXTRA_DECODE = ("c5_video_mix_decode",)
+CPU_SAMPLE_ROWS = 4096       # candidate rows of the oracle sample (drawn before the timed run)
 
 
-def counter_traffic(kernel_key):
-    """HBM bytes per launch (read + write, calibrated) from the committed counter runs, or None
-    when the kernel source changed since they were taken."""
+def counter_entry(kernel_key):
+    """Committed counter-run figures of one kernel on one workload (profiles/counters.json), or
+    None when the kernel's source changed since they were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "counters.json")
     try:
@@ -52,9 +68,33 @@ def counter_traffic(kernel_key):
         cur = hashlib.sha256(open(os.path.join(ROOT, ent["source"]), "rb").read()).hexdigest()[:16]
         if cur != ent["sha256_16"]:
             return None
-        return (ent["read_gb_per_launch"] + ent["write_gb_per_launch"]) * 1e9
+        return ent
     except (OSError, KeyError, ValueError):
         return None
+
+
+def counter_traffic(kernel_key):
+    """HBM bytes per launch (read + write, calibrated) from the committed counter runs, or None."""
+    ent = counter_entry(kernel_key)
+    return None if ent is None else (ent["read_gb_per_launch"] + ent["write_gb_per_launch"]) * 1e9
+
+
+def hbm_roofline(kernel, kernel_key, avg_launch_ms, algorithmic_bytes, ceiling=None, **extra):
+    """An HBM-bound kernel read against the 8 TB/s peak: achieved = counter bytes per launch over
+    the launch's average time (null when no current counter run exists), beside the algorithmic
+    bytes' effective rate and, where given, the gather probe's ceiling on the same rows."""
+    traffic = counter_traffic(kernel_key)
+    achieved = None if traffic is None else traffic / (avg_launch_ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "kernel": kernel, "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": None if achieved is None else achieved / PEAK_HBM_GBS, "traffic": traffic,
+         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated; FETCH_SIZE counts L2 "
+                         "misses, Infinity Cache hits included)",
+         "avg_launch_ms": avg_launch_ms, "algorithmic_bytes_per_launch": algorithmic_bytes,
+         "effective_algorithmic_gbs": algorithmic_bytes / (avg_launch_ms * 1e-3) / 1e9}
+    if ceiling is not None:
+        r["gather_ceiling"] = dict(ceiling, frac_of_ceiling=ceiling["ms"] / avg_launch_ms)
+    r.update(extra)
+    return r
 
 
 def log(msg):
@@ -69,6 +109,7 @@ def parse():
     ap.add_argument("--workload", default=PREFILL)
     ap.add_argument("--decode-workload", default=DECODE)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 256K video-mix and 32K extra fields")
     ap.add_argument("--no-correlated", action="store_true", help="skip the correlated-query prefill context line")
     ap.add_argument("--bwd-workload", default="c2_prefill_32k")
     ap.add_argument("--no-bwd", action="store_true")
@@ -126,13 +167,53 @@ class Timer:
         self.pending, self.total, self.count = {}, {}, {}
 
 
-def prefill_bench(args, dsa, inp):
+def best_ms(fn, reps=3):
+    """Best of `reps` event-timed calls (after one untimed call)."""
     import torch
-    spec = inp.WORKLOADS[args.workload]
-    assert spec["kind"] == "prefill"
+    fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return min(out)
+
+
+def gather_ceiling(dsa, k, v, idx, nsplits=(1,), row_stride=0, group_fastest=False):
+    """The gather probe over the same key / value rows in the same work order, with both load
+    shapes (64-byte pieces of 16 rows per instruction, or 4 whole rows per instruction), 1, 2 and 4
+    chunks in flight per wave and each given number of index ranges per row (one wave each): the
+    best time is the achievable ceiling of that access pattern."""
+    import torch
+    rows = idx.shape[0]
+    hkv = k.shape[1]
+    wgs = ((rows * hkv * max(nsplits) + 3) // 4 + 7) // 8 * 8
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    by_cfg = {}
+    for whole in (False, True):
+        for nsplit in nsplits:
+            for depth in (1, 2, 4):
+                by_cfg[f"{'whole_rows' if whole else 'row_pieces'}_nsplit{nsplit}_depth{depth}"] = best_ms(
+                    lambda: dsa.dsa_probe_gather(k, v, idx, sink, nsplit=nsplit, row_stride=row_stride,
+                                                 group_fastest=group_fastest, depth=depth, whole_rows=whole))
+    best = min(by_cfg, key=by_cfg.get)
+    return {"ms": by_cfg[best], "config": best, "ms_by_config": by_cfg,
+            "what": "dsa_probe_gather: the same K and V rows, same work order, no arithmetic"}
+
+
+def prefill_section(args, dsa, inp, name, steps, warmup, full):
+    """The fused prefill on workload `name` (the timed step), then the same chunk schedule through the
+    separate entry points for per-kernel times and rooflines.  `full` adds the prefill without dedup,
+    the 16-row merged-set statistics, the gather ceilings and the rows kept for the oracle's check."""
+    import torch
     t0 = time.time()
-    pi = inp.workload(args.workload)
-    log(f"generated {args.workload} inputs in {time.time() - t0:.1f}s")
+    pi = inp.workload(name)
+    log(f"generated {name} inputs in {time.time() - t0:.1f}s")
     dev = dsa.upload_prefill_inputs(pi)
     lens = [int(x) for x in pi.seq_lens]
     total = sum(lens)
@@ -190,50 +271,80 @@ def prefill_bench(args, dsa, inp):
                         max_seqlen, k, out, lse, idx, workspace)
 
     # Timed region: the fused entry point, inputs already resident.
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         fused()
     torch.cuda.synchronize()
-    log(f"prefill warmup done; timing {args.steps} steps")
+    log(f"{name}: prefill warmup done; timing {steps} steps")
     t_start = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         fused()
     torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t_start) * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / steps
+
+    samples = None
+    if full:
+        # The timed run's outputs on the rows the oracle may check (drawn before it runs).
+        cand = np.random.default_rng(123).integers(0, total, CPU_SAMPLE_ROWS)
+        sel = torch.from_numpy(cand.astype(np.int64)).cuda()
+        samples = {"rows": cand.tolist(), "idx": idx[sel].cpu().numpy(), "out": out[sel].float().cpu().numpy(),
+                   "lse": lse[sel].cpu().numpy()}
 
     # Attribution: the same schedule through the separate entry points, HIP events per kernel.
     step()
     timer.collect()
     timer.reset()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
-    sep_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    sep_ms = (time.perf_counter() - t0) * 1e3 / steps
     timer.collect()
-    kern = {n: timer.total[n] / args.steps for n in timer.total}            # ms per step
-    launches = {n: timer.count[n] / args.steps for n in timer.count}
-    log(f"prefill {ms_per_step:.1f} ms/step (separate entry points {sep_ms:.1f}); kernels {kern}")
+    kern = {n: timer.total[n] / steps for n in timer.total}            # ms per step
+    launches = {n: timer.count[n] / steps for n in timer.count}
+    log(f"{name}: prefill {ms_per_step:.1f} ms/step (separate entry points {sep_ms:.1f}); kernels {kern}")
 
-    # The same fused call with a workspace too small for the merged sets: attention per row.
-    ws_chunk = ws[:ws_chunk_bytes]
-    fused(ws_chunk)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
+    res = {"name": name, "pi": pi, "rows_total": total, "ms_per_step": ms_per_step, "sep_ms": sep_ms,
+           "kern": kern, "launches": launches, "samples": samples}
+    if full:
+        # The same fused call with a workspace too small for the merged sets: attention per row.
+        ws_chunk = ws[:ws_chunk_bytes]
         fused(ws_chunk)
-    torch.cuda.synchronize()
-    no_dedup_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    out_nd = out.clone()
-    fused()
-    torch.cuda.synchronize()
-    dd_err = (out.float() - out_nd.float()).abs()
-    log(f"prefill without dedup {no_dedup_ms:.1f} ms/step; |O dedup - O per row| max {float(dd_err.max()):.2e}")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fused(ws_chunk)
+        torch.cuda.synchronize()
+        res["no_dedup_ms"] = (time.perf_counter() - t0) * 1e3 / steps
+        out_nd = out.clone()
+        # the per-row kernel alone on the same sets, for its own gather ceiling
+        res["per_row_attn_ms"] = best_ms(lambda: dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"],
+                                                                         out_nd, None))
+        dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out_nd, None)
+        fused()
+        torch.cuda.synchronize()
+        res["max_abs_out_vs_per_row"] = float((out.float() - out_nd.float()).abs().max())
+        log(f"{name}: prefill without dedup {res['no_dedup_ms']:.1f} ms/step; per-row attention kernel "
+            f"{res['per_row_attn_ms']:.1f} ms; |O dedup - O per row| max {res['max_abs_out_vs_per_row']:.2e}")
+        del out_nd
+        # Gather ceilings: the per-row kernel's rows (every selected position of every row, KV
+        # group slowest) and the merged-set kernel's rows (every merged KV row of every 8-row
+        # block), each through the gather probe.
+        if len(lens) == 1:
+            res["ceiling_per_row"] = gather_ceiling(dsa, dev["k"], dev["v"], idx)
+            dsa.dsa_query_union(idx, dev["cu"], u_counts, u_rows, u_masks, ublk)
+            merged_idx = torch.where(torch.arange(cap, device="cuda")[None, :] < u_counts[:, None], u_rows,
+                                     torch.full_like(u_rows, -1))
+            res["ceiling_merged"] = gather_ceiling(dsa, dev["k"], dev["v"], merged_idx)
+            del merged_idx
+            log(f"{name}: gather ceilings per row {res['ceiling_per_row']['ms']:.1f} ms, merged sets "
+                f"{res['ceiling_merged']['ms']:.1f} ms")
 
     # Algorithmic work per step.
     pairs = sum(n * (n + 1) // 2 for n in lens)
     idx_flops = pairs * 2 * h_idx * d_idx
     sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
     attn_bytes = sel_pairs * (2 * hkv * d * 2 + 4) + total * (2 * hq * d * 2 + 4 * hq)
+    dsa.dsa_query_union(idx, dev["cu"], u_counts, u_rows, u_masks, ublk)
     counts = u_counts.cpu().numpy().astype(np.int64)
     merged = int(counts.sum())
     padded = int(((counts + 31) // 32 * 32).sum())
@@ -245,35 +356,196 @@ def prefill_bench(args, dsa, inp):
     merged_flops = merged * hkv * 2 * (2 * ublk * (hq // hkv) * d)
     union_bytes = total * k * 4 + padded * 6
     topk_bytes = pairs * 4 + total * k * 4   # one pass over each row's scores + index write
-    idx_tflops = idx_flops / (kern["indexer"] * 1e-3) / 1e12
-    attn_gbs = merged_bytes / (kern["sparse_attn"] * 1e-3) / 1e9
-    attn_tflops = merged_flops / (kern["sparse_attn"] * 1e-3) / 1e12
-    union_gbs = union_bytes / (kern["query_union"] * 1e-3) / 1e9
-    topk_gbs = topk_bytes / (kern["topk"] * 1e-3) / 1e9
-    stats16 = {}
-    nb16, cap16 = dsa.dsa_query_union_size(total, k, 16)
-    c16 = torch.empty(nb16, dtype=torch.int32, device="cuda")
-    r16 = torch.empty((nb16, cap16), dtype=torch.int32, device="cuda")
-    m16 = torch.empty((nb16, cap16), dtype=torch.int16, device="cuda")
-    dsa.dsa_query_union(idx, dev["cu"], c16, r16, m16, 16)
-    c16 = c16.cpu().numpy()
-    for t in (8192, 32768, 65536, total - 16):
-        stats16[str(t)] = int(c16[min(t // 16, nb16 - 1)])
-    dedup = {"block_rows": ublk, "merged_rows_per_block_mean": float(counts.mean()),
-             "index_slots_per_block": ublk * k, "merged_fraction": merged / float(total * k),
-             "prefill_ms_without_dedup": no_dedup_ms, "max_abs_out_vs_per_row": float(dd_err.max()),
-             "union16_at_t": stats16, "union16_mean": float(c16.mean())}
-    del r16, m16
-
-    res = dict(
-        pi=pi, rows_total=total, ms_per_step=ms_per_step, sep_ms=sep_ms, kern=kern, launches=launches,
-        idx_flops=idx_flops, idx_tflops=idx_tflops, attn_bytes=attn_bytes, attn_gbs=attn_gbs, topk_bytes=topk_bytes,
-        topk_gbs=topk_gbs, pairs=pairs, sel_pairs=sel_pairs, merged_bytes=merged_bytes,
-        merged_flops=merged_flops, attn_tflops=attn_tflops, union_gbs=union_gbs, union_bytes=union_bytes, dedup=dedup,
-    )
+    res.update(pairs=pairs, idx_flops=idx_flops, sel_pairs=sel_pairs, attn_bytes=attn_bytes, merged=merged,
+               merged_bytes=merged_bytes, merged_flops=merged_flops, union_bytes=union_bytes, topk_bytes=topk_bytes,
+               idx_tflops=idx_flops / (kern["indexer"] * 1e-3) / 1e12,
+               attn_tflops=merged_flops / (kern["sparse_attn"] * 1e-3) / 1e12,
+               union_gbs=union_bytes / (kern["query_union"] * 1e-3) / 1e9,
+               topk_gbs=topk_bytes / (kern["topk"] * 1e-3) / 1e9,
+               merged_fraction=merged / float(sel_pairs), block_rows=ublk,
+               merged_rows_per_block_mean=float(counts.mean()))
+    if full:
+        stats16 = {}
+        nb16, cap16 = dsa.dsa_query_union_size(total, k, 16)
+        c16 = torch.empty(nb16, dtype=torch.int32, device="cuda")
+        r16 = torch.empty((nb16, cap16), dtype=torch.int32, device="cuda")
+        m16 = torch.empty((nb16, cap16), dtype=torch.int16, device="cuda")
+        dsa.dsa_query_union(idx, dev["cu"], c16, r16, m16, 16)
+        c16 = c16.cpu().numpy()
+        for t in (8192, 32768, 65536, total - 16):
+            stats16[str(t)] = int(c16[min(t // 16, nb16 - 1)])
+        res["union16_at_t"] = stats16
+        res["union16_mean"] = float(c16.mean())
+        del r16, m16
     del dev, ws, scores, out, lse, idx, u_rows, u_masks
     torch.cuda.empty_cache()
     return res
+
+
+def indexer_roofline(pre, counter_key=None):
+    r = {"bound": "mfma", "kernel": "indexer_prefill_kernel", "achieved": pre["idx_tflops"],
+         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
+         "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
+         "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]}
+    if counter_key:
+        r["traffic"] = counter_traffic(counter_key)
+        r["traffic_unit"] = "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)"
+    return r
+
+
+def prefill_summary(pre):
+    """Extra-field summary of a prefill section (the 256K mix, the 32K prefill)."""
+    kern = pre["kern"]
+    return {"workload": pre["name"], "tokens": pre["rows_total"], "ms_per_step": pre["ms_per_step"],
+            "tokens_per_s": pre["rows_total"] / (pre["ms_per_step"] * 1e-3),
+            "separate_entry_points_ms_per_step": pre["sep_ms"], "kernel_ms_per_step": kern,
+            "roofline_indexer": indexer_roofline(pre),
+            "sparse_attn_effective_algorithmic_gbs": pre["merged_bytes"] / (kern["sparse_attn"] * 1e-3) / 1e9,
+            "merged_rows_per_8_row_block_mean": pre["merged_rows_per_block_mean"],
+            "topk_gbs": pre["topk_gbs"]}
+
+
+def decode_section(args, dsa, inp, name, full):
+    """The decode step on workload `name`: eager median, per kernel through the separate entry points
+    (decode indexer, top-k, decode attention), the attention's gather ceiling; `full` adds the step
+    captured in a HIP graph and the torch.topk-shaped top-k on the step's scores."""
+    import torch
+    t0 = time.time()
+    di = inp.workload(name)
+    log(f"generated {name} inputs in {time.time() - t0:.1f}s")
+    dev = dsa.upload_decode_inputs(di)
+    batch, hq, d = di.q.shape
+    s_max, hkv = di.k_cache.shape[1], di.k_cache.shape[2]
+    h_idx, d_idx = di.q_idx.shape[1], di.q_idx.shape[2]
+    k = di.top_k
+    ws = torch.empty(dsa.dsa_decode_workspace_size(batch, s_max, hq, hkv, d, h_idx, d_idx, k), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(dev["q"])
+    lse = torch.empty(batch, hq, dtype=torch.float32, device="cuda")
+    idx = torch.empty(batch, k, dtype=torch.int32, device="cuda")
+    max_len = int(di.seq_lens.max())
+
+    def step():
+        dsa.dsa_decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
+                       dev["seq_lens"], max_len, k, out, lse, idx, ws)
+
+    def timed_median(fn, n_iter):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n_iter):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        return times[len(times) // 2], times[0]
+
+    n_iter = max(20, args.steps * 4)
+    us_median, us_min = timed_median(step, n_iter)
+    samples = {"idx": idx.cpu().numpy(), "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+    lens = di.seq_lens.astype(np.int64)
+    idx_bytes = int((lens * d_idx * 2).sum())
+    score_bytes = int((lens * 4).sum())
+    attn_bytes = int((np.minimum(lens, k) * (2 * hkv * d * 2 + 4)).sum() + batch * hq * d * 2 * 2)
+    bytes_step = idx_bytes + 2 * score_bytes + attn_bytes
+    log(f"{name}: decode median {us_median:.1f} us (min {us_min:.1f})")
+
+    # Per kernel through the separate entry points (same kernels, same order, same buffers).
+    ld = (s_max + 3) // 4 * 4
+    scores = torch.empty(batch, ld, dtype=torch.float32, device="cuda")
+    tk_ws = torch.empty(dsa.dsa_topk_workspace_size(batch, ld, k), dtype=torch.uint8, device="cuda")
+    at_ws_n = dsa.dsa_sparse_gqa_attn_decode_workspace_size(batch, hq, hkv, k)
+    at_ws = torch.empty(max(at_ws_n, 16), dtype=torch.uint8, device="cuda")
+    idx2 = torch.empty_like(idx)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    per = {}
+    per["indexer"] = timed_median(lambda: dsa.dsa_decode_index_scores(dev["q_idx"], dev["w"], dev["k_idx_cache"],
+                                                                       dev["seq_lens"], max_len, scores), n_iter)[0]
+    per["topk"] = timed_median(lambda: dsa.dsa_topk(scores, dev["seq_lens"], k, idx2, workspace=tk_ws), n_iter)[0]
+    per["attention"] = timed_median(lambda: dsa.dsa_sparse_gqa_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"],
+                                                                          idx2, dev["seq_lens"], out2, lse2,
+                                                                          workspace=at_ws), n_iter)[0]
+    torch.cuda.synchronize()
+    same = bool(torch.equal(idx, idx2) and torch.equal(out.view(torch.int16), out2.view(torch.int16)))
+    ceiling = gather_ceiling(dsa, dev["k_cache"].view(batch * s_max, hkv, d), dev["v_cache"].view(batch * s_max, hkv, d),
+                             idx2, nsplits=(1, 2, 4, 8, 16, 32), row_stride=s_max, group_fastest=True)
+    log(f"{name}: decode kernels (us) {per}; separate entry points equal the fused step: {same}; attention gather "
+        f"ceiling {ceiling['ms'] * 1e3:.1f} us")
+    res = dict(name=name, us_median=us_median, us_min=us_min, bytes_step=bytes_step,
+               gbs=bytes_step / (us_median * 1e-6) / 1e9, batch=batch, s_max=s_max, kernel_us=per,
+               separate_entry_points_equal_fused=same, idx_bytes=idx_bytes, attn_bytes=attn_bytes,
+               score_bytes=score_bytes, attn_ceiling=ceiling, samples=samples, di=di)
+
+    if full:
+        # The same step captured once in a HIP graph and replayed: no host launch work per step.
+        eager = (out.clone(), lse.clone(), idx.clone())
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        g_med, g_min = timed_median(graph.replay, n_iter)
+        graph_same = bool(torch.equal(out, eager[0]) and torch.equal(lse, eager[1]) and torch.equal(idx, eager[2]))
+        res["graph_us"] = {"median": g_med, "min": g_min, "same_outputs_as_eager": graph_same}
+        log(f"{name}: decode in a HIP graph: median {g_med:.1f} us (min {g_min:.1f}); outputs equal: {graph_same}")
+        del graph
+
+        # The torch.topk-shaped top-k on the decode step's scores, beside the ascending form.
+        idx_s = torch.empty(batch, k, dtype=torch.int32, device="cuda")
+        val_s = torch.empty(batch, k, dtype=torch.float32, device="cuda")
+        timing = {}
+        for nm, fn in (("ascending", dsa.dsa_topk), ("sorted", dsa.dsa_topk_sorted)):
+            timing[nm] = timed_median(lambda: fn(scores, dev["seq_lens"], k, idx_s, val_s, workspace=tk_ws),
+                                      n_iter)[0]
+            if nm == "ascending":
+                asc_i = idx_s.cpu().numpy().copy()
+        got_i = idx_s.cpu().numpy()
+        got_v = val_s.cpu().numpy()
+        ok = True
+        for j in range(batch):
+            order_ok = bool(np.all((got_v[j, :-1] > got_v[j, 1:]) |
+                                   ((got_v[j, :-1] == got_v[j, 1:]) & (got_i[j, :-1] < got_i[j, 1:]))))
+            ok = ok and order_ok and bool(np.array_equal(np.sort(got_i[j]), asc_i[j]))
+        res["topk_sorted"] = {"rows": batch, "row_len": int(lens.max()), "k": k, "us_sorted": timing["sorted"],
+                              "us_ascending": timing["ascending"], "same_set_as_ascending_form_and_ordered": ok}
+        log(f"{name}: torch.topk-shaped top-k {timing['sorted']:.1f} us (ascending {timing['ascending']:.1f} us); "
+            f"ordered: {ok}")
+    del dev, ws, tk_ws, scores, at_ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_rooflines(dec):
+    us = dec["kernel_us"]
+    return {
+        "roofline_decode_step": {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": dec["gbs"] / PEAK_HBM_GBS, "algorithmic_bytes_per_step": dec["bytes_step"]},
+        "roofline_decode_indexer": hbm_roofline("indexer_decode_coop_kernel",
+                                                f"indexer_decode_coop_kernel@{dec['name']}", us["indexer"] * 1e-3,
+                                                dec["idx_bytes"] + dec["score_bytes"]),
+        "roofline_decode_attn": hbm_roofline("decode sparse attention (split partials + combine)",
+                                             f"sparse_attn_kernel@{dec['name']}", us["attention"] * 1e-3,
+                                             dec["attn_bytes"], ceiling=dec["attn_ceiling"],
+                                             note="each cache row is read by one query, so physical bytes equal "
+                                                  "algorithmic bytes: effective_algorithmic_gbs is the HBM rate"),
+    }
+
+
+def decode_summary(dec):
+    r = {"workload": dec["name"], "batch": dec["batch"], "s_max": dec["s_max"], "us_per_step": dec["us_median"],
+         "us_min": dec["us_min"], "kernel_us_separate_entry_points": dec["kernel_us"]}
+    r.update(decode_rooflines(dec))
+    return r
 
 
 def correlated_bench(args, dsa, inp):
@@ -332,120 +604,6 @@ def correlated_bench(args, dsa, inp):
     del dev, ws, out, lse, idx, r16, m16
     torch.cuda.empty_cache()
     return out_j
-
-
-def decode_bench(args, dsa, inp):
-    import torch
-    t0 = time.time()
-    di = inp.workload(args.decode_workload)
-    log(f"generated {args.decode_workload} inputs in {time.time() - t0:.1f}s")
-    dev = dsa.upload_decode_inputs(di)
-    batch, hq, d = di.q.shape
-    s_max, hkv = di.k_cache.shape[1], di.k_cache.shape[2]
-    h_idx, d_idx = di.q_idx.shape[1], di.q_idx.shape[2]
-    k = di.top_k
-    ws = torch.empty(dsa.dsa_decode_workspace_size(batch, s_max, hq, hkv, d, h_idx, d_idx, k), dtype=torch.uint8,
-                     device="cuda")
-    out = torch.empty_like(dev["q"])
-    lse = torch.empty(batch, hq, dtype=torch.float32, device="cuda")
-    idx = torch.empty(batch, k, dtype=torch.int32, device="cuda")
-    max_len = int(di.seq_lens.max())
-
-    def step():
-        dsa.dsa_decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
-                       dev["seq_lens"], max_len, k, out, lse, idx, ws)
-
-    for _ in range(3):
-        step()
-    torch.cuda.synchronize()
-    n_iter = max(20, args.steps * 4)
-    evs = []
-    for _ in range(n_iter):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        step()
-        b.record()
-        evs.append((a, b))
-    torch.cuda.synchronize()
-    times = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    us_median = times[len(times) // 2]
-    us_min = times[0]
-    lens = di.seq_lens.astype(np.int64)
-    bytes_step = int((lens * d_idx * 2).sum() + (lens * 4 * 2).sum()
-                     + (np.minimum(lens, k) * (2 * hkv * d * 2 + 4)).sum() + batch * hq * d * 2 * 2)
-    log(f"decode median {us_median:.1f} us (min {us_min:.1f})")
-
-    # The same step captured once in a HIP graph and replayed: no host launch work per step.
-    eager = (out.clone(), lse.clone(), idx.clone())
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        step()
-    for _ in range(3):
-        graph.replay()
-    torch.cuda.synchronize()
-    gevs = []
-    for _ in range(n_iter):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b.record()
-        gevs.append((a, b))
-    torch.cuda.synchronize()
-    gtimes = sorted(a.elapsed_time(b) * 1e3 for a, b in gevs)
-    graph_same = bool(torch.equal(out, eager[0]) and torch.equal(lse, eager[1]) and torch.equal(idx, eager[2]))
-    graph_us = {"median": gtimes[len(gtimes) // 2], "min": gtimes[0], "same_outputs_as_eager": graph_same}
-    log(f"decode in a HIP graph: median {graph_us['median']:.1f} us (min {graph_us['min']:.1f}); "
-        f"outputs equal to the eager call: {graph_same}")
-    del graph
-
-    # The torch.topk-shaped top-k on the decode step's own scores (the first region of the decode
-    # workspace, left there by the last step), beside the ascending form.
-    ld = (s_max + 3) // 4 * 4
-    scores = ws.view(torch.float32)[: batch * ld].view(batch, ld)
-    row_len = dev["seq_lens"]
-    tk_ws = torch.empty(dsa.dsa_topk_workspace_size(batch, ld, k), dtype=torch.uint8, device="cuda")
-    idx_s = torch.empty(batch, k, dtype=torch.int32, device="cuda")
-    val_s = torch.empty(batch, k, dtype=torch.float32, device="cuda")
-    timing = {}
-    for name, fn in (("ascending", dsa.dsa_topk), ("sorted", dsa.dsa_topk_sorted)):
-        for _ in range(3):
-            fn(scores, row_len, k, idx_s, val_s, workspace=tk_ws)
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(20):
-            fn(scores, row_len, k, idx_s, val_s, workspace=tk_ws)
-        b.record()
-        torch.cuda.synchronize()
-        timing[name] = a.elapsed_time(b) * 1e3 / 20
-        if name == "ascending":
-            asc_i = idx_s.cpu().numpy().copy()
-    # The sorted form holds the ascending form's set, by descending value (equal values by position).
-    got_i = idx_s.cpu().numpy()
-    got_v = val_s.cpu().numpy()
-    ok = True
-    for j in range(batch):
-        order_ok = bool(np.all((got_v[j, :-1] > got_v[j, 1:]) |
-                               ((got_v[j, :-1] == got_v[j, 1:]) & (got_i[j, :-1] < got_i[j, 1:]))))
-        ok = ok and order_ok and bool(np.array_equal(np.sort(got_i[j]), asc_i[j]))
-    topk_sorted = {"rows": batch, "row_len": int(lens.max()), "k": k, "us_sorted": timing["sorted"],
-                   "us_ascending": timing["ascending"], "same_set_as_ascending_form_and_ordered": ok}
-    log(f"torch.topk-shaped top-k {timing['sorted']:.1f} us (ascending form {timing['ascending']:.1f} us); "
-        f"same set as the ascending form, ordered: {ok}")
-    del dev, ws, tk_ws
-    torch.cuda.empty_cache()
-    return dict(us_median=us_median, us_min=us_min, graph_us=graph_us, bytes_step=bytes_step,
-                gbs=bytes_step / (us_median * 1e-6) / 1e9, batch=batch, s_max=s_max,
-                topk_sorted=topk_sorted)
 
 
 def attn_bwd_bench(args, dsa, inp):
@@ -568,44 +726,6 @@ def warmup_bench(args, dsa, inp):
                     "causal pair"}
 
 
-def measured_peaks(dsa):
-    """What the box reaches on the two priced resources (the library's probe kernels): an
-    MFMA-only loop of 16x16x32 and of 32x32x16 bf16 instructions, and a streaming read of 4 GiB.
-    Best of several timed launches each."""
-    import torch
-
-    def best_ms(fn, reps):
-        fn()
-        torch.cuda.synchronize()
-        out = []
-        for _ in range(reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            torch.cuda.synchronize()
-            out.append(a.elapsed_time(b))
-        return min(out)
-
-    grid, iters = 2048, 20000
-    sink = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
-    res = {}
-    for shape in (16, 32):
-        flops = dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink)
-        ms = best_ms(lambda: dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink), 5)
-        res[f"mfma_bf16_{shape}x{shape}x{512 // shape}_tflops"] = flops / (ms * 1e-3) / 1e12
-    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
-    best = {g: buf.numel() / (best_ms(lambda: dsa.dsa_probe_stream_read(buf, g, sink), 6) * 1e-3) / 1e9
-            for g in (2048, 8192, 16384, 32768, 65536)}
-    res["stream_read_gbs"] = max(best.values())
-    res["stream_read_gbs_by_grid"] = best
-    del buf, sink
-    torch.cuda.empty_cache()
-    log(f"measured peaks: {res}")
-    return res
-
-
 def _sdpa_first_backend(torch, fn):
     """Run fn under the first fused SDPA backend that accepts it (flash, then memory-efficient;
     never the math backend, which would materialise the score matrix).  Returns (name, result)."""
@@ -699,9 +819,45 @@ def dense_bench(args, dsa, inp, dsa_prefill_ms, dsa_decode_us):
     return res
 
 
-def cpu_baseline(args, pi):
-    """The oracle as it stands, on a bounded sample of rows of the same workload (the only leg of
-    the benchmark that runs it)."""
+def measured_peaks(dsa):
+    """What the box reaches on the two priced resources (the probe library): an MFMA-only loop of
+    16x16x32 and of 32x32x16 bf16 instructions, and a streaming read of 4 GiB.  Best of several
+    timed launches each."""
+    import torch
+
+    grid, iters = 2048, 20000
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+    res = {}
+    for shape in (16, 32):
+        flops = dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink)
+        ms = best_ms(lambda: dsa.dsa_probe_mfma_bf16(shape, grid, iters, sink), 5)
+        res[f"mfma_bf16_{shape}x{shape}x{512 // shape}_tflops"] = flops / (ms * 1e-3) / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    best = {g: buf.numel() / (best_ms(lambda: dsa.dsa_probe_stream_read(buf, g, sink), 6) * 1e-3) / 1e9
+            for g in (2048, 8192, 16384, 32768, 65536)}
+    res["stream_read_gbs"] = max(best.values())
+    res["stream_read_gbs_by_grid"] = best
+    del buf, sink
+    torch.cuda.empty_cache()
+    log(f"measured peaks: {res}")
+    return res
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(args, pre, dec):
+    """The oracle as it stands, on a bounded sample of rows of the same 128K workload (the only leg of
+    the benchmark that runs it): its whole-job rate extrapolated by causal work, and its agreement
+    with the timed run's outputs on those rows (index mismatches, max / mean absolute O error, lse
+    error), plus every row of the timed decode step."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import dsa_testlib as tl
     try:
@@ -709,22 +865,56 @@ def cpu_baseline(args, pi):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    pi = pre["pi"]
+    smp = pre["samples"]
     total = sum(int(x) for x in pi.seq_lens)
-    rng = np.random.default_rng(123)
-    rows = rng.integers(0, total, 4096).tolist()
+    rows = smp["rows"]
     done = 0
+    idx_rows_bad = idx_slots_bad = 0
+    err_max = err_sum = lse_max = 0.0
+    n_err = 0
     t0 = time.perf_counter()
     while done < len(rows) and time.perf_counter() - t0 < args.cpu_seconds:
-        tl.oracle_prefill_rows_lazy(pi, rows[done:done + 4])
+        want = tl.oracle_prefill_rows_lazy(pi, rows[done:done + 4])
+        got_i = smp["idx"][done:done + 4]
+        bad = got_i != want["idx"]
+        idx_rows_bad += int(bad.any(axis=1).sum())
+        idx_slots_bad += int(bad.sum())
+        e = np.abs(smp["out"][done:done + 4].astype(np.float64) - want["out"])
+        err_max = max(err_max, float(e.max()))
+        err_sum += float(e.sum())
+        n_err += e.size
+        lse_max = max(lse_max, float(np.abs(smp["lse"][done:done + 4] - want["lse"]).max()))
         done += 4
     el = time.perf_counter() - t0
     work_sample = sum(r + 1 for r in rows[:done])           # indexer work grows with the prefix length
     work_all = total * (total + 1) / 2
     rows_per_s = done / el
     tokens_per_s = total / (el * work_all / work_sample)     # whole-job rate, extrapolated by work
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} uniformly drawn rows of the 128K prefill in {el:.1f}s ({rows_per_s:.2f} rows/s); "
-                      f"whole-job rate extrapolated by causal work (sum of t+1)"}
+    res = {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} uniformly drawn rows of the 128K prefill in {el:.1f}s ({rows_per_s:.2f} rows/s); "
+                     f"whole-job rate extrapolated by causal work (sum of t+1)",
+           "host_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(),
+           "parity_vs_timed_prefill": {"rows": done, "index_mismatch_rows": idx_rows_bad,
+                                       "index_mismatch_slots": idx_slots_bad, "out_max_abs": err_max,
+                                       "out_mean_abs": err_sum / max(1, n_err), "lse_max_abs": lse_max,
+                                       "tolerance": {"out_max_abs": tl.MAX_ABS, "out_mean_abs": tl.MEAN_ABS,
+                                                     "lse_max_abs": tl.LSE_ABS}}}
+    if dec is not None:
+        t1 = time.perf_counter()
+        di = dec["di"]
+        batch = di.q.shape[0]
+        want = tl.oracle_decode_rows_lazy(di, range(batch))
+        got = dec["samples"]
+        bad = got["idx"] != np.asarray(want["idx"])
+        e = np.abs(got["out"].astype(np.float64) - np.asarray(want["out"]))
+        res["parity_vs_timed_decode"] = {
+            "workload": dec["name"], "rows": batch, "index_mismatch_rows": int(bad.any(axis=1).sum()),
+            "index_mismatch_slots": int(bad.sum()), "out_max_abs": float(e.max()), "out_mean_abs": float(e.mean()),
+            "lse_max_abs": float(np.abs(got["lse"] - np.asarray(want["lse"])).max()),
+            "oracle_s": time.perf_counter() - t1}
+    log(f"cpu baseline: {res}")
+    return res
 
 
 def main():
@@ -742,19 +932,30 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dsa.load()
-    pre = prefill_bench(args, dsa, inp)
+    pre = prefill_section(args, dsa, inp, args.workload, args.steps, args.warmup, full=True)
     peaks = measured_peaks(dsa)
     corr = None if args.no_correlated else correlated_bench(args, dsa, inp)
-    dec = None if args.no_decode else decode_bench(args, dsa, inp)
+    dec = None if args.no_decode else decode_section(args, dsa, inp, args.decode_workload, full=True)
+    extra = {}
+    if not args.no_extra:
+        for name in EXTRA_PREFILL:
+            extra[name] = prefill_summary(prefill_section(args, dsa, inp, name, min(args.steps, 5), 1, full=False))
+        if not args.no_decode:
+            for name in EXTRA_DECODE:
+                extra[name] = decode_summary(decode_section(args, dsa, inp, name, full=False))
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp)
     wup = None if args.no_bwd else warmup_bench(args, dsa, inp)
     dense = None if args.no_dense else dense_bench(args, dsa, inp, pre["ms_per_step"],
                                                    None if dec is None else dec["us_median"])
-    cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre["pi"])
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, pre, dec)
 
     total = pre["rows_total"]
     value = total / (pre["ms_per_step"] * 1e-3)
     kern = pre["kern"]
+    attn_ms = kern["sparse_attn"] / pre["launches"]["sparse_attn"]
+    roof = indexer_roofline(pre, f"indexer_prefill_kernel@{pre['name']}")
+    roof["measured_peak"] = peaks["mfma_bf16_16x16x32_tflops"]
+    roof["frac_of_measured_peak"] = pre["idx_tflops"] / peaks["mfma_bf16_16x16x32_tflops"]
     line = {
         "metric": "DSA prefill tokens/s at 128K (k=2048) + decode µs/step; % HBM/MFMA peak",
         "value": value,
@@ -774,31 +975,30 @@ def main():
         "separate_entry_points_ms_per_step": pre["sep_ms"],
         "kernel_ms_per_step": kern,
         "kernel_launches_per_step": pre["launches"],
-        "roofline": {"bound": "mfma", "kernel": "indexer_prefill", "achieved": pre["idx_tflops"],
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": counter_traffic("indexer_prefill_kernel@prefill_128k"),
-                     "traffic_unit": "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)",
-                     "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
-                     "measured_peak": peaks["mfma_bf16_16x16x32_tflops"],
-                     "frac_of_measured_peak": pre["idx_tflops"] / peaks["mfma_bf16_16x16x32_tflops"],
-                     "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]},
-        "roofline_sparse_attn": {"bound": "hbm", "kernel": "sparse_attn_union (8-row blocks)",
-                                 "achieved": pre["attn_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                 "frac": pre["attn_gbs"] / PEAK_HBM_GBS,
-                                 "measured_peak": peaks["stream_read_gbs"],
-                                 "frac_of_measured_peak": pre["attn_gbs"] / peaks["stream_read_gbs"],
-                                 "traffic": counter_traffic("sparse_attn_union_kernel@prefill_128k"),
-                                 "algorithmic_bytes_per_launch": pre["merged_bytes"],
-                                 "mfma_tflops": pre["attn_tflops"], "mfma_frac": pre["attn_tflops"] / PEAK_BF16_TFLOPS,
-                                 "bytes_without_dedup": pre["attn_bytes"]},
+        "roofline": roof,
+        "roofline_sparse_attn": hbm_roofline(
+            "sparse_attn_union_kernel (8-row merged sets)", f"sparse_attn_union_kernel@{pre['name']}", attn_ms,
+            pre["merged_bytes"], ceiling=pre.get("ceiling_merged"),
+            mfma_tflops=pre["attn_tflops"], mfma_frac=pre["attn_tflops"] / PEAK_BF16_TFLOPS,
+            bytes_without_dedup=pre["attn_bytes"],
+            note="merged K/V rows are re-read by neighbouring blocks through L2 and the Infinity Cache, so the "
+                 "effective algorithmic rate can exceed the HBM peak; the counter rate is the L2-miss traffic"),
+        "roofline_sparse_attn_per_row": hbm_roofline(
+            "sparse_attn_kernel (per row, the path without dedup)", f"sparse_attn_kernel@{pre['name']}",
+            pre["per_row_attn_ms"], pre["attn_bytes"], ceiling=pre.get("ceiling_per_row")),
         "roofline_query_union": {"bound": "hbm", "achieved": pre["union_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": pre["union_gbs"] / PEAK_HBM_GBS,
                                  "algorithmic_bytes_per_launch": pre["union_bytes"]},
-        "measured_peaks": peaks,
-        "dedup": pre["dedup"],
-        "prefill_correlated_queries": corr,
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": pre["topk_gbs"] / PEAK_HBM_GBS},
+                          "frac": pre["topk_gbs"] / PEAK_HBM_GBS,
+                          "algorithmic_bytes_per_step": pre["topk_bytes"]},
+        "measured_peaks": peaks,
+        "dedup": {"block_rows": pre["block_rows"], "merged_rows_per_block_mean": pre["merged_rows_per_block_mean"],
+                  "index_slots_per_block": pre["block_rows"] * 2048, "merged_fraction": pre["merged_fraction"],
+                  "prefill_ms_without_dedup": pre["no_dedup_ms"],
+                  "max_abs_out_vs_per_row": pre["max_abs_out_vs_per_row"],
+                  "union16_at_t": pre["union16_at_t"], "union16_mean": pre["union16_mean"]},
+        "prefill_correlated_queries": corr,
         "cpu_baseline": cpu,
     }
     if dec is not None:
@@ -806,10 +1006,15 @@ def main():
         line["decode_us_min"] = dec["us_min"]
         line["decode_us_per_step_hip_graph"] = dec["graph_us"]
         line["decode_config"] = {"workload": "decode_b32_128k: batch 32, 131072-token caches, k=2048"}
-        line["roofline_decode"] = {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                   "frac": dec["gbs"] / PEAK_HBM_GBS,
-                                   "frac_of_measured_peak": dec["gbs"] / peaks["stream_read_gbs"]}
+        line["decode_kernel_us_separate_entry_points"] = dec["kernel_us"]
+        dr = decode_rooflines(dec)
+        line["roofline_decode"] = dict(dr["roofline_decode_step"],
+                                       frac_of_measured_peak=dec["gbs"] / peaks["stream_read_gbs"])
+        line["roofline_decode_indexer"] = dr["roofline_decode_indexer"]
+        line["roofline_decode_attn"] = dr["roofline_decode_attn"]
         line["topk_sorted_decode_scores"] = dec["topk_sorted"]
+    for name, summary in extra.items():
+        line[name] = summary
     if bwd is not None:
         line["sparse_attn_backward"] = bwd
     if wup is not None:

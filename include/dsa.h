@@ -220,6 +220,27 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v,
                         void* out, float* lse, void* stream);
 
 /*
+ * Sparse GQA attention of one new token per sequence over selected positions of a contiguous KV
+ * cache (the attention step of dsa_decode; digest section 八, DSA-specific decode).
+ *
+ * q   [batch, hq, head_dim] bf16              the new token of each sequence
+ * k_cache, v_cache [batch, s_max, hkv, head_dim] bf16
+ * idx [batch, k_sel] int32                   positions into cache[b, 0 : seq_lens[b]]; entries < 0 or
+ *                                            >= seq_lens[b] are ignored
+ * seq_lens [batch] int32 (device)            1 <= seq_lens[b] <= s_max
+ * out [batch, hq, head_dim] bf16, lse [batch, hq] float or NULL   as for dsa_sparse_gqa_attn
+ * workspace  at least dsa_sparse_gqa_attn_decode_workspace_size bytes (per-split partials; 0 bytes
+ *            and NULL allowed when that size is 0), 16-byte aligned; contents on return unspecified.
+ * The index entries of a sequence are split into ranges attended in parallel and merged by their
+ * (max, sum) pairs, so the result equals dsa_sparse_gqa_attn's on the same positions up to rounding.
+ */
+int dsa_sparse_gqa_attn_decode_workspace_size(int batch, int hq, int hkv, int k_sel, size_t* bytes);
+int dsa_sparse_gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* idx,
+                               int k_sel, const int32_t* seq_lens, int batch, int s_max, int hq, int hkv,
+                               int head_dim, float softmax_scale, void* out, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * Adjacent-query dedup, step 1 (digest section 八: neighbouring query tokens select largely the
  * same positions, so the top-k sets of 16 adjacent queries are de-duplicated and the attention
  * kernel masks inside its matrix tiles).

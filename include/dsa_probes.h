@@ -48,14 +48,17 @@ int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sin
  * group g, split) reads, for every index entry p >= 0 of its row (idx [rows, k_sel] int32, the
  * row's entries split into nsplit ranges of 32-entry chunks), the key row and the value row
  * k[P, g, :], v[P, g, :] with P = row * row_stride + p (256 bytes each; P >= n_pos reads row 0),
- * with the same 16-byte loads and `depth` (1, 2 or 4) chunks of 32 entries in flight.  Work
- * order: KV group slowest (group_fastest = 0, the prefill kernels') or fastest (the decode
- * kernel's).  k, v [n_pos, hkv, 128] bf16, 16-byte aligned.  sink [sink_len] uint32 with
- * sink_len >= the number of workgroups, ceil(rows * hkv * nsplit / 4) rounded up to 8.
+ * with 16-byte loads and `depth` (1, 2 or 4) chunks of 32 entries in flight.  Load shape:
+ * whole_rows = 0 reads as the per-row attention kernel does (each lane 64 contiguous bytes of one
+ * entry's row, 16 rows per instruction); whole_rows = 1 lets 16 lanes read one whole 256-byte row
+ * (4 rows per instruction, the shape of the kernels' row copies into LDS).  Work order: KV group
+ * slowest (group_fastest = 0, the prefill kernels') or fastest (the decode kernel's).
+ * k, v [n_pos, hkv, 128] bf16, 16-byte aligned.  sink [sink_len] uint32 with sink_len >= the
+ * number of workgroups, ceil(rows * hkv * nsplit / 4) rounded up to 8.
  */
 int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const int32_t* idx, int k_sel, int rows,
-                     int nsplit, int64_t row_stride, int group_fastest, int depth, uint32_t* sink, int64_t sink_len,
-                     void* stream);
+                     int nsplit, int64_t row_stride, int group_fastest, int depth, int whole_rows, uint32_t* sink,
+                     int64_t sink_len, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ EXPORTED = (
     "dsa_prefill_workspace_size", "dsa_prefill", "dsa_decode_workspace_size", "dsa_decode", "dsa_attn_head_mean",
     "dsa_indexer_kl", "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union",
     "dsa_sparse_gqa_attn_union", "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
-    "dsa_decode_noalloc",
+    "dsa_decode_noalloc", "dsa_sparse_gqa_attn_decode_workspace_size", "dsa_sparse_gqa_attn_decode",
 )
 # The measurement probes (include/dsa_probes.h), a separate library used by the benchmark.
 PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather")
@@ -85,6 +85,8 @@ def load():
         "dsa_decode_workspace_size": ([_I, _I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
         "dsa_decode": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                         _P], _I),
+        "dsa_sparse_gqa_attn_decode_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_sparse_gqa_attn_decode": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _SZ, _P], _I),
         "dsa_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
                                _I),
     }
@@ -111,7 +113,7 @@ def load_probes():
         "dsa_probe_last_error": ([], ctypes.c_char_p),
         "dsa_probe_mfma_bf16": ([_I, _I, _I, _P, ctypes.POINTER(ctypes.c_longlong), _P], _I),
         "dsa_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
-        "dsa_probe_gather": ([_P, _P, _I64, _I, _P, _I, _I, _I, _I64, _I, _I, _P, _I64, _P], _I),
+        "dsa_probe_gather": ([_P, _P, _I64, _I, _P, _I, _I, _I, _I64, _I, _I, _I, _P, _I64, _P], _I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -250,6 +252,29 @@ def dsa_sparse_gqa_attn(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=N
     _check(load().dsa_sparse_gqa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), idx.shape[1], _ptr(cu_seqlens),
                                       cu_seqlens.shape[0] - 1, total, hq, hkv, d, scale, _ptr(out), _ptr(lse),
                                       _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_decode_workspace_size(batch, hq, hkv, k_sel) -> int:
+    n = _SZ(0)
+    _check(load().dsa_sparse_gqa_attn_decode_workspace_size(batch, hq, hkv, k_sel, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_sparse_gqa_attn_decode(q, k_cache, v_cache, idx, seq_lens, out, lse=None, softmax_scale=None, workspace=None,
+                               stream=None):
+    """Sparse GQA attention of each sequence's new token over idx[b, :] positions of its cache;
+    allocates the workspace when none is given."""
+    import torch
+    batch, hq, d = q.shape
+    s_max, hkv = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if workspace is None:
+        nbytes = dsa_sparse_gqa_attn_decode_workspace_size(batch, hq, hkv, idx.shape[1])
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(load().dsa_sparse_gqa_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), idx.shape[1],
+                                             _ptr(seq_lens), batch, s_max, hq, hkv, d, scale, _ptr(out), _ptr(lse),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream)))
 
 
 def dsa_query_union_size(total_tokens, k_sel, block_rows=16):
@@ -437,11 +462,12 @@ def dsa_probe_stream_read(src, grid, sink, stream=None):
                                                      _stream(stream)))
 
 
-def dsa_probe_gather(k, v, idx, sink, nsplit=1, row_stride=0, group_fastest=False, depth=2, stream=None):
+def dsa_probe_gather(k, v, idx, sink, nsplit=1, row_stride=0, group_fastest=False, depth=2, whole_rows=False,
+                     stream=None):
     """Enqueue the gather probe: the key and value rows the sparse attention reads for index sets
     idx[rows, k_sel] over k, v [n_pos, hkv, 128] (position row * row_stride + p)."""
     n_pos, hkv = k.shape[0], k.shape[1]
     rows, k_sel = idx.shape
     _check_probe(load_probes().dsa_probe_gather(_ptr(k), _ptr(v), n_pos, hkv, _ptr(idx), k_sel, rows, nsplit,
-                                                row_stride, int(bool(group_fastest)), depth, _ptr(sink), sink.numel(),
-                                                _stream(stream)))
+                                                row_stride, int(bool(group_fastest)), depth, int(bool(whole_rows)),
+                                                _ptr(sink), sink.numel(), _stream(stream)))

@@ -210,6 +210,40 @@ int decode_nsplit(int batch, int hkv, int top_k) {
   return std::max(1, std::min(want, nchunk));
 }
 
+// Decode attention over a contiguous cache: partials of nsplit index ranges per (sequence, group),
+// then their combine.  `part` holds decode_attn_part_bytes(batch, hq, nsplit) bytes.
+size_t decode_attn_part_bytes(int batch, int hq, int nsplit) {
+  return nsplit > 1 ? (size_t)batch * hq * nsplit * (128 + 2) * 4 : 0;
+}
+
+hipError_t launch_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* idx, int k_sel,
+                              const int32_t* seq_lens, int batch, int s_max, int hq, int hkv, float softmax_scale,
+                              void* out, float* lse, void* part, hipStream_t s) {
+  const int nsplit = decode_nsplit(batch, hkv, k_sel);
+  dsa::SparseAttnArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = nullptr;
+  a.batch = batch;
+  a.seq_lens = seq_lens;
+  a.s_max = s_max;
+  a.rows = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.nsplit = nsplit;
+  a.part_o = static_cast<float*>(part);
+  a.part_ml = a.part_o + (size_t)batch * hq * nsplit * 128;
+  hipError_t e = dsa::launch_sparse_attn(a, s);
+  if (e != hipSuccess || nsplit == 1) return e;
+  return dsa::launch_attn_combine(a, s);
+}
+
 int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu, int batch,
                       int h_idx, int d_idx, int row_begin, int row_end, int out_row0, float* scores, long long ld,
                       hipStream_t stream) {
@@ -866,10 +900,9 @@ int dsa_decode_workspace_size(int batch, int s_max, int hq, int hkv, int head_di
   DSA_TRY(check_indexer_shape(h_idx, d_idx));
   DSA_TRY(check_topk(top_k));
   const long long ld = round_up(s_max, 4);
-  const long long nsplit = decode_nsplit(batch, hkv, top_k);
   const long long score_bytes = (long long)batch * ld * 4;
-  const long long part_bytes = (long long)batch * hq * nsplit * (128 + 2) * 4;
-  *bytes = (size_t)(round_up(score_bytes, 256) + topk_scratch(batch, ld) + part_bytes);
+  const size_t part_bytes = decode_attn_part_bytes(batch, hq, decode_nsplit(batch, hkv, top_k));
+  *bytes = (size_t)round_up(score_bytes, 256) + topk_scratch(batch, ld) + part_bytes;
   return DSA_OK;
 }
 
@@ -908,12 +941,10 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const long long ld = round_up(s_max, 4);
-  const int nsplit = decode_nsplit(batch, hkv, top_k);
   float* scores = static_cast<float*>(workspace);
   char* after_scores = static_cast<char*>(workspace) + round_up((long long)batch * ld * 4, 256);
   void* topk_ws = topk_scratch(batch, ld) ? static_cast<void*>(after_scores) : nullptr;
-  float* part_o = reinterpret_cast<float*>(after_scores + topk_scratch(batch, ld));
-  float* part_ml = part_o + (size_t)batch * hq * nsplit * 128;
+  void* part = after_scores + topk_scratch(batch, ld);
 
   dsa::IndexerDecodeArgs ia;
   ia.q_idx = static_cast<const uint16_t*>(q_idx);
@@ -941,28 +972,47 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   t.workspace = topk_ws;
   DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
 
-  dsa::SparseAttnArgs a = {};
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_cache);
-  a.v = static_cast<const uint16_t*>(v_cache);
-  a.idx = idx_out;
-  a.k_sel = top_k;
-  a.cu_seqlens = nullptr;
-  a.batch = batch;
-  a.seq_lens = seq_lens;
-  a.s_max = s_max;
-  a.rows = batch;
-  a.hq = hq;
-  a.hkv = hkv;
-  a.softmax_scale = softmax_scale;
-  a.out = static_cast<uint16_t*>(out);
-  a.lse = lse;
-  a.nsplit = nsplit;
-  a.part_o = part_o;
-  a.part_ml = part_ml;
-  if (nsplit == 1) return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
-  DSA_TRY(hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch"));
-  return hip_status(dsa::launch_attn_combine(a, s), "combine launch");
+  return hip_status(launch_decode_attn(q, k_cache, v_cache, idx_out, top_k, seq_lens, batch, s_max, hq, hkv,
+                                       softmax_scale, out, lse, part, s),
+                    "decode attention launch");
+}
+
+int dsa_sparse_gqa_attn_decode_workspace_size(int batch, int hq, int hkv, int k_sel, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (batch <= 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "batch and k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, 128));
+  *bytes = decode_attn_part_bytes(batch, hq, decode_nsplit(batch, hkv, k_sel));
+  return DSA_OK;
+}
+
+int dsa_sparse_gqa_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* idx, int k_sel,
+                               const int32_t* seq_lens, int batch, int s_max, int hq, int hkv, int head_dim,
+                               float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn_decode", "batch=%d s_max=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, s_max, hq, hkv,
+               k_sel, workspace_bytes);
+  DSA_NONNULL(q);
+  DSA_NONNULL(k_cache);
+  DSA_NONNULL(v_cache);
+  DSA_NONNULL(idx);
+  DSA_NONNULL(seq_lens);
+  DSA_NONNULL(out);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k_cache);
+  DSA_ALIGNED(v_cache);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(workspace);
+  if (batch <= 0 || s_max <= 0) return fail(DSA_ERR_INVALID_ARG, "batch and s_max must be positive");
+  if (k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  const size_t need = decode_attn_part_bytes(batch, hq, decode_nsplit(batch, hkv, k_sel));
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
+  return hip_status(launch_decode_attn(q, k_cache, v_cache, idx, k_sel, seq_lens, batch, s_max, hq, hkv,
+                                       softmax_scale, out, lse, workspace, static_cast<hipStream_t>(stream)),
+                    "decode attention launch");
 }
 
 }  // extern "C"

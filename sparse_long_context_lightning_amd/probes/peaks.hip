@@ -74,10 +74,13 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 }
 
 // Gather: the sparse attention's memory traffic with nothing else.  One wave per (row, KV
-// group, split) in the attention kernels' work orders; per chunk of 32 index entries each lane
-// reads 64 contiguous bytes of the key row and of the value row of two entries (the same 16-byte
-// loads the attention issues), DEPTH chunks in flight, and folds the data into one word.
-template <int DEPTH>
+// group, split) in the attention kernels' work orders; per chunk of 32 index entries the wave
+// reads the 32 key rows and 32 value rows with 16 loads of 16 bytes per lane, DEPTH chunks in
+// flight, and folds the data into one word.  Load shape 0 (the per-row attention kernel's): lane
+// (n, q) reads 64 contiguous bytes of entries n and 16 + n, four 16-byte pieces, so one
+// instruction touches 16 rows; shape 1 (whole rows): the 16 lanes of a lane group read one
+// 256-byte row, so one instruction covers four whole rows.
+template <int DEPTH, int SHAPE>
 __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                      long long n_pos, const int* __restrict__ idx, int k_sel, int rows,
                                                      int hkv, int nsplit, long long row_stride, int group_fastest,
@@ -111,25 +114,38 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
   const int* idx_row = idx + (long long)row * k_sel;
   const long long base = (long long)row * row_stride;
   const size_t pos_stride = (size_t)hkv * 128;
-  const uint16_t* kb = k + (size_t)g * 128 + lg * 32;
-  const uint16_t* vb = v + (size_t)g * 128 + lg * 32;
+  const uint16_t* kb = k + (size_t)g * 128 + (SHAPE == 0 ? lg * 32 : n * 8);
+  const uint16_t* vb = v + (size_t)g * 128 + (SHAPE == 0 ? lg * 32 : n * 8);
   u32x4 acc = {0u, 0u, 0u, 0u};
   for (int c0 = c_begin; c0 < c_end; c0 += DEPTH) {
     u32x4 buf[DEPTH][2][8];
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
+      if (SHAPE == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int s = (c0 + d) * 32 + 16 * j + n;
-        int p = (c0 + d < c_end && s < k_sel) ? idx_row[s] : -1;
-        long long pos = p >= 0 ? base + p : 0;
-        pos = pos < n_pos ? pos : 0;
-        const uint16_t* kp = kb + (size_t)pos * pos_stride;
-        const uint16_t* vp = vb + (size_t)pos * pos_stride;
+        for (int j = 0; j < 2; ++j) {
+          const int s = (c0 + d) * 32 + 16 * j + n;
+          int p = (c0 + d < c_end && s < k_sel) ? idx_row[s] : -1;
+          long long pos = p >= 0 ? base + p : 0;
+          pos = pos < n_pos ? pos : 0;
+          const uint16_t* kp = kb + (size_t)pos * pos_stride;
+          const uint16_t* vp = vb + (size_t)pos * pos_stride;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          buf[d][j][q] = ldg16(kp + q * 8);
-          buf[d][j][4 + q] = ldg16(vp + q * 8);
+          for (int q = 0; q < 4; ++q) {
+            buf[d][j][q] = ldg16(kp + q * 8);
+            buf[d][j][4 + q] = ldg16(vp + q * 8);
+          }
+        }
+      } else {
+        // instruction j reads entries 4 j + lg whole (lane n: bytes 16 n .. 16 n + 15)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int s = (c0 + d) * 32 + 4 * j + lg;
+          int p = (c0 + d < c_end && s < k_sel) ? idx_row[s] : -1;
+          long long pos = p >= 0 ? base + p : 0;
+          pos = pos < n_pos ? pos : 0;
+          buf[d][j >> 2][j & 3] = ldg16(kb + (size_t)pos * pos_stride);
+          buf[d][j >> 2][4 + (j & 3)] = ldg16(vb + (size_t)pos * pos_stride);
         }
       }
     }
@@ -198,8 +214,8 @@ int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sin
 }
 
 int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const int32_t* idx, int k_sel, int rows,
-                     int nsplit, int64_t row_stride, int group_fastest, int depth, uint32_t* sink, int64_t sink_len,
-                     void* stream) {
+                     int nsplit, int64_t row_stride, int group_fastest, int depth, int whole_rows, uint32_t* sink,
+                     int64_t sink_len, void* stream) {
   g_probe_error[0] = 0;
   if (!k || !v || !idx || !sink) return probe_fail(DSA_PROBE_ERR_INVALID_ARG, "pointers must not be null");
   if (((reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v)) & 15u) != 0)
@@ -216,15 +232,19 @@ int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
-  if (depth == 1)
-    hipLaunchKernelGGL(gather_kernel<1>, dim3((unsigned)grid), dim3(256), 0, s, kk, vv, (long long)n_pos, idx, k_sel,
-                       rows, hkv, nsplit, (long long)row_stride, group_fastest, 0xFFFFFFFFu, sink);
-  else if (depth == 2)
-    hipLaunchKernelGGL(gather_kernel<2>, dim3((unsigned)grid), dim3(256), 0, s, kk, vv, (long long)n_pos, idx, k_sel,
-                       rows, hkv, nsplit, (long long)row_stride, group_fastest, 0xFFFFFFFFu, sink);
-  else
-    hipLaunchKernelGGL(gather_kernel<4>, dim3((unsigned)grid), dim3(256), 0, s, kk, vv, (long long)n_pos, idx, k_sel,
-                       rows, hkv, nsplit, (long long)row_stride, group_fastest, 0xFFFFFFFFu, sink);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, kk, vv, (long long)n_pos, idx, k_sel, rows, hkv,
+                       nsplit, (long long)row_stride, group_fastest, 0xFFFFFFFFu, sink);
+  };
+  if (whole_rows) {
+    if (depth == 1) go(gather_kernel<1, 1>);
+    else if (depth == 2) go(gather_kernel<2, 1>);
+    else go(gather_kernel<4, 1>);
+  } else {
+    if (depth == 1) go(gather_kernel<1, 0>);
+    else if (depth == 2) go(gather_kernel<2, 0>);
+    else go(gather_kernel<4, 0>);
+  }
   return launched("gather probe launch");
 }
 

@@ -26,7 +26,7 @@ def _declared(header=HEADER):
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -149,7 +149,7 @@ def test_probe_validation():
 
     def gather(**o):
         a = dict(k=FAKE, v=FAKE, n_pos=1024, hkv=4, idx=FAKE, k_sel=64, rows=100, nsplit=1, row_stride=0,
-                 group_fastest=0, depth=2, sink=FAKE, sink_len=1 << 20, stream=None)
+                 group_fastest=0, depth=2, whole_rows=0, sink=FAKE, sink_len=1 << 20, stream=None)
         a.update(o)
         return lib.dsa_probe_gather(*a.values())
 

@@ -154,7 +154,10 @@ def test_topk_random_rows_with_ties(dsa, seed):
     tl.check_index_structure(idx, lens, k)
 
 
-def test_topk_special_rows(dsa):
+# Up to 512 rows take the fused one-workgroup-per-row kernel, more rows the three-kernel path:
+# the special-row tests run both (the rows repeated past 512).
+@pytest.mark.parametrize("copies", [1, 65])
+def test_topk_special_rows(dsa, copies):
     n, k = 5000, 2048
     rows = []
     rows.append(np.zeros(n))                          # all equal -> fallback path, 0..k-1
@@ -174,23 +177,38 @@ def test_topk_special_rows(dsa):
     r[4000] = np.inf
     r[10] = -np.inf
     rows.append(r)
-    scores = np.stack(rows).astype(np.float32)
-    lens = [n] * len(rows)
+    scores = np.tile(np.stack(rows).astype(np.float32), (copies, 1))
+    lens = [n] * len(scores)
     idx, val = _run_topk(dsa, scores, lens, k)
-    _check_topk(scores, lens, k, idx, val)
+    _check_topk(scores[:len(rows)], lens[:len(rows)], k, idx[:len(rows)], val[:len(rows)])
+    for c in range(1, copies):
+        assert np.array_equal(idx[c * len(rows):(c + 1) * len(rows)], idx[:len(rows)])
     assert idx[0].tolist() == list(range(k))
     assert idx[2].tolist() == list(range(n - k, n))
 
 
-def test_topk_rows_that_overflow_the_candidate_buffer(dsa):
+@pytest.mark.parametrize("copies", [1, 129])
+def test_topk_rows_that_overflow_the_candidate_buffer(dsa, copies):
     # long runs of equal scores: more than 8192 positions tie at the threshold, so the row
     # takes the exact global-memory path; the result must still be the unique lowest-position set
     rng = np.random.default_rng(21)
     ld, k = 50000, 2048
     rows = [np.zeros(ld), (rng.random(ld) < 0.5).astype(np.float64), np.repeat(np.arange(10.0), ld // 10),
             rng.integers(0, 3, ld).astype(np.float64)]
-    scores = np.stack(rows).astype(np.float32)
-    lens = [ld, ld, ld, 20000]
+    scores = np.tile(np.stack(rows).astype(np.float32), (copies, 1))
+    lens = [ld, ld, ld, 20000] * copies
+    idx, val = _run_topk(dsa, scores, lens, k)
+    _check_topk(scores[:4], lens[:4], k, idx[:4], val[:4])
+    for c in range(1, copies):
+        assert np.array_equal(idx[4 * c:4 * c + 4], idx[:4])
+
+
+def test_topk_rows_of_262144(dsa):
+    """The longest rows the wave-parallel kernels take (the 256K decode's), with ties."""
+    rng = np.random.default_rng(19)
+    ld, k = 262144, 2048
+    scores = (rng.integers(0, 9000, size=(3, ld)) / 8.0).astype(np.float32)
+    lens = [ld, 262143, 150001]
     idx, val = _run_topk(dsa, scores, lens, k)
     _check_topk(scores, lens, k, idx, val)
 
@@ -512,3 +530,54 @@ def test_outputs_and_workspaces_leave_guard_bands_untouched(dsa):
     assert not torch.isnan(out.float()).any() and not torch.isnan(lse).any() and bool((idx != -99).all())
     want = tl.oracle_decode_rows_lazy(di, range(b))
     tl.assert_idx_equal(idx.cpu().numpy(), np.asarray(want["idx"]), what="guarded decode idx")
+
+
+# ------------------------------------------------------------------------------ decode attention alone
+
+@pytest.mark.parametrize("hq,hkv,k_sel,batch", [(32, 4, 2048, 6), (8, 2, 100, 5), (16, 1, 64, 3), (12, 4, 300, 2)])
+def test_decode_attention_matches_oracle(dsa, hq, hkv, k_sel, batch):
+    """dsa_sparse_gqa_attn_decode on drawn index sets (any order, with negative entries, entries at
+    or past the cache length, and repeats) against the oracle's per-row attention; rows with no
+    valid entry give O = 0 and lse = -inf."""
+    torch = _torch()
+    s_max = 4000
+    rng = np.random.default_rng(hq * 7 + k_sel)
+    seq = rng.integers(1, s_max + 1, size=batch)
+    seq[0] = s_max
+    di = inp.decode_inputs(batch, s_max, seq, 4, 64, hq, hkv, 128, k_sel, seed=300 + hq)
+    dev = tl.upload_decode(di)
+    idx = np.empty((batch, k_sel), dtype=np.int32)
+    for b in range(batch):
+        idx[b] = rng.integers(-5, int(seq[b]) + 5, size=k_sel)
+    idx[-1, :] = -1            # no valid entry at all
+    idx[0, 1] = idx[0, 0]      # a repeated position counts twice
+    idx_t = torch.from_numpy(idx).cuda()
+    out = torch.full_like(dev["q"], float("nan"))
+    lse = torch.full((batch, hq), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_gqa_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], idx_t, dev["seq_lens"], out, lse)
+    torch.cuda.synchronize()
+    got_o, got_l = tl.bf16_tensor_to_f64(out), lse.cpu().numpy()
+    scale = orc.default_softmax_scale(128)
+    for b in range(batch - 1):
+        n = int(seq[b])
+        sel = np.where((idx[b] >= 0) & (idx[b] < n), idx[b], -1)
+        o, l, _ = orc.sparse_gqa_attention_row(tl.f64(di.q[b]), tl.f64(di.k_cache[b, :n]), tl.f64(di.v_cache[b, :n]),
+                                               sel, scale)
+        tl.assert_attn_close(got_o[b], o, f"decode attention, sequence {b}")
+        assert np.max(np.abs(got_l[b] - l)) <= tl.LSE_ABS
+    assert np.all(got_o[-1] == 0.0) and np.all(np.isneginf(got_l[-1]))
+
+
+def test_decode_attention_is_the_decode_steps_attention(dsa):
+    """dsa_decode's outputs equal dsa_sparse_gqa_attn_decode's on dsa_decode's own index sets, bit for bit."""
+    torch = _torch()
+    seq = [3000, 1, 700, 2049]
+    di = inp.decode_inputs(len(seq), 3000, seq, 64, 128, 32, 4, 128, 2048, seed=808)
+    dev = tl.upload_decode(di)
+    out, lse, idx = dsa.decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
+                               dev["seq_lens"], 2048)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    dsa.dsa_sparse_gqa_attn_decode(dev["q"], dev["k_cache"], dev["v_cache"], idx, dev["seq_lens"], out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)

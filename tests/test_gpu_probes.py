@@ -20,8 +20,9 @@ def test_probes_run_and_store_nothing(dsa):
     assert torch.count_nonzero(sink).item() == 0
 
 
-@pytest.mark.parametrize("depth,group_fastest,nsplit", [(1, False, 1), (2, True, 4), (4, False, 2)])
-def test_gather_probe_runs_and_stores_nothing(dsa, depth, group_fastest, nsplit):
+@pytest.mark.parametrize("depth,group_fastest,nsplit,whole", [(1, False, 1, False), (2, True, 4, True),
+                                                              (4, False, 2, True), (2, False, 3, False)])
+def test_gather_probe_runs_and_stores_nothing(dsa, depth, group_fastest, nsplit, whole):
     import torch
     n_pos, hkv, rows, k_sel = 5000, 4, 300, 100   # ragged: 100 entries = 3 chunks + 4
     k = torch.randn(n_pos, hkv, 128, device="cuda").to(torch.bfloat16)
@@ -31,9 +32,10 @@ def test_gather_probe_runs_and_stores_nothing(dsa, depth, group_fastest, nsplit)
     # positions past n_pos and negative entries are both legal (they read row 0 / nothing)
     idx = torch.randint(-10, n_pos + 10, (rows, k_sel), generator=g, device="cuda", dtype=torch.int32)
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
-    dsa.dsa_probe_gather(k, v, idx, sink, nsplit=nsplit, group_fastest=group_fastest, depth=depth)
+    dsa.dsa_probe_gather(k, v, idx, sink, nsplit=nsplit, group_fastest=group_fastest, depth=depth, whole_rows=whole)
     # decode layout: row r reads positions r * row_stride + p
     idx_d = torch.randint(0, 16, (rows, k_sel), generator=g, device="cuda", dtype=torch.int32)
-    dsa.dsa_probe_gather(k, v, idx_d, sink, nsplit=nsplit, row_stride=16, group_fastest=group_fastest, depth=depth)
+    dsa.dsa_probe_gather(k, v, idx_d, sink, nsplit=nsplit, row_stride=16, group_fastest=group_fastest, depth=depth,
+                         whole_rows=whole)
     torch.cuda.synchronize()
     assert torch.count_nonzero(sink).item() == 0
