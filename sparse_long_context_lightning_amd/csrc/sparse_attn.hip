@@ -244,23 +244,52 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SparseAttnArgs a, floa
   }
 }
 
-// Merge split partials: one wave per (row, head), two output dims per lane.
+// Merge split partials: one wave per (row, head), two output dims per lane.  The splits'
+// (max, sum) pairs are fetched by the lanes together (lane s holds split s, 64 splits per
+// round) and reduced across the wave, so only the value rows are read in a loop, eight in flight.
 __global__ __launch_bounds__(256) void attn_combine_kernel(SparseAttnArgs a) {
   const long long item = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (item >= (long long)a.rows * a.hq) return;
-  const size_t slot0 = (size_t)item * a.nsplit;
+  const int ns = a.nsplit;
+  const size_t slot0 = (size_t)item * ns;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + slot0;
   float mmax = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mmax = fmaxf(mmax, a.part_ml[(slot0 + s) * 2]);
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float2 v = (s0 + lane < ns) ? ml[s0 + lane] : make_float2(-INFINITY, 0.f);
+    mmax = fmaxf(mmax, v.x);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, o));
   const float m_use = (mmax == -INFINITY) ? 0.f : mmax;
   float l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float sc = exp2f(a.part_ml[(slot0 + s) * 2] - m_use);
-    l += a.part_ml[(slot0 + s) * 2 + 1] * sc;
-    const float2 po = *reinterpret_cast<const float2*>(a.part_o + (slot0 + s) * 128 + 2 * lane);
-    o0 += po.x * sc;
-    o1 += po.y * sc;
+  const float2* po = reinterpret_cast<const float2*>(a.part_o + slot0 * 128) + lane;
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float2 v = (s0 + lane < ns) ? ml[s0 + lane] : make_float2(-INFINITY, 0.f);
+    const float sc_mine = (s0 + lane < ns) ? exp2f(v.x - m_use) : 0.f;
+    l += v.y * sc_mine;
+    const int cnt = min(64, ns - s0);
+    int s = 0;
+    for (; s + 8 <= cnt; s += 8) {
+      float2 pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = po[(size_t)(s0 + s + j) * 64];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float sc = __shfl(sc_mine, s + j);
+        o0 += pv[j].x * sc;
+        o1 += pv[j].y * sc;
+      }
+    }
+    for (; s < cnt; ++s) {
+      const float2 pv = po[(size_t)(s0 + s) * 64];
+      const float sc = __shfl(sc_mine, s);
+      o0 += pv.x * sc;
+      o1 += pv.y * sc;
+    }
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   reinterpret_cast<uint32_t*>(a.out + (size_t)item * 128)[lane] = pack_bf16x2(o0 * inv, o1 * inv);
   if (a.lse && lane == 0) a.lse[item] = l > 0.f ? (mmax + log2f(l)) * kLn2 : -INFINITY;
