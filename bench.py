@@ -608,7 +608,9 @@ def correlated_bench(args, dsa, inp):
 
 def attn_bwd_bench(args, dsa, inp):
     """Backward of the sparse attention on the 32K prefill (training side), after one fused
-    prefill that provides O, lse and the index sets; dO is synthetic."""
+    prefill that provides O, lse and the index sets; dO is synthetic.  Both forms: per row (one
+    float atomic per selected (row, KV head, dim) for dk / dv) and with dk / dv summed over the
+    merged sets of blocks of adjacent rows first (one atomic per merged position)."""
     import torch
     pi = inp.workload(args.bwd_workload)
     dev = dsa.upload_prefill_inputs(pi)
@@ -621,37 +623,70 @@ def attn_bwd_bench(args, dsa, inp):
     dq = torch.empty(out.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(dev["k"].shape, dtype=torch.float32, device="cuda")
     dv = torch.empty_like(dk)
+    total, hq = out.shape[0], out.shape[1]
+    hkv, d = pi.k.shape[1], pi.k.shape[2]
+    ws = torch.empty(max(dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total, k, hq, hkv), 16),
+                     dtype=torch.uint8, device="cuda")
 
-    def run():
+    def per_row():
         dsa.dsa_sparse_gqa_attn_bwd(dev["q"], dev["k"], dev["v"], out, lse, dout, idx, dev["cu"], dq, dk, dv)
 
-    run()
-    torch.cuda.synchronize()
+    def dedup():
+        dsa.dsa_sparse_gqa_attn_bwd_dedup(dev["q"], dev["k"], dev["v"], out, lse, dout, idx, dev["cu"], dq, dk, dv,
+                                          workspace=ws)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms_row = timed(per_row)
+    ref = (dq.clone(), dk.clone(), dv.clone())
+    ms = timed(dedup)
+    # the two forms agree up to the order of the float additions
+    agree = {n: float((x - y).abs().max() / y.abs().max().clamp_min(1e-30))
+             for n, x, y in zip(("dq", "dk", "dv"), (dq, dk, dv), ref)}
+    # merged-set sizes: the workspace begins with the per-block counts (int32)
+    rows_per_block = 16 if hq // hkv == 16 else 32
+    n_blocks = (total + rows_per_block - 1) // rows_per_block
+    merged = int(ws[:4 * n_blocks].view(torch.int32).to(torch.int64).sum().item())
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(3):
-        run()
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / 3
     a.record()
     dsa.dsa_sparse_gqa_attn(dev["q"], dev["k"], dev["v"], idx, dev["cu"], out, lse)
     b.record()
     torch.cuda.synchronize()
     fwd_ms = a.elapsed_time(b)
     lens = [int(x) for x in pi.seq_lens]
-    hkv, d = pi.k.shape[1], pi.k.shape[2]
     sel_pairs = sum(sum(min(t + 1, k) for t in range(n)) for n in lens)
+    atomics_row = sel_pairs * hkv * 2 * d
+    atomics_dedup = merged * hkv * 2 * d
     # per selected (row, KV group): K and V rows gathered (2 x 256 B) and 2 x 128 fp32 atomics
     algo_bytes = sel_pairs * hkv * (2 * d * 2 + 2 * d * 4)
-    total = sum(lens)
-    log(f"attention backward {ms:.1f} ms (forward {fwd_ms:.1f} ms) on {args.bwd_workload}")
-    del dev, dq, dk, dv, dout, out, lse, idx
+    log(f"attention backward {ms:.1f} ms with merged sets of {rows_per_block} rows (per row {ms_row:.1f} ms, "
+        f"forward {fwd_ms:.1f} ms) on {args.bwd_workload}; merged positions {merged / sel_pairs:.3f} of the "
+        f"selected pairs; agreement {agree}")
+    del dev, dq, dk, dv, dout, out, lse, idx, ws, ref
     torch.cuda.empty_cache()
-    return {"workload": args.bwd_workload, "ms": ms, "forward_ms": fwd_ms, "tokens_per_s": total / (ms * 1e-3),
-            "algorithmic_gb_per_s": algo_bytes / (ms * 1e-3) / 1e9,
-            "note": "dq, dk, dv from dO; dk/dv scattered with fp32 atomics (bound by L2 atomic throughput)"}
+    return {"workload": args.bwd_workload, "ms": ms, "per_row_ms": ms_row, "forward_ms": fwd_ms,
+            "tokens_per_s": total / (ms * 1e-3), "merged_block_rows": rows_per_block,
+            "merged_positions_per_selected_pair": merged / sel_pairs,
+            "float_atomic_adds": {"per_row": atomics_row, "merged_sets": atomics_dedup},
+            "atomic_adds_per_s": {"per_row": atomics_row / (ms_row * 1e-3),
+                                  "merged_sets": atomics_dedup / (ms * 1e-3)},
+            "dedup_vs_per_row_max_rel_diff": agree,
+            "algorithmic_gb_per_s_per_row_form": algo_bytes / (ms_row * 1e-3) / 1e9,
+            "note": "dq, dk, dv from dO; dk/dv with fp32 atomics, whose device rate (measured_peaks: the "
+                    "same for 64 or 16 consecutive floats per row and instruction) bounds both forms; the "
+                    "merged-set form issues one atomic per merged position and dim instead of one per "
+                    "selected pair"}
 
 
 def warmup_bench(args, dsa, inp):
@@ -820,9 +855,9 @@ def dense_bench(args, dsa, inp, dsa_prefill_ms, dsa_decode_us):
 
 
 def measured_peaks(dsa):
-    """What the box reaches on the two priced resources (the probe library): an MFMA-only loop of
-    16x16x32 and of 32x32x16 bf16 instructions, and a streaming read of 4 GiB.  Best of several
-    timed launches each."""
+    """What the box reaches on the priced resources (the probe library): an MFMA-only loop of
+    16x16x32 and of 32x32x16 bf16 instructions, a streaming read of 4 GiB, and float-atomic adds in
+    the attention backward's two scatter shapes.  Best of several timed launches each."""
     import torch
 
     grid, iters = 2048, 20000
@@ -837,7 +872,14 @@ def measured_peaks(dsa):
             for g in (2048, 8192, 16384, 32768, 65536)}
     res["stream_read_gbs"] = max(best.values())
     res["stream_read_gbs_by_grid"] = best
-    del buf, sink
+    del buf
+    # float atomics over 134 MB (the 32K backward's dk + dv), 64 or 16 consecutive floats per row piece
+    abuf = torch.zeros(262144, 128, dtype=torch.float32, device="cuda")
+    for w in (64, 16):
+        adds = dsa.dsa_probe_atomic_add(abuf, w, 8192, 256)
+        res[f"float_atomic_adds_per_s_{w}_per_row"] = adds / (best_ms(lambda: dsa.dsa_probe_atomic_add(abuf, w, 8192,
+                                                                                                     256), 3) * 1e-3)
+    del abuf, sink
     torch.cuda.empty_cache()
     log(f"measured peaks: {res}")
     return res
@@ -944,6 +986,12 @@ def main():
             for name in EXTRA_DECODE:
                 extra[name] = decode_summary(decode_section(args, dsa, inp, name, full=False))
     bwd = None if args.no_bwd else attn_bwd_bench(args, dsa, inp)
+    if bwd is not None:
+        ceiling = peaks.get("float_atomic_adds_per_s_16_per_row")
+        bwd["atomic_adds_per_s"]["probe_ceiling"] = ceiling
+        if ceiling:
+            bwd["atomic_frac_of_probe"] = {k: v / ceiling for k, v in bwd["atomic_adds_per_s"].items()
+                                           if k != "probe_ceiling"}
     wup = None if args.no_bwd else warmup_bench(args, dsa, inp)
     dense = None if args.no_dense else dense_bench(args, dsa, inp, pre["ms_per_step"],
                                                    None if dec is None else dec["us_median"])

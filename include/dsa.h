@@ -329,6 +329,34 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
                             float* dq, float* dk, float* dv, void* stream);
 
 /*
+ * dsa_sparse_gqa_attn_bwd with adjacent-query dedup (digest section 八: adjacent queries select
+ * largely the same positions).  The float-atomic adds of dk / dv bound the per-row backward, so
+ * here the index sets of each block of 32 adjacent packed rows (16 when hq / hkv = 16) are merged
+ * in the workspace, and every merged position's contributions are summed over the block's rows
+ * and heads before they are added: one atomic per (merged position, KV head, dim) instead of one
+ * per (row, selected entry, KV head, dim).  Blocks in which a row lists a position twice are done
+ * per row (each entry counts once per occurrence, as in dsa_sparse_gqa_attn_bwd).
+ *
+ * Arguments as dsa_sparse_gqa_attn_bwd, plus:
+ * workspace           device memory of at least
+ *                     dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total_tokens, k_sel, hq, hkv)
+ *                     bytes, 16-byte aligned, owned by the caller, clobbered (per block a count, a
+ *                     path flag, up to R x k_sel merged positions and 32-bit row masks: about
+ *                     8 k_sel bytes per row).  When that size is 0 (hq / hkv not 4, 8 or 16) the
+ *                     call is the per-row backward and the workspace may be NULL.
+ * The result equals dsa_sparse_gqa_attn_bwd's up to the order of the float additions; dZ and P
+ * enter the dk / dv products as bf16 in both.
+ */
+int dsa_sparse_gqa_attn_bwd_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv,
+                                                 size_t* bytes);
+int dsa_sparse_gqa_attn_bwd_dedup(const void* q, const void* k, const void* v, const void* out,
+                                  const float* lse, const void* dout, const int32_t* idx, int k_sel,
+                                  const int32_t* cu_seqlens, int batch, int total_tokens,
+                                  int hq, int hkv, int head_dim, float softmax_scale,
+                                  float* dq, float* dk, float* dv, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Workspace bytes for dsa_prefill: the larger of (a) a score buffer for a chunk of 2048 query
  * rows (never the whole L x L matrix) plus the top-k scratch of those rows and (b), when
  * hq / hkv is 4, 8 or 16, the merged index sets of dsa_sparse_gqa_attn_dedup, which reuse the

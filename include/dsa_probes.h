@@ -2,9 +2,10 @@
  * dsa_probes.h - measurement probes for MI355X, built as their own library (libdsa_probes.so).
  *
  * They compute nothing of the method.  They measure what the device reaches on the resources
- * the DSA path's kernels are priced against (bf16 MFMA issue, streaming HBM reads, and random
- * 256-byte row gathers in the sparse attention's access pattern), so that a kernel's fraction of
- * a spec peak can be read beside its fraction of an achievable one.  The benchmark is their only
+ * the DSA path's kernels are priced against (bf16 MFMA issue, streaming HBM reads, random
+ * 256-byte row gathers in the sparse attention's access pattern, and the float-atomic adds that
+ * the attention backward scatters with), so that a kernel's fraction of a spec peak can be read
+ * beside its fraction of an achievable one.  The benchmark is their only
  * user; the product library (dsa.h) does not depend on them.
  *
  * Conventions: device pointers; `stream` is a hipStream_t (NULL = default stream); each call
@@ -59,6 +60,17 @@ int dsa_probe_stream_read(const void* src, size_t bytes, int grid, uint32_t* sin
 int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const int32_t* idx, int k_sel, int rows,
                      int nsplit, int64_t row_stride, int group_fastest, int depth, int whole_rows, uint32_t* sink,
                      int64_t sink_len, void* stream);
+
+/*
+ * Float-atomic throughput in the shapes the attention backward scatters dk / dv with: `grid`
+ * workgroups of four waves, each wave running `iters` atomic adds of 1.0 at 64 addresses, which
+ * lie in 64 / floats_per_row rows of 128 floats (pseudo-random rows in [0, n_rows)) with
+ * floats_per_row (16 or 64) consecutive floats in each.  buf [n_rows, 128] float (accumulates:
+ * zero it first to check the count).  *adds (host, may be NULL) receives the additions one call
+ * makes.  n_rows in [1, 2^32], grid in [1, 2^20], iters >= 1.
+ */
+int dsa_probe_atomic_add(float* buf, int64_t n_rows, int floats_per_row, int grid, int iters, long long* adds,
+                         void* stream);
 
 #ifdef __cplusplus
 }

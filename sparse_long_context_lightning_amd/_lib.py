@@ -31,9 +31,11 @@ EXPORTED = (
     "dsa_indexer_kl", "dsa_index_scores_bwd", "dsa_query_union_size", "dsa_query_union",
     "dsa_sparse_gqa_attn_union", "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
     "dsa_decode_noalloc", "dsa_sparse_gqa_attn_decode_workspace_size", "dsa_sparse_gqa_attn_decode",
+    "dsa_sparse_gqa_attn_bwd_dedup_workspace_size", "dsa_sparse_gqa_attn_bwd_dedup",
 )
 # The measurement probes (include/dsa_probes.h), a separate library used by the benchmark.
-PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather")
+PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather",
+                   "dsa_probe_atomic_add")
 
 
 class DsaError(RuntimeError):
@@ -74,6 +76,9 @@ def load():
         "dsa_sparse_gqa_attn": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P],
                                     _I),
+        "dsa_sparse_gqa_attn_bwd_dedup_workspace_size": ([_I, _I, _I, _I, ctypes.POINTER(_SZ)], _I),
+        "dsa_sparse_gqa_attn_bwd_dedup": ([_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P,
+                                           _P, _SZ, _P], _I),
         "dsa_query_union_size": ([_I, _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
         "dsa_query_union": ([_P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P], _I),
         "dsa_sparse_gqa_attn_union": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
@@ -114,6 +119,7 @@ def load_probes():
         "dsa_probe_mfma_bf16": ([_I, _I, _I, _P, ctypes.POINTER(ctypes.c_longlong), _P], _I),
         "dsa_probe_stream_read": ([_P, _SZ, _I, _P, _P], _I),
         "dsa_probe_gather": ([_P, _P, _I64, _I, _P, _I, _I, _I, _I64, _I, _I, _I, _P, _I64, _P], _I),
+        "dsa_probe_atomic_add": ([_P, _I64, _I, _I, _I, ctypes.POINTER(ctypes.c_longlong), _P], _I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -311,8 +317,8 @@ def dsa_sparse_gqa_attn_dedup_workspace_size(total_tokens, k_sel, hq, hkv):
 
 def dsa_sparse_gqa_attn_dedup(q, k, v, idx, cu_seqlens, out, lse=None, softmax_scale=None, workspace=None,
                               stream=None):
-    """dsa_sparse_gqa_attn with adjacent-query dedup (merged sets of 16-row blocks where they pay);
-    allocates the workspace when none is given."""
+    """dsa_sparse_gqa_attn with adjacent-query dedup (merged sets of 8-row blocks); allocates the
+    workspace when none is given."""
     import torch
     total, hq, d = q.shape
     hkv = k.shape[1]
@@ -334,6 +340,30 @@ def dsa_sparse_gqa_attn_bwd(q, k, v, out, lse, dout, idx, cu_seqlens, dq, dk, dv
     _check(load().dsa_sparse_gqa_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(idx),
                                           idx.shape[1], _ptr(cu_seqlens), cu_seqlens.shape[0] - 1, total, hq, hkv, d,
                                           scale, _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total_tokens, k_sel, hq, hkv):
+    n = _SZ(0)
+    _check(load().dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total_tokens, k_sel, hq, hkv, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_sparse_gqa_attn_bwd_dedup(q, k, v, out, lse, dout, idx, cu_seqlens, dq, dk, dv, softmax_scale=None,
+                                  workspace=None, stream=None):
+    """dsa_sparse_gqa_attn_bwd with dk / dv summed over the merged sets of blocks of adjacent rows
+    before they are added; allocates the workspace when none is given."""
+    import torch
+    total, hq, d = q.shape
+    hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    if workspace is None:
+        nbytes = dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total, idx.shape[1], hq, hkv)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    _check(load().dsa_sparse_gqa_attn_bwd_dedup(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
+                                                _ptr(idx), idx.shape[1], _ptr(cu_seqlens), cu_seqlens.shape[0] - 1,
+                                                total, hq, hkv, d, scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                _stream(stream)))
 
 
 def dsa_prefill_workspace_size(batch, total_tokens, max_seqlen, hq, hkv, head_dim, h_idx, d_idx, top_k) -> int:
@@ -460,6 +490,14 @@ def dsa_probe_stream_read(src, grid, sink, stream=None):
     """Enqueue the streaming-read probe over the whole of `src`."""
     _check_probe(load_probes().dsa_probe_stream_read(_ptr(src), src.numel() * src.element_size(), grid, _ptr(sink),
                                                      _stream(stream)))
+
+
+def dsa_probe_atomic_add(buf, floats_per_row, grid, iters, stream=None):
+    """Enqueue the float-atomic probe over buf [n_rows, 128] float32; returns the adds it makes."""
+    n = ctypes.c_longlong(0)
+    _check_probe(load_probes().dsa_probe_atomic_add(_ptr(buf), buf.shape[0], floats_per_row, grid, iters,
+                                                    ctypes.byref(n), _stream(stream)))
+    return n.value
 
 
 def dsa_probe_gather(k, v, idx, sink, nsplit=1, row_stride=0, group_fastest=False, depth=2, whole_rows=False,

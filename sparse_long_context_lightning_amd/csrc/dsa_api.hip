@@ -137,7 +137,7 @@ struct UnionLayout {
   int n_blocks = 0, cap = 0;
   size_t counts = 0, flags = 0, rows = 0, masks = 0, bytes = 0;
 };
-UnionLayout union_layout(int total_tokens, int k_sel, int block_rows = kUnionBlockRows) {
+UnionLayout union_layout(int total_tokens, int k_sel, int block_rows = kUnionBlockRows, int mask_bytes = 2) {
   UnionLayout u;
   u.n_blocks = (total_tokens + block_rows - 1) / block_rows;
   u.cap = (int)round_up((long long)block_rows * k_sel, dsa::kUnionChunk);
@@ -149,9 +149,15 @@ UnionLayout union_layout(int total_tokens, int k_sel, int block_rows = kUnionBlo
   u.rows = (size_t)off;
   off += round_up((long long)u.n_blocks * u.cap * 4, 256);
   u.masks = (size_t)off;
-  off += round_up((long long)u.n_blocks * u.cap * 2, 256);
+  off += round_up((long long)u.n_blocks * u.cap * mask_bytes, 256);
   u.bytes = (size_t)off;
   return u;
+}
+
+// Workspace of the merged-set attention backward: the same lists with 32-bit masks, for blocks of
+// union_bwd_block_rows(hq / hkv) rows.
+UnionLayout union_bwd_layout(int total_tokens, int k_sel, int hq, int hkv) {
+  return union_layout(total_tokens, k_sel, dsa::union_bwd_block_rows(hq / hkv), 4);
 }
 
 // Sparse attention of the prefill rows described by `a` with adjacent-query dedup: merged sets
@@ -202,6 +208,64 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   a.skip_block = flags;
   a.skip_block_rows = kUnionBlockRows;
   return dsa::launch_sparse_attn(a, s);
+}
+
+// Backward of the sparse attention with adjacent-query dedup: dk / dv zeroed, the merged sets
+// of every block built, the merged-set backward on the blocks where no row repeats a position,
+// the per-row backward on the rows of the others.  `ws` holds union_bwd_layout(..).bytes bytes.
+hipError_t launch_attn_bwd_dedup(dsa::SparseAttnBwdArgs a, void* ws, hipStream_t s) {
+  const int R = dsa::union_bwd_block_rows(a.hq / a.hkv);
+  const UnionLayout u = union_bwd_layout(a.rows, a.k_sel, a.hq, a.hkv);
+  char* base = static_cast<char*>(ws);
+  int* counts = reinterpret_cast<int*>(base + u.counts);
+  int* flags = reinterpret_cast<int*>(base + u.flags);
+  int* kv_rows = reinterpret_cast<int*>(base + u.rows);
+  uint32_t* masks = reinterpret_cast<uint32_t*>(base + u.masks);
+  const long long nkv = (long long)a.rows * a.hkv * 128;
+  hipError_t e = dsa::launch_zero_f32(a.dk, nkv, s);
+  if (e == hipSuccess) e = dsa::launch_zero_f32(a.dv, nkv, s);
+  if (e != hipSuccess) return e;
+  dsa::QueryUnionArgs q = {};
+  q.idx = a.idx;
+  q.k_sel = a.k_sel;
+  q.cu_seqlens = a.cu_seqlens;
+  q.batch = a.batch;
+  q.rows = a.rows;
+  q.block_rows = R;
+  q.block_begin = 0;
+  q.block_end = u.n_blocks;
+  q.cap = u.cap;
+  q.counts = counts;
+  q.kv_rows = kv_rows;
+  q.masks32 = masks;
+  q.use_union = flags;
+  q.ratio = 1.0f;  // every block whose rows list no position twice
+  e = dsa::launch_query_union(q, s);
+  if (e != hipSuccess) return e;
+  dsa::UnionBwdArgs m = {};
+  m.q = a.q;
+  m.k = a.k;
+  m.v = a.v;
+  m.out = a.out;
+  m.dout = a.dout;
+  m.lse = a.lse;
+  m.counts = counts;
+  m.kv_rows = kv_rows;
+  m.masks = masks;
+  m.cap = u.cap;
+  m.use_union = flags;
+  m.rows = a.rows;
+  m.hq = a.hq;
+  m.hkv = a.hkv;
+  m.softmax_scale = a.softmax_scale;
+  m.dq = a.dq;
+  m.dk = a.dk;
+  m.dv = a.dv;
+  e = dsa::launch_sparse_attn_bwd_union(m, s);
+  if (e != hipSuccess) return e;
+  a.skip_block = flags;
+  a.skip_block_rows = R;
+  return dsa::launch_sparse_attn_bwd(a, s);
 }
 
 int decode_nsplit(int batch, int hkv, int top_k) {
@@ -783,6 +847,74 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
   a.dk = dk;
   a.dv = dv;
   return hip_status(dsa::launch_sparse_attn_bwd(a, static_cast<hipStream_t>(stream)), "sparse attention backward launch");
+}
+
+int dsa_sparse_gqa_attn_bwd_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv, size_t* bytes) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(bytes);
+  if (total_tokens < 0 || k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "total_tokens >= 0 and k_sel > 0 required");
+  if (k_sel > (1 << 24)) return fail(DSA_ERR_UNSUPPORTED, "k_sel %d too large", k_sel);
+  *bytes = dsa::union_bwd_supported(hq, hkv) ? union_bwd_layout(total_tokens, k_sel, hq, hkv).bytes : 0;
+  return DSA_OK;
+}
+
+int dsa_sparse_gqa_attn_bwd_dedup(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                  const void* dout, const int32_t* idx, int k_sel, const int32_t* cu_seqlens,
+                                  int batch, int total_tokens, int hq, int hkv, int head_dim, float softmax_scale,
+                                  float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  g_last_error[0] = 0;
+  dsa::api_log("dsa_sparse_gqa_attn_bwd_dedup", "batch=%d total=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, total_tokens,
+               hq, hkv, k_sel, workspace_bytes);
+  DSA_NONNULL(q);
+  DSA_NONNULL(k);
+  DSA_NONNULL(v);
+  DSA_NONNULL(out);
+  DSA_NONNULL(lse);
+  DSA_NONNULL(dout);
+  DSA_NONNULL(idx);
+  DSA_NONNULL(cu_seqlens);
+  DSA_NONNULL(dq);
+  DSA_NONNULL(dk);
+  DSA_NONNULL(dv);
+  DSA_ALIGNED(q);
+  DSA_ALIGNED(k);
+  DSA_ALIGNED(v);
+  DSA_ALIGNED(out);
+  DSA_ALIGNED(dout);
+  DSA_ALIGNED(dq);
+  DSA_ALIGNED(dk);
+  DSA_ALIGNED(dv);
+  if (batch <= 0 || total_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "batch must be positive, total_tokens >= 0");
+  if (k_sel <= 0) return fail(DSA_ERR_INVALID_ARG, "k_sel must be positive");
+  DSA_TRY(check_attn_shape(hq, hkv, head_dim));
+  size_t need = 0;
+  DSA_TRY(dsa_sparse_gqa_attn_bwd_dedup_workspace_size(total_tokens, k_sel, hq, hkv, &need));
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", workspace_bytes, need);
+  if (need > 0) DSA_ALIGNED(workspace);
+  if (total_tokens == 0) return DSA_OK;
+  dsa::SparseAttnBwdArgs a = {};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<const uint16_t*>(out);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.idx = idx;
+  a.k_sel = k_sel;
+  a.cu_seqlens = cu_seqlens;
+  a.batch = batch;
+  a.rows = total_tokens;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.softmax_scale = softmax_scale;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) return hip_status(dsa::launch_sparse_attn_bwd(a, s), "sparse attention backward launch");
+  return hip_status(launch_attn_bwd_dedup(a, workspace, s), "dedup attention backward launch");
 }
 
 int dsa_prefill_workspace_size(int batch, int total_tokens, int max_seqlen, int hq, int hkv, int head_dim, int h_idx,

@@ -88,6 +88,8 @@ struct SparseAttnBwdArgs {
   float* dq;  // [rows, hq, 128]
   float* dk;  // [rows, hkv, 128]
   float* dv;  // [rows, hkv, 128]
+  const int* skip_block;  // optional: rows of blocks b (skip_block_rows rows each) with
+  int skip_block_rows;    // skip_block[b] != 0 are left alone (dk / dv are then not zeroed)
 };
 
 // Backward of the indexer scores for packed rows [row_begin, row_end) of one sequence starting at
@@ -123,8 +125,9 @@ struct HeadMeanArgs {
 // (the last block may be shorter).  Its merged list has counts[b] entries at kv_rows / masks +
 // b * cap: packed KV rows in ascending order and 16-bit masks (bit j: row R b + j selected the
 // KV row), padded with mask-0 entries to a multiple of kUnionChunk.  cap must be a multiple of
-// kUnionChunk and at least R * k_sel rounded up to one.
-constexpr int kMaxQueryBlock = 16;
+// kUnionChunk and at least R * k_sel rounded up to one.  With masks32 set instead of masks, the
+// masks are 32-bit and R may be any of 1 .. 32 (the attention backward's blocks).
+constexpr int kMaxQueryBlock = 32;
 constexpr int kUnionChunk = 32;
 inline bool union_block_rows_ok(int r) { return r == 8 || r == 16; }
 struct QueryUnionArgs {
@@ -139,6 +142,7 @@ struct QueryUnionArgs {
   int* counts;
   int* kv_rows;
   uint16_t* masks;
+  uint32_t* masks32;  // set (and masks NULL) for 32-bit masks
   // Optional: use_union[b] = 1 when the merged set is at most ratio x (rows x k_sel) entries,
   // i.e. when the merged-set attention is expected to beat the per-row one for the block, and
   // no row of the block lists a position twice.
@@ -160,6 +164,34 @@ struct UnionAttnArgs {
   float* lse;
   const int* use_union;  // optional: blocks with use_union[b] == 0 are left alone
 };
+// Backward of the sparse attention over merged sets (32-bit masks) of blocks of
+// union_bwd_block_rows(hq / hkv) rows: dq of the blocks' rows written, their dk / dv
+// contributions added to dk / dv (which the caller has zeroed).
+struct UnionBwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* out;
+  const uint16_t* dout;
+  const float* lse;
+  const int* counts;
+  const int* kv_rows;
+  const uint32_t* masks;
+  int cap;
+  const int* use_union;  // optional: blocks with use_union[b] == 0 are left alone
+  int rows, hq, hkv;
+  float softmax_scale;
+  float* dq;
+  float* dk;
+  float* dv;
+};
+// hq / hkv in {4, 8, 16}; blocks of 32 rows (16 at hq / hkv = 16), so a block's (row, head)
+// pairs of one KV group number 128 or 256.
+bool union_bwd_supported(int hq, int hkv);
+int union_bwd_block_rows(int g);
+hipError_t launch_sparse_attn_bwd_union(const UnionBwdArgs& a, hipStream_t s);
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s);
+
 hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s);
 // The union attention handles G = hq / hkv in {4, 8, 16}.
 bool union_attn_supported(int hq, int hkv, long long rows);

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void sparse_attn_bwd_kernel(SparseAttnBwdArgs 
   // KV group slowest, as in the forward.
   const int g = (int)(item / a.rows);
   const int row = (int)(item - (long long)g * a.rows);
+  if (a.skip_block && a.skip_block[row / a.skip_block_rows] != 0) return;  // done over its block's merged set
   unsigned char* klds = klds_all[wave];
   uint16_t* zt = zt_all[wave][0];
   uint16_t* pt = zt_all[wave][1];
@@ -259,12 +260,21 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ p, lo
 
 }  // namespace
 
+hipError_t launch_zero_f32(float* p, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned zgrid = (unsigned)std::min<long long>((n + 255) / 256, 16384);
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(zgrid), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn_bwd(const SparseAttnBwdArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  const long long nkv = (long long)a.rows * a.hkv * 128;
-  const unsigned zgrid = (unsigned)std::min<long long>((nkv + 255) / 256, 16384);
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(zgrid), dim3(256), 0, s, a.dk, nkv);
-  hipLaunchKernelGGL(zero_f32_kernel, dim3(zgrid), dim3(256), 0, s, a.dv, nkv);
+  if (!a.skip_block) {
+    const long long nkv = (long long)a.rows * a.hkv * 128;
+    hipError_t e = launch_zero_f32(a.dk, nkv, s);
+    if (e == hipSuccess) e = launch_zero_f32(a.dv, nkv, s);
+    if (e != hipSuccess) return e;
+  }
   const long long items = (long long)a.rows * a.hkv;
   const long long n_wg = (items + 3) / 4;
   const long long grid = (n_wg + 7) / 8 * 8;

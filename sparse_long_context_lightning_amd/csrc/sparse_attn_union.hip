@@ -27,6 +27,8 @@
 //     the P^T registers carry, and the row sums on the same MFMA with a ones operand.
 // The cost per block grows with R x |merged set| while the gathered bytes shrink with the
 // overlap, so R trades compute against memory traffic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -49,13 +51,14 @@ __device__ __forceinline__ int lanes_below(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
 }
 
-// BPP bits per position (8 for blocks of up to 8 rows, 16 for up to 16): a window covers
-// kBitmapWords * 32 / BPP KV rows.
+// BPP bits per position (8 for blocks of up to 8 rows, 16 for up to 16, 32 for up to 32 with
+// 32-bit masks): a window covers kBitmapWords * 32 / BPP KV rows.
 template <int BPP>
 __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionArgs a) {
   constexpr int PPW = 32 / BPP;                  // positions per dword
   constexpr int kWindow = kBitmapWords * PPW;
-  constexpr uint32_t kField = BPP == 8 ? 0xFFu : 0xFFFFu;
+  constexpr uint32_t kField = BPP == 8 ? 0xFFu : BPP == 16 ? 0xFFFFu : 0xFFFFFFFFu;
+  typedef typename std::conditional<BPP == 32, uint32_t, uint16_t>::type MaskT;
   constexpr int kWaves = kUnionThreads / 64;
   __shared__ __attribute__((aligned(16))) uint32_t bm[kBitmapWords];
   __shared__ int row_base[kMaxQueryBlock], row_t[kMaxQueryBlock];
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
   const int b0 = row_base[0];          // no entry of the block names a KV row below this one
   const int span = r0 + nr - b0;       // KV rows b0 .. r0 + nr - 1
   int* out_rows = a.kv_rows + (size_t)b * a.cap;
-  uint16_t* out_masks = a.masks + (size_t)b * a.cap;
+  MaskT* out_masks = reinterpret_cast<MaskT*>(BPP == 32 ? (void*)a.masks32 : (void*)a.masks) + (size_t)b * a.cap;
   int total = 0;
   for (int w0 = 0; w0 < span; w0 += kWindow) {
     const int lo = b0 + w0;
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
         const int p = ir[i];
         const int x = off + p;
         if (p >= 0 && p <= t && x >= 0 && x < limit) {
-          const uint32_t bit = 1u << (BPP * (x % PPW) + j);
+          const uint32_t bit = 1u << ((BPP == 32 ? 0 : BPP * (x % PPW)) + j);
           if (atomicOr(&bm[x / PPW], bit) & bit) repeated = 1;
         }
       }
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
         const uint32_t m = (wd >> (BPP * f)) & kField;
         if (m != 0u) {
           out_rows[e] = lo + x * PPW + f;
-          out_masks[e] = (uint16_t)m;
+          out_masks[e] = (MaskT)m;
           ++e;
         }
       }
@@ -399,6 +402,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_union_kernel(UnionAttnArg
 hipError_t launch_query_union(const QueryUnionArgs& a, hipStream_t s) {
   const int nb = a.block_end - a.block_begin;
   if (nb <= 0) return hipSuccess;
+  if (a.masks32) {
+    if (a.block_rows < 1 || a.block_rows > 32) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(query_union_kernel<32>, dim3(nb), dim3(kUnionThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (!union_block_rows_ok(a.block_rows)) return hipErrorInvalidValue;
   if (a.block_rows <= 8)
     hipLaunchKernelGGL(query_union_kernel<8>, dim3(nb), dim3(kUnionThreads), 0, s, a);

@@ -160,6 +160,23 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
   if (r == never) sink[blockIdx.x] = r;
 }
 
+// Float-atomic throughput: each instruction adds 1.0 at 64 addresses lying in 64 / W rows of 128
+// floats with W consecutive floats in each (W = 64: one row piece, as the per-row attention
+// backward scatters dk / dv; W = 16: four rows, as the merged-set backward does).  Rows are drawn
+// from [0, n_rows) by a per-wave (and per row piece) LCG; every address stays in its row.
+template <int W>
+__global__ __launch_bounds__(256) void atomic_add_kernel(float* __restrict__ buf, long long n_rows, int iters) {
+  const int lane = threadIdx.x & 63;
+  const unsigned wave = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const int grp = lane / W, off = lane % W;
+  unsigned s = (wave * 2654435761u) ^ ((unsigned)grp * 40503u) ^ 0x9E3779B9u;
+  for (int i = 0; i < iters; ++i) {
+    s = s * 1664525u + 1013904223u;
+    const long long r = (long long)(((unsigned long long)s * (unsigned long long)n_rows) >> 32);
+    unsafeAtomicAdd(buf + r * 128 + (i % (128 / W)) * W + off, 1.0f);
+  }
+}
+
 thread_local char g_probe_error[256] = "";
 
 int probe_fail(int status, const char* fmt, ...) {
@@ -246,6 +263,23 @@ int dsa_probe_gather(const void* k, const void* v, int64_t n_pos, int hkv, const
     else go(gather_kernel<4, 0>);
   }
   return launched("gather probe launch");
+}
+
+int dsa_probe_atomic_add(float* buf, int64_t n_rows, int floats_per_row, int grid, int iters, long long* adds,
+                         void* stream) {
+  g_probe_error[0] = 0;
+  if (!buf) return probe_fail(DSA_PROBE_ERR_INVALID_ARG, "buf is null");
+  if (n_rows < 1 || n_rows > (1LL << 32)) return probe_fail(DSA_PROBE_ERR_INVALID_ARG, "n_rows out of range");
+  if (floats_per_row != 16 && floats_per_row != 64)
+    return probe_fail(DSA_PROBE_ERR_INVALID_ARG, "floats_per_row must be 16 or 64, got %d", floats_per_row);
+  if (grid < 1 || grid > (1 << 20) || iters < 1) return probe_fail(DSA_PROBE_ERR_INVALID_ARG, "grid / iters out of range");
+  if (adds) *adds = (long long)grid * 4 * iters * 64;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (floats_per_row == 16)
+    hipLaunchKernelGGL(atomic_add_kernel<16>, dim3(grid), dim3(256), 0, s, buf, (long long)n_rows, iters);
+  else
+    hipLaunchKernelGGL(atomic_add_kernel<64>, dim3(grid), dim3(256), 0, s, buf, (long long)n_rows, iters);
+  return launched("atomic-add probe launch");
 }
 
 }  // extern "C"

@@ -26,7 +26,7 @@ def _declared(header=HEADER):
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -158,6 +158,12 @@ def test_probe_validation():
     assert gather(depth=3) == bad
     assert gather(rows=0) == bad
     assert gather(row_stride=-1) == bad
+    adds = ctypes.c_longlong(0)
+    assert lib.dsa_probe_atomic_add(None, 1024, 64, 64, 10, ctypes.byref(adds), None) == bad
+    assert lib.dsa_probe_atomic_add(FAKE, 0, 64, 64, 10, ctypes.byref(adds), None) == bad
+    assert lib.dsa_probe_atomic_add(FAKE, 1024, 32, 64, 10, ctypes.byref(adds), None) == bad
+    assert lib.dsa_probe_atomic_add(FAKE, 1024, 16, 0, 10, ctypes.byref(adds), None) == bad
+    assert lib.dsa_probe_atomic_add(FAKE, 1024, 16, 64, 0, ctypes.byref(adds), None) == bad
     assert gather(sink_len=99) == bad     # 100 rows x 4 groups / 4 waves = 100 workgroups, padded to 104
 
 
@@ -213,6 +219,44 @@ def test_dedup_attention_validation():
     assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size((1 << 22) - 1, 64, 32, 4) > 0
     assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(1 << 22, 64, 32, 4) == 0
     assert dsa.dsa_sparse_gqa_attn_dedup_workspace_size(1 << 22, 64, 16, 2) > 0
+
+
+def test_dedup_backward_validation_and_workspace_size():
+    lib = dsa.load()
+    sc = ctypes.c_float(0.1)
+
+    def _bwd_union(total, k, rows):   # per block: count, flag, rows x k int32 KV rows and uint32 masks
+        nb, cap = (total + rows - 1) // rows, (rows * k + 31) // 32 * 32
+        r = lambda x: (x + 255) // 256 * 256
+        return 2 * r(nb * 4) + 2 * r(nb * cap * 4)
+    assert dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(32768, 2048, 32, 4) == _bwd_union(32768, 2048, 32)
+    assert dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(300, 64, 8, 2) == _bwd_union(300, 64, 32)
+    assert dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(300, 64, 16, 1) == _bwd_union(300, 64, 16)
+    # group sizes without the merged-set backward: the per-row backward, no workspace
+    assert dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(300, 64, 4, 4) == 0
+    assert dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(300, 64, 12, 4) == 0
+    need = dsa.dsa_sparse_gqa_attn_bwd_dedup_workspace_size(300, 64, 32, 4)
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64, FAKE, 1, 300, 32, 4, 128, sc, FAKE, FAKE, FAKE]
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*base, None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*base, FAKE, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*base, MISALIGNED, need, None) == dsa.DSA_ERR_INVALID_ARG
+    for i in (4, 5, 6, 15, 16, 17):    # lse, dout, idx, dq, dk, dv are required
+        bad = list(base)
+        bad[i] = None
+        assert lib.dsa_sparse_gqa_attn_bwd_dedup(*bad, FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG, i
+    bad = list(base)
+    bad[15] = MISALIGNED
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*bad, FAKE, need, None) == dsa.DSA_ERR_INVALID_ARG
+    bad = list(base)
+    bad[13] = 64
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*bad, FAKE, need, None) == dsa.DSA_ERR_UNSUPPORTED
+    zero = list(base)
+    zero[10] = 0
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*zero, FAKE, need, None) == dsa.DSA_OK
+    per_row = list(base)
+    per_row[12] = 32   # group size 1: no workspace needed, the per-row path (nothing enqueued: total 0)
+    per_row[10] = 0
+    assert lib.dsa_sparse_gqa_attn_bwd_dedup(*per_row, None, 0, None) == dsa.DSA_OK
 
 
 def test_zero_sized_calls_are_no_ops():

@@ -39,3 +39,14 @@ def test_gather_probe_runs_and_stores_nothing(dsa, depth, group_fastest, nsplit,
                          whole_rows=whole)
     torch.cuda.synchronize()
     assert torch.count_nonzero(sink).item() == 0
+
+
+@pytest.mark.parametrize("floats_per_row", [16, 64])
+def test_atomic_probe_adds_exactly_its_count(dsa, floats_per_row):
+    import torch
+    buf = torch.zeros(5000, 128, dtype=torch.float32, device="cuda")
+    adds = dsa.dsa_probe_atomic_add(buf, floats_per_row, 96, 7)
+    assert adds == 96 * 4 * 7 * 64
+    torch.cuda.synchronize()
+    # each float receives a small integer count: the sum is exact
+    assert int(buf.double().sum().item()) == adds
