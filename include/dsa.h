@@ -142,9 +142,10 @@ int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w,
  * For packed rows [row_begin, row_begin + row_count) with local position t:
  *   probs[i * ld + s] = (1 / hq) sum_h softmax_s(scale <q[r, h], k[o + s, h / G]>)  for s <= t
  *   lse[i * hq + h]   = log sum_s exp(scale <q[r, h], k[o + s, h / G]>)  (the dense causal lse)
- * (i = r - row_begin).  Entries with s > t are left untouched.  q, k, cu_seqlens_host as for
- * dsa_prefill / dsa_index_scores.  Needs hq / hkv >= 4 and hkv in {1, 2, 4, 8}.  Costs two dense
- * passes of Q K^T over the causal prefix (statistics, then probabilities).
+ * (i = r - row_begin).  Entries with s > t are left untouched (entries s <= t may hold scratch
+ * values while the call runs).  q, k, cu_seqlens_host as for dsa_prefill / dsa_index_scores.
+ * Needs hq / hkv in {4, 8, 12, 16} and hkv in {1, 2, 4, 8} (DSA_ERR_UNSUPPORTED otherwise).
+ * Costs two dense passes of Q K^T over the causal prefix (statistics, then probabilities).
  */
 int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_host, int batch,
                        int total_tokens, int hq, int hkv, int head_dim, float softmax_scale,

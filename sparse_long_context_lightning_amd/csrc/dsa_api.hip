@@ -509,8 +509,8 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
     return fail(DSA_ERR_INVALID_ARG, "row range [%d, %d + %d) outside [0, %d)", row_begin, row_begin, row_count,
                 total_tokens);
   DSA_TRY(check_attn_shape(hq, hkv, head_dim));
-  if (hq / hkv < 4 || (hkv != 1 && hkv != 2 && hkv != 4 && hkv != 8))
-    return fail(DSA_ERR_UNSUPPORTED, "the head-mean target needs hq / hkv >= 4 and hkv in {1, 2, 4, 8}");
+  if (hq / hkv < 4 || (hq / hkv) % 4 != 0 || (hkv != 1 && hkv != 2 && hkv != 4 && hkv != 8))
+    return fail(DSA_ERR_UNSUPPORTED, "the head-mean target needs hq / hkv in {4, 8, 12, 16} and hkv in {1, 2, 4, 8}");
   int max_len = 0;
   DSA_TRY(check_cu_host(cu_seqlens_host, batch, total_tokens, &max_len));
   if (ld <= 0) return fail(DSA_ERR_INVALID_ARG, "ld must be positive");

@@ -259,6 +259,18 @@ def test_dedup_backward_validation_and_workspace_size():
     assert lib.dsa_sparse_gqa_attn_bwd_dedup(*per_row, None, 0, None) == dsa.DSA_OK
 
 
+def test_head_mean_rejects_group_sizes_that_are_not_multiples_of_4():
+    lib = dsa.load()
+    cu_arr, cu_p = _cu([0, 300])
+    sc = ctypes.c_float(0.1)
+    call = lambda hq, hkv: lib.dsa_attn_head_mean(FAKE, FAKE, cu_p, 1, 300, hq, hkv, 128, sc, 0, 0, FAKE, 300, FAKE,
+                                                  None)
+    for hq, hkv in ((24, 4), (20, 4), (12, 2), (6, 1), (8, 4), (64, 16)):
+        assert call(hq, hkv) == dsa.DSA_ERR_UNSUPPORTED, (hq, hkv)
+    for hq, hkv in ((16, 4), (32, 4), (48, 4), (64, 4), (12, 1)):
+        assert call(hq, hkv) == dsa.DSA_OK, (hq, hkv)   # zero rows: validated, nothing enqueued
+
+
 def test_zero_sized_calls_are_no_ops():
     lib = dsa.load()
     cu_arr, cu_p = _cu([0, 64])

@@ -33,7 +33,8 @@ def _target_case(dsa, lens, hq, hkv, row_begin=0, row_count=None, seed=0):
     return pi, probs.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("lens,hq,hkv", [([300, 70], 32, 4), ([200], 16, 1), ([129, 3], 16, 4), ([150], 32, 8)])
+@pytest.mark.parametrize("lens,hq,hkv", [([300, 70], 32, 4), ([200], 16, 1), ([129, 3], 16, 4), ([150], 32, 8),
+                                         ([170, 40], 48, 4), ([90], 12, 1), ([260], 24, 2)])
 def test_head_mean_target_matches_oracle(dsa, lens, hq, hkv):
     pi, probs, lse = _target_case(dsa, lens, hq, hkv, seed=sum(lens) + hq)
     q, k = tl.f64(pi.q), tl.f64(pi.k)
@@ -49,6 +50,32 @@ def test_head_mean_target_matches_oracle(dsa, lens, hq, hkv):
             assert np.all(np.isnan(probs[r, t + 1:])), "entries past the prefix must stay untouched"
             z = scale * np.einsum("shd,hd->hs", np.repeat(k[o:o + t + 1], g, axis=1), q[r])
             np.testing.assert_allclose(lse[r], logsumexp(z, axis=1), atol=1e-4, rtol=1e-5)
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 4), (16, 1), (32, 8), (64, 4), (48, 4), (4, 1)])
+def test_head_mean_target_with_split_keys(dsa, hq, hkv):
+    """Rows whose prefixes span several 2048-key splits (the kernel's key split: per-split
+    statistics merged into lse, per-split probabilities): a window of a 5000-token sequence packed
+    after a 700-token one that crosses the 4096-key split boundary, and a window across the two
+    sequences' boundary; probabilities, untouched entries past each prefix and lse."""
+    lens = [700, 5000]
+    o = lens[0]
+    for row_begin, row_count in ((o + 4060, 70), (o - 6, 12), (o + 2040, 17)):
+        pi, probs, lse = _target_case(dsa, lens, hq, hkv, row_begin=row_begin, row_count=row_count,
+                                      seed=hq + 7 * hkv + row_begin)
+        q, k = tl.f64(pi.q), tl.f64(pi.k)
+        scale = orc.default_softmax_scale(128)
+        g = hq // hkv
+        for i in range(row_count):
+            r = row_begin + i
+            b = 0 if r < o else 1
+            t = r - (0 if b == 0 else o)
+            kp = k[(0 if b == 0 else o):r + 1]
+            want = orc.attention_head_mean_row(q[r], kp, scale)
+            np.testing.assert_allclose(probs[i, :t + 1], want, atol=2e-6, rtol=2e-4, err_msg=f"row {r}")
+            assert np.all(np.isnan(probs[i, t + 1:])), f"row {r}: entries past the prefix must stay untouched"
+            z = scale * np.einsum("shd,hd->hs", np.repeat(kp, g, axis=1), q[r])
+            np.testing.assert_allclose(lse[i], logsumexp(z, axis=1), atol=1e-4, rtol=1e-5, err_msg=f"lse of row {r}")
 
 
 def test_head_mean_target_row_window(dsa):
@@ -109,6 +136,11 @@ def test_head_mean_target_full_32k(dsa):
         dsa.dsa_attn_head_mean(dev["q"], dev["k"], pi.cu_seqlens, c0, chunk, probs, lse, ld=total)
         torch.cuda.synchronize()
         got = probs.cpu().numpy().astype(np.float64)
+        got_lse = lse.cpu().numpy().astype(np.float64)
+        g = hq // k.shape[1]
         for r in rows:
             want = orc.attention_head_mean_row(q[r], k[:r + 1], scale)
             np.testing.assert_allclose(got[r - c0, :r + 1], want, atol=2e-6, rtol=2e-4, err_msg=f"row {r}")
+            z = scale * np.einsum("shd,hd->hs", np.repeat(k[:r + 1], g, axis=1), q[r])
+            np.testing.assert_allclose(got_lse[r - c0], logsumexp(z, axis=1), atol=1e-4, rtol=1e-5,
+                                       err_msg=f"lse of row {r}")
