@@ -116,6 +116,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense-attention context line")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle baseline sample")
+    ap.add_argument("--training-only", action="store_true",
+                    help="run only the training-side sections (attention backward, indexer warm-up) and print them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for counter calibration) and exit")
     return ap.parse_args()
@@ -974,6 +976,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dsa.load()
+    if args.training_only:
+        print(json.dumps({"sparse_attn_backward": attn_bwd_bench(args, dsa, inp),
+                          "indexer_warmup_objective": warmup_bench(args, dsa, inp)}))
+        return
     pre = prefill_section(args, dsa, inp, args.workload, args.steps, args.warmup, full=True)
     peaks = measured_peaks(dsa)
     corr = None if args.no_correlated else correlated_bench(args, dsa, inp)
