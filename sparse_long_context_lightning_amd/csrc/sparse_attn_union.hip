@@ -8,8 +8,8 @@
 //
 // query_union_kernel: one workgroup per block of R rows.  Entry p of row r (sequence offset
 // o, local position t) counts when 0 <= p <= t and names packed KV row o + p; bit j (row j of
-// the block) is OR-ed into an R-bit-per-position bitmap in LDS (128 KiB: one window of 131072
-// KV rows at R = 8, 65536 at R = 16), and each window is compacted in ascending order with
+// the block) is OR-ed into an R-bit-per-position bitmap in LDS (64 KiB: one window of 65536
+// KV rows at R = 8, 32768 at R = 16, 16384 at R = 32), and each window is compacted in ascending order with
 // ballots.  The list is padded to a multiple of 32 entries with (the block's smallest possible
 // KV row, mask 0).
 //
@@ -36,7 +36,10 @@ namespace dsa {
 namespace {
 
 constexpr int kUnionThreads = 512;
-constexpr int kBitmapWords = 32768;  // 128 KiB of LDS: 4 positions per dword at 8 rows, 2 at 16
+// 64 KiB of LDS: 4 positions per dword at 8 rows, 2 at 16, 1 at 32.  Two workgroups fit a CU;
+// with 128 KiB (one per CU, every window twice as long) the 128K prefill's builder took 1.35
+// against 1.06 ms, with 32 / 16 KiB 1.08 / 1.27 ms.
+constexpr int kBitmapWords = 16384;
 
 __device__ __forceinline__ int seq_of_row(const int* cu, int batch, int r) {
   int lo = 0, hi = batch;  // largest s with cu[s] <= r
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
   __shared__ __attribute__((aligned(16))) uint32_t bm[kBitmapWords];
   __shared__ int row_base[kMaxQueryBlock], row_t[kMaxQueryBlock];
   __shared__ int wave_cnt[kWaves];
-  __shared__ int repeated;  // some row lists one position twice
+  __shared__ int wave_chk[kWaves][2];  // valid entries set and bits found, per wave
   const int b = a.block_begin + blockIdx.x;
   const int r0 = b * a.block_rows;
   const int nr = min(a.block_rows, a.rows - r0);
@@ -77,29 +80,50 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
     row_base[tid] = base;
     row_t[tid] = t;
   }
-  if (tid == 0) repeated = 0;
   __syncthreads();
   const int b0 = row_base[0];          // no entry of the block names a KV row below this one
   const int span = r0 + nr - b0;       // KV rows b0 .. r0 + nr - 1
   int* out_rows = a.kv_rows + (size_t)b * a.cap;
   MaskT* out_masks = reinterpret_cast<MaskT*>(BPP == 32 ? (void*)a.masks32 : (void*)a.masks) + (size_t)b * a.cap;
   int total = 0;
+  // A row that lists a position twice sets one bit for two valid entries: the block repeats a
+  // position exactly when the bits in its bitmaps number fewer than its valid entries, so the
+  // bits are set with ORs that return nothing and counted in the compaction.
+  int entries = 0, bits = 0;
+  constexpr int kRowGroup = 8;                                    // rows whose entries are loaded together
+  constexpr int kEpt = (kMaxTopK + kUnionThreads - 1) / kUnionThreads;  // entries per thread, row and pass
   for (int w0 = 0; w0 < span; w0 += kWindow) {
     const int lo = b0 + w0;
     const int limit = min(kWindow, span - w0);   // positions in this window
     const int words = (limit + PPW - 1) / PPW;
     for (int i = tid; i < (words + 3) / 4; i += kUnionThreads) reinterpret_cast<uint4*>(bm)[i] = uint4{0, 0, 0, 0};
     __syncthreads();
-    for (int j = 0; j < nr; ++j) {
-      const int* ir = a.idx + (size_t)(r0 + j) * a.k_sel;
-      const int off = row_base[j] - lo, t = row_t[j];
-#pragma unroll 8
-      for (int i = tid; i < a.k_sel; i += kUnionThreads) {
-        const int p = ir[i];
-        const int x = off + p;
-        if (p >= 0 && p <= t && x >= 0 && x < limit) {
-          const uint32_t bit = 1u << ((BPP == 32 ? 0 : BPP * (x % PPW)) + j);
-          if (atomicOr(&bm[x / PPW], bit) & bit) repeated = 1;
+    for (int j0 = 0; j0 < nr; j0 += kRowGroup) {
+      for (int c0 = 0; c0 < a.k_sel; c0 += kEpt * kUnionThreads) {
+        // every load of the row group issued before any bit is set: one memory latency per group
+        int pv[kRowGroup][kEpt];
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; ++jj)
+#pragma unroll
+          for (int e = 0; e < kEpt; ++e) {
+            const int j = j0 + jj, i = c0 + e * kUnionThreads + tid;
+            pv[jj][e] = (j < nr && i < a.k_sel) ? a.idx[(size_t)(r0 + j) * a.k_sel + i] : -1;
+          }
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; ++jj) {
+          const int j = j0 + jj;
+          if (j >= nr) break;
+          const int off = row_base[j] - lo, t = row_t[j];
+#pragma unroll
+          for (int e = 0; e < kEpt; ++e) {
+            const int p = pv[jj][e];
+            const int x = off + p;
+            if (p >= 0 && p <= t && x >= 0 && x < limit) {
+              const uint32_t bit = 1u << ((BPP == 32 ? 0 : BPP * (x % PPW)) + j);
+              __hip_atomic_fetch_or(&bm[x / PPW], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+              ++entries;
+            }
+          }
         }
       }
     }
@@ -117,7 +141,9 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
     int cnt = 0;
     for (int s = s_begin; s < s_end; s += 64) {
       const int x = s + lane;
-      cnt += x < s_end ? nz_count(bm[x]) : 0;
+      const uint32_t wd = x < s_end ? bm[x] : 0u;
+      cnt += nz_count(wd);
+      bits += __popc(wd);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
@@ -150,7 +176,23 @@ __global__ __launch_bounds__(kUnionThreads) void query_union_kernel(QueryUnionAr
     out_rows[e] = b0;
     out_masks[e] = 0;
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    entries += __shfl_xor(entries, o);
+    bits += __shfl_xor(bits, o);
+  }
+  if (lane == 0) {
+    wave_chk[wave][0] = entries;
+    wave_chk[wave][1] = bits;
+  }
+  __syncthreads();
   if (tid == 0) {
+    int all_entries = 0, all_bits = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      all_entries += wave_chk[w][0];
+      all_bits += wave_chk[w][1];
+    }
+    const bool repeated = all_bits < all_entries;  // some row lists one position twice
     a.counts[b] = total;
     // A block whose rows repeat a position stays with the per-row attention, which counts each
     // listed entry.
