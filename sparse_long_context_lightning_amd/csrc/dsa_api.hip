@@ -308,9 +308,11 @@ hipError_t launch_decode_attn(const void* q, const void* k_cache, const void* v_
   return dsa::launch_attn_combine(a, s);
 }
 
+// mode 0: scores (dsa_index_scores); 1 / 2: the fused top-k's sampling and emitting passes over
+// the top-k scratch `ts` of the rows [row_begin, row_end) (one sequence's chunk).
 int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu, int batch,
                       int h_idx, int d_idx, int row_begin, int row_end, int out_row0, float* scores, long long ld,
-                      hipStream_t stream) {
+                      hipStream_t stream, int mode = 0, const dsa::TopkScratch* ts = nullptr, int k = 0) {
   for (int b = 0; b < batch; ++b) {
     const int r0 = std::max(row_begin, cu[b]);
     const int r1 = std::min(row_end, cu[b + 1]);
@@ -328,7 +330,12 @@ int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, cons
     a.scores = scores;
     a.ld = ld;
     a.key_split = kKeySplit;
-    DSA_TRY(hip_status(dsa::launch_indexer_prefill(a, stream), "indexer launch"));
+    if (mode == 1)
+      DSA_TRY(hip_status(dsa::launch_indexer_prefill_sample(a, *ts, k, stream), "sampling indexer launch"));
+    else if (mode == 2)
+      DSA_TRY(hip_status(dsa::launch_indexer_prefill_emit(a, *ts, k, stream), "emitting indexer launch"));
+    else
+      DSA_TRY(hip_status(dsa::launch_indexer_prefill(a, stream), "indexer launch"));
   }
   return DSA_OK;
 }
@@ -986,7 +993,6 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
     const int o = cu_seqlens_host[b], e = cu_seqlens_host[b + 1];
     for (int c0 = o; c0 < e; c0 += (int)chunk) {
       const int c1 = (int)std::min<long long>(e, c0 + chunk);
-      DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s));
       dsa::TopkArgs t;
       t.scores = scores;
       t.ld = ld;
@@ -997,7 +1003,22 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
       t.idx_out = idx_out + (size_t)c0 * top_k;
       t.values_out = nullptr;
       t.workspace = topk_ws;
-      DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+      // Fused top-k (64-head indexer, more than 512 rows): a sampling indexer pass, the threshold
+      // from its samples, the indexer pass that also appends the candidates, the select.  The
+      // scores are still written, for the select's exact redo of a row whose candidates under-
+      // or overflow.  Otherwise: the indexer, then threshold / collect / select over the scores.
+      if (topk_ws && dsa::indexer_emit_supported(h_idx, d_idx) && c1 - c0 > 512) {
+        const dsa::TopkScratch ts = dsa::topk_wave_scratch(topk_ws, c1 - c0);
+        DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 1,
+                                  &ts, top_k));
+        DSA_TRY(hip_status(dsa::launch_topk_wave_threshold_from_samples(t, s), "top-k threshold launch"));
+        DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 2,
+                                  &ts, top_k));
+        DSA_TRY(hip_status(dsa::launch_topk_wave_select(t, s), "top-k select launch"));
+      } else {
+        DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s));
+        DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+      }
     }
   }
   dsa::SparseAttnArgs a = {};

@@ -45,11 +45,26 @@ __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2,
 // sequence against one split of keys; key tiles of 64 rows are staged in LDS (double buffered)
 // and shared by the 4 waves.  Each wave keeps its 16 RT (token, head) query rows in registers
 // (RT = 4: one token of 64 heads), so every key operand read from LDS feeds RT MFMAs.
-template <int H, int DI, int RT>
+//
+// MODE 0 writes the scores.  The prefill's fused top-k adds two modes (64 heads only, one token
+// per wave):
+//   MODE 1 (sample): the workgroup's keys are 2048 stratified positions of the causal prefix of
+//     its first row (one jittered run of 4 in each of 512 strata, or the whole prefix when it is
+//     no longer), gathered tile by tile; each row with more than k positions gets their scores
+//     as floats at the start of its candidate list and their number in tau_lo;
+//   MODE 2 (emit): the scores are written as in MODE 0, and every (key, position) whose key
+//     reaches the row's tau_lo is staged in LDS and appended to the row's candidate list with one
+//     atomic per stage, which makes the top-k's separate pass over the scores unnecessary.
+constexpr int kSampleCount = 2048;  // sample positions per row (512 strata of 4)
+constexpr int kEmitStage = 512;     // staged candidates per wave
+
+template <int H, int DI, int RT, int MODE>
 __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ w,
     int seq_off, int row_begin, int row_end, int out_row0, float* __restrict__ scores, long long ld,
-    int key_split, int n_rowblk) {
+    int key_split, int n_rowblk, uint32_t* __restrict__ tau_lo, uint32_t* __restrict__ cnt,
+    uint2* __restrict__ cand, int topk) {
+  static_assert(MODE == 0 || (H == 64 && RT == 4), "the fused top-k modes take one 64-head token per wave");
   // RT row tiles of 16 (token, head) rows per wave.
   constexpr int TOKW = (H >= 16) ? 16 * RT / H : 4 * RT;  // tokens per wave (H = 4: 4 per row tile)
   constexpr int TOKWG = 4 * TOKW;
@@ -74,9 +89,15 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int r0 = row_begin + rb * TOKWG;
   if (r0 >= row_end) return;
   const int t_last = min(r0 + TOKWG, row_end) - 1 - seq_off;
-  const int kbeg = split * key_split;
+  // MODE 1: the sample of the first row's prefix (n0 positions), m <= kSampleCount entries
+  const int n0 = r0 - seq_off + 1;
+  const bool whole = n0 <= kSampleCount;
+  const uint32_t sf = whole ? 1u : (uint32_t)(n0 >> 2) / (kSampleCount / 4);  // float4 slots per stratum
+  const int m = whole ? n0 : kSampleCount;
+  if (MODE == 1 && (split > 0 || t_last + 1 <= topk)) return;  // one split; no row needs a threshold
+  const int kbeg = MODE == 1 ? 0 : split * key_split;
   if (kbeg > t_last) return;
-  const int kend = min(kbeg + key_split, t_last + 1);
+  const int kend = MODE == 1 ? m : min(kbeg + key_split, t_last + 1);
   const int ntiles = (kend - kbeg + 63) >> 6;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -132,6 +153,19 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
       lds_dst[b][p] = __builtin_amdgcn_readfirstlane(lds_offset(&lds[b][p * 4096 + wave * 1024]));
   }
   auto load_tile = [&](int tile, int buf) {
+    if (MODE == 1) {
+      // gathered rows: row rr of the tile is sample entry j = 64 tile + rr (the last one repeated
+      // past m), stratum j / 4 at its jittered slot
+#pragma unroll
+      for (int p = 0; p < NLD; ++p) {
+        const uint32_t j = (uint32_t)min(tile * 64 + st_row[p], m - 1);
+        const uint32_t st = j >> 2;
+        const uint32_t pos = whole ? j : 4u * (st * sf + ((st * 2654435761u) >> 8) % sf) + (j & 3u);
+        const uint32_t off = pos * (uint32_t)(DI * 2) + (st_off[p] - (uint32_t)st_row[p] * (uint32_t)(DI * 2));
+        lds_dma16_saddr(ktile, off, buf ? lds_dst[1][p] : lds_dst[0][p]);
+      }
+      return;
+    }
     const char* base = ktile + (size_t)tile * 64 * DI * 2;
     const int keys_left = kend - kbeg - tile * 64;
     if (keys_left >= 64) {
@@ -147,6 +181,25 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   };
   auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
+  // MODE 2: this wave's token (one per wave), its threshold and its candidate list.
+  __shared__ uint2 stage_all[MODE == 2 ? 4 : 1][MODE == 2 ? kEmitStage : 1];
+  uint2* stage = stage_all[MODE == 2 ? wave : 0];
+  uint32_t ns = 0;
+  const int er = wave_r0 - out_row0;  // the token's row in the top-k scratch
+  const bool e_ok = MODE == 2 && wave_r0 < row_end && wave_r0 - seq_off + 1 > topk;
+  const uint32_t tau = e_ok ? tau_lo[er] : 0xFFFFFFFFu;
+  auto flush = [&]() {
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&cnt[er], ns);
+    base = __shfl(base, 0);
+    wave_lds_sync();
+    uint2* cand_row = cand + (size_t)er * kTopkCandCap;
+    for (uint32_t i = lane; i < ns; i += 64)
+      if (base + i < (uint32_t)kTopkCandCap) cand_row[base + i] = stage[i];
+    ns = 0;
+    wave_lds_sync();
+  };
+
   load_tile(0, 0);
   wait_tile();
   __syncthreads();
@@ -154,7 +207,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   for (int it = 0; it < ntiles; ++it) {
     if (it + 1 < ntiles) load_tile(it + 1, (it + 1) & 1);
     const int key0 = kbeg + it * 64;
-    if (wave_r0 < row_end && key0 <= wave_t_last) {
+    if (wave_r0 < row_end && (MODE == 1 || key0 <= wave_t_last)) {
       const unsigned char* tile = lds[it & 1];
       float part[4][NSLOT];
 #pragma unroll
@@ -190,7 +243,23 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
           const float v = transpose_reduce4(part[0][s], part[1][s], part[2][s], part[3][s]);
           const int r = wave_r0 + s;
           const int key = key0 + lane;
+          if (MODE == 1) {
+            if (r < row_end && key < m && r - seq_off + 1 > topk)
+              reinterpret_cast<float*>(cand + (size_t)(r - out_row0) * kTopkCandCap)[key] = v;
+            continue;
+          }
           if (r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
+          if (MODE == 2) {
+            const uint32_t kk = float_key(v);
+            const bool take = e_ok && key <= r - seq_off && kk >= tau;
+            const unsigned long long b = __ballot(take);
+            if (b != 0ull) {
+              if (take) stage[ns + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u))] =
+                  make_uint2(kk, (uint32_t)key);
+              ns += (uint32_t)__popcll(b);
+              if (ns > (uint32_t)(kEmitStage - 64)) flush();
+            }
+          }
         }
       } else {
 #pragma unroll
@@ -206,6 +275,14 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     }
     if (it + 1 < ntiles) wait_tile();
     __syncthreads();
+  }
+  if (MODE == 2 && ns > 0) flush();
+  if (MODE == 1 && lane == 0) {
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const int r = wave_r0 + s;
+      if (r < row_end && r - seq_off + 1 > topk) tau_lo[r - out_row0] = (uint32_t)m;
+    }
   }
 }
 
@@ -333,26 +410,39 @@ __global__ __launch_bounds__(256) void indexer_decode_coop_kernel(
 // ---------------------------------------------------------------------------------------
 // Host launchers.
 
-template <int H, int DI, int RT>
-static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, hipStream_t s) {
+template <int H, int DI, int RT, int MODE>
+static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, const TopkScratch* t, int k, hipStream_t s) {
   constexpr int TOKWG = 4 * ((H >= 16) ? 16 * RT / H : 4 * RT);
   const int rows = a.row_end - a.row_begin;
   const int n_rowblk = (rows + TOKWG - 1) / TOKWG;
   const int t_max = a.row_end - 1 - a.seq_off;
-  const int n_split = (t_max + a.key_split) / a.key_split;
+  const int n_split = MODE == 1 ? 1 : (t_max + a.key_split) / a.key_split;
   long long n = (long long)n_rowblk * n_split;
   n = (n + 7) / 8 * 8;
-  hipLaunchKernelGGL((indexer_prefill_kernel<H, DI, RT>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx, a.w,
-                     a.seq_off, a.row_begin, a.row_end, a.out_row0, a.scores, a.ld, a.key_split, n_rowblk);
+  hipLaunchKernelGGL((indexer_prefill_kernel<H, DI, RT, MODE>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx,
+                     a.w, a.seq_off, a.row_begin, a.row_end, a.out_row0, a.scores, a.ld, a.key_split, n_rowblk,
+                     t ? t->tau_lo : nullptr, t ? t->cnt : nullptr, t ? t->cand : nullptr, k);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s) {
-  if (a.h_idx == 64 && a.d_idx == 128) return launch_prefill_t<64, 128, 4>(a, s);
-  if (a.h_idx == 32 && a.d_idx == 128) return launch_prefill_t<32, 128, 4>(a, s);
-  if (a.h_idx == 16 && a.d_idx == 128) return launch_prefill_t<16, 128, 4>(a, s);
-  if (a.h_idx == 4 && a.d_idx == 64) return launch_prefill_t<4, 64, 4>(a, s);
+  if (a.h_idx == 64 && a.d_idx == 128) return launch_prefill_t<64, 128, 4, 0>(a, nullptr, 0, s);
+  if (a.h_idx == 32 && a.d_idx == 128) return launch_prefill_t<32, 128, 4, 0>(a, nullptr, 0, s);
+  if (a.h_idx == 16 && a.d_idx == 128) return launch_prefill_t<16, 128, 4, 0>(a, nullptr, 0, s);
+  if (a.h_idx == 4 && a.d_idx == 64) return launch_prefill_t<4, 64, 4, 0>(a, nullptr, 0, s);
   return hipErrorInvalidValue;
+}
+
+bool indexer_emit_supported(int h_idx, int d_idx) { return h_idx == 64 && d_idx == 128; }
+
+hipError_t launch_indexer_prefill_sample(const IndexerPrefillArgs& a, const TopkScratch& t, int k, hipStream_t s) {
+  if (!indexer_emit_supported(a.h_idx, a.d_idx)) return hipErrorInvalidValue;
+  return launch_prefill_t<64, 128, 4, 1>(a, &t, k, s);
+}
+
+hipError_t launch_indexer_prefill_emit(const IndexerPrefillArgs& a, const TopkScratch& t, int k, hipStream_t s) {
+  if (!indexer_emit_supported(a.h_idx, a.d_idx)) return hipErrorInvalidValue;
+  return launch_prefill_t<64, 128, 4, 2>(a, &t, k, s);
 }
 
 // Keys per decode workgroup: 2 tiles of 64, both loaded at once (short workgroups, four per CU,

@@ -31,7 +31,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kCapW = 8192;    // candidate list length per row
+constexpr int kCapW = kTopkCandCap;  // candidate list length per row
 constexpr int kStrata = 512;   // sample strata per row: 4 consecutive scores each (8 per lane)
 constexpr int kBins = 1024;    // radix histogram bins (10-bit digits)
 constexpr int kStage = 512;    // per-wave LDS stage of the collect kernel
@@ -155,6 +155,67 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
   const int m = whole ? n : 4 * kStrata;
   // Two 10-bit rounds below the sample's common prefix; tau_lo is the lower edge of the sub-bin
   // that holds the sample's r-th largest key.
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if ((valid >> j) & 1ull) f(key[j], 0u);
+  };
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  each([&](uint32_t kk, uint32_t) {
+    kmin = min(kmin, kk);
+    kmax = max(kmax, kk);
+  });
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  uint32_t need = sample_rank(m, n, k);
+  int low = (kmin == kmax) ? 0 : 32 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = low >= 32 ? 0u : ~((1u << low) - 1u);
+  uint32_t prefix = kmin & mask;
+  for (int round = 0; round < 2 && low > 0; ++round) {
+    const int width = min(low, 10);
+    const int shift = low - width;
+    uint32_t above, in_bin;
+    const uint32_t digit =
+        wave_radix_round(each, prefix, mask, shift, width, need, hist_all[wave], lane, &above, &in_bin);
+    prefix |= digit << shift;
+    mask |= ((1u << width) - 1u) << shift;
+    need -= above;
+    low = shift;
+  }
+  if (lane == 0) tau_lo[row] = prefix;
+}
+
+// The same threshold from a sample the prefill's sampling indexer pass computed directly: m
+// scores (m = tau_lo[row] on entry, at most 4 kStrata) as floats at the start of the row's
+// candidate list; the rank rule and the radix rounds are those above.
+__global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long ld, int rows,
+                                                                     const int* __restrict__ row_len, int len_base,
+                                                                     int k, uint32_t* __restrict__ tau_lo,
+                                                                     uint32_t* __restrict__ cnt,
+                                                                     const uint2* __restrict__ cand) {
+  __shared__ uint32_t hist_all[4][kBins];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const int n = row_length(row_len, len_base, row, ld);
+  const int m = (int)tau_lo[row];
+  if (lane == 0) cnt[row] = 0;
+  if (n <= k) return;
+  const float* smp = reinterpret_cast<const float*>(cand + (size_t)row * kCapW);
+  uint32_t key[32];
+  unsigned long long valid = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = 4 * (lane + 64 * j);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p < m) v = *reinterpret_cast<const float4*>(smp + p);
+    key[4 * j + 0] = float_key(v.x);
+    key[4 * j + 1] = float_key(v.y);
+    key[4 * j + 2] = float_key(v.z);
+    key[4 * j + 3] = float_key(v.w);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) valid |= (unsigned long long)(p + c < m) << (4 * j + c);
+  }
   auto each = [&](auto f) {
 #pragma unroll
     for (int j = 0; j < 32; ++j)
@@ -581,6 +642,35 @@ __global__ __launch_bounds__(NT) void topk_threshold_block_kernel(const float* _
 size_t topk_wave_workspace_bytes(int rows) {
   const size_t head = ((size_t)rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   return head + (size_t)rows * kCapW * sizeof(uint2);
+}
+
+TopkScratch topk_wave_scratch(void* workspace, int rows) {
+  TopkScratch t;
+  t.tau_lo = static_cast<uint32_t*>(workspace);
+  t.cnt = t.tau_lo + rows;
+  const size_t head = ((size_t)rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+  t.cand = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + head);
+  return t;
+}
+
+hipError_t launch_topk_wave_threshold_from_samples(const TopkArgs& a, hipStream_t s) {
+  if (a.rows <= 512) return hipErrorInvalidValue;
+  const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
+  hipLaunchKernelGGL(topk_threshold_sampled_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a.ld, a.rows,
+                     a.row_len, a.len_base, a.k, t.tau_lo, t.cnt, t.cand);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_wave_select(const TopkArgs& a, hipStream_t s) {
+  if (a.rows <= 512) return hipErrorInvalidValue;
+  const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
+  if (a.ld <= 131072)
+    hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
+                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, a.values_out);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
+                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, a.values_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
