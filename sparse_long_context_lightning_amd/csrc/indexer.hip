@@ -33,6 +33,16 @@ __device__ __forceinline__ float swap_sum16(float a, float b) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_int(a), __float_as_int(b), false, false);
   return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
+// Slot permutation of a key row's 16-byte pieces in an LDS tile.  ds_read_b128 serves a wave in
+// lane groups that mix the four 16-lane quarters, so the plain row XOR (piece ^ r) puts lanes of
+// different quarters on the same slots; 256-byte rows use swz, which keeps every group on
+// distinct slots (128-byte rows keep the plain XOR).
+template <int CPR>
+__device__ __forceinline__ int tile_swizzle(int r) {
+  if constexpr (CPR == 16) return swz(r);
+  return r % CPR;
+}
+
 __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2, float p3) {
   // lanes < 32 now hold subtiles 0 / 1 over groups {g, g^2}; lanes >= 32 subtiles 2 / 3
   const float k0 = swap_sum32(p0, p2);
@@ -75,8 +85,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   constexpr int NSLOT = (H >= 16) ? TOKW : RT;
   static_assert(H == 4 || H == 16 || H == 32 || H == 64, "unsupported indexer head count");
   static_assert(DI == 64 || DI == 128, "unsupported indexer dim");
-  // Key tiles: 64 rows, chunk c of row r stored at slot c ^ (r % CPR) (XOR swizzle keeps the
-  // MFMA operand reads free of bank conflicts without padding, so whole waves can fill the
+  // Key tiles: 64 rows, chunk c of row r stored at slot c ^ tile_swizzle<CPR>(r) (the swizzle keeps
+  // the MFMA operand reads free of bank conflicts without padding, so whole waves can fill the
   // tile with direct global-to-LDS loads).
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][64 * PITCH];
 
@@ -100,7 +110,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int kend = MODE == 1 ? m : min(kbeg + key_split, t_last + 1);
   const int ntiles = (kend - kbeg + 63) >> 6;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform over the wave: kept in a scalar register, as is all that derives from it
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, lg = lane >> 4;
 
   // Query rows of this wave as MFMA A operands: lane supplies row 16*rt + n.
@@ -133,7 +144,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
 
   // Tile staging: instruction p of wave w fills LDS bytes [p*4096 + w*1024, +1024) of the
   // tile, lane l the 16 bytes at + 16 l, i.e. row r = (p*4096 + w*1024 + 16 l) / PITCH, slot
-  // l % CPR, which holds the row's chunk (l % CPR) ^ (r % CPR).  Full tiles use fixed
+  // l % CPR, which holds the row's chunk (l % CPR) ^ tile_swizzle(r).  Full tiles use fixed
   // per-thread byte offsets from a tile base that advances uniformly (kept in scalar registers,
   // as are the LDS destinations, so a copy costs no vector instruction); only the last, partial
   // tile clamps its rows to the key range.
@@ -145,7 +156,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   for (int p = 0; p < NLD; ++p) {
     const int pos = p * 4096 + wave * 1024 + lane * 16;
     const int r = pos / PITCH;
-    const int chunk = (lane % CPR) ^ (r % CPR);
+    const int chunk = (lane % CPR) ^ tile_swizzle<CPR>(r);
     st_row[p] = r;
     st_off[p] = (uint32_t)(r * DI + chunk * 8) * 2u;
 #pragma unroll
@@ -210,33 +221,64 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     if (wave_r0 < row_end && (MODE == 1 || key0 <= wave_t_last)) {
       const unsigned char* tile = lds[it & 1];
       float part[4][NSLOT];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
+      // Software pipeline over the four 16-key subtiles: the B operand of subtile st + 1 is read
+      // from LDS while subtile st's MFMAs run, and the ReLU / weight / head-sum epilogue of
+      // subtile st - 1 is interleaved with those MFMAs (one MFMA, then two VALU operations), so
+      // each wave keeps the matrix pipe fed through its own epilogue.
+      auto read_b = [&](int st, u32x4 (&b)[NKS]) {
         const unsigned char* bp = tile + (16 * st + n) * PITCH;
-        u32x4 breg[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          breg[ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * NKS + ks) ^ (n % CPR)) * 16));
-        f32x4 c[RT];
+          b[ks] = *reinterpret_cast<const u32x4*>(bp + (((lg * NKS + ks) ^ tile_swizzle<CPR>(n)) * 16));
+      };
+      auto mma = [&](const u32x4 (&b)[NKS], f32x4 (&c)[RT]) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Raised wave priority while this wave issues its MFMAs: the arbiter then prefers the
-        // waves that keep the matrix pipe fed over those in their epilogue.
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], breg[ks], c[rt]);
-        __builtin_amdgcn_s_setprio(0);
+          for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(areg[rt][ks], b[ks], c[rt]);
+      };
+      auto epilogue = [&](const f32x4 (&c)[RT], float (&p)[NSLOT]) {
 #pragma unroll
-        for (int s = 0; s < NSLOT; ++s) part[st][s] = 0.f;
+        for (int s = 0; s < NSLOT; ++s) p[s] = 0.f;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           const int slot = (H >= 16) ? (16 * rt) / H : rt;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part[st][slot] = fmaf(relu(c[rt][i]), wreg[rt][i], part[st][slot]);
+          for (int i = 0; i < 4; ++i) p[slot] = fmaf(relu(c[rt][i]), wreg[rt][i], p[slot]);
         }
-      }
+      };
+      // A pipeline stage's schedule: its LDS reads (nr instructions) first, then one MFMA and two
+      // VALU operations (ReLU and fma of one earlier result) at a time; stages are fenced off
+      // from each other.
+      auto schedule = [&](auto reads) {
+        if constexpr (decltype(reads)::value) __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+#pragma unroll
+        for (int i = 0; i < RT * NKS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      u32x4 b0[NKS], b1[NKS];
+      f32x4 c0[RT], c1[RT];
+      read_b(0, b0);
+      read_b(1, b1);
+      mma(b0, c0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(2, b0);
+      mma(b1, c1);
+      epilogue(c0, part[0]);
+      schedule(std::true_type{});
+      read_b(3, b1);
+      mma(b0, c0);
+      epilogue(c1, part[1]);
+      schedule(std::true_type{});
+      mma(b1, c1);
+      epilogue(c0, part[2]);
+      schedule(std::false_type{});
+      epilogue(c1, part[3]);
       if constexpr (H >= 16) {
 #pragma unroll
         for (int s = 0; s < NSLOT; ++s) {
@@ -336,14 +378,14 @@ __global__ __launch_bounds__(256) void indexer_decode_coop_kernel(
   }
 
   // Tile staging as in the prefill kernel: instruction p of wave w fills LDS bytes
-  // [p*4096 + w*1024, +1024) of the tile; the row's piece (l % CPR) ^ (r % CPR) lands at slot l % CPR.
+  // [p*4096 + w*1024, +1024) of the tile; the row's piece (l % CPR) ^ tile_swizzle(r) lands at slot l % CPR.
   const uint16_t* kseq = k_cache + ((size_t)b * s_max + kbeg) * DI;
   int st_row[NLD], st_off[NLD];
 #pragma unroll
   for (int p = 0; p < NLD; ++p) {
     const int pos = p * 4096 + wave * 1024 + lane * 16;
     const int r = pos / PITCH;
-    const int chunk = (lane % CPR) ^ (r % CPR);
+    const int chunk = (lane % CPR) ^ tile_swizzle<CPR>(r);
     st_row[p] = r;
     st_off[p] = chunk * 8;
   }
@@ -383,7 +425,7 @@ __global__ __launch_bounds__(256) void indexer_decode_coop_kernel(
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 bq = *reinterpret_cast<const u32x4*>(bp + (((lg * NKS + ks) ^ (n % CPR)) * 16));
+        const u32x4 bq = *reinterpret_cast<const u32x4*>(bp + (((lg * NKS + ks) ^ tile_swizzle<CPR>(n)) * 16));
         c = mfma16x16x32(areg[ks], bq, c);
       }
       float acc = 0.f;

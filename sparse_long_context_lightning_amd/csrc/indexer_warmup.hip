@@ -138,7 +138,8 @@ __global__ __launch_bounds__(64 * HeadMeanShape<HKV>::NWV) void attn_head_mean_k
 
   // DMA mapping: instruction p of wave w (job P = p * NWV + w) fills LDS bytes [P*1024, +1024);
   // lane l's 16 bytes land at row (position pos, group gg), slot l % 16, which holds piece
-  // (l % 16) ^ (pos % 16).
+  // (l % 16) ^ swz(pos) (the plain pos % 16 would put lanes of different quarters of a wave on
+  // the same LDS slots in the operand reads).
   const uint16_t* kseq = a.k + (size_t)a.seq_off * HKV * 128;
   const int kv_len = wg_last - a.seq_off + 1;  // positions the workgroup can use
   auto load_tile = [&](int tile, int buf) {
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(64 * HeadMeanShape<HKV>::NWV) void attn_head_mean_k
       const int byte = (p * NWV + wave) * 1024 + lane * 16;
       const int pos_in = byte / ROWB;
       const int gg = (byte % ROWB) / 256;
-      const int piece = (lane & 15) ^ (pos_in & 15);
+      const int piece = (lane & 15) ^ swz(pos_in);
       const int pos = min(tile * TK + pos_in, kv_len - 1);
       lds_dma16(kseq + (size_t)pos * HKV * 128 + gg * 128 + piece * 8, &tiles[buf][(p * NWV + wave) * 1024]);
     }
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(64 * HeadMeanShape<HKV>::NWV) void attn_head_mean_k
         for (int rt = 0; rt < RT; ++rt) c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 kb = *reinterpret_cast<const u32x4*>(rowp + (((lg * 4 + ks) ^ (pos_t & 15)) * 16));
+          const u32x4 kb = *reinterpret_cast<const u32x4*>(rowp + (((lg * 4 + ks) ^ swz(pos_t)) * 16));
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) c[rt] = mfma16x16x32(qa[rt][ks], kb, c[rt]);
         }
