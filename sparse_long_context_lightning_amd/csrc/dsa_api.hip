@@ -308,8 +308,9 @@ hipError_t launch_decode_attn(const void* q, const void* k_cache, const void* v_
   return dsa::launch_attn_combine(a, s);
 }
 
-// mode 0: scores (dsa_index_scores); 1 / 2: the fused top-k's sampling and emitting passes over
-// the top-k scratch `ts` of the rows [row_begin, row_end) (one sequence's chunk).
+// mode 0: scores (dsa_index_scores); 1 / 2 / 3: the fused top-k's sampling, emitting and
+// rescoring passes over the top-k scratch `ts` of the rows [row_begin, row_end) (one sequence's
+// chunk).
 int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu, int batch,
                       int h_idx, int d_idx, int row_begin, int row_end, int out_row0, float* scores, long long ld,
                       hipStream_t stream, int mode = 0, const dsa::TopkScratch* ts = nullptr, int k = 0) {
@@ -334,6 +335,8 @@ int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, cons
       DSA_TRY(hip_status(dsa::launch_indexer_prefill_sample(a, *ts, k, stream), "sampling indexer launch"));
     else if (mode == 2)
       DSA_TRY(hip_status(dsa::launch_indexer_prefill_emit(a, *ts, k, stream), "emitting indexer launch"));
+    else if (mode == 3)
+      DSA_TRY(hip_status(dsa::launch_indexer_prefill_rescore(a, *ts, stream), "rescoring indexer launch"));
     else
       DSA_TRY(hip_status(dsa::launch_indexer_prefill(a, stream), "indexer launch"));
   }
@@ -1004,9 +1007,10 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
       t.values_out = nullptr;
       t.workspace = topk_ws;
       // Fused top-k (64-head indexer, more than 512 rows): a sampling indexer pass, the threshold
-      // from its samples, the indexer pass that also appends the candidates, the select.  The
-      // scores are still written, for the select's exact redo of a row whose candidates under-
-      // or overflow.  Otherwise: the indexer, then threshold / collect / select over the scores.
+      // from its samples, the indexer pass that appends the candidates (no scores written), the
+      // select; a row whose candidates under- or overflowed is then scored into the chunk's score
+      // rows and selected exactly from them (two launches that find nothing to do when no row
+      // failed).  Otherwise: the indexer, then threshold / collect / select over the scores.
       if (topk_ws && dsa::indexer_emit_supported(h_idx, d_idx) && c1 - c0 > 512) {
         const dsa::TopkScratch ts = dsa::topk_wave_scratch(topk_ws, c1 - c0);
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 1,
@@ -1015,6 +1019,9 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 2,
                                   &ts, top_k));
         DSA_TRY(hip_status(dsa::launch_topk_wave_select(t, s), "top-k select launch"));
+        DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 3,
+                                  &ts, top_k));
+        DSA_TRY(hip_status(dsa::launch_topk_wave_redo(t, s), "top-k redo launch"));
       } else {
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s));
         DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));

@@ -56,16 +56,19 @@ __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2,
 // and shared by the 4 waves.  Each wave keeps its 16 RT (token, head) query rows in registers
 // (RT = 4: one token of 64 heads), so every key operand read from LDS feeds RT MFMAs.
 //
-// MODE 0 writes the scores.  The prefill's fused top-k adds two modes (64 heads only, one token
-// per wave):
+// MODE 0 writes the scores (with only_rows set, only for the 4-row blocks holding a flagged row:
+// the fused top-k's rescoring pass).  The prefill's fused top-k adds two modes (64 heads only,
+// one token per wave):
 //   MODE 1 (sample): the workgroup's keys are 2048 stratified positions of the causal prefix of
 //     its first row (one jittered run of 4 in each of 512 strata, or the whole prefix when it is
-//     no longer), gathered tile by tile; each row with more than k positions gets their scores
-//     as floats at the start of its candidate list and their number in tau_lo;
-//   MODE 2 (emit): the scores are written as in MODE 0, and every (key, position) whose key
-//     reaches the row's tau_lo is staged in LDS and appended to the row's candidate list with one
-//     atomic per stage, which makes the top-k's separate pass over the scores unnecessary.
+//     no longer), gathered tile by tile by kSampleSplits workgroups; each row with more than k
+//     positions gets their scores as floats at the start of its candidate list and their number
+//     in tau_lo;
+//   MODE 2 (emit): every (key, position) whose key reaches the row's tau_lo is staged in LDS and
+//     appended to the row's candidate list with one atomic per stage; no score is written, so
+//     neither this pass nor the top-k moves the score rows through memory.
 constexpr int kSampleCount = 2048;  // sample positions per row (512 strata of 4)
+constexpr int kSampleSplits = 4;    // workgroups per row block in the sampling pass (512 entries each)
 constexpr int kEmitStage = 512;     // staged candidates per wave
 
 template <int H, int DI, int RT, int MODE>
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const float* __restrict__ w,
     int seq_off, int row_begin, int row_end, int out_row0, float* __restrict__ scores, long long ld,
     int key_split, int n_rowblk, uint32_t* __restrict__ tau_lo, uint32_t* __restrict__ cnt,
-    uint2* __restrict__ cand, int topk) {
+    uint2* __restrict__ cand, int topk, const uint32_t* __restrict__ only_rows) {
   static_assert(MODE == 0 || (H == 64 && RT == 4), "the fused top-k modes take one 64-head token per wave");
   // RT row tiles of 16 (token, head) rows per wave.
   constexpr int TOKW = (H >= 16) ? 16 * RT / H : 4 * RT;  // tokens per wave (H = 4: 4 per row tile)
@@ -98,16 +101,23 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int rb = wi - split * n_rowblk;
   const int r0 = row_begin + rb * TOKWG;
   if (r0 >= row_end) return;
+  if (MODE == 0 && only_rows) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < TOKWG; ++i) any |= r0 + i < row_end && only_rows[r0 + i - out_row0] != 0;
+    if (!any) return;
+  }
   const int t_last = min(r0 + TOKWG, row_end) - 1 - seq_off;
   // MODE 1: the sample of the first row's prefix (n0 positions), m <= kSampleCount entries
   const int n0 = r0 - seq_off + 1;
   const bool whole = n0 <= kSampleCount;
   const uint32_t sf = whole ? 1u : (uint32_t)(n0 >> 2) / (kSampleCount / 4);  // float4 slots per stratum
   const int m = whole ? n0 : kSampleCount;
-  if (MODE == 1 && (split > 0 || t_last + 1 <= topk)) return;  // one split; no row needs a threshold
-  const int kbeg = MODE == 1 ? 0 : split * key_split;
-  if (kbeg > t_last) return;
-  const int kend = MODE == 1 ? m : min(kbeg + key_split, t_last + 1);
+  if (MODE == 1 && t_last + 1 <= topk) return;  // no row needs a threshold
+  // MODE 1: split s takes sample entries [s * kSampleCount / kSampleSplits, ...) of the m
+  const int kbeg = MODE == 1 ? split * (kSampleCount / kSampleSplits) : split * key_split;
+  if (MODE == 1 ? kbeg >= m : kbeg > t_last) return;
+  const int kend = MODE == 1 ? min(m, kbeg + kSampleCount / kSampleSplits) : min(kbeg + key_split, t_last + 1);
   const int ntiles = (kend - kbeg + 63) >> 6;
 
   // the wave index is uniform over the wave: kept in a scalar register, as is all that derives from it
@@ -148,7 +158,8 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   // per-thread byte offsets from a tile base that advances uniformly (kept in scalar registers,
   // as are the LDS destinations, so a copy costs no vector instruction); only the last, partial
   // tile clamps its rows to the key range.
-  const char* ktile = reinterpret_cast<const char*>(k_idx + (size_t)(seq_off + kbeg) * DI);
+  // (MODE 1 gathers by absolute position: its base is the sequence start)
+  const char* ktile = reinterpret_cast<const char*>(k_idx + (size_t)(seq_off + (MODE == 1 ? 0 : kbeg)) * DI);
   int st_row[NLD];
   uint32_t st_off[NLD];      // byte offset of the lane's 16 bytes within a tile
   uint32_t lds_dst[2][NLD];  // wave-uniform LDS destinations
@@ -169,7 +180,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
       // past m), stratum j / 4 at its jittered slot
 #pragma unroll
       for (int p = 0; p < NLD; ++p) {
-        const uint32_t j = (uint32_t)min(tile * 64 + st_row[p], m - 1);
+        const uint32_t j = (uint32_t)min(kbeg + tile * 64 + st_row[p], m - 1);
         const uint32_t st = j >> 2;
         const uint32_t pos = whole ? j : 4u * (st * sf + ((st * 2654435761u) >> 8) % sf) + (j & 3u);
         const uint32_t off = pos * (uint32_t)(DI * 2) + (st_off[p] - (uint32_t)st_row[p] * (uint32_t)(DI * 2));
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
               reinterpret_cast<float*>(cand + (size_t)(r - out_row0) * kTopkCandCap)[key] = v;
             continue;
           }
-          if (r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
+          if (MODE == 0 && r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
           if (MODE == 2) {
             const uint32_t kk = float_key(v);
             const bool take = e_ok && key <= r - seq_off && kk >= tau;
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     __syncthreads();
   }
   if (MODE == 2 && ns > 0) flush();
-  if (MODE == 1 && lane == 0) {
+  if (MODE == 1 && split == 0 && lane == 0) {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
       const int r = wave_r0 + s;
@@ -453,17 +464,18 @@ __global__ __launch_bounds__(256) void indexer_decode_coop_kernel(
 // Host launchers.
 
 template <int H, int DI, int RT, int MODE>
-static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, const TopkScratch* t, int k, hipStream_t s) {
+static hipError_t launch_prefill_t(const IndexerPrefillArgs& a, const TopkScratch* t, int k, hipStream_t s,
+                                   const uint32_t* only_rows = nullptr) {
   constexpr int TOKWG = 4 * ((H >= 16) ? 16 * RT / H : 4 * RT);
   const int rows = a.row_end - a.row_begin;
   const int n_rowblk = (rows + TOKWG - 1) / TOKWG;
   const int t_max = a.row_end - 1 - a.seq_off;
-  const int n_split = MODE == 1 ? 1 : (t_max + a.key_split) / a.key_split;
+  const int n_split = MODE == 1 ? kSampleSplits : (t_max + a.key_split) / a.key_split;
   long long n = (long long)n_rowblk * n_split;
   n = (n + 7) / 8 * 8;
   hipLaunchKernelGGL((indexer_prefill_kernel<H, DI, RT, MODE>), dim3((unsigned)n), dim3(256), 0, s, a.q_idx, a.k_idx,
                      a.w, a.seq_off, a.row_begin, a.row_end, a.out_row0, a.scores, a.ld, a.key_split, n_rowblk,
-                     t ? t->tau_lo : nullptr, t ? t->cnt : nullptr, t ? t->cand : nullptr, k);
+                     t ? t->tau_lo : nullptr, t ? t->cnt : nullptr, t ? t->cand : nullptr, k, only_rows);
   return hipGetLastError();
 }
 
@@ -485,6 +497,11 @@ hipError_t launch_indexer_prefill_sample(const IndexerPrefillArgs& a, const Topk
 hipError_t launch_indexer_prefill_emit(const IndexerPrefillArgs& a, const TopkScratch& t, int k, hipStream_t s) {
   if (!indexer_emit_supported(a.h_idx, a.d_idx)) return hipErrorInvalidValue;
   return launch_prefill_t<64, 128, 4, 2>(a, &t, k, s);
+}
+
+hipError_t launch_indexer_prefill_rescore(const IndexerPrefillArgs& a, const TopkScratch& t, hipStream_t s) {
+  if (!indexer_emit_supported(a.h_idx, a.d_idx)) return hipErrorInvalidValue;
+  return launch_prefill_t<64, 128, 4, 0>(a, nullptr, 0, s, t.fail);
 }
 
 // Keys per decode workgroup: 2 tiles of 64, both loaded at once (short workgroups, four per CU,

@@ -44,22 +44,27 @@ struct TopkArgs {
 
 // Scratch of the wave-parallel top-k (per-row threshold, counter and candidate list).
 size_t topk_wave_workspace_bytes(int rows);
-// Its layout: tau_lo [rows] uint32, cnt [rows] uint32, then (256-byte aligned) cand [rows,
-// kTopkCandCap] (key, position) pairs.
+// Its layout: tau_lo [rows] uint32, cnt [rows] uint32, fail [rows] uint32 (the fused form's
+// redo flags), then (256-byte aligned) cand [rows, kTopkCandCap] (key, position) pairs.
 constexpr int kTopkCandCap = 8192;
 struct TopkScratch {
   uint32_t* tau_lo;
   uint32_t* cnt;
+  uint32_t* fail;
   uint2* cand;
 };
 TopkScratch topk_wave_scratch(void* workspace, int rows);
-// The prefill's fused top-k (no collect pass): the sampling indexer pass leaves, per row with
-// more than k positions, m <= 2048 sample scores as floats at the start of the row's candidate
-// list and m in tau_lo; this threshold launch turns them into tau_lo (and clears cnt), the
-// emitting indexer pass appends the candidates itself, and the select launch finishes.  Rows
-// must be more than 512 (the sample size of the few-row form differs).
+// The prefill's fused top-k (no collect pass, no scores written): the sampling indexer pass
+// leaves, per row with more than k positions, m <= 2048 sample scores as floats at the start of
+// the row's candidate list and m in tau_lo; this threshold launch turns them into tau_lo (and
+// clears cnt and fail), the emitting indexer pass appends the candidates itself, and the select
+// launch finishes every row whose list holds k to kTopkCandCap entries and sets fail for the
+// others.  The rescoring indexer pass then writes the flagged rows' scores (a.scores) and the
+// redo launch selects those rows exactly from them; both find nothing to do when no row failed.
+// Rows must be more than 512 (the sample size of the few-row form differs); no values_out.
 hipError_t launch_topk_wave_threshold_from_samples(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_wave_select(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_wave_redo(const TopkArgs& a, hipStream_t s);
 // Longest row (ld) the wave-parallel top-k handles; longer rows use the row-block kernel.
 constexpr long long kTopkWaveMaxLd = 262144;
 hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s);
@@ -214,13 +219,15 @@ bool union_attn_supported(int hq, int hkv, long long rows);
 hipError_t launch_sparse_attn_union(const UnionAttnArgs& a, hipStream_t s);
 
 hipError_t launch_indexer_prefill(const IndexerPrefillArgs& a, hipStream_t s);
-// The fused top-k's two indexer passes (h_idx = 64, d_idx = 128 only; rows index the top-k
-// scratch as packed row - out_row0): 2048 stratified sample scores per row (sample), and the
-// full scores with every (key, position) at or above the row's tau_lo appended to its
-// candidate list (emit).
+// The fused top-k's indexer passes (h_idx = 64, d_idx = 128 only; rows index the top-k scratch
+// as packed row - out_row0): 2048 stratified sample scores per row (sample); every (key,
+// position) at or above the row's tau_lo appended to its candidate list, no scores written
+// (emit); the scores of the rows whose fail flag is set, as launch_indexer_prefill writes them
+// (rescore: the other 4-row blocks return at once).
 bool indexer_emit_supported(int h_idx, int d_idx);
 hipError_t launch_indexer_prefill_sample(const IndexerPrefillArgs& a, const TopkScratch& t, int k, hipStream_t s);
 hipError_t launch_indexer_prefill_emit(const IndexerPrefillArgs& a, const TopkScratch& t, int k, hipStream_t s);
+hipError_t launch_indexer_prefill_rescore(const IndexerPrefillArgs& a, const TopkScratch& t, hipStream_t s);
 hipError_t launch_attn_head_mean(const HeadMeanArgs& a, hipStream_t s);
 // Row loss KL(target || softmax(scores)) and grad = softmax(scores) - target (grad may alias
 // scores); row lengths from row_len or len_base + row + 1.

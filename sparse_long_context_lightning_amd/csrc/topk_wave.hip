@@ -25,6 +25,11 @@
 //      ascending order.  About 20 KB of LDS per row lets several rows run per CU.
 // A row whose candidates number fewer than k or more than the list holds is redone exactly by
 // the same workgroup from the row itself.  No result depends on the path taken or on timing.
+//
+// The prefill's fused form replaces 1-2: its indexer passes leave a sample per row and then
+// append the candidates themselves without writing scores, so the select only flags a row whose
+// list under- or overflowed; the indexer then scores the flagged rows (and only those) into the
+// score rows, and a second select launch redoes them exactly from there.
 #include "common.h"
 #include "kernels.h"
 
@@ -192,6 +197,7 @@ __global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long l
                                                                      const int* __restrict__ row_len, int len_base,
                                                                      int k, uint32_t* __restrict__ tau_lo,
                                                                      uint32_t* __restrict__ cnt,
+                                                                     uint32_t* __restrict__ fail,
                                                                      const uint2* __restrict__ cand) {
   __shared__ uint32_t hist_all[4][kBins];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -199,7 +205,10 @@ __global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long l
   if (row >= rows) return;
   const int n = row_length(row_len, len_base, row, ld);
   const int m = (int)tau_lo[row];
-  if (lane == 0) cnt[row] = 0;
+  if (lane == 0) {
+    cnt[row] = 0;
+    fail[row] = 0;
+  }
   if (n <= k) return;
   const float* smp = reinterpret_cast<const float*>(cand + (size_t)row * kCapW);
   uint32_t key[32];
@@ -543,7 +552,8 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
                                                                   int len_base, int k, const uint32_t* __restrict__ cnt,
                                                                   const uint2* __restrict__ cand,
                                                                   int* __restrict__ idx_out,
-                                                                  float* __restrict__ values_out) {
+                                                                  float* __restrict__ values_out,
+                                                                  uint32_t* __restrict__ fail, int redo) {
   constexpr int kPer = kCapW / NT;  // candidates per thread
   __shared__ __attribute__((aligned(16))) uint32_t bits[NW];
   __shared__ SelSmem<NT> sm;
@@ -553,6 +563,9 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
   int* out = idx_out + (size_t)row * k;
   float* vout = values_out ? values_out + (size_t)row * k : nullptr;
   const float* src = scores + (size_t)row * ld;
+  // Fused prefill (fail non-null, no scores written): a row whose list under- or overflowed is
+  // flagged here (redo = 0) and finished by the redo launch (redo = 1) once its scores exist.
+  if (redo && (n <= k || fail[row] == 0)) return;
 
   if (n <= k) {
     for (int i = tid; i < k; i += NT) {
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
     return;
   }
   const uint32_t count = cnt[row];
-  if (count >= (uint32_t)k && count <= (uint32_t)kCapW) {
+  if (!redo && count >= (uint32_t)k && count <= (uint32_t)kCapW) {
     const uint2* cr = cand + (size_t)row * kCapW;
     uint32_t ck[kPer], cp[kPer];
 #pragma unroll
@@ -578,6 +591,8 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(const float* __restrict
         if (tid + NT * j < (int)count) f(ck[j], cp[j]);
     };
     block_select_emit<NT, NW>(sm, bits, each, k, src, out, vout);
+  } else if (fail && !redo) {
+    if (tid == 0) fail[row] = 1;
   } else {
     auto each = [&](auto f) {
       for (int i = tid; i < n; i += NT) f(float_key(src[i]), (uint32_t)i);
@@ -639,17 +654,16 @@ __global__ __launch_bounds__(NT) void topk_threshold_block_kernel(const float* _
 
 }  // namespace
 
-size_t topk_wave_workspace_bytes(int rows) {
-  const size_t head = ((size_t)rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
-  return head + (size_t)rows * kCapW * sizeof(uint2);
-}
+static size_t topk_wave_head_bytes(int rows) { return ((size_t)rows * 3 * sizeof(uint32_t) + 255) / 256 * 256; }
+
+size_t topk_wave_workspace_bytes(int rows) { return topk_wave_head_bytes(rows) + (size_t)rows * kCapW * sizeof(uint2); }
 
 TopkScratch topk_wave_scratch(void* workspace, int rows) {
   TopkScratch t;
   t.tau_lo = static_cast<uint32_t*>(workspace);
   t.cnt = t.tau_lo + rows;
-  const size_t head = ((size_t)rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
-  t.cand = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + head);
+  t.fail = t.cnt + rows;
+  t.cand = reinterpret_cast<uint2*>(static_cast<char*>(workspace) + topk_wave_head_bytes(rows));
   return t;
 }
 
@@ -657,27 +671,33 @@ hipError_t launch_topk_wave_threshold_from_samples(const TopkArgs& a, hipStream_
   if (a.rows <= 512) return hipErrorInvalidValue;
   const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
   hipLaunchKernelGGL(topk_threshold_sampled_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0, s, a.ld, a.rows,
-                     a.row_len, a.len_base, a.k, t.tau_lo, t.cnt, t.cand);
+                     a.row_len, a.len_base, a.k, t.tau_lo, t.cnt, t.fail, t.cand);
   return hipGetLastError();
 }
 
-hipError_t launch_topk_wave_select(const TopkArgs& a, hipStream_t s) {
-  if (a.rows <= 512) return hipErrorInvalidValue;
+static hipError_t launch_fused_select(const TopkArgs& a, int redo, hipStream_t s) {
+  // the candidate lists hold keys and positions only: no values without the scores
+  if (a.rows <= 512 || a.values_out) return hipErrorInvalidValue;
   const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
   if (a.ld <= 131072)
     hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, a.values_out);
+                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
+                       redo);
   else
     hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, a.values_out);
+                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
+                       redo);
   return hipGetLastError();
 }
 
+hipError_t launch_topk_wave_select(const TopkArgs& a, hipStream_t s) { return launch_fused_select(a, 0, s); }
+hipError_t launch_topk_wave_redo(const TopkArgs& a, hipStream_t s) { return launch_fused_select(a, 1, s); }
+
 hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
-  uint32_t* tau_lo = static_cast<uint32_t*>(a.workspace);
-  uint32_t* cnt = tau_lo + a.rows;
-  const size_t head = ((size_t)a.rows * 2 * sizeof(uint32_t) + 255) / 256 * 256;
-  uint2* cand = reinterpret_cast<uint2*>(static_cast<char*>(a.workspace) + head);
+  const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
+  uint32_t* tau_lo = t.tau_lo;
+  uint32_t* cnt = t.cnt;
+  uint2* cand = t.cand;
   const bool few = a.rows <= 512;
   if (few) {
     // few rows: a 1024-thread workgroup per row and a four times larger sample
@@ -710,17 +730,17 @@ hipError_t launch_topk_wave(const TopkArgs& a, hipStream_t s) {
   if (few) {
     if (a.ld <= 131072)
       hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreadsFew>), dim3((unsigned)a.rows), dim3(kSelThreadsFew), 0,
-                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out, nullptr, 0);
     else
       hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreadsFew>), dim3((unsigned)a.rows), dim3(kSelThreadsFew), 0,
-                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+                         s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out, nullptr, 0);
   } else {
     if (a.ld <= 131072)
       hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out, nullptr, 0);
     else
       hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out);
+                         a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, cnt, cand, a.idx_out, a.values_out, nullptr, 0);
   }
   return hipGetLastError();
 }

@@ -380,6 +380,30 @@ def test_prefill_varlen_and_chunking(dsa, lens, chunk_rows):
     tl.check_index_structure(got_idx, row_lens, pi.top_k)
 
 
+def test_prefill_fused_topk_rows_whose_candidates_overflow(dsa):
+    """The fused prefill top-k keeps at most 8192 candidates per row.  Rows past position 8192
+    whose indexer weights are all zero score exactly 0 at every position, so every position ties at
+    the threshold and the list overflows: such a row is flagged, scored into the chunk's score rows
+    and selected exactly (the lowest k positions among equals).  Their 4-row neighbours and the rest
+    of the chunk keep the candidate path."""
+    lens = [9000]
+    pi = inp.prefill_inputs(lens, 64, 128, 32, 4, 128, 512, seed=91)
+    tied = [8200, 8203, 8640, 8999]
+    pi.w[tied] = 0.0
+    dev = tl.upload_prefill(pi)
+    out, lse, idx = dsa.prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"],
+                                pi.cu_seqlens, pi.top_k)
+    got_idx = idx.cpu().numpy()
+    for r in tied:
+        assert np.array_equal(got_idx[r], np.arange(pi.top_k)), f"row {r}"
+    rows = tied + [8201, 8202, 8641, 8500, 8998, 8191, 4000, 100]
+    want = tl.oracle_prefill_rows_lazy(pi, rows)
+    tl.assert_idx_equal(got_idx[rows], want["idx"], rows, "idx")
+    tl.assert_attn_close(tl.bf16_tensor_to_f64(out)[rows], want["out"], "O")
+    assert np.max(np.abs(lse.cpu().numpy()[rows] - want["lse"])) <= tl.LSE_ABS
+    tl.check_index_structure(got_idx, np.arange(1, lens[0] + 1), pi.top_k)
+
+
 def test_prefill_equals_composition_and_is_deterministic(dsa):
     torch = _torch()
     lens = [900, 333]
