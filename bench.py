@@ -6,11 +6,12 @@
 A step is one pass of the whole prefill path (indexer -> top-k -> sparse GQA attention) over
 the 128K-token prefill workload (batch 1, L = 131072 causal, k = 2048, 64 indexer heads of
 dim 128, 32 query / 4 KV heads of dim 128, keys in 16-token blocks), with every input already
-resident in HBM.  The timed step is the fused dsa_prefill call; the same chunk schedule is then
-driven through the C ABI's separate entry points with HIP events on the launch stream around
-every kernel, which gives the per-kernel times (and the rooflines) beside it.  The attention
-step runs with adjacent-query dedup (merged index sets of 8-row blocks); the fused call is also
-timed with a workspace too small for the merged sets, which attends per row.
+resident in HBM.  The timed step is the fused dsa_prefill call; the same call is then repeated
+with the library's launch timing on (dsa_timing_enable: two HIP events on the launch stream
+around each of its launches), which gives the per-kernel times of that very schedule (and the
+rooflines) beside it.  The attention step runs with adjacent-query dedup (merged index sets of
+8-row blocks); the fused call is also timed with a workspace too small for the merged sets,
+which attends per row.
 
 Each sparse-attention kernel is read three ways: its HBM traffic from the committed rocprofv3
 counter runs (FETCH_SIZE + WRITE_SIZE, calibrated) over its time against the 8 TB/s peak, its
@@ -136,39 +137,6 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
 
 
-class Timer:
-    """HIP events on torch's current stream (the stream every library call is enqueued on)."""
-
-    def __init__(self):
-        import torch
-        self.torch = torch
-        self.pending = {}
-        self.total = {}
-        self.count = {}
-
-    def start(self, name):
-        ev = self.torch.cuda.Event(enable_timing=True)
-        ev.record()
-        return (name, ev)
-
-    def stop(self, tok):
-        name, ev0 = tok
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev1.record()
-        self.pending.setdefault(name, []).append((ev0, ev1))
-
-    def collect(self):
-        self.torch.cuda.synchronize()
-        for name, evs in self.pending.items():
-            for a, b in evs:
-                self.total[name] = self.total.get(name, 0.0) + a.elapsed_time(b)
-                self.count[name] = self.count.get(name, 0) + 1
-        self.pending = {}
-
-    def reset(self):
-        self.pending, self.total, self.count = {}, {}, {}
-
-
 def best_ms(fn, reps=3):
     """Best of `reps` event-timed calls (after one untimed call)."""
     import torch
@@ -209,9 +177,10 @@ def gather_ceiling(dsa, k, v, idx, nsplits=(1,), row_stride=0, group_fastest=Fal
 
 
 def prefill_section(args, dsa, inp, name, steps, warmup, full):
-    """The fused prefill on workload `name` (the timed step), then the same chunk schedule through the
-    separate entry points for per-kernel times and rooflines.  `full` adds the prefill without dedup,
-    the 16-row merged-set statistics, the gather ceilings and the rows kept for the oracle's check."""
+    """The fused prefill on workload `name` (the timed step), then the same fused call with the
+    library's launch timing on (HIP events on the launch stream around each of its launches) for
+    per-kernel times and rooflines.  `full` adds the prefill without dedup, the 16-row merged-set
+    statistics, the gather ceilings and the rows kept for the oracle's check."""
     import torch
     t0 = time.time()
     pi = inp.workload(name)
@@ -237,36 +206,12 @@ def prefill_section(args, dsa, inp, name, steps, warmup, full):
     u_counts = torch.empty(nb, dtype=torch.int32, device="cuda")
     u_rows = torch.empty((nb, cap), dtype=torch.int32, device="cuda")
     u_masks = torch.empty((nb, cap), dtype=torch.int16, device="cuda")
-    scores = ws.view(torch.float32)[: chunk * ld].view(chunk, ld)
-    # Same carving as dsa_prefill: the chunk's scores, then the top-k scratch (256-byte aligned).
+    # Same carving as dsa_prefill: the chunk's score rows, then the top-k scratch (256-byte aligned;
+    # per row a threshold, a candidate count and a redo flag, then the candidate lists).
     topk_off = (chunk * ld * 4 + 255) // 256 * 256
-    topk_ws = ws[topk_off:]
     out = torch.empty_like(dev["q"])
     lse = torch.empty(total, hq, dtype=torch.float32, device="cuda")
     idx = torch.empty(total, k, dtype=torch.int32, device="cuda")
-    row_len = torch.from_numpy(np.concatenate([np.arange(1, n + 1) for n in lens]).astype(np.int32)).cuda()
-    timer = Timer()
-
-    def step():
-        for b in range(len(lens)):
-            o, e = int(cu[b]), int(cu[b + 1])
-            for c0 in range(o, e, chunk):
-                c1 = min(e, c0 + chunk)
-                tok = timer.start("indexer")
-                dsa.dsa_index_scores(dev["q_idx"], dev["k_idx"], dev["w"], cu, c0, c1 - c0, scores, ld=ld)
-                timer.stop(tok)
-                tok = timer.start("topk")
-                dsa.dsa_topk(scores, row_len[c0:c1], k, idx[c0:c1], workspace=topk_ws, ld=ld)
-                timer.stop(tok)
-        # The attention step as dsa_prefill runs it (top-k sets never repeat a position, so every
-        # 8-row block is attended from its merged set): merged sets, then the merged-set kernel.
-        tok = timer.start("query_union")
-        dsa.dsa_query_union(idx, dev["cu"], u_counts, u_rows, u_masks, ublk)
-        timer.stop(tok)
-        tok = timer.start("sparse_attn")
-        dsa.dsa_sparse_gqa_attn_union(dev["q"], dev["k"], dev["v"], u_counts, u_rows, u_masks, out, lse,
-                                      block_rows=ublk)
-        timer.stop(tok)
 
     def fused(workspace=ws):
         dsa.dsa_prefill(dev["q"], dev["k"], dev["v"], dev["q_idx"], dev["k_idx"], dev["w"], dev["cu"], cu,
@@ -291,22 +236,32 @@ def prefill_section(args, dsa, inp, name, steps, warmup, full):
         samples = {"rows": cand.tolist(), "idx": idx[sel].cpu().numpy(), "out": out[sel].float().cpu().numpy(),
                    "lse": lse[sel].cpu().numpy()}
 
-    # Attribution: the same schedule through the separate entry points, HIP events per kernel.
-    step()
-    timer.collect()
-    timer.reset()
+    # Attribution: the same fused call with the library's launch timing on (two HIP events on the
+    # launch stream around each launch, summed per launch name); the timed region ran with it off.
+    dsa.dsa_timing_enable(True)
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        fused()
     torch.cuda.synchronize()
-    sep_ms = (time.perf_counter() - t0) * 1e3 / steps
-    timer.collect()
-    kern = {n: timer.total[n] / steps for n in timer.total}            # ms per step
-    launches = {n: timer.count[n] / steps for n in timer.count}
-    log(f"{name}: prefill {ms_per_step:.1f} ms/step (separate entry points {sep_ms:.1f}); kernels {kern}")
+    timing_on_ms = (time.perf_counter() - t0) * 1e3 / steps
+    rec = dsa.dsa_timing_read()
+    dsa.dsa_timing_enable(False)
+    kern = {n: ms / steps for n, (ms, c) in rec.items()}            # ms per step
+    launches = {n: c / steps for n, (ms, c) in rec.items()}
+    log(f"{name}: prefill {ms_per_step:.1f} ms/step (with launch timing {timing_on_ms:.1f}); kernels "
+        + ", ".join(f"{n} {v:.2f}" for n, v in kern.items()))
 
-    res = {"name": name, "pi": pi, "rows_total": total, "ms_per_step": ms_per_step, "sep_ms": sep_ms,
-           "kern": kern, "launches": launches, "samples": samples}
+    # The fused top-k's candidate counts of the last chunk: the chunk-only workspace leaves the
+    # top-k scratch intact (the merged sets of the dedup attention would reuse it).
+    fused(ws[:ws_chunk_bytes])
+    torch.cuda.synchronize()
+    last_rows = (lens[-1] - 1) % chunk + 1
+    cnt = ws[topk_off + 4 * chunk: topk_off + 8 * chunk].view(torch.int32)[:last_rows].cpu().numpy()
+    last_n = np.arange(lens[-1] - last_rows + 1, lens[-1] + 1)
+    cand_mean = float(cnt[last_n > k].mean()) if (last_n > k).any() else 0.0
+
+    res = {"name": name, "pi": pi, "rows_total": total, "ms_per_step": ms_per_step, "timing_on_ms": timing_on_ms,
+           "kern": kern, "launches": launches, "samples": samples, "candidates_per_row_mean": cand_mean}
     if full:
         # The same fused call with a workspace too small for the merged sets: attention per row.
         ws_chunk = ws[:ws_chunk_bytes]
@@ -357,13 +312,22 @@ def prefill_section(args, dsa, inp, name, steps, warmup, full):
     # sums on a ones operand, not counted).
     merged_flops = merged * hkv * 2 * (2 * ublk * (hq // hkv) * d)
     union_bytes = total * k * 4 + padded * 6
-    topk_bytes = pairs * 4 + total * k * 4   # one pass over each row's scores + index write
+    # The fused top-k (indexer_emit is the indexer itself; its candidate appends are counted here):
+    # per row with more than k positions, 2048 sample floats written and read and its candidates
+    # (key, position) written and read; every row's k indices written.
+    ikey = "indexer_emit" if "indexer_emit" in kern else "indexer"
+    topk_parts = [n for n in ("indexer_sample", "topk_threshold", "topk_select", "indexer_rescore", "topk_redo",
+                              "topk") if n in kern]
+    rows_long = sum(max(0, n - k) for n in lens)
+    topk_bytes = rows_long * (2048 * 4 * 2 + cand_mean * 8 * 2) + total * k * 4
+    topk_ms = sum(kern[n] for n in topk_parts)
     res.update(pairs=pairs, idx_flops=idx_flops, sel_pairs=sel_pairs, attn_bytes=attn_bytes, merged=merged,
                merged_bytes=merged_bytes, merged_flops=merged_flops, union_bytes=union_bytes, topk_bytes=topk_bytes,
-               idx_tflops=idx_flops / (kern["indexer"] * 1e-3) / 1e12,
-               attn_tflops=merged_flops / (kern["sparse_attn"] * 1e-3) / 1e12,
+               indexer_key=ikey, topk_parts=topk_parts, topk_ms=topk_ms,
+               idx_tflops=idx_flops / (kern[ikey] * 1e-3) / 1e12,
+               attn_tflops=merged_flops / (kern["sparse_attn_union"] * 1e-3) / 1e12,
                union_gbs=union_bytes / (kern["query_union"] * 1e-3) / 1e9,
-               topk_gbs=topk_bytes / (kern["topk"] * 1e-3) / 1e9,
+               topk_gbs=topk_bytes / (topk_ms * 1e-3) / 1e9,
                merged_fraction=merged / float(sel_pairs), block_rows=ublk,
                merged_rows_per_block_mean=float(counts.mean()))
     if full:
@@ -379,16 +343,19 @@ def prefill_section(args, dsa, inp, name, steps, warmup, full):
         res["union16_at_t"] = stats16
         res["union16_mean"] = float(c16.mean())
         del r16, m16
-    del dev, ws, scores, out, lse, idx, u_rows, u_masks
+    del dev, ws, out, lse, idx, u_rows, u_masks
     torch.cuda.empty_cache()
     return res
 
 
 def indexer_roofline(pre, counter_key=None):
-    r = {"bound": "mfma", "kernel": "indexer_prefill_kernel", "achieved": pre["idx_tflops"],
-         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
-         "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"]["indexer"],
-         "avg_launch_ms": pre["kern"]["indexer"] / pre["launches"]["indexer"]}
+    ik = pre["indexer_key"]
+    r = {"bound": "mfma", "kernel": "indexer_prefill_kernel<64, 128, 4, 2> (the fused top-k's emitting pass)"
+                                    if ik == "indexer_emit" else "indexer_prefill_kernel",
+         "achieved": pre["idx_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+         "frac": pre["idx_tflops"] / PEAK_BF16_TFLOPS,
+         "algorithmic_flops_per_launch": pre["idx_flops"] / pre["launches"][ik],
+         "avg_launch_ms": pre["kern"][ik] / pre["launches"][ik]}
     if counter_key:
         r["traffic"] = counter_traffic(counter_key)
         r["traffic_unit"] = "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)"
@@ -400,9 +367,10 @@ def prefill_summary(pre):
     kern = pre["kern"]
     return {"workload": pre["name"], "tokens": pre["rows_total"], "ms_per_step": pre["ms_per_step"],
             "tokens_per_s": pre["rows_total"] / (pre["ms_per_step"] * 1e-3),
-            "separate_entry_points_ms_per_step": pre["sep_ms"], "kernel_ms_per_step": kern,
+            "ms_per_step_with_launch_timing": pre["timing_on_ms"], "kernel_ms_per_step": kern,
             "roofline_indexer": indexer_roofline(pre),
-            "sparse_attn_effective_algorithmic_gbs": pre["merged_bytes"] / (kern["sparse_attn"] * 1e-3) / 1e9,
+            "sparse_attn_effective_algorithmic_gbs": pre["merged_bytes"] / (kern["sparse_attn_union"] * 1e-3) / 1e9,
+            "indexer_plus_topk_ms_per_step": kern[pre["indexer_key"]] + pre["topk_ms"],
             "merged_rows_per_8_row_block_mean": pre["merged_rows_per_block_mean"],
             "topk_gbs": pre["topk_gbs"]}
 
@@ -1006,8 +974,8 @@ def main():
     total = pre["rows_total"]
     value = total / (pre["ms_per_step"] * 1e-3)
     kern = pre["kern"]
-    attn_ms = kern["sparse_attn"] / pre["launches"]["sparse_attn"]
-    roof = indexer_roofline(pre, f"indexer_prefill_kernel@{pre['name']}")
+    attn_ms = kern["sparse_attn_union"] / pre["launches"]["sparse_attn_union"]
+    roof = indexer_roofline(pre, f"indexer_prefill_kernel<64, 128, 4, 2>@{pre['name']}")
     roof["measured_peak"] = peaks["mfma_bf16_16x16x32_tflops"]
     roof["frac_of_measured_peak"] = pre["idx_tflops"] / peaks["mfma_bf16_16x16x32_tflops"]
     line = {
@@ -1026,12 +994,12 @@ def main():
         "config": {"workload": "prefill_128k_blocks16: batch 1, L=131072 causal, k=2048, indexer 64x128 bf16, "
                                "GQA 32q/4kv heads x 128",
                    "global_batch": 1, "seq_len": total, "top_k": 2048},
-        "separate_entry_points_ms_per_step": pre["sep_ms"],
+        "ms_per_step_with_launch_timing": pre["timing_on_ms"],
         "kernel_ms_per_step": kern,
         "kernel_launches_per_step": pre["launches"],
         "roofline": roof,
         "roofline_sparse_attn": hbm_roofline(
-            "sparse_attn_union_kernel (8-row merged sets)", f"sparse_attn_union_kernel@{pre['name']}", attn_ms,
+            "sparse_attn_union_kernel (8-row merged sets)", f"sparse_attn_union_kernel<8, 2, 2>@{pre['name']}", attn_ms,
             pre["merged_bytes"], ceiling=pre.get("ceiling_merged"),
             mfma_tflops=pre["attn_tflops"], mfma_frac=pre["attn_tflops"] / PEAK_BF16_TFLOPS,
             bytes_without_dedup=pre["attn_bytes"],
@@ -1044,8 +1012,13 @@ def main():
                                  "frac": pre["union_gbs"] / PEAK_HBM_GBS,
                                  "algorithmic_bytes_per_launch": pre["union_bytes"]},
         "roofline_topk": {"bound": "hbm", "achieved": pre["topk_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": pre["topk_gbs"] / PEAK_HBM_GBS,
-                          "algorithmic_bytes_per_step": pre["topk_bytes"]},
+                          "frac": pre["topk_gbs"] / PEAK_HBM_GBS, "kernels": pre["topk_parts"],
+                          "ms_per_step": pre["topk_ms"], "algorithmic_bytes_per_step": pre["topk_bytes"],
+                          "candidates_per_row_mean": pre["candidates_per_row_mean"],
+                          "note": "fused top-k: no score is written or re-read; the bytes are the sample, the "
+                                  "candidate lists (written by the emitting indexer, read by the select) and the "
+                                  "index rows, so the kernels are latency-bound rather than HBM-bound"},
+        "indexer_plus_topk_ms_per_step": kern[pre["indexer_key"]] + pre["topk_ms"],
         "measured_peaks": peaks,
         "dedup": {"block_rows": pre["block_rows"], "merged_rows_per_block_mean": pre["merged_rows_per_block_mean"],
                   "index_slots_per_block": pre["block_rows"] * 2048, "merged_fraction": pre["merged_fraction"],

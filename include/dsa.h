@@ -40,7 +40,8 @@
  *   - Positions are sequence-local.  Selected positions that lie outside the causal prefix
  *     [0, t] (or outside [0, seq_len) in decode) are ignored by the attention calls.
  *   - With DSA_LOG=1 in the environment every entry point logs its call (name and sizes) and
- *     every rejected call its reason, one line each on stderr.
+ *     every rejected call its reason, and every kernel launch it makes its name ("launch ..."),
+ *     one line each on stderr.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -71,6 +72,30 @@ const char* dsa_status_string(int status);
 
 /* Message of the last failing call made by this host thread ("" if none). */
 const char* dsa_last_error(void);
+
+/*
+ * Launch timing, a diagnostic of the library's own kernel launches (for the benchmark's
+ * per-kernel attribution of the fused calls; off by default).
+ *
+ * dsa_timing_enable(on)   waits for the launches recorded so far, clears the record and turns
+ *                         timing on (on != 0) or off.  While on, each launch the library makes
+ *                         is bracketed by two HIP events recorded on the launch's stream, and
+ *                         its time is later added to the entry of its name ("indexer_emit",
+ *                         "topk_select", "sparse_attn_union", ...; one name may cover a short
+ *                         sequence of kernels, e.g. "topk").  The events cost a little time
+ *                         between launches, so time throughput with timing off.
+ * dsa_timing_count(n)     waits for every recorded launch (host-blocking), adds their times to
+ *                         the record and returns the number of names in *n.
+ * dsa_timing_entry(i, name, total_ms, launches)
+ *                         entry i < n of the record as of the last dsa_timing_count: the name (a
+ *                         static string owned by the library), the summed milliseconds and the
+ *                         number of launches.  i out of range: DSA_ERR_INVALID_ARG.
+ * Not thread-safe (one host thread drives timed calls); do not turn it on while a stream is
+ * being captured into a graph.  Errors of the event calls: DSA_ERR_HIP.
+ */
+int dsa_timing_enable(int on);
+int dsa_timing_count(int* n);
+int dsa_timing_entry(int i, const char** name, double* total_ms, int64_t* launches);
 
 /*
  * Lightning-indexer scores (digest section 一: light scout, MQA-shared key).

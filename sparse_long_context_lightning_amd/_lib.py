@@ -32,6 +32,7 @@ EXPORTED = (
     "dsa_sparse_gqa_attn_union", "dsa_sparse_gqa_attn_dedup_workspace_size", "dsa_sparse_gqa_attn_dedup",
     "dsa_decode_noalloc", "dsa_sparse_gqa_attn_decode_workspace_size", "dsa_sparse_gqa_attn_decode",
     "dsa_sparse_gqa_attn_bwd_dedup_workspace_size", "dsa_sparse_gqa_attn_bwd_dedup",
+    "dsa_timing_enable", "dsa_timing_count", "dsa_timing_entry",
 )
 # The measurement probes (include/dsa_probes.h), a separate library used by the benchmark.
 PROBES_EXPORTED = ("dsa_probe_last_error", "dsa_probe_mfma_bf16", "dsa_probe_stream_read", "dsa_probe_gather",
@@ -65,6 +66,10 @@ def load():
         "dsa_abi_version": ([], _I),
         "dsa_status_string": ([_I], ctypes.c_char_p),
         "dsa_last_error": ([], ctypes.c_char_p),
+        "dsa_timing_enable": ([_I], _I),
+        "dsa_timing_count": ([ctypes.POINTER(_I)], _I),
+        "dsa_timing_entry": ([_I, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                              ctypes.POINTER(_I64)], _I),
         "dsa_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
         "dsa_decode_index_scores": ([_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I64, _P], _I),
         "dsa_topk_workspace_size": ([_I, _I64, _I, ctypes.POINTER(_SZ)], _I),
@@ -172,6 +177,26 @@ def dsa_status_string(status: int) -> str:
 
 def dsa_last_error() -> str:
     return load().dsa_last_error().decode()
+
+
+def dsa_timing_enable(on: bool):
+    """Clear the launch-timing record and turn per-launch timing on or off."""
+    _check(load().dsa_timing_enable(1 if on else 0))
+
+
+def dsa_timing_read() -> dict:
+    """Wait for the timed launches and return {name: (total_ms, launches)}."""
+    lib = load()
+    n = _I(0)
+    _check(lib.dsa_timing_count(ctypes.byref(n)))
+    out = {}
+    for i in range(n.value):
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double()
+        cnt = _I64()
+        _check(lib.dsa_timing_entry(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)))
+        out[name.value.decode()] = (ms.value, int(cnt.value))
+    return out
 
 
 def dsa_index_scores(q_idx, k_idx, w, cu_seqlens_host, row_begin, row_count, scores, ld=None, stream=None):

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "kernels.h"
@@ -43,6 +44,84 @@ int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return DSA_OK;
   return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
+
+// Launch timing (dsa_timing_enable): while on, every launch of the library is bracketed by two
+// HIP events on its stream, and the pairs are summed per launch name when the record is read.
+// A diagnostic: one host thread, no graph capture while it is on.
+struct TimedLaunch {
+  int slot;
+  hipEvent_t a, b;
+};
+struct TimingRecord {
+  bool on = false;
+  std::vector<const char*> names;  // static strings
+  std::vector<double> ms;
+  std::vector<long long> launches;
+  std::vector<TimedLaunch> pending;
+  std::vector<hipEvent_t> pool;  // events whose pair has been read, for reuse
+};
+TimingRecord g_timing;
+
+int timing_slot(const char* name) {
+  for (size_t i = 0; i < g_timing.names.size(); ++i)
+    if (strcmp(g_timing.names[i], name) == 0) return (int)i;
+  g_timing.names.push_back(name);
+  g_timing.ms.push_back(0.0);
+  g_timing.launches.push_back(0);
+  return (int)g_timing.names.size() - 1;
+}
+
+hipEvent_t timing_event() {
+  if (!g_timing.pool.empty()) {
+    hipEvent_t e = g_timing.pool.back();
+    g_timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
+
+// Waits for the recorded launches and adds their times to the record.
+hipError_t timing_resolve() {
+  hipError_t err = hipSuccess;
+  for (const TimedLaunch& t : g_timing.pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.a, t.b);
+    if (e == hipSuccess) {
+      g_timing.ms[t.slot] += ms;
+      g_timing.launches[t.slot] += 1;
+    } else if (err == hipSuccess) {
+      err = e;
+    }
+    g_timing.pool.push_back(t.a);
+    g_timing.pool.push_back(t.b);
+  }
+  g_timing.pending.clear();
+  return err;
+}
+
+// One library launch: logged with DSA_LOG, timed while launch timing is on.
+class LaunchScope {
+ public:
+  LaunchScope(const char* name, hipStream_t s) : name_(name), s_(s) {
+    if (log_enabled()) fprintf(stderr, "[dsa]   launch %s\n", name);
+    if (!g_timing.on) return;
+    a_ = timing_event();
+    b_ = timing_event();
+    if (a_ && b_ && hipEventRecord(a_, s) != hipSuccess) a_ = nullptr;
+  }
+  ~LaunchScope() {
+    if (a_ && b_ && hipEventRecord(b_, s_) == hipSuccess) g_timing.pending.push_back({timing_slot(name_), a_, b_});
+  }
+  LaunchScope(const LaunchScope&) = delete;
+  LaunchScope& operator=(const LaunchScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -102,6 +181,28 @@ int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) 
   do {                             \
     const int st_ = (expr);        \
     if (st_ != DSA_OK) return st_; \
+  } while (0)
+
+// A library launch (expr returns hipError_t) under a LaunchScope named `name`.
+#define DSA_LAUNCH(name, stream, expr)     \
+  do {                                     \
+    hipError_t e_;                         \
+    {                                      \
+      LaunchScope ls_(name, stream);       \
+      e_ = (expr);                         \
+    }                                      \
+    DSA_TRY(hip_status(e_, name " launch")); \
+  } while (0)
+
+// The same for a launch whose status is the caller's return value.
+#define DSA_LAUNCH_RETURN(name, stream, expr) \
+  do {                                        \
+    hipError_t e_;                            \
+    {                                         \
+      LaunchScope ls_(name, stream);          \
+      e_ = (expr);                            \
+    }                                         \
+    return hip_status(e_, name " launch");    \
   } while (0)
 
 #define DSA_NONNULL(p) \
@@ -185,7 +286,11 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   q.masks = masks;
   q.use_union = flags;
   q.ratio = kUnionRatio;
-  hipError_t e = dsa::launch_query_union(q, s);
+  hipError_t e;
+  {
+    LaunchScope ls("query_union", s);
+    e = dsa::launch_query_union(q, s);
+  }
   if (e != hipSuccess) return e;
   dsa::UnionAttnArgs m = {};
   m.q = a.q;
@@ -203,10 +308,14 @@ hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   m.out = a.out;
   m.lse = a.lse;
   m.use_union = flags;
-  e = dsa::launch_sparse_attn_union(m, s);
+  {
+    LaunchScope ls("sparse_attn_union", s);
+    e = dsa::launch_sparse_attn_union(m, s);
+  }
   if (e != hipSuccess) return e;
   a.skip_block = flags;
   a.skip_block_rows = kUnionBlockRows;
+  LaunchScope ls("sparse_attn", s);
   return dsa::launch_sparse_attn(a, s);
 }
 
@@ -303,8 +412,13 @@ hipError_t launch_decode_attn(const void* q, const void* k_cache, const void* v_
   a.nsplit = nsplit;
   a.part_o = static_cast<float*>(part);
   a.part_ml = a.part_o + (size_t)batch * hq * nsplit * 128;
-  hipError_t e = dsa::launch_sparse_attn(a, s);
+  hipError_t e;
+  {
+    LaunchScope ls("sparse_attn_decode", s);
+    e = dsa::launch_sparse_attn(a, s);
+  }
   if (e != hipSuccess || nsplit == 1) return e;
+  LaunchScope ls("attn_combine", s);
   return dsa::launch_attn_combine(a, s);
 }
 
@@ -332,13 +446,13 @@ int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, cons
     a.ld = ld;
     a.key_split = kKeySplit;
     if (mode == 1)
-      DSA_TRY(hip_status(dsa::launch_indexer_prefill_sample(a, *ts, k, stream), "sampling indexer launch"));
+      DSA_LAUNCH("indexer_sample", stream, dsa::launch_indexer_prefill_sample(a, *ts, k, stream));
     else if (mode == 2)
-      DSA_TRY(hip_status(dsa::launch_indexer_prefill_emit(a, *ts, k, stream), "emitting indexer launch"));
+      DSA_LAUNCH("indexer_emit", stream, dsa::launch_indexer_prefill_emit(a, *ts, k, stream));
     else if (mode == 3)
-      DSA_TRY(hip_status(dsa::launch_indexer_prefill_rescore(a, *ts, stream), "rescoring indexer launch"));
+      DSA_LAUNCH("indexer_rescore", stream, dsa::launch_indexer_prefill_rescore(a, *ts, stream));
     else
-      DSA_TRY(hip_status(dsa::launch_indexer_prefill(a, stream), "indexer launch"));
+      DSA_LAUNCH("indexer", stream, dsa::launch_indexer_prefill(a, stream));
   }
   return DSA_OK;
 }
@@ -368,6 +482,38 @@ void api_log(const char* name, const char* fmt, ...) {
 extern "C" {
 
 int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+int dsa_timing_enable(int on) {
+  g_last_error[0] = 0;
+  const hipError_t e = timing_resolve();  // finish the launches recorded so far before clearing
+  for (size_t i = 0; i < g_timing.ms.size(); ++i) {
+    g_timing.ms[i] = 0.0;
+    g_timing.launches[i] = 0;
+  }
+  g_timing.on = on != 0;
+  return hip_status(e, "launch timing");
+}
+
+int dsa_timing_count(int* n) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(n);
+  const hipError_t e = timing_resolve();
+  *n = (int)g_timing.names.size();
+  return hip_status(e, "launch timing");
+}
+
+int dsa_timing_entry(int i, const char** name, double* total_ms, int64_t* launches) {
+  g_last_error[0] = 0;
+  DSA_NONNULL(name);
+  DSA_NONNULL(total_ms);
+  DSA_NONNULL(launches);
+  if (i < 0 || i >= (int)g_timing.names.size())
+    return fail(DSA_ERR_INVALID_ARG, "timing entry %d outside [0, %d)", i, (int)g_timing.names.size());
+  *name = g_timing.names[i];
+  *total_ms = g_timing.ms[i];
+  *launches = g_timing.launches[i];
+  return DSA_OK;
+}
 
 const char* dsa_status_string(int status) {
   switch (status) {
@@ -446,7 +592,8 @@ int dsa_decode_index_scores(const void* q_idx, const float* w, const void* k_idx
   ia.d_idx = d_idx;
   ia.scores = scores;
   ia.ld = ld;
-  return hip_status(dsa::launch_indexer_decode(ia, static_cast<hipStream_t>(stream)), "decode indexer launch");
+  DSA_LAUNCH_RETURN("indexer_decode", static_cast<hipStream_t>(stream),
+                    dsa::launch_indexer_decode(ia, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, const int32_t* cu_seqlens_host,
@@ -499,7 +646,7 @@ int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, c
     a.dq = dq_idx;
     a.dw = dw;
     a.dk = dk_idx;
-    DSA_TRY(hip_status(dsa::launch_indexer_bwd(a, s), "indexer backward launch"));
+    DSA_LAUNCH("indexer_bwd", s, dsa::launch_indexer_bwd(a, s));
   }
   return DSA_OK;
 }
@@ -548,7 +695,7 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
     a.lse = lse;
     a.probs = probs;
     a.ld = ld;
-    DSA_TRY(hip_status(dsa::launch_attn_head_mean(a, s), "head-mean target launch"));
+    DSA_LAUNCH("attn_head_mean", s, dsa::launch_attn_head_mean(a, s));
   }
   return DSA_OK;
 }
@@ -564,9 +711,9 @@ int dsa_indexer_kl(const float* scores, const float* target, int64_t ld, int row
   DSA_NONNULL(grad);
   if (rows < 0 || ld <= 0) return fail(DSA_ERR_INVALID_ARG, "rows must be non-negative and ld positive");
   if (rows == 0) return DSA_OK;
-  return hip_status(dsa::launch_indexer_kl(scores, target, ld, rows, row_len, 0, row_loss, grad,
-                                           static_cast<hipStream_t>(stream)),
-                    "indexer KL launch");
+  DSA_LAUNCH_RETURN("indexer_kl", static_cast<hipStream_t>(stream),
+                    dsa::launch_indexer_kl(scores, target, ld, rows, row_len, 0, row_loss, grad,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int dsa_topk_workspace_size(int rows, int64_t ld, int k, size_t* bytes) {
@@ -607,10 +754,10 @@ int topk_entry(const float* scores, int64_t ld, int rows, const int32_t* row_len
   a.values_out = ranked ? nullptr : values_out;
   a.workspace = need ? workspace : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  DSA_TRY(hip_status(dsa::launch_topk(a, s), "top-k launch"));
+  DSA_LAUNCH("topk", s, dsa::launch_topk(a, s));
   if (!ranked) return DSA_OK;
   a.values_out = values_out;
-  return hip_status(dsa::launch_topk_rank(a, s), "top-k rank-order launch");
+  DSA_LAUNCH_RETURN("topk_rank", s, dsa::launch_topk_rank(a, s));
 }
 
 }  // namespace
@@ -660,7 +807,8 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.nsplit = 1;
-  return hip_status(dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
+  DSA_LAUNCH_RETURN("sparse_attn", static_cast<hipStream_t>(stream),
+                    dsa::launch_sparse_attn(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_query_union_size(int total_tokens, int k_sel, int block_rows, int* n_blocks, int* cap) {
@@ -705,7 +853,8 @@ int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, in
   a.counts = counts;
   a.kv_rows = kv_rows;
   a.masks = masks;
-  return hip_status(dsa::launch_query_union(a, static_cast<hipStream_t>(stream)), "query union launch");
+  DSA_LAUNCH_RETURN("query_union", static_cast<hipStream_t>(stream),
+                    dsa::launch_query_union(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const int32_t* counts,
@@ -751,7 +900,8 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
   a.softmax_scale = softmax_scale;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  return hip_status(dsa::launch_sparse_attn_union(a, static_cast<hipStream_t>(stream)), "merged-set attention launch");
+  DSA_LAUNCH_RETURN("sparse_attn_union", static_cast<hipStream_t>(stream),
+                    dsa::launch_sparse_attn_union(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_sparse_gqa_attn_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv, size_t* bytes) {
@@ -805,7 +955,7 @@ int dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v, const
   a.lse = lse;
   a.nsplit = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (need == 0) return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
+  if (need == 0) DSA_LAUNCH_RETURN("sparse_attn", s, dsa::launch_sparse_attn(a, s));
   return hip_status(launch_attn_dedup(a, workspace, s), "dedup attention launch");
 }
 
@@ -856,7 +1006,8 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  return hip_status(dsa::launch_sparse_attn_bwd(a, static_cast<hipStream_t>(stream)), "sparse attention backward launch");
+  DSA_LAUNCH_RETURN("sparse_attn_bwd", static_cast<hipStream_t>(stream),
+                    dsa::launch_sparse_attn_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_sparse_gqa_attn_bwd_dedup_workspace_size(int total_tokens, int k_sel, int hq, int hkv, size_t* bytes) {
@@ -923,7 +1074,7 @@ int dsa_sparse_gqa_attn_bwd_dedup(const void* q, const void* k, const void* v, c
   a.dk = dk;
   a.dv = dv;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (need == 0) return hip_status(dsa::launch_sparse_attn_bwd(a, s), "sparse attention backward launch");
+  if (need == 0) DSA_LAUNCH_RETURN("sparse_attn_bwd", s, dsa::launch_sparse_attn_bwd(a, s));
   return hip_status(launch_attn_bwd_dedup(a, workspace, s), "dedup attention backward launch");
 }
 
@@ -1015,16 +1166,16 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
         const dsa::TopkScratch ts = dsa::topk_wave_scratch(topk_ws, c1 - c0);
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 1,
                                   &ts, top_k));
-        DSA_TRY(hip_status(dsa::launch_topk_wave_threshold_from_samples(t, s), "top-k threshold launch"));
+        DSA_LAUNCH("topk_threshold", s, dsa::launch_topk_wave_threshold_from_samples(t, s));
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 2,
                                   &ts, top_k));
-        DSA_TRY(hip_status(dsa::launch_topk_wave_select(t, s), "top-k select launch"));
+        DSA_LAUNCH("topk_select", s, dsa::launch_topk_wave_select(t, s));
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s, 3,
                                   &ts, top_k));
-        DSA_TRY(hip_status(dsa::launch_topk_wave_redo(t, s), "top-k redo launch"));
+        DSA_LAUNCH("topk_redo", s, dsa::launch_topk_wave_redo(t, s));
       } else {
         DSA_TRY(launch_index_rows(q_idx, k_idx, w, cu_seqlens_host, batch, h_idx, d_idx, c0, c1, c0, scores, ld, s));
-        DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+        DSA_LAUNCH("topk", s, dsa::launch_topk(t, s));
       }
     }
   }
@@ -1048,7 +1199,7 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
   // runs with adjacent-query dedup; otherwise per row.
   if (dsa::union_attn_supported(hq, hkv, total_tokens) && workspace_bytes >= union_layout(total_tokens, top_k).bytes)
     return hip_status(launch_attn_dedup(a, workspace, s), "dedup attention launch");
-  return hip_status(dsa::launch_sparse_attn(a, s), "sparse attention launch");
+  DSA_LAUNCH_RETURN("sparse_attn", s, dsa::launch_sparse_attn(a, s));
 }
 
 int dsa_decode_workspace_size(int batch, int s_max, int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k,
@@ -1118,7 +1269,7 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   ia.d_idx = d_idx;
   ia.scores = scores;
   ia.ld = ld;
-  DSA_TRY(hip_status(dsa::launch_indexer_decode(ia, s), "decode indexer launch"));
+  DSA_LAUNCH("indexer_decode", s, dsa::launch_indexer_decode(ia, s));
 
   dsa::TopkArgs t;
   t.scores = scores;
@@ -1130,7 +1281,7 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
   t.idx_out = idx_out;
   t.values_out = nullptr;
   t.workspace = topk_ws;
-  DSA_TRY(hip_status(dsa::launch_topk(t, s), "top-k launch"));
+  DSA_LAUNCH("topk", s, dsa::launch_topk(t, s));
 
   return hip_status(launch_decode_attn(q, k_cache, v_cache, idx_out, top_k, seq_lens, batch, s_max, hq, hkv,
                                        softmax_scale, out, lse, part, s),

@@ -60,14 +60,16 @@ __device__ __forceinline__ float transpose_reduce4(float p0, float p1, float p2,
 // the fused top-k's rescoring pass).  The prefill's fused top-k adds two modes (64 heads only,
 // one token per wave):
 //   MODE 1 (sample): the workgroup's keys are 2048 stratified positions of the causal prefix of
-//     its first row (one jittered run of 4 in each of 512 strata, or the whole prefix when it is
-//     no longer), gathered tile by tile by kSampleSplits workgroups; each row with more than k
-//     positions gets their scores as floats at the start of its candidate list and their number
-//     in tau_lo;
+//     its first row (one jittered run of 4 in each of 512 strata; 4096 in 1024 strata past
+//     131072 positions, where 2048 would leave too few samples above the k-th score to keep the
+//     candidate count inside the list; or the whole prefix when it is no longer), gathered tile
+//     by tile by kSampleSplits workgroups; each row with more than k positions gets their scores
+//     as floats at the start of its candidate list and their number in tau_lo;
 //   MODE 2 (emit): every (key, position) whose key reaches the row's tau_lo is staged in LDS and
 //     appended to the row's candidate list with one atomic per stage; no score is written, so
 //     neither this pass nor the top-k moves the score rows through memory.
 constexpr int kSampleCount = 2048;  // sample positions per row (512 strata of 4)
+constexpr int kSampleLongRow = 131072;  // longer prefixes take 2 kSampleCount positions
 constexpr int kSampleSplits = 4;    // workgroups per row block in the sampling pass (512 entries each)
 constexpr int kEmitStage = 512;     // staged candidates per wave
 
@@ -108,16 +110,17 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     if (!any) return;
   }
   const int t_last = min(r0 + TOKWG, row_end) - 1 - seq_off;
-  // MODE 1: the sample of the first row's prefix (n0 positions), m <= kSampleCount entries
+  // MODE 1: the sample of the first row's prefix (n0 positions), m <= msz entries
   const int n0 = r0 - seq_off + 1;
-  const bool whole = n0 <= kSampleCount;
-  const uint32_t sf = whole ? 1u : (uint32_t)(n0 >> 2) / (kSampleCount / 4);  // float4 slots per stratum
-  const int m = whole ? n0 : kSampleCount;
+  const int msz = n0 > kSampleLongRow ? 2 * kSampleCount : kSampleCount;
+  const bool whole = n0 <= msz;
+  const uint32_t sf = whole ? 1u : (uint32_t)(n0 >> 2) / (uint32_t)(msz / 4);  // float4 slots per stratum
+  const int m = whole ? n0 : msz;
   if (MODE == 1 && t_last + 1 <= topk) return;  // no row needs a threshold
-  // MODE 1: split s takes sample entries [s * kSampleCount / kSampleSplits, ...) of the m
-  const int kbeg = MODE == 1 ? split * (kSampleCount / kSampleSplits) : split * key_split;
+  // MODE 1: split s takes sample entries [s * msz / kSampleSplits, ...) of the m
+  const int kbeg = MODE == 1 ? split * (msz / kSampleSplits) : split * key_split;
   if (MODE == 1 ? kbeg >= m : kbeg > t_last) return;
-  const int kend = MODE == 1 ? min(m, kbeg + kSampleCount / kSampleSplits) : min(kbeg + key_split, t_last + 1);
+  const int kend = MODE == 1 ? min(m, kbeg + msz / kSampleSplits) : min(kbeg + key_split, t_last + 1);
   const int ntiles = (kend - kbeg + 63) >> 6;
 
   // the wave index is uniform over the wave: kept in a scalar register, as is all that derives from it

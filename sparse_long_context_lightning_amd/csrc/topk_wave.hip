@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256) void topk_threshold_kernel(const float* __rest
 }
 
 // The same threshold from a sample the prefill's sampling indexer pass computed directly: m
-// scores (m = tau_lo[row] on entry, at most 4 kStrata) as floats at the start of the row's
-// candidate list; the rank rule and the radix rounds are those above.
+// scores (m = tau_lo[row] on entry, at most 8 kStrata: twice the sample for rows past 131072
+// positions) as floats at the start of the row's candidate list; the rank rule and the radix
+// rounds are those above.
 __global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long ld, int rows,
                                                                      const int* __restrict__ row_len, int len_base,
                                                                      int k, uint32_t* __restrict__ tau_lo,
@@ -211,10 +212,10 @@ __global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long l
   }
   if (n <= k) return;
   const float* smp = reinterpret_cast<const float*>(cand + (size_t)row * kCapW);
-  uint32_t key[32];
+  uint32_t key[64];
   unsigned long long valid = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 16; ++j) {
     const int p = 4 * (lane + 64 * j);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p < m) v = *reinterpret_cast<const float4*>(smp + p);
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256) void topk_threshold_sampled_kernel(long long l
   }
   auto each = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
+    for (int j = 0; j < 64; ++j)
       if ((valid >> j) & 1ull) f(key[j], 0u);
   };
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;

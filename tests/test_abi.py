@@ -26,7 +26,7 @@ def _declared(header=HEADER):
 def test_library_exports_every_declared_symbol():
     lib = dsa.load()
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dsa.EXPORTED)
@@ -41,6 +41,20 @@ def test_probe_library_exports_every_declared_symbol():
     assert set(names) == set(dsa.PROBES_EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_launch_timing_record_without_launches():
+    # Turning the timing on or off and reading an empty record make no HIP call.
+    lib = dsa.load()
+    dsa.dsa_timing_enable(True)
+    dsa.dsa_timing_enable(False)
+    assert dsa.dsa_timing_read() == {}
+    n = ctypes.c_int(-1)
+    assert lib.dsa_timing_count(None) == dsa.DSA_ERR_INVALID_ARG
+    assert lib.dsa_timing_count(ctypes.byref(n)) == dsa.DSA_OK and n.value == 0
+    name, ms, cnt = ctypes.c_char_p(), ctypes.c_double(), ctypes.c_int64()
+    assert lib.dsa_timing_entry(0, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)) == dsa.DSA_ERR_INVALID_ARG
+    assert "outside" in dsa.dsa_last_error()
 
 
 def test_version_and_status_strings():
