@@ -501,7 +501,7 @@ def decode_rooflines(dec):
         "roofline_decode_step": {"bound": "hbm", "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": dec["gbs"] / PEAK_HBM_GBS, "algorithmic_bytes_per_step": dec["bytes_step"]},
         "roofline_decode_indexer": hbm_roofline("indexer_decode_coop_kernel",
-                                                f"indexer_decode_coop_kernel@{dec['name']}", us["indexer"] * 1e-3,
+                                                f"indexer_decode_coop_kernel<64, 128, 2>@{dec['name']}", us["indexer"] * 1e-3,
                                                 dec["idx_bytes"] + dec["score_bytes"]),
         "roofline_decode_attn": hbm_roofline("decode sparse attention (split partials + combine)",
                                              f"sparse_attn_kernel@{dec['name']}", us["attention"] * 1e-3,
