@@ -211,7 +211,18 @@ int check_cu_host(const int32_t* cu, int batch, int total_tokens, int* max_len) 
 #define DSA_ALIGNED(p) \
   if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p)
 
-constexpr int kKeySplit = 4096;        // keys per prefill-indexer workgroup
+constexpr int kKeySplit = 4096;        // keys per prefill-indexer workgroup (at most)
+
+// Keys per prefill-indexer workgroup for rows whose longest prefix is t_max + 1: up to
+// kKeySplit, but short prefixes are cut into about 16 splits of at least 1024 keys (multiples
+// of the 64-key tile), so a launch over short rows still has many workgroups of similar length
+// instead of a few rounds of long ones.  Every score is computed by exactly one workgroup, so the
+// split never changes a result.
+int key_split_for(int t_max) {
+  const int want = (t_max + 1 + 15) / 16;
+  const int ks = (want + 63) / 64 * 64;
+  return std::min(kKeySplit, std::max(1024, ks));
+}
 constexpr int kMinChunkRows = 64;
 constexpr int kDefaultChunkRows = 2048;
 
@@ -444,7 +455,7 @@ int launch_index_rows(const void* q_idx, const void* k_idx, const float* w, cons
     a.out_row0 = out_row0;
     a.scores = scores;
     a.ld = ld;
-    a.key_split = kKeySplit;
+    a.key_split = key_split_for(r1 - 1 - cu[b]);
     if (mode == 1)
       DSA_LAUNCH("indexer_sample", stream, dsa::launch_indexer_prefill_sample(a, *ts, k, stream));
     else if (mode == 2)

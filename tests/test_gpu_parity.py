@@ -63,9 +63,10 @@ def test_index_scores_row_window(dsa):
 
 @pytest.mark.parametrize("h_idx,d_idx", [(64, 128), (4, 64), (32, 128), (16, 128)])
 def test_index_scores_bit_exact_across_key_splits(dsa, h_idx, d_idx):
-    """Rows whose prefixes span several 4096-key workgroup splits, with a partial last split: windows
-    around the split boundaries and the last rows of a 9500-token sequence packed after a 700-token
-    one (window starts not aligned to the 4-token workgroups)."""
+    """Rows whose prefixes span several workgroup key splits (1024 keys at these lengths; every
+    multiple of 4096 is a boundary at any split size), with a partial last split: windows around
+    the boundaries at 4096 and 8192 and the last rows of a 9500-token sequence packed after a
+    700-token one (window starts not aligned to the 4-token workgroups)."""
     torch = _torch()
     lens = [700, 9500]
     pi = inp.prefill_inputs(lens, h_idx, d_idx, 8, 2, 128, 16, seed=901 + h_idx)
