@@ -213,6 +213,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   const int er = wave_r0 - out_row0;  // the token's row in the top-k scratch
   const bool e_ok = MODE == 2 && wave_r0 < row_end && wave_r0 - seq_off + 1 > topk;
   const uint32_t tau = e_ok ? tau_lo[er] : 0xFFFFFFFFu;
+  // The same test on the float itself: the key order is the float order (non-NaN scores, -0 = +0)
+  // and key_float inverts float_key, so float_key(v) >= tau exactly when v >= tau_f (the one key
+  // with no float, 0x7FFFFFFF, gives -0.0, which is still the right bound; no threshold: NaN).
+  const float tau_f = key_float(tau);
   auto flush = [&]() {
     uint32_t base = 0;
     if (lane == 0) base = atomicAdd(&cnt[er], ns);
@@ -306,12 +310,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
           }
           if (MODE == 0 && r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
           if (MODE == 2) {
-            const uint32_t kk = float_key(v);
-            const bool take = e_ok && key <= r - seq_off && kk >= tau;
+            const bool take = e_ok && key <= r - seq_off && v >= tau_f;
             const unsigned long long b = __ballot(take);
             if (b != 0ull) {
               if (take) stage[ns + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u))] =
-                  make_uint2(kk, (uint32_t)key);
+                  make_uint2(float_key(v), (uint32_t)key);
               ns += (uint32_t)__popcll(b);
               if (ns > (uint32_t)(kEmitStage - 64)) flush();
             }
