@@ -680,7 +680,10 @@ static hipError_t launch_fused_select(const TopkArgs& a, int redo, hipStream_t s
   // the candidate lists hold keys and positions only: no values without the scores
   if (a.rows <= 512 || a.values_out) return hipErrorInvalidValue;
   const TopkScratch t = topk_wave_scratch(a.workspace, a.rows);
-  if (a.ld <= 131072)
+  // The position bitmap covers the launch's longest row (causal rows: len_base + rows), not ld: a
+  // chunk of short rows in a long packed batch keeps the smaller bitmap and more rows per CU.
+  const long long max_len = a.row_len ? a.ld : std::min<long long>(a.ld, (long long)a.len_base + a.rows);
+  if (max_len <= 131072)
     hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
                        a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
                        redo);
