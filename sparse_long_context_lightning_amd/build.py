@@ -39,6 +39,8 @@ COMPILE_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 LINK_FLAGS = ["--offload-arch=gfx950", "-shared", "-fPIC"]
+# libdsa.so marks each library call as a roctx range (ROCm's marker library).
+ROCTX_LIBS = ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx"]
 
 _NOISE = "is not a recognized feature for this target"
 
@@ -59,14 +61,14 @@ def _run(cmd, verbose):
         sys.stderr.write(err + "\n")
 
 
-def _build_lib(srcs, dest, tmp_dir, verbose, extra_flags, jobs):
+def _build_lib(srcs, dest, tmp_dir, verbose, extra_flags, jobs, libs=()):
     objs = [os.path.join(tmp_dir, os.path.basename(s) + ".o") for s in srcs]
     cmds = [[HIPCC, *COMPILE_FLAGS, *(extra_flags or []), "-c", "-o", o, s] for s, o in zip(srcs, objs)]
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     out = os.path.join(tmp_dir, os.path.basename(dest))
-    _run([HIPCC, *LINK_FLAGS, "-o", out, *objs], verbose)
+    _run([HIPCC, *LINK_FLAGS, "-o", out, *objs, *libs], verbose)
     # Replace atomically so a process that has the old library mapped keeps working.
     tmp_final = dest + ".tmp"
     shutil.copyfile(out, tmp_final)
@@ -80,7 +82,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     jobs = max(1, min(8, os.cpu_count() or 1))
     tmp_dir = tempfile.mkdtemp(prefix="dsa_build_")
     try:
-        _build_lib(sources(CSRC), LIB, tmp_dir, verbose, extra_flags, jobs)
+        _build_lib(sources(CSRC), LIB, tmp_dir, verbose, extra_flags, jobs, ROCTX_LIBS)
         _build_lib(sources(PROBES), PROBES_LIB, tmp_dir, verbose, extra_flags, jobs)
         return LIB
     finally:

@@ -46,6 +46,7 @@ extern "C" int dsa_decode_noalloc(const void* q, const void* q_idx, const float*
                                   int top_k, float softmax_scale, void* out, float* lse, int32_t* idx_out,
                                   void* stream) {
   dsa::api_clear_error();
+  const dsa::ApiRange range_("dsa_decode_noalloc");
   dsa::api_log("dsa_decode_noalloc", "batch=%d s_max=%d max_seq_len=%d hq=%d hkv=%d h_idx=%d d_idx=%d top_k=%d",
                batch, s_max, max_seq_len, hq, hkv, h_idx, d_idx, top_k);
   size_t need = 0;

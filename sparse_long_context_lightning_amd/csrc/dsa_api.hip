@@ -8,6 +8,8 @@
 #include <algorithm>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/dsa.h"
 #include "kernels.h"
 
@@ -479,6 +481,8 @@ int api_fail(int status, const char* fmt, ...) {
   return st;
 }
 void api_clear_error() { g_last_error[0] = 0; }
+ApiRange::ApiRange(const char* name) { roctxRangePushA(name); }
+ApiRange::~ApiRange() { roctxRangePop(); }
 void api_log(const char* name, const char* fmt, ...) {
   if (!log_enabled()) return;
   char buf[400];
@@ -543,6 +547,7 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, const float* w, const
                      int total_tokens, int h_idx, int d_idx, int row_begin, int row_count, float* scores, int64_t ld,
                      void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_index_scores");
   dsa::api_log("dsa_index_scores", "batch=%d total=%d h_idx=%d d_idx=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, h_idx, d_idx, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q_idx);
   DSA_NONNULL(k_idx);
@@ -574,6 +579,7 @@ int dsa_decode_index_scores(const void* q_idx, const float* w, const void* k_idx
                             int batch, int s_max, int max_seq_len, int h_idx, int d_idx, float* scores, int64_t ld,
                             void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_decode_index_scores");
   dsa::api_log("dsa_decode_index_scores", "batch=%d s_max=%d max_seq_len=%d h_idx=%d d_idx=%d ld=%lld", batch, s_max,
            max_seq_len, h_idx, d_idx, (long long)ld);
   DSA_NONNULL(q_idx);
@@ -611,6 +617,7 @@ int dsa_index_scores_bwd(const void* q_idx, const void* k_idx, const float* w, c
                          int batch, int total_tokens, int h_idx, int d_idx, int row_begin, int row_count,
                          const float* dscores, int64_t ld, float* dq_idx, float* dw, float* dk_idx, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_index_scores_bwd");
   dsa::api_log("dsa_index_scores_bwd", "batch=%d total=%d h_idx=%d d_idx=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, h_idx, d_idx, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q_idx);
   DSA_NONNULL(k_idx);
@@ -666,6 +673,7 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
                        int hq, int hkv, int head_dim, float softmax_scale, int row_begin, int row_count, float* probs,
                        int64_t ld, float* lse, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_attn_head_mean");
   dsa::api_log("dsa_attn_head_mean", "batch=%d total=%d hq=%d hkv=%d rows=[%d,+%d) ld=%lld", batch, total_tokens, hq, hkv, row_begin, row_count, (long long)ld);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -714,6 +722,7 @@ int dsa_attn_head_mean(const void* q, const void* k, const int32_t* cu_seqlens_h
 int dsa_indexer_kl(const float* scores, const float* target, int64_t ld, int rows, const int32_t* row_len,
                    float* row_loss, float* grad, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_indexer_kl");
   dsa::api_log("dsa_indexer_kl", "rows=%d ld=%lld", rows, (long long)ld);
   DSA_NONNULL(scores);
   DSA_NONNULL(target);
@@ -741,6 +750,7 @@ namespace {
 int topk_entry(const float* scores, int64_t ld, int rows, const int32_t* row_len, int k, int32_t* idx_out,
                float* values_out, void* workspace, size_t workspace_bytes, void* stream, bool ranked) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_(ranked ? "dsa_topk_sorted" : "dsa_topk");
   dsa::api_log(ranked ? "dsa_topk_sorted" : "dsa_topk", "rows=%d ld=%lld k=%d ws=%zu", rows, (long long)ld, k, workspace_bytes);
   DSA_NONNULL(scores);
   DSA_NONNULL(row_len);
@@ -787,6 +797,7 @@ int dsa_sparse_gqa_attn(const void* q, const void* k, const void* v, const int32
                         const int32_t* cu_seqlens, int batch, int total_tokens, int hq, int hkv, int head_dim,
                         float softmax_scale, void* out, float* lse, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn");
   dsa::api_log("dsa_sparse_gqa_attn", "batch=%d total=%d hq=%d hkv=%d d=%d k_sel=%d", batch, total_tokens, hq, hkv, head_dim, k_sel);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -837,6 +848,7 @@ int dsa_query_union_size(int total_tokens, int k_sel, int block_rows, int* n_blo
 int dsa_query_union(const int32_t* idx, int k_sel, const int32_t* cu_seqlens, int batch, int total_tokens,
                     int block_rows, int cap, int32_t* counts, int32_t* kv_rows, uint16_t* masks, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_query_union");
   dsa::api_log("dsa_query_union", "batch=%d total=%d k_sel=%d block_rows=%d cap=%d", batch, total_tokens, k_sel, block_rows, cap);
   DSA_NONNULL(idx);
   DSA_NONNULL(cu_seqlens);
@@ -873,6 +885,7 @@ int dsa_sparse_gqa_attn_union(const void* q, const void* k, const void* v, const
                               int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, void* out,
                               float* lse, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn_union");
   dsa::api_log("dsa_sparse_gqa_attn_union", "total=%d hq=%d hkv=%d block_rows=%d cap=%d", total_tokens, hq, hkv, block_rows, cap);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -929,6 +942,7 @@ int dsa_sparse_gqa_attn_dedup(const void* q, const void* k, const void* v, const
                               float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn_dedup");
   dsa::api_log("dsa_sparse_gqa_attn_dedup", "batch=%d total=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, total_tokens, hq, hkv, k_sel, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -975,6 +989,7 @@ int dsa_sparse_gqa_attn_bwd(const void* q, const void* k, const void* v, const v
                             int total_tokens, int hq, int hkv, int head_dim, float softmax_scale, float* dq,
                             float* dk, float* dv, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn_bwd");
   dsa::api_log("dsa_sparse_gqa_attn_bwd", "batch=%d total=%d hq=%d hkv=%d k_sel=%d", batch, total_tokens, hq, hkv, k_sel);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -1036,6 +1051,7 @@ int dsa_sparse_gqa_attn_bwd_dedup(const void* q, const void* k, const void* v, c
                                   float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes,
                                   void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn_bwd_dedup");
   dsa::api_log("dsa_sparse_gqa_attn_bwd_dedup", "batch=%d total=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, total_tokens,
                hq, hkv, k_sel, workspace_bytes);
   DSA_NONNULL(q);
@@ -1111,6 +1127,7 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
                 int max_seqlen, int hq, int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale,
                 void* out, float* lse, int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_prefill");
   dsa::api_log("dsa_prefill", "batch=%d total=%d max_seqlen=%d hq=%d hkv=%d h_idx=%d d_idx=%d top_k=%d ws=%zu", batch, total_tokens, max_seqlen, hq, hkv, h_idx, d_idx, top_k, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(k);
@@ -1233,6 +1250,7 @@ int dsa_decode(const void* q, const void* q_idx, const float* w, const void* k_c
                int hkv, int head_dim, int h_idx, int d_idx, int top_k, float softmax_scale, void* out, float* lse,
                int32_t* idx_out, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_decode");
   dsa::api_log("dsa_decode", "batch=%d s_max=%d max_seq_len=%d hq=%d hkv=%d h_idx=%d d_idx=%d top_k=%d ws=%zu", batch, s_max, max_seq_len, hq, hkv, h_idx, d_idx, top_k, workspace_bytes);
   DSA_NONNULL(q);
   DSA_NONNULL(q_idx);
@@ -1313,6 +1331,7 @@ int dsa_sparse_gqa_attn_decode(const void* q, const void* k_cache, const void* v
                                float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
                                void* stream) {
   g_last_error[0] = 0;
+  const dsa::ApiRange range_("dsa_sparse_gqa_attn_decode");
   dsa::api_log("dsa_sparse_gqa_attn_decode", "batch=%d s_max=%d hq=%d hkv=%d k_sel=%d ws=%zu", batch, s_max, hq, hkv,
                k_sel, workspace_bytes);
   DSA_NONNULL(q);

@@ -248,5 +248,13 @@ hipError_t launch_indexer_bwd(const IndexerBwdArgs& a, hipStream_t s);
 int api_fail(int status, const char* fmt, ...);
 void api_clear_error();
 void api_log(const char* name, const char* fmt, ...);
+// One library call as a roctx range (named after the entry point), so a profiler's marker trace
+// shows each call around its kernels; without a profiler attached the calls do nothing.
+struct ApiRange {
+  explicit ApiRange(const char* name);
+  ~ApiRange();
+  ApiRange(const ApiRange&) = delete;
+  ApiRange& operator=(const ApiRange&) = delete;
+};
 
 }  // namespace dsa
