@@ -206,6 +206,12 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
   };
   auto wait_tile = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
+  // MODE 1: the wave's sample scores, staged in LDS until the end (so the tile waits need not
+  // wait for stores) — at most 2 kSampleCount / kSampleSplits entries.
+  constexpr int kSmpStage = MODE == 1 ? 2 * kSampleCount / kSampleSplits : 1;
+  __shared__ float smp_stage_all[MODE == 1 ? 4 : 1][kSmpStage];
+  float* smp_stage = smp_stage_all[MODE == 1 ? wave : 0];
+
   // MODE 2: this wave's token (one per wave), its threshold and its candidate list.
   __shared__ uint2 stage_all[MODE == 2 ? 4 : 1][MODE == 2 ? kEmitStage : 1];
   uint2* stage = stage_all[MODE == 2 ? wave : 0];
@@ -304,8 +310,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
           const int r = wave_r0 + s;
           const int key = key0 + lane;
           if (MODE == 1) {
-            if (r < row_end && key < m && r - seq_off + 1 > topk)
-              reinterpret_cast<float*>(cand + (size_t)(r - out_row0) * kTopkCandCap)[key] = v;
+            if (key < kend) smp_stage[key - kbeg] = v;
             continue;
           }
           if (MODE == 0 && r < row_end && key <= r - seq_off) scores[(size_t)(r - out_row0) * ld + key] = v;
@@ -336,6 +341,11 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(
     __syncthreads();
   }
   if (MODE == 2 && ns > 0) flush();
+  if (MODE == 1 && wave_r0 < row_end && wave_r0 - seq_off + 1 > topk) {
+    // the token's sample scores leave in one coalesced burst
+    float* dst_row = reinterpret_cast<float*>(cand + (size_t)(wave_r0 - out_row0) * kTopkCandCap);
+    for (int i = lane; i < kend - kbeg; i += 64) dst_row[kbeg + i] = smp_stage[i];
+  }
   if (MODE == 1 && split == 0 && lane == 0) {
 #pragma unroll
     for (int s = 0; s < NSLOT; ++s) {
