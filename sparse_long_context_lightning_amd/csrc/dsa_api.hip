@@ -1160,11 +1160,11 @@ int dsa_prefill(const void* q, const void* k, const void* v, const void* q_idx, 
   if (!workspace || workspace_bytes < prefill_chunk_bytes(min_rows, ld))
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes of the smallest chunk (%d rows)",
                 workspace_bytes, prefill_chunk_bytes(min_rows, ld), min_rows);
-  // Largest chunk of at most kDefaultChunkRows rows (a multiple of 64 when above 64) whose scores
-  // and top-k scratch fit (larger chunks measured slower).
+  // Largest chunk of at most kDefaultChunkRows rows (a multiple of 64 when above 64 and short of
+  // all rows) whose scores and top-k scratch fit (larger chunks measured slower).
   long long chunk = std::min<long long>(std::min(total_tokens, kDefaultChunkRows), (long long)(workspace_bytes / (ld * 4)));
   while (chunk > min_rows && prefill_chunk_bytes((int)chunk, ld) > workspace_bytes) --chunk;
-  if (chunk > 64) chunk = chunk / 64 * 64;
+  if (chunk > 64 && chunk < total_tokens) chunk = chunk / 64 * 64;  // (one chunk for everything: as is)
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* scores = static_cast<float*>(workspace);
   void* topk_ws = topk_scratch((int)chunk, ld)

@@ -47,3 +47,29 @@ def test_launch_timing_of_the_fused_prefill(dsa):
     want = tl.oracle_prefill_rows_lazy(pi, [2999, 2048, 600])
     tl.assert_idx_equal(idx1.cpu().numpy()[[2999, 2048, 600]], want["idx"], [2999, 2048, 600], "idx")
     assert np.isfinite(lse1.cpu().numpy()).all()
+
+
+def test_launch_log_of_the_fused_prefill(dsa):
+    """DSA_LOG=1: besides the call line, one stderr line per kernel launch, in launch order (a
+    child process, since the variable is read once per process)."""
+    import os
+    import subprocess
+    import sys
+    code = (
+        "import torch\n"
+        "import sparse_long_context_lightning_amd as dsa\n"
+        "from sparse_long_context_lightning_amd import inputs as inp\n"
+        "pi = inp.prefill_inputs([1000], 64, 128, 32, 4, 128, 256, seed=9)\n"
+        "dev = dsa.upload_prefill_inputs(pi)\n"
+        "dsa.prefill(dev['q'], dev['k'], dev['v'], dev['q_idx'], dev['k_idx'], dev['w'], pi.cu_seqlens, pi.top_k)\n"
+        "torch.cuda.synchronize()\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300,
+                         env=dict(os.environ, DSA_LOG="1"))
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [l.strip() for l in res.stderr.splitlines() if l.startswith("[dsa]")]
+    assert any(l.startswith("[dsa] dsa_prefill(batch=1 total=1000") for l in lines), lines
+    launches = [l.split("launch ", 1)[1] for l in lines if "launch " in l]
+    # one chunk of all 1000 rows on the fused top-k path, then the attention with dedup
+    assert launches == ["indexer_sample", "topk_threshold", "indexer_emit", "topk_select", "indexer_rescore",
+                        "topk_redo", "query_union", "sparse_attn_union", "sparse_attn"], launches
