@@ -73,3 +73,30 @@ def test_launch_log_of_the_fused_prefill(dsa):
     # one chunk of all 1000 rows on the fused top-k path, then the attention with dedup
     assert launches == ["indexer_sample", "topk_threshold", "indexer_emit", "topk_select", "indexer_rescore",
                         "topk_redo", "query_union", "sparse_attn_union", "sparse_attn"], launches
+
+
+def test_launch_timing_of_the_decode_step(dsa):
+    """The decode step's launches by name: the decode indexer, the top-k (one entry for its
+    threshold / collect / select), the split attention and its combine — one each per step."""
+    import torch
+    seq = [3000, 1, 700, 2049, 2999]
+    di = inp.decode_inputs(len(seq), 3000, seq, 64, 128, 32, 4, 128, 512, seed=21)
+    dev = tl.upload_decode(di)
+
+    def run():
+        return dsa.decode(dev["q"], dev["q_idx"], dev["w"], dev["k_cache"], dev["v_cache"], dev["k_idx_cache"],
+                          dev["seq_lens"], 512, max_seq_len=max(seq))
+
+    out0, lse0, idx0 = run()
+    dsa.dsa_timing_enable(True)
+    out1, lse1, idx1 = run()
+    out2, lse2, idx2 = run()
+    rec = dsa.dsa_timing_read()
+    dsa.dsa_timing_enable(False)
+    assert set(rec) >= {"indexer_decode", "topk", "sparse_attn_decode", "attn_combine"}, rec
+    for name in ("indexer_decode", "topk", "sparse_attn_decode", "attn_combine"):
+        ms, n = rec[name]
+        assert n == 2 and ms > 0, (name, rec[name])
+    for o, l, i in ((out1, lse1, idx1), (out2, lse2, idx2)):
+        assert torch.equal(i, idx0) and torch.equal(o.view(torch.int16), out0.view(torch.int16))
+        assert torch.equal(l, lse0)
