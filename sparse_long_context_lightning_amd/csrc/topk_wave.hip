@@ -349,6 +349,7 @@ __global__ __launch_bounds__(NW * 64) void topk_collect_kernel(const float* __re
 // workgroup, several workgroups per CU), 1024 when they are few (decode: a CU per row).
 constexpr int kSelThreads = 256;
 constexpr int kSelThreadsFew = 1024;
+constexpr int kSelThreadsFused = 512;  // the prefill's fused select (measured: 256 and 1024 slower)
 
 template <int NT>
 struct SelSmem {
@@ -684,12 +685,12 @@ static hipError_t launch_fused_select(const TopkArgs& a, int redo, hipStream_t s
   // chunk of short rows in a long packed batch keeps the smaller bitmap and more rows per CU.
   const long long max_len = a.row_len ? a.ld : std::min<long long>(a.ld, (long long)a.len_base + a.rows);
   if (max_len <= 131072)
-    hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
+    hipLaunchKernelGGL((topk_select_kernel<4096, kSelThreadsFused>), dim3((unsigned)a.rows), dim3(kSelThreadsFused), 0,
+                       s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
                        redo);
   else
-    hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreads>), dim3((unsigned)a.rows), dim3(kSelThreads), 0, s,
-                       a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
+    hipLaunchKernelGGL((topk_select_kernel<8192, kSelThreadsFused>), dim3((unsigned)a.rows), dim3(kSelThreadsFused), 0,
+                       s, a.scores, a.ld, a.rows, a.row_len, a.len_base, a.k, t.cnt, t.cand, a.idx_out, nullptr, t.fail,
                        redo);
   return hipGetLastError();
 }
