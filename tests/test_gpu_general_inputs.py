@@ -79,3 +79,33 @@ def test_topk_general_inputs_by_value(dsa):
         kth = np.sort(want)[::-1][top_k - 1]
         tol = 2 * (128 + 64 + 2) * 2.0 ** -24 * np.max(np.abs(wf[t]) @ (np.abs(qf[t]) @ np.abs(kf[:t + 1]).T))
         assert np.all(want[sel] >= kth - tol), f"row {t}: a selected score is below the k-th largest"
+
+
+def test_fused_prefill_general_inputs_equals_composition(dsa):
+    """The prefill's fused top-k (sampled threshold, candidates compared as floats in the indexer
+    pass) on general inputs with signed weights, where scores and, for rows a little longer than k,
+    the thresholds themselves are negative: its index sets equal dsa_topk over dsa_index_scores of
+    the same rows (the same fp32 scores, one tie rule), in both of the sequence's chunks."""
+    import torch
+    from sparse_long_context_lightning_amd import to_device_bf16
+    lens = [3000]
+    top_k = 256
+    cu, qi, ki, w = _general_inputs(lens, 64, 128, seed=313)
+    total = int(cu[-1])
+    rng = np.random.default_rng(314)
+    q, k, v = (inp.f32_to_bf16_bits(rng.standard_normal(s).astype(np.float32))
+               for s in ((total, 32, 128), (total, 4, 128), (total, 4, 128)))
+    dq, dk, dv, dqi, dki = (to_device_bf16(x) for x in (q, k, v, qi, ki))
+    dw = torch.from_numpy(w).cuda()
+    out, lse, idx = dsa.prefill(dq, dk, dv, dqi, dki, dw, cu, top_k)
+    scores = torch.empty((total, total), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores(dqi, dki, dw, cu, 0, total, scores)
+    row_len = torch.arange(1, total + 1, dtype=torch.int32, device="cuda")
+    ref = torch.empty((total, top_k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(scores, row_len, top_k, ref)
+    got, want = idx.cpu().numpy(), ref.cpu().numpy()
+    assert np.array_equal(got, want), f"first differing row {int(np.argmax((got != want).any(axis=1)))}"
+    # the rows just past k select with a negative k-th score
+    sc = scores.cpu().numpy()
+    kth = np.array([np.sort(sc[t, :t + 1])[::-1][top_k - 1] for t in range(top_k, 700)])
+    assert (kth < 0).sum() > 50
