@@ -50,6 +50,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+MAX_ENGINE_CLOCK_GHZ = 2.4    # the engine clock at which that peak is quoted
 
 PREFILL = "c3_prefill_128k"
 DECODE = "c4_decode_b32_128k"
@@ -359,6 +360,14 @@ def indexer_roofline(pre, counter_key=None):
     if counter_key:
         r["traffic"] = counter_traffic(counter_key)
         r["traffic_unit"] = "bytes per launch (HBM read+write, rocprofv3 FETCH_SIZE/WRITE_SIZE, calibrated)"
+        ent = counter_entry(counter_key)
+        if ent is not None and "shader_clock_ghz" in ent:
+            # The 2.5 PFLOP/s peak holds at the 2.4 GHz maximum engine clock; the committed clock
+            # pass measures the clock this kernel actually runs at (power-limited below 2.4 GHz).
+            clk = ent["shader_clock_ghz"]
+            r["shader_clock_ghz_by_counters"] = clk
+            r["peak_at_that_clock"] = PEAK_BF16_TFLOPS * clk / MAX_ENGINE_CLOCK_GHZ
+            r["frac_at_that_clock"] = pre["idx_tflops"] / r["peak_at_that_clock"]
     return r
 
 
