@@ -275,7 +275,7 @@ UnionLayout union_bwd_layout(int total_tokens, int k_sel, int hq, int hkv) {
 }
 
 // Sparse attention of the prefill rows described by `a` with adjacent-query dedup: merged sets
-// of every 16-row block, the merged-set kernel on the blocks flagged for it, the per-row kernel
+// of every kUnionBlockRows-row block, the merged-set kernel on the blocks flagged for it, the per-row kernel
 // on the others.  `ws` holds union_layout(a.rows, a.k_sel).bytes bytes.
 hipError_t launch_attn_dedup(dsa::SparseAttnArgs a, void* ws, hipStream_t s) {
   const UnionLayout u = union_layout(a.rows, a.k_sel);
